@@ -1,0 +1,91 @@
+"""Pins for the oracle's bitstream reader, fp64 GEMV and bf16 decode emulation.
+
+* the reader inverts the input generator's packer (two independent codes);
+* the per-block fp64 GEMV equals a dense numpy matmul of the fully decoded matrix;
+* the bf16 rounding equals torch's fp32 -> bfloat16 conversion (a library routine);
+* the bf16 decode is within one bf16 ulp of the exact fp64 weight.
+"""
+
+import numpy as np
+import torch
+
+from oracle import bijection, leech, reference
+from weight_decompression_amd import synth
+
+
+def test_reader_inverts_packer():
+    rng = np.random.default_rng(0)
+    for width in (7, 25, 44, 48, 57, 64):
+        hi = (1 << width) - 1
+        vals = rng.integers(0, hi, size=777, dtype=np.uint64, endpoint=True)
+        packed = synth.pack_fields(vals, width)
+        assert packed.size % 16 == 0 and packed.size >= (777 * width + 7) // 8 + 16
+        for j in range(0, 777, 13):
+            assert reference.read_field(packed.tobytes(), j, width) == int(vals[j])
+
+
+def test_gemv_equals_dense_matmul_euclid():
+    C3 = leech.index_count(3)
+    t = synth.make_tensor("t", 99, 0, 12, 100, C3, mode=reference.MODE_EUCLID, max_shell=3,
+                          shape_bits=25, gain_bits=0, x_dtype="f32", batch=2)
+    packed = t.packed.tobytes()
+    y, mag = reference.gemv(packed, t.rows, t.cols, 3, t.mode, 25, 0, t.scales_f16,
+                            t.scales_f16, t.x_f32)
+    W = np.zeros((t.rows, t.kb * 24))
+    for r in range(t.rows):
+        W[r] = reference.decode_row_points(packed, t.rows, t.cols, 3, 25, 0, r) * float(t.scales_f16[r])
+    x = np.zeros((2, t.kb * 24))
+    x[:, : t.cols] = t.x_f32
+    dense = x @ W.T
+    assert np.allclose(y, dense, rtol=1e-12, atol=1e-12)
+    assert np.allclose(mag, np.abs(x[:, None, :] * W[None, :, :]).sum(axis=2), rtol=1e-12)
+
+
+def test_gemv_equals_dense_matmul_shapegain():
+    C10 = leech.index_count(10)
+    t = synth.make_tensor("t", 98, 0, 6, 75, C10, batch=1)
+    packed = t.packed.tobytes()
+    y, _ = reference.gemv(packed, t.rows, t.cols, 10, t.mode, 44, 4, t.scales_f16, None, t.x_as_f64())
+    W = np.zeros((t.rows, t.kb * 24))
+    for r in range(t.rows):
+        for b in range(t.kb):
+            I, g = int(t.shape_idx[r, b]), int(t.gain_idx[r, b])
+            v = np.array(bijection.unrank(I, 10), dtype=np.float64)
+            W[r, b * 24:(b + 1) * 24] = float(t.scales_f16[g]) * v / np.linalg.norm(v)
+    x = np.zeros(t.kb * 24)
+    x[: t.cols] = t.x_as_f64()[0]
+    assert np.allclose(y[0], W @ x, rtol=1e-12, atol=1e-12)
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(1)
+    a = np.concatenate([rng.standard_normal(5000).astype(np.float32) * 10.0 ** rng.integers(-6, 6, 5000),
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 65504.0], dtype=np.float32)])
+    ours = reference.f32_to_bf16_bits(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(synth.bf16_round(a), ref)
+
+
+def test_bf16_decode_within_one_ulp_of_fp64():
+    C10 = leech.index_count(10)
+    t = synth.make_tensor("t", 97, 0, 3, 50, C10, batch=0)
+    packed = t.packed.tobytes()
+    for r in range(t.rows):
+        bits = reference.decode_row_bf16(packed, t.rows, t.cols, 10, t.mode, 44, 4, t.scales_f16, None, r)
+        got = reference.bf16_bits_to_f32(bits).astype(np.float64)
+        exact = []
+        for b in range(t.kb):
+            I, g = int(t.shape_idx[r, b]), int(t.gain_idx[r, b])
+            v = np.array(bijection.unrank(I, 10), dtype=np.float64)
+            exact.extend(float(t.scales_f16[g]) * v / np.linalg.norm(v))
+        exact = np.array(exact[: t.cols])
+        ulp = np.maximum(np.abs(exact), 1e-30) * 2.0 ** -7
+        assert np.all(np.abs(got - exact) <= ulp)
+
+
+def test_tolerance_rule():
+    y_ref = np.array([1.0, -2.0, 0.0])
+    mag = np.array([10.0, 4.0, 0.0])
+    ok = reference.gemv_within_tolerance(np.array([1.0 + 9e-4, -2.0 - 5e-4, 0.0]), y_ref, mag)
+    assert list(ok) == [True, False, True]
