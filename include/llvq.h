@@ -1,0 +1,137 @@
+/*
+ * llvq.h -- C ABI of the LLVQ (Leech-lattice vector quantization) decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (arXiv 2603.11021, "Leech Lattice Vector Quantization for Efficient LLM
+ * Compression"; papernotes.org notes, 方法详解 / 整体框架 and 关键设计 1, 2, 4;
+ * gist.science summary, Methodik / 3. Indexierungsschema and 4.
+ * Dequantisierungskernel; gptget.net, 原文摘要): weight rows are cut into 24-long
+ * blocks along the input channels; each block is stored as an integer index of a
+ * point of the Leech lattice (union of shells 2..M), optionally with a scalar-quantised
+ * gain.  The library turns indices back into lattice points (shell -> class -> Golay
+ * codeword / sign pattern / lexicographic permutation rank, undone with integer
+ * division and modulo) and, in the fused GEMV, dots them with the activations without
+ * writing decoded weights to memory.  The pages state the problem as converting to
+ * and from bitstrings without materialising the codebook, plus a fully parallel
+ * dequantisation kernel; the three compute entry points below are exactly those.
+ *
+ * Conventions fixed by this library (the pages leave them open):
+ *   Lattice coordinates are integers, sqrt(8) times the standard ones; shell m is the
+ *   set of points with x.x = 16 m (standard squared norm 2m).  Shape indices number
+ *   the points of shells 2..M in shell order, then class order, then
+ *   I_class = r + A * (s + 2^B * R) with r the codeword, s the sign pattern and R the
+ *   lexicographic rank of the absolute values.
+ *
+ *   Packed weights: a flat little-endian bitstream of fields of f = shape_bits +
+ *   gain_bits bits, one per block, row-major over (row, block); field j starts at bit
+ *   f*j and holds  shape | gain << shape_bits.  A row of K columns has
+ *   Kb = ceil(K/24) blocks; columns K..24*Kb-1 are padding (activations are taken as
+ *   zero there).  The buffer must hold llvq_packed_bytes(desc) bytes: the fields
+ *   rounded up to 16 bytes plus 16 bytes of slack that the kernels may read.
+ *
+ *   Reconstruction: SHAPEGAIN w_hat = G[g] * v / (4 sqrt(m)), G a per-tensor fp16 table
+ *   of 2^gain_bits entries; EUCLID w_hat = s[row] * v with s a per-row fp16 scale.
+ *
+ * Memory and streams: every array argument of the compute calls is a device pointer
+ * owned by the caller.  The calls validate their arguments on the host, enqueue work
+ * on `stream` (a hipStream_t; NULL means the default stream) and return without
+ * synchronising.  The library allocates no device memory and keeps no state between
+ * calls; its tables are compiled into the shared object.  Calls are thread-safe.
+ *
+ * Errors: synchronous return codes (below) report invalid arguments and launch
+ * failures; nothing is enqueued when a call returns an error.  Data errors found on
+ * the device (a shape index >= the number of points in shells 2..M, a point that is not
+ * in the lattice or not in shells 2..M) are counted: if `err_count` is not NULL the
+ * kernels add the number of such blocks/points to *err_count (a device int32, not
+ * cleared by the library).  Such a block decodes to the zero vector; such a point
+ * ranks to UINT64_MAX.
+ */
+#ifndef LLVQ_H_
+#define LLVQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  LLVQ_OK = 0,
+  LLVQ_EINVAL = -1,        /* invalid argument (null pointer, bad size, bad descriptor) */
+  LLVQ_EUNSUPPORTED = -2,  /* valid request this build does not implement              */
+  LLVQ_EHIP = -3           /* the HIP runtime reported an error at launch              */
+};
+
+enum { LLVQ_MODE_EUCLID = 0, LLVQ_MODE_SHAPEGAIN = 1 };
+enum { LLVQ_OUT_POINTS_I8 = 0, LLVQ_OUT_BF16 = 1 };
+enum { LLVQ_X_F32 = 0, LLVQ_X_BF16 = 1 };
+
+#define LLVQ_MAX_BATCH 16
+
+/* Description of one packed weight tensor W_hat [rows][cols]. */
+typedef struct {
+  int32_t mode;        /* LLVQ_MODE_EUCLID or LLVQ_MODE_SHAPEGAIN                        */
+  int32_t rows;        /* N >= 1: output features                                        */
+  int32_t cols;        /* K >= 1: input features; Kb = ceil(K/24) blocks per row          */
+  int32_t max_shell;   /* M in [2, 10]: shape indices cover shells 2..M                  */
+  int32_t shape_bits;  /* 1..60, with llvq_index_count(M) <= 2^shape_bits                 */
+  int32_t gain_bits;   /* EUCLID: 0.  SHAPEGAIN: 1..8.  shape_bits + gain_bits <= 64      */
+} llvq_desc;
+
+/* Number of valid shape indices for shells 2..max_shell (|Lambda24(M)|).  Host only.
+ * Writes *out and returns LLVQ_OK, or LLVQ_EINVAL if max_shell is outside [2, 10] or out
+ * is NULL. */
+int llvq_index_count(int32_t max_shell, uint64_t* out);
+
+/* Bytes the packed buffer of `d` must hold (see "Packed weights"), or a negative error
+ * code for an invalid descriptor.  Host only. */
+int64_t llvq_packed_bytes(const llvq_desc* d);
+
+/* Static text for a return code.  Host only. */
+const char* llvq_error_string(int code);
+
+/* Decode every block of a packed tensor (gist.science, Methodik / 4.
+ * Dequantisierungskernel: the index -> vector walk back through shell, class and the
+ * local symmetries).
+ *   packed  : llvq_packed_bytes(d) bytes, any alignment.
+ *   scales  : fp16; SHAPEGAIN: gain table [2^gain_bits]; EUCLID: row scales [rows].
+ *             Unused (may be NULL) for LLVQ_OUT_POINTS_I8.
+ *   out_kind: LLVQ_OUT_POINTS_I8 -> out is int8 [rows][Kb*24], the raw integer lattice
+ *             points including the padding columns (4-byte aligned);
+ *             LLVQ_OUT_BF16 -> out is bf16 [rows][cols], the reconstructed weights with
+ *             the padding columns dropped, each bit-defined as
+ *             bf16_rne(f32(v) * f32(f32(G[g]) * f32(1/(4 sqrt m)))) (SHAPEGAIN) or
+ *             bf16_rne(f32(v) * f32(s[row])) (EUCLID) (2-byte aligned).
+ * Returns LLVQ_OK, LLVQ_EINVAL or LLVQ_EHIP. */
+int llvq_decode(const llvq_desc* d, const void* packed, const void* scales, int32_t out_kind,
+                void* out, int32_t* err_count, void* stream);
+
+/* Fused dequantise-GEMV / small-batch GEMM: y[b][r] = sum_k W_hat[r][k] * x[b][k]
+ * (papernotes.org, 关键设计 4: decode each block from its index and accumulate its dot
+ * product with the activations without writing W_hat to memory).
+ *   packed, scales : as for llvq_decode (scales required).
+ *   x      : [batch][cols], contiguous, fp32 (LLVQ_X_F32, 4-byte aligned) or bf16
+ *            (LLVQ_X_BF16, 2-byte aligned).
+ *   batch  : 1..LLVQ_MAX_BATCH.
+ *   y      : fp32 [batch][rows], 4-byte aligned, overwritten (never accumulated into).
+ * Accumulation is fp32; results are deterministic (bitwise identical across runs).
+ * Returns LLVQ_OK, LLVQ_EINVAL or LLVQ_EHIP. */
+int llvq_gemv(const llvq_desc* d, const void* packed, const void* scales, const void* x,
+              int32_t x_dtype, int32_t batch, float* y, int32_t* err_count, void* stream);
+
+/* Rank lattice points: the inverse of the decode (gptget.net, 原文摘要: conversion to
+ * and from bitstrings without materialising the codebook).
+ *   points    : int8 [n][24] integer lattice coordinates (any alignment).
+ *   n         : number of points, >= 0 (0 is a no-op).
+ *   max_shell : M in [2, 10].
+ *   indices   : uint64 [n] output shape indices (8-byte aligned); UINT64_MAX for a point
+ *               that is not in the lattice or not in shells 2..M (counted in err_count).
+ * Returns LLVQ_OK, LLVQ_EINVAL or LLVQ_EHIP. */
+int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell, uint64_t* indices,
+                    int32_t* err_count, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLVQ_H_ */

@@ -1,0 +1,35 @@
+"""Timed CPU oracle run used as the reported CPU baseline of the benchmark.
+
+Runs the oracle exactly as it stands (decode every block of the sampled rows with the
+pure-Python bijection, then the fp64 dot products; oracle/reference.py) in a process
+pool over rows, and reports the wall time.  It is a reported baseline, not a target.
+"""
+
+import multiprocessing as mp
+import os
+import time
+
+from . import reference
+
+
+def _rows(args):
+    packed, rows, cols, M, mode, sb, gb, gains, scales, x, row_list = args
+    reference.gemv(packed, rows, cols, M, mode, sb, gb, gains, scales, x, row_list)
+    return len(row_list)
+
+
+def time_gemv_rows(packed, rows, cols, M, mode, shape_bits, gain_bits, gains, row_scales, x, row_list,
+                   procs=None):
+    """Wall seconds for the oracle GEMV of `row_list`, and the number of processes used."""
+    procs = procs or os.cpu_count() or 1
+    procs = max(1, min(procs, len(row_list)))
+    chunks = [row_list[i::procs] for i in range(procs)]
+    args = [(packed, rows, cols, M, mode, shape_bits, gain_bits, gains, row_scales, x, c) for c in chunks if c]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(len(args)) as pool:
+        pool.map(_rows, [(packed, rows, cols, M, mode, shape_bits, gain_bits, gains, row_scales, x, [row_list[0]])])
+        t0 = time.perf_counter()
+        done = sum(pool.map(_rows, args))
+        dt = time.perf_counter() - t0
+    assert done == len(row_list)
+    return dt, len(args)

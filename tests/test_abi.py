@@ -1,0 +1,107 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every function
+include/llvq.h declares, and its host-side validation rejects bad arguments before any
+launch (a rejected call enqueues nothing, so these run on a CPU-only machine)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_decompression_amd as wd
+from oracle import leech
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llvq.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(llvq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(wd.LIB_PATH):
+        pytest.fail("libllvq.so is not built (run __graft_entry__.build())")
+    return wd.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    declared = header_functions()
+    assert declared, "no functions found in include/llvq.h"
+    assert set(declared) == set(wd.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_index_count_matches_oracle(lib):
+    for M in range(2, 11):
+        assert wd.index_count(M) == leech.index_count(M)
+    out = ctypes.c_uint64()
+    assert lib.llvq_index_count(1, ctypes.byref(out)) == -1
+    assert lib.llvq_index_count(11, ctypes.byref(out)) == -1
+    assert lib.llvq_index_count(10, None) == -1
+
+
+def test_packed_bytes_rule(lib):
+    d = wd.make_desc(wd.MODE_SHAPEGAIN, 4096, 11008, 10, 44, 4)
+    nbits = 4096 * 459 * 48
+    assert wd.packed_bytes(d) == (nbits // 8 + 15) // 16 * 16 + 16
+    d1 = wd.make_desc(wd.MODE_EUCLID, 256, 240, 3, 25, 0)
+    assert wd.packed_bytes(d1) == ((256 * 10 * 25 + 7) // 8 + 15) // 16 * 16 + 16
+
+
+@pytest.mark.parametrize("bad", [
+    dict(mode=2), dict(rows=0), dict(cols=-1), dict(max_shell=1), dict(max_shell=11),
+    dict(shape_bits=43),                 # C_10 > 2^43
+    dict(gain_bits=0),                   # shape-gain needs a gain field
+    dict(gain_bits=9), dict(shape_bits=61),
+    dict(mode=0, gain_bits=4),           # Euclidean mode has no gain field
+])
+def test_descriptor_validation(lib, bad):
+    args = dict(mode=1, rows=8, cols=48, max_shell=10, shape_bits=44, gain_bits=4)
+    args.update(bad)
+    d = wd.Desc(args["mode"], args["rows"], args["cols"], args["max_shell"], args["shape_bits"], args["gain_bits"])
+    assert lib.llvq_packed_bytes(ctypes.byref(d)) == -1
+    dummy = ctypes.c_void_p(0x1000)
+    assert lib.llvq_gemv(ctypes.byref(d), dummy, dummy, dummy, 1, 1, dummy, None, None) == -1
+    assert lib.llvq_decode(ctypes.byref(d), dummy, dummy, 0, dummy, None, None) == -1
+
+
+def test_pointer_and_batch_validation(lib):
+    d = wd.make_desc(wd.MODE_SHAPEGAIN, 8, 48, 10, 44, 4)
+    p = ctypes.c_void_p(0x10000)
+    assert lib.llvq_gemv(ctypes.byref(d), None, p, p, 1, 1, p, None, None) == -1          # null packed
+    assert lib.llvq_gemv(ctypes.byref(d), ctypes.c_void_p(0x10004), p, p, 1, 1, p, None, None) == -1  # misaligned
+    assert lib.llvq_gemv(ctypes.byref(d), p, p, p, 1, 0, p, None, None) == -1             # batch 0
+    assert lib.llvq_gemv(ctypes.byref(d), p, p, p, 1, 17, p, None, None) == -1            # batch 17
+    assert lib.llvq_gemv(ctypes.byref(d), p, p, p, 7, 1, p, None, None) == -1             # bad x dtype
+    assert lib.llvq_decode(ctypes.byref(d), p, p, 5, p, None, None) == -1                 # bad out kind
+    assert lib.llvq_decode(ctypes.byref(d), p, None, 1, p, None, None) == -1              # bf16 needs scales
+    assert lib.llvq_gemv(None, p, p, p, 1, 1, p, None, None) == -1                        # null descriptor
+
+
+def test_encode_validation_and_empty(lib):
+    p = ctypes.c_void_p(0x10000)
+    assert lib.llvq_encode_ref(p, 10, 1, p, None, None) == -1
+    assert lib.llvq_encode_ref(p, -1, 10, p, None, None) == -1
+    assert lib.llvq_encode_ref(None, 10, 10, p, None, None) == -1
+    assert lib.llvq_encode_ref(p, 10, 10, ctypes.c_void_p(0x10004), None, None) == -1
+    assert lib.llvq_encode_ref(None, 0, 10, None, None, None) == 0                       # empty: no-op
+
+
+def test_error_strings(lib):
+    for code in (0, -1, -2, -3, 42):
+        assert isinstance(lib.llvq_error_string(code), bytes)
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = wd._lib
+    try:
+        wd._lib = None
+        with pytest.raises(RuntimeError, match="not found"):
+            wd.load_library(str(tmp_path / "missing.so"))
+    finally:
+        wd._lib = saved

@@ -1,0 +1,306 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: decoded lattice points and bf16 weights bit-exact; GEMV outputs within 1e-4 of the
+fp64 oracle, normalised by sum_k |W_hat[r,k] x[k]|; indices bit-exact in the rank
+round trip.  Inputs are the seeded synthetic workloads of weight_decompression_amd/synth.py.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import weight_decompression_amd as wd
+from oracle import bijection, classes, golay, leech, reference
+from weight_decompression_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+C3 = leech.index_count(3)
+C10 = leech.index_count(10)
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    wd.load_library()
+    torch.cuda.init()
+    yield
+
+
+def dev(t: synth.Tensor):
+    packed = torch.from_numpy(t.packed).cuda()
+    scales = torch.from_numpy(t.scales_f16.copy()).cuda()
+    x = None
+    if t.x_bits is not None:
+        x = torch.from_numpy(t.x_bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+    elif t.x_f32 is not None:
+        x = torch.from_numpy(t.x_f32.copy()).cuda()
+    desc = wd.make_desc(t.mode, t.rows, t.cols, t.max_shell, t.shape_bits, t.gain_bits)
+    assert packed.numel() >= wd.packed_bytes(desc)
+    return desc, packed, scales, x
+
+
+def gpu_points(t):
+    desc, packed, scales, _ = dev(t)
+    out = torch.empty((t.rows, t.kb * 24), dtype=torch.int8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.decode(desc, packed, scales, wd.OUT_POINTS_I8, out, err)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), int(err.item())
+
+
+def gpu_gemv(t, repeat=1):
+    desc, packed, scales, x = dev(t)
+    batch = x.shape[0]
+    outs = []
+    for _ in range(repeat):
+        y = torch.full((batch, t.rows), float("nan"), dtype=torch.float32, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        wd.gemv(desc, packed, scales, x, y, err)
+        torch.cuda.synchronize()
+        outs.append((y.cpu().numpy(), int(err.item())))
+    return outs
+
+
+def oracle_gemv(t, rows):
+    x = t.x_as_f64()
+    return reference.gemv(t.packed.tobytes(), t.rows, t.cols, t.max_shell, t.mode, t.shape_bits, t.gain_bits,
+                          t.scales_f16, t.scales_f16, x, rows)
+
+
+def check_gemv(t, rows, label):
+    (y, err), = gpu_gemv(t)
+    assert err == 0
+    assert np.all(np.isfinite(y)), label
+    y_ref, mag = oracle_gemv(t, rows)
+    got = y[:, rows].astype(np.float64)
+    e = reference.normalized_errors(got, y_ref, mag)
+    say(f"{label}: max normalised error {e.max():.3e} over {e.size} outputs")
+    assert np.all(reference.gemv_within_tolerance(got, y_ref, mag)), (label, e.max())
+    return y
+
+
+def sample_rows(n, k, seed):
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, n - 1), size=min(k, n - 2), replace=False)
+    return sorted(set([0, n - 1] + [int(v) for v in mid]))
+
+
+# ---------------------------------------------------------------------------
+# decode -> int8 points
+
+def test_decode_points_tiny_workload_full():
+    t = synth.workload1(C3)
+    say(f"decode points {t.name}")
+    pts, err = gpu_points(t)
+    assert err == 0
+    for r in range(t.rows):
+        ref = reference.decode_row_points(t.packed.tobytes(), t.rows, t.cols, 3, 25, 0, r)
+        assert np.array_equal(pts[r].astype(np.int64), ref), r
+
+
+def point_list_tensor(indices, max_shell=10, shape_bits=44, gain_bits=4):
+    idx = np.asarray(indices, dtype=np.uint64).reshape(-1, 1)
+    packed = synth.pack_fields(idx, shape_bits + gain_bits)
+    return synth.Tensor("points", synth.MODE_SHAPEGAIN, idx.shape[0], 24, max_shell, shape_bits, gain_bits, idx,
+                        np.zeros_like(idx), np.ones(1 << gain_bits, dtype=np.float16), packed)
+
+
+def test_decode_points_every_class_boundary_and_shell():
+    rng = np.random.default_rng(7)
+    idx = []
+    for c in classes.class_table(10):
+        idx += [c.start, c.end - 1, c.start + int(rng.integers(0, c.size))]
+    Cm = leech.cumulative_counts(10)
+    for m in range(2, 11):
+        idx += [int(v) for v in rng.integers(Cm[m - 1], Cm[m], size=300, dtype=np.uint64)]
+    idx += [0, C10 - 1]
+    say(f"decode points: {len(idx)} indices over all classes")
+    t = point_list_tensor(idx)
+    pts, err = gpu_points(t)
+    assert err == 0
+    for j, I in enumerate(idx):
+        assert list(pts[j].astype(int)) == bijection.unrank(int(I), 10), I
+
+
+def test_decode_points_uniform_sample_matches_oracle():
+    t = synth.make_tensor("u", 11, 0, 64, 24 * 40, C10, batch=0)
+    pts, err = gpu_points(t)
+    assert err == 0
+    for r in range(0, 64, 7):
+        ref = reference.decode_row_points(t.packed.tobytes(), t.rows, t.cols, 10, 44, 4, r)
+        assert np.array_equal(pts[r].astype(np.int64), ref), r
+
+
+def test_out_of_range_index_gives_zero_block_and_counts():
+    idx = [5, C10, C10 + 12345, (1 << 44) - 1, 7]
+    t = point_list_tensor(idx)
+    pts, err = gpu_points(t)
+    assert err == 3
+    assert list(pts[0]) == bijection.unrank(5, 10)
+    assert not pts[1:4].any()
+    assert list(pts[4]) == bijection.unrank(7, 10)
+
+
+# ---------------------------------------------------------------------------
+# decode -> bf16
+
+def test_decode_bf16_shapegain_bit_exact():
+    t = synth.make_tensor("bf", 12, 0, 48, 4096, C10, batch=0)
+    desc, packed, scales, _ = dev(t)
+    out = torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device="cuda")
+    wd.decode(desc, packed, scales, wd.OUT_BF16, out)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for r in sample_rows(t.rows, 10, 1):
+        ref = reference.decode_row_bf16(t.packed.tobytes(), t.rows, t.cols, 10, t.mode, 44, 4, t.scales_f16, None, r)
+        assert np.array_equal(got[r], ref), r
+
+
+def test_decode_bf16_euclid_ragged_bit_exact():
+    t = synth.make_tensor("bfe", 13, 0, 37, 100, C3, mode=synth.MODE_EUCLID, max_shell=3, shape_bits=25,
+                          gain_bits=0, batch=0)
+    desc, packed, scales, _ = dev(t)
+    out = torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device="cuda")
+    wd.decode(desc, packed, scales, wd.OUT_BF16, out)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for r in range(t.rows):
+        ref = reference.decode_row_bf16(t.packed.tobytes(), t.rows, t.cols, 3, t.mode, 25, 0, None, t.scales_f16, r)
+        assert np.array_equal(got[r], ref), r
+
+
+# ---------------------------------------------------------------------------
+# fused GEMV
+
+def test_gemv_tiny_workload_all_rows():
+    t = synth.workload1(C3)
+    check_gemv(t, list(range(t.rows)), t.name)
+
+
+def test_gemv_q_proj_4096x4096_sampled_and_deterministic():
+    t = synth.workload2(C10)
+    check_gemv(t, sample_rows(t.rows, 40, 2), t.name)
+    (y1, _), (y2, _) = gpu_gemv(t, repeat=2)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def _fidelity(which):
+    path = os.path.join(HERE, "golden", f"fidelity_c3_{which}.npz")
+    if not os.path.exists(path):
+        return None
+    z = np.load(path)
+    return z["shape_idx"], z["gain_idx"].astype(np.uint64)
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_gemv_mlp_shapes_with_fidelity_rows(which):
+    fid = _fidelity(which)
+    t = synth.workload3(C10, which, fid)
+    rows = sample_rows(t.rows, 24, 3 + which)
+    if fid is not None:
+        rows = sorted(set(rows) | set(range(0, fid[0].shape[0], 4)))
+    check_gemv(t, rows, t.name)
+
+
+@pytest.mark.parametrize("batch", [1, 4, 8, 16])
+def test_gemm_28672x8192_small_batch(batch):
+    t = synth.workload4(C10, batch)
+    check_gemv(t, sample_rows(t.rows, 12, 5 + batch), f"{t.name} batch {batch}")
+
+
+@pytest.mark.parametrize("rows,cols,batch,xd", [(1, 1, 1, "f32"), (3, 23, 2, "bf16"), (5, 25, 3, "f32"),
+                                                (70, 100, 1, "bf16"), (2, 24 * 65 + 7, 16, "bf16")])
+def test_gemv_ragged_edges(rows, cols, batch, xd):
+    t = synth.make_tensor("edge", 14, rows * 1000 + cols, rows, cols, C10, batch=batch, x_dtype=xd)
+    check_gemv(t, list(range(rows)), f"edge {rows}x{cols} b{batch}")
+
+
+def test_gemv_euclid_fp32_and_bf16_x():
+    for xd in ("f32", "bf16"):
+        t = synth.make_tensor("eu", 15, 1 if xd == "f32" else 2, 64, 240, C3, mode=synth.MODE_EUCLID, max_shell=3,
+                              shape_bits=25, gain_bits=0, batch=2, x_dtype=xd)
+        check_gemv(t, list(range(t.rows)), f"euclid x={xd}")
+
+
+def test_gemv_other_max_shells():
+    for M in (2, 5, 8):
+        C = leech.index_count(M)
+        bits = max(1, (C - 1).bit_length())
+        t = synth.make_tensor(f"M{M}", 16, M, 33, 24 * 70 + 5, C, max_shell=M, shape_bits=bits, gain_bits=3)
+        check_gemv(t, list(range(t.rows)), f"max_shell {M} ({bits}+3 bit fields)")
+
+
+# ---------------------------------------------------------------------------
+# rank (encode_ref) and the index round trip
+
+def membership_torch(pts):
+    """Vectorised lattice membership (independent of both implementations):
+    parity, sum rule and the residue mask looked up in a 2^24 codeword bitmap."""
+    x = pts.to(torch.int32)
+    p = x[:, :1] & 1
+    same = ((x & 1) == p).all(dim=1)
+    sums = x.sum(dim=1)
+    sum_ok = ((sums - 4 * p[:, 0]) % 8) == 0
+    want = torch.where(p == 1, 1, 2)
+    bits = (((x % 4) == want).to(torch.int64) << torch.arange(24, device=x.device)).sum(dim=1)
+    bitmap = torch.zeros(1 << 24, dtype=torch.bool, device=x.device)
+    bitmap[torch.tensor(golay.table(), dtype=torch.int64, device=x.device)] = True
+    return same & sum_ok & bitmap[bits]
+
+
+def test_round_trip_one_million_points():
+    n = 1 << 20
+    idx = synth.workload5_roundtrip_indices(C10, n, chunk=0)
+    t = point_list_tensor(idx)
+    desc, packed, scales, _ = dev(t)
+    pts = torch.empty((n, 24), dtype=torch.int8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.decode(desc, packed, scales, wd.OUT_POINTS_I8, pts, err)
+    back = torch.empty(n, dtype=torch.int64, device="cuda")
+    wd.encode_ref(pts, 10, back, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    expect = torch.from_numpy(idx.view(np.int64)).cuda()
+    assert torch.equal(back, expect)
+    assert bool(membership_torch(pts).all())
+    n2 = (pts.to(torch.int32) ** 2).sum(dim=1)
+    assert bool(((n2 % 16) == 0).all()) and int(n2.min()) >= 32 and int(n2.max()) <= 160
+    sample = np.random.default_rng(8).choice(n, 300, replace=False)
+    host = pts.cpu().numpy()
+    for j in sample:
+        assert list(host[j].astype(int)) == bijection.unrank(int(idx[j]), 10)
+
+
+def test_rank_matches_oracle_and_flags_bad_points():
+    rng = np.random.default_rng(9)
+    good = [bijection.unrank(int(I), 10) for I in rng.integers(0, C10, size=200, dtype=np.uint64)]
+    bad = [[1] * 24, [0] * 24, [2] + [0] * 23, [4, 4] + [0] * 22 + [0], [12] * 24]
+    bad[3] = [4, 4] + [0] * 22
+    pts = np.array(good + bad, dtype=np.int8)
+    expect = [bijection.rank(x, 10) for x in good]
+    p = torch.from_numpy(pts).cuda()
+    out = torch.empty(len(pts), dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.encode_ref(p, 10, out, err)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint64)
+    assert [int(v) for v in got[:200]] == expect
+    # [4,4,0..] is a lattice point of shell 2 (valid); the others are not points of shells 2..10
+    assert int(got[200 + 3]) == bijection.rank(bad[3], 10)
+    assert all(int(v) == (1 << 64) - 1 for i, v in enumerate(got[200:]) if i != 3)
+    assert int(err.item()) == 4
+    # a shell-10 point is out of range when only shells 2..9 are allowed
+    out9 = torch.empty(1, dtype=torch.int64, device="cuda")
+    x10 = torch.from_numpy(np.array([bijection.unrank(C10 - 1, 10)], dtype=np.int8)).cuda()
+    wd.encode_ref(x10, 9, out9)
+    torch.cuda.synchronize()
+    assert int(out9.cpu().numpy().view(np.uint64)[0]) == (1 << 64) - 1

@@ -1,0 +1,76 @@
+"""Build the LLVQ HIP library in-tree.
+
+Steps:
+  1. compile the host table generator (csrc/gen_tables.cpp) with g++;
+  2. run it to write the table header (and a JSON dump of the same tables);
+  3. compile csrc/llvq.hip for gfx950 with hipcc into weight_decompression_amd/libllvq.so.
+
+Generated files go to <repo>/_build/ (not committed).  Packed-fp32 VALU instructions
+are switched off for all device code.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+REPO_DIR = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(REPO_DIR, "include")
+BUILD_DIR = os.path.join(REPO_DIR, "_build")
+LIB_PATH = os.path.join(PKG_DIR, "libllvq.so")
+TABLES_INC = os.path.join(BUILD_DIR, "llvq_tables.inc")
+TABLES_JSON = os.path.join(BUILD_DIR, "llvq_tables.json")
+GEN_BIN = os.path.join(BUILD_DIR, "gen_tables")
+
+OFFLOAD_ARCH = "gfx950"
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print("+ " + " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build_tables(verbose=True):
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    _run(["g++", "-O2", "-std=c++17", "-Wall", "-o", GEN_BIN, os.path.join(CSRC, "gen_tables.cpp")], verbose)
+    _run([GEN_BIN, "--header", TABLES_INC], verbose)
+    _run([GEN_BIN, "--json", TABLES_JSON], verbose)
+
+
+def hipcc_path():
+    p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(p):
+        raise RuntimeError("hipcc not found: the LLVQ library needs ROCm's hipcc to build")
+    return p
+
+
+def build(verbose=True):
+    build_tables(verbose)
+    tmp = LIB_PATH + ".tmp"
+    cmd = [
+        hipcc_path(),
+        f"--offload-arch={OFFLOAD_ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-shared",
+        "-fvisibility=hidden",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall",
+        "-I", INCLUDE,
+        "-I", CSRC,
+        "-I", BUILD_DIR,
+        "-o", tmp,
+        os.path.join(CSRC, "llvq.hip"),
+    ]
+    _run(cmd, verbose)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,589 @@
+// LLVQ decode / fused dequant-GEMV / rank kernels for gfx950, and the C ABI around them.
+//
+// Method: "Leech Lattice Vector Quantization for Efficient LLM Compression"
+// (papernotes.org notes, 方法详解 / 关键设计 2 for the index hierarchy and its
+// div/mod inverse, 关键设计 4 for the fused kernel; gist.science summary, Methodik /
+// 4. Dequantisierungskernel).  Conventions are those of include/llvq.h and of the table
+// generator gen_tables.cpp.
+//
+// Decode of one 24-block (one lane):
+//   field -> shape index I (and gain index g)
+//   class k with start_k <= I < start_{k+1}: bucket table on the top bits of I, then a
+//     short forward scan;
+//   J = I - start_k;  r = J mod A,  I' = J div A,  s = I' mod 2^B,  R = I' div 2^B;
+//   codeword c = T[toff + r];
+//   R is the lexicographic rank of the absolute values.  It is unranked by exact
+//     arithmetic decoding: u = (R + 1/2) / P and, at each of the 24 steps with n values
+//     left and counts c_j, the value index is the number of cumulative counts
+//     C_j <= u*n; then u <- (u*n - C_k) / c_k.  In fp64 the decision margins
+//     (>= n/(2Q) with Q <= 4.2e8 arrangements left) dwarf the rounding error, so every
+//     decision is exact.  Even classes run the support values (w steps) and then the
+//     complement values on the same u; this reproduces I'' = rank_S * P_T + rank_T.
+//   Values are placed in position order (support values on the codeword's positions,
+//     complement values on the others) and signed: odd classes by the codeword and
+//     |v| mod 4; even classes from the bits of s on the nonzero positions in ascending
+//     order, except the highest codeword position, whose sign fixes the parity pi.
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "llvq.h"
+#include "llvq_tables.h"
+
+#define LLVQ_API extern "C" __attribute__((visibility("default")))
+
+namespace host_tables {
+#define LLVQ_TABLE static const
+#include "llvq_tables.inc"
+#undef LLVQ_TABLE
+}  // namespace host_tables
+
+namespace dev_tables {
+#define LLVQ_TABLE __device__ const
+#include "llvq_tables.inc"
+#undef LLVQ_TABLE
+}  // namespace dev_tables
+
+namespace {
+
+constexpr int kDim = 24;
+
+struct KDesc {
+  int32_t mode, rows, cols, kb;
+  int32_t max_shell, shape_bits, gain_bits, field_bits;
+  uint64_t index_count;
+  uint64_t shape_mask;
+  int32_t ncls, bshift;
+};
+
+// ---------------------------------------------------------------------------
+// device helpers
+
+__device__ __forceinline__ uint64_t read_field(const uint8_t* __restrict__ packed, uint64_t j, int f) {
+  const uint64_t bit = j * (uint64_t)f;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(packed) + (bit >> 5);
+  const uint32_t sh = (uint32_t)(bit & 31u);
+  uint64_t v = ((uint64_t)w[0] | ((uint64_t)w[1] << 32)) >> sh;
+  if (sh + (uint32_t)f > 64u) v |= (uint64_t)w[2] << (64u - sh);
+  return f == 64 ? v : (v & ((1ull << f) - 1ull));
+}
+
+__device__ __forceinline__ int find_class(uint64_t I, const KDesc& d) {
+  int k = dev_tables::kBucketTable[d.max_shell][(uint32_t)(I >> d.bshift)];
+  while (k + 1 < d.ncls && I >= dev_tables::kClassTable[k + 1].start) ++k;
+  return k;
+}
+
+// Integer lattice point of shape index I (class k already found).
+__device__ __forceinline__ void decode_point(uint64_t I, int k, int v[kDim]) {
+  const LlvqClassRec& cr = dev_tables::kClassTable[k];
+  const uint64_t J = I - cr.start;
+  const uint32_t A = cr.A;
+  uint32_t r, ip;
+  if (A == 4096u) {
+    r = (uint32_t)J & 4095u;
+    ip = (uint32_t)(J >> 12);
+  } else if (A == 1u) {
+    r = 0u;
+    ip = (uint32_t)J;
+  } else {
+    // quotient < 2^32; fp64 estimate then one exact correction on the remainder
+    uint32_t q = (uint32_t)((double)J / (double)A);
+    int32_t rem = (int32_t)((uint32_t)J - q * A);
+    if (rem < 0) {
+      q -= 1u;
+      rem += (int32_t)A;
+    } else if (rem >= (int32_t)A) {
+      q += 1u;
+      rem -= (int32_t)A;
+    }
+    r = (uint32_t)rem;
+    ip = q;
+  }
+  const uint32_t B = cr.B;
+  const uint32_t s = ip & ((1u << B) - 1u);
+  const uint32_t R = ip >> B;
+  const uint32_t c = dev_tables::kGolayTable[cr.toff + r];
+  const int w = cr.w;
+
+  double u = ((double)R + 0.5) * cr.inv_p;
+  uint32_t cnt = w ? cr.cnt_s : cr.cnt_t;
+  uint64_t codes = 0;
+#pragma unroll
+  for (int i = 0; i < kDim; ++i) {
+    if (i == w) cnt = cr.cnt_t;
+    const int left = (i < w) ? (w - i) : (kDim - i);
+    const double y = u * (double)left;
+    const int c0 = cnt & 0xff, c1 = (cnt >> 8) & 0xff, c2 = (cnt >> 16) & 0xff, c3 = (int)(cnt >> 24);
+    const int t1 = c0, t2 = t1 + c1, t3 = t2 + c2;
+    const int kk = (y >= (double)t1) + (y >= (double)t2) + (y >= (double)t3);
+    const int ck = kk == 0 ? c0 : kk == 1 ? c1 : kk == 2 ? c2 : c3;
+    const int Ck = kk == 0 ? 0 : kk == 1 ? t1 : kk == 2 ? t2 : t3;
+    u = (y - (double)Ck) / (double)ck;
+    cnt -= 1u << (8 * kk);
+    codes |= (uint64_t)kk << (2 * i);
+  }
+
+  const uint32_t sel = w ? c : 0u;
+  uint64_t sS = codes;
+  uint64_t sT = codes >> (2 * w);
+  const int q = w ? (31 - __clz((int)c)) : -1;
+  uint32_t sbits = s;
+  uint32_t negS = 0;
+#pragma unroll
+  for (int p = 0; p < kDim; ++p) {
+    const bool inS = (sel >> p) & 1u;
+    const uint32_t code = (uint32_t)(inS ? sS : sT) & 3u;
+    if (inS)
+      sS >>= 2;
+    else
+      sT >>= 2;
+    const uint32_t vals = inS ? cr.vals_s : cr.vals_t;
+    const int a = (int)((vals >> (8 * code)) & 0xffu);
+    uint32_t neg;
+    if (cr.parity) {
+      neg = (uint32_t)(((a & 3) == 1) != (((c >> p) & 1u) != 0u));
+    } else if (a == 0) {
+      neg = 0u;
+    } else if (p == q) {
+      neg = (negS & 1u) ^ cr.pi;
+    } else {
+      neg = sbits & 1u;
+      sbits >>= 1;
+      if (inS) negS += neg;
+    }
+    v[p] = neg ? -a : a;
+  }
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ---------------------------------------------------------------------------
+// kernels
+
+__global__ __launch_bounds__(256) void k_decode_points(KDesc d, const uint8_t* __restrict__ packed,
+                                                        int8_t* __restrict__ out, int32_t* err) {
+  const uint64_t nblocks = (uint64_t)d.rows * (uint64_t)d.kb;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < nblocks; j += stride) {
+    const uint64_t I = read_field(packed, j, d.field_bits) & d.shape_mask;
+    int v[kDim];
+    if (I < d.index_count) {
+      decode_point(I, find_class(I, d), v);
+    } else {
+#pragma unroll
+      for (int p = 0; p < kDim; ++p) v[p] = 0;
+      if (err) atomicAdd(err, 1);
+    }
+    uint32_t* o = reinterpret_cast<uint32_t*>(out + j * kDim);
+#pragma unroll
+    for (int qd = 0; qd < kDim / 4; ++qd) {
+      o[qd] = ((uint32_t)(v[4 * qd] & 0xff)) | ((uint32_t)(v[4 * qd + 1] & 0xff) << 8) |
+              ((uint32_t)(v[4 * qd + 2] & 0xff) << 16) | ((uint32_t)(v[4 * qd + 3] & 0xff) << 24);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_decode_bf16(KDesc d, const uint8_t* __restrict__ packed,
+                                                      const __half* __restrict__ scales,
+                                                      uint16_t* __restrict__ out, int32_t* err) {
+  const uint64_t nblocks = (uint64_t)d.rows * (uint64_t)d.kb;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; j < nblocks; j += stride) {
+    const uint64_t fld = read_field(packed, j, d.field_bits);
+    const uint64_t I = fld & d.shape_mask;
+    const uint32_t row = (uint32_t)(j / (uint64_t)d.kb);
+    const uint32_t blk = (uint32_t)(j - (uint64_t)row * d.kb);
+    int v[kDim];
+    float scale = 0.0f;
+    if (I < d.index_count) {
+      const int k = find_class(I, d);
+      decode_point(I, k, v);
+      if (d.mode == LLVQ_MODE_SHAPEGAIN) {
+        const uint32_t g = (uint32_t)(fld >> d.shape_bits);
+        scale = __fmul_rn(__half2float(scales[g]), dev_tables::kInvNorm32[dev_tables::kClassTable[k].m]);
+      } else {
+        scale = __half2float(scales[row]);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < kDim; ++p) v[p] = 0;
+      if (err) atomicAdd(err, 1);
+    }
+    uint16_t* o = out + (uint64_t)row * d.cols + (uint64_t)blk * kDim;
+    const int lim = d.cols - (int)blk * kDim;
+#pragma unroll
+    for (int p = 0; p < kDim; ++p)
+      if (p < lim) o[p] = f32_to_bf16_rne(__fmul_rn((float)v[p], scale));
+  }
+}
+
+template <int BATCH, bool XBF16>
+__global__ __launch_bounds__(256) void k_gemv(KDesc d, const uint8_t* __restrict__ packed,
+                                               const __half* __restrict__ scales, const void* __restrict__ xv,
+                                               float* __restrict__ y, int32_t* err) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const int nwaves = (int)((gridDim.x * blockDim.x) >> 6);
+  const float* xf = reinterpret_cast<const float*>(xv);
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(xv);
+  for (int r = wave; r < d.rows; r += nwaves) {
+    float acc[BATCH];
+#pragma unroll
+    for (int bb = 0; bb < BATCH; ++bb) acc[bb] = 0.0f;
+    for (int blk = lane; blk < d.kb; blk += 64) {
+      const uint64_t j = (uint64_t)r * d.kb + blk;
+      const uint64_t fld = read_field(packed, j, d.field_bits);
+      const uint64_t I = fld & d.shape_mask;
+      if (I >= d.index_count) {
+        if (err) atomicAdd(err, 1);
+        continue;
+      }
+      const int k = find_class(I, d);
+      int v[kDim];
+      decode_point(I, k, v);
+      float scale = 1.0f;
+      if (d.mode == LLVQ_MODE_SHAPEGAIN) {
+        const uint32_t g = (uint32_t)(fld >> d.shape_bits);
+        scale = __half2float(scales[g]) * dev_tables::kInvNorm32[dev_tables::kClassTable[k].m];
+      }
+      const int col0 = blk * kDim;
+      const int lim = d.cols - col0;
+#pragma unroll
+      for (int bb = 0; bb < BATCH; ++bb) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int p = 0; p < kDim; ++p) {
+          if (p < lim) {
+            const uint64_t xi = (uint64_t)bb * d.cols + col0 + p;
+            const float xval = XBF16 ? bf16_to_f32(xb[xi]) : xf[xi];
+            dot = fmaf((float)v[p], xval, dot);
+          }
+        }
+        acc[bb] = fmaf(scale, dot, acc[bb]);
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < BATCH; ++bb) {
+      float t = acc[bb];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+      acc[bb] = t;
+    }
+    if (lane == 0) {
+      const float rs = d.mode == LLVQ_MODE_SHAPEGAIN ? 1.0f : __half2float(scales[r]);
+#pragma unroll
+      for (int bb = 0; bb < BATCH; ++bb) y[(uint64_t)bb * d.rows + r] = acc[bb] * rs;
+    }
+  }
+}
+
+// multiset helpers for the rank kernel -------------------------------------------------
+
+__device__ __forceinline__ uint64_t arrangements_u64(const int cnt[4]) {
+  // multinomial via successive binomials, all values < 2^32 for the classes used
+  uint64_t q = 1;
+  int n = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    for (int t = 1; t <= cnt[j]; ++t) {
+      ++n;
+      q = q * (uint64_t)n / (uint64_t)t;
+    }
+  }
+  return q;
+}
+
+// lexicographic rank of the sequence of value indices idx[0..len-1]
+__device__ __forceinline__ uint64_t lex_rank(const int* idx, int len, int cnt[4]) {
+  uint64_t q = arrangements_u64(cnt);
+  uint64_t rank = 0;
+  for (int i = 0; i < len; ++i) {
+    const int n = len - i;
+    const int a = idx[i];
+    for (int j = 0; j < a; ++j) rank += q * (uint64_t)cnt[j] / (uint64_t)n;
+    q = q * (uint64_t)cnt[a] / (uint64_t)n;
+    cnt[a] -= 1;
+  }
+  return rank;
+}
+
+__device__ __forceinline__ int index_of_value(uint32_t vals, int d, int a) {
+  for (int j = 0; j < d; ++j)
+    if ((int)((vals >> (8 * j)) & 0xffu) == a) return j;
+  return -1;
+}
+
+__device__ uint64_t rank_point(const int x[kDim], int max_shell, int ncls) {
+  const uint64_t bad = ~0ull;
+  const int p = x[0] & 1;
+  int sum = 0, norm = 0;
+  uint32_t mask = 0;
+  for (int i = 0; i < kDim; ++i) {
+    if ((x[i] & 1) != p) return bad;
+    sum += x[i];
+    norm += x[i] * x[i];
+    if ((x[i] & 3) == (p ? 1 : 2)) mask |= 1u << i;
+  }
+  if (((sum - 4 * p) & 7) != 0) return bad;
+  if (norm % 16) return bad;
+  const int m = norm / 16;
+  if (m < 2 || m > max_shell) return bad;
+  // codeword position: binary search inside the slice of its weight (T sorted by weight, mask)
+  const int wt = __popc(mask);
+  int lo = 0, hi = 4095;
+  {
+    // weight slices 0:[0], 8:[1,759], 12:[760,3335], 16:[3336,4094], 24:[4095]
+    if (wt == 0) { lo = 0; hi = 0; }
+    else if (wt == 8) { lo = 1; hi = 759; }
+    else if (wt == 12) { lo = 760; hi = 3335; }
+    else if (wt == 16) { lo = 3336; hi = 4094; }
+    else if (wt == 24) { lo = 4095; hi = 4095; }
+    else return bad;
+  }
+  int pos = -1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    const uint32_t cm = dev_tables::kGolayTable[mid];
+    if (cm == mask) { pos = mid; break; }
+    if (cm < mask) lo = mid + 1; else hi = mid - 1;
+  }
+  if (pos < 0) return bad;
+  // histogram of absolute values
+  int hist[13];
+  for (int a = 0; a < 13; ++a) hist[a] = 0;
+  for (int i = 0; i < kDim; ++i) {
+    const int a = x[i] < 0 ? -x[i] : x[i];
+    if (a > 12) return bad;
+    hist[a]++;
+  }
+  int nd = 0;
+  for (int a = 0; a < 13; ++a) nd += hist[a] != 0;
+  int k = -1;
+  for (int kk = 0; kk < ncls; ++kk) {
+    const LlvqClassRec& cr = dev_tables::kClassTable[kk];
+    if (cr.m != m || cr.parity != p || cr.d_s + cr.d_t != nd) continue;
+    bool ok = true;
+    for (int j = 0; j < cr.d_s && ok; ++j)
+      ok = hist[(cr.vals_s >> (8 * j)) & 0xffu] == (int)((cr.cnt_s >> (8 * j)) & 0xffu);
+    for (int j = 0; j < cr.d_t && ok; ++j)
+      ok = hist[(cr.vals_t >> (8 * j)) & 0xffu] == (int)((cr.cnt_t >> (8 * j)) & 0xffu);
+    if (ok) { k = kk; break; }
+  }
+  if (k < 0) return bad;
+  const LlvqClassRec& cr = dev_tables::kClassTable[k];
+  const uint32_t r = (uint32_t)pos - cr.toff;
+  uint64_t R;
+  uint32_t s = 0;
+  if (p) {
+    int idx[kDim];
+    int cnt[4] = {0, 0, 0, 0};
+    for (int j = 0; j < cr.d_t; ++j) cnt[j] = (int)((cr.cnt_t >> (8 * j)) & 0xffu);
+    for (int i = 0; i < kDim; ++i) idx[i] = index_of_value(cr.vals_t, cr.d_t, x[i] < 0 ? -x[i] : x[i]);
+    R = lex_rank(idx, kDim, cnt);
+  } else {
+    int idxS[kDim], idxT[kDim];
+    int nS = 0, nT = 0;
+    for (int i = 0; i < kDim; ++i) {
+      const int a = x[i] < 0 ? -x[i] : x[i];
+      if ((mask >> i) & 1u) idxS[nS++] = index_of_value(cr.vals_s, cr.d_s, a);
+      else idxT[nT++] = index_of_value(cr.vals_t, cr.d_t, a);
+    }
+    int cntS[4] = {0, 0, 0, 0}, cntT[4] = {0, 0, 0, 0};
+    for (int j = 0; j < cr.d_s; ++j) cntS[j] = (int)((cr.cnt_s >> (8 * j)) & 0xffu);
+    for (int j = 0; j < cr.d_t; ++j) cntT[j] = (int)((cr.cnt_t >> (8 * j)) & 0xffu);
+    const uint64_t rS = lex_rank(idxS, nS, cntS);
+    const uint64_t rT = lex_rank(idxT, nT, cntT);
+    R = rS * (uint64_t)cr.p_t + rT;
+    const int q = cr.w ? (31 - __clz((int)mask)) : -1;
+    int j = 0;
+    for (int i = 0; i < kDim; ++i) {
+      if (x[i] == 0 || i == q) continue;
+      if (x[i] < 0) s |= 1u << j;
+      ++j;
+    }
+  }
+  return cr.start + (uint64_t)r + (uint64_t)cr.A * ((uint64_t)s + (R << cr.B));
+}
+
+__global__ __launch_bounds__(256) void k_rank(const int8_t* __restrict__ pts, int64_t n, int max_shell, int ncls,
+                                               uint64_t* __restrict__ out, int32_t* err) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += stride) {
+    int x[kDim];
+    for (int i = 0; i < kDim; ++i) x[i] = pts[t * kDim + i];
+    const uint64_t I = rank_point(x, max_shell, ncls);
+    out[t] = I;
+    if (I == ~0ull && err) atomicAdd(err, 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int make_kdesc(const llvq_desc* d, KDesc* k) {
+  if (!d) return LLVQ_EINVAL;
+  if (d->mode != LLVQ_MODE_EUCLID && d->mode != LLVQ_MODE_SHAPEGAIN) return LLVQ_EINVAL;
+  if (d->rows <= 0 || d->cols <= 0) return LLVQ_EINVAL;
+  if (d->max_shell < 2 || d->max_shell > LLVQ_MAX_SHELL) return LLVQ_EINVAL;
+  if (d->shape_bits < 1 || d->shape_bits > 60) return LLVQ_EINVAL;
+  if (d->mode == LLVQ_MODE_EUCLID && d->gain_bits != 0) return LLVQ_EINVAL;
+  if (d->mode == LLVQ_MODE_SHAPEGAIN && (d->gain_bits < 1 || d->gain_bits > 8)) return LLVQ_EINVAL;
+  if (d->shape_bits + d->gain_bits > 64) return LLVQ_EINVAL;
+  const uint64_t count = host_tables::kIndexCount[d->max_shell];
+  if (d->shape_bits < 64 && count > (1ull << d->shape_bits)) return LLVQ_EINVAL;
+  k->mode = d->mode;
+  k->rows = d->rows;
+  k->cols = d->cols;
+  k->kb = (d->cols + kDim - 1) / kDim;
+  k->max_shell = d->max_shell;
+  k->shape_bits = d->shape_bits;
+  k->gain_bits = d->gain_bits;
+  k->field_bits = d->shape_bits + d->gain_bits;
+  k->index_count = count;
+  k->shape_mask = (1ull << d->shape_bits) - 1ull;
+  k->ncls = host_tables::kNumClassesUpTo[d->max_shell];
+  k->bshift = host_tables::kBucketShift[d->max_shell];
+  return LLVQ_OK;
+}
+
+int64_t packed_bytes_of(const KDesc& k) {
+  const uint64_t nbits = (uint64_t)k.rows * (uint64_t)k.kb * (uint64_t)k.field_bits;
+  uint64_t nbytes = (nbits + 7) / 8;
+  nbytes = (nbytes + 15) / 16 * 16;
+  return (int64_t)(nbytes + 16);
+}
+
+unsigned grid_for(uint64_t work_items, unsigned block) {
+  uint64_t g = (work_items + block - 1) / block;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return (unsigned)g;
+}
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? LLVQ_OK : LLVQ_EHIP;
+}
+
+}  // namespace
+
+LLVQ_API int llvq_index_count(int32_t max_shell, uint64_t* out) {
+  if (!out || max_shell < 2 || max_shell > LLVQ_MAX_SHELL) return LLVQ_EINVAL;
+  *out = host_tables::kIndexCount[max_shell];
+  return LLVQ_OK;
+}
+
+LLVQ_API int64_t llvq_packed_bytes(const llvq_desc* d) {
+  KDesc k;
+  const int st = make_kdesc(d, &k);
+  if (st != LLVQ_OK) return st;
+  return packed_bytes_of(k);
+}
+
+LLVQ_API const char* llvq_error_string(int code) {
+  switch (code) {
+    case LLVQ_OK: return "ok";
+    case LLVQ_EINVAL: return "invalid argument";
+    case LLVQ_EUNSUPPORTED: return "unsupported request";
+    case LLVQ_EHIP: return "HIP launch error";
+    default: return "unknown error code";
+  }
+}
+
+LLVQ_API int llvq_decode(const llvq_desc* d, const void* packed, const void* scales, int32_t out_kind,
+                         void* out, int32_t* err_count, void* stream) {
+  KDesc k;
+  int st = make_kdesc(d, &k);
+  if (st != LLVQ_OK) return st;
+  if (!packed || !out || !aligned(packed, 16)) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  const uint64_t nblocks = (uint64_t)k.rows * (uint64_t)k.kb;
+  const unsigned block = 256;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (out_kind == LLVQ_OUT_POINTS_I8) {
+    if (!aligned(out, 4)) return LLVQ_EINVAL;
+    hipLaunchKernelGGL(k_decode_points, dim3(grid_for(nblocks, block)), dim3(block), 0, s, k,
+                       static_cast<const uint8_t*>(packed), static_cast<int8_t*>(out), err_count);
+    return launch_status();
+  }
+  if (out_kind == LLVQ_OUT_BF16) {
+    if (!scales || !aligned(out, 2) || !aligned(scales, 2)) return LLVQ_EINVAL;
+    hipLaunchKernelGGL(k_decode_bf16, dim3(grid_for(nblocks, block)), dim3(block), 0, s, k,
+                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales),
+                       static_cast<uint16_t*>(out), err_count);
+    return launch_status();
+  }
+  return LLVQ_EINVAL;
+}
+
+namespace {
+template <int BATCH>
+int launch_gemv(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype, float* y,
+                int32_t* err, hipStream_t s) {
+  const unsigned block = 256;
+  const unsigned waves_per_block = block / 64;
+  unsigned grid = (unsigned)((k.rows + waves_per_block - 1) / waves_per_block);
+  if (grid > 8192) grid = 8192;
+  if (x_dtype == LLVQ_X_BF16)
+    hipLaunchKernelGGL((k_gemv<BATCH, true>), dim3(grid), dim3(block), 0, s, k, static_cast<const uint8_t*>(packed),
+                       static_cast<const __half*>(scales), x, y, err);
+  else
+    hipLaunchKernelGGL((k_gemv<BATCH, false>), dim3(grid), dim3(block), 0, s, k, static_cast<const uint8_t*>(packed),
+                       static_cast<const __half*>(scales), x, y, err);
+  return launch_status();
+}
+}  // namespace
+
+LLVQ_API int llvq_gemv(const llvq_desc* d, const void* packed, const void* scales, const void* x, int32_t x_dtype,
+                       int32_t batch, float* y, int32_t* err_count, void* stream) {
+  KDesc k;
+  int st = make_kdesc(d, &k);
+  if (st != LLVQ_OK) return st;
+  if (!packed || !scales || !x || !y) return LLVQ_EINVAL;
+  if (!aligned(packed, 16) || !aligned(scales, 2) || !aligned(y, 4)) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  if (x_dtype == LLVQ_X_F32) {
+    if (!aligned(x, 4)) return LLVQ_EINVAL;
+  } else if (x_dtype == LLVQ_X_BF16) {
+    if (!aligned(x, 2)) return LLVQ_EINVAL;
+  } else {
+    return LLVQ_EINVAL;
+  }
+  if (batch < 1 || batch > LLVQ_MAX_BATCH) return LLVQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (batch) {
+#define LLVQ_GEMV_CASE(B) \
+  case B:                 \
+    return launch_gemv<B>(k, packed, scales, x, x_dtype, y, err_count, s);
+    LLVQ_GEMV_CASE(1) LLVQ_GEMV_CASE(2) LLVQ_GEMV_CASE(3) LLVQ_GEMV_CASE(4)
+    LLVQ_GEMV_CASE(5) LLVQ_GEMV_CASE(6) LLVQ_GEMV_CASE(7) LLVQ_GEMV_CASE(8)
+    LLVQ_GEMV_CASE(9) LLVQ_GEMV_CASE(10) LLVQ_GEMV_CASE(11) LLVQ_GEMV_CASE(12)
+    LLVQ_GEMV_CASE(13) LLVQ_GEMV_CASE(14) LLVQ_GEMV_CASE(15) LLVQ_GEMV_CASE(16)
+#undef LLVQ_GEMV_CASE
+    default:
+      return LLVQ_EINVAL;
+  }
+}
+
+LLVQ_API int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell, uint64_t* indices,
+                             int32_t* err_count, void* stream) {
+  if (max_shell < 2 || max_shell > LLVQ_MAX_SHELL || n < 0) return LLVQ_EINVAL;
+  if (n == 0) return LLVQ_OK;
+  if (!points || !indices || !aligned(indices, 8)) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  const unsigned block = 256;
+  hipLaunchKernelGGL(k_rank, dim3(grid_for((uint64_t)n, block)), dim3(block), 0,
+                     reinterpret_cast<hipStream_t>(stream), points, n, max_shell,
+                     host_tables::kNumClassesUpTo[max_shell], indices, err_count);
+  return launch_status();
+}
