@@ -20,10 +20,12 @@ Readings taken (listed in the design doc):
   ascending position order, the complement values the other positions likewise;
 * signs, odd classes: x_i > 0 iff (|x_i| = 1 mod 4) == (i in c), i.e. the positions
   = 1 mod 4 are exactly the codeword;
-* signs, even classes: take the nonzero positions in ascending order, drop q = the
-  highest position of c (when w > 0); bit j of s (LSB first) is the sign of the j-th
-  remaining position, 1 meaning negative; x_q takes the sign that makes the number of
-  negative support entries = pi mod 2 (this is the sum = 0 mod 8 rule).
+* signs, even classes: the free positions are, in this order, the codeword's positions
+  in ascending order without q = its highest position, then the nonzero positions off
+  the codeword in ascending order (the order in which the two parts are unranked); bit
+  j of s (LSB first) is the sign of the j-th free position, 1 meaning negative; x_q
+  takes the sign that makes the number of negative support entries = pi mod 2 (this is
+  the sum = 0 mod 8 rule).
 """
 
 from . import golay
@@ -123,9 +125,8 @@ def unrank(I: int, M: int) -> list:
     for pos, a in zip(complement, multiset_unrank(rank_T, cl.complement_values)):
         absx[pos] = a
 
-    nonzero = [i for i in range(DIM) if absx[i] != 0]
     q = support[-1] if cl.w > 0 else None
-    free = [i for i in nonzero if i != q]
+    free = [i for i in support if i != q] + [i for i in complement if absx[i] != 0]
     negative = set(free[j] for j in range(len(free)) if (s >> j) & 1)
     if q is not None:
         neg_on_support = sum(1 for i in support if i in negative)
@@ -181,7 +182,7 @@ def rank(x, M: int) -> int:
         rank_T = multiset_rank([absx[i] for i in complement])
         R = rank_S * cl.P_T + rank_T
         q = support[-1] if cl.w > 0 else None
-        free = [i for i in range(DIM) if absx[i] != 0 and i != q]
+        free = [i for i in support if i != q] + [i for i in complement if absx[i] != 0]
         s = 0
         for j, i in enumerate(free):
             if x[i] < 0:

@@ -143,6 +143,25 @@ def test_regression_vectors():
         assert bijection.rank(x, M) == I
 
 
+def test_even_class_sign_bit_order():
+    # Worked by hand from the stated conventions.  Class 4.2^8.0^15 of shell 3 starts at
+    # 5,472,208 (w = 8, A = 759, B = 8, P_S = 1, P_T = 16, pi = (8*2 + 4)/4 mod 2 = 1).
+    # Take r = 0 (codeword T[1] = 0x00149f: positions 0,1,2,3,4,7,10,12; q = 12),
+    # s = 2^5 and I'' = 15: the complement arrangement of rank 15 puts the 4 on the first
+    # complement position (5).  Free positions in order: support 0,1,2,3,4,7,10 then the
+    # nonzero complement position 5, so bit 5 makes position 7 negative; one negative on
+    # the support already has parity pi, so q stays positive.
+    I = 5472208 + 0 + 759 * ((1 << 5) + 256 * 15)
+    x = [2, 2, 2, 2, 2, 4, 0, -2, 0, 0, 2, 0, 2] + [0] * 11
+    assert bijection.unrank(I, 10) == x
+    assert bijection.rank(x, 10) == I
+    # bit 7 is the complement position: -4 there, and q flips to restore parity pi
+    I2 = 5472208 + 759 * ((1 << 7) + 256 * 15)
+    x2 = [2, 2, 2, 2, 2, -4, 0, 2, 0, 0, 2, 0, -2] + [0] * 11
+    assert bijection.unrank(I2, 10) == x2
+    assert bijection.rank(x2, 10) == I2
+
+
 def test_rank_rejects_bad_points():
     with pytest.raises(ValueError):
         bijection.rank([1] * 24, M)                 # norm 24 is not a lattice point here

@@ -125,12 +125,17 @@ __device__ __forceinline__ void decode_point(uint64_t I, int k, int v[kDim]) {
     codes |= (uint64_t)kk << (2 * i);
   }
 
+  // signs of even classes: bits 0..w-2 of s go to the support positions below q (the
+  // highest support position) in ascending order, the following bits to the nonzero
+  // complement positions in ascending order; q fixes the parity of support negatives
   const uint32_t sel = w ? c : 0u;
   uint64_t sS = codes;
   uint64_t sT = codes >> (2 * w);
   const int q = w ? (31 - __clz((int)c)) : -1;
-  uint32_t sbits = s;
-  uint32_t negS = 0;
+  const uint32_t wm1 = w ? (uint32_t)(w - 1) : 0u;
+  uint32_t bitsS = s;
+  uint32_t bitsT = wm1 ? (s >> wm1) : s;
+  const uint32_t negq = w ? (((uint32_t)__popc(s & ((1u << wm1) - 1u)) & 1u) ^ cr.pi) : 0u;
 #pragma unroll
   for (int p = 0; p < kDim; ++p) {
     const bool inS = (sel >> p) & 1u;
@@ -147,11 +152,13 @@ __device__ __forceinline__ void decode_point(uint64_t I, int k, int v[kDim]) {
     } else if (a == 0) {
       neg = 0u;
     } else if (p == q) {
-      neg = (negS & 1u) ^ cr.pi;
+      neg = negq;
+    } else if (inS) {
+      neg = bitsS & 1u;
+      bitsS >>= 1;
     } else {
-      neg = sbits & 1u;
-      sbits >>= 1;
-      if (inS) negS += neg;
+      neg = bitsT & 1u;
+      bitsT >>= 1;
     }
     v[p] = neg ? -a : a;
   }
@@ -164,6 +171,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+#include "llvq_gemv_b1.h"
 
 // ---------------------------------------------------------------------------
 // kernels
@@ -405,7 +414,12 @@ __device__ uint64_t rank_point(const int x[kDim], int max_shell, int ncls) {
     const int q = cr.w ? (31 - __clz((int)mask)) : -1;
     int j = 0;
     for (int i = 0; i < kDim; ++i) {
-      if (x[i] == 0 || i == q) continue;
+      if (!((mask >> i) & 1u) || i == q) continue;
+      if (x[i] < 0) s |= 1u << j;
+      ++j;
+    }
+    for (int i = 0; i < kDim; ++i) {
+      if (((mask >> i) & 1u) || x[i] == 0) continue;
       if (x[i] < 0) s |= 1u << j;
       ++j;
     }
@@ -527,6 +541,34 @@ LLVQ_API int llvq_decode(const llvq_desc* d, const void* packed, const void* sca
 }
 
 namespace {
+constexpr uint32_t kLdsBudget = 160u * 1024u / 2u;   // two workgroups per CU
+
+// Batch-1 fused GEMV (llvq_gemv_b1.h).  Returns LLVQ_EUNSUPPORTED when the shape does
+// not fit its tiling (the generic kernel then runs).
+int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype,
+                   float* y, int32_t* err, hipStream_t s) {
+  if (k.kb > kB1TileMax) return LLVQ_EUNSUPPORTED;
+  const int rpt = kB1TileMax / k.kb;
+  const int tmax = rpt * k.kb;
+  const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
+  B1Args a;
+  a.rows_per_tile = rpt;
+  a.tile_blocks_max = tmax;
+  a.nbuckets = nbuckets;
+  a.L = b1_layout(k.ncls, nbuckets, k.kb, tmax, x_dtype == LLVQ_X_F32);
+  if (a.L.total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  const int ntiles = (k.rows + rpt - 1) / rpt;
+  int grid = 512;
+  if (grid > ntiles) grid = ntiles;
+  if (x_dtype == LLVQ_X_F32)
+    hipLaunchKernelGGL((k_gemv_b1<true>), dim3(grid), dim3(kB1Threads), a.L.total, s, k, a,
+                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, y, err);
+  else
+    hipLaunchKernelGGL((k_gemv_b1<false>), dim3(grid), dim3(kB1Threads), a.L.total, s, k, a,
+                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, y, err);
+  return launch_status();
+}
+
 template <int BATCH>
 int launch_gemv(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype, float* y,
                 int32_t* err, hipStream_t s) {
@@ -561,6 +603,10 @@ LLVQ_API int llvq_gemv(const llvq_desc* d, const void* packed, const void* scale
   }
   if (batch < 1 || batch > LLVQ_MAX_BATCH) return LLVQ_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (batch == 1) {
+    const int st1 = launch_gemv_b1(k, packed, scales, x, x_dtype, y, err_count, s);
+    if (st1 != LLVQ_EUNSUPPORTED) return st1;
+  }
   switch (batch) {
 #define LLVQ_GEMV_CASE(B) \
   case B:                 \

@@ -1,0 +1,405 @@
+// Fused LLVQ dequant-GEMV for one activation row (batch 1), gfx950.
+// Included once by llvq.hip (uses its KDesc, read_field and table namespaces).
+//
+// Work split: a workgroup of kB1Threads lanes owns tiles of R consecutive rows
+// (T = R * Kb <= kB1TileMax blocks).  For each tile:
+//   1. classify: every block's field is read, its class found (bucket table + short
+//      scan) and its flat tile index appended to one of two LDS queues: odd-coset
+//      classes at the front, even-coset classes at the back.  Invalid indices
+//      (>= the shell-union size) contribute 0 and are counted.
+//   2. decode + dot, one lane per block, queues processed in 64-block wave chunks so
+//      that a wave is (almost always) single-parity:
+//      - odd path: the 24 absolute values are unranked in position order with a
+//        compile-time number of values left; the sign of each value follows from the
+//        codeword bit and the value mod 4, folded into one byte-table lookup (v_perm);
+//      - even path: support values then complement values in decode order, placed on
+//        the codeword's (resp. complement's) positions through a per-lane LDS scratch
+//        row; the sign bits of s are consumed on nonzero positions in ascending order
+//        per part, the last support position taking the parity-fixing sign.
+//      Each block's scaled dot product goes to an LDS partial slot.
+//   3. row sums of the partial slots in a fixed order (deterministic), stored to y.
+//
+// Rank unranking (both paths): exact arithmetic decoding in fp64.  With y = u * n the
+// value slot is the number of cumulative counts C_j <= floor(y) (SWAR compare of the
+// three thresholds packed in one dword) and y <- (y - C_k) * (n' / c_k), n' the values
+// left after the step, with n'/c from an LDS table.  The decision margins (>= n/(2Q),
+// Q <= 4.2e8 arrangements) exceed the accumulated rounding error by a factor > 1e5.
+
+#pragma once
+
+constexpr int kB1Threads = 512;
+constexpr int kB1Waves = kB1Threads / 64;
+constexpr int kB1TileMax = 2048;
+constexpr int kB1Bias = 12;        // value tables store 12 +- v (|v| <= 12)
+constexpr int kScratchStride = 32; // bytes of LDS scratch per lane (even path)
+
+struct B1Layout {
+  // byte offsets inside the dynamic LDS segment
+  uint32_t ftab;     // double F[25][32]: F[n][c] = n / c   (must stay at offset 0)
+  uint32_t cls;      // LlvqClassHot[ncls]
+  uint32_t gains;    // float[256]
+  uint32_t bucket;   // uint8[nbuckets]
+  uint32_t xs;       // x, kb*24 elements (fp32 or bf16), zero padded
+  uint32_t xsum;     // float[kb]: sum of the 24 x values of each block column
+  uint32_t queue;    // uint32[T_max]
+  uint32_t part;     // float[T_max]
+  uint32_t scratch;  // uint8[kB1Threads * kScratchStride]
+  uint32_t ctr;      // int[4]
+  uint32_t total;
+};
+
+__host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
+
+__host__ __device__ inline B1Layout b1_layout(int ncls, int nbuckets, int kb, int tmax, bool xf32) {
+  B1Layout L;
+  uint32_t o = 0;
+  L.ftab = o;    o = align16(o + 25u * 32u * 8u);
+  L.cls = o;     o = align16(o + (uint32_t)ncls * (uint32_t)sizeof(LlvqClassHot));
+  L.gains = o;   o = align16(o + 256u * 4u);
+  L.bucket = o;  o = align16(o + (uint32_t)nbuckets);
+  L.xs = o;      o = align16(o + (uint32_t)kb * 24u * (xf32 ? 4u : 2u));
+  L.xsum = o;    o = align16(o + (uint32_t)kb * 4u);
+  L.queue = o;   o = align16(o + (uint32_t)tmax * 4u);
+  L.part = o;    o = align16(o + (uint32_t)tmax * 4u);
+  L.scratch = o; o = align16(o + (uint32_t)kB1Threads * kScratchStride);
+  L.ctr = o;     o = align16(o + 16u);
+  L.total = o;
+  return L;
+}
+
+struct B1Args {
+  int rows_per_tile;
+  int tile_blocks_max;
+  int nbuckets;
+  B1Layout L;
+};
+
+// Full-rate 24-bit multiply-add and bit count with accumulator (the compiler otherwise
+// picks a quarter-rate 64-bit multiply-add, and does not fold the addend into v_bcnt).
+__device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+  return d;
+}
+
+__device__ __forceinline__ uint32_t bcnt_add(uint32_t a, uint32_t c) {
+  uint32_t d;
+  asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(d) : "v"(a), "s"(c));
+  return d;
+}
+
+// SWAR value-slot choice: number of thresholds C_j <= f (j = 1..3), as 0/1 bytes.
+__device__ __forceinline__ uint32_t swar_ge(uint32_t f, uint32_t nc) {
+  const uint32_t t = mad_u24(f, 0x010101u, nc);
+  return (t >> 7) & 0x010101u;
+}
+
+template <bool XF32>
+__device__ __forceinline__ void load_x24(const uint8_t* smem, const B1Layout& L, uint32_t blk, float xv[24]) {
+  if (XF32) {
+    const float4* p = reinterpret_cast<const float4*>(smem + L.xs + blk * 96u);
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      const float4 v = p[q];
+      xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(smem + L.xs + blk * 48u);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const uint4 v = p[q];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        xv[8 * q + 2 * h] = __uint_as_float(w[h] << 16);
+        xv[8 * q + 2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
+      }
+    }
+  }
+}
+
+// Common per-block setup from the class record: J / A split, codeword, initial y.
+struct BlockStart {
+  uint32_t c;   // codeword
+  uint32_t s;   // sign bits
+  double y;     // y_0 = (R + 1/2) * n0 / P
+};
+
+__device__ __forceinline__ BlockStart block_start(double Id, const LlvqClassHot& h) {
+  BlockStart bs;
+  const double Jd = Id - h.start;
+  const uint32_t q = (uint32_t)__builtin_fma(Jd, h.inv_a, 0x1p-13);    // floor(J / A), exact
+  const uint32_t r = (uint32_t)__builtin_fma(-(double)q, h.a, Jd);      // J - q A, exact
+  const uint32_t B = h.meta & 31u;
+  bs.s = q & ((1u << B) - 1u);
+  const uint32_t R = q >> B;
+  bs.c = dev_tables::kGolayTable[h.toff + r];
+  bs.y = __builtin_fma((double)R, h.y0s, 0.5 * h.y0s);
+  return bs;
+}
+
+// Odd coset: returns sum_p (12 + v_p) * x_p.
+template <bool XF32>
+__device__ __forceinline__ float dot_odd(const uint8_t* smem, const B1Layout& L, const LlvqClassHot& h,
+                                         const BlockStart& bs, uint32_t blk) {
+  const double* F = reinterpret_cast<const double*>(smem + L.ftab);
+  float xv[24];
+  load_x24<XF32>(smem, L, blk, xv);
+  double y = bs.y;
+  uint32_t nc = h.nc0, cnt = h.cnt0;
+  const uint32_t notc = ~bs.c;
+  float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 24; ++p) {
+    uint32_t kb;
+    if (p < 23) {
+      const uint32_t f = (uint32_t)y;
+      const uint32_t g = swar_ge(f, nc);
+      kb = bcnt_add(g, 0x0c0c0c00u);
+      const uint32_t ck = __builtin_amdgcn_perm(0u, cnt, kb);
+      const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
+      const double fac = F[(23 - p) * 32 + ck];
+      y = (y - (double)Ck) * fac;
+      cnt -= ((g << 8) | 1u) - g;
+      nc += g ^ 0x010101u;
+    } else {
+      // one value left: the slot whose count is nonzero
+      kb = ((uint32_t)__builtin_ctz(cnt) >> 3) + 0x0c0c0c00u;
+    }
+    const uint32_t sel = kb + (((notc >> p) & 1u) << 2);
+    const uint32_t bv = __builtin_amdgcn_perm(h.sv0hi, h.sv0lo, sel);
+    if (p & 1)
+      acc1 = __builtin_fmaf((float)(bv & 0xffu), xv[p], acc1);
+    else
+      acc0 = __builtin_fmaf((float)(bv & 0xffu), xv[p], acc0);
+  }
+  return acc0 + acc1;
+}
+
+// Even coset: returns sum_p (12 + v_p) * x_p.
+template <bool XF32>
+__device__ __forceinline__ float dot_even(uint8_t* smem, const B1Layout& L, const LlvqClassHot& h,
+                                          const BlockStart& bs, uint32_t blk, uint32_t lane_scratch) {
+  const uint32_t w = (h.meta >> 8) & 31u;
+  const uint32_t pi = (h.meta >> 16) & 1u;
+  const bool two = w != 0u && w != 24u;
+  const uint32_t n0 = w ? w : 24u;
+  // last support step takes the sign fixing the parity of negatives on the support;
+  // the support's other w-1 signs are bits 0..w-2 of s (all support values are nonzero)
+  const uint32_t negq = w ? (((uint32_t)__builtin_popcount(bs.s & ((1u << (w - 1u)) - 1u)) & 1u) ^ pi) : 0u;
+  double y = bs.y;
+  uint32_t nc = h.nc0, cnt = h.cnt0, svlo = h.sv0lo, svhi = h.sv0hi;
+  uint32_t nz = (h.meta >> 20) & 15u;
+  uint32_t m = w ? bs.c : 0xffffffu;
+  uint32_t s = bs.s;
+  uint32_t nb = (n0 - 1u) * 256u;   // byte offset of F[n'][0] for the values left after the step
+  uint8_t* scr = smem + lane_scratch;
+#pragma unroll
+  for (int i = 0; i < 24; ++i) {
+    if (i == 8 || i == 12 || i == 16) {
+      const bool sw = two && (w == (uint32_t)i);
+      nc = sw ? h.nc1 : nc;
+      cnt = sw ? h.cnt1 : cnt;
+      svlo = sw ? h.sv1lo : svlo;
+      svhi = sw ? h.sv1hi : svhi;
+      nz = sw ? ((h.meta >> 24) & 15u) : nz;
+      m = sw ? (~bs.c & 0xffffffu) : m;
+    }
+    const uint32_t f = (uint32_t)y;
+    const uint32_t g = swar_ge(f, nc);
+    const uint32_t kb = bcnt_add(g, 0x0c0c0c00u);
+    const uint32_t ck = __builtin_amdgcn_perm(0u, cnt, kb);
+    const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
+    if (i < 23) {
+      const double fac = *reinterpret_cast<const double*>(smem + L.ftab + nb + (ck << 3));
+      y = (y - (double)Ck) * fac;
+      cnt -= ((g << 8) | 1u) - g;
+      nc += g ^ 0x010101u;
+      // the last support step (i = w - 1) hands over to the complement: n' = 24 - w
+      if (i == 6 || i == 10 || i == 14)
+        nb = (two && w == (uint32_t)(i + 2)) ? (24u - w) * 256u : nb - 256u;
+      else
+        nb -= 256u;
+    }
+    // sign: nonzero positions consume bits of s in decode order; the last support
+    // step takes the parity-fixing sign and consumes no bit
+    uint32_t free_ = (nz >> (kb & 31u)) & 1u;
+    uint32_t neg = s & free_;
+    if (i == 7 || i == 11 || i == 15 || i == 23) {
+      const bool isq = w == (uint32_t)(i + 1);
+      neg = isq ? negq : neg;
+      free_ = isq ? 0u : free_;
+    }
+    s >>= free_;
+    const uint32_t bv = __builtin_amdgcn_perm(svhi, svlo, kb + (neg << 2));
+    const uint32_t pos = (uint32_t)__builtin_ctz(m);
+    m &= m - 1u;
+    scr[pos] = (uint8_t)bv;
+  }
+  float xv[24];
+  load_x24<XF32>(smem, L, blk, xv);
+  const uint4 r0 = *reinterpret_cast<const uint4*>(scr);
+  const uint2 r1 = *reinterpret_cast<const uint2*>(scr + 16);
+  const uint32_t wv[6] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y};
+  float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 24; ++p) {
+    const float v = (float)((wv[p >> 2] >> (8 * (p & 3))) & 0xffu);
+    if (p & 1)
+      acc1 = __builtin_fmaf(v, xv[p], acc1);
+    else
+      acc0 = __builtin_fmaf(v, xv[p], acc0);
+  }
+  return acc0 + acc1;
+}
+
+template <bool XF32>
+__global__ __launch_bounds__(kB1Threads) void k_gemv_b1(KDesc d, B1Args a, const uint8_t* __restrict__ packed,
+                                                         const __half* __restrict__ scales, const void* __restrict__ xv,
+                                                         float* __restrict__ y, int32_t* err) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const B1Layout& L = a.L;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kb = d.kb;
+  const int ncls = d.ncls;
+
+  // ---- prologue: tables and activations into LDS
+  {
+    double* F = reinterpret_cast<double*>(smem + L.ftab);
+    for (int i = tid; i < 25 * 32; i += kB1Threads) {
+      const int n = i >> 5, c = i & 31;
+      F[i] = (c >= 1 && c <= 24) ? (double)n / (double)c : 0.0;
+    }
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(dev_tables::kClassHot);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(smem + L.cls);
+    const int nw = ncls * (int)(sizeof(LlvqClassHot) / 4);
+    for (int i = tid; i < nw; i += kB1Threads) dst[i] = src[i];
+    float* G = reinterpret_cast<float*>(smem + L.gains);
+    if (d.mode == LLVQ_MODE_SHAPEGAIN)
+      for (int i = tid; i < (1 << d.gain_bits); i += kB1Threads) G[i] = __half2float(scales[i]);
+    uint8_t* bk = smem + L.bucket;
+    for (int i = tid; i < a.nbuckets; i += kB1Threads) bk[i] = dev_tables::kBucketTable[d.max_shell][i];
+    const int ncol = kb * 24;
+    if (XF32) {
+      float* xs = reinterpret_cast<float*>(smem + L.xs);
+      const float* xg = reinterpret_cast<const float*>(xv);
+      for (int i = tid; i < ncol; i += kB1Threads) xs[i] = i < d.cols ? xg[i] : 0.0f;
+    } else {
+      uint16_t* xs = reinterpret_cast<uint16_t*>(smem + L.xs);
+      const uint16_t* xg = reinterpret_cast<const uint16_t*>(xv);
+      for (int i = tid; i < ncol; i += kB1Threads) xs[i] = i < d.cols ? xg[i] : (uint16_t)0;
+    }
+  }
+  __syncthreads();
+  {
+    float* xsum = reinterpret_cast<float*>(smem + L.xsum);
+    for (int b = tid; b < kb; b += kB1Threads) {
+      float xx[24];
+      load_x24<XF32>(smem, L, (uint32_t)b, xx);
+      float s0 = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 24; ++p) s0 += xx[p];
+      xsum[b] = s0;
+    }
+  }
+  const LlvqClassHot* cls = reinterpret_cast<const LlvqClassHot*>(smem + L.cls);
+  const float* G = reinterpret_cast<const float*>(smem + L.gains);
+  const float* xsum = reinterpret_cast<const float*>(smem + L.xsum);
+  const uint8_t* bk = smem + L.bucket;
+  uint32_t* queue = reinterpret_cast<uint32_t*>(smem + L.queue);
+  float* part = reinterpret_cast<float*>(smem + L.part);
+  int* ctr = reinterpret_cast<int*>(smem + L.ctr);
+  const uint32_t lane_scratch = L.scratch + (uint32_t)tid * kScratchStride;
+  const float inv_kb = 1.0f / (float)kb;
+  const int ntiles = (d.rows + a.rows_per_tile - 1) / a.rows_per_tile;
+
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int row0 = tile * a.rows_per_tile;
+    const int nrows = min(a.rows_per_tile, d.rows - row0);
+    const int T = nrows * kb;
+    if (tid == 0) { ctr[0] = 0; ctr[1] = 0; }
+    __syncthreads();
+
+    // ---- 1. classify
+    for (int base = 0; base < T; base += kB1Threads) {
+      const int f = base + tid;
+      bool valid = false, odd = false;
+      uint32_t entry = 0;
+      if (f < T) {
+        const uint32_t rl = (uint32_t)(((float)f + 0.5f) * inv_kb);
+        const uint32_t b = (uint32_t)f - rl * (uint32_t)kb;
+        const uint64_t j = (uint64_t)(row0 + (int)rl) * (uint64_t)kb + b;
+        const uint64_t I = read_field(packed, j, d.field_bits) & d.shape_mask;
+        if (I < d.index_count) {
+          valid = true;
+          const double Id = (double)I;
+          uint32_t k = bk[(uint32_t)(I >> d.bshift)];
+          while ((int)k + 1 < ncls && Id >= cls[k + 1].start) ++k;
+          odd = ((cls[k].meta >> 17) & 1u) != 0u;
+          entry = (uint32_t)f | (k << 16);
+        } else {
+          part[f] = 0.0f;
+          if (err) atomicAdd(err, 1);
+        }
+      }
+      const uint64_t bo = __ballot(valid && odd);
+      const uint64_t be = __ballot(valid && !odd);
+      int baseo = 0, basee = 0;
+      if (lane == 0) {
+        baseo = atomicAdd(&ctr[0], __popcll(bo));
+        basee = atomicAdd(&ctr[1], __popcll(be));
+      }
+      baseo = __shfl(baseo, 0, 64);
+      basee = __shfl(basee, 0, 64);
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      if (valid && odd) queue[baseo + __popcll(bo & below)] = entry;
+      if (valid && !odd) queue[T - 1 - (basee + __popcll(be & below))] = entry;
+    }
+    __syncthreads();
+    const int nodd = ctr[0];
+    const int neven = ctr[1];
+
+    // ---- 2. decode + dot (odd queue [0, nodd), even queue [T - neven, T))
+    for (int pass = 0; pass < 2; ++pass) {
+      const int qbeg = pass == 0 ? 0 : T - neven;
+      const int qn = pass == 0 ? nodd : neven;
+      for (int c0 = wave * 64; c0 < qn; c0 += kB1Threads) {
+        const int e = c0 + lane;
+        if (e >= qn) continue;
+        const uint32_t entry = queue[qbeg + e];
+        const uint32_t f = entry & 0xffffu;
+        const uint32_t k = entry >> 16;
+        const uint32_t rl = (uint32_t)(((float)f + 0.5f) * inv_kb);
+        const uint32_t b = f - rl * (uint32_t)kb;
+        const uint64_t j = (uint64_t)(row0 + (int)rl) * (uint64_t)kb + b;
+        const uint64_t fld = read_field(packed, j, d.field_bits);
+        const double Id = (double)(fld & d.shape_mask);
+        const LlvqClassHot h = cls[k];
+        const BlockStart bs = block_start(Id, h);
+        const float raw = pass == 0 ? dot_odd<XF32>(smem, L, h, bs, b)
+                                    : dot_even<XF32>(smem, L, h, bs, b, lane_scratch);
+        const float dotv = __builtin_fmaf(-(float)kB1Bias, xsum[b], raw);
+        float scale = 1.0f;
+        if (d.mode == LLVQ_MODE_SHAPEGAIN) scale = G[(uint32_t)(fld >> d.shape_bits)] * h.invnorm;
+        part[f] = scale * dotv;
+      }
+    }
+    __syncthreads();
+
+    // ---- 3. row sums (fixed order)
+    for (int rl = wave; rl < nrows; rl += kB1Waves) {
+      float acc = 0.0f;
+      for (int b = lane; b < kb; b += 64) acc += part[rl * kb + b];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      if (lane == 0) {
+        const int r = row0 + rl;
+        const float rs = d.mode == LLVQ_MODE_SHAPEGAIN ? 1.0f : __half2float(scales[r]);
+        y[r] = acc * rs;
+      }
+    }
+    __syncthreads();
+  }
+}

@@ -23,3 +23,32 @@ struct LlvqClassRec {
   uint8_t d_t;       // distinct complement values
   uint8_t pad;
 };
+
+// Hot-path class record kept in LDS by the fused GEMV (80 bytes, five 16-byte rows).
+// The absolute values of a class are unranked in at most two parts.  Odd classes and
+// even classes with w = 0 or w = 24 have one part of 24 values; other even classes have
+// the support part (w values, placed on the codeword's positions) followed by the
+// complement part (24 - w values).  Per part X (0 = first, 1 = second):
+//   ncX  SWAR thresholds: byte j-1 (j = 1..3) = 0x80 - C_j, C_j = sum of the counts of
+//        value slots below j; unused slots have count 0.
+//   cntX counts of the part's value slots 0..3, one per byte.
+//   svX  8-byte table read with v_perm (svXhi:svXlo), entries biased by +12:
+//        even classes: bytes 0-3 = 12 + |v_j|, bytes 4-7 = 12 - |v_j| (negative sign);
+//        odd classes:  bytes 0-3 = 12 + b(v_j) for positions on the codeword,
+//                      bytes 4-7 = 12 - b(v_j) off it, b(v) = v if v = 1 mod 4 else -v.
+// meta: B (bits 0-4) | w (bits 8-12) | pi (bit 16) | parity (bit 17) |
+//       nonzero mask of part-0 slots (bits 20-23) | nonzero mask of part-1 slots (24-27).
+struct LlvqClassHot {
+  double start;      // first global index (exact in fp64)
+  double y0s;        // n0 / P: length of the first part over the number of arrangements
+  double inv_a;      // 1 / A
+  double a;          // A
+  uint32_t toff;     // Golay table position of codeword r = 0
+  uint32_t meta;
+  uint32_t nc0, cnt0;
+  uint32_t nc1, cnt1;
+  uint32_t sv0lo, sv0hi;
+  uint32_t sv1lo, sv1hi;
+  float invnorm;     // fp32 1/(4 sqrt m), computed in fp64 and rounded once
+  uint32_t m;        // shell
+};
