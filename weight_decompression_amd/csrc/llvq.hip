@@ -548,14 +548,15 @@ constexpr uint32_t kLdsBudget = 160u * 1024u / 2u;   // two workgroups per CU
 int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype,
                    float* y, int32_t* err, hipStream_t s) {
   if (k.kb > kB1TileMax) return LLVQ_EUNSUPPORTED;
-  const int rpt = kB1TileMax / k.kb;
+  int rpt = kB1TileMax / k.kb;
+  if (rpt > k.rows) rpt = k.rows;
   const int tmax = rpt * k.kb;
   const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
   B1Args a;
   a.rows_per_tile = rpt;
   a.tile_blocks_max = tmax;
   a.nbuckets = nbuckets;
-  a.L = b1_layout(k.ncls, nbuckets, k.kb, tmax, x_dtype == LLVQ_X_F32);
+  a.L = b1_layout(k.ncls, 1 << k.gain_bits, nbuckets, k.kb, tmax, x_dtype == LLVQ_X_F32);
   if (a.L.total > kLdsBudget) return LLVQ_EUNSUPPORTED;
   const int ntiles = (k.rows + rpt - 1) / rpt;
   int grid = 512;

@@ -14,54 +14,61 @@
 //        codeword bit and the value mod 4, folded into one byte-table lookup (v_perm);
 //      - even path: support values then complement values in decode order, placed on
 //        the codeword's (resp. complement's) positions through a per-lane LDS scratch
-//        row; the sign bits of s are consumed on nonzero positions in ascending order
-//        per part, the last support position taking the parity-fixing sign.
+//        row; sign bits of s are consumed in decode order on nonzero positions, the
+//        last support position taking the parity-fixing sign.
 //      Each block's scaled dot product goes to an LDS partial slot.
 //   3. row sums of the partial slots in a fixed order (deterministic), stored to y.
 //
 // Rank unranking (both paths): exact arithmetic decoding in fp64.  With y = u * n the
 // value slot is the number of cumulative counts C_j <= floor(y) (SWAR compare of the
 // three thresholds packed in one dword) and y <- (y - C_k) * (n' / c_k), n' the values
-// left after the step, with n'/c from an LDS table.  The decision margins (>= n/(2Q),
+// left after the step, n'/c from an LDS table.  The decision margins (>= n/(2Q),
 // Q <= 4.2e8 arrangements) exceed the accumulated rounding error by a factor > 1e5.
+// The last 6 values come from a table of all 4^6 slot sequences grouped by composition
+// in lexicographic order: with counts c (sum 6) and y in [0, 6), the rank inside the
+// group is floor(y * Q(c) / 6).
 
 #pragma once
 
 constexpr int kB1Threads = 512;
 constexpr int kB1Waves = kB1Threads / 64;
 constexpr int kB1TileMax = 2048;
-constexpr int kB1Bias = 12;        // value tables store 12 +- v (|v| <= 12)
-constexpr int kScratchStride = 32; // bytes of LDS scratch per lane (even path)
+constexpr int kB1Bias = 12;         // value tables store 12 +- v (|v| <= 12)
+constexpr int kTail = 6;            // values resolved by the tail table
+constexpr int kSteps = 24 - kTail;  // values resolved step by step
+constexpr int kFStride = 25;        // F[n][c] row length (c = 0..24)
 
 struct B1Layout {
   // byte offsets inside the dynamic LDS segment
-  uint32_t ftab;     // double F[25][32]: F[n][c] = n / c   (must stay at offset 0)
+  uint32_t ftab;     // double F[25][25]: F[n][c] = n / c   (must stay at offset 0)
   uint32_t cls;      // LlvqClassHot[ncls]
-  uint32_t gains;    // float[256]
+  uint32_t gains;    // float[2^gain_bits]
   uint32_t bucket;   // uint8[nbuckets]
+  uint32_t tail;     // uint16[4096]
+  uint32_t tcomp;    // LlvqTailComp[343]
   uint32_t xs;       // x, kb*24 elements (fp32 or bf16), zero padded
   uint32_t xsum;     // float[kb]: sum of the 24 x values of each block column
-  uint32_t queue;    // uint32[T_max]
-  uint32_t part;     // float[T_max]
-  uint32_t scratch;  // uint8[kB1Threads * kScratchStride]
+  uint32_t queue;    // uint64[T]: I | f << 44 | class << 56
+  uint32_t part;     // float[T]: block scale, then the block's scaled dot product
   uint32_t ctr;      // int[4]
   uint32_t total;
 };
 
 __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
 
-__host__ __device__ inline B1Layout b1_layout(int ncls, int nbuckets, int kb, int tmax, bool xf32) {
+__host__ __device__ inline B1Layout b1_layout(int ncls, int ngains, int nbuckets, int kb, int tmax, bool xf32) {
   B1Layout L;
   uint32_t o = 0;
-  L.ftab = o;    o = align16(o + 25u * 32u * 8u);
+  L.ftab = o;    o = align16(o + 25u * kFStride * 8u);
   L.cls = o;     o = align16(o + (uint32_t)ncls * (uint32_t)sizeof(LlvqClassHot));
-  L.gains = o;   o = align16(o + 256u * 4u);
+  L.gains = o;   o = align16(o + (uint32_t)ngains * 4u);
   L.bucket = o;  o = align16(o + (uint32_t)nbuckets);
+  L.tail = o;    o = align16(o + 4096u * 2u);
+  L.tcomp = o;   o = align16(o + 343u * (uint32_t)sizeof(LlvqTailComp));
   L.xs = o;      o = align16(o + (uint32_t)kb * 24u * (xf32 ? 4u : 2u));
   L.xsum = o;    o = align16(o + (uint32_t)kb * 4u);
-  L.queue = o;   o = align16(o + (uint32_t)tmax * 4u);
+  L.queue = o;   o = align16(o + (uint32_t)tmax * 8u);
   L.part = o;    o = align16(o + (uint32_t)tmax * 4u);
-  L.scratch = o; o = align16(o + (uint32_t)kB1Threads * kScratchStride);
   L.ctr = o;     o = align16(o + 16u);
   L.total = o;
   return L;
@@ -138,6 +145,22 @@ __device__ __forceinline__ BlockStart block_start(double Id, const LlvqClassHot&
   return bs;
 }
 
+// Slot codes of the last 6 values (2 bits each, first of the six in the low bits), from
+// the counts left (sum 6) and y in [0, 6).
+__device__ __forceinline__ uint32_t tail_codes(const uint8_t* smem, const B1Layout& L, uint32_t cnt, double y) {
+  const uint32_t ci = __builtin_amdgcn_udot4(cnt, 0x00310701u, 0u, false);   // c0 + 7 c1 + 49 c2
+  const LlvqTailComp tc = reinterpret_cast<const LlvqTailComp*>(smem + L.tcomp)[ci];
+  const uint32_t r = (uint32_t)((float)y * tc.q_over_6);
+  return reinterpret_cast<const uint16_t*>(smem + L.tail)[tc.offset + r];
+}
+
+// bf16/fp32 activation at column col (LDS)
+template <bool XF32>
+__device__ __forceinline__ float x_at(const uint8_t* smem, const B1Layout& L, uint32_t col) {
+  if (XF32) return reinterpret_cast<const float*>(smem + L.xs)[col];
+  return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(smem + L.xs)[col] << 16);
+}
+
 // Odd coset: returns sum_p (12 + v_p) * x_p.
 template <bool XF32>
 __device__ __forceinline__ float dot_odd(const uint8_t* smem, const B1Layout& L, const LlvqClassHot& h,
@@ -150,23 +173,28 @@ __device__ __forceinline__ float dot_odd(const uint8_t* smem, const B1Layout& L,
   const uint32_t notc = ~bs.c;
   float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
-  for (int p = 0; p < 24; ++p) {
-    uint32_t kb;
-    if (p < 23) {
-      const uint32_t f = (uint32_t)y;
-      const uint32_t g = swar_ge(f, nc);
-      kb = bcnt_add(g, 0x0c0c0c00u);
-      const uint32_t ck = __builtin_amdgcn_perm(0u, cnt, kb);
-      const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
-      const double fac = F[(23 - p) * 32 + ck];
-      y = (y - (double)Ck) * fac;
-      cnt -= ((g << 8) | 1u) - g;
-      nc += g ^ 0x010101u;
-    } else {
-      // one value left: the slot whose count is nonzero
-      kb = ((uint32_t)__builtin_ctz(cnt) >> 3) + 0x0c0c0c00u;
-    }
+  for (int p = 0; p < kSteps; ++p) {
+    const uint32_t f = (uint32_t)y;
+    const uint32_t g = swar_ge(f, nc);
+    const uint32_t kb = bcnt_add(g, 0x0c0c0c00u);
+    const uint32_t ck = __builtin_amdgcn_perm(0u, cnt, kb);
+    const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
+    const double fac = F[(23 - p) * kFStride + ck];
+    y = (y - (double)Ck) * fac;
+    cnt -= ((g << 8) | 1u) - g;
+    nc += g ^ 0x010101u;
     const uint32_t sel = kb + (((notc >> p) & 1u) << 2);
+    const uint32_t bv = __builtin_amdgcn_perm(h.sv0hi, h.sv0lo, sel);
+    if (p & 1)
+      acc1 = __builtin_fmaf((float)(bv & 0xffu), xv[p], acc1);
+    else
+      acc0 = __builtin_fmaf((float)(bv & 0xffu), xv[p], acc0);
+  }
+  const uint32_t codes = tail_codes(smem, L, cnt, y);
+#pragma unroll
+  for (int p = kSteps; p < 24; ++p) {
+    const uint32_t k = (codes >> (2 * (p - kSteps))) & 3u;
+    const uint32_t sel = (k | 0x0c0c0c00u) + (((notc >> p) & 1u) << 2);
     const uint32_t bv = __builtin_amdgcn_perm(h.sv0hi, h.sv0lo, sel);
     if (p & 1)
       acc1 = __builtin_fmaf((float)(bv & 0xffu), xv[p], acc1);
@@ -176,10 +204,11 @@ __device__ __forceinline__ float dot_odd(const uint8_t* smem, const B1Layout& L,
   return acc0 + acc1;
 }
 
-// Even coset: returns sum_p (12 + v_p) * x_p.
+// Even coset: returns sum_p (12 + v_p) * x_p, values visited in decode order and their
+// activations gathered from LDS by position.
 template <bool XF32>
-__device__ __forceinline__ float dot_even(uint8_t* smem, const B1Layout& L, const LlvqClassHot& h,
-                                          const BlockStart& bs, uint32_t blk, uint32_t lane_scratch) {
+__device__ __forceinline__ float dot_even(const uint8_t* smem, const B1Layout& L, const LlvqClassHot& h,
+                                          const BlockStart& bs, uint32_t blk) {
   const uint32_t w = (h.meta >> 8) & 31u;
   const uint32_t pi = (h.meta >> 16) & 1u;
   const bool two = w != 0u && w != 24u;
@@ -192,8 +221,10 @@ __device__ __forceinline__ float dot_even(uint8_t* smem, const B1Layout& L, cons
   uint32_t nz = (h.meta >> 20) & 15u;
   uint32_t m = w ? bs.c : 0xffffffu;
   uint32_t s = bs.s;
-  uint32_t nb = (n0 - 1u) * 256u;   // byte offset of F[n'][0] for the values left after the step
-  uint8_t* scr = smem + lane_scratch;
+  uint32_t nb = (n0 - 1u) * (kFStride * 8u);   // byte offset of F[n'][0], n' = values left after the step
+  const uint32_t col0 = blk * 24u;
+  uint32_t codes = 0;
+  float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
   for (int i = 0; i < 24; ++i) {
     if (i == 8 || i == 12 || i == 16) {
@@ -205,21 +236,25 @@ __device__ __forceinline__ float dot_even(uint8_t* smem, const B1Layout& L, cons
       nz = sw ? ((h.meta >> 24) & 15u) : nz;
       m = sw ? (~bs.c & 0xffffffu) : m;
     }
-    const uint32_t f = (uint32_t)y;
-    const uint32_t g = swar_ge(f, nc);
-    const uint32_t kb = bcnt_add(g, 0x0c0c0c00u);
-    const uint32_t ck = __builtin_amdgcn_perm(0u, cnt, kb);
-    const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
-    if (i < 23) {
+    uint32_t kb;
+    if (i < kSteps) {
+      const uint32_t f = (uint32_t)y;
+      const uint32_t g = swar_ge(f, nc);
+      kb = bcnt_add(g, 0x0c0c0c00u);
+      const uint32_t ck = __builtin_amdgcn_perm(0u, cnt, kb);
+      const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
       const double fac = *reinterpret_cast<const double*>(smem + L.ftab + nb + (ck << 3));
       y = (y - (double)Ck) * fac;
       cnt -= ((g << 8) | 1u) - g;
       nc += g ^ 0x010101u;
       // the last support step (i = w - 1) hands over to the complement: n' = 24 - w
       if (i == 6 || i == 10 || i == 14)
-        nb = (two && w == (uint32_t)(i + 2)) ? (24u - w) * 256u : nb - 256u;
+        nb = (two && w == (uint32_t)(i + 2)) ? (24u - w) * (kFStride * 8u) : nb - kFStride * 8u;
       else
-        nb -= 256u;
+        nb -= kFStride * 8u;
+      if (i == kSteps - 1) codes = tail_codes(smem, L, cnt, y);
+    } else {
+      kb = ((codes >> (2 * (i - kSteps))) & 3u) | 0x0c0c0c00u;
     }
     // sign: nonzero positions consume bits of s in decode order; the last support
     // step takes the parity-fixing sign and consumes no bit
@@ -234,23 +269,23 @@ __device__ __forceinline__ float dot_even(uint8_t* smem, const B1Layout& L, cons
     const uint32_t bv = __builtin_amdgcn_perm(svhi, svlo, kb + (neg << 2));
     const uint32_t pos = (uint32_t)__builtin_ctz(m);
     m &= m - 1u;
-    scr[pos] = (uint8_t)bv;
-  }
-  float xv[24];
-  load_x24<XF32>(smem, L, blk, xv);
-  const uint4 r0 = *reinterpret_cast<const uint4*>(scr);
-  const uint2 r1 = *reinterpret_cast<const uint2*>(scr + 16);
-  const uint32_t wv[6] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y};
-  float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-  for (int p = 0; p < 24; ++p) {
-    const float v = (float)((wv[p >> 2] >> (8 * (p & 3))) & 0xffu);
-    if (p & 1)
-      acc1 = __builtin_fmaf(v, xv[p], acc1);
+    const float xp = x_at<XF32>(smem, L, col0 + pos);
+    if (i & 1)
+      acc1 = __builtin_fmaf((float)(bv & 0xffu), xp, acc1);
     else
-      acc0 = __builtin_fmaf(v, xv[p], acc0);
+      acc0 = __builtin_fmaf((float)(bv & 0xffu), xp, acc0);
   }
   return acc0 + acc1;
+}
+
+// LDS copy of n 32-bit words with 16-byte vector moves (n a multiple of 4 where the
+// source and destination are 16-byte aligned; the tail is copied word by word).
+__device__ __forceinline__ void lds_copy_words(uint32_t* dst, const uint32_t* src, int n, int tid) {
+  const int n4 = n >> 2;
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  for (int i = tid; i < n4; i += kB1Threads) d4[i] = s4[i];
+  for (int i = (n4 << 2) + tid; i < n; i += kB1Threads) dst[i] = src[i];
 }
 
 template <bool XF32>
@@ -261,35 +296,46 @@ __global__ __launch_bounds__(kB1Threads) void k_gemv_b1(KDesc d, B1Args a, const
   const B1Layout& L = a.L;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
   const int kb = d.kb;
   const int ncls = d.ncls;
+  const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
 
   // ---- prologue: tables and activations into LDS
   {
     double* F = reinterpret_cast<double*>(smem + L.ftab);
-    for (int i = tid; i < 25 * 32; i += kB1Threads) {
-      const int n = i >> 5, c = i & 31;
-      F[i] = (c >= 1 && c <= 24) ? (double)n / (double)c : 0.0;
+    for (int i = tid; i < 25 * kFStride; i += kB1Threads) {
+      const int n = i / kFStride, c = i - n * kFStride;
+      F[i] = c >= 1 ? (double)n / (double)c : 0.0;
     }
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(dev_tables::kClassHot);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(smem + L.cls);
-    const int nw = ncls * (int)(sizeof(LlvqClassHot) / 4);
-    for (int i = tid; i < nw; i += kB1Threads) dst[i] = src[i];
+    lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.cls), reinterpret_cast<const uint32_t*>(dev_tables::kClassHot),
+                   ncls * (int)(sizeof(LlvqClassHot) / 4), tid);
+    lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.tail), reinterpret_cast<const uint32_t*>(dev_tables::kTail6),
+                   2048, tid);
+    lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.tcomp),
+                   reinterpret_cast<const uint32_t*>(dev_tables::kTailComp), 343 * 2, tid);
+    lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.bucket),
+                   reinterpret_cast<const uint32_t*>(dev_tables::kBucketTable[d.max_shell]), (a.nbuckets + 3) >> 2, tid);
     float* G = reinterpret_cast<float*>(smem + L.gains);
-    if (d.mode == LLVQ_MODE_SHAPEGAIN)
+    if (sg)
       for (int i = tid; i < (1 << d.gain_bits); i += kB1Threads) G[i] = __half2float(scales[i]);
-    uint8_t* bk = smem + L.bucket;
-    for (int i = tid; i < a.nbuckets; i += kB1Threads) bk[i] = dev_tables::kBucketTable[d.max_shell][i];
     const int ncol = kb * 24;
     if (XF32) {
       float* xs = reinterpret_cast<float*>(smem + L.xs);
       const float* xg = reinterpret_cast<const float*>(xv);
       for (int i = tid; i < ncol; i += kB1Threads) xs[i] = i < d.cols ? xg[i] : 0.0f;
     } else {
+      // pairs of bf16 as dwords when the row is dword aligned
       uint16_t* xs = reinterpret_cast<uint16_t*>(smem + L.xs);
       const uint16_t* xg = reinterpret_cast<const uint16_t*>(xv);
-      for (int i = tid; i < ncol; i += kB1Threads) xs[i] = i < d.cols ? xg[i] : (uint16_t)0;
+      if ((((uintptr_t)xg) & 3u) == 0u) {
+        const int full = d.cols >> 1;
+        const uint32_t* xg2 = reinterpret_cast<const uint32_t*>(xg);
+        uint32_t* xs2 = reinterpret_cast<uint32_t*>(xs);
+        for (int i = tid; i < ncol / 2; i += kB1Threads)
+          xs2[i] = i < full ? xg2[i] : ((i == full && (d.cols & 1)) ? (uint32_t)xg[d.cols - 1] : 0u);
+      } else {
+        for (int i = tid; i < ncol; i += kB1Threads) xs[i] = i < d.cols ? xg[i] : (uint16_t)0;
+      }
     }
   }
   __syncthreads();
@@ -308,37 +354,45 @@ __global__ __launch_bounds__(kB1Threads) void k_gemv_b1(KDesc d, B1Args a, const
   const float* G = reinterpret_cast<const float*>(smem + L.gains);
   const float* xsum = reinterpret_cast<const float*>(smem + L.xsum);
   const uint8_t* bk = smem + L.bucket;
-  uint32_t* queue = reinterpret_cast<uint32_t*>(smem + L.queue);
+  uint64_t* queue = reinterpret_cast<uint64_t*>(smem + L.queue);
   float* part = reinterpret_cast<float*>(smem + L.part);
   int* ctr = reinterpret_cast<int*>(smem + L.ctr);
-  const uint32_t lane_scratch = L.scratch + (uint32_t)tid * kScratchStride;
   const float inv_kb = 1.0f / (float)kb;
   const int ntiles = (d.rows + a.rows_per_tile - 1) / a.rows_per_tile;
+  constexpr int kCl = (kB1TileMax + kB1Threads - 1) / kB1Threads;   // classify blocks per thread
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int row0 = tile * a.rows_per_tile;
     const int nrows = min(a.rows_per_tile, d.rows - row0);
     const int T = nrows * kb;
-    if (tid == 0) { ctr[0] = 0; ctr[1] = 0; }
+    if (tid == 0) { ctr[0] = 0; ctr[1] = 0; ctr[2] = 0; }
     __syncthreads();
 
-    // ---- 1. classify
-    for (int base = 0; base < T; base += kB1Threads) {
-      const int f = base + tid;
+    // ---- 1. classify: all field loads first, then the class search and queueing
+    uint64_t fld[kCl];
+#pragma unroll
+    for (int t = 0; t < kCl; ++t) {
+      const int f = t * kB1Threads + tid;
+      fld[t] = 0;
+      if (f < T) fld[t] = read_field(packed, (uint64_t)row0 * (uint64_t)kb + (uint64_t)f, d.field_bits);
+    }
+#pragma unroll
+    for (int t = 0; t < kCl; ++t) {
+      const int f = t * kB1Threads + tid;
+      if (t * kB1Threads >= T) break;
       bool valid = false, odd = false;
-      uint32_t entry = 0;
+      uint64_t entry = 0;
       if (f < T) {
-        const uint32_t rl = (uint32_t)(((float)f + 0.5f) * inv_kb);
-        const uint32_t b = (uint32_t)f - rl * (uint32_t)kb;
-        const uint64_t j = (uint64_t)(row0 + (int)rl) * (uint64_t)kb + b;
-        const uint64_t I = read_field(packed, j, d.field_bits) & d.shape_mask;
+        const uint64_t I = fld[t] & d.shape_mask;
         if (I < d.index_count) {
           valid = true;
           const double Id = (double)I;
           uint32_t k = bk[(uint32_t)(I >> d.bshift)];
           while ((int)k + 1 < ncls && Id >= cls[k + 1].start) ++k;
-          odd = ((cls[k].meta >> 17) & 1u) != 0u;
-          entry = (uint32_t)f | (k << 16);
+          const LlvqClassHot& h = cls[k];
+          odd = ((h.meta >> 17) & 1u) != 0u;
+          entry = I | ((uint64_t)f << 44) | ((uint64_t)k << 56);
+          part[f] = sg ? G[(uint32_t)(fld[t] >> d.shape_bits)] * h.invnorm : 1.0f;
         } else {
           part[f] = 0.0f;
           if (err) atomicAdd(err, 1);
@@ -360,43 +414,39 @@ __global__ __launch_bounds__(kB1Threads) void k_gemv_b1(KDesc d, B1Args a, const
     __syncthreads();
     const int nodd = ctr[0];
     const int neven = ctr[1];
+    const int nco = (nodd + 63) >> 6;
+    const int nchunks = nco + ((neven + 63) >> 6);
 
-    // ---- 2. decode + dot (odd queue [0, nodd), even queue [T - neven, T))
-    for (int pass = 0; pass < 2; ++pass) {
-      const int qbeg = pass == 0 ? 0 : T - neven;
-      const int qn = pass == 0 ? nodd : neven;
-      for (int c0 = wave * 64; c0 < qn; c0 += kB1Threads) {
-        const int e = c0 + lane;
-        if (e >= qn) continue;
-        const uint32_t entry = queue[qbeg + e];
-        const uint32_t f = entry & 0xffffu;
-        const uint32_t k = entry >> 16;
-        const uint32_t rl = (uint32_t)(((float)f + 0.5f) * inv_kb);
-        const uint32_t b = f - rl * (uint32_t)kb;
-        const uint64_t j = (uint64_t)(row0 + (int)rl) * (uint64_t)kb + b;
-        const uint64_t fld = read_field(packed, j, d.field_bits);
-        const double Id = (double)(fld & d.shape_mask);
-        const LlvqClassHot h = cls[k];
-        const BlockStart bs = block_start(Id, h);
-        const float raw = pass == 0 ? dot_odd<XF32>(smem, L, h, bs, b)
-                                    : dot_even<XF32>(smem, L, h, bs, b, lane_scratch);
-        const float dotv = __builtin_fmaf(-(float)kB1Bias, xsum[b], raw);
-        float scale = 1.0f;
-        if (d.mode == LLVQ_MODE_SHAPEGAIN) scale = G[(uint32_t)(fld >> d.shape_bits)] * h.invnorm;
-        part[f] = scale * dotv;
-      }
+    // ---- 2. decode + dot: 64-block chunks handed out dynamically (odd chunks first)
+    for (;;) {
+      int c = 0;
+      if (lane == 0) c = atomicAdd(&ctr[2], 1);
+      c = __shfl(c, 0, 64);
+      if (c >= nchunks) break;
+      const bool odd = c < nco;
+      const int e = odd ? (c << 6) + lane : ((c - nco) << 6) + lane;
+      if (e >= (odd ? nodd : neven)) continue;
+      const uint64_t entry = queue[odd ? e : T - 1 - e];
+      const uint32_t f = (uint32_t)(entry >> 44) & 0xfffu;
+      const uint32_t k = (uint32_t)(entry >> 56);
+      const uint32_t rl = (uint32_t)(((float)f + 0.5f) * inv_kb);
+      const uint32_t b = f - rl * (uint32_t)kb;
+      const LlvqClassHot h = cls[k];
+      const BlockStart bs = block_start((double)(entry & 0xfffffffffffull), h);
+      const float raw = odd ? dot_odd<XF32>(smem, L, h, bs, b) : dot_even<XF32>(smem, L, h, bs, b);
+      part[f] *= __builtin_fmaf(-(float)kB1Bias, xsum[b], raw);
     }
     __syncthreads();
 
     // ---- 3. row sums (fixed order)
-    for (int rl = wave; rl < nrows; rl += kB1Waves) {
+    for (int rl = tid >> 6; rl < nrows; rl += kB1Waves) {
       float acc = 0.0f;
       for (int b = lane; b < kb; b += 64) acc += part[rl * kb + b];
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
       if (lane == 0) {
         const int r = row0 + rl;
-        const float rs = d.mode == LLVQ_MODE_SHAPEGAIN ? 1.0f : __half2float(scales[r]);
+        const float rs = sg ? 1.0f : __half2float(scales[r]);
         y[r] = acc * rs;
       }
     }

@@ -52,3 +52,9 @@ struct LlvqClassHot {
   float invnorm;     // fp32 1/(4 sqrt m), computed in fp64 and rounded once
   uint32_t m;        // shell
 };
+
+// Composition record of the 6-position tail table (see gen_tables.cpp).
+struct LlvqTailComp {
+  float q_over_6;    // arrangements of the composition / 6
+  uint32_t offset;   // first entry of the composition's group in the tail table
+};
