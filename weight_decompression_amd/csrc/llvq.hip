@@ -54,6 +54,7 @@ struct KDesc {
   int32_t max_shell, shape_bits, gain_bits, field_bits;
   uint64_t index_count;
   uint64_t shape_mask;
+  uint32_t shape_mask_lo, shape_mask_hi;
   int32_t ncls, bshift;
 };
 
@@ -465,6 +466,8 @@ int make_kdesc(const llvq_desc* d, KDesc* k) {
   k->field_bits = d->shape_bits + d->gain_bits;
   k->index_count = count;
   k->shape_mask = (1ull << d->shape_bits) - 1ull;
+  k->shape_mask_lo = (uint32_t)k->shape_mask;
+  k->shape_mask_hi = (uint32_t)(k->shape_mask >> 32);
   k->ncls = host_tables::kNumClassesUpTo[d->max_shell];
   k->bshift = host_tables::kBucketShift[d->max_shell];
   return LLVQ_OK;
@@ -548,6 +551,7 @@ constexpr uint32_t kLdsBudget = 160u * 1024u / 2u;   // two workgroups per CU
 int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype,
                    float* y, int32_t* err, hipStream_t s) {
   if (k.kb > kB1TileMax) return LLVQ_EUNSUPPORTED;
+  if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;   // 32-bit field index
   int rpt = kB1TileMax / k.kb;
   if (rpt > k.rows) rpt = k.rows;
   const int tmax = rpt * k.kb;

@@ -95,6 +95,29 @@ __device__ __forceinline__ uint32_t bcnt_add(uint32_t a, uint32_t c) {
   return d;
 }
 
+// Field j of the packed stream as (lo, hi) words, fields of f <= 64 bits.  48-bit fields
+// (the 2-bit format) start at byte 6j: two dword loads and a funnel shift.
+__device__ __forceinline__ void field_words(const uint8_t* __restrict__ packed, uint32_t j, int f,
+                                            uint32_t& lo, uint32_t& hi) {
+  if (f == 48) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(packed) + ((3u * j) >> 1);
+    const uint32_t w0 = w[0], w1 = w[1];
+    const uint32_t sh = (j & 1u) << 4;
+    lo = __builtin_amdgcn_alignbit(w1, w0, sh);
+    hi = (w1 >> sh) & 0xffffu;
+  } else {
+    const uint64_t v = read_field(packed, j, f);
+    lo = (uint32_t)v;
+    hi = (uint32_t)(v >> 32);
+  }
+}
+
+__device__ __forceinline__ uint32_t lshl_add(uint32_t a, uint32_t s, uint32_t b) {
+  uint32_t d;
+  asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "i"(s), "v"(b));
+  return d;
+}
+
 // SWAR value-slot choice: number of thresholds C_j <= f (j = 1..3), as 0/1 bytes.
 __device__ __forceinline__ uint32_t swar_ge(uint32_t f, uint32_t nc) {
   const uint32_t t = mad_u24(f, 0x010101u, nc);
@@ -183,7 +206,7 @@ __device__ __forceinline__ float dot_odd(const uint8_t* smem, const B1Layout& L,
     y = (y - (double)Ck) * fac;
     cnt -= ((g << 8) | 1u) - g;
     nc += g ^ 0x010101u;
-    const uint32_t sel = kb + (((notc >> p) & 1u) << 2);
+    const uint32_t sel = lshl_add(__builtin_amdgcn_ubfe(notc, p, 1), 2, kb);
     const uint32_t bv = __builtin_amdgcn_perm(h.sv0hi, h.sv0lo, sel);
     if (p & 1)
       acc1 = __builtin_fmaf((float)(bv & 0xffu), xv[p], acc1);
@@ -193,8 +216,8 @@ __device__ __forceinline__ float dot_odd(const uint8_t* smem, const B1Layout& L,
   const uint32_t codes = tail_codes(smem, L, cnt, y);
 #pragma unroll
   for (int p = kSteps; p < 24; ++p) {
-    const uint32_t k = (codes >> (2 * (p - kSteps))) & 3u;
-    const uint32_t sel = (k | 0x0c0c0c00u) + (((notc >> p) & 1u) << 2);
+    const uint32_t k = __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | 0x0c0c0c00u;
+    const uint32_t sel = lshl_add(__builtin_amdgcn_ubfe(notc, p, 1), 2, k);
     const uint32_t bv = __builtin_amdgcn_perm(h.sv0hi, h.sv0lo, sel);
     if (p & 1)
       acc1 = __builtin_fmaf((float)(bv & 0xffu), xv[p], acc1);
@@ -369,12 +392,13 @@ __global__ __launch_bounds__(kB1Threads) void k_gemv_b1(KDesc d, B1Args a, const
     __syncthreads();
 
     // ---- 1. classify: all field loads first, then the class search and queueing
-    uint64_t fld[kCl];
+    uint32_t flo[kCl], fhi[kCl];
 #pragma unroll
     for (int t = 0; t < kCl; ++t) {
       const int f = t * kB1Threads + tid;
-      fld[t] = 0;
-      if (f < T) fld[t] = read_field(packed, (uint64_t)row0 * (uint64_t)kb + (uint64_t)f, d.field_bits);
+      flo[t] = 0u;
+      fhi[t] = 0u;
+      if (f < T) field_words(packed, (uint32_t)(row0 * kb + f), d.field_bits, flo[t], fhi[t]);
     }
 #pragma unroll
     for (int t = 0; t < kCl; ++t) {
@@ -383,16 +407,22 @@ __global__ __launch_bounds__(kB1Threads) void k_gemv_b1(KDesc d, B1Args a, const
       bool valid = false, odd = false;
       uint64_t entry = 0;
       if (f < T) {
-        const uint64_t I = fld[t] & d.shape_mask;
+        const uint32_t ilo = flo[t] & d.shape_mask_lo;
+        const uint32_t ihi = fhi[t] & d.shape_mask_hi;
+        const uint64_t I = ((uint64_t)ihi << 32) | ilo;
         if (I < d.index_count) {
           valid = true;
-          const double Id = (double)I;
-          uint32_t k = bk[(uint32_t)(I >> d.bshift)];
+          const double Id = __builtin_fma((double)ihi, 4294967296.0, (double)ilo);
+          const uint32_t bidx = d.bshift >= 32 ? (ihi >> (d.bshift - 32)) : __builtin_amdgcn_alignbit(ihi, ilo, d.bshift);
+          uint32_t k = bk[bidx];
           while ((int)k + 1 < ncls && Id >= cls[k + 1].start) ++k;
           const LlvqClassHot& h = cls[k];
           odd = ((h.meta >> 17) & 1u) != 0u;
           entry = I | ((uint64_t)f << 44) | ((uint64_t)k << 56);
-          part[f] = sg ? G[(uint32_t)(fld[t] >> d.shape_bits)] * h.invnorm : 1.0f;
+          const uint32_t gsh = d.shape_bits >= 32 ? (fhi[t] >> (d.shape_bits - 32))
+                                                  : __builtin_amdgcn_alignbit(fhi[t], flo[t], d.shape_bits);
+          const uint32_t g = gsh & ((1u << d.gain_bits) - 1u);
+          part[f] = sg ? G[g] * h.invnorm : 1.0f;
         } else {
           part[f] = 0.0f;
           if (err) atomicAdd(err, 1);
