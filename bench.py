@@ -41,18 +41,20 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # sha256 is given (profiles/ holds the summaries).  When the source changes they no longer
 # apply and the benchmark reports null for them.
 KERNEL_PROFILE = {
-    "source_sha256": None,
-    "valu_lane_ops_per_block": None,   # SQ_INSTS_VALU * 64 / blocks
-    "fetch_bytes_per_launch": None,    # FETCH_SIZE scaled by the copy-kernel calibration
-    "write_bytes_per_launch": None,
+    "source_sha256": "0e2b6c48e4dcb0ff5557a159e8798ae3c7a549e4419e51c49a553d867f38e1e4",
+    "summary": "profiles/k_gemv_b1_4096x11008_bf16_batch1.md",
+    "valu_lane_ops_per_block": 778.9,      # SQ_INSTS_VALU * 64 / blocks
+    "fetch_bytes_per_launch": 12212254,    # FETCH_SIZE scaled by the copy-kernel calibration (x 1.9998)
+    "write_bytes_per_launch": 32768,       # WRITE_SIZE (x 1.0000)
 }
 
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for rel in ("weight_decompression_amd/csrc/llvq.hip", "weight_decompression_amd/csrc/gen_tables.cpp"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "weight_decompression_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -84,7 +86,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-rows", type=int, default=192)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB mebibytes (HBM counter calibration)")
     a = ap.parse_args()
+
+    if a.copy_calibration:
+        import torch
+        n = a.copy_calibration * 1024 * 1024
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this LLVQ build runs on exactly one GPU (no sharding or collectives are "
@@ -159,7 +176,8 @@ def main():
         ops = KERNEL_PROFILE["valu_lane_ops_per_block"] * blocks
         roof = {"bound": "alu", "achieved": ops / sec / 1e12, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
                 "frac": ops / sec / 1e12 / VALU_PEAK_TOPS, "traffic": traffic,
-                "valu_lane_ops_per_block": KERNEL_PROFILE["valu_lane_ops_per_block"], "hbm": hbm}
+                "valu_lane_ops_per_block": KERNEL_PROFILE["valu_lane_ops_per_block"],
+                "profile": KERNEL_PROFILE["summary"], "hbm": hbm}
     else:
         roof = dict(hbm)
         roof["traffic"] = traffic
