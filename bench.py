@@ -17,6 +17,10 @@ measured VALU instructions per block of the current kernel source) with the HBM 
 beside it; `cpu_baseline` times the CPU oracle on a row sample of the same tensor.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-rows R] [--no-cpu]
+       python bench.py --workload {gemv_11008x4096,gemv_4096x4096,gemv_28672x8192} [--batch B]
+       python bench.py --workload decode_bf16_7b [--layers 32]
+       python bench.py --workload roundtrip [--points 100000000]
+The other workloads print one line each in the same format (their own metric).
 """
 
 import argparse
@@ -37,15 +41,18 @@ HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, published
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12  # 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz (lane-ops/s)
 ROTATE_BYTES = 512 * 1024 * 1024
 
-# Per-kernel figures taken with rocprofv3 on the GEMV kernel built from the source whose
+# Per-workload figures taken with rocprofv3 on the kernels built from the source whose
 # sha256 is given (profiles/ holds the summaries).  When the source changes they no longer
 # apply and the benchmark reports null for them.
-KERNEL_PROFILE = {
-    "source_sha256": "0e2b6c48e4dcb0ff5557a159e8798ae3c7a549e4419e51c49a553d867f38e1e4",
-    "summary": "profiles/k_gemv_b1_4096x11008_bf16_batch1.md",
-    "valu_lane_ops_per_block": 778.9,      # SQ_INSTS_VALU * 64 / blocks
-    "fetch_bytes_per_launch": 12212254,    # FETCH_SIZE scaled by the copy-kernel calibration (x 1.9998)
-    "write_bytes_per_launch": 32768,       # WRITE_SIZE (x 1.0000)
+KERNEL_PROFILES = {
+    "gemv_4096x11008_b1": {
+        "source_sha256": "0e2b6c48e4dcb0ff5557a159e8798ae3c7a549e4419e51c49a553d867f38e1e4",
+        "summary": "profiles/k_gemv_b1_4096x11008_bf16_batch1.md",
+        "unit_of_work": "24-weight block",
+        "valu_lane_ops_per_unit": 778.9,       # SQ_INSTS_VALU * 64 / blocks
+        "fetch_bytes_per_launch": 12212254,    # FETCH_SIZE scaled by the copy-kernel calibration (x 1.9998)
+        "write_bytes_per_launch": 32768,       # WRITE_SIZE (x 1.0000)
+    },
 }
 
 
@@ -79,6 +86,223 @@ def cpu_baseline(t, rows):
                       f"+ fp64 GEMV, {procs} processes, {dt:.2f} s wall"}
 
 
+def time_steps(launch, steps, warmup, stream):
+    """Run `launch(i)` warmup times, then time `steps` calls with HIP events on `stream`."""
+    import torch
+    rc = 0
+    for i in range(warmup):
+        rc |= launch(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        rc |= launch(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    if rc != 0:
+        raise RuntimeError(f"llvq call returned {rc}")
+    return ev0.elapsed_time(ev1) / steps * 1e-3, wall
+
+
+def roofline(profile_key, ops_units, sec, alg_bytes, per_unit_text):
+    """VALU roofline from the profiled lane-op count of the current source, with the HBM figure beside it."""
+    hbm = {"bound": "hbm", "achieved": alg_bytes / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": alg_bytes / sec / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": alg_bytes, "per_unit": per_unit_text}
+    prof = KERNEL_PROFILES.get(profile_key, {})
+    prof_ok = prof.get("source_sha256") == kernel_source_sha()
+    traffic = None
+    if prof_ok and prof.get("fetch_bytes_per_launch") is not None:
+        traffic = prof["fetch_bytes_per_launch"] + prof["write_bytes_per_launch"]
+    if prof_ok and prof.get("valu_lane_ops_per_unit"):
+        ops = prof["valu_lane_ops_per_unit"] * ops_units
+        return {"bound": "alu", "achieved": ops / sec / 1e12, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
+                "frac": ops / sec / 1e12 / VALU_PEAK_TOPS, "traffic": traffic,
+                "valu_lane_ops_per_unit": prof["valu_lane_ops_per_unit"], "unit_of_work": prof["unit_of_work"],
+                "profile": prof["summary"], "hbm": hbm}
+    roof = dict(hbm)
+    roof["traffic"] = traffic
+    roof["note"] = "VALU instructions not profiled for this kernel source"
+    return roof
+
+
+def base_line(metric, value, unit, steps, warmup, sec, dtype, workload, extra_cfg):
+    cfg = {"workload": workload}
+    cfg.update(extra_cfg)
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": sec * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": dtype, "data": "synthetic", "config": cfg}
+
+
+def rotating_copies(packed, nbytes_min):
+    """Device copies of a packed stream spanning >= nbytes_min bytes (so the LLC cannot hold them)."""
+    import torch
+    stride = (packed.size + 255) // 256 * 256
+    ncopies = max(2, math.ceil(nbytes_min / stride))
+    big = torch.empty((ncopies, stride), dtype=torch.uint8, device="cuda:0")
+    src = torch.zeros(stride, dtype=torch.uint8)
+    src[: packed.size] = torch.from_numpy(packed)
+    big[:] = src.to("cuda:0")
+    return big
+
+
+def run_gemv(a, name, t, profile_key, label):
+    """Time llvq_gemv on one packed tensor (rotating copies) and build its JSON line."""
+    import numpy as np
+    import torch
+    import weight_decompression_amd as wd
+
+    lib = wd.load_library()
+    desc = wd.make_desc(t.mode, t.rows, t.cols, t.max_shell, t.shape_bits, t.gain_bits)
+    batch = t.x_bits.shape[0] if t.x_bits is not None else t.x_f32.shape[0]
+    blocks = t.rows * t.kb
+    big = rotating_copies(t.packed, ROTATE_BYTES)
+    ncopies = big.shape[0]
+    scales = torch.from_numpy(t.scales_f16.copy()).cuda()
+    if t.x_bits is not None:
+        x = torch.from_numpy(t.x_bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+        xk, xb = wd.X_BF16, 2
+    else:
+        x = torch.from_numpy(t.x_f32.copy()).cuda()
+        xk, xb = wd.X_F32, 4
+    y = torch.empty((batch, t.rows), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    dref = ctypes.byref(desc)
+    args = [(dref, ctypes.c_void_p(big[i].data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+             ctypes.c_void_p(x.data_ptr()), xk, batch, ctypes.c_void_p(y.data_ptr()), None, sptr)
+            for i in range(ncopies)]
+    gemv = lib.llvq_gemv
+    sec, wall = time_steps(lambda i: gemv(*args[i % ncopies]), a.steps, a.warmup, stream)
+    if not bool(torch.isfinite(y).all()):
+        raise RuntimeError("non-finite GEMV output")
+    packed_bytes = blocks * t.field_bits / 8
+    alg_bytes = packed_bytes + xb * t.cols * batch + 4 * t.rows * batch
+    out = base_line(METRIC if name == DEFAULT_WORKLOAD else
+                    f"compressed-weight GB/s, LLVQ dequant-GEMV, batch {batch}, 1 MI355X",
+                    packed_bytes / sec / 1e9, "GB/s", a.steps, a.warmup, sec, "f32", label,
+                    {"rows": t.rows, "cols": t.cols, "blocks": blocks, "field_bits": t.field_bits,
+                     "max_shell": t.max_shell, "batch": batch, "rotating_copies": ncopies})
+    out["dtype_detail"] = "exact integer/fp64 index decode, fp32 accumulation, " + \
+        ("bf16" if xk == wd.X_BF16 else "fp32") + " x, fp16 scales"
+    out["roofline"] = roofline(profile_key, blocks, sec, alg_bytes,
+                               f"{t.field_bits / 8:g} B packed index per 24-weight block + x + y")
+    out["weights_per_s"] = t.rows * t.cols * batch / sec
+    out["wall_s_timed"] = wall
+    if name == DEFAULT_WORKLOAD and not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(t, min(a.cpu_rows, t.rows))
+    return out
+
+
+def run_decode_7b(a):
+    """Bulk decode-to-bf16 of 32 layers x (4 x 4096x4096 + 3 x 4096x11008)."""
+    import torch
+    import weight_decompression_amd as wd
+    from weight_decompression_amd import synth
+
+    lib = wd.load_library()
+    C10 = wd.index_count(10)
+    layers = a.layers
+    items = []
+    blocks = 0
+    weights = 0
+    for L in range(layers):
+        for j in range(len(synth.workload5_shapes())):
+            t = synth.workload5_tensor(C10, L, j)
+            desc = wd.make_desc(t.mode, t.rows, t.cols, t.max_shell, t.shape_bits, t.gain_bits)
+            packed = torch.from_numpy(t.packed).cuda()
+            scales = torch.from_numpy(t.scales_f16.copy()).cuda()
+            out = torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device="cuda:0")
+            items.append((desc, packed, scales, out))
+            blocks += t.rows * t.kb
+            weights += t.rows * t.cols
+        print(f"bench: layer {L} generated", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    calls = [(ctypes.byref(d), ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(s.data_ptr()), wd.OUT_BF16,
+              ctypes.c_void_p(o.data_ptr()), None, sptr) for d, p, s, o in items]
+    dec = lib.llvq_decode
+
+    def step(_):
+        rc = 0
+        for c in calls:
+            rc |= dec(*c)
+        return rc
+
+    sec, wall = time_steps(step, a.steps, a.warmup, stream)
+    packed_bytes = blocks * 6
+    alg_bytes = packed_bytes + 2 * weights
+    out = base_line("bulk LLVQ decode-to-bf16 throughput, 7B-shaped weight set, 1 MI355X",
+                    weights / sec, "weights/s", a.steps, a.warmup, sec, "f32",
+                    f"llvq_decode bf16, {layers} layers x (4 x 4096x4096 + 3 x 4096x11008)",
+                    {"layers": layers, "tensors": len(items), "blocks": blocks, "weights": weights,
+                     "packed_bytes": packed_bytes, "bf16_bytes": 2 * weights})
+    out["compressed_GBps"] = packed_bytes / sec / 1e9
+    out["bf16_written_GBps"] = 2 * weights / sec / 1e9
+    out["roofline"] = roofline("decode_bf16", blocks, sec, alg_bytes,
+                               "6 B packed index read + 48 B bf16 written per 24-weight block")
+    out["wall_s_timed"] = wall
+    return out
+
+
+def run_roundtrip(a):
+    """Index -> point -> index round trip on n uniform indices over shells 2..10."""
+    import numpy as np
+    import torch
+    import weight_decompression_amd as wd
+    from weight_decompression_amd import synth
+
+    lib = wd.load_library()
+    C10 = wd.index_count(10)
+    n = a.points
+    kb = 1000
+    rows = (n + kb - 1) // kb
+    n = rows * kb
+    idx = synth.workload5_roundtrip_indices(C10, n)
+    packed = synth.pack_fields(idx, 48)
+    del idx
+    desc = wd.make_desc(wd.MODE_SHAPEGAIN, rows, kb * 24, 10, 44, 4)
+    pk = torch.from_numpy(packed).cuda()
+    ref = torch.from_numpy(packed[: n * 6].view(np.uint8)).cuda()
+    del packed
+    scales = torch.ones(16, dtype=torch.float16, device="cuda:0")
+    pts = torch.empty((n, 24), dtype=torch.int8, device="cuda:0")
+    back = torch.empty(n, dtype=torch.int64, device="cuda:0")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(_):
+        rc = lib.llvq_decode(ctypes.byref(desc), ctypes.c_void_p(pk.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                             wd.OUT_POINTS_I8, ctypes.c_void_p(pts.data_ptr()), ctypes.c_void_p(err.data_ptr()), sptr)
+        rc |= lib.llvq_encode_ref(ctypes.c_void_p(pts.data_ptr()), n, 10, ctypes.c_void_p(back.data_ptr()),
+                                  ctypes.c_void_p(err.data_ptr()), sptr)
+        return rc
+
+    sec, wall = time_steps(step, a.steps, a.warmup, stream)
+    # the round trip must reproduce every index: compare the low 48 bits of the packed field
+    b8 = back.view(torch.uint8).view(n, 8)[:, :6].reshape(-1)
+    ok = bool(torch.equal(b8, ref)) and int(err.item()) == 0
+    out = base_line("LLVQ index->point->index round trip throughput, 1 MI355X", n / sec, "points/s",
+                    a.steps, a.warmup, sec, "int64",
+                    f"llvq_decode points + llvq_encode_ref, {n} uniform indices over shells 2..10",
+                    {"points": n})
+    out["round_trip_exact"] = ok
+    out["roofline"] = roofline("roundtrip", n, sec, n * (6 + 24 + 24 + 8),
+                               "6 B index read + 24 B point written (decode); 24 B read + 8 B written (rank)")
+    out["wall_s_timed"] = wall
+    if not ok:
+        raise RuntimeError("round trip mismatch")
+    return out
+
+
+DEFAULT_WORKLOAD = "gemv_4096x11008"
+WORKLOADS = ("gemv_4096x11008", "gemv_11008x4096", "gemv_4096x4096", "gemv_28672x8192", "decode_bf16_7b",
+             "roundtrip")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,6 +310,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-rows", type=int, default=192)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--workload", choices=WORKLOADS, default=DEFAULT_WORKLOAD,
+                    help="default: the 4096x11008 batch-1 GEMV (the headline line)")
+    ap.add_argument("--batch", type=int, default=1, help="activation rows (GEMV workloads)")
+    ap.add_argument("--layers", type=int, default=32, help="layers of the 7B-shaped set (decode_bf16_7b)")
+    ap.add_argument("--points", type=int, default=100_000_000, help="indices in the round trip")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB mebibytes (HBM counter calibration)")
     a = ap.parse_args()
@@ -108,104 +337,31 @@ def main():
               "built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
-    import torch
-
     import weight_decompression_amd as wd
     from weight_decompression_amd import synth
 
-    lib = wd.load_library()
     C10 = wd.index_count(10)
-    t = synth.workload3(C10, 1, load_fidelity(1), batch=1)
-    desc = wd.make_desc(t.mode, t.rows, t.cols, t.max_shell, t.shape_bits, t.gain_bits)
-    blocks = t.rows * t.kb
-    dev = torch.device("cuda:0")
-
-    need = wd.packed_bytes(desc)
-    stride = (need + 255) // 256 * 256
-    ncopies = max(2, math.ceil(ROTATE_BYTES / stride))
-    big = torch.empty((ncopies, stride), dtype=torch.uint8, device=dev)
-    src = torch.zeros(stride, dtype=torch.uint8)
-    src[: t.packed.size] = torch.from_numpy(t.packed)
-    big[:] = src.to(dev)
-    scales = torch.from_numpy(t.scales_f16.copy()).to(dev)
-    x = torch.from_numpy(t.x_bits.view(np.int16).copy()).to(dev).view(torch.bfloat16)
-    y = torch.empty((1, t.rows), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    sptr = ctypes.c_void_p(stream.cuda_stream)
-    dref = ctypes.byref(desc)
-    args = [(dref, ctypes.c_void_p(big[i].data_ptr()), ctypes.c_void_p(scales.data_ptr()),
-             ctypes.c_void_p(x.data_ptr()), wd.X_BF16, 1, ctypes.c_void_p(y.data_ptr()), None, sptr)
-            for i in range(ncopies)]
-    gemv = lib.llvq_gemv
-
-    rc = 0
-    for i in range(a.warmup):
-        rc |= gemv(*args[i % ncopies])
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(a.steps):
-        rc |= gemv(*args[i % ncopies])
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    if rc != 0:
-        raise RuntimeError(f"llvq_gemv returned {rc}")
-    ms_total = ev0.elapsed_time(ev1)
-    ms = ms_total / a.steps
-    sec = ms * 1e-3
-    y_h = y.cpu().numpy()
-    if not np.all(np.isfinite(y_h)):
-        raise RuntimeError("non-finite GEMV output")
-
-    packed_bytes = blocks * t.field_bits / 8
-    alg_bytes = packed_bytes + 2 * t.cols + 4 * t.rows
-    value = packed_bytes / sec / 1e9
-    hbm = {"bound": "hbm", "achieved": alg_bytes / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": alg_bytes / sec / 1e9 / HBM_PEAK_GBS,
-           "bytes_per_launch": alg_bytes, "per_unit": "6 B packed index per 24-weight block + x + y"}
-    prof_ok = KERNEL_PROFILE["source_sha256"] == kernel_source_sha()
-    traffic = None
-    if prof_ok and KERNEL_PROFILE["fetch_bytes_per_launch"] is not None:
-        traffic = KERNEL_PROFILE["fetch_bytes_per_launch"] + KERNEL_PROFILE["write_bytes_per_launch"]
-    if prof_ok and KERNEL_PROFILE["valu_lane_ops_per_block"]:
-        ops = KERNEL_PROFILE["valu_lane_ops_per_block"] * blocks
-        roof = {"bound": "alu", "achieved": ops / sec / 1e12, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
-                "frac": ops / sec / 1e12 / VALU_PEAK_TOPS, "traffic": traffic,
-                "valu_lane_ops_per_block": KERNEL_PROFILE["valu_lane_ops_per_block"],
-                "profile": KERNEL_PROFILE["summary"], "hbm": hbm}
+    w = a.workload
+    if w == "gemv_4096x11008":
+        t = synth.workload3(C10, 1, load_fidelity(1), batch=a.batch)
+        out = run_gemv(a, w, t, f"gemv_4096x11008_b{a.batch}",
+                       f"llvq_gemv 2-bit shape-gain 4096x11008 (MLP down-proj), batch {a.batch}")
+    elif w == "gemv_11008x4096":
+        t = synth.workload3(C10, 0, load_fidelity(0), batch=a.batch)
+        out = run_gemv(a, w, t, f"gemv_11008x4096_b{a.batch}",
+                       f"llvq_gemv 2-bit shape-gain 11008x4096 (MLP up-proj), batch {a.batch}")
+    elif w == "gemv_4096x4096":
+        t = synth.workload2(C10, batch=a.batch)
+        out = run_gemv(a, w, t, f"gemv_4096x4096_b{a.batch}",
+                       f"llvq_gemv 2-bit shape-gain 4096x4096 (q_proj), batch {a.batch}")
+    elif w == "gemv_28672x8192":
+        t = synth.workload4(C10, a.batch)
+        out = run_gemv(a, w, t, f"gemv_28672x8192_b{a.batch}",
+                       f"llvq_gemv 2-bit shape-gain 28672x8192, batch {a.batch}")
+    elif w == "decode_bf16_7b":
+        out = run_decode_7b(a)
     else:
-        roof = dict(hbm)
-        roof["traffic"] = traffic
-        roof["note"] = "VALU instructions per block not profiled for this kernel source"
-
-    out = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "dtype_detail": "exact integer/fp64 index decode, fp32 dot-product accumulation, bf16 x, fp16 gains",
-        "data": "synthetic",
-        "config": {"workload": "llvq_gemv 2-bit shape-gain 4096x11008 (MLP down-proj), batch 1",
-                   "rows": t.rows, "cols": t.cols, "blocks": blocks, "field_bits": t.field_bits,
-                   "max_shell": t.max_shell, "batch": 1, "rotating_copies": ncopies},
-        "roofline": roof,
-        "weights_per_s": t.rows * t.cols / sec,
-        "wall_s_timed": wall,
-    }
-    if not a.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(t, min(a.cpu_rows, t.rows))
+        out = run_roundtrip(a)
     print(json.dumps(out), flush=True)
 
 

@@ -98,10 +98,5 @@ def test_error_strings(lib):
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
-    saved = wd._lib
-    try:
-        wd._lib = None
-        with pytest.raises(RuntimeError, match="not found"):
-            wd.load_library(str(tmp_path / "missing.so"))
-    finally:
-        wd._lib = saved
+    with pytest.raises(RuntimeError, match="not found"):
+        wd.load_library(str(tmp_path / "missing.so"))

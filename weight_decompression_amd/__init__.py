@@ -41,14 +41,20 @@ class Desc(ctypes.Structure):
                 f"shape_bits={self.shape_bits}, gain_bits={self.gain_bits})")
 
 
-_lib = None
+_libs = {}
 
 
 def load_library(path=LIB_PATH):
-    """Load libllvq.so (raises if it has not been built)."""
-    global _lib
-    if _lib is not None:
-        return _lib
+    """Load libllvq.so (raises if it has not been built).
+
+    torch is imported first: PyTorch wheels carry their own HIP runtime, and the
+    library must bind to the same runtime as the streams and device pointers it is
+    handed (loaded first, it would bind to the system runtime and every launch on a
+    torch stream would fail)."""
+    path = os.path.abspath(path)
+    if path in _libs:
+        return _libs[path]
+    import torch  # noqa: F401  (selects the process's HIP runtime)
     if not os.path.exists(path):
         raise RuntimeError(f"LLVQ HIP library not found at {path}; build it with "
                            f"`python -m weight_decompression_amd.build_lib` (no CPU fallback exists)")
@@ -67,7 +73,7 @@ def load_library(path=LIB_PATH):
     lib.llvq_gemv.restype = ctypes.c_int
     lib.llvq_encode_ref.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.llvq_encode_ref.restype = ctypes.c_int
-    _lib = lib
+    _libs[path] = lib
     return lib
 
 
