@@ -173,6 +173,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+#include "llvq_engine.h"
 #include "llvq_gemv_b1.h"
 
 // ---------------------------------------------------------------------------
@@ -544,32 +545,65 @@ LLVQ_API int llvq_decode(const llvq_desc* d, const void* packed, const void* sca
 }
 
 namespace {
-constexpr uint32_t kLdsBudget = 160u * 1024u / 2u;   // two workgroups per CU
+constexpr uint32_t kLdsBudget = 160u * 1024u;   // one workgroup per CU
+constexpr int kGridMax = 256;                    // one workgroup per CU
+
+// Rows per tile for the engine kernels: among the R with R * Kb <= tmax, the one that
+// minimises the work of the busiest workgroup, counting each tile as its blocks plus a
+// fixed overhead of kTileOverhead blocks (a tile's first classify unit and its last,
+// partly filled chunks leave waves idle).  Ties go to larger tiles.
+constexpr long kTileOverhead = 1024;
+
+int pick_rows_per_tile(int rows, int kb, int tmax, int* ntiles_out, int* grid_out) {
+  int rmax = tmax / kb;
+  if (rmax > rows) rmax = rows;
+  if (rmax < 1) return 0;
+  int best_r = 0;
+  long best_cost = -1;
+  for (int r = rmax; r >= 1; --r) {
+    const long nt = (rows + r - 1) / r;
+    const long g = nt < kGridMax ? nt : kGridMax;
+    const long cost = ((nt + g - 1) / g) * ((long)r * kb + kTileOverhead);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_r = r;
+    }
+  }
+  const int nt = (rows + best_r - 1) / best_r;
+  *ntiles_out = nt;
+  *grid_out = nt < kGridMax ? nt : kGridMax;
+  return best_r;
+}
 
 // Batch-1 fused GEMV (llvq_gemv_b1.h).  Returns LLVQ_EUNSUPPORTED when the shape does
 // not fit its tiling (the generic kernel then runs).
 int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype,
                    float* y, int32_t* err, hipStream_t s) {
-  if (k.kb > kB1TileMax) return LLVQ_EUNSUPPORTED;
   if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;   // 32-bit field index
-  int rpt = kB1TileMax / k.kb;
-  if (rpt > k.rows) rpt = k.rows;
-  const int tmax = rpt * k.kb;
+  const bool xf32 = x_dtype == LLVQ_X_F32;
   const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
-  B1Args a;
-  a.rows_per_tile = rpt;
-  a.tile_blocks_max = tmax;
+  // LDS: fixed tables + one tile buffer of 12 bytes per block + x + xsum
+  ELayout L;
+  const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0);
+  const uint32_t xbytes = align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u)) + align16((uint32_t)k.kb * 4u);
+  if (base + xbytes + 12u * (uint32_t)k.kb > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((kLdsBudget - base - xbytes) / 12u) & ~15;
+  if (tmax > kETileMax) tmax = kETileMax;
+  EArgs a;
+  int grid = 0;
+  a.rows_per_tile = pick_rows_per_tile(k.rows, k.kb, tmax, &a.ntiles, &grid);
+  if (a.rows_per_tile == 0) return LLVQ_EUNSUPPORTED;
   a.nbuckets = nbuckets;
-  a.L = b1_layout(k.ncls, 1 << k.gain_bits, nbuckets, k.kb, tmax, x_dtype == LLVQ_X_F32);
-  if (a.L.total > kLdsBudget) return LLVQ_EUNSUPPORTED;
-  const int ntiles = (k.rows + rpt - 1) / rpt;
-  int grid = 512;
-  if (grid > ntiles) grid = ntiles;
-  if (x_dtype == LLVQ_X_F32)
-    hipLaunchKernelGGL((k_gemv_b1<true>), dim3(grid), dim3(kB1Threads), a.L.total, s, k, a,
+  engine_layout_base(a.L, k.ncls, 1 << k.gain_bits, nbuckets, a.rows_per_tile * k.kb);
+  a.xs = a.L.total;
+  a.xsum = a.xs + align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u));
+  const uint32_t total = a.xsum + align16((uint32_t)k.kb * 4u);
+  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  if (xf32)
+    hipLaunchKernelGGL((k_gemv_b1<true>), dim3(grid), dim3(kEThreads), total, s, k, a,
                        static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, y, err);
   else
-    hipLaunchKernelGGL((k_gemv_b1<false>), dim3(grid), dim3(kB1Threads), a.L.total, s, k, a,
+    hipLaunchKernelGGL((k_gemv_b1<false>), dim3(grid), dim3(kEThreads), total, s, k, a,
                        static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, y, err);
   return launch_status();
 }

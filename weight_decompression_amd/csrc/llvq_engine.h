@@ -1,0 +1,373 @@
+// Tiled LLVQ block decoder shared by the fused kernels (gfx950).
+// Included once by llvq.hip (uses its KDesc, read_field and table namespaces).
+//
+// A workgroup of kEThreads lanes (16 waves, one workgroup per CU) is persistent over
+// tiles of R consecutive rows (T = R * Kb <= kETileMax blocks).  Per tile, with a
+// workgroup barrier between the phases:
+//   1. classify: every block's field is read, its class found (bucket table on the top
+//      index bits + a short scan of the class starts) and the block appended to one of
+//      two LDS queues: odd-coset classes from the front, even-coset classes from the
+//      back.  The block's scale goes to an LDS slot.  Indices >= the shell-union size
+//      contribute 0 and are counted.
+//   2. decode: chunks of 64 consecutive entries of one queue, one block per lane, so a
+//      wavefront runs one of the two (very different) decoders without divergence;
+//      chunks are handed out by an LDS counter, odd chunks first.
+//   3. a consumer turns the decoded values into the kernel's result (dot product,
+//      stored weights, ...).
+//
+// Rank unranking: exact arithmetic decoding in fp64.  With y = u * n the value slot is
+// the number of cumulative counts C_j <= floor(y) (SWAR compare of the three thresholds
+// packed in one dword) and y <- (y - C_k) * (n' / c_k), n' the values left after the
+// step, n'/c from an LDS table.  The decision margins (>= n/(2Q), Q <= 4.2e8
+// arrangements) exceed the accumulated rounding error by a factor > 1e5.  The last 6
+// values come from a table of all 4^6 slot sequences grouped by composition in
+// lexicographic order: with counts c (sum 6) and y in [0, 6), the rank inside the
+// group is floor(y * Q(c) / 6).
+
+#pragma once
+
+constexpr int kEThreads = 1024;
+constexpr int kEWaves = kEThreads / 64;
+constexpr int kETileMax = 4096;     // block index inside a tile fits 12 bits
+constexpr int kEUnit = 256;         // fields per classify unit (4 per lane)
+constexpr int kBias = 12;           // value tables store 12 +- v (|v| <= 12)
+constexpr int kTail = 6;            // values resolved by the tail table
+constexpr int kSteps = 24 - kTail;  // values resolved step by step
+constexpr int kFStride = 25;        // F[n][c] row length (c = 0..24)
+
+struct ELayout {
+  // byte offsets inside the dynamic LDS segment
+  uint32_t ftab;      // double F[25][25]: F[n][c] = n / c   (offset 0)
+  uint32_t cls;       // LlvqClassHot[ncls]
+  uint32_t gains;     // float[2^gain_bits]
+  uint32_t bucket;    // uint8[nbuckets]
+  uint32_t tail;      // uint16[4096]
+  uint32_t tcomp;     // LlvqTailComp[343]
+  uint32_t ctr;       // int[4]: odd queue fill, even queue fill, next chunk
+  uint32_t queue;     // uint64[tmax]: I | f << 44 | class << 56
+  uint32_t part;      // float[tmax]: block scale, then the block's result
+  uint32_t total;     // end of the engine's part; consumer data follows
+};
+
+__host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
+
+__host__ __device__ inline uint32_t engine_layout_base(ELayout& L, int ncls, int ngains, int nbuckets, int tmax) {
+  uint32_t o = 0;
+  L.ftab = o;     o = align16(o + 25u * kFStride * 8u);
+  L.cls = o;      o = align16(o + (uint32_t)ncls * (uint32_t)sizeof(LlvqClassHot));
+  L.gains = o;    o = align16(o + (uint32_t)ngains * 4u);
+  L.bucket = o;   o = align16(o + (uint32_t)nbuckets);
+  L.tail = o;     o = align16(o + 4096u * 2u);
+  L.tcomp = o;    o = align16(o + 343u * (uint32_t)sizeof(LlvqTailComp));
+  L.ctr = o;      o = align16(o + 16u);
+  L.queue = o;    o = align16(o + (uint32_t)tmax * 8u);
+  L.part = o;     o = align16(o + (uint32_t)tmax * 4u);
+  L.total = o;
+  return o;
+}
+
+struct EArgs {
+  int rows_per_tile;
+  int ntiles;
+  int nbuckets;
+  ELayout L;
+  uint32_t xs;     // GEMV: x, kb*24 elements (fp32 or bf16), zero padded
+  uint32_t xsum;   // GEMV: float[kb], sum of the 24 x values of each block column
+};
+
+// ---------------------------------------------------------------------------
+// ALU helpers.  Full-rate 24-bit multiply-add and bit count with accumulator (the
+// compiler otherwise picks a quarter-rate 64-bit multiply-add, and does not fold the
+// addend into v_bcnt).
+
+__device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+  return d;
+}
+
+__device__ __forceinline__ uint32_t bcnt_add(uint32_t a, uint32_t c) {
+  uint32_t d;
+  asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(d) : "v"(a), "s"(c));
+  return d;
+}
+
+__device__ __forceinline__ uint32_t lshl_add(uint32_t a, uint32_t s, uint32_t b) {
+  uint32_t d;
+  asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "i"(s), "v"(b));
+  return d;
+}
+
+// Field j of the packed stream as (lo, hi) words, fields of f <= 64 bits.  48-bit fields
+// (the 2-bit format) start at byte 6j: two dword loads and a funnel shift.
+__device__ __forceinline__ void field_words(const uint8_t* __restrict__ packed, uint32_t j, int f,
+                                            uint32_t& lo, uint32_t& hi) {
+  if (f == 48) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(packed) + ((3u * j) >> 1);
+    const uint32_t w0 = w[0], w1 = w[1];
+    const uint32_t sh = (j & 1u) << 4;
+    lo = __builtin_amdgcn_alignbit(w1, w0, sh);
+    hi = (w1 >> sh) & 0xffffu;
+  } else {
+    const uint64_t v = read_field(packed, j, f);
+    lo = (uint32_t)v;
+    hi = (uint32_t)(v >> 32);
+  }
+}
+
+// SWAR value-slot choice: number of thresholds C_j <= f (j = 1..3), as 0/1 bytes.
+__device__ __forceinline__ uint32_t swar_ge(uint32_t f, uint32_t nc) {
+  const uint32_t t = mad_u24(f, 0x010101u, nc);
+  return (t >> 7) & 0x010101u;
+}
+
+// ---------------------------------------------------------------------------
+// per-block decoders
+
+// Common per-block setup from the class record: J / A split, codeword, initial y.
+struct BlockStart {
+  uint32_t c;   // codeword
+  uint32_t s;   // sign bits
+  double y;     // y_0 = (R + 1/2) * n0 / P
+};
+
+__device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELayout& L, double Id,
+                                                  const LlvqClassHot& h) {
+  BlockStart bs;
+  const double Jd = Id - h.start;
+  const uint32_t q = (uint32_t)__builtin_fma(Jd, h.inv_a, 0x1p-13);    // floor(J / A), exact
+  const uint32_t r = (uint32_t)__builtin_fma(-(double)q, h.a, Jd);      // J - q A, exact
+  const uint32_t B = h.meta & 31u;
+  bs.s = q & ((1u << B) - 1u);
+  const uint32_t R = q >> B;
+  bs.c = dev_tables::kGolayTable[h.toff + r];
+  bs.y = __builtin_fma((double)R, h.y0s, 0.5 * h.y0s);
+  return bs;
+}
+
+// Slot codes of the last 6 values (2 bits each, first of the six in the low bits), from
+// the counts left (sum 6) and y in [0, 6).
+__device__ __forceinline__ uint32_t tail_codes(const uint8_t* smem, const ELayout& L, uint32_t cnt, double y) {
+  const uint32_t ci = __builtin_amdgcn_udot4(cnt, 0x00310701u, 0u, false);   // c0 + 7 c1 + 49 c2
+  const LlvqTailComp tc = reinterpret_cast<const LlvqTailComp*>(smem + L.tcomp)[ci];
+  const uint32_t r = (uint32_t)((float)y * tc.q_over_6);
+  return reinterpret_cast<const uint16_t*>(smem + L.tail)[tc.offset + r];
+}
+
+// Odd coset: one part of 24 values, visited in position order.  step(p) returns the
+// biased value byte 12 + v_p in the low 8 bits (upper bits zero).  The sign of each value
+// follows from the codeword bit and the value mod 4, folded into one byte-table lookup.
+struct OddDec {
+  double y;
+  uint32_t nc, cnt, notc, svlo, svhi, codes;
+
+  __device__ __forceinline__ void init(const LlvqClassHot& h, const BlockStart& bs) {
+    y = bs.y;
+    nc = h.nc0;
+    cnt = h.cnt0;
+    notc = ~bs.c;
+    svlo = h.sv0lo;
+    svhi = h.sv0hi;
+    codes = 0u;
+  }
+
+  __device__ __forceinline__ uint32_t step(const uint8_t* smem, const ELayout& L, int p) {
+    uint32_t k;
+    if (p < kSteps) {
+      const double* F = reinterpret_cast<const double*>(smem + L.ftab);
+      const uint32_t f = (uint32_t)y;
+      const uint32_t g = swar_ge(f, nc);
+      k = bcnt_add(g, 0x0c0c0c00u);
+      const uint32_t ck = __builtin_amdgcn_perm(0u, cnt, k);
+      const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
+      const double fac = F[(23 - p) * kFStride + ck];
+      y = (y - (double)Ck) * fac;
+      cnt -= ((g << 8) | 1u) - g;
+      nc += g ^ 0x010101u;
+      if (p == kSteps - 1) codes = tail_codes(smem, L, cnt, y);
+    } else {
+      k = __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | 0x0c0c0c00u;
+    }
+    const uint32_t sel = lshl_add(__builtin_amdgcn_ubfe(notc, p, 1), 2, k);
+    return __builtin_amdgcn_perm(svhi, svlo, sel);
+  }
+};
+
+// Even coset: support values (on the codeword's positions, ascending) then complement
+// values (other positions, ascending), on one arithmetic-decoding state.  step(i)
+// returns the biased value byte of the i-th decoded value and its position.  Nonzero
+// positions consume the bits of s in decode order; the last support position takes the
+// sign that fixes the parity of negatives on the support and consumes no bit.
+struct EvenDec {
+  double y;
+  uint32_t nc, cnt, svlo, svhi, nz, m, s, nb, codes, negq, w, c;
+  bool two;
+
+  __device__ __forceinline__ void init(const LlvqClassHot& h, const BlockStart& bs) {
+    w = (h.meta >> 8) & 31u;
+    const uint32_t pi = (h.meta >> 16) & 1u;
+    two = w != 0u && w != 24u;
+    const uint32_t n0 = w ? w : 24u;
+    // the support's first w-1 signs are bits 0..w-2 of s (all support values are nonzero)
+    negq = w ? (((uint32_t)__builtin_popcount(bs.s & ((1u << (w - 1u)) - 1u)) & 1u) ^ pi) : 0u;
+    y = bs.y;
+    nc = h.nc0;
+    cnt = h.cnt0;
+    svlo = h.sv0lo;
+    svhi = h.sv0hi;
+    nz = (h.meta >> 20) & 15u;
+    c = bs.c;
+    m = w ? bs.c : 0xffffffu;
+    s = bs.s;
+    nb = (n0 - 1u) * (kFStride * 8u);   // byte offset of F[n'][0], n' = values left after the step
+    codes = 0u;
+  }
+
+  __device__ __forceinline__ uint32_t step(const uint8_t* smem, const ELayout& L, const LlvqClassHot& h, int i,
+                                           uint32_t& pos) {
+    if (i == 8 || i == 12 || i == 16) {
+      const bool sw = two && (w == (uint32_t)i);
+      nc = sw ? h.nc1 : nc;
+      cnt = sw ? h.cnt1 : cnt;
+      svlo = sw ? h.sv1lo : svlo;
+      svhi = sw ? h.sv1hi : svhi;
+      nz = sw ? ((h.meta >> 24) & 15u) : nz;
+      m = sw ? (~c & 0xffffffu) : m;
+    }
+    uint32_t kb;
+    if (i < kSteps) {
+      const uint32_t f = (uint32_t)y;
+      const uint32_t g = swar_ge(f, nc);
+      kb = bcnt_add(g, 0x0c0c0c00u);
+      const uint32_t ck = __builtin_amdgcn_perm(0u, cnt, kb);
+      const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
+      const double fac = *reinterpret_cast<const double*>(smem + L.ftab + nb + (ck << 3));
+      y = (y - (double)Ck) * fac;
+      cnt -= ((g << 8) | 1u) - g;
+      nc += g ^ 0x010101u;
+      // the last support step (i = w - 1) hands over to the complement: n' = 24 - w
+      if (i == 6 || i == 10 || i == 14)
+        nb = (two && w == (uint32_t)(i + 2)) ? (24u - w) * (kFStride * 8u) : nb - kFStride * 8u;
+      else
+        nb -= kFStride * 8u;
+      if (i == kSteps - 1) codes = tail_codes(smem, L, cnt, y);
+    } else {
+      kb = ((codes >> (2 * (i - kSteps))) & 3u) | 0x0c0c0c00u;
+    }
+    uint32_t free_ = (nz >> (kb & 31u)) & 1u;
+    uint32_t neg = s & free_;
+    if (i == 7 || i == 11 || i == 15 || i == 23) {
+      const bool isq = w == (uint32_t)(i + 1);
+      neg = isq ? negq : neg;
+      free_ = isq ? 0u : free_;
+    }
+    s >>= free_;
+    pos = (uint32_t)__builtin_ctz(m);
+    m &= m - 1u;
+    return __builtin_amdgcn_perm(svhi, svlo, kb + (neg << 2));
+  }
+};
+
+// ---------------------------------------------------------------------------
+// workgroup set-up and classification
+
+// LDS copy of n 32-bit words with 16-byte vector moves (n a multiple of 4 where the
+// source and destination are 16-byte aligned; the tail is copied word by word).
+__device__ __forceinline__ void lds_copy_words(uint32_t* dst, const uint32_t* src, int n, int tid) {
+  const int n4 = n >> 2;
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  for (int i = tid; i < n4; i += kEThreads) d4[i] = s4[i];
+  for (int i = (n4 << 2) + tid; i < n; i += kEThreads) dst[i] = src[i];
+}
+
+// Tables into LDS.  The caller synchronises afterwards.
+__device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L, const KDesc& d, int nbuckets,
+                                                const __half* __restrict__ scales, int tid) {
+  double* F = reinterpret_cast<double*>(smem + L.ftab);
+  for (int i = tid; i < 25 * kFStride; i += kEThreads) {
+    const int n = i / kFStride, c = i - n * kFStride;
+    F[i] = c >= 1 ? (double)n / (double)c : 0.0;
+  }
+  lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.cls), reinterpret_cast<const uint32_t*>(dev_tables::kClassHot),
+                 d.ncls * (int)(sizeof(LlvqClassHot) / 4), tid);
+  lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.tail), reinterpret_cast<const uint32_t*>(dev_tables::kTail6),
+                 2048, tid);
+  lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.tcomp), reinterpret_cast<const uint32_t*>(dev_tables::kTailComp),
+                 343 * 2, tid);
+  lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.bucket),
+                 reinterpret_cast<const uint32_t*>(dev_tables::kBucketTable[d.max_shell]), (nbuckets + 3) >> 2, tid);
+  if (d.mode == LLVQ_MODE_SHAPEGAIN) {
+    float* G = reinterpret_cast<float*>(smem + L.gains);
+    for (int i = tid; i < (1 << d.gain_bits); i += kEThreads) G[i] = __half2float(scales[i]);
+  }
+}
+
+// Classify unit u of a tile (kEUnit fields, 4 per lane): class search, queue append,
+// block scale.  Fields f of the tile are the consecutive fields j0 + f of the stream.
+__device__ __forceinline__ void classify_unit(uint8_t* smem, const ELayout& L, const KDesc& d,
+                                              const uint8_t* __restrict__ packed, uint32_t j0, int T, int u, int lane,
+                                              int32_t* err) {
+  int* ctr = reinterpret_cast<int*>(smem + L.ctr);
+  uint64_t* queue = reinterpret_cast<uint64_t*>(smem + L.queue);
+  float* part = reinterpret_cast<float*>(smem + L.part);
+  const LlvqClassHot* cls = reinterpret_cast<const LlvqClassHot*>(smem + L.cls);
+  const float* G = reinterpret_cast<const float*>(smem + L.gains);
+  const uint8_t* bk = smem + L.bucket;
+  const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
+  constexpr int kPer = kEUnit / 64;
+  uint32_t flo[kPer], fhi[kPer];
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    const int f = u * kEUnit + t * 64 + lane;
+    flo[t] = 0u;
+    fhi[t] = 0u;
+    if (f < T) field_words(packed, j0 + (uint32_t)f, d.field_bits, flo[t], fhi[t]);
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    const int f = u * kEUnit + t * 64 + lane;
+    if (u * kEUnit + t * 64 >= T) break;
+    bool valid = false, odd = false;
+    uint64_t entry = 0;
+    if (f < T) {
+      const uint32_t ilo = flo[t] & d.shape_mask_lo;
+      const uint32_t ihi = fhi[t] & d.shape_mask_hi;
+      const uint64_t I = ((uint64_t)ihi << 32) | ilo;
+      if (I < d.index_count) {
+        valid = true;
+        const double Id = __builtin_fma((double)ihi, 4294967296.0, (double)ilo);
+        const uint32_t bidx = d.bshift >= 32 ? (ihi >> (d.bshift - 32)) : __builtin_amdgcn_alignbit(ihi, ilo, d.bshift);
+        uint32_t k = bk[bidx];
+        while ((int)k + 1 < d.ncls && Id >= cls[k + 1].start) ++k;
+        const LlvqClassHot& h = cls[k];
+        odd = ((h.meta >> 17) & 1u) != 0u;
+        entry = I | ((uint64_t)f << 44) | ((uint64_t)k << 56);
+        const uint32_t gsh = d.shape_bits >= 32 ? (fhi[t] >> (d.shape_bits - 32))
+                                                : __builtin_amdgcn_alignbit(fhi[t], flo[t], d.shape_bits);
+        const uint32_t g = gsh & ((1u << d.gain_bits) - 1u);
+        part[f] = sg ? G[g] * h.invnorm : 1.0f;
+      } else {
+        part[f] = 0.0f;
+        if (err) atomicAdd(err, 1);
+      }
+    }
+    const uint64_t bo = __ballot(valid && odd);
+    const uint64_t be = __ballot(valid && !odd);
+    int baseo = 0, basee = 0;
+    if (lane == 0) {
+      baseo = atomicAdd(&ctr[0], __popcll(bo));
+      basee = atomicAdd(&ctr[1], __popcll(be));
+    }
+    baseo = __builtin_amdgcn_readfirstlane(baseo);
+    basee = __builtin_amdgcn_readfirstlane(basee);
+    if (valid && odd) queue[baseo + __popcll(bo & below)] = entry;
+    if (valid && !odd) queue[T - 1 - (basee + __popcll(be & below))] = entry;
+  }
+}
+
+// Entry fields
+__device__ __forceinline__ uint32_t entry_f(uint64_t e) { return (uint32_t)(e >> 44) & 0xfffu; }
+__device__ __forceinline__ uint32_t entry_k(uint64_t e) { return (uint32_t)(e >> 56); }
+__device__ __forceinline__ double entry_I(uint64_t e) { return (double)(e & 0xfffffffffffull); }
