@@ -175,6 +175,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 
 #include "llvq_engine.h"
 #include "llvq_gemv_b1.h"
+#include "llvq_tile.h"
 
 // ---------------------------------------------------------------------------
 // kernels
@@ -518,32 +519,6 @@ LLVQ_API const char* llvq_error_string(int code) {
   }
 }
 
-LLVQ_API int llvq_decode(const llvq_desc* d, const void* packed, const void* scales, int32_t out_kind,
-                         void* out, int32_t* err_count, void* stream) {
-  KDesc k;
-  int st = make_kdesc(d, &k);
-  if (st != LLVQ_OK) return st;
-  if (!packed || !out || !aligned(packed, 16)) return LLVQ_EINVAL;
-  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
-  const uint64_t nblocks = (uint64_t)k.rows * (uint64_t)k.kb;
-  const unsigned block = 256;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (out_kind == LLVQ_OUT_POINTS_I8) {
-    if (!aligned(out, 4)) return LLVQ_EINVAL;
-    hipLaunchKernelGGL(k_decode_points, dim3(grid_for(nblocks, block)), dim3(block), 0, s, k,
-                       static_cast<const uint8_t*>(packed), static_cast<int8_t*>(out), err_count);
-    return launch_status();
-  }
-  if (out_kind == LLVQ_OUT_BF16) {
-    if (!scales || !aligned(out, 2) || !aligned(scales, 2)) return LLVQ_EINVAL;
-    hipLaunchKernelGGL(k_decode_bf16, dim3(grid_for(nblocks, block)), dim3(block), 0, s, k,
-                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales),
-                       static_cast<uint16_t*>(out), err_count);
-    return launch_status();
-  }
-  return LLVQ_EINVAL;
-}
-
 namespace {
 constexpr uint32_t kLdsBudget = 160u * 1024u;   // one workgroup per CU
 constexpr int kGridMax = 256;                    // one workgroup per CU
@@ -608,6 +583,38 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   return launch_status();
 }
 
+// Whole-tensor decode through the byte tile (llvq_tile.h).  LLVQ_EUNSUPPORTED when the
+// shape does not fit (the one-block-per-lane kernels then run).
+int launch_decode_tile(const KDesc& k, const void* packed, const void* scales, int32_t out_kind, void* out,
+                       int32_t* err, hipStream_t s) {
+  if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;
+  const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
+  ELayout L;
+  const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0);
+  // per block: queue entry 8 B + scale 4 B + 24 value bytes
+  if (base + 64u + 36u * (uint32_t)k.kb > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((kLdsBudget - base - 64u) / 36u) & ~15;
+  if (tmax > kETileMax) tmax = kETileMax;
+  EArgs a;
+  int grid = 0;
+  a.rows_per_tile = pick_rows_per_tile(k.rows, k.kb, tmax, &a.ntiles, &grid);
+  if (a.rows_per_tile == 0) return LLVQ_EUNSUPPORTED;
+  a.nbuckets = nbuckets;
+  const int T = a.rows_per_tile * k.kb;
+  engine_layout_base(a.L, k.ncls, 1 << k.gain_bits, nbuckets, T);
+  a.xs = a.L.total;
+  a.xsum = 0;
+  const uint32_t total = a.xs + align16(24u * (uint32_t)T);
+  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  if (out_kind == LLVQ_OUT_POINTS_I8)
+    hipLaunchKernelGGL((k_decode_tile<LLVQ_OUT_POINTS_I8>), dim3(grid), dim3(kEThreads), total, s, k, a,
+                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), out, err);
+  else
+    hipLaunchKernelGGL((k_decode_tile<LLVQ_OUT_BF16>), dim3(grid), dim3(kEThreads), total, s, k, a,
+                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), out, err);
+  return launch_status();
+}
+
 template <int BATCH>
 int launch_gemv(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype, float* y,
                 int32_t* err, hipStream_t s) {
@@ -624,6 +631,37 @@ int launch_gemv(const KDesc& k, const void* packed, const void* scales, const vo
   return launch_status();
 }
 }  // namespace
+
+LLVQ_API int llvq_decode(const llvq_desc* d, const void* packed, const void* scales, int32_t out_kind,
+                         void* out, int32_t* err_count, void* stream) {
+  KDesc k;
+  int st = make_kdesc(d, &k);
+  if (st != LLVQ_OK) return st;
+  if (!packed || !out || !aligned(packed, 16)) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  if (out_kind == LLVQ_OUT_POINTS_I8) {
+    if (!aligned(out, 4)) return LLVQ_EINVAL;
+  } else if (out_kind == LLVQ_OUT_BF16) {
+    if (!scales || !aligned(out, 2) || !aligned(scales, 2)) return LLVQ_EINVAL;
+  } else {
+    return LLVQ_EINVAL;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int st1 = launch_decode_tile(k, packed, out_kind == LLVQ_OUT_BF16 ? scales : nullptr, out_kind, out,
+                                     err_count, s);
+  if (st1 != LLVQ_EUNSUPPORTED) return st1;
+  const uint64_t nblocks = (uint64_t)k.rows * (uint64_t)k.kb;
+  const unsigned block = 256;
+  if (out_kind == LLVQ_OUT_POINTS_I8) {
+    hipLaunchKernelGGL(k_decode_points, dim3(grid_for(nblocks, block)), dim3(block), 0, s, k,
+                       static_cast<const uint8_t*>(packed), static_cast<int8_t*>(out), err_count);
+    return launch_status();
+  }
+  hipLaunchKernelGGL(k_decode_bf16, dim3(grid_for(nblocks, block)), dim3(block), 0, s, k,
+                     static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales),
+                     static_cast<uint16_t*>(out), err_count);
+  return launch_status();
+}
 
 LLVQ_API int llvq_gemv(const llvq_desc* d, const void* packed, const void* scales, const void* x, int32_t x_dtype,
                        int32_t batch, float* y, int32_t* err_count, void* stream) {

@@ -297,7 +297,7 @@ __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L,
                  343 * 2, tid);
   lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.bucket),
                  reinterpret_cast<const uint32_t*>(dev_tables::kBucketTable[d.max_shell]), (nbuckets + 3) >> 2, tid);
-  if (d.mode == LLVQ_MODE_SHAPEGAIN) {
+  if (d.mode == LLVQ_MODE_SHAPEGAIN && scales != nullptr) {
     float* G = reinterpret_cast<float*>(smem + L.gains);
     for (int i = tid; i < (1 << d.gain_bits); i += kEThreads) G[i] = __half2float(scales[i]);
   }
@@ -305,9 +305,11 @@ __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L,
 
 // Classify unit u of a tile (kEUnit fields, 4 per lane): class search, queue append,
 // block scale.  Fields f of the tile are the consecutive fields j0 + f of the stream.
+// With zero_bytes set, an invalid block's 24 value bytes at zero_bytes + 24 f are set to
+// the bias (value 0) for consumers that read every block's bytes.
 __device__ __forceinline__ void classify_unit(uint8_t* smem, const ELayout& L, const KDesc& d,
                                               const uint8_t* __restrict__ packed, uint32_t j0, int T, int u, int lane,
-                                              int32_t* err) {
+                                              int32_t* err, uint8_t* zero_bytes = nullptr) {
   int* ctr = reinterpret_cast<int*>(smem + L.ctr);
   uint64_t* queue = reinterpret_cast<uint64_t*>(smem + L.queue);
   float* part = reinterpret_cast<float*>(smem + L.part);
@@ -350,6 +352,13 @@ __device__ __forceinline__ void classify_unit(uint8_t* smem, const ELayout& L, c
         part[f] = sg ? G[g] * h.invnorm : 1.0f;
       } else {
         part[f] = 0.0f;
+        if (zero_bytes) {
+          uint2* zb = reinterpret_cast<uint2*>(zero_bytes + 24u * (uint32_t)f);
+          const uint2 z = make_uint2(0x0c0c0c0cu, 0x0c0c0c0cu);
+          zb[0] = z;
+          zb[1] = z;
+          zb[2] = z;
+        }
         if (err) atomicAdd(err, 1);
       }
     }
