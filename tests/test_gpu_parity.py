@@ -218,7 +218,8 @@ def test_gemm_28672x8192_small_batch(batch):
 
 
 @pytest.mark.parametrize("rows,cols,batch,xd", [(1, 1, 1, "f32"), (3, 23, 2, "bf16"), (5, 25, 3, "f32"),
-                                                (70, 100, 1, "bf16"), (2, 24 * 65 + 7, 16, "bf16")])
+                                                (70, 100, 1, "bf16"), (2, 24 * 65 + 7, 16, "bf16"),
+                                                (37, 1001, 5, "bf16"), (17, 24 * 300 + 1, 9, "bf16")])
 def test_gemv_ragged_edges(rows, cols, batch, xd):
     t = synth.make_tensor("edge", 14, rows * 1000 + cols, rows, cols, C10, batch=batch, x_dtype=xd)
     check_gemv(t, list(range(rows)), f"edge {rows}x{cols} b{batch}")
@@ -235,8 +236,10 @@ def test_gemv_other_max_shells():
     for M in (2, 5, 8):
         C = leech.index_count(M)
         bits = max(1, (C - 1).bit_length())
-        t = synth.make_tensor(f"M{M}", 16, M, 33, 24 * 70 + 5, C, max_shell=M, shape_bits=bits, gain_bits=3)
-        check_gemv(t, list(range(t.rows)), f"max_shell {M} ({bits}+3 bit fields)")
+        for batch in (1, 3):
+            t = synth.make_tensor(f"M{M}", 16, M, 33, 24 * 70 + 5, C, max_shell=M, shape_bits=bits, gain_bits=3,
+                                  batch=batch)
+            check_gemv(t, list(range(t.rows)), f"max_shell {M} ({bits}+3 bit fields) batch {batch}")
 
 
 # ---------------------------------------------------------------------------

@@ -176,6 +176,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 #include "llvq_engine.h"
 #include "llvq_gemv_b1.h"
 #include "llvq_tile.h"
+#include "llvq_gemm.h"
 
 // ---------------------------------------------------------------------------
 // kernels
@@ -615,6 +616,39 @@ int launch_decode_tile(const KDesc& k, const void* packed, const void* scales, i
   return launch_status();
 }
 
+// Small-batch GEMM on matrix cores (llvq_gemm.h), bf16 activations, batch 2..16.
+// LLVQ_EUNSUPPORTED when the shape does not fit (the VALU kernel then runs).
+int launch_gemm_mfma(const KDesc& k, const void* packed, const void* scales, const void* x, int batch, float* y,
+                     int32_t* err, hipStream_t s) {
+  if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;
+  const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
+  ELayout L;
+  const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0);
+  const uint32_t red = (uint32_t)kEWaves * 64u * 4u * 4u;
+  // per block: queue entry 8 B + scale 4 B + 24 value bytes; at least one block column
+  if (base + red + 64u + 36u * kGRows > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((kLdsBudget - base - red - 64u) / 36u);
+  if (tmax > kETileMax) tmax = kETileMax;
+  const int wmax = tmax / kGRows;
+  GArgs g;
+  g.nchunk = (k.kb + wmax - 1) / wmax;
+  g.w = (k.kb + g.nchunk - 1) / g.nchunk;
+  g.ngroups = (k.rows + kGRows - 1) / kGRows;
+  g.batch = batch;
+  g.e.rows_per_tile = kGRows;
+  g.e.ntiles = g.ngroups;
+  g.e.nbuckets = nbuckets;
+  engine_layout_base(g.e.L, k.ncls, 1 << k.gain_bits, nbuckets, kGRows * g.w);
+  g.e.xs = g.e.L.total;
+  g.e.xsum = g.e.xs + align16(24u * (uint32_t)(kGRows * g.w));
+  const uint32_t total = g.e.xsum + red;
+  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  const int grid = g.ngroups < kGridMax ? g.ngroups : kGridMax;
+  hipLaunchKernelGGL(k_gemm_mfma, dim3(grid), dim3(kEThreads), total, s, k, g, static_cast<const uint8_t*>(packed),
+                     static_cast<const __half*>(scales), static_cast<const uint16_t*>(x), y, err);
+  return launch_status();
+}
+
 template <int BATCH>
 int launch_gemv(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype, float* y,
                 int32_t* err, hipStream_t s) {
@@ -683,6 +717,9 @@ LLVQ_API int llvq_gemv(const llvq_desc* d, const void* packed, const void* scale
   if (batch == 1) {
     const int st1 = launch_gemv_b1(k, packed, scales, x, x_dtype, y, err_count, s);
     if (st1 != LLVQ_EUNSUPPORTED) return st1;
+  } else if (x_dtype == LLVQ_X_BF16) {
+    const int st2 = launch_gemm_mfma(k, packed, scales, x, batch, y, err_count, s);
+    if (st2 != LLVQ_EUNSUPPORTED) return st2;
   }
   switch (batch) {
 #define LLVQ_GEMV_CASE(B) \

@@ -303,13 +303,27 @@ __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L,
   }
 }
 
+// Field index in the stream of tile block f.  A tile is nr rows of w blocks starting at
+// field j0 (row stride Kb fields); w == Kb makes the tile one contiguous run.
+struct TileMap {
+  uint32_t j0;      // stream index of the tile's first block
+  uint32_t w;       // blocks per tile row
+  uint32_t stride;  // stream fields per tensor row (Kb)
+  float inv_w;      // 1 / w
+  __device__ __forceinline__ uint32_t field(uint32_t f) const {
+    if (w == stride) return j0 + f;
+    const uint32_t rl = (uint32_t)(((float)f + 0.5f) * inv_w);
+    return j0 + rl * stride + (f - rl * w);
+  }
+};
+
 // Classify unit u of a tile (kEUnit fields, 4 per lane): class search, queue append,
-// block scale.  Fields f of the tile are the consecutive fields j0 + f of the stream.
+// block scale.
 // With zero_bytes set, an invalid block's 24 value bytes at zero_bytes + 24 f are set to
 // the bias (value 0) for consumers that read every block's bytes.
 __device__ __forceinline__ void classify_unit(uint8_t* smem, const ELayout& L, const KDesc& d,
-                                              const uint8_t* __restrict__ packed, uint32_t j0, int T, int u, int lane,
-                                              int32_t* err, uint8_t* zero_bytes = nullptr) {
+                                              const uint8_t* __restrict__ packed, const TileMap& tm, int T, int u,
+                                              int lane, int32_t* err, uint8_t* zero_bytes = nullptr) {
   int* ctr = reinterpret_cast<int*>(smem + L.ctr);
   uint64_t* queue = reinterpret_cast<uint64_t*>(smem + L.queue);
   float* part = reinterpret_cast<float*>(smem + L.part);
@@ -324,7 +338,7 @@ __device__ __forceinline__ void classify_unit(uint8_t* smem, const ELayout& L, c
     const int f = u * kEUnit + t * 64 + lane;
     flo[t] = 0u;
     fhi[t] = 0u;
-    if (f < T) field_words(packed, j0 + (uint32_t)f, d.field_bits, flo[t], fhi[t]);
+    if (f < T) field_words(packed, tm.field((uint32_t)f), d.field_bits, flo[t], fhi[t]);
   }
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll

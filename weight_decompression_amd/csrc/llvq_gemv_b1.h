@@ -162,7 +162,8 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
     __syncthreads();
 
     // ---- 1. classify: wave w takes unit w (T <= kEWaves * kEUnit)
-    if (wave * kEUnit < T) classify_unit(smem, L, d, packed, (uint32_t)(row0 * kb), T, wave, lane, err);
+    const TileMap tm = {(uint32_t)(row0 * kb), (uint32_t)kb, (uint32_t)kb, inv_kb};
+    if (wave * kEUnit < T) classify_unit(smem, L, d, packed, tm, T, wave, lane, err);
     __syncthreads();
     const int nodd = ctr[0];
     const int neven = ctr[1];

@@ -91,8 +91,9 @@ __global__ __launch_bounds__(kEThreads) void k_decode_tile(KDesc d, EArgs a, con
     const int T = nrows * kb;
     if (tid == 0) { ctr[0] = 0; ctr[1] = 0; ctr[2] = 0; }
     __syncthreads();
+    const TileMap tm = {(uint32_t)(row0 * kb), (uint32_t)kb, (uint32_t)kb, 1.0f / (float)kb};
     if (wave * kEUnit < T)
-      classify_unit(smem, L, d, packed, (uint32_t)(row0 * kb), T, wave, lane, err, smem + tb);
+      classify_unit(smem, L, d, packed, tm, T, wave, lane, err, smem + tb);
     __syncthreads();
     const int nodd = ctr[0];
     const int neven = ctr[1];
