@@ -5,6 +5,7 @@ fp64 oracle, normalised by sum_k |W_hat[r,k] x[k]|; indices bit-exact in the ran
 round trip.  Inputs are the seeded synthetic workloads of weight_decompression_amd/synth.py.
 """
 
+import ctypes
 import os
 
 import numpy as np
@@ -307,3 +308,46 @@ def test_rank_matches_oracle_and_flags_bad_points():
     wd.encode_ref(x10, 9, out9)
     torch.cuda.synchronize()
     assert int(out9.cpu().numpy().view(np.uint64)[0]) == (1 << 64) - 1
+
+
+def test_rank_perturbed_points_and_unaligned_input():
+    # valid points of every shell and small perturbations of them: the GPU rank must give
+    # the oracle's index exactly when the oracle says the point is in shells 2..10, and
+    # UINT64_MAX (counted) otherwise
+    rng = np.random.default_rng(21)
+    pts = []
+    for I in rng.integers(0, C10, size=600, dtype=np.uint64):
+        x = bijection.unrank(int(I), 10)
+        pts.append(list(x))
+        y = list(x)
+        i, j = rng.choice(24, size=2, replace=False)
+        d = int(rng.choice([-4, -2, 2, 4]))
+        y[i] += d
+        y[j] -= d
+        pts.append(y)
+        z = list(x)
+        z[int(rng.integers(24))] *= -1
+        pts.append(z)
+    pts = [[max(-128, min(127, v)) for v in x] for x in pts]
+    expect = []
+    for x in pts:
+        n2 = leech.norm2(x)
+        ok = leech.in_leech(x) and n2 % 16 == 0 and 2 <= n2 // 16 <= 10
+        expect.append(bijection.rank(x, 10) if ok else (1 << 64) - 1)
+    nbad = sum(1 for e in expect if e == (1 << 64) - 1)
+    assert 0 < nbad < len(pts)
+    arr = np.array(pts, dtype=np.int8)
+    for offset in (0, 1):
+        buf = torch.zeros(arr.size + 8, dtype=torch.int8, device="cuda")
+        view = buf[offset:offset + arr.size]
+        view.copy_(torch.from_numpy(arr.ravel()).cuda())
+        say(f"rank: {len(pts)} points, byte offset {offset}")
+        out = torch.empty(len(pts), dtype=torch.int64, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        wd.load_library().llvq_encode_ref(ctypes.c_void_p(view.data_ptr()), len(pts), 10,
+                                           ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(err.data_ptr()),
+                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        got = [int(v) for v in out.cpu().numpy().view(np.uint64)]
+        assert got == expect
+        assert int(err.item()) == nbad

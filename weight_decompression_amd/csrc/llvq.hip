@@ -298,150 +298,7 @@ __global__ __launch_bounds__(256) void k_gemv(KDesc d, const uint8_t* __restrict
   }
 }
 
-// multiset helpers for the rank kernel -------------------------------------------------
-
-__device__ __forceinline__ uint64_t arrangements_u64(const int cnt[4]) {
-  // multinomial via successive binomials, all values < 2^32 for the classes used
-  uint64_t q = 1;
-  int n = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    for (int t = 1; t <= cnt[j]; ++t) {
-      ++n;
-      q = q * (uint64_t)n / (uint64_t)t;
-    }
-  }
-  return q;
-}
-
-// lexicographic rank of the sequence of value indices idx[0..len-1]
-__device__ __forceinline__ uint64_t lex_rank(const int* idx, int len, int cnt[4]) {
-  uint64_t q = arrangements_u64(cnt);
-  uint64_t rank = 0;
-  for (int i = 0; i < len; ++i) {
-    const int n = len - i;
-    const int a = idx[i];
-    for (int j = 0; j < a; ++j) rank += q * (uint64_t)cnt[j] / (uint64_t)n;
-    q = q * (uint64_t)cnt[a] / (uint64_t)n;
-    cnt[a] -= 1;
-  }
-  return rank;
-}
-
-__device__ __forceinline__ int index_of_value(uint32_t vals, int d, int a) {
-  for (int j = 0; j < d; ++j)
-    if ((int)((vals >> (8 * j)) & 0xffu) == a) return j;
-  return -1;
-}
-
-__device__ uint64_t rank_point(const int x[kDim], int max_shell, int ncls) {
-  const uint64_t bad = ~0ull;
-  const int p = x[0] & 1;
-  int sum = 0, norm = 0;
-  uint32_t mask = 0;
-  for (int i = 0; i < kDim; ++i) {
-    if ((x[i] & 1) != p) return bad;
-    sum += x[i];
-    norm += x[i] * x[i];
-    if ((x[i] & 3) == (p ? 1 : 2)) mask |= 1u << i;
-  }
-  if (((sum - 4 * p) & 7) != 0) return bad;
-  if (norm % 16) return bad;
-  const int m = norm / 16;
-  if (m < 2 || m > max_shell) return bad;
-  // codeword position: binary search inside the slice of its weight (T sorted by weight, mask)
-  const int wt = __popc(mask);
-  int lo = 0, hi = 4095;
-  {
-    // weight slices 0:[0], 8:[1,759], 12:[760,3335], 16:[3336,4094], 24:[4095]
-    if (wt == 0) { lo = 0; hi = 0; }
-    else if (wt == 8) { lo = 1; hi = 759; }
-    else if (wt == 12) { lo = 760; hi = 3335; }
-    else if (wt == 16) { lo = 3336; hi = 4094; }
-    else if (wt == 24) { lo = 4095; hi = 4095; }
-    else return bad;
-  }
-  int pos = -1;
-  while (lo <= hi) {
-    const int mid = (lo + hi) >> 1;
-    const uint32_t cm = dev_tables::kGolayTable[mid];
-    if (cm == mask) { pos = mid; break; }
-    if (cm < mask) lo = mid + 1; else hi = mid - 1;
-  }
-  if (pos < 0) return bad;
-  // histogram of absolute values
-  int hist[13];
-  for (int a = 0; a < 13; ++a) hist[a] = 0;
-  for (int i = 0; i < kDim; ++i) {
-    const int a = x[i] < 0 ? -x[i] : x[i];
-    if (a > 12) return bad;
-    hist[a]++;
-  }
-  int nd = 0;
-  for (int a = 0; a < 13; ++a) nd += hist[a] != 0;
-  int k = -1;
-  for (int kk = 0; kk < ncls; ++kk) {
-    const LlvqClassRec& cr = dev_tables::kClassTable[kk];
-    if (cr.m != m || cr.parity != p || cr.d_s + cr.d_t != nd) continue;
-    bool ok = true;
-    for (int j = 0; j < cr.d_s && ok; ++j)
-      ok = hist[(cr.vals_s >> (8 * j)) & 0xffu] == (int)((cr.cnt_s >> (8 * j)) & 0xffu);
-    for (int j = 0; j < cr.d_t && ok; ++j)
-      ok = hist[(cr.vals_t >> (8 * j)) & 0xffu] == (int)((cr.cnt_t >> (8 * j)) & 0xffu);
-    if (ok) { k = kk; break; }
-  }
-  if (k < 0) return bad;
-  const LlvqClassRec& cr = dev_tables::kClassTable[k];
-  const uint32_t r = (uint32_t)pos - cr.toff;
-  uint64_t R;
-  uint32_t s = 0;
-  if (p) {
-    int idx[kDim];
-    int cnt[4] = {0, 0, 0, 0};
-    for (int j = 0; j < cr.d_t; ++j) cnt[j] = (int)((cr.cnt_t >> (8 * j)) & 0xffu);
-    for (int i = 0; i < kDim; ++i) idx[i] = index_of_value(cr.vals_t, cr.d_t, x[i] < 0 ? -x[i] : x[i]);
-    R = lex_rank(idx, kDim, cnt);
-  } else {
-    int idxS[kDim], idxT[kDim];
-    int nS = 0, nT = 0;
-    for (int i = 0; i < kDim; ++i) {
-      const int a = x[i] < 0 ? -x[i] : x[i];
-      if ((mask >> i) & 1u) idxS[nS++] = index_of_value(cr.vals_s, cr.d_s, a);
-      else idxT[nT++] = index_of_value(cr.vals_t, cr.d_t, a);
-    }
-    int cntS[4] = {0, 0, 0, 0}, cntT[4] = {0, 0, 0, 0};
-    for (int j = 0; j < cr.d_s; ++j) cntS[j] = (int)((cr.cnt_s >> (8 * j)) & 0xffu);
-    for (int j = 0; j < cr.d_t; ++j) cntT[j] = (int)((cr.cnt_t >> (8 * j)) & 0xffu);
-    const uint64_t rS = lex_rank(idxS, nS, cntS);
-    const uint64_t rT = lex_rank(idxT, nT, cntT);
-    R = rS * (uint64_t)cr.p_t + rT;
-    const int q = cr.w ? (31 - __clz((int)mask)) : -1;
-    int j = 0;
-    for (int i = 0; i < kDim; ++i) {
-      if (!((mask >> i) & 1u) || i == q) continue;
-      if (x[i] < 0) s |= 1u << j;
-      ++j;
-    }
-    for (int i = 0; i < kDim; ++i) {
-      if (((mask >> i) & 1u) || x[i] == 0) continue;
-      if (x[i] < 0) s |= 1u << j;
-      ++j;
-    }
-  }
-  return cr.start + (uint64_t)r + (uint64_t)cr.A * ((uint64_t)s + (R << cr.B));
-}
-
-__global__ __launch_bounds__(256) void k_rank(const int8_t* __restrict__ pts, int64_t n, int max_shell, int ncls,
-                                               uint64_t* __restrict__ out, int32_t* err) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += stride) {
-    int x[kDim];
-    for (int i = 0; i < kDim; ++i) x[i] = pts[t * kDim + i];
-    const uint64_t I = rank_point(x, max_shell, ncls);
-    out[t] = I;
-    if (I == ~0ull && err) atomicAdd(err, 1);
-  }
-}
+#include "llvq_rank.h"
 
 // ---------------------------------------------------------------------------
 // host side
@@ -742,8 +599,11 @@ LLVQ_API int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell,
   if (!points || !indices || !aligned(indices, 8)) return LLVQ_EINVAL;
   if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
   const unsigned block = 256;
-  hipLaunchKernelGGL(k_rank, dim3(grid_for((uint64_t)n, block)), dim3(block), 0,
-                     reinterpret_cast<hipStream_t>(stream), points, n, max_shell,
-                     host_tables::kNumClassesUpTo[max_shell], indices, err_count);
+  if (aligned(points, 8))
+    hipLaunchKernelGGL((k_rank<true>), dim3(grid_for((uint64_t)n, block)), dim3(block), 0,
+                       reinterpret_cast<hipStream_t>(stream), points, n, max_shell, indices, err_count);
+  else
+    hipLaunchKernelGGL((k_rank<false>), dim3(grid_for((uint64_t)n, block)), dim3(block), 0,
+                       reinterpret_cast<hipStream_t>(stream), points, n, max_shell, indices, err_count);
   return launch_status();
 }

@@ -58,3 +58,18 @@ struct LlvqTailComp {
   float q_over_6;    // arrangements of the composition / 6
   uint32_t offset;   // first entry of the composition's group in the tail table
 };
+
+// Class record of the rank (point -> index) kernel.
+struct LlvqClassRank {
+  uint64_t start;    // first global shape index of the class
+  double p_s;        // arrangements of the support values (even classes; 1 for odd)
+  double p_t;        // arrangements of the complement values (odd classes: all 24 values)
+  uint32_t A;        // codewords the index r ranges over
+  uint32_t toff;     // position in the sorted Golay table of codeword r = 0
+  uint32_t key;      // s1 | s3 << 6 | s4 << 17, s_k = sum of |x_i|^k
+  uint32_t slot_lo;  // slot of absolute value a in its part, byte (a >> 1), a >> 1 = 0..3
+  uint32_t slot_hi;  //   ... a >> 1 = 4..7; 0x80 = value not in the class
+  uint32_t cnt_s;    // counts of the support slots (even classes), one per byte
+  uint32_t cnt_t;    // counts of the complement slots (odd classes: all values)
+  uint32_t meta;     // B | w << 8 | pi << 16 | parity << 17 | m << 20
+};

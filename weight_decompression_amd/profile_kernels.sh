@@ -1,0 +1,35 @@
+#!/bin/bash
+# rocprofv3 profile of one bench.py workload on one GPU.
+# Usage (from the repository root, on a machine with the GPU):
+#   bash weight_decompression_amd/profile_kernels.sh OUTDIR "BENCH ARGS" KERNEL:UNITS:ALG_BYTES [...]
+# Runs, each in its own rocprofv3 process:
+#   trace          kernel trace + stats of `bench.py BENCH ARGS`
+#   pmc_valu       SQ counters (VALU / LDS / SALU instructions, wave cycles)
+#   pmc_fetch      FETCH_SIZE;  pmc_write  WRITE_SIZE
+#   copy_fetch, copy_write   the same two counters over a plain 256 MiB device copy
+# then writes OUTDIR/summary.md with one section per KERNEL (a substring of the kernel
+# name), UNITS its work units per launch (24-blocks or points) and ALG_BYTES its
+# algorithmic HBM bytes per launch.
+set -o pipefail
+OUT="$(cd "$(dirname "$1")" && pwd)/$(basename "$1")"
+ARGS="$2"
+shift 2
+REPO="$(cd "$(dirname "$0")/.." && pwd)"
+mkdir -p "$OUT"
+cd /tmp && export TMPDIR=/tmp
+run() { echo "== $1 $(date +%T)"; shift; "$@" || exit $?; }
+run trace timeout -k 10 600 rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/trace" -o run -- \
+  python3 "$REPO/bench.py" --no-cpu $ARGS
+run valu timeout -s KILL 300 rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_WAVES SQ_ACTIVE_INST_VALU \
+  SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_INSTS_MFMA --output-format csv -d "$OUT/pmc_valu" -o pmc -- \
+  python3 "$REPO/bench.py" --no-cpu $ARGS
+run fetch timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/pmc_fetch" -o pmc -- \
+  python3 "$REPO/bench.py" --no-cpu $ARGS
+run write timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/pmc_write" -o pmc -- \
+  python3 "$REPO/bench.py" --no-cpu $ARGS
+run copy_fetch timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/copy_fetch" -o pmc -- \
+  python3 "$REPO/bench.py" --copy-calibration 256
+run copy_write timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/copy_write" -o pmc -- \
+  python3 "$REPO/bench.py" --copy-calibration 256
+cd "$REPO" && python3 -m weight_decompression_amd.profile_summary "$OUT" "$ARGS" "$@" > "$OUT/summary.md" || exit $?
+echo "profile done"
