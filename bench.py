@@ -46,12 +46,36 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "0e2b6c48e4dcb0ff5557a159e8798ae3c7a549e4419e51c49a553d867f38e1e4",
-        "summary": "profiles/k_gemv_b1_4096x11008_bf16_batch1.md",
-        "unit_of_work": "24-weight block",
-        "valu_lane_ops_per_unit": 778.9,       # SQ_INSTS_VALU * 64 / blocks
-        "fetch_bytes_per_launch": 12212254,    # FETCH_SIZE scaled by the copy-kernel calibration (x 1.9998)
-        "write_bytes_per_launch": 32768,       # WRITE_SIZE (x 1.0000)
+        "source_sha256": "b777b4c7c9c43121aa40c63c053e6578d071102fa8372f8ce77793cac7e71241",
+        "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
+        "unit_of_work": "24-weight block (k_gemv_b1)",
+        "valu_lane_ops_per_unit": 749.2,       # SQ_INSTS_VALU * 64 / blocks
+        "fetch_bytes_per_launch": 12151700,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
+    },
+    "gemv_28672x8192_b16": {
+        "source_sha256": "b777b4c7c9c43121aa40c63c053e6578d071102fa8372f8ce77793cac7e71241",
+        "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
+        "unit_of_work": "24-weight block (k_gemm_mfma)",
+        "valu_lane_ops_per_unit": 881.9,
+        "fetch_bytes_per_launch": 61689184,
+        "write_bytes_per_launch": 1835008,
+    },
+    "decode_bf16": {
+        "source_sha256": "b777b4c7c9c43121aa40c63c053e6578d071102fa8372f8ce77793cac7e71241",
+        "summary": "profiles/decode_bf16_7b_layer_k_decode_tile.md",
+        "unit_of_work": "24-weight block (k_decode_tile<bf16>)",
+        "valu_lane_ops_per_unit": 796.0,
+        "fetch_bytes_per_launch": None,        # per-launch figures of a mixed-shape layer; see the summary
+        "write_bytes_per_launch": None,
+    },
+    "roundtrip": {
+        "source_sha256": "b777b4c7c9c43121aa40c63c053e6578d071102fa8372f8ce77793cac7e71241",
+        "summary": "profiles/roundtrip_1e7_k_decode_tile_k_rank.md",
+        "unit_of_work": "point: decode to int8 (682.8) + rank (1348.6)",
+        "valu_lane_ops_per_unit": 2031.4,
+        "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
+        "write_bytes_per_launch": None,
     },
 }
 

@@ -47,7 +47,8 @@ def summarise(outdir, bench_args, specs):
     lines = ["# rocprofv3 summary: bench.py " + bench_args, ""]
     lines.append("Command (from the repository root):")
     lines.append("")
-    lines.append(f"    bash weight_decompression_amd/profile_kernels.sh OUTDIR \"{bench_args}\" " + " ".join(specs))
+    lines.append(f"    bash weight_decompression_amd/profile_kernels.sh OUTDIR \"{bench_args}\" " +
+                 " ".join(f"'{s}'" for s in specs))
     lines.append("")
     with open(os.path.join(outdir, "trace", "run_kernel_stats.csv")) as f:
         stats = list(csv.DictReader(f))
