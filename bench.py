@@ -332,7 +332,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--cpu-rows", type=int, default=192)
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows of the tensor the CPU oracle is timed on")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", choices=WORKLOADS, default=DEFAULT_WORKLOAD,
                     help="default: the 4096x11008 batch-1 GEMV (the headline line)")
