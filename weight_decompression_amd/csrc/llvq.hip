@@ -415,19 +415,19 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;   // 32-bit field index
   const bool xf32 = x_dtype == LLVQ_X_F32;
   const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
-  // LDS: fixed tables + one tile buffer of 12 bytes per block + x + xsum
+  // LDS: fixed tables + two tile buffers of 12 bytes per block (+ counters) + x + xsum
   ELayout L;
-  const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0);
+  const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 2);
   const uint32_t xbytes = align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u)) + align16((uint32_t)k.kb * 4u);
-  if (base + xbytes + 12u * (uint32_t)k.kb > kLdsBudget) return LLVQ_EUNSUPPORTED;
-  int tmax = (int)((kLdsBudget - base - xbytes) / 12u) & ~15;
+  if (base + xbytes + 64u + 24u * (uint32_t)k.kb > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((kLdsBudget - base - xbytes - 64u) / 24u) & ~15;
   if (tmax > kETileMax) tmax = kETileMax;
   EArgs a;
   int grid = 0;
   a.rows_per_tile = pick_rows_per_tile(k.rows, k.kb, tmax, &a.ntiles, &grid);
   if (a.rows_per_tile == 0) return LLVQ_EUNSUPPORTED;
   a.nbuckets = nbuckets;
-  engine_layout_base(a.L, k.ncls, 1 << k.gain_bits, nbuckets, a.rows_per_tile * k.kb);
+  engine_layout_base(a.L, k.ncls, 1 << k.gain_bits, nbuckets, a.rows_per_tile * k.kb, 2);
   a.xs = a.L.total;
   a.xsum = a.xs + align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u));
   const uint32_t total = a.xsum + align16((uint32_t)k.kb * 4u);

@@ -35,6 +35,13 @@ constexpr int kTail = 6;            // values resolved by the tail table
 constexpr int kSteps = 24 - kTail;  // values resolved step by step
 constexpr int kFStride = 25;        // F[n][c] row length (c = 0..24)
 
+// One tile's queues and block slots.
+struct TileBuf {
+  uint32_t ctr;       // int[2]: odd queue fill, even queue fill
+  uint32_t queue;     // uint64[tmax]: I | f << 44 | class << 56
+  uint32_t part;      // float[tmax]: block scale, then the block's result
+};
+
 struct ELayout {
   // byte offsets inside the dynamic LDS segment
   uint32_t ftab;      // double F[25][25]: F[n][c] = n / c   (offset 0)
@@ -43,15 +50,15 @@ struct ELayout {
   uint32_t bucket;    // uint8[nbuckets]
   uint32_t tail;      // uint16[4096]
   uint32_t tcomp;     // LlvqTailComp[343]
-  uint32_t ctr;       // int[4]: odd queue fill, even queue fill, next chunk
-  uint32_t queue;     // uint64[tmax]: I | f << 44 | class << 56
-  uint32_t part;      // float[tmax]: block scale, then the block's result
+  uint32_t work;      // int[4]: work-item counter of the current phase
+  TileBuf buf[2];     // one or two tile buffers
   uint32_t total;     // end of the engine's part; consumer data follows
 };
 
 __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
 
-__host__ __device__ inline uint32_t engine_layout_base(ELayout& L, int ncls, int ngains, int nbuckets, int tmax) {
+__host__ __device__ inline uint32_t engine_layout_base(ELayout& L, int ncls, int ngains, int nbuckets, int tmax,
+                                                      int nbuf = 1) {
   uint32_t o = 0;
   L.ftab = o;     o = align16(o + 25u * kFStride * 8u);
   L.cls = o;      o = align16(o + (uint32_t)ncls * (uint32_t)sizeof(LlvqClassHot));
@@ -59,9 +66,16 @@ __host__ __device__ inline uint32_t engine_layout_base(ELayout& L, int ncls, int
   L.bucket = o;   o = align16(o + (uint32_t)nbuckets);
   L.tail = o;     o = align16(o + 4096u * 2u);
   L.tcomp = o;    o = align16(o + 343u * (uint32_t)sizeof(LlvqTailComp));
-  L.ctr = o;      o = align16(o + 16u);
-  L.queue = o;    o = align16(o + (uint32_t)tmax * 8u);
-  L.part = o;     o = align16(o + (uint32_t)tmax * 4u);
+  L.work = o;     o = align16(o + 16u);
+  for (int b = 0; b < 2; ++b) {
+    if (b < nbuf) {
+      L.buf[b].ctr = o;    o = align16(o + 16u);
+      L.buf[b].queue = o;  o = align16(o + (uint32_t)tmax * 8u);
+      L.buf[b].part = o;   o = align16(o + (uint32_t)tmax * 4u);
+    } else {
+      L.buf[b] = L.buf[0];
+    }
+  }
   L.total = o;
   return o;
 }
@@ -89,6 +103,13 @@ __device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) 
 __device__ __forceinline__ uint32_t bcnt_add(uint32_t a, uint32_t c) {
   uint32_t d;
   asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(d) : "v"(a), "s"(c));
+  return d;
+}
+
+// (a << 8) | 1: the one-hot count decrement (a - this) of a SWAR slot choice a.
+__device__ __forceinline__ uint32_t shl8_or1(uint32_t a) {
+  uint32_t d;
+  asm("v_lshl_or_b32 %0, %1, 8, 1" : "=v"(d) : "v"(a));
   return d;
 }
 
@@ -159,13 +180,13 @@ __device__ __forceinline__ uint32_t tail_codes(const uint8_t* smem, const ELayou
 // follows from the codeword bit and the value mod 4, folded into one byte-table lookup.
 struct OddDec {
   double y;
-  uint32_t nc, cnt, notc, svlo, svhi, codes;
+  uint32_t nc, cnt, notc4, svlo, svhi, codes;
 
   __device__ __forceinline__ void init(const LlvqClassHot& h, const BlockStart& bs) {
     y = bs.y;
     nc = h.nc0;
     cnt = h.cnt0;
-    notc = ~bs.c;
+    notc4 = ~bs.c << 2;   // bit p + 2 = position p is off the codeword
     svlo = h.sv0lo;
     svhi = h.sv0hi;
     codes = 0u;
@@ -182,14 +203,14 @@ struct OddDec {
       const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
       const double fac = F[(23 - p) * kFStride + ck];
       y = (y - (double)Ck) * fac;
-      cnt -= ((g << 8) | 1u) - g;
+      cnt = (cnt + g) - shl8_or1(g);   // one count down in slot k
       nc += g ^ 0x010101u;
       if (p == kSteps - 1) codes = tail_codes(smem, L, cnt, y);
     } else {
       k = __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | 0x0c0c0c00u;
     }
-    const uint32_t sel = lshl_add(__builtin_amdgcn_ubfe(notc, p, 1), 2, k);
-    return __builtin_amdgcn_perm(svhi, svlo, sel);
+    // selector byte 4..7 picks the negated entry
+    return __builtin_amdgcn_perm(svhi, svlo, k + ((notc4 >> p) & 4u));
   }
 };
 
@@ -243,7 +264,7 @@ struct EvenDec {
       const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
       const double fac = *reinterpret_cast<const double*>(smem + L.ftab + nb + (ck << 3));
       y = (y - (double)Ck) * fac;
-      cnt -= ((g << 8) | 1u) - g;
+      cnt = (cnt + g) - shl8_or1(g);
       nc += g ^ 0x010101u;
       // the last support step (i = w - 1) hands over to the complement: n' = 24 - w
       if (i == 6 || i == 10 || i == 14)
@@ -317,77 +338,123 @@ struct TileMap {
   }
 };
 
-// Classify unit u of a tile (kEUnit fields, 4 per lane): class search, queue append,
-// block scale.
+// Fields of classify unit u of a tile, 4 per lane (f = 256 u + 64 t + lane); fields past
+// the tile read as zero.
+struct UnitFields {
+  uint32_t lo[kEUnit / 64], hi[kEUnit / 64];
+};
+
+__device__ __forceinline__ UnitFields load_unit(const KDesc& d, const uint8_t* __restrict__ packed,
+                                                const TileMap& tm, int T, int u, int lane) {
+  UnitFields uf;
+#pragma unroll
+  for (int t = 0; t < kEUnit / 64; ++t) {
+    const int f = u * kEUnit + t * 64 + lane;
+    uf.lo[t] = 0u;
+    uf.hi[t] = 0u;
+    if (f < T) field_words(packed, tm.field((uint32_t)f), d.field_bits, uf.lo[t], uf.hi[t]);
+  }
+  return uf;
+}
+
+// Classify the loaded unit: class search, block scale, queue append.  The four fields of
+// a lane are searched together (independent LDS reads), the bucket's first two class
+// boundaries are tested at once (a longer scan is rare), and one queue reservation per
+// parity covers the whole unit.
 // With zero_bytes set, an invalid block's 24 value bytes at zero_bytes + 24 f are set to
 // the bias (value 0) for consumers that read every block's bytes.
-__device__ __forceinline__ void classify_unit(uint8_t* smem, const ELayout& L, const KDesc& d,
-                                              const uint8_t* __restrict__ packed, const TileMap& tm, int T, int u,
-                                              int lane, int32_t* err, uint8_t* zero_bytes = nullptr) {
-  int* ctr = reinterpret_cast<int*>(smem + L.ctr);
-  uint64_t* queue = reinterpret_cast<uint64_t*>(smem + L.queue);
-  float* part = reinterpret_cast<float*>(smem + L.part);
+__device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L, const TileBuf& tb, const KDesc& d,
+                                                const UnitFields& uf, int T, int u, int lane, int32_t* err,
+                                                uint8_t* zero_bytes = nullptr) {
+  int* ctr = reinterpret_cast<int*>(smem + tb.ctr);
+  uint64_t* queue = reinterpret_cast<uint64_t*>(smem + tb.queue);
+  float* part = reinterpret_cast<float*>(smem + tb.part);
   const LlvqClassHot* cls = reinterpret_cast<const LlvqClassHot*>(smem + L.cls);
   const float* G = reinterpret_cast<const float*>(smem + L.gains);
   const uint8_t* bk = smem + L.bucket;
   const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
   constexpr int kPer = kEUnit / 64;
-  uint32_t flo[kPer], fhi[kPer];
+  const int ncls = d.ncls;
+  bool valid[kPer], odd[kPer];
+  uint64_t entry[kPer];
+  uint32_t kk[kPer];
+  double Id[kPer];
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
     const int f = u * kEUnit + t * 64 + lane;
-    flo[t] = 0u;
-    fhi[t] = 0u;
-    if (f < T) field_words(packed, tm.field((uint32_t)f), d.field_bits, flo[t], fhi[t]);
+    const uint32_t ilo = uf.lo[t] & d.shape_mask_lo;
+    const uint32_t ihi = uf.hi[t] & d.shape_mask_hi;
+    const uint64_t I = ((uint64_t)ihi << 32) | ilo;
+    valid[t] = f < T && I < d.index_count;
+    entry[t] = I | ((uint64_t)(uint32_t)f << 44);
+    Id[t] = __builtin_fma((double)ihi, 4294967296.0, (double)ilo);
+    const uint32_t bidx = d.bshift >= 32 ? (ihi >> (d.bshift - 32)) : __builtin_amdgcn_alignbit(ihi, ilo, d.bshift);
+    kk[t] = valid[t] ? (uint32_t)bk[bidx] : 0u;
   }
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    uint32_t k = kk[t];
+    if (valid[t]) {
+      const bool c1 = (int)k + 1 < ncls && Id[t] >= cls[k + 1].start;
+      const bool c2 = (int)k + 2 < ncls && Id[t] >= cls[k + 2].start;
+      k += (uint32_t)c1 + (uint32_t)(c1 && c2);
+      if (c1 && c2)
+        while ((int)k + 1 < ncls && Id[t] >= cls[k + 1].start) ++k;
+    }
+    kk[t] = k;
+  }
+  int no = 0, ne = 0;
+  uint64_t bo[kPer], be[kPer];
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    const int f = u * kEUnit + t * 64 + lane;
+    odd[t] = false;
+    if (valid[t]) {
+      const LlvqClassHot& h = cls[kk[t]];
+      odd[t] = ((h.meta >> 17) & 1u) != 0u;
+      entry[t] |= (uint64_t)kk[t] << 56;
+      const uint32_t gsh = d.shape_bits >= 32 ? (uf.hi[t] >> (d.shape_bits - 32))
+                                              : __builtin_amdgcn_alignbit(uf.hi[t], uf.lo[t], d.shape_bits);
+      const uint32_t g = gsh & ((1u << d.gain_bits) - 1u);
+      part[f] = sg ? G[g] * h.invnorm : 1.0f;
+    } else if (f < T) {
+      part[f] = 0.0f;
+      if (zero_bytes) {
+        uint2* zb = reinterpret_cast<uint2*>(zero_bytes + 24u * (uint32_t)f);
+        const uint2 z = make_uint2(0x0c0c0c0cu, 0x0c0c0c0cu);
+        zb[0] = z;
+        zb[1] = z;
+        zb[2] = z;
+      }
+      if (err) atomicAdd(err, 1);
+    }
+    bo[t] = __ballot(valid[t] && odd[t]);
+    be[t] = __ballot(valid[t] && !odd[t]);
+    no += __popcll(bo[t]);
+    ne += __popcll(be[t]);
+  }
+  int baseo = 0, basee = 0;
+  if (lane == 0) {
+    baseo = atomicAdd(&ctr[0], no);
+    basee = atomicAdd(&ctr[1], ne);
+  }
+  baseo = __builtin_amdgcn_readfirstlane(baseo);
+  basee = __builtin_amdgcn_readfirstlane(basee);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
-    const int f = u * kEUnit + t * 64 + lane;
-    if (u * kEUnit + t * 64 >= T) break;
-    bool valid = false, odd = false;
-    uint64_t entry = 0;
-    if (f < T) {
-      const uint32_t ilo = flo[t] & d.shape_mask_lo;
-      const uint32_t ihi = fhi[t] & d.shape_mask_hi;
-      const uint64_t I = ((uint64_t)ihi << 32) | ilo;
-      if (I < d.index_count) {
-        valid = true;
-        const double Id = __builtin_fma((double)ihi, 4294967296.0, (double)ilo);
-        const uint32_t bidx = d.bshift >= 32 ? (ihi >> (d.bshift - 32)) : __builtin_amdgcn_alignbit(ihi, ilo, d.bshift);
-        uint32_t k = bk[bidx];
-        while ((int)k + 1 < d.ncls && Id >= cls[k + 1].start) ++k;
-        const LlvqClassHot& h = cls[k];
-        odd = ((h.meta >> 17) & 1u) != 0u;
-        entry = I | ((uint64_t)f << 44) | ((uint64_t)k << 56);
-        const uint32_t gsh = d.shape_bits >= 32 ? (fhi[t] >> (d.shape_bits - 32))
-                                                : __builtin_amdgcn_alignbit(fhi[t], flo[t], d.shape_bits);
-        const uint32_t g = gsh & ((1u << d.gain_bits) - 1u);
-        part[f] = sg ? G[g] * h.invnorm : 1.0f;
-      } else {
-        part[f] = 0.0f;
-        if (zero_bytes) {
-          uint2* zb = reinterpret_cast<uint2*>(zero_bytes + 24u * (uint32_t)f);
-          const uint2 z = make_uint2(0x0c0c0c0cu, 0x0c0c0c0cu);
-          zb[0] = z;
-          zb[1] = z;
-          zb[2] = z;
-        }
-        if (err) atomicAdd(err, 1);
-      }
-    }
-    const uint64_t bo = __ballot(valid && odd);
-    const uint64_t be = __ballot(valid && !odd);
-    int baseo = 0, basee = 0;
-    if (lane == 0) {
-      baseo = atomicAdd(&ctr[0], __popcll(bo));
-      basee = atomicAdd(&ctr[1], __popcll(be));
-    }
-    baseo = __builtin_amdgcn_readfirstlane(baseo);
-    basee = __builtin_amdgcn_readfirstlane(basee);
-    if (valid && odd) queue[baseo + __popcll(bo & below)] = entry;
-    if (valid && !odd) queue[T - 1 - (basee + __popcll(be & below))] = entry;
+    if (valid[t] && odd[t]) queue[baseo + __popcll(bo[t] & below)] = entry[t];
+    if (valid[t] && !odd[t]) queue[T - 1 - (basee + __popcll(be[t] & below))] = entry[t];
+    baseo += __popcll(bo[t]);
+    basee += __popcll(be[t]);
   }
+}
+
+__device__ __forceinline__ void classify_unit(uint8_t* smem, const ELayout& L, const TileBuf& tb, const KDesc& d,
+                                              const uint8_t* __restrict__ packed, const TileMap& tm, int T, int u,
+                                              int lane, int32_t* err, uint8_t* zero_bytes = nullptr) {
+  const UnitFields uf = load_unit(d, packed, tm, T, u, lane);
+  classify_fields(smem, L, tb, d, uf, T, u, lane, err, zero_bytes);
 }
 
 // Entry fields

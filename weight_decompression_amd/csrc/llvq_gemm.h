@@ -56,8 +56,9 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
   const bool xa16 = ((((uintptr_t)x) & 15u) == 0u) && ((K & 7) == 0);
 
   engine_prologue(smem, L, d, g.e.nbuckets, scales, tid);
-  int* ctr = reinterpret_cast<int*>(smem + L.ctr);
-  const float* part = reinterpret_cast<const float*>(smem + L.part);
+  int* ctr = reinterpret_cast<int*>(smem + L.buf[0].ctr);
+  int* work = reinterpret_cast<int*>(smem + L.work);
+  const float* part = reinterpret_cast<const float*>(smem + L.buf[0].part);
 
   // lane roles in the MFMA: A row / B column = lane % 16, k group = lane / 16
   const int mr = lane & 15;
@@ -71,10 +72,10 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
       const int b0 = cc * g.w;
       const int w = min(g.w, kb - b0);
       const int T = nrows * w;
-      if (tid == 0) { ctr[0] = 0; ctr[1] = 0; ctr[2] = 0; }
+      if (tid == 0) { ctr[0] = 0; ctr[1] = 0; work[0] = 0; }
       __syncthreads();
       const TileMap tm = {(uint32_t)(row0 * kb + b0), (uint32_t)w, (uint32_t)kb, 1.0f / (float)w};
-      if (wave * kEUnit < T) classify_unit(smem, L, d, packed, tm, T, wave, lane, err, smem + tb);
+      if (wave * kEUnit < T) classify_unit(smem, L, L.buf[0], d, packed, tm, T, wave, lane, err, smem + tb);
       __syncthreads();
       const int nodd = ctr[0];
       const int neven = ctr[1];
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
       const int nch = nco + ((neven + 63) >> 6);
       for (;;) {
         int c = 0;
-        if (lane == 0) c = atomicAdd(&ctr[2], 1);
+        if (lane == 0) c = atomicAdd(&work[0], 1);
         c = __builtin_amdgcn_readfirstlane(c);
         if (c >= nch) break;
         bytes_chunk(smem, L, tb, T, c, nco, nodd, neven, lane);

@@ -48,13 +48,13 @@ __device__ __forceinline__ uint32_t block_col(uint32_t f, float inv_kb, uint32_t
 // One decode chunk: 64 consecutive entries of one parity queue (chunks 0..nco-1 are the
 // odd queue, the rest the even queue), one block per lane.  Result: part[f] *= dot.
 template <bool XF32>
-__device__ __forceinline__ void gemv_chunk(uint8_t* smem, const EArgs& a, int T, uint32_t kb, float inv_kb, int c,
-                                           int nco, int nodd, int neven, int lane) {
+__device__ __forceinline__ void gemv_chunk(uint8_t* smem, const EArgs& a, const TileBuf& tb, int T, uint32_t kb,
+                                           float inv_kb, int c, int nco, int nodd, int neven, int lane) {
   const ELayout& L = a.L;
   const LlvqClassHot* cls = reinterpret_cast<const LlvqClassHot*>(smem + L.cls);
   const float* xsum = reinterpret_cast<const float*>(smem + a.xsum);
-  const uint64_t* queue = reinterpret_cast<const uint64_t*>(smem + L.queue);
-  float* part = reinterpret_cast<float*>(smem + L.part);
+  const uint64_t* queue = reinterpret_cast<const uint64_t*>(smem + tb.queue);
+  float* part = reinterpret_cast<float*>(smem + tb.part);
   if (c < nco) {
     const int e = (c << 6) + lane;
     if (e >= nodd) return;
@@ -115,7 +115,14 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
   const int kb = d.kb;
   const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
 
-  // ---- set-up: tables and activations into LDS
+  // ---- set-up: the first tile's fields are requested before the tables and activations
+  // are staged in LDS, so their memory latency overlaps the staging
+  const float inv_kb0 = 1.0f / (float)kb;
+  int row00 = blockIdx.x * a.rows_per_tile;
+  const int T0 = min(a.rows_per_tile, d.rows - row00) * kb;
+  const TileMap tm0 = {(uint32_t)(row00 * kb), (uint32_t)kb, (uint32_t)kb, inv_kb0};
+  UnitFields uf0 = {};
+  if (blockIdx.x < a.ntiles && wave * kEUnit < T0) uf0 = load_unit(d, packed, tm0, T0, wave, lane);
   engine_prologue(smem, L, d, a.nbuckets, scales, tid);
   {
     const int ncol = kb * 24;
@@ -150,37 +157,66 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
       xsum[b] = s0;
     }
   }
-  int* ctr = reinterpret_cast<int*>(smem + L.ctr);
-  const float* part = reinterpret_cast<const float*>(smem + L.part);
+  int* work = reinterpret_cast<int*>(smem + L.work);
   const float inv_kb = 1.0f / (float)kb;
 
-  for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-    const int row0 = tile * a.rows_per_tile;
-    const int nrows = min(a.rows_per_tile, d.rows - row0);
+  // Tiles of this workgroup: blockIdx.x + lt * gridDim.x, using buffer lt & 1.  Phase lt
+  // decodes tile lt and, as work runs out, classifies tile lt + 1 into the other buffer, so
+  // the classification fills the tail of the decode; then the rows of tile lt are summed.
+  auto tile_rows = [&](int tile, int* row0, int* nrows) {
+    *row0 = tile * a.rows_per_tile;
+    *nrows = min(a.rows_per_tile, d.rows - *row0);
+  };
+  // classify tile 0 (fields loaded above)
+  if (blockIdx.x < a.ntiles) {
+    if (tid == 0) {
+      int* c0 = reinterpret_cast<int*>(smem + L.buf[0].ctr);
+      int* c1 = reinterpret_cast<int*>(smem + L.buf[1].ctr);
+      c0[0] = 0; c0[1] = 0; c1[0] = 0; c1[1] = 0; work[0] = 0;
+    }
+    __syncthreads();
+    if (wave * kEUnit < T0) classify_fields(smem, L, L.buf[0], d, uf0, T0, wave, lane, err);
+    __syncthreads();
+  }
+  int lt = 0;
+  for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x, ++lt) {
+    const TileBuf& cur = L.buf[lt & 1];
+    const TileBuf& nxt = L.buf[(lt & 1) ^ 1];
+    int row0, nrows;
+    tile_rows(tile, &row0, &nrows);
     const int T = nrows * kb;
-    if (tid == 0) { ctr[0] = 0; ctr[1] = 0; ctr[2] = 0; }
-    __syncthreads();
-
-    // ---- 1. classify: wave w takes unit w (T <= kEWaves * kEUnit)
-    const TileMap tm = {(uint32_t)(row0 * kb), (uint32_t)kb, (uint32_t)kb, inv_kb};
-    if (wave * kEUnit < T) classify_unit(smem, L, d, packed, tm, T, wave, lane, err);
-    __syncthreads();
+    const int* ctr = reinterpret_cast<const int*>(smem + cur.ctr);
     const int nodd = ctr[0];
     const int neven = ctr[1];
     const int nco = (nodd + 63) >> 6;
     const int nch = nco + ((neven + 63) >> 6);
+    // next tile's classify units
+    const int tile1 = tile + gridDim.x;
+    int row1 = 0, nrows1 = 0, T1 = 0, nun1 = 0;
+    if (tile1 < a.ntiles) {
+      tile_rows(tile1, &row1, &nrows1);
+      T1 = nrows1 * kb;
+      nun1 = (T1 + kEUnit - 1) / kEUnit;
+    }
+    const TileMap tm1 = {(uint32_t)(row1 * kb), (uint32_t)kb, (uint32_t)kb, inv_kb};
 
-    // ---- 2. decode + dot: 64-block chunks handed out dynamically (odd chunks first)
+    // ---- decode + dot of this tile (odd chunks first), then classify units of the next
     for (;;) {
       int c = 0;
-      if (lane == 0) c = atomicAdd(&ctr[2], 1);
+      if (lane == 0) c = atomicAdd(&work[0], 1);
       c = __builtin_amdgcn_readfirstlane(c);
-      if (c >= nch) break;
-      gemv_chunk<XF32>(smem, a, T, (uint32_t)kb, inv_kb, c, nco, nodd, neven, lane);
+      if (c < nch) {
+        gemv_chunk<XF32>(smem, a, cur, T, (uint32_t)kb, inv_kb, c, nco, nodd, neven, lane);
+      } else if (c < nch + nun1) {
+        classify_unit(smem, L, nxt, d, packed, tm1, T1, c - nch, lane, err);
+      } else {
+        break;
+      }
     }
     __syncthreads();
 
-    // ---- 3. row sums (fixed order)
+    // ---- row sums of this tile (fixed order); reset this buffer's counters for tile lt + 2
+    const float* part = reinterpret_cast<const float*>(smem + cur.part);
     for (int rl = wave; rl < nrows; rl += kEWaves) {
       float acc = 0.0f;
       for (int b = lane; b < kb; b += 64) acc += part[rl * kb + b];
@@ -191,6 +227,12 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
         const float rs = sg ? 1.0f : __half2float(scales[r]);
         y[r] = acc * rs;
       }
+    }
+    if (tid == 0) {
+      int* cc = reinterpret_cast<int*>(smem + cur.ctr);
+      cc[0] = 0;
+      cc[1] = 0;
+      work[0] = 0;
     }
     __syncthreads();
   }

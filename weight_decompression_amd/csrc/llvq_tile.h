@@ -13,7 +13,7 @@
 __device__ __forceinline__ void bytes_chunk(uint8_t* smem, const ELayout& L, uint32_t tb, int T, int c, int nco,
                                             int nodd, int neven, int lane) {
   const LlvqClassHot* cls = reinterpret_cast<const LlvqClassHot*>(smem + L.cls);
-  const uint64_t* queue = reinterpret_cast<const uint64_t*>(smem + L.queue);
+  const uint64_t* queue = reinterpret_cast<const uint64_t*>(smem + L.buf[0].queue);
   if (c < nco) {
     const int e = (c << 6) + lane;
     if (e >= nodd) return;
@@ -82,18 +82,19 @@ __global__ __launch_bounds__(kEThreads) void k_decode_tile(KDesc d, EArgs a, con
   const uint32_t rowbytes = (uint32_t)kb * 24u;
 
   engine_prologue(smem, L, d, a.nbuckets, scales, tid);
-  int* ctr = reinterpret_cast<int*>(smem + L.ctr);
-  const float* part = reinterpret_cast<const float*>(smem + L.part);
+  int* ctr = reinterpret_cast<int*>(smem + L.buf[0].ctr);
+  int* work = reinterpret_cast<int*>(smem + L.work);
+  const float* part = reinterpret_cast<const float*>(smem + L.buf[0].part);
 
   for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int row0 = tile * a.rows_per_tile;
     const int nrows = min(a.rows_per_tile, d.rows - row0);
     const int T = nrows * kb;
-    if (tid == 0) { ctr[0] = 0; ctr[1] = 0; ctr[2] = 0; }
+    if (tid == 0) { ctr[0] = 0; ctr[1] = 0; work[0] = 0; }
     __syncthreads();
     const TileMap tm = {(uint32_t)(row0 * kb), (uint32_t)kb, (uint32_t)kb, 1.0f / (float)kb};
     if (wave * kEUnit < T)
-      classify_unit(smem, L, d, packed, tm, T, wave, lane, err, smem + tb);
+      classify_unit(smem, L, L.buf[0], d, packed, tm, T, wave, lane, err, smem + tb);
     __syncthreads();
     const int nodd = ctr[0];
     const int neven = ctr[1];
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kEThreads) void k_decode_tile(KDesc d, EArgs a, con
     const int nch = nco + ((neven + 63) >> 6);
     for (;;) {
       int c = 0;
-      if (lane == 0) c = atomicAdd(&ctr[2], 1);
+      if (lane == 0) c = atomicAdd(&work[0], 1);
       c = __builtin_amdgcn_readfirstlane(c);
       if (c >= nch) break;
       bytes_chunk(smem, L, tb, T, c, nco, nodd, neven, lane);
