@@ -46,34 +46,34 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "b777b4c7c9c43121aa40c63c053e6578d071102fa8372f8ce77793cac7e71241",
+        "source_sha256": "24a43eaf553e5aa6ff1472cb2d63cc9175f40f2af6121dc32f3492901960a9bb",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
-        "valu_lane_ops_per_unit": 749.2,       # SQ_INSTS_VALU * 64 / blocks
-        "fetch_bytes_per_launch": 12151700,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "valu_lane_ops_per_unit": 769.1,       # SQ_INSTS_VALU * 64 / blocks
+        "fetch_bytes_per_launch": 12260231,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "b777b4c7c9c43121aa40c63c053e6578d071102fa8372f8ce77793cac7e71241",
+        "source_sha256": "24a43eaf553e5aa6ff1472cb2d63cc9175f40f2af6121dc32f3492901960a9bb",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
-        "valu_lane_ops_per_unit": 881.9,
-        "fetch_bytes_per_launch": 61689184,
+        "valu_lane_ops_per_unit": 901.6,
+        "fetch_bytes_per_launch": 61704537,
         "write_bytes_per_launch": 1835008,
     },
     "decode_bf16": {
-        "source_sha256": "b777b4c7c9c43121aa40c63c053e6578d071102fa8372f8ce77793cac7e71241",
+        "source_sha256": "24a43eaf553e5aa6ff1472cb2d63cc9175f40f2af6121dc32f3492901960a9bb",
         "summary": "profiles/decode_bf16_7b_layer_k_decode_tile.md",
         "unit_of_work": "24-weight block (k_decode_tile<bf16>)",
-        "valu_lane_ops_per_unit": 796.0,
+        "valu_lane_ops_per_unit": 803.2,
         "fetch_bytes_per_launch": None,        # per-launch figures of a mixed-shape layer; see the summary
         "write_bytes_per_launch": None,
     },
     "roundtrip": {
-        "source_sha256": "b777b4c7c9c43121aa40c63c053e6578d071102fa8372f8ce77793cac7e71241",
+        "source_sha256": "24a43eaf553e5aa6ff1472cb2d63cc9175f40f2af6121dc32f3492901960a9bb",
         "summary": "profiles/roundtrip_1e7_k_decode_tile_k_rank.md",
-        "unit_of_work": "point: decode to int8 (682.8) + rank (1348.6)",
-        "valu_lane_ops_per_unit": 2031.4,
+        "unit_of_work": "point: decode to int8 (684.7) + rank (1348.6)",
+        "valu_lane_ops_per_unit": 2033.3,
         "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
         "write_bytes_per_launch": None,
     },
