@@ -18,8 +18,10 @@
 // Rank unranking: exact arithmetic decoding in fp64.  With y = u * n the value slot is
 // the number of cumulative counts C_j <= floor(y) (SWAR compare of the three thresholds
 // packed in one dword) and y <- (y - C_k) * (n' / c_k), n' the values left after the
-// step, n'/c from an LDS table.  The decision margins (>= n/(2Q), Q <= 4.2e8
-// arrangements) exceed the accumulated rounding error by a factor > 1e5.  The last 6
+// step, n'/c from an LDS table.  Counts are kept times 8 (a count byte is then the
+// byte offset of its table entry), so the step computes (8 y - 8 C_k) * (n' / 8 c_k),
+// which rounds exactly like the unscaled form.  The decision margins (>= n/(2Q),
+// Q <= 4.2e8 arrangements) exceed the accumulated rounding error by a factor > 1e5.  The last 6
 // values come from a table of all 4^6 slot sequences grouped by composition in
 // lexicographic order: with counts c (sum 6) and y in [0, 6), the rank inside the
 // group is floor(y * Q(c) / 6).
@@ -33,7 +35,8 @@ constexpr int kEUnit = 256;         // fields per classify unit (4 per lane)
 constexpr int kBias = 12;           // value tables store 12 +- v (|v| <= 12)
 constexpr int kTail = 6;            // values resolved by the tail table
 constexpr int kSteps = 24 - kTail;  // values resolved step by step
-constexpr int kFStride = 25;        // F[n][c] row length (c = 0..24)
+constexpr int kFStride = 25;        // F row length (c = 0..24)
+constexpr uint32_t kFRow = kFStride * 8u;   // F row in bytes
 
 // One tile's queues and block slots.
 struct TileBuf {
@@ -44,7 +47,7 @@ struct TileBuf {
 
 struct ELayout {
   // byte offsets inside the dynamic LDS segment
-  uint32_t ftab;      // double F[25][25]: F[n][c] = n / c   (offset 0)
+  uint32_t ftab;      // double F[25][25]: F[r][c] = (23 - r) / (8 c), always at offset 0
   uint32_t cls;       // LlvqClassHot[ncls]
   uint32_t gains;     // float[2^gain_bits]
   uint32_t bucket;    // uint8[nbuckets]
@@ -142,6 +145,37 @@ __device__ __forceinline__ uint32_t swar_ge(uint32_t f, uint32_t nc) {
   return (t >> 7) & 0x010101u;
 }
 
+// popcount(a) + b, b in a vector register
+__device__ __forceinline__ uint32_t bcnt_addv(uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// 8 at the byte of the slot chosen by the SWAR flags g: (g << 8 | 1) - g = 255 g + 1 is
+// the one-hot byte of the slot, times 8 for the scaled counts.
+__device__ __forceinline__ uint32_t dec8(uint32_t g) {
+  uint32_t d;
+  asm("v_mad_u32_u24 %0, %1, %2, 8" : "=v"(d) : "v"(g), "s"(2040u));
+  return d;
+}
+
+// median of (a, b, 1): 1 if a >= 1, else b (b in {0, 1})
+__device__ __forceinline__ uint32_t med3_1(uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_med3_u32 %0, %1, %2, 1" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// Entry of the F table at byte offset o.  The table sits at offset 0 of the dynamic LDS
+// segment, and the engine's kernels declare no static LDS, so o is the LDS address itself
+// (no base register add per step).
+typedef const __attribute__((address_space(3))) double* lds_f64_ptr;
+__device__ __forceinline__ double ftab_at(const uint8_t* smem, uint32_t o) {
+  (void)smem;
+  return *reinterpret_cast<lds_f64_ptr>((uintptr_t)o);
+}
+
 // ---------------------------------------------------------------------------
 // per-block decoders
 
@@ -167,25 +201,47 @@ __device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELa
 }
 
 // Slot codes of the last 6 values (2 bits each, first of the six in the low bits), from
-// the counts left (sum 6) and y in [0, 6).
-__device__ __forceinline__ uint32_t tail_codes(const uint8_t* smem, const ELayout& L, uint32_t cnt, double y) {
-  const uint32_t ci = __builtin_amdgcn_udot4(cnt, 0x00310701u, 0u, false);   // c0 + 7 c1 + 49 c2
-  const LlvqTailComp tc = reinterpret_cast<const LlvqTailComp*>(smem + L.tcomp)[ci];
+// the counts left (times 8, sum 48) and y in [0, 6).
+__device__ __forceinline__ uint32_t tail_codes(const uint8_t* smem, const ELayout& L, uint32_t cnt8, double y) {
+  const uint32_t ci8 = __builtin_amdgcn_udot4(cnt8, 0x00310701u, 0u, false);   // 8 (c0 + 7 c1 + 49 c2)
+  const LlvqTailComp tc = *reinterpret_cast<const LlvqTailComp*>(smem + L.tcomp + ci8);
   const uint32_t r = (uint32_t)((float)y * tc.q_over_6);
   return reinterpret_cast<const uint16_t*>(smem + L.tail)[tc.offset + r];
 }
 
+// One arithmetic-decoding step on (y, nc, cnt8) with F row offset fo (bytes): returns the
+// SWAR flags g of the chosen slot; k = popcount(g) + sel is the caller's selector.
+struct StepOut {
+  uint32_t g, k;
+};
+
+__device__ __forceinline__ StepOut decode_step(const uint8_t* smem, double& y, uint32_t& nc, uint32_t& cnt8,
+                                               uint32_t sel, uint32_t fo) {
+  const uint32_t f = (uint32_t)y;
+  const uint32_t g = swar_ge(f, nc);
+  const uint32_t k = bcnt_addv(g, sel);
+  const uint32_t c8 = __builtin_amdgcn_perm(cnt8, cnt8, k);        // 8 c_k (selector 0..7)
+  const uint32_t C8 = __builtin_amdgcn_udot4(g, cnt8, 0u, false);  // 8 C_k
+  const double fac = ftab_at(smem, fo + c8);                       // n' / (8 c_k)
+  y = __builtin_fma(y, 8.0, -(double)C8) * fac;
+  cnt8 -= dec8(g);
+  nc += g ^ 0x010101u;
+  return {g, k};
+}
+
 // Odd coset: one part of 24 values, visited in position order.  step(p) returns the
 // biased value byte 12 + v_p in the low 8 bits (upper bits zero).  The sign of each value
-// follows from the codeword bit and the value mod 4, folded into one byte-table lookup.
+// follows from the codeword bit and the value mod 4, folded into one byte-table lookup:
+// the selector's +4 (negated entry) for positions off the codeword rides in the addend of
+// the slot popcount.
 struct OddDec {
   double y;
-  uint32_t nc, cnt, notc4, svlo, svhi, codes;
+  uint32_t nc, cnt8, notc4, svlo, svhi, codes;
 
   __device__ __forceinline__ void init(const LlvqClassHot& h, const BlockStart& bs) {
     y = bs.y;
     nc = h.nc0;
-    cnt = h.cnt0;
+    cnt8 = h.cnt0;
     notc4 = ~bs.c << 2;   // bit p + 2 = position p is off the codeword
     svlo = h.sv0lo;
     svhi = h.sv0hi;
@@ -193,95 +249,84 @@ struct OddDec {
   }
 
   __device__ __forceinline__ uint32_t step(const uint8_t* smem, const ELayout& L, int p) {
+    const uint32_t sel = ((notc4 >> p) & 4u) | 0x0c0c0c00u;
     uint32_t k;
     if (p < kSteps) {
-      const double* F = reinterpret_cast<const double*>(smem + L.ftab);
-      const uint32_t f = (uint32_t)y;
-      const uint32_t g = swar_ge(f, nc);
-      k = bcnt_add(g, 0x0c0c0c00u);
-      const uint32_t ck = __builtin_amdgcn_perm(0u, cnt, k);
-      const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
-      const double fac = F[(23 - p) * kFStride + ck];
-      y = (y - (double)Ck) * fac;
-      cnt = (cnt + g) - shl8_or1(g);   // one count down in slot k
-      nc += g ^ 0x010101u;
-      if (p == kSteps - 1) codes = tail_codes(smem, L, cnt, y);
+      // values left after the step: 23 - p, F row p
+      k = decode_step(smem, y, nc, cnt8, sel, kFRow * (uint32_t)p).k;
+      if (p == kSteps - 1) codes = tail_codes(smem, L, cnt8, y);
     } else {
-      k = __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | 0x0c0c0c00u;
+      k = __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | sel;
     }
-    // selector byte 4..7 picks the negated entry
-    return __builtin_amdgcn_perm(svhi, svlo, k + ((notc4 >> p) & 4u));
+    return __builtin_amdgcn_perm(svhi, svlo, k);
   }
 };
 
 // Even coset: support values (on the codeword's positions, ascending) then complement
 // values (other positions, ascending), on one arithmetic-decoding state.  step(i)
 // returns the biased value byte of the i-th decoded value and its position.  Nonzero
-// positions consume the bits of s in decode order; the last support position takes the
-// sign that fixes the parity of negatives on the support and consumes no bit.
+// values take the bits of s in decode order; the last support value's sign fixes the
+// parity of negatives on the support, and init inserts it into s at bit w - 1 (the
+// support values are all nonzero, so they take bits 0..w-1).  Zero can only be a part's
+// slot 0, so a value takes a sign bit unless its slot is 0 and the part's slot 0 is zero.
 struct EvenDec {
   double y;
-  uint32_t nc, cnt, svlo, svhi, nz, m, s, nb, codes, negq, w, c;
-  bool two;
+  uint32_t nc, cnt8, svlo, svhi, nz0, nz1, m, s, codes, c, hp, fo, swi;
 
-  __device__ __forceinline__ void init(const LlvqClassHot& h, const BlockStart& bs) {
-    w = (h.meta >> 8) & 31u;
+  // hp: LDS byte offset of the class record
+  __device__ __forceinline__ void init(const LlvqClassHot& h, const BlockStart& bs, uint32_t hp_) {
+    const uint32_t w = (h.meta >> 8) & 31u;
     const uint32_t pi = (h.meta >> 16) & 1u;
-    two = w != 0u && w != 24u;
-    const uint32_t n0 = w ? w : 24u;
-    // the support's first w-1 signs are bits 0..w-2 of s (all support values are nonzero)
-    negq = w ? (((uint32_t)__builtin_popcount(bs.s & ((1u << (w - 1u)) - 1u)) & 1u) ^ pi) : 0u;
+    const bool two = w != 0u && w != 24u;
+    swi = two ? w : 0u;
+    s = bs.s;
+    if (w) {
+      const uint32_t lo = s & ((1u << (w - 1u)) - 1u);
+      const uint32_t negq = ((uint32_t)__builtin_popcount(lo) & 1u) ^ pi;
+      s = lo | (negq << (w - 1u)) | ((s >> (w - 1u)) << w);
+    }
     y = bs.y;
     nc = h.nc0;
-    cnt = h.cnt0;
+    cnt8 = h.cnt0;
     svlo = h.sv0lo;
     svhi = h.sv0hi;
-    nz = (h.meta >> 20) & 15u;
+    nz0 = (h.meta >> 20) & 1u;
+    nz1 = (h.meta >> 24) & 1u;
     c = bs.c;
     m = w ? bs.c : 0xffffffu;
-    s = bs.s;
-    nb = (n0 - 1u) * (kFStride * 8u);   // byte offset of F[n'][0], n' = values left after the step
+    // F rows: values left after step i are w - 1 - i on the support of a two-part class
+    // (row i + 24 - w), else 23 - i (row i); the last support step continues into the
+    // complement (24 - w left), row i.
+    fo = two ? (24u - w) * kFRow : 0u;
+    hp = hp_;
     codes = 0u;
   }
 
-  __device__ __forceinline__ uint32_t step(const uint8_t* smem, const ELayout& L, const LlvqClassHot& h, int i,
-                                           uint32_t& pos) {
+  __device__ __forceinline__ uint32_t step(const uint8_t* smem, const ELayout& L, int i, uint32_t& pos) {
     if (i == 8 || i == 12 || i == 16) {
-      const bool sw = two && (w == (uint32_t)i);
-      nc = sw ? h.nc1 : nc;
-      cnt = sw ? h.cnt1 : cnt;
-      svlo = sw ? h.sv1lo : svlo;
-      svhi = sw ? h.sv1hi : svhi;
-      nz = sw ? ((h.meta >> 24) & 15u) : nz;
-      m = sw ? (~c & 0xffffffu) : m;
+      if (swi == (uint32_t)i) {   // two-part class: the complement's tables
+        const uint4 q = *reinterpret_cast<const uint4*>(smem + hp + 64u);
+        nc = q.x;
+        cnt8 = q.y;
+        svlo = q.z;
+        svhi = q.w;
+        nz0 = nz1;
+        m = ~c & 0xffffffu;
+      }
     }
-    uint32_t kb;
+    uint32_t kb, free_;
     if (i < kSteps) {
-      const uint32_t f = (uint32_t)y;
-      const uint32_t g = swar_ge(f, nc);
-      kb = bcnt_add(g, 0x0c0c0c00u);
-      const uint32_t ck = __builtin_amdgcn_perm(0u, cnt, kb);
-      const uint32_t Ck = __builtin_amdgcn_udot4(g, cnt, 0u, false);
-      const double fac = *reinterpret_cast<const double*>(smem + L.ftab + nb + (ck << 3));
-      y = (y - (double)Ck) * fac;
-      cnt = (cnt + g) - shl8_or1(g);
-      nc += g ^ 0x010101u;
-      // the last support step (i = w - 1) hands over to the complement: n' = 24 - w
-      if (i == 6 || i == 10 || i == 14)
-        nb = (two && w == (uint32_t)(i + 2)) ? (24u - w) * (kFStride * 8u) : nb - kFStride * 8u;
-      else
-        nb -= kFStride * 8u;
-      if (i == kSteps - 1) codes = tail_codes(smem, L, cnt, y);
+      const StepOut so = decode_step(smem, y, nc, cnt8, 0x0c0c0c00u, fo + kFRow * (uint32_t)i);
+      kb = so.k;
+      free_ = med3_1(so.g, nz0);
+      if (i == 6 || i == 10 || i == 14) fo = swi == (uint32_t)(i + 2) ? 0u : fo;
+      if (i == kSteps - 1) codes = tail_codes(smem, L, cnt8, y);
     } else {
-      kb = ((codes >> (2 * (i - kSteps))) & 3u) | 0x0c0c0c00u;
+      const uint32_t code = __builtin_amdgcn_ubfe(codes, 2 * (i - kSteps), 2);
+      kb = code | 0x0c0c0c00u;
+      free_ = med3_1(code, nz0);
     }
-    uint32_t free_ = (nz >> (kb & 31u)) & 1u;
-    uint32_t neg = s & free_;
-    if (i == 7 || i == 11 || i == 15 || i == 23) {
-      const bool isq = w == (uint32_t)(i + 1);
-      neg = isq ? negq : neg;
-      free_ = isq ? 0u : free_;
-    }
+    const uint32_t neg = s & free_;
     s >>= free_;
     pos = (uint32_t)__builtin_ctz(m);
     m &= m - 1u;
@@ -307,8 +352,8 @@ __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L,
                                                 const __half* __restrict__ scales, int tid) {
   double* F = reinterpret_cast<double*>(smem + L.ftab);
   for (int i = tid; i < 25 * kFStride; i += kEThreads) {
-    const int n = i / kFStride, c = i - n * kFStride;
-    F[i] = c >= 1 ? (double)n / (double)c : 0.0;
+    const int r = i / kFStride, c = i - r * kFStride;
+    F[i] = (c >= 1 && r <= 23) ? (double)(23 - r) / (double)(8 * c) : 0.0;
   }
   lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.cls), reinterpret_cast<const uint32_t*>(dev_tables::kClassHot),
                  d.ncls * (int)(sizeof(LlvqClassHot) / 4), tid);

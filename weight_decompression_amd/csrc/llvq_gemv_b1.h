@@ -86,13 +86,13 @@ __device__ __forceinline__ void gemv_chunk(uint8_t* smem, const EArgs& a, const 
     const LlvqClassHot hE = cls[entry_k(ee)];
     const BlockStart se = block_start(smem, L, entry_I(ee), hE);
     EvenDec ev;
-    ev.init(hE, se);
+    ev.init(hE, se, L.cls + entry_k(ee) * (uint32_t)sizeof(LlvqClassHot));
     const uint32_t col0 = be * 24u;
     float ae0 = 0.0f, ae1 = 0.0f;
 #pragma unroll
     for (int i = 0; i < 24; ++i) {
       uint32_t pos;
-      const uint32_t bve = ev.step(smem, L, hE, i, pos);
+      const uint32_t bve = ev.step(smem, L, i, pos);
       const float xp = x_at<XF32>(smem, a.xs, col0 + pos);
       if (i & 1)
         ae1 = __builtin_fmaf((float)(bve & 0xffu), xp, ae1);

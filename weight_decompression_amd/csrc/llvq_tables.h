@@ -31,7 +31,8 @@ struct LlvqClassRec {
 // complement part (24 - w values).  Per part X (0 = first, 1 = second):
 //   ncX  SWAR thresholds: byte j-1 (j = 1..3) = 0x80 - C_j, C_j = sum of the counts of
 //        value slots below j; unused slots have count 0.
-//   cntX counts of the part's value slots 0..3, one per byte.
+//   cntX counts of the part's value slots 0..3 times 8, one per byte (8 c_j <= 192: the
+//        byte is the offset of entry c_j in a row of 8-byte table entries).
 //   svX  8-byte table read with v_perm (svXhi:svXlo), entries biased by +12:
 //        even classes: bytes 0-3 = 12 + |v_j|, bytes 4-7 = 12 - |v_j| (negative sign);
 //        odd classes:  bytes 0-3 = 12 + b(v_j) for positions on the codeword,
@@ -45,12 +46,10 @@ struct LlvqClassHot {
   double a;          // A
   uint32_t toff;     // Golay table position of codeword r = 0
   uint32_t meta;
-  uint32_t nc0, cnt0;
-  uint32_t nc1, cnt1;
-  uint32_t sv0lo, sv0hi;
-  uint32_t sv1lo, sv1hi;
   float invnorm;     // fp32 1/(4 sqrt m), computed in fp64 and rounded once
   uint32_t m;        // shell
+  uint32_t nc0, cnt0, sv0lo, sv0hi;   // part 0 (byte offset 48)
+  uint32_t nc1, cnt1, sv1lo, sv1hi;   // part 1 (byte offset 64: one 16-byte read)
 };
 
 // Composition record of the 6-position tail table (see gen_tables.cpp).

@@ -43,12 +43,12 @@ __device__ __forceinline__ void bytes_chunk(uint8_t* smem, const ELayout& L, uin
     const LlvqClassHot h = cls[entry_k(ee)];
     const BlockStart bs = block_start(smem, L, entry_I(ee), h);
     EvenDec ev;
-    ev.init(h, bs);
+    ev.init(h, bs, L.cls + entry_k(ee) * (uint32_t)sizeof(LlvqClassHot));
     uint8_t* dst = smem + tb + 24u * f;
 #pragma unroll
     for (int i = 0; i < 24; ++i) {
       uint32_t pos;
-      const uint32_t bv = ev.step(smem, L, h, i, pos);
+      const uint32_t bv = ev.step(smem, L, i, pos);
       dst[pos] = (uint8_t)bv;
     }
   }
