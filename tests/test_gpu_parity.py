@@ -194,6 +194,17 @@ def test_gemv_q_proj_4096x4096_sampled_and_deterministic():
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
+def test_gemv_batch1_two_buffer_pipeline_ragged():
+    # 3001 x 28800 (Kb = 1200): a workgroup's rows do not fit one LDS tile, so the batch-1
+    # kernel runs several 2-row tiles per workgroup with the next tile classified during the
+    # decode of the current one; the last tile holds one row.
+    t = synth.make_tensor("pipe", 17, 1, 3001, 28800, C10)
+    rows = sorted(set(sample_rows(t.rows, 20, 17)) | {2996, 2997, 2998, 2999, 3000})
+    check_gemv(t, rows, "3001x28800 batch 1")
+    (y1, _), (y2, _) = gpu_gemv(t, repeat=2)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
 def _fidelity(which):
     path = os.path.join(HERE, "golden", f"fidelity_c3_{which}.npz")
     if not os.path.exists(path):

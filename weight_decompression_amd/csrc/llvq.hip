@@ -415,19 +415,40 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;   // 32-bit field index
   const bool xf32 = x_dtype == LLVQ_X_F32;
   const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
-  // LDS: fixed tables + two tile buffers of 12 bytes per block (+ counters) + x + xsum
+  // LDS: fixed tables + one or two tile buffers of 12 bytes per block (+ counters) + x + xsum
   ELayout L;
-  const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 2);
   const uint32_t xbytes = align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u)) + align16((uint32_t)k.kb * 4u);
-  if (base + xbytes + 64u + 24u * (uint32_t)k.kb > kLdsBudget) return LLVQ_EUNSUPPORTED;
-  int tmax = (int)((kLdsBudget - base - xbytes - 64u) / 24u) & ~15;
-  if (tmax > kETileMax) tmax = kETileMax;
   EArgs a;
-  int grid = 0;
-  a.rows_per_tile = pick_rows_per_tile(k.rows, k.kb, tmax, &a.ntiles, &grid);
-  if (a.rows_per_tile == 0) return LLVQ_EUNSUPPORTED;
+  int grid = 0, nbuf = 2;
+  // Two buffers: tiles of at most tmax2 blocks, the next tile classified while one decodes.
+  const uint32_t base2 = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 2);
+  int r2 = 0, nt2 = 0, g2 = 0;
+  long cost2 = -1;
+  if (base2 + xbytes + 64u + 24u * (uint32_t)k.kb <= kLdsBudget) {
+    int tmax2 = (int)((kLdsBudget - base2 - xbytes - 64u) / 24u) & ~15;
+    if (tmax2 > kETileMax) tmax2 = kETileMax;
+    r2 = pick_rows_per_tile(k.rows, k.kb, tmax2, &nt2, &g2);
+    if (r2 > 0) cost2 = (long)((nt2 + g2 - 1) / g2) * ((long)r2 * k.kb + kTileOverhead);
+  }
+  // One buffer: every workgroup's rows as a single tile (no second tile to overlap with),
+  // when they fit and the busiest workgroup has no more work than with two buffers.
+  const uint32_t base1 = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 1);
+  const int r1 = (k.rows + kGridMax - 1) / kGridMax;
+  const long t1 = (long)r1 * k.kb;
+  if (base1 + xbytes + 64u <= kLdsBudget && t1 <= kETileMax &&
+      t1 <= (long)((kLdsBudget - base1 - xbytes - 64u) / 12u) && (cost2 < 0 || t1 + kTileOverhead <= cost2)) {
+    nbuf = 1;
+    a.rows_per_tile = r1;
+    a.ntiles = (k.rows + r1 - 1) / r1;
+    grid = a.ntiles;
+  } else {
+    if (r2 == 0) return LLVQ_EUNSUPPORTED;
+    a.rows_per_tile = r2;
+    a.ntiles = nt2;
+    grid = g2;
+  }
   a.nbuckets = nbuckets;
-  engine_layout_base(a.L, k.ncls, 1 << k.gain_bits, nbuckets, a.rows_per_tile * k.kb, 2);
+  engine_layout_base(a.L, k.ncls, 1 << k.gain_bits, nbuckets, a.rows_per_tile * k.kb, nbuf);
   a.xs = a.L.total;
   a.xsum = a.xs + align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u));
   const uint32_t total = a.xsum + align16((uint32_t)k.kb * 4u);

@@ -30,7 +30,7 @@
 
 constexpr int kEThreads = 1024;
 constexpr int kEWaves = kEThreads / 64;
-constexpr int kETileMax = 4096;     // block index inside a tile fits 12 bits
+constexpr int kETileMax = 16384;    // block index inside a tile fits 14 bits
 constexpr int kEUnit = 256;         // fields per classify unit (4 per lane)
 constexpr int kBias = 12;           // value tables store 12 +- v (|v| <= 12)
 constexpr int kTail = 6;            // values resolved by the tail table
@@ -41,7 +41,7 @@ constexpr uint32_t kFRow = kFStride * 8u;   // F row in bytes
 // One tile's queues and block slots.
 struct TileBuf {
   uint32_t ctr;       // int[2]: odd queue fill, even queue fill
-  uint32_t queue;     // uint64[tmax]: I | f << 44 | class << 56
+  uint32_t queue;     // uint64[tmax]: J | f << 42 | class << 56 (see entry_J)
   uint32_t part;      // float[tmax]: block scale, then the block's result
 };
 
@@ -122,23 +122,6 @@ __device__ __forceinline__ uint32_t lshl_add(uint32_t a, uint32_t s, uint32_t b)
   return d;
 }
 
-// Field j of the packed stream as (lo, hi) words, fields of f <= 64 bits.  48-bit fields
-// (the 2-bit format) start at byte 6j: two dword loads and a funnel shift.
-__device__ __forceinline__ void field_words(const uint8_t* __restrict__ packed, uint32_t j, int f,
-                                            uint32_t& lo, uint32_t& hi) {
-  if (f == 48) {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(packed) + ((3u * j) >> 1);
-    const uint32_t w0 = w[0], w1 = w[1];
-    const uint32_t sh = (j & 1u) << 4;
-    lo = __builtin_amdgcn_alignbit(w1, w0, sh);
-    hi = (w1 >> sh) & 0xffffu;
-  } else {
-    const uint64_t v = read_field(packed, j, f);
-    lo = (uint32_t)v;
-    hi = (uint32_t)(v >> 32);
-  }
-}
-
 // SWAR value-slot choice: number of thresholds C_j <= f (j = 1..3), as 0/1 bytes.
 __device__ __forceinline__ uint32_t swar_ge(uint32_t f, uint32_t nc) {
   const uint32_t t = mad_u24(f, 0x010101u, nc);
@@ -186,10 +169,9 @@ struct BlockStart {
   double y;     // y_0 = (R + 1/2) * n0 / P
 };
 
-__device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELayout& L, double Id,
+__device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELayout& L, double Jd,
                                                   const LlvqClassHot& h) {
   BlockStart bs;
-  const double Jd = Id - h.start;
   const uint32_t q = (uint32_t)__builtin_fma(Jd, h.inv_a, 0x1p-13);    // floor(J / A), exact
   const uint32_t r = (uint32_t)__builtin_fma(-(double)q, h.a, Jd);      // J - q A, exact
   const uint32_t B = h.meta & 31u;
@@ -337,36 +319,78 @@ struct EvenDec {
 // ---------------------------------------------------------------------------
 // workgroup set-up and classification
 
-// LDS copy of n 32-bit words with 16-byte vector moves (n a multiple of 4 where the
-// source and destination are 16-byte aligned; the tail is copied word by word).
-__device__ __forceinline__ void lds_copy_words(uint32_t* dst, const uint32_t* src, int n, int tid) {
-  const int n4 = n >> 2;
-  const uint4* s4 = reinterpret_cast<const uint4*>(src);
-  uint4* d4 = reinterpret_cast<uint4*>(dst);
-  for (int i = tid; i < n4; i += kEThreads) d4[i] = s4[i];
-  for (int i = (n4 << 2) + tid; i < n; i += kEThreads) dst[i] = src[i];
+// A copy of n4 16-byte words from global memory into LDS (byte offset dst, 16-byte
+// aligned), split so that a lane's loads (its first two words) can be issued before any
+// store: copy_issue, then copy_finish.
+struct CopySeg {
+  const uint4* src;
+  uint32_t dst;
+  int n4;
+};
+
+typedef uint32_t llvq_u32x4 __attribute__((ext_vector_type(4)));
+
+struct CopyRegs {
+  llvq_u32x4 a, b;   // words tid and tid + kEThreads
+};
+
+__device__ __forceinline__ CopyRegs copy_issue(const CopySeg& c, int tid) {
+  const llvq_u32x4* s = reinterpret_cast<const llvq_u32x4*>(c.src);
+  CopyRegs v = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  if (tid < c.n4) v.a = s[tid];
+  if (tid + kEThreads < c.n4) v.b = s[tid + kEThreads];
+  return v;
 }
 
-// Tables into LDS.  The caller synchronises afterwards.
+__device__ __forceinline__ void copy_finish(uint8_t* smem, const CopyRegs& v, const CopySeg& c, int tid) {
+  llvq_u32x4* d = reinterpret_cast<llvq_u32x4*>(smem + c.dst);
+  if (tid < c.n4) d[tid] = v.a;
+  if (tid + kEThreads < c.n4) d[tid + kEThreads] = v.b;
+  const llvq_u32x4* s = reinterpret_cast<const llvq_u32x4*>(c.src);
+  for (int i = tid + 2 * kEThreads; i < c.n4; i += kEThreads) d[i] = s[i];
+}
+
+// Words n4 * 4 .. nw - 1 of a table (the part past its whole 16-byte words).
+__device__ __forceinline__ void copy_word_tail(uint8_t* smem, uint32_t dst, const void* src, int nw, int tid) {
+  for (int i = (nw & ~3) + tid; i < nw; i += kEThreads)
+    reinterpret_cast<uint32_t*>(smem + dst)[i] = reinterpret_cast<const uint32_t*>(src)[i];
+}
+
+// Tables into LDS, plus an optional extra segment (a consumer's activations).  All of a
+// lane's global loads are issued before its first LDS store, so the workgroup waits for
+// about one memory latency rather than one per copy.  The caller synchronises afterwards.
 __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L, const KDesc& d, int nbuckets,
-                                                const __half* __restrict__ scales, int tid) {
+                                                const __half* __restrict__ scales, int tid,
+                                                CopySeg extra = {nullptr, 0u, 0}) {
+  const int cls_w = d.ncls * (int)(sizeof(LlvqClassHot) / 4);
+  const int bk_w = (nbuckets + 3) >> 2;
+  const uint8_t* bk_src = dev_tables::kBucketTable[d.max_shell];
+  const CopySeg s_cls = {reinterpret_cast<const uint4*>(dev_tables::kClassHot), L.cls, cls_w >> 2};
+  const CopySeg s_tail = {reinterpret_cast<const uint4*>(dev_tables::kTail6), L.tail, 4096 * 2 / 16};
+  const CopySeg s_tcomp = {reinterpret_cast<const uint4*>(dev_tables::kTailComp), L.tcomp, (343 * 2) >> 2};
+  const CopySeg s_bk = {reinterpret_cast<const uint4*>(bk_src), L.bucket, bk_w >> 2};
+  const CopyRegs v_cls = copy_issue(s_cls, tid);
+  const CopyRegs v_tail = copy_issue(s_tail, tid);
+  const CopyRegs v_tcomp = copy_issue(s_tcomp, tid);
+  const CopyRegs v_bk = copy_issue(s_bk, tid);
+  const CopyRegs v_x = copy_issue(extra, tid);
   double* F = reinterpret_cast<double*>(smem + L.ftab);
   for (int i = tid; i < 25 * kFStride; i += kEThreads) {
     const int r = i / kFStride, c = i - r * kFStride;
     F[i] = (c >= 1 && r <= 23) ? (double)(23 - r) / (double)(8 * c) : 0.0;
   }
-  lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.cls), reinterpret_cast<const uint32_t*>(dev_tables::kClassHot),
-                 d.ncls * (int)(sizeof(LlvqClassHot) / 4), tid);
-  lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.tail), reinterpret_cast<const uint32_t*>(dev_tables::kTail6),
-                 2048, tid);
-  lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.tcomp), reinterpret_cast<const uint32_t*>(dev_tables::kTailComp),
-                 343 * 2, tid);
-  lds_copy_words(reinterpret_cast<uint32_t*>(smem + L.bucket),
-                 reinterpret_cast<const uint32_t*>(dev_tables::kBucketTable[d.max_shell]), (nbuckets + 3) >> 2, tid);
   if (d.mode == LLVQ_MODE_SHAPEGAIN && scales != nullptr) {
     float* G = reinterpret_cast<float*>(smem + L.gains);
     for (int i = tid; i < (1 << d.gain_bits); i += kEThreads) G[i] = __half2float(scales[i]);
   }
+  copy_finish(smem, v_cls, s_cls, tid);
+  copy_finish(smem, v_tail, s_tail, tid);
+  copy_finish(smem, v_tcomp, s_tcomp, tid);
+  copy_finish(smem, v_bk, s_bk, tid);
+  copy_finish(smem, v_x, extra, tid);
+  copy_word_tail(smem, L.cls, dev_tables::kClassHot, cls_w, tid);
+  copy_word_tail(smem, L.tcomp, dev_tables::kTailComp, 343 * 2, tid);
+  copy_word_tail(smem, L.bucket, bk_src, bk_w, tid);
 }
 
 // Field index in the stream of tile block f.  A tile is nr rows of w blocks starting at
@@ -383,10 +407,15 @@ struct TileMap {
   }
 };
 
-// Fields of classify unit u of a tile, 4 per lane (f = 256 u + 64 t + lane); fields past
-// the tile read as zero.
+// Fields of classify unit u of a tile, 4 per lane (f = 256 u + 64 t + lane), as raw
+// words: the field is bits sh.. of the 96-bit word triple (w2:w1:w0), any width up to
+// 64 bits.  Bits above the field are not cleared (the consumers mask what they extract).
+// The four fields' words are requested together by straight-line code and not used here,
+// so the loads stay in flight until the classification needs them.  A field past the
+// tile reads the tile's last field (T >= 1 for every unit handed out) and is not used.
+// The reads stay inside the packed buffer's 16 bytes of slack.
 struct UnitFields {
-  uint32_t lo[kEUnit / 64], hi[kEUnit / 64];
+  uint32_t w0[kEUnit / 64], w1[kEUnit / 64], w2[kEUnit / 64], sh[kEUnit / 64];
 };
 
 __device__ __forceinline__ UnitFields load_unit(const KDesc& d, const uint8_t* __restrict__ packed,
@@ -394,10 +423,13 @@ __device__ __forceinline__ UnitFields load_unit(const KDesc& d, const uint8_t* _
   UnitFields uf;
 #pragma unroll
   for (int t = 0; t < kEUnit / 64; ++t) {
-    const int f = u * kEUnit + t * 64 + lane;
-    uf.lo[t] = 0u;
-    uf.hi[t] = 0u;
-    if (f < T) field_words(packed, tm.field((uint32_t)f), d.field_bits, uf.lo[t], uf.hi[t]);
+    const int f = min(u * kEUnit + t * 64 + lane, T - 1);
+    const uint64_t bit = (uint64_t)tm.field((uint32_t)f) * (uint32_t)d.field_bits;
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(packed) + (bit >> 5);
+    uf.w0[t] = p[0];
+    uf.w1[t] = p[1];
+    uf.w2[t] = p[2];
+    uf.sh[t] = (uint32_t)bit & 31u;
   }
   return uf;
 }
@@ -424,14 +456,16 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
   uint64_t entry[kPer];
   uint32_t kk[kPer];
   double Id[kPer];
+  uint32_t flo[kPer], fhi[kPer];
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
     const int f = u * kEUnit + t * 64 + lane;
-    const uint32_t ilo = uf.lo[t] & d.shape_mask_lo;
-    const uint32_t ihi = uf.hi[t] & d.shape_mask_hi;
+    flo[t] = __builtin_amdgcn_alignbit(uf.w1[t], uf.w0[t], uf.sh[t]);
+    fhi[t] = __builtin_amdgcn_alignbit(uf.w2[t], uf.w1[t], uf.sh[t]);
+    const uint32_t ilo = flo[t] & d.shape_mask_lo;
+    const uint32_t ihi = fhi[t] & d.shape_mask_hi;
     const uint64_t I = ((uint64_t)ihi << 32) | ilo;
     valid[t] = f < T && I < d.index_count;
-    entry[t] = I | ((uint64_t)(uint32_t)f << 44);
     Id[t] = __builtin_fma((double)ihi, 4294967296.0, (double)ilo);
     const uint32_t bidx = d.bshift >= 32 ? (ihi >> (d.bshift - 32)) : __builtin_amdgcn_alignbit(ihi, ilo, d.bshift);
     kk[t] = valid[t] ? (uint32_t)bk[bidx] : 0u;
@@ -457,9 +491,12 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
     if (valid[t]) {
       const LlvqClassHot& h = cls[kk[t]];
       odd[t] = ((h.meta >> 17) & 1u) != 0u;
-      entry[t] |= (uint64_t)kk[t] << 56;
-      const uint32_t gsh = d.shape_bits >= 32 ? (uf.hi[t] >> (d.shape_bits - 32))
-                                              : __builtin_amdgcn_alignbit(uf.hi[t], uf.lo[t], d.shape_bits);
+      // J = I - start as the low bits of 2^52 + J (exact: J < 2^41 < 2^52)
+      const uint64_t jb = __builtin_bit_cast(uint64_t, Id[t] + (0x1p52 - h.start));
+      const uint32_t ehi = ((uint32_t)(jb >> 32) & 0x3ffu) | ((uint32_t)f << 10) | (kk[t] << 24);
+      entry[t] = ((uint64_t)ehi << 32) | (uint32_t)jb;
+      const uint32_t gsh = d.shape_bits >= 32 ? (fhi[t] >> (d.shape_bits - 32))
+                                              : __builtin_amdgcn_alignbit(fhi[t], flo[t], d.shape_bits);
       const uint32_t g = gsh & ((1u << d.gain_bits) - 1u);
       part[f] = sg ? G[g] * h.invnorm : 1.0f;
     } else if (f < T) {
@@ -502,7 +539,12 @@ __device__ __forceinline__ void classify_unit(uint8_t* smem, const ELayout& L, c
   classify_fields(smem, L, tb, d, uf, T, u, lane, err, zero_bytes);
 }
 
-// Entry fields
-__device__ __forceinline__ uint32_t entry_f(uint64_t e) { return (uint32_t)(e >> 44) & 0xfffu; }
+// Queue entry fields: J | f << 42 | k << 56 with J = I - start(k) the index inside the
+// class (every class has fewer than 2^41 indices), f the block's index in the tile and
+// k the class.  J comes back as a double by placing it in the mantissa of 2^52.
+__device__ __forceinline__ uint32_t entry_f(uint64_t e) { return (uint32_t)(e >> 42) & 0x3fffu; }
 __device__ __forceinline__ uint32_t entry_k(uint64_t e) { return (uint32_t)(e >> 56); }
-__device__ __forceinline__ double entry_I(uint64_t e) { return (double)(e & 0xfffffffffffull); }
+__device__ __forceinline__ double entry_J(uint64_t e) {
+  const uint32_t hi = ((uint32_t)(e >> 32) & 0x3ffu) | 0x43300000u;
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | (uint32_t)e) - 0x1p52;
+}

@@ -62,7 +62,7 @@ __device__ __forceinline__ void gemv_chunk(uint8_t* smem, const EArgs& a, const 
     const uint32_t fo = entry_f(eo);
     const uint32_t bo = block_col(fo, inv_kb, kb);
     const LlvqClassHot hO = cls[entry_k(eo)];
-    const BlockStart so = block_start(smem, L, entry_I(eo), hO);
+    const BlockStart so = block_start(smem, L, entry_J(eo), hO);
     float xv[24];
     load_x24<XF32>(smem, a.xs, bo, xv);
     OddDec od;
@@ -84,7 +84,7 @@ __device__ __forceinline__ void gemv_chunk(uint8_t* smem, const EArgs& a, const 
     const uint32_t fe = entry_f(ee);
     const uint32_t be = block_col(fe, inv_kb, kb);
     const LlvqClassHot hE = cls[entry_k(ee)];
-    const BlockStart se = block_start(smem, L, entry_I(ee), hE);
+    const BlockStart se = block_start(smem, L, entry_J(ee), hE);
     EvenDec ev;
     ev.init(hE, se, L.cls + entry_k(ee) * (uint32_t)sizeof(LlvqClassHot));
     const uint32_t col0 = be * 24u;
@@ -121,12 +121,21 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
   int row00 = blockIdx.x * a.rows_per_tile;
   const int T0 = min(a.rows_per_tile, d.rows - row00) * kb;
   const TileMap tm0 = {(uint32_t)(row00 * kb), (uint32_t)kb, (uint32_t)kb, inv_kb0};
-  UnitFields uf0 = {};
-  if (blockIdx.x < a.ntiles && wave * kEUnit < T0) uf0 = load_unit(d, packed, tm0, T0, wave, lane);
-  engine_prologue(smem, L, d, a.nbuckets, scales, tid);
+  // (unconditional, so the loads stay in flight: the grid never exceeds the tile count, so
+  // T0 >= 1, and a wave without a unit of tile 0 reads unit 0 and ignores it)
+  const UnitFields uf0 = load_unit(d, packed, tm0, T0, min(wave, (T0 - 1) / kEUnit), lane);
+  // activations: the whole 16-byte words of a 16-byte aligned bf16 row go with the table
+  // copies; the rest (and the zero padding to Kb * 24 columns) follows
+  const bool xa16 = !XF32 && ((((uintptr_t)xv) & 15u) == 0u);
+  const int xw = xa16 ? (d.cols >> 3) : 0;
+  engine_prologue(smem, L, d, a.nbuckets, scales, tid, CopySeg{reinterpret_cast<const uint4*>(xv), a.xs, xw});
   {
     const int ncol = kb * 24;
-    if (XF32) {
+    if (xa16) {
+      uint16_t* xs = reinterpret_cast<uint16_t*>(smem + a.xs);
+      const uint16_t* xg = reinterpret_cast<const uint16_t*>(xv);
+      for (int i = (xw << 3) + tid; i < ncol; i += kEThreads) xs[i] = i < d.cols ? xg[i] : (uint16_t)0;
+    } else if (XF32) {
       float* xs = reinterpret_cast<float*>(smem + a.xs);
       const float* xg = reinterpret_cast<const float*>(xv);
       for (int i = tid; i < ncol; i += kEThreads) xs[i] = i < d.cols ? xg[i] : 0.0f;
@@ -172,10 +181,20 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
     if (tid == 0) {
       int* c0 = reinterpret_cast<int*>(smem + L.buf[0].ctr);
       int* c1 = reinterpret_cast<int*>(smem + L.buf[1].ctr);
-      c0[0] = 0; c0[1] = 0; c1[0] = 0; c1[1] = 0; work[0] = 0;
+      c0[0] = 0; c0[1] = 0; c1[0] = 0; c1[1] = 0; work[0] = 0; work[1] = 0;
     }
     __syncthreads();
-    if (wave * kEUnit < T0) classify_fields(smem, L, L.buf[0], d, uf0, T0, wave, lane, err);
+    const int nun0 = (T0 + kEUnit - 1) / kEUnit;
+    if (wave < nun0) classify_fields(smem, L, L.buf[0], d, uf0, T0, wave, lane, err);
+    // units past the first kEWaves (tiles of more than kEWaves * kEUnit blocks), handed out
+    // by their own counter
+    for (;;) {
+      int u = 0;
+      if (lane == 0) u = atomicAdd(&work[1], 1);
+      u = __builtin_amdgcn_readfirstlane(u) + kEWaves;
+      if (u >= nun0) break;
+      classify_unit(smem, L, L.buf[0], d, packed, tm0, T0, u, lane, err);
+    }
     __syncthreads();
   }
   int lt = 0;

@@ -20,7 +20,7 @@ __device__ __forceinline__ void bytes_chunk(uint8_t* smem, const ELayout& L, uin
     const uint64_t eo = queue[e];
     const uint32_t f = entry_f(eo);
     const LlvqClassHot h = cls[entry_k(eo)];
-    const BlockStart bs = block_start(smem, L, entry_I(eo), h);
+    const BlockStart bs = block_start(smem, L, entry_J(eo), h);
     OddDec od;
     od.init(h, bs);
     uint2* dst = reinterpret_cast<uint2*>(smem + tb + 24u * f);
@@ -41,7 +41,7 @@ __device__ __forceinline__ void bytes_chunk(uint8_t* smem, const ELayout& L, uin
     const uint64_t ee = queue[T - 1 - e];
     const uint32_t f = entry_f(ee);
     const LlvqClassHot h = cls[entry_k(ee)];
-    const BlockStart bs = block_start(smem, L, entry_I(ee), h);
+    const BlockStart bs = block_start(smem, L, entry_J(ee), h);
     EvenDec ev;
     ev.init(h, bs, L.cls + entry_k(ee) * (uint32_t)sizeof(LlvqClassHot));
     uint8_t* dst = smem + tb + 24u * f;
