@@ -205,6 +205,16 @@ def test_gemv_batch1_two_buffer_pipeline_ragged():
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
+def test_gemv_batch1_large_single_tile():
+    # 24577 x 2048 (Kb = 86): each workgroup's 97 rows (8342 blocks, 33 classification
+    # units for 16 waves) form one LDS tile; the last workgroup's tile has 36 rows.
+    t = synth.make_tensor("seg", 18, 1, 24577, 2048, C10)
+    rows = set(sample_rows(t.rows, 16, 18)) | {32, 33, 65, 66, 97 + 32, 97 + 65, 24576, 24575, 24541}
+    check_gemv(t, sorted(rows), "24577x2048 batch 1")
+    (y1, _), (y2, _) = gpu_gemv(t, repeat=2)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
 def _fidelity(which):
     path = os.path.join(HERE, "golden", f"fidelity_c3_{which}.npz")
     if not os.path.exists(path):

@@ -418,7 +418,7 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   // LDS: fixed tables + one or two tile buffers of 12 bytes per block (+ counters) + x + xsum
   ELayout L;
   const uint32_t xbytes = align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u)) + align16((uint32_t)k.kb * 4u);
-  EArgs a;
+  EArgs a = {};
   int grid = 0, nbuf = 2;
   // Two buffers: tiles of at most tmax2 blocks, the next tile classified while one decodes.
   const uint32_t base2 = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 2);
@@ -474,7 +474,7 @@ int launch_decode_tile(const KDesc& k, const void* packed, const void* scales, i
   if (base + 64u + 36u * (uint32_t)k.kb > kLdsBudget) return LLVQ_EUNSUPPORTED;
   int tmax = (int)((kLdsBudget - base - 64u) / 36u) & ~15;
   if (tmax > kETileMax) tmax = kETileMax;
-  EArgs a;
+  EArgs a = {};
   int grid = 0;
   a.rows_per_tile = pick_rows_per_tile(k.rows, k.kb, tmax, &a.ntiles, &grid);
   if (a.rows_per_tile == 0) return LLVQ_EUNSUPPORTED;
@@ -508,7 +508,7 @@ int launch_gemm_mfma(const KDesc& k, const void* packed, const void* scales, con
   int tmax = (int)((kLdsBudget - base - red - 64u) / 36u);
   if (tmax > kETileMax) tmax = kETileMax;
   const int wmax = tmax / kGRows;
-  GArgs g;
+  GArgs g = {};
   g.nchunk = (k.kb + wmax - 1) / wmax;
   g.w = (k.kb + g.nchunk - 1) / g.nchunk;
   g.ngroups = (k.rows + kGRows - 1) / kGRows;

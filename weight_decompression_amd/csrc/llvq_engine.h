@@ -48,7 +48,7 @@ struct TileBuf {
 struct ELayout {
   // byte offsets inside the dynamic LDS segment
   uint32_t ftab;      // double F[25][25]: F[r][c] = (23 - r) / (8 c), always at offset 0
-  uint32_t cls;       // LlvqClassHot[ncls]
+  uint32_t cls;       // LlvqClassHot[ncls + 2]: the last two are sentinels (start only, +inf)
   uint32_t gains;     // float[2^gain_bits]
   uint32_t bucket;    // uint8[nbuckets]
   uint32_t tail;      // uint16[4096]
@@ -64,7 +64,7 @@ __host__ __device__ inline uint32_t engine_layout_base(ELayout& L, int ncls, int
                                                       int nbuf = 1) {
   uint32_t o = 0;
   L.ftab = o;     o = align16(o + 25u * kFStride * 8u);
-  L.cls = o;      o = align16(o + (uint32_t)ncls * (uint32_t)sizeof(LlvqClassHot));
+  L.cls = o;      o = align16(o + (uint32_t)(ncls + 2) * (uint32_t)sizeof(LlvqClassHot));
   L.gains = o;    o = align16(o + (uint32_t)ngains * 4u);
   L.bucket = o;   o = align16(o + (uint32_t)nbuckets);
   L.tail = o;     o = align16(o + 4096u * 2u);
@@ -389,6 +389,7 @@ __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L,
   copy_finish(smem, v_bk, s_bk, tid);
   copy_finish(smem, v_x, extra, tid);
   copy_word_tail(smem, L.cls, dev_tables::kClassHot, cls_w, tid);
+  if (tid < 2) reinterpret_cast<LlvqClassHot*>(smem + L.cls)[d.ncls + tid].start = __builtin_inf();
   copy_word_tail(smem, L.tcomp, dev_tables::kTailComp, 343 * 2, tid);
   copy_word_tail(smem, L.bucket, bk_src, bk_w, tid);
 }
@@ -436,8 +437,10 @@ __device__ __forceinline__ UnitFields load_unit(const KDesc& d, const uint8_t* _
 
 // Classify the loaded unit: class search, block scale, queue append.  The four fields of
 // a lane are searched together (independent LDS reads), the bucket's first two class
-// boundaries are tested at once (a longer scan is rare), and one queue reservation per
-// parity covers the whole unit.
+// boundaries are tested at once (a longer scan is rare; the sentinel records end it), and
+// one queue reservation per parity covers the whole unit.  The common path is straight-line
+// code: an invalid block (index >= the shell-union size) is classified as block 0 of class
+// 0 and dropped.
 // With zero_bytes set, an invalid block's 24 value bytes at zero_bytes + 24 f are set to
 // the bias (value 0) for consumers that read every block's bytes.
 __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L, const TileBuf& tb, const KDesc& d,
@@ -451,12 +454,9 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
   const uint8_t* bk = smem + L.bucket;
   const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
   constexpr int kPer = kEUnit / 64;
-  const int ncls = d.ncls;
-  bool valid[kPer], odd[kPer];
-  uint64_t entry[kPer];
-  uint32_t kk[kPer];
+  bool valid[kPer];
+  uint32_t kk[kPer], flo[kPer], fhi[kPer];
   double Id[kPer];
-  uint32_t flo[kPer], fhi[kPer];
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
     const int f = u * kEUnit + t * 64 + lane;
@@ -466,54 +466,67 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
     const uint32_t ihi = fhi[t] & d.shape_mask_hi;
     const uint64_t I = ((uint64_t)ihi << 32) | ilo;
     valid[t] = f < T && I < d.index_count;
-    Id[t] = __builtin_fma((double)ihi, 4294967296.0, (double)ilo);
+    Id[t] = valid[t] ? __builtin_fma((double)ihi, 4294967296.0, (double)ilo) : 0.0;
     const uint32_t bidx = d.bshift >= 32 ? (ihi >> (d.bshift - 32)) : __builtin_amdgcn_alignbit(ihi, ilo, d.bshift);
-    kk[t] = valid[t] ? (uint32_t)bk[bidx] : 0u;
+    kk[t] = bk[valid[t] ? bidx : 0u];
   }
+  bool more = false;
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
-    uint32_t k = kk[t];
-    if (valid[t]) {
-      const bool c1 = (int)k + 1 < ncls && Id[t] >= cls[k + 1].start;
-      const bool c2 = (int)k + 2 < ncls && Id[t] >= cls[k + 2].start;
-      k += (uint32_t)c1 + (uint32_t)(c1 && c2);
-      if (c1 && c2)
-        while ((int)k + 1 < ncls && Id[t] >= cls[k + 1].start) ++k;
-    }
-    kk[t] = k;
+    const uint32_t k = kk[t];
+    const bool c1 = Id[t] >= cls[k + 1].start;
+    const bool c2 = Id[t] >= cls[k + 2].start;
+    kk[t] = k + (uint32_t)c1 + (uint32_t)c2;   // c2 implies c1
+    more = more || c2;
+  }
+  if (more) {
+#pragma unroll
+    for (int t = 0; t < kPer; ++t)
+      while (Id[t] >= cls[kk[t] + 1].start) ++kk[t];
   }
   int no = 0, ne = 0;
   uint64_t bo[kPer], be[kPer];
+  uint64_t entry[kPer];
+  uint32_t po[kPer], pe[kPer];
+  bool bad = false;
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
     const int f = u * kEUnit + t * 64 + lane;
-    odd[t] = false;
-    if (valid[t]) {
-      const LlvqClassHot& h = cls[kk[t]];
-      odd[t] = ((h.meta >> 17) & 1u) != 0u;
-      // J = I - start as the low bits of 2^52 + J (exact: J < 2^41 < 2^52)
-      const uint64_t jb = __builtin_bit_cast(uint64_t, Id[t] + (0x1p52 - h.start));
-      const uint32_t ehi = ((uint32_t)(jb >> 32) & 0x3ffu) | ((uint32_t)f << 10) | (kk[t] << 24);
-      entry[t] = ((uint64_t)ehi << 32) | (uint32_t)jb;
-      const uint32_t gsh = d.shape_bits >= 32 ? (fhi[t] >> (d.shape_bits - 32))
-                                              : __builtin_amdgcn_alignbit(fhi[t], flo[t], d.shape_bits);
-      const uint32_t g = gsh & ((1u << d.gain_bits) - 1u);
-      part[f] = sg ? G[g] * h.invnorm : 1.0f;
-    } else if (f < T) {
-      part[f] = 0.0f;
-      if (zero_bytes) {
-        uint2* zb = reinterpret_cast<uint2*>(zero_bytes + 24u * (uint32_t)f);
-        const uint2 z = make_uint2(0x0c0c0c0cu, 0x0c0c0c0cu);
-        zb[0] = z;
-        zb[1] = z;
-        zb[2] = z;
-      }
-      if (err) atomicAdd(err, 1);
-    }
-    bo[t] = __ballot(valid[t] && odd[t]);
-    be[t] = __ballot(valid[t] && !odd[t]);
+    const uint32_t k = kk[t];
+    const LlvqClassHot& h = cls[k];
+    const bool odd = ((h.meta >> 17) & 1u) != 0u;
+    // J = I - start as the low bits of 2^52 + J (exact: J < 2^41 < 2^52)
+    const uint64_t jb = __builtin_bit_cast(uint64_t, Id[t] + (0x1p52 - h.start));
+    const uint32_t ehi = ((uint32_t)(jb >> 32) & 0x3ffu) | ((uint32_t)f << 10) | (k << 24);
+    entry[t] = ((uint64_t)ehi << 32) | (uint32_t)jb;
+    const uint32_t gsh = d.shape_bits >= 32 ? (fhi[t] >> (d.shape_bits - 32))
+                                            : __builtin_amdgcn_alignbit(fhi[t], flo[t], d.shape_bits);
+    const uint32_t g = gsh & ((1u << d.gain_bits) - 1u);
+    const float sc = sg ? G[g] * h.invnorm : 1.0f;
+    if (f < T) part[f] = valid[t] ? sc : 0.0f;
+    bad = bad || (f < T && !valid[t]);
+    bo[t] = __ballot(valid[t] && odd);
+    be[t] = __ballot(valid[t] && !odd);
+    po[t] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bo[t] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bo[t], 0u));
+    pe[t] = __builtin_amdgcn_mbcnt_hi((uint32_t)(be[t] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be[t], 0u));
     no += __popcll(bo[t]);
     ne += __popcll(be[t]);
+  }
+  if (bad) {
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      const int f = u * kEUnit + t * 64 + lane;
+      if (f < T && !valid[t]) {
+        if (zero_bytes) {
+          uint2* zb = reinterpret_cast<uint2*>(zero_bytes + 24u * (uint32_t)f);
+          const uint2 z = make_uint2(0x0c0c0c0cu, 0x0c0c0c0cu);
+          zb[0] = z;
+          zb[1] = z;
+          zb[2] = z;
+        }
+        if (err) atomicAdd(err, 1);
+      }
+    }
   }
   int baseo = 0, basee = 0;
   if (lane == 0) {
@@ -522,11 +535,12 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
   }
   baseo = __builtin_amdgcn_readfirstlane(baseo);
   basee = __builtin_amdgcn_readfirstlane(basee);
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
-    if (valid[t] && odd[t]) queue[baseo + __popcll(bo[t] & below)] = entry[t];
-    if (valid[t] && !odd[t]) queue[T - 1 - (basee + __popcll(be[t] & below))] = entry[t];
+    const bool odd = (bo[t] >> lane) & 1u;
+    const bool even = (be[t] >> lane) & 1u;
+    if (odd) queue[baseo + (int)po[t]] = entry[t];
+    if (even) queue[T - 1 - (basee + (int)pe[t])] = entry[t];
     baseo += __popcll(bo[t]);
     basee += __popcll(be[t]);
   }
