@@ -46,34 +46,34 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "5679008767fff9a6b9e01541db01a95e03483725324a133a1fa8a0ffcefb7e17",
+        "source_sha256": "0797d29689142954bcb0de296f583858da7c8bd0ec9dc0e32874ff36b9348c1a",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
-        "valu_lane_ops_per_unit": 699.0,       # SQ_INSTS_VALU * 64 / blocks
-        "fetch_bytes_per_launch": 12251015,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "valu_lane_ops_per_unit": 672.4,       # SQ_INSTS_VALU * 64 / blocks
+        "fetch_bytes_per_launch": 12229516,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "5679008767fff9a6b9e01541db01a95e03483725324a133a1fa8a0ffcefb7e17",
+        "source_sha256": "0797d29689142954bcb0de296f583858da7c8bd0ec9dc0e32874ff36b9348c1a",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
-        "valu_lane_ops_per_unit": 824.4,
-        "fetch_bytes_per_launch": 61704537,
+        "valu_lane_ops_per_unit": 803.8,
+        "fetch_bytes_per_launch": 61798731,
         "write_bytes_per_launch": 1835008,
     },
     "decode_bf16": {
-        "source_sha256": "5679008767fff9a6b9e01541db01a95e03483725324a133a1fa8a0ffcefb7e17",
+        "source_sha256": "0797d29689142954bcb0de296f583858da7c8bd0ec9dc0e32874ff36b9348c1a",
         "summary": "profiles/decode_bf16_7b_layer_k_decode_tile.md",
         "unit_of_work": "24-weight block (k_decode_tile<bf16>)",
-        "valu_lane_ops_per_unit": 727.6,
+        "valu_lane_ops_per_unit": 721.5,
         "fetch_bytes_per_launch": None,        # per-launch figures of a mixed-shape layer; see the summary
         "write_bytes_per_launch": None,
     },
     "roundtrip": {
-        "source_sha256": "5679008767fff9a6b9e01541db01a95e03483725324a133a1fa8a0ffcefb7e17",
+        "source_sha256": "0797d29689142954bcb0de296f583858da7c8bd0ec9dc0e32874ff36b9348c1a",
         "summary": "profiles/roundtrip_1e7_k_decode_tile_k_rank.md",
-        "unit_of_work": "point: decode to int8 (612.9) + rank (1348.6)",
-        "valu_lane_ops_per_unit": 1961.5,
+        "unit_of_work": "point: decode to int8 (603.8) + rank (1348.6)",
+        "valu_lane_ops_per_unit": 1952.4,
         "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
         "write_bytes_per_launch": None,
     },
