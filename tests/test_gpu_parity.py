@@ -151,6 +151,61 @@ def test_out_of_range_index_gives_zero_block_and_counts():
     assert list(pts[4]) == bijection.unrank(7, 10)
 
 
+def _with_invalid_blocks(t, positions):
+    """Copy of tensor t whose blocks at (row, block) positions hold shape indices past the
+    shell union (they must decode to zero and be counted)."""
+    import dataclasses
+    shape = t.shape_idx.copy()
+    for j, (r, b) in enumerate(positions):
+        shape[r, b] = np.uint64(C10 + 1000 * j)
+    packed = synth.pack_fields(shape | (t.gain_idx << np.uint64(t.shape_bits)), t.shape_bits + t.gain_bits)
+    return dataclasses.replace(t, shape_idx=shape, packed=packed)
+
+
+def test_decode_two_buffer_pipeline_with_invalid_blocks():
+    # 2598 x 11008 (Kb = 459): a workgroup's rows do not fit one LDS tile, so the decode runs
+    # 4-row tiles (3 per workgroup, the last tile 2 rows) with the next tile classified during
+    # the decode of the current one; invalid blocks are spread over the tensor.
+    t0 = synth.make_tensor("dpipe", 19, 1, 2598, 11008, C10, batch=0)
+    rng = np.random.default_rng(19)
+    pos = [(0, 0), (0, 458), (2597, 458), (2596, 3), (1300, 200)]
+    pos += [(int(r), int(b)) for r, b in zip(rng.integers(0, 2598, 35), rng.integers(0, 459, 35))]
+    pos = sorted(set(pos))
+    t = _with_invalid_blocks(t0, pos)
+    bad = {}
+    for r, b in pos:
+        bad.setdefault(r, set()).add(b)
+    rows = sorted(set(sample_rows(t.rows, 10, 19)) | set(bad) | {2596, 2597})
+    pts, err = gpu_points(t)
+    assert err == len(pos)
+    raw = t.packed.tobytes()
+    for r in rows:
+        ref = reference.decode_row_points(raw, t.rows, t.cols, 10, 44, 4, r) if r not in bad else None
+        if ref is None:
+            for b in range(t.kb):
+                blk = pts[r, 24 * b:24 * b + 24]
+                if b in bad[r]:
+                    assert not blk.any(), (r, b)
+                else:
+                    assert list(blk.astype(int)) == bijection.unrank(int(t.shape_idx[r, b]), 10), (r, b)
+        else:
+            assert np.array_equal(pts[r].astype(np.int64), ref), r
+    desc, packed, scales, _ = dev(t)
+    out = torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device="cuda")
+    err_t = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.decode(desc, packed, scales, wd.OUT_BF16, out, err_t)
+    torch.cuda.synchronize()
+    assert int(err_t.item()) == len(pos)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    ok_rows = [r for r in rows if r not in bad]
+    for r in ok_rows:
+        ref = reference.decode_row_bf16(raw, t.rows, t.cols, 10, t.mode, 44, 4, t.scales_f16, None, r)
+        assert np.array_equal(got[r], ref), r
+    for r in bad:
+        for b in bad[r]:
+            assert not got[r, 24 * b:min(24 * b + 24, t.cols)].any(), (r, b)
+
+
 # ---------------------------------------------------------------------------
 # decode -> bf16
 

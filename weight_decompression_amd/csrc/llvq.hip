@@ -468,19 +468,40 @@ int launch_decode_tile(const KDesc& k, const void* packed, const void* scales, i
                        int32_t* err, hipStream_t s) {
   if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;
   const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
+  // LDS per block: queue entry 8 B + scale 4 B per tile buffer, 24 value bytes.  One buffer
+  // when every workgroup's rows fit one tile (and that costs the busiest workgroup no more),
+  // else two, the next tile classified during the decode of the current one.
   ELayout L;
-  const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0);
-  // per block: queue entry 8 B + scale 4 B + 24 value bytes
-  if (base + 64u + 36u * (uint32_t)k.kb > kLdsBudget) return LLVQ_EUNSUPPORTED;
-  int tmax = (int)((kLdsBudget - base - 64u) / 36u) & ~15;
-  if (tmax > kETileMax) tmax = kETileMax;
+  const int ng = 1 << k.gain_bits;
+  const uint32_t base2 = engine_layout_base(L, k.ncls, ng, nbuckets, 0, 2);
+  int r2 = 0, nt2 = 0, g2 = 0;
+  long cost2 = -1;
+  if (base2 + 64u + 48u * (uint32_t)k.kb <= kLdsBudget) {
+    int tmax2 = (int)((kLdsBudget - base2 - 64u) / 48u) & ~15;
+    if (tmax2 > kETileMax) tmax2 = kETileMax;
+    r2 = pick_rows_per_tile(k.rows, k.kb, tmax2, &nt2, &g2);
+    if (r2 > 0) cost2 = (long)((nt2 + g2 - 1) / g2) * ((long)r2 * k.kb + kTileOverhead);
+  }
+  const uint32_t base1 = engine_layout_base(L, k.ncls, ng, nbuckets, 0, 1);
+  const int r1 = (k.rows + kGridMax - 1) / kGridMax;
+  const long t1 = (long)r1 * k.kb;
   EArgs a = {};
-  int grid = 0;
-  a.rows_per_tile = pick_rows_per_tile(k.rows, k.kb, tmax, &a.ntiles, &grid);
-  if (a.rows_per_tile == 0) return LLVQ_EUNSUPPORTED;
+  int grid = 0, nbuf = 2;
+  if (t1 <= kETileMax && base1 + 64u + 36u * (uint32_t)t1 <= kLdsBudget &&
+      (cost2 < 0 || t1 + kTileOverhead <= cost2)) {
+    nbuf = 1;
+    a.rows_per_tile = r1;
+    a.ntiles = (k.rows + r1 - 1) / r1;
+    grid = a.ntiles;
+  } else {
+    if (r2 == 0) return LLVQ_EUNSUPPORTED;
+    a.rows_per_tile = r2;
+    a.ntiles = nt2;
+    grid = g2;
+  }
   a.nbuckets = nbuckets;
   const int T = a.rows_per_tile * k.kb;
-  engine_layout_base(a.L, k.ncls, 1 << k.gain_bits, nbuckets, T);
+  engine_layout_base(a.L, k.ncls, ng, nbuckets, T, nbuf);
   a.xs = a.L.total;
   a.xsum = 0;
   const uint32_t total = a.xs + align16(24u * (uint32_t)T);

@@ -36,6 +36,7 @@ constexpr int kBias = 12;           // value tables store 12 +- v (|v| <= 12)
 constexpr int kTail = 6;            // values resolved by the tail table
 constexpr int kSteps = 24 - kTail;  // values resolved step by step
 constexpr int kFStride = 25;        // F row length (c = 0..24)
+constexpr uint32_t kInvalidClass = 0xffu;   // queue entry class of a block to be written as zeros
 constexpr uint32_t kFRow = kFStride * 8u;   // F row in bytes
 
 // One tile's queues and block slots.
@@ -441,11 +442,11 @@ __device__ __forceinline__ UnitFields load_unit(const KDesc& d, const uint8_t* _
 // one queue reservation per parity covers the whole unit.  The common path is straight-line
 // code: an invalid block (index >= the shell-union size) is classified as block 0 of class
 // 0 and dropped.
-// With zero_bytes set, an invalid block's 24 value bytes at zero_bytes + 24 f are set to
-// the bias (value 0) for consumers that read every block's bytes.
+// With queue_invalid set, an invalid block of the tile is appended to the even queue with
+// class kInvalidClass, for consumers that write every block (its values are zero).
 __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L, const TileBuf& tb, const KDesc& d,
                                                 const UnitFields& uf, int T, int u, int lane, int32_t* err,
-                                                uint8_t* zero_bytes = nullptr) {
+                                                bool queue_invalid = false) {
   int* ctr = reinterpret_cast<int*>(smem + tb.ctr);
   uint64_t* queue = reinterpret_cast<uint64_t*>(smem + tb.queue);
   float* part = reinterpret_cast<float*>(smem + tb.part);
@@ -497,8 +498,9 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
     const bool odd = ((h.meta >> 17) & 1u) != 0u;
     // J = I - start as the low bits of 2^52 + J (exact: J < 2^41 < 2^52)
     const uint64_t jb = __builtin_bit_cast(uint64_t, Id[t] + (0x1p52 - h.start));
-    const uint32_t ehi = ((uint32_t)(jb >> 32) & 0x3ffu) | ((uint32_t)f << 10) | (k << 24);
+    const uint32_t ehi = ((uint32_t)(jb >> 32) & 0x3ffu) | ((uint32_t)f << 10) | ((valid[t] ? k : kInvalidClass) << 24);
     entry[t] = ((uint64_t)ehi << 32) | (uint32_t)jb;
+    const bool qinv = queue_invalid && f < T && !valid[t];
     const uint32_t gsh = d.shape_bits >= 32 ? (fhi[t] >> (d.shape_bits - 32))
                                             : __builtin_amdgcn_alignbit(fhi[t], flo[t], d.shape_bits);
     const uint32_t g = gsh & ((1u << d.gain_bits) - 1u);
@@ -506,7 +508,7 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
     if (f < T) part[f] = valid[t] ? sc : 0.0f;
     bad = bad || (f < T && !valid[t]);
     bo[t] = __ballot(valid[t] && odd);
-    be[t] = __ballot(valid[t] && !odd);
+    be[t] = __ballot((valid[t] && !odd) || qinv);
     po[t] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bo[t] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bo[t], 0u));
     pe[t] = __builtin_amdgcn_mbcnt_hi((uint32_t)(be[t] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be[t], 0u));
     no += __popcll(bo[t]);
@@ -516,16 +518,7 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
 #pragma unroll
     for (int t = 0; t < kPer; ++t) {
       const int f = u * kEUnit + t * 64 + lane;
-      if (f < T && !valid[t]) {
-        if (zero_bytes) {
-          uint2* zb = reinterpret_cast<uint2*>(zero_bytes + 24u * (uint32_t)f);
-          const uint2 z = make_uint2(0x0c0c0c0cu, 0x0c0c0c0cu);
-          zb[0] = z;
-          zb[1] = z;
-          zb[2] = z;
-        }
-        if (err) atomicAdd(err, 1);
-      }
+      if (f < T && !valid[t] && err) atomicAdd(err, 1);
     }
   }
   int baseo = 0, basee = 0;
@@ -548,9 +541,9 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
 
 __device__ __forceinline__ void classify_unit(uint8_t* smem, const ELayout& L, const TileBuf& tb, const KDesc& d,
                                               const uint8_t* __restrict__ packed, const TileMap& tm, int T, int u,
-                                              int lane, int32_t* err, uint8_t* zero_bytes = nullptr) {
+                                              int lane, int32_t* err, bool queue_invalid = false) {
   const UnitFields uf = load_unit(d, packed, tm, T, u, lane);
-  classify_fields(smem, L, tb, d, uf, T, u, lane, err, zero_bytes);
+  classify_fields(smem, L, tb, d, uf, T, u, lane, err, queue_invalid);
 }
 
 // Queue entry fields: J | f << 42 | k << 56 with J = I - start(k) the index inside the

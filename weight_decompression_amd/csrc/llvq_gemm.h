@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
       if (tid == 0) { ctr[0] = 0; ctr[1] = 0; work[0] = 0; }
       __syncthreads();
       const TileMap tm = {(uint32_t)(row0 * kb + b0), (uint32_t)w, (uint32_t)kb, 1.0f / (float)w};
-      if (wave * kEUnit < T) classify_unit(smem, L, L.buf[0], d, packed, tm, T, wave, lane, err, smem + tb);
+      if (wave * kEUnit < T) classify_unit(smem, L, L.buf[0], d, packed, tm, T, wave, lane, err, true);
       __syncthreads();
       const int nodd = ctr[0];
       const int neven = ctr[1];
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
         if (lane == 0) c = atomicAdd(&work[0], 1);
         c = __builtin_amdgcn_readfirstlane(c);
         if (c >= nch) break;
-        bytes_chunk(smem, L, tb, T, c, nco, nodd, neven, lane);
+        bytes_chunk(smem, L, L.buf[0], tb, T, c, nco, nodd, neven, lane);
       }
       __syncthreads();
 

@@ -9,11 +9,12 @@
 
 #pragma once
 
-// Decode chunk c of the tile into the byte tile (same chunk numbering as the GEMV).
-__device__ __forceinline__ void bytes_chunk(uint8_t* smem, const ELayout& L, uint32_t tb, int T, int c, int nco,
-                                            int nodd, int neven, int lane) {
+// Decode chunk c of a tile (queues of buffer qb) into the byte tile (same chunk numbering
+// as the GEMV).  A block queued with class kInvalidClass gets 24 zero values.
+__device__ __forceinline__ void bytes_chunk(uint8_t* smem, const ELayout& L, const TileBuf& qb, uint32_t tb, int T,
+                                            int c, int nco, int nodd, int neven, int lane) {
   const LlvqClassHot* cls = reinterpret_cast<const LlvqClassHot*>(smem + L.cls);
-  const uint64_t* queue = reinterpret_cast<const uint64_t*>(smem + L.buf[0].queue);
+  const uint64_t* queue = reinterpret_cast<const uint64_t*>(smem + qb.queue);
   if (c < nco) {
     const int e = (c << 6) + lane;
     if (e >= nodd) return;
@@ -40,6 +41,14 @@ __device__ __forceinline__ void bytes_chunk(uint8_t* smem, const ELayout& L, uin
     if (e >= neven) return;
     const uint64_t ee = queue[T - 1 - e];
     const uint32_t f = entry_f(ee);
+    if (entry_k(ee) == kInvalidClass) {
+      uint2* zb = reinterpret_cast<uint2*>(smem + tb + 24u * f);
+      const uint2 z = make_uint2(0x0c0c0c0cu, 0x0c0c0c0cu);
+      zb[0] = z;
+      zb[1] = z;
+      zb[2] = z;
+      return;
+    }
     const LlvqClassHot h = cls[entry_k(ee)];
     const BlockStart bs = block_start(smem, L, entry_J(ee), h);
     EvenDec ev;
@@ -80,34 +89,71 @@ __global__ __launch_bounds__(kEThreads) void k_decode_tile(KDesc d, EArgs a, con
   const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
   const uint32_t tb = a.xs;                 // byte tile
   const uint32_t rowbytes = (uint32_t)kb * 24u;
+  const float inv_kb = 1.0f / (float)kb;
 
+  // Tiles of this workgroup: blockIdx.x + lt * gridDim.x, queues and scale slots in buffer
+  // lt & 1.  Phase lt decodes tile lt into the byte tile and, as work runs out, classifies
+  // tile lt + 1 into the other buffer; then the byte tile is stored.  The first tile's
+  // fields are requested before the tables are staged (the grid never exceeds the tile
+  // count, so T0 >= 1; a wave without a unit reads the tile's last unit and ignores it).
+  const int row00 = blockIdx.x * a.rows_per_tile;
+  const int T0 = min(a.rows_per_tile, d.rows - row00) * kb;
+  const TileMap tm0 = {(uint32_t)(row00 * kb), (uint32_t)kb, (uint32_t)kb, inv_kb};
+  const UnitFields uf0 = load_unit(d, packed, tm0, T0, min(wave, (T0 - 1) / kEUnit), lane);
   engine_prologue(smem, L, d, a.nbuckets, scales, tid);
-  int* ctr = reinterpret_cast<int*>(smem + L.buf[0].ctr);
   int* work = reinterpret_cast<int*>(smem + L.work);
-  const float* part = reinterpret_cast<const float*>(smem + L.buf[0].part);
+  if (tid == 0) {
+    int* c0 = reinterpret_cast<int*>(smem + L.buf[0].ctr);
+    int* c1 = reinterpret_cast<int*>(smem + L.buf[1].ctr);
+    c0[0] = 0; c0[1] = 0; c1[0] = 0; c1[1] = 0; work[0] = 0; work[1] = 0;
+  }
+  __syncthreads();
+  {
+    const int nun0 = (T0 + kEUnit - 1) / kEUnit;
+    if (wave < nun0) classify_fields(smem, L, L.buf[0], d, uf0, T0, wave, lane, err, true);
+    for (;;) {
+      int u = 0;
+      if (lane == 0) u = atomicAdd(&work[1], 1);
+      u = __builtin_amdgcn_readfirstlane(u) + kEWaves;
+      if (u >= nun0) break;
+      classify_unit(smem, L, L.buf[0], d, packed, tm0, T0, u, lane, err, true);
+    }
+  }
+  __syncthreads();
 
-  for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+  int lt = 0;
+  for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x, ++lt) {
+    const TileBuf& cur = L.buf[lt & 1];
+    const TileBuf& nxt = L.buf[(lt & 1) ^ 1];
     const int row0 = tile * a.rows_per_tile;
     const int nrows = min(a.rows_per_tile, d.rows - row0);
     const int T = nrows * kb;
-    if (tid == 0) { ctr[0] = 0; ctr[1] = 0; work[0] = 0; }
-    __syncthreads();
-    const TileMap tm = {(uint32_t)(row0 * kb), (uint32_t)kb, (uint32_t)kb, 1.0f / (float)kb};
-    if (wave * kEUnit < T)
-      classify_unit(smem, L, L.buf[0], d, packed, tm, T, wave, lane, err, smem + tb);
-    __syncthreads();
+    const int* ctr = reinterpret_cast<const int*>(smem + cur.ctr);
     const int nodd = ctr[0];
     const int neven = ctr[1];
     const int nco = (nodd + 63) >> 6;
     const int nch = nco + ((neven + 63) >> 6);
+    const int tile1 = tile + gridDim.x;
+    int T1 = 0, nun1 = 0;
+    if (tile1 < a.ntiles) {
+      T1 = min(a.rows_per_tile, d.rows - tile1 * a.rows_per_tile) * kb;
+      nun1 = (T1 + kEUnit - 1) / kEUnit;
+    }
+    const TileMap tm1 = {(uint32_t)(tile1 * a.rows_per_tile * kb), (uint32_t)kb, (uint32_t)kb, inv_kb};
     for (;;) {
       int c = 0;
       if (lane == 0) c = atomicAdd(&work[0], 1);
       c = __builtin_amdgcn_readfirstlane(c);
-      if (c >= nch) break;
-      bytes_chunk(smem, L, tb, T, c, nco, nodd, neven, lane);
+      if (c < nch) {
+        bytes_chunk(smem, L, cur, tb, T, c, nco, nodd, neven, lane);
+      } else if (c < nch + nun1) {
+        classify_unit(smem, L, nxt, d, packed, tm1, T1, c - nch, lane, err, true);
+      } else {
+        break;
+      }
     }
     __syncthreads();
+    const float* part = reinterpret_cast<const float*>(smem + cur.part);
 
     // ---- store phase
     if (OUT == LLVQ_OUT_POINTS_I8) {
@@ -158,6 +204,12 @@ __global__ __launch_bounds__(kEThreads) void k_decode_tile(KDesc d, EArgs a, con
           }
         }
       }
+    }
+    if (tid == 0) {
+      int* cc = reinterpret_cast<int*>(smem + cur.ctr);
+      cc[0] = 0;
+      cc[1] = 0;
+      work[0] = 0;
     }
     __syncthreads();
   }
