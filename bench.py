@@ -46,34 +46,34 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "0797d29689142954bcb0de296f583858da7c8bd0ec9dc0e32874ff36b9348c1a",
+        "source_sha256": "59bf46ff3397cb641359250473936cd3a410099c66dbe394b9bb8f05cc332a80",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
-        "valu_lane_ops_per_unit": 672.4,       # SQ_INSTS_VALU * 64 / blocks
-        "fetch_bytes_per_launch": 12229516,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "valu_lane_ops_per_unit": 670.3,       # SQ_INSTS_VALU * 64 / blocks
+        "fetch_bytes_per_launch": 12228495,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "0797d29689142954bcb0de296f583858da7c8bd0ec9dc0e32874ff36b9348c1a",
+        "source_sha256": "59bf46ff3397cb641359250473936cd3a410099c66dbe394b9bb8f05cc332a80",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
-        "valu_lane_ops_per_unit": 803.8,
-        "fetch_bytes_per_launch": 61798731,
+        "valu_lane_ops_per_unit": 806.9,
+        "fetch_bytes_per_launch": 61800795,
         "write_bytes_per_launch": 1835008,
     },
     "decode_bf16": {
-        "source_sha256": "0797d29689142954bcb0de296f583858da7c8bd0ec9dc0e32874ff36b9348c1a",
+        "source_sha256": "59bf46ff3397cb641359250473936cd3a410099c66dbe394b9bb8f05cc332a80",
         "summary": "profiles/decode_bf16_7b_layer_k_decode_tile.md",
         "unit_of_work": "24-weight block (k_decode_tile<bf16>)",
-        "valu_lane_ops_per_unit": 721.5,
+        "valu_lane_ops_per_unit": 760.4,
         "fetch_bytes_per_launch": None,        # per-launch figures of a mixed-shape layer; see the summary
         "write_bytes_per_launch": None,
     },
     "roundtrip": {
-        "source_sha256": "0797d29689142954bcb0de296f583858da7c8bd0ec9dc0e32874ff36b9348c1a",
+        "source_sha256": "59bf46ff3397cb641359250473936cd3a410099c66dbe394b9bb8f05cc332a80",
         "summary": "profiles/roundtrip_1e7_k_decode_tile_k_rank.md",
-        "unit_of_work": "point: decode to int8 (603.8) + rank (1348.6)",
-        "valu_lane_ops_per_unit": 1952.4,
+        "unit_of_work": "point: decode to int8 (627.0) + rank (951.2)",
+        "valu_lane_ops_per_unit": 1578.2,
         "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
         "write_bytes_per_launch": None,
     },
