@@ -1,0 +1,109 @@
+// VALU issue-rate microbenchmarks for gfx950: one kernel per instruction, 16 independent
+// dependency chains per lane, each chain step a single inline-asm ALU instruction (no
+// memory access inside the timed loop).  The rate of an instruction is
+// (launched lanes x ITERS x CH) / 64 / seconds / 256 CUs / clock: wave-instructions issued
+// per CU per clock.  Used to check the VALU peak assumed for the decode kernels against the
+// instruction mix those kernels actually execute.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define ITERS 512
+#define CH 16
+
+#define K32(NAME, ASM)                                                                              \
+  __global__ __launch_bounds__(256) void NAME(uint32_t* out, uint32_t seed) {                      \
+    uint32_t a[CH];                                                                                 \
+    const uint32_t b = seed, c = seed * 3u;                                                         \
+    for (int j = 0; j < CH; ++j) a[j] = threadIdx.x * 7u + j + seed;                                \
+    for (int it = 0; it < ITERS; ++it) {                                                            \
+      _Pragma("unroll") for (int j = 0; j < CH; ++j) asm volatile(ASM : "+v"(a[j]) : "v"(b), "v"(c)); \
+    }                                                                                               \
+    uint32_t s = 0;                                                                                 \
+    for (int j = 0; j < CH; ++j) s ^= a[j];                                                         \
+    out[blockIdx.x * 256 + threadIdx.x] = s;                                                        \
+  }
+
+#define K64(NAME, ASM)                                                                              \
+  __global__ __launch_bounds__(256) void NAME(uint32_t* out, uint32_t seed) {                      \
+    double a[CH];                                                                                   \
+    const double b = 1.0 + 1e-9 * seed, c = 1e-7;                                                   \
+    for (int j = 0; j < CH; ++j) a[j] = threadIdx.x * 0.5 + j;                                      \
+    for (int it = 0; it < ITERS; ++it) {                                                            \
+      _Pragma("unroll") for (int j = 0; j < CH; ++j) asm volatile(ASM : "+v"(a[j]) : "v"(b), "v"(c)); \
+    }                                                                                               \
+    double s = 0;                                                                                   \
+    for (int j = 0; j < CH; ++j) s += a[j];                                                         \
+    out[blockIdx.x * 256 + threadIdx.x] = (uint32_t)s;                                              \
+  }
+
+// The instruction list: name (as the assembler prints it, without _e32/_e64) and its kernel.
+K32(k_add_u32, "v_add_u32 %0, %0, %1")
+K32(k_sub_u32, "v_sub_u32 %0, %0, %1")
+K32(k_and_b32, "v_and_b32 %0, %0, %1")
+K32(k_or_b32, "v_or_b32 %0, %0, %1")
+K32(k_xor_b32, "v_xor_b32 %0, %0, %1")
+K32(k_not_b32, "v_not_b32 %0, %0")
+K32(k_mov_b32, "v_mov_b32 %0, %1")
+K32(k_lshrrev_b32, "v_lshrrev_b32 %0, %1, %0")
+K32(k_lshlrev_b32, "v_lshlrev_b32 %0, %1, %0")
+// lane-select with a 64-bit mask in a scalar register pair (the form the kernels use)
+__global__ __launch_bounds__(256) void k_cndmask_b32(uint32_t* out, uint32_t seed) {
+  uint32_t a[CH];
+  const uint32_t b = seed;
+  const uint64_t m = __ballot((threadIdx.x & 1u) != 0u);
+  for (int j = 0; j < CH; ++j) a[j] = threadIdx.x * 7u + j + seed;
+  for (int it = 0; it < ITERS; ++it) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) asm volatile("v_cndmask_b32_e64 %0, %0, %1, %2" : "+v"(a[j]) : "v"(b), "s"(m));
+  }
+  uint32_t s = 0;
+  for (int j = 0; j < CH; ++j) s ^= a[j];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+K32(k_mul_f32, "v_mul_f32 %0, %0, %1")
+K32(k_add_f32, "v_add_f32 %0, %0, %1")
+K32(k_fmac_f32, "v_fmac_f32 %0, %1, %2")
+K32(k_fma_f32, "v_fma_f32 %0, %0, %1, %2")
+K32(k_cvt_f32_u32, "v_cvt_f32_u32 %0, %0")
+K32(k_cvt_f32_ubyte0, "v_cvt_f32_ubyte0 %0, %0")
+K32(k_xad_u32, "v_xad_u32 %0, %0, %1, %2")
+K32(k_ffbl_b32, "v_ffbl_b32 %0, %0")
+K32(k_bfi_b32, "v_bfi_b32 %0, %0, %1, %2")
+K32(k_bfe_u32, "v_bfe_u32 %0, %0, %1, 4")
+K32(k_alignbit_b32, "v_alignbit_b32 %0, %0, %1, %2")
+K32(k_lshl_or_b32, "v_lshl_or_b32 %0, %0, 3, %1")
+K32(k_lshl_add_u32, "v_lshl_add_u32 %0, %0, 3, %1")
+K32(k_add3_u32, "v_add3_u32 %0, %0, %1, %2")
+K32(k_and_or_b32, "v_and_or_b32 %0, %0, %1, %2")
+K32(k_or3_b32, "v_or3_b32 %0, %0, %1, %2")
+K32(k_mad_u32_u24, "v_mad_u32_u24 %0, %0, %1, %2")
+K32(k_mul_lo_u32, "v_mul_lo_u32 %0, %0, %1")
+K32(k_perm_b32, "v_perm_b32 %0, %0, %1, %2")
+K32(k_dot4_u32_u8, "v_dot4_u32_u8 %0, %0, %1, %2")
+K32(k_bcnt_u32_b32, "v_bcnt_u32_b32 %0, %0, %1")
+K32(k_med3_u32, "v_med3_u32 %0, %0, %1, %2")
+K64(k_fma_f64, "v_fma_f64 %0, %0, %1, %2")
+K64(k_mul_f64, "v_mul_f64 %0, %0, %1")
+K64(k_add_f64, "v_add_f64 %0, %0, %1")
+
+typedef void (*kfn)(uint32_t*, uint32_t);
+static const kfn kKernels[] = {
+    k_add_u32,     k_sub_u32,      k_and_b32,        k_or_b32,       k_xor_b32,      k_not_b32,      k_mov_b32,
+    k_lshrrev_b32, k_lshlrev_b32,  k_cndmask_b32,    k_mul_f32,      k_add_f32,      k_fmac_f32,     k_fma_f32,
+    k_cvt_f32_u32, k_cvt_f32_ubyte0, k_xad_u32,      k_ffbl_b32,     k_bfi_b32,      k_bfe_u32,      k_alignbit_b32,
+    k_lshl_or_b32, k_lshl_add_u32, k_add3_u32,       k_and_or_b32,   k_or3_b32,      k_mad_u32_u24,  k_mul_lo_u32,
+    k_perm_b32,    k_dot4_u32_u8,  k_bcnt_u32_b32,   k_med3_u32,     k_fma_f64,      k_mul_f64,      k_add_f64};
+
+extern "C" __attribute__((visibility("default"))) int ir_count() { return (int)(sizeof(kKernels) / sizeof(kKernels[0])); }
+
+// Instructions per chain step and per-launch geometry, for the caller's rate arithmetic.
+extern "C" __attribute__((visibility("default"))) int ir_iters() { return ITERS * CH; }
+
+// Launch kernel `which` on `blocks` workgroups of 256 lanes writing out[blocks * 256]
+// (device memory owned by the caller) on the null stream.  0 on success.
+extern "C" __attribute__((visibility("default"))) int ir_run(int which, void* out, uint32_t seed, int blocks) {
+  if (which < 0 || which >= ir_count() || blocks <= 0 || !out) return -1;
+  hipLaunchKernelGGL(kKernels[which], dim3(blocks), dim3(256), 0, 0, static_cast<uint32_t*>(out), seed);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
