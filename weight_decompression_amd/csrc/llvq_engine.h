@@ -489,7 +489,6 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
   uint64_t bo[kPer], be[kPer];
   uint64_t entry[kPer];
   uint32_t po[kPer], pe[kPer];
-  bool qo[kPer], qe[kPer];   // the lane's field goes to the odd / even queue
   bool bad = false;
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
@@ -508,10 +507,8 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
     const float sc = sg ? G[g] * h.invnorm : 1.0f;
     if (f < T) part[f] = valid[t] ? sc : 0.0f;
     bad = bad || (f < T && !valid[t]);
-    qo[t] = valid[t] && odd;
-    qe[t] = (valid[t] && !odd) || qinv;
-    bo[t] = __ballot(qo[t]);
-    be[t] = __ballot(qe[t]);
+    bo[t] = __ballot(valid[t] && odd);
+    be[t] = __ballot((valid[t] && !odd) || qinv);
     po[t] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bo[t] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bo[t], 0u));
     pe[t] = __builtin_amdgcn_mbcnt_hi((uint32_t)(be[t] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be[t], 0u));
     no += __popcll(bo[t]);
@@ -533,8 +530,10 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
   basee = __builtin_amdgcn_readfirstlane(basee);
 #pragma unroll
   for (int t = 0; t < kPer; ++t) {
-    if (qo[t]) queue[baseo + (int)po[t]] = entry[t];
-    if (qe[t]) queue[T - 1 - (basee + (int)pe[t])] = entry[t];
+    const bool odd = (bo[t] >> lane) & 1u;
+    const bool even = (be[t] >> lane) & 1u;
+    if (odd) queue[baseo + (int)po[t]] = entry[t];
+    if (even) queue[T - 1 - (basee + (int)pe[t])] = entry[t];
     baseo += __popcll(bo[t]);
     basee += __popcll(be[t]);
   }
