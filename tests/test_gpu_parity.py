@@ -294,6 +294,35 @@ def test_gemm_28672x8192_small_batch(batch):
     check_gemv(t, sample_rows(t.rows, 12, 5 + batch), f"{t.name} batch {batch}")
 
 
+@pytest.mark.parametrize("rows,cols,batch", [(37, 24 * 50 + 16, 7), (20, 24 * 3 + 8, 2), (53, 24 * 400, 16),
+                                             (16, 24 * 171, 3), (33, 24 * 700 + 8, 11)])
+def test_gemm_aligned_column_layouts(rows, cols, batch):
+    # bf16 activations with 16-byte aligned rows (cols % 8 == 0) take the matrix-core path's
+    # buffer-load form: last blocks of 8 or 16 columns, chunks narrower than one batch of
+    # four columns per wave, several column chunks, ragged row groups
+    t = synth.make_tensor("mf", 17, rows * 7 + cols, rows, cols, C10, batch=batch)
+    check_gemv(t, list(range(rows)), f"mfma {rows}x{cols} b{batch}")
+
+
+def test_gemm_unaligned_activations_match_aligned():
+    # the same activations 2 bytes off a 16-byte boundary take the per-element loads
+    t = synth.make_tensor("mfu", 18, 1, 45, 24 * 90 + 16, C10, batch=6)
+    desc, packed, scales, x = dev(t)
+    y_ref, mag = oracle_gemv(t, list(range(t.rows)))
+    outs = []
+    for off in (0, 1):
+        buf = torch.zeros(x.numel() + 8, dtype=torch.bfloat16, device="cuda")
+        buf[off:off + x.numel()] = x.reshape(-1)
+        xv = buf[off:off + x.numel()].view(x.shape)
+        y = torch.full((x.shape[0], t.rows), float("nan"), dtype=torch.float32, device="cuda")
+        wd.gemv(desc, packed, scales, xv, y)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.all(reference.gemv_within_tolerance(got, y_ref, mag)), off
+        outs.append(got)
+    assert np.array_equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("rows,cols,batch,xd", [(1, 1, 1, "f32"), (3, 23, 2, "bf16"), (5, 25, 3, "f32"),
                                                 (70, 100, 1, "bf16"), (2, 24 * 65 + 7, 16, "bf16"),
                                                 (37, 1001, 5, "bf16"), (17, 24 * 300 + 1, 9, "bf16")])

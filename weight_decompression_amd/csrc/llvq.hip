@@ -520,6 +520,8 @@ int launch_decode_tile(const KDesc& k, const void* packed, const void* scales, i
 int launch_gemm_mfma(const KDesc& k, const void* packed, const void* scales, const void* x, int batch, float* y,
                      int32_t* err, hipStream_t s) {
   if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;
+  // the activations are addressed with 32-bit buffer offsets (bit 31 marks "no data")
+  if ((uint64_t)batch * (uint64_t)k.cols * 2u + 8192u >= (1ull << 31)) return LLVQ_EUNSUPPORTED;
   const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
   ELayout L;
   const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0);
@@ -528,7 +530,8 @@ int launch_gemm_mfma(const KDesc& k, const void* packed, const void* scales, con
   if (base + red + 64u + 36u * kGRows > kLdsBudget) return LLVQ_EUNSUPPORTED;
   int tmax = (int)((kLdsBudget - base - red - 64u) / 36u);
   if (tmax > kETileMax) tmax = kETileMax;
-  const int wmax = tmax / kGRows;
+  // chunks of at most kEWaves units of kEUnit blocks: one classification unit per wave
+  const int wmax = min(tmax / kGRows, kEWaves * kEUnit / kGRows);
   GArgs g = {};
   g.nchunk = (k.kb + wmax - 1) / wmax;
   g.w = (k.kb + g.nchunk - 1) / g.nchunk;

@@ -4,13 +4,18 @@
 //
 // A workgroup owns groups of 16 rows.  The row group is processed in column chunks of
 // at most w blocks: the tile engine decodes the 16 x w blocks into the LDS byte tile,
-// then each wave runs one v_mfma_f32_16x16x32_bf16 per block column it owns:
-//   A (16 x 32): the block's 24 values of the 16 rows as exact small integers in bf16,
-//                the last 8 k zero;
-//   B (32 x 16): the block's 24 activations of every batch row, read from global memory;
-//   C (16 x 16): the block's dot products, scaled by each row's block scale and added to
-//                the wave's accumulator (the scale differs per block, so every block has
-//                its own product).
+// then each wave takes the block columns it owns through the matrix cores
+// (v_mfma_f32_16x16x32_bf16, D = A B + C):
+//   A (16 x 32): the block's 24 activations of every batch row (k 24..31 zero), read
+//                from global memory with buffer loads (lanes without data read zeros);
+//   B (32 x 16): the block's 24 biased value bytes (v + 12) of the 16 rows as exact bf16
+//                integers, with a second product against a constant -12 operand removing
+//                the bias, so the byte -> bf16 conversion is one instruction per value;
+//   D (16 x 16): the block's dot products of every (batch row, row) pair; each lane holds
+//                one weight row and four batch rows, so the block scale of the row is a
+//                single LDS read, applied with four fused multiply-adds into the wave's
+//                accumulator (the scale differs per block, so every block has its own
+//                product).
 // After the row group the 16 waves' accumulators are summed in a fixed order.  The
 // result does not depend on scheduling, and all rounding is fp32 accumulation.
 
@@ -29,14 +34,26 @@ struct GArgs {
   int batch;
 };
 
-// 8 biased value bytes -> 8 bf16 values (byte - 12, exact)
-__device__ __forceinline__ llvq_bf16x8 bytes_to_bf16x8(uint2 u) {
+// 8 biased value bytes -> 8 bf16 values of the bytes themselves (0..24, exact)
+__device__ __forceinline__ llvq_bf16x8 biased_to_bf16x8(uint2 u) {
   float v[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) v[q] = (float)(((q < 4 ? u.x : u.y) >> (8 * (q & 3))) & 0xffu) - (float)kBias;
+  for (int q = 0; q < 8; ++q) v[q] = (float)(((q < 4 ? u.x : u.y) >> (8 * (q & 3))) & 0xffu);
   const uint4 pk = make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
                               pack_bf16(v[6], v[7]));
   return __builtin_bit_cast(llvq_bf16x8, pk);
+}
+
+// One block column through the matrix cores: acc[i] += sc * sum_k xa[4 kg + i][k] (w[mr][k] - 12)
+// for this lane's weight row mr and batch rows 4 kg + i.
+__device__ __forceinline__ void mfma_column(llvq_f32x4& acc, llvq_u32x4 xa, uint2 wb, float sc,
+                                            llvq_bf16x8 m12) {
+  const llvq_bf16x8 av = __builtin_bit_cast(llvq_bf16x8, xa);
+  const llvq_f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  llvq_f32x4 cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, m12, zero, 0, 0, 0);
+  cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, biased_to_bf16x8(wb), cb, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, cb[i], acc[i]);
 }
 
 __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const uint8_t* __restrict__ packed,
@@ -58,11 +75,16 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
   engine_prologue(smem, L, d, g.e.nbuckets, scales, tid);
   int* ctr = reinterpret_cast<int*>(smem + L.buf[0].ctr);
   int* work = reinterpret_cast<int*>(smem + L.work);
-  const float* part = reinterpret_cast<const float*>(smem + L.buf[0].part);
 
-  // lane roles in the MFMA: A row / B column = lane % 16, k group = lane / 16
+  // lane roles in the MFMA: A row (batch row) / B column (weight row) = lane % 16,
+  // k group = lane / 16
   const int mr = lane & 15;
   const int kg = lane >> 4;
+  const bool xlane = kg < 3 && mr < g.batch;
+  // activations as a buffer resource: reads past the end of x return zeros
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0, g.batch * K * 2, 0x00020000);
+  const llvq_bf16x8 m12 = __builtin_bit_cast(llvq_bf16x8, llvq_u32x4{0xc140c140u, 0xc140c140u, 0xc140c140u, 0xc140c140u});
 
   for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {
     const int row0 = grp * kGRows;
@@ -74,6 +96,7 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
       const int T = nrows * w;
       if (tid == 0) { ctr[0] = 0; ctr[1] = 0; work[0] = 0; }
       __syncthreads();
+      // one classification unit per wave (chunks hold at most 16 x 256 blocks)
       const TileMap tm = {(uint32_t)(row0 * kb + b0), (uint32_t)w, (uint32_t)kb, 1.0f / (float)w};
       if (wave * kEUnit < T) classify_unit(smem, L, L.buf[0], d, packed, tm, T, wave, lane, err, true);
       __syncthreads();
@@ -90,36 +113,90 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
       }
       __syncthreads();
 
-      // ---- matrix-core phase: wave takes block columns wave, wave + 16, ...
+      // ---- matrix-core phase: wave takes block columns bl = wave + 16 j, j < ncw.  The
+      // lane (mr, kg) reads 8 value bytes of row mr at k = 8 kg (k 24..31 read the next
+      // bytes: finite values that meet zero activations), the block scale of row mr, and 8
+      // activations of batch row mr.  Rows past nrows read stale finite bytes and stale
+      // scales; they only reach accumulators of rows that are never written.
       const uint32_t rowbytes = 24u * (uint32_t)w;
-      for (int bl = wave; bl < w; bl += kEWaves) {
-        uint2 ab = make_uint2(0x0c0c0c0cu, 0x0c0c0c0cu);   // value 0
-        if (kg < 3 && mr < nrows)
-          ab = *reinterpret_cast<const uint2*>(smem + tb + (uint32_t)mr * rowbytes + 24u * (uint32_t)bl + 8u * kg);
-        const llvq_bf16x8 av = bytes_to_bf16x8(ab);
-        uint4 xb = make_uint4(0u, 0u, 0u, 0u);
-        const int col = (b0 + bl) * 24 + 8 * kg;
-        if (kg < 3 && mr < g.batch) {
-          const uint16_t* xr = x + (size_t)mr * (size_t)K;
-          if (xa16 && col + 8 <= K) {
-            xb = *reinterpret_cast<const uint4*>(xr + col);
-          } else {
-            uint32_t wv[4] = {0u, 0u, 0u, 0u};
+      const int ncw = (w - wave + kEWaves - 1) / kEWaves;
+      const uint32_t abase = tb + (uint32_t)mr * rowbytes + 24u * (uint32_t)wave + 8u * (uint32_t)kg;
+      const uint32_t pbase = L.buf[0].part + 4u * ((uint32_t)mr * (uint32_t)w + (uint32_t)wave);
+      if (xa16) {
+        // With K % 8 == 0 a lane's 8 activations are all inside the row or all past it,
+        // except in a last block of K % 24 columns, which its wave takes separately.
+        const bool tail = (K % 24 != 0) && (b0 + w == kb);
+        const int tw = (w - 1) & (kEWaves - 1);
+        const int nfast = ncw - ((tail && wave == tw) ? 1 : 0);
+        const int nfull = nfast >> 2;
+        const int rem = nfast & 3;
+        // byte offset of this lane's activations in column j = 0; column j adds 768 j
+        const uint32_t vbase = xlane ? 2u * ((uint32_t)mr * (uint32_t)K + (uint32_t)(b0 + wave) * 24u + 8u * (uint32_t)kg)
+                                     : 0x80000000u;
+        llvq_u32x4 xa[4], xb[4];
+        auto xload = [&](llvq_u32x4 (&xv)[4], int s4) {
+          const uint32_t vo = vbase + 3072u * (uint32_t)s4;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) xv[t] = __builtin_amdgcn_raw_buffer_load_b128(xrs, vo + 768u * t, 0, 0);
+        };
+        auto batch = [&](const llvq_u32x4 (&xv)[4], int s4) {
+          const uint32_t ao = abase + 1536u * (uint32_t)s4;
+          const uint32_t po = pbase + 256u * (uint32_t)s4;
+          uint2 wb[4];
+          float sc[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            wb[t] = *reinterpret_cast<const uint2*>(smem + ao + 384u * t);
+            sc[t] = *reinterpret_cast<const float*>(smem + po + 64u * t);
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) mfma_column(acc, xv[t], wb[t], sc[t], m12);
+        };
+        auto partial = [&](const llvq_u32x4 (&xv)[4], int s4) {
+#pragma unroll
+          for (int t = 0; t < 3; ++t) {
+            if (t < rem) {
+              const uint2 wb = *reinterpret_cast<const uint2*>(smem + abase + 1536u * (uint32_t)s4 + 384u * t);
+              const float sc = *reinterpret_cast<const float*>(smem + pbase + 256u * (uint32_t)s4 + 64u * t);
+              mfma_column(acc, xv[t], wb, sc, m12);
+            }
+          }
+        };
+        // batches of 4 columns, the next batch's activations requested before the current
+        // batch's products (loads past the last column read unused data or zeros)
+        xload(xa, 0);
+        int s4 = 0;
+        for (;;) {
+          if (s4 >= nfull) { if (rem) partial(xa, s4); break; }
+          xload(xb, s4 + 1);
+          batch(xa, s4);
+          ++s4;
+          if (s4 >= nfull) { if (rem) partial(xb, s4); break; }
+          xload(xa, s4 + 1);
+          batch(xb, s4);
+          ++s4;
+        }
+        if (tail && wave == tw) {
+          const int j = ncw - 1;
+          const bool in = xlane && 8 * kg < K % 24;
+          const llvq_u32x4 xv = __builtin_amdgcn_raw_buffer_load_b128(xrs, in ? vbase + 768u * (uint32_t)j : 0x80000000u, 0, 0);
+          const uint2 wb = *reinterpret_cast<const uint2*>(smem + abase + 384u * (uint32_t)j);
+          const float sc = *reinterpret_cast<const float*>(smem + pbase + 64u * (uint32_t)j);
+          mfma_column(acc, xv, wb, sc, m12);
+        }
+      } else {
+        for (int j = 0; j < ncw; ++j) {
+          const int col = (b0 + wave + kEWaves * j) * 24 + 8 * kg;
+          uint32_t wv[4] = {0u, 0u, 0u, 0u};
+          if (xlane) {
+            const uint16_t* xr = x + (size_t)mr * (size_t)K;
 #pragma unroll
             for (int q = 0; q < 8; ++q)
               if (col + q < K) wv[q >> 1] |= (uint32_t)xr[col + q] << (16 * (q & 1));
-            xb = make_uint4(wv[0], wv[1], wv[2], wv[3]);
           }
-        }
-        const llvq_bf16x8 bv = __builtin_bit_cast(llvq_bf16x8, xb);
-        const llvq_f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-        const llvq_f32x4 cb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, zero, 0, 0, 0);
-        // D rows 4 kg + i, column mr; scale of (row, block) from the engine's slot
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * kg + i;
-          const float sc = r < nrows ? part[r * w + bl] : 0.0f;
-          acc[i] = __builtin_fmaf(sc, cb[i], acc[i]);
+          const uint2 wb = *reinterpret_cast<const uint2*>(smem + abase + 384u * (uint32_t)j);
+          const float sc = *reinterpret_cast<const float*>(smem + pbase + 64u * (uint32_t)j);
+          mfma_column(acc, llvq_u32x4{wv[0], wv[1], wv[2], wv[3]}, wb, sc, m12);
         }
       }
       __syncthreads();
@@ -131,8 +208,8 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
     if (tid < kGRows * 16) {
       const int r = tid >> 4;       // row in group
       const int n = tid & 15;       // batch row
-      const int l = n + 16 * (r >> 2);
-      const int i = r & 3;
+      const int l = r + 16 * (n >> 2);
+      const int i = n & 3;
       float s = 0.0f;
       for (int wv = 0; wv < kEWaves; ++wv) s += red[(wv * 64 + l) * 4 + i];
       if (r < nrows && n < g.batch) {
