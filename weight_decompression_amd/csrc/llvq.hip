@@ -525,10 +525,11 @@ int launch_gemm_mfma(const KDesc& k, const void* packed, const void* scales, con
   const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
   ELayout L;
   const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0);
-  const uint32_t red = (uint32_t)kEWaves * 64u * 4u * 4u;
-  // per block: queue entry 8 B + scale 4 B + 24 value bytes; at least one block column
-  if (base + red + 64u + 36u * kGRows > kLdsBudget) return LLVQ_EUNSUPPORTED;
-  int tmax = (int)((kLdsBudget - base - red - 64u) / 36u);
+  const uint32_t red = (uint32_t)kEWaves * 64u * 4u * 4u;   // reduction buffer, over the byte tile
+  // per block: queue entry 8 B + two block scales 8 B + 24 value bytes; at least one
+  // block column; slack for the alignment of the three arrays
+  if (base + 64u + 40u * kGRows > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((kLdsBudget - base - 64u) / 40u);
   if (tmax > kETileMax) tmax = kETileMax;
   // chunks of at most kEWaves units of kEUnit blocks: one classification unit per wave
   const int wmax = min(tmax / kGRows, kEWaves * kEUnit / kGRows);
@@ -540,10 +541,14 @@ int launch_gemm_mfma(const KDesc& k, const void* packed, const void* scales, con
   g.e.rows_per_tile = kGRows;
   g.e.ntiles = g.ngroups;
   g.e.nbuckets = nbuckets;
-  engine_layout_base(g.e.L, k.ncls, 1 << k.gain_bits, nbuckets, kGRows * g.w);
-  g.e.xs = g.e.L.total;
-  g.e.xsum = g.e.xs + align16(24u * (uint32_t)(kGRows * g.w));
-  const uint32_t total = g.e.xsum + red;
+  const uint32_t T = (uint32_t)(kGRows * g.w);
+  engine_layout_base(g.e.L, k.ncls, 1 << k.gain_bits, nbuckets, (int)T);
+  g.part2 = g.e.L.total;
+  g.e.xs = g.part2 + align16(4u * T);
+  g.e.xsum = g.e.xs;
+  // (16 bytes past the tile: the k 24..31 lanes of the last block read 8 bytes beyond it)
+  const uint32_t tile = align16(24u * T) + 16u;
+  const uint32_t total = g.e.xs + (tile > red ? tile : red);
   if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
   const int grid = g.ngroups < kGridMax ? g.ngroups : kGridMax;
   hipLaunchKernelGGL(k_gemm_mfma, dim3(grid), dim3(kEThreads), total, s, k, g, static_cast<const uint8_t*>(packed),

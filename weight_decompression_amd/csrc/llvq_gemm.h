@@ -18,6 +18,16 @@
 //                product).
 // After the row group the 16 waves' accumulators are summed in a fixed order.  The
 // result does not depend on scheduling, and all rounding is fp32 accumulation.
+//
+// Phases of a workgroup, over its chunks q = 0, 1, ... (row groups in grid stride, column
+// chunks in order):
+//   decode q:      the chunk's queue entries -> byte tile;
+//   products q + classification q + 1: the matrix-core work of chunk q, while the waves
+//                  with a classification unit of chunk q + 1 first classify it.  The queue
+//                  is free once decode q has ended; the block scales and fill counters
+//                  alternate between two sets, so chunk q's scales stay readable.
+// One barrier ends each phase; after the last chunk of a row group the accumulators are
+// summed through the byte tile (two more barriers).
 
 #pragma once
 
@@ -27,7 +37,8 @@ typedef float llvq_f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGRows = 16;   // rows per group (MFMA M)
 
 struct GArgs {
-  EArgs e;        // engine layout; e.xs = byte tile, e.xsum = wave accumulators
+  EArgs e;        // engine layout (one tile buffer); e.xs = byte tile and reduction buffer
+  uint32_t part2; // the second block-scale array
   int w;          // blocks per column chunk
   int nchunk;     // column chunks per row group
   int ngroups;    // row groups
@@ -69,12 +80,49 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
   const int K = d.cols;
   const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
   const uint32_t tb = g.e.xs;
-  float* red = reinterpret_cast<float*>(smem + g.e.xsum);   // [kEWaves][64][4]
+  float* red = reinterpret_cast<float*>(smem + tb);   // [kEWaves][64][4], between row groups
   const bool xa16 = ((((uintptr_t)x) & 15u) == 0u) && ((K & 7) == 0);
+  int* work = reinterpret_cast<int*>(smem + L.work);   // [0] decode items, [2..3] counters of set 1
+  // scale arrays and fill counters of even / odd chunks; the queue is shared
+  const TileBuf set0 = L.buf[0];
+  const TileBuf set1 = {L.work + 8u, L.buf[0].queue, g.part2};
 
-  engine_prologue(smem, L, d, g.e.nbuckets, scales, tid);
-  int* ctr = reinterpret_cast<int*>(smem + L.buf[0].ctr);
-  int* work = reinterpret_cast<int*>(smem + L.work);
+  // chunk q of this workgroup
+  struct Chunk {
+    int grp, cc, b0, w, nrows, T;
+  };
+  auto chunk = [&](int q) {
+    Chunk c;
+    c.grp = blockIdx.x + (q / g.nchunk) * (int)gridDim.x;
+    c.cc = q % g.nchunk;
+    c.b0 = c.cc * g.w;
+    c.w = min(g.w, kb - c.b0);
+    c.nrows = min(kGRows, d.rows - c.grp * kGRows);
+    c.T = c.nrows * c.w;
+    return c;
+  };
+  auto tile_map = [&](const Chunk& c) {
+    return TileMap{(uint32_t)(c.grp * kGRows * kb + c.b0), (uint32_t)c.w, (uint32_t)kb, 1.0f / (float)c.w};
+  };
+  // the grid never exceeds the group count
+  const int nq = ((g.ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x) * g.nchunk;
+
+  // classification of chunk 0: its fields are requested before the tables are staged (a
+  // wave without a unit reads the chunk's last unit and ignores it; a chunk holds at most
+  // 16 x 256 blocks, one unit per wave)
+  {
+    const Chunk c0 = chunk(0);
+    const UnitFields uf0 = load_unit(d, packed, tile_map(c0), c0.T, min(wave, (c0.T - 1) / kEUnit), lane);
+    engine_prologue(smem, L, d, g.e.nbuckets, scales, tid);
+    if (tid == 0) {
+      int* c0c = reinterpret_cast<int*>(smem + set0.ctr);
+      int* c1c = reinterpret_cast<int*>(smem + set1.ctr);
+      c0c[0] = 0; c0c[1] = 0; c1c[0] = 0; c1c[1] = 0; work[0] = 0;
+    }
+    __syncthreads();
+    if (wave * kEUnit < c0.T) classify_fields(smem, L, set0, d, uf0, c0.T, wave, lane, err, true);
+    __syncthreads();
+  }
 
   // lane roles in the MFMA: A row (batch row) / B column (weight row) = lane % 16,
   // k group = lane / 16
@@ -86,42 +134,53 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0, g.batch * K * 2, 0x00020000);
   const llvq_bf16x8 m12 = __builtin_bit_cast(llvq_bf16x8, llvq_u32x4{0xc140c140u, 0xc140c140u, 0xc140c140u, 0xc140c140u});
 
-  for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {
-    const int row0 = grp * kGRows;
-    const int nrows = min(kGRows, d.rows - row0);
-    llvq_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int cc = 0; cc < g.nchunk; ++cc) {
-      const int b0 = cc * g.w;
-      const int w = min(g.w, kb - b0);
-      const int T = nrows * w;
-      if (tid == 0) { ctr[0] = 0; ctr[1] = 0; work[0] = 0; }
-      __syncthreads();
-      // one classification unit per wave (chunks hold at most 16 x 256 blocks)
-      const TileMap tm = {(uint32_t)(row0 * kb + b0), (uint32_t)w, (uint32_t)kb, 1.0f / (float)w};
-      if (wave * kEUnit < T) classify_unit(smem, L, L.buf[0], d, packed, tm, T, wave, lane, err, true);
-      __syncthreads();
+  llvq_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int q = 0; q < nq; ++q) {
+    const Chunk c = chunk(q);
+    const TileBuf cur = (q & 1) ? set1 : set0;
+    const TileBuf nxt = (q & 1) ? set0 : set1;
+    const int b0 = c.b0;
+    const int w = c.w;
+
+    // ---- decode of chunk q into the byte tile
+    {
+      const int* ctr = reinterpret_cast<const int*>(smem + cur.ctr);
       const int nodd = ctr[0];
       const int neven = ctr[1];
       const int nco = (nodd + 63) >> 6;
       const int nch = nco + ((neven + 63) >> 6);
-      for (;;) {
-        int c = 0;
-        if (lane == 0) c = atomicAdd(&work[0], 1);
-        c = __builtin_amdgcn_readfirstlane(c);
-        if (c >= nch) break;
-        bytes_chunk(smem, L, L.buf[0], tb, T, c, nco, nodd, neven, lane);
+      if (tid == 0) {   // counters of chunk q + 1 (last read by decode q - 1)
+        int* cn = reinterpret_cast<int*>(smem + nxt.ctr);
+        cn[0] = 0;
+        cn[1] = 0;
       }
-      __syncthreads();
+      for (;;) {
+        int ci = 0;
+        if (lane == 0) ci = atomicAdd(&work[0], 1);
+        ci = __builtin_amdgcn_readfirstlane(ci);
+        if (ci >= nch) break;
+        bytes_chunk(smem, L, cur, tb, c.T, ci, nco, nodd, neven, lane);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) work[0] = 0;
 
-      // ---- matrix-core phase: wave takes block columns bl = wave + 16 j, j < ncw.  The
-      // lane (mr, kg) reads 8 value bytes of row mr at k = 8 kg (k 24..31 read the next
-      // bytes: finite values that meet zero activations), the block scale of row mr, and 8
-      // activations of batch row mr.  Rows past nrows read stale finite bytes and stale
-      // scales; they only reach accumulators of rows that are never written.
+    // ---- classification of chunk q + 1 (waves with a unit)
+    if (q + 1 < nq) {
+      const Chunk cn = chunk(q + 1);
+      if (wave * kEUnit < cn.T) classify_unit(smem, L, nxt, d, packed, tile_map(cn), cn.T, wave, lane, err, true);
+    }
+
+    // ---- chunk q through the matrix cores: wave takes block columns bl = wave + 16 j,
+    // j < ncw.  The lane (mr, kg) reads 8 value bytes of row mr at k = 8 kg (k 24..31 read
+    // the next bytes: finite values that meet zero activations), the block scale of row
+    // mr, and 8 activations of batch row mr.  Rows past nrows read stale finite bytes and
+    // stale scales; they only reach accumulators of rows that are never written.
+    {
       const uint32_t rowbytes = 24u * (uint32_t)w;
       const int ncw = (w - wave + kEWaves - 1) / kEWaves;
       const uint32_t abase = tb + (uint32_t)mr * rowbytes + 24u * (uint32_t)wave + 8u * (uint32_t)kg;
-      const uint32_t pbase = L.buf[0].part + 4u * ((uint32_t)mr * (uint32_t)w + (uint32_t)wave);
+      const uint32_t pbase = cur.part + 4u * ((uint32_t)mr * (uint32_t)w + (uint32_t)wave);
       if (xa16) {
         // With K % 8 == 0 a lane's 8 activations are all inside the row or all past it,
         // except in a last block of K % 24 columns, which its wave takes separately.
@@ -131,8 +190,8 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
         const int nfull = nfast >> 2;
         const int rem = nfast & 3;
         // byte offset of this lane's activations in column j = 0; column j adds 768 j
-        const uint32_t vbase = xlane ? 2u * ((uint32_t)mr * (uint32_t)K + (uint32_t)(b0 + wave) * 24u + 8u * (uint32_t)kg)
-                                     : 0x80000000u;
+        const uint32_t vbase =
+            xlane ? 2u * ((uint32_t)mr * (uint32_t)K + (uint32_t)(b0 + wave) * 24u + 8u * (uint32_t)kg) : 0x80000000u;
         llvq_u32x4 xa[4], xb[4];
         auto xload = [&](llvq_u32x4 (&xv)[4], int s4) {
           const uint32_t vo = vbase + 3072u * (uint32_t)s4;
@@ -167,11 +226,17 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
         xload(xa, 0);
         int s4 = 0;
         for (;;) {
-          if (s4 >= nfull) { if (rem) partial(xa, s4); break; }
+          if (s4 >= nfull) {
+            if (rem) partial(xa, s4);
+            break;
+          }
           xload(xb, s4 + 1);
           batch(xa, s4);
           ++s4;
-          if (s4 >= nfull) { if (rem) partial(xb, s4); break; }
+          if (s4 >= nfull) {
+            if (rem) partial(xb, s4);
+            break;
+          }
           xload(xa, s4 + 1);
           batch(xb, s4);
           ++s4;
@@ -179,7 +244,8 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
         if (tail && wave == tw) {
           const int j = ncw - 1;
           const bool in = xlane && 8 * kg < K % 24;
-          const llvq_u32x4 xv = __builtin_amdgcn_raw_buffer_load_b128(xrs, in ? vbase + 768u * (uint32_t)j : 0x80000000u, 0, 0);
+          const llvq_u32x4 xv =
+              __builtin_amdgcn_raw_buffer_load_b128(xrs, in ? vbase + 768u * (uint32_t)j : 0x80000000u, 0, 0);
           const uint2 wb = *reinterpret_cast<const uint2*>(smem + abase + 384u * (uint32_t)j);
           const float sc = *reinterpret_cast<const float*>(smem + pbase + 64u * (uint32_t)j);
           mfma_column(acc, xv, wb, sc, m12);
@@ -191,31 +257,38 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
           if (xlane) {
             const uint16_t* xr = x + (size_t)mr * (size_t)K;
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-              if (col + q < K) wv[q >> 1] |= (uint32_t)xr[col + q] << (16 * (q & 1));
+            for (int e = 0; e < 8; ++e)
+              if (col + e < K) wv[e >> 1] |= (uint32_t)xr[col + e] << (16 * (e & 1));
           }
           const uint2 wb = *reinterpret_cast<const uint2*>(smem + abase + 384u * (uint32_t)j);
           const float sc = *reinterpret_cast<const float*>(smem + pbase + 64u * (uint32_t)j);
           mfma_column(acc, llvq_u32x4{wv[0], wv[1], wv[2], wv[3]}, wb, sc, m12);
         }
       }
-      __syncthreads();
     }
-    // ---- reduce the waves' accumulators in a fixed order
+
+    // ---- after the row group's last chunk: sum the waves' accumulators in a fixed order
+    // (the byte tile is free once every wave's products are done)
+    if (c.cc == g.nchunk - 1) {
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(wave * 64 + lane) * 4 + i] = acc[i];
-    __syncthreads();
-    if (tid < kGRows * 16) {
-      const int r = tid >> 4;       // row in group
-      const int n = tid & 15;       // batch row
-      const int l = r + 16 * (n >> 2);
-      const int i = n & 3;
-      float s = 0.0f;
-      for (int wv = 0; wv < kEWaves; ++wv) s += red[(wv * 64 + l) * 4 + i];
-      if (r < nrows && n < g.batch) {
-        const float rs = sg ? 1.0f : __half2float(scales[row0 + r]);
-        y[(size_t)n * d.rows + row0 + r] = s * rs;
+      for (int i = 0; i < 4; ++i) red[(wave * 64 + lane) * 4 + i] = acc[i];
+      __syncthreads();
+      if (tid < kGRows * 16) {
+        const int r = tid >> 4;       // row in group
+        const int n = tid & 15;       // batch row
+        const int l = r + 16 * (n >> 2);
+        const int i = n & 3;
+        float s = 0.0f;
+        for (int wv = 0; wv < kEWaves; ++wv) s += red[(wv * 64 + l) * 4 + i];
+        if (r < c.nrows && n < g.batch) {
+          const int row = c.grp * kGRows + r;
+          const float rs = sg ? 1.0f : __half2float(scales[row]);
+          y[(size_t)n * d.rows + row] = s * rs;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = 0.0f;
     }
     __syncthreads();
   }
