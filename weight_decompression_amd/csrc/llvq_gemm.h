@@ -162,14 +162,17 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
         bytes_chunk(smem, L, cur, tb, c.T, ci, nco, nodd, neven, lane);
       }
     }
+    // fields of this wave's classification unit of chunk q + 1, requested as the wave runs
+    // out of decode work so that they arrive during the wait for the other waves
+    const bool more = q + 1 < nq;
+    const Chunk cn = chunk(more ? q + 1 : q);
+    UnitFields uf;
+    if (more && wave * kEUnit < cn.T) uf = load_unit(d, packed, tile_map(cn), cn.T, wave, lane);
     __syncthreads();
     if (tid == 0) work[0] = 0;
 
     // ---- classification of chunk q + 1 (waves with a unit)
-    if (q + 1 < nq) {
-      const Chunk cn = chunk(q + 1);
-      if (wave * kEUnit < cn.T) classify_unit(smem, L, nxt, d, packed, tile_map(cn), cn.T, wave, lane, err, true);
-    }
+    if (more && wave * kEUnit < cn.T) classify_fields(smem, L, nxt, d, uf, cn.T, wave, lane, err, true);
 
     // ---- chunk q through the matrix cores: wave takes block columns bl = wave + 16 j,
     // j < ncw.  The lane (mr, kg) reads 8 value bytes of row mr at k = 8 kg (k 24..31 read
