@@ -538,6 +538,7 @@ int launch_gemm_mfma(const KDesc& k, const void* packed, const void* scales, con
   g.w = (k.kb + g.nchunk - 1) / g.nchunk;
   g.ngroups = (k.rows + kGRows - 1) / kGRows;
   g.batch = batch;
+  g.rbal = 24;   // measured on 28672 x 8192, batch 2..16 (a unit classifies 256 blocks)
   g.e.rows_per_tile = kGRows;
   g.e.ntiles = g.ngroups;
   g.e.nbuckets = nbuckets;

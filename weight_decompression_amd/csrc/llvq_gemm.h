@@ -39,6 +39,7 @@ constexpr int kGRows = 16;   // rows per group (MFMA M)
 struct GArgs {
   EArgs e;        // engine layout (one tile buffer); e.xs = byte tile and reduction buffer
   uint32_t part2; // the second block-scale array
+  int rbal;       // block columns that weigh as much as one classification unit
   int w;          // blocks per column chunk
   int nchunk;     // column chunks per row group
   int ngroups;    // row groups
@@ -53,6 +54,24 @@ __device__ __forceinline__ llvq_bf16x8 biased_to_bf16x8(uint2 u) {
   const uint4 pk = make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
                               pack_bf16(v[6], v[7]));
   return __builtin_bit_cast(llvq_bf16x8, pk);
+}
+
+// Block columns [*cb, *cb + *n) of wave `wave` among w columns, when waves 0..ncls-1 also
+// classify one unit each and a unit weighs as much as `rbal` columns: every wave gets the
+// same total weight as far as whole columns allow (a fixed function of its arguments, so
+// the accumulation order does not depend on scheduling).
+__device__ __forceinline__ void column_range(int w, int ncls, int rbal, int wave, int* cb, int* n) {
+  const int nfree = kEWaves - ncls;
+  if (nfree > 0 && w < nfree * rbal) {   // the waves without a unit take every column
+    const int a = w / nfree, r = w % nfree, i = wave - ncls;
+    *cb = i < 0 ? 0 : i * a + min(i, r);
+    *n = i < 0 ? 0 : a + (i < r ? 1 : 0);
+    return;
+  }
+  const int base = w - nfree * rbal;   // columns beyond the waves' unit weights
+  const int b = base / kEWaves, r = base % kEWaves;
+  *cb = wave * b + min(wave, r) + rbal * max(0, wave - ncls);
+  *n = b + (wave < r ? 1 : 0) + (wave >= ncls ? rbal : 0);
 }
 
 // One block column through the matrix cores: acc[i] += sc * sum_k xa[4 kg + i][k] (w[mr][k] - 12)
@@ -174,42 +193,42 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
     // ---- classification of chunk q + 1 (waves with a unit)
     if (more && wave * kEUnit < cn.T) classify_fields(smem, L, nxt, d, uf, cn.T, wave, lane, err, true);
 
-    // ---- chunk q through the matrix cores: wave takes block columns bl = wave + 16 j,
-    // j < ncw.  The lane (mr, kg) reads 8 value bytes of row mr at k = 8 kg (k 24..31 read
-    // the next bytes: finite values that meet zero activations), the block scale of row
-    // mr, and 8 activations of batch row mr.  Rows past nrows read stale finite bytes and
-    // stale scales; they only reach accumulators of rows that are never written.
+    // ---- chunk q through the matrix cores: wave takes the block columns [cb, cb + ncw).
+    // The lane (mr, kg) reads 8 value bytes of row mr at k = 8 kg (k 24..31 read the next
+    // bytes: finite values that meet zero activations), the block scale of row mr, and 8
+    // activations of batch row mr.  Rows past nrows read stale finite bytes and stale
+    // scales; they only reach accumulators of rows that are never written.
     {
+      int cb, ncw;
+      column_range(w, more ? min(kEWaves, (cn.T + kEUnit - 1) / kEUnit) : 0, g.rbal, wave, &cb, &ncw);
       const uint32_t rowbytes = 24u * (uint32_t)w;
-      const int ncw = (w - wave + kEWaves - 1) / kEWaves;
-      const uint32_t abase = tb + (uint32_t)mr * rowbytes + 24u * (uint32_t)wave + 8u * (uint32_t)kg;
-      const uint32_t pbase = cur.part + 4u * ((uint32_t)mr * (uint32_t)w + (uint32_t)wave);
+      const uint32_t abase = tb + (uint32_t)mr * rowbytes + 24u * (uint32_t)cb + 8u * (uint32_t)kg;
+      const uint32_t pbase = cur.part + 4u * ((uint32_t)mr * (uint32_t)w + (uint32_t)cb);
       if (xa16) {
         // With K % 8 == 0 a lane's 8 activations are all inside the row or all past it,
         // except in a last block of K % 24 columns, which its wave takes separately.
-        const bool tail = (K % 24 != 0) && (b0 + w == kb);
-        const int tw = (w - 1) & (kEWaves - 1);
-        const int nfast = ncw - ((tail && wave == tw) ? 1 : 0);
+        const bool tail = (K % 24 != 0) && (b0 + w == kb) && ncw > 0 && cb + ncw == w;
+        const int nfast = ncw - (tail ? 1 : 0);
         const int nfull = nfast >> 2;
         const int rem = nfast & 3;
-        // byte offset of this lane's activations in column j = 0; column j adds 768 j
+        // byte offset of this lane's activations in column j = 0; column j adds 48 j
         const uint32_t vbase =
-            xlane ? 2u * ((uint32_t)mr * (uint32_t)K + (uint32_t)(b0 + wave) * 24u + 8u * (uint32_t)kg) : 0x80000000u;
+            xlane ? 2u * ((uint32_t)mr * (uint32_t)K + (uint32_t)(b0 + cb) * 24u + 8u * (uint32_t)kg) : 0x80000000u;
         llvq_u32x4 xa[4], xb[4];
         auto xload = [&](llvq_u32x4 (&xv)[4], int s4) {
-          const uint32_t vo = vbase + 3072u * (uint32_t)s4;
+          const uint32_t vo = vbase + 192u * (uint32_t)s4;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) xv[t] = __builtin_amdgcn_raw_buffer_load_b128(xrs, vo + 768u * t, 0, 0);
+          for (int t = 0; t < 4; ++t) xv[t] = __builtin_amdgcn_raw_buffer_load_b128(xrs, vo + 48u * t, 0, 0);
         };
         auto batch = [&](const llvq_u32x4 (&xv)[4], int s4) {
-          const uint32_t ao = abase + 1536u * (uint32_t)s4;
-          const uint32_t po = pbase + 256u * (uint32_t)s4;
+          const uint32_t ao = abase + 96u * (uint32_t)s4;
+          const uint32_t po = pbase + 16u * (uint32_t)s4;
           uint2 wb[4];
           float sc[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            wb[t] = *reinterpret_cast<const uint2*>(smem + ao + 384u * t);
-            sc[t] = *reinterpret_cast<const float*>(smem + po + 64u * t);
+            wb[t] = *reinterpret_cast<const uint2*>(smem + ao + 24u * t);
+            sc[t] = *reinterpret_cast<const float*>(smem + po + 4u * t);
           }
 #pragma unroll
           for (int t = 0; t < 4; ++t) mfma_column(acc, xv[t], wb[t], sc[t], m12);
@@ -218,8 +237,8 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
 #pragma unroll
           for (int t = 0; t < 3; ++t) {
             if (t < rem) {
-              const uint2 wb = *reinterpret_cast<const uint2*>(smem + abase + 1536u * (uint32_t)s4 + 384u * t);
-              const float sc = *reinterpret_cast<const float*>(smem + pbase + 256u * (uint32_t)s4 + 64u * t);
+              const uint2 wb = *reinterpret_cast<const uint2*>(smem + abase + 96u * (uint32_t)s4 + 24u * t);
+              const float sc = *reinterpret_cast<const float*>(smem + pbase + 16u * (uint32_t)s4 + 4u * t);
               mfma_column(acc, xv[t], wb, sc, m12);
             }
           }
@@ -244,18 +263,18 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
           batch(xb, s4);
           ++s4;
         }
-        if (tail && wave == tw) {
+        if (tail) {
           const int j = ncw - 1;
           const bool in = xlane && 8 * kg < K % 24;
           const llvq_u32x4 xv =
-              __builtin_amdgcn_raw_buffer_load_b128(xrs, in ? vbase + 768u * (uint32_t)j : 0x80000000u, 0, 0);
-          const uint2 wb = *reinterpret_cast<const uint2*>(smem + abase + 384u * (uint32_t)j);
-          const float sc = *reinterpret_cast<const float*>(smem + pbase + 64u * (uint32_t)j);
+              __builtin_amdgcn_raw_buffer_load_b128(xrs, in ? vbase + 48u * (uint32_t)j : 0x80000000u, 0, 0);
+          const uint2 wb = *reinterpret_cast<const uint2*>(smem + abase + 24u * (uint32_t)j);
+          const float sc = *reinterpret_cast<const float*>(smem + pbase + 4u * (uint32_t)j);
           mfma_column(acc, xv, wb, sc, m12);
         }
       } else {
         for (int j = 0; j < ncw; ++j) {
-          const int col = (b0 + wave + kEWaves * j) * 24 + 8 * kg;
+          const int col = (b0 + cb + j) * 24 + 8 * kg;
           uint32_t wv[4] = {0u, 0u, 0u, 0u};
           if (xlane) {
             const uint16_t* xr = x + (size_t)mr * (size_t)K;
@@ -263,8 +282,8 @@ __global__ __launch_bounds__(kEThreads) void k_gemm_mfma(KDesc d, GArgs g, const
             for (int e = 0; e < 8; ++e)
               if (col + e < K) wv[e >> 1] |= (uint32_t)xr[col + e] << (16 * (e & 1));
           }
-          const uint2 wb = *reinterpret_cast<const uint2*>(smem + abase + 384u * (uint32_t)j);
-          const float sc = *reinterpret_cast<const float*>(smem + pbase + 64u * (uint32_t)j);
+          const uint2 wb = *reinterpret_cast<const uint2*>(smem + abase + 24u * (uint32_t)j);
+          const float sc = *reinterpret_cast<const float*>(smem + pbase + 4u * (uint32_t)j);
           mfma_column(acc, llvq_u32x4{wv[0], wv[1], wv[2], wv[3]}, wb, sc, m12);
         }
       }
