@@ -46,23 +46,23 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "59bf46ff3397cb641359250473936cd3a410099c66dbe394b9bb8f05cc332a80",
+        "source_sha256": "e7ef51fb352c9bcc09a67daeec50ab75473c498c8335924b045a7c2b76c7b40a",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
         "valu_lane_ops_per_unit": 670.3,       # SQ_INSTS_VALU * 64 / blocks
-        "fetch_bytes_per_launch": 12228495,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "fetch_bytes_per_launch": 12228493,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "59bf46ff3397cb641359250473936cd3a410099c66dbe394b9bb8f05cc332a80",
+        "source_sha256": "e7ef51fb352c9bcc09a67daeec50ab75473c498c8335924b045a7c2b76c7b40a",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
-        "valu_lane_ops_per_unit": 806.9,
-        "fetch_bytes_per_launch": 61800795,
+        "valu_lane_ops_per_unit": 695.4,
+        "fetch_bytes_per_launch": 61928800,
         "write_bytes_per_launch": 1835008,
     },
     "decode_bf16": {
-        "source_sha256": "59bf46ff3397cb641359250473936cd3a410099c66dbe394b9bb8f05cc332a80",
+        "source_sha256": "e7ef51fb352c9bcc09a67daeec50ab75473c498c8335924b045a7c2b76c7b40a",
         "summary": "profiles/decode_bf16_7b_layer_k_decode_tile.md",
         "unit_of_work": "24-weight block (k_decode_tile<bf16>)",
         "valu_lane_ops_per_unit": 760.4,
@@ -70,7 +70,7 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": None,
     },
     "roundtrip": {
-        "source_sha256": "59bf46ff3397cb641359250473936cd3a410099c66dbe394b9bb8f05cc332a80",
+        "source_sha256": "e7ef51fb352c9bcc09a67daeec50ab75473c498c8335924b045a7c2b76c7b40a",
         "summary": "profiles/roundtrip_1e7_k_decode_tile_k_rank.md",
         "unit_of_work": "point: decode to int8 (627.0) + rank (951.2)",
         "valu_lane_ops_per_unit": 1578.2,
