@@ -22,7 +22,13 @@ pattern and permutation follow in closed form:
 
 Both objectives reduce to max <x, v> inside one class because the norm is constant on
 a class.  Exact ties between candidates are broken towards the smaller global index.
-The tests pin this against literal enumeration of whole shells.
+The angular objective does not see the scale of v, so a shell-8 point 2u whose half u
+is a lattice point ties exactly with u (shell 2); the fp64 objectives of the two are
+computed along different paths and need not come out equal, so that tie is resolved
+explicitly: a shell-8 winner of that form is replaced by u, whose index is smaller
+(indices ascend with the shell).  Within shells 2..10 this is the only collinear pair
+(k v needs shell k^2 m <= 10).  The tests pin this against literal enumeration of whole
+shells.
 """
 
 import numpy as np
@@ -30,6 +36,7 @@ import numpy as np
 from . import golay
 from .bijection import rank
 from .classes import class_table
+from .leech import in_leech
 
 DIM = 24
 
@@ -165,7 +172,21 @@ def search(x, M, mode="angular"):
             c = T[pos]
             v = _odd_point(x, cl, c) if cl.parity == 1 else _even_point(x, cl, c)
             candidates.append((rank(v, M), v))
-    return min(candidates, key=lambda t: t[0])
+    I, v = min(candidates, key=lambda t: t[0])
+    if mode == "angular":
+        u = primitive_half(v)
+        if u is not None:
+            return rank(u, M), u
+    return I, v
+
+
+def primitive_half(v):
+    """u = v / 2 when v is in shell 8 and u is a lattice point (then u is in shell 2 and
+    ties with v under the angular objective), else None."""
+    if sum(int(a) * int(a) for a in v) != 16 * 8 or any(int(a) % 2 for a in v):
+        return None
+    u = [int(a) // 2 for a in v]
+    return u if in_leech(u) else None
 
 
 def nearest_gain(norm, gains):

@@ -96,3 +96,38 @@ def test_shape_gain_fidelity_band():
 def test_nearest_gain_ties_go_low():
     assert search.nearest_gain(1.5, [1.0, 2.0, 3.0]) == 0
     assert search.nearest_gain(2.9, [1.0, 2.0, 3.0]) == 2
+
+
+def test_angular_collinear_tie_goes_to_the_shell2_point(shell2_points):
+    # The angular objective ignores |v|: u (shell 2) and 2u (shell 8) tie exactly, and the
+    # smaller index is u's.  x = u (and x = 2u) must come back as u with M = 10.
+    rng = np.random.default_rng(3)
+    C2 = leech.index_count(2)
+    for I in rng.integers(0, C2, size=6):
+        u = [int(a) for a in shell2_points[int(I)]]
+        for x in (np.array(u, dtype=np.float64), 2.0 * np.array(u, dtype=np.float64)):
+            J, v = search.search(x, 10, "angular")
+            assert (J, v) == (int(I), u)
+        assert search.primitive_half([2 * a for a in u]) == u
+
+
+def test_primitive_half_only_for_halvable_shell8_points(shell2_points):
+    # a shell-8 point with even coordinates halves to a lattice point exactly when its half
+    # is one of the enumerated shell-2 points
+    s2 = {tuple(int(a) for a in p) for p in shell2_points}
+    rng = np.random.default_rng(4)
+    lo, hi = leech.index_count(7), leech.index_count(8)
+    seen_even = 0
+    for I in rng.integers(lo, hi, size=4000):
+        v = bijection.unrank(int(I), 8)
+        h = search.primitive_half(v)
+        if all(a % 2 == 0 for a in v):
+            seen_even += 1
+            half = tuple(a // 2 for a in v)
+            assert (h is not None) == (half in s2)
+            if h is not None:
+                assert tuple(h) == half
+        else:
+            assert h is None
+    assert seen_even > 0
+    assert search.primitive_half(bijection.unrank(5, 10)) is None      # a shell-2 point
