@@ -65,6 +65,7 @@ enum {
 enum { LLVQ_MODE_EUCLID = 0, LLVQ_MODE_SHAPEGAIN = 1 };
 enum { LLVQ_OUT_POINTS_I8 = 0, LLVQ_OUT_BF16 = 1 };
 enum { LLVQ_X_F32 = 0, LLVQ_X_BF16 = 1 };
+enum { LLVQ_SEARCH_ANGULAR = 0, LLVQ_SEARCH_EUCLID = 1 };
 
 #define LLVQ_MAX_BATCH 16
 
@@ -129,6 +130,30 @@ int llvq_gemv(const llvq_desc* d, const void* packed, const void* scales, const 
  * Returns LLVQ_OK, LLVQ_EINVAL or LLVQ_EHIP. */
 int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell, uint64_t* indices,
                     int32_t* err_count, void* stream);
+
+/* Quantise: nearest point of the shell union 2..M to each 24-vector, and its index
+ * (papernotes.org notes, 关键设计 1: the single-shell search extended to the union of
+ * shells 2..M, with an angular objective for shape-gain and a Euclidean one for spherical
+ * shaping; gist.science page, Methodik / 2. Multi-Shell Search).  Exhaustive over every
+ * class and every Golay codeword it can use, so the result is the exact optimum up to
+ * fp32 rounding of the objective.
+ *   x         : fp32 [n][24] input vectors, 4-byte aligned.  EUCLID takes them in the
+ *               lattice's integer units (sqrt(8) x standard coordinates, shell m has
+ *               squared norm 16 m).
+ *   n         : number of vectors, >= 0 (0 is a no-op).
+ *   max_shell : M in [2, 10].
+ *   objective : LLVQ_SEARCH_ANGULAR maximises <x, v> / |v| (scale-free: collinear points
+ *               of different shells tie); LLVQ_SEARCH_EUCLID minimises |x - v|^2.
+ *   points    : int8 [n][24] output, the chosen points (any alignment; also the input of
+ *               the rank step that follows on the same stream).
+ *   indices   : uint64 [n] output, the points' shape indices (8-byte aligned).
+ *   err_count : nullable; a vector with a non-finite coordinate gets the
+ *               zero point and index UINT64_MAX and is counted.
+ * Exact float ties of the objective go to a fixed candidate order (not necessarily the
+ * smaller index).  Both outputs are written on `stream`; the call allocates nothing.
+ * Returns LLVQ_OK, LLVQ_EINVAL or LLVQ_EHIP. */
+int llvq_search(const float* x, int64_t n, int32_t max_shell, int32_t objective, int8_t* points,
+                uint64_t* indices, int32_t* err_count, void* stream);
 
 #ifdef __cplusplus
 }

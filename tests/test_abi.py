@@ -92,6 +92,19 @@ def test_encode_validation_and_empty(lib):
     assert lib.llvq_encode_ref(None, 0, 10, None, None, None) == 0                       # empty: no-op
 
 
+def test_search_validation_and_empty(lib):
+    p = ctypes.c_void_p(0x10000)
+    assert lib.llvq_search(p, 10, 1, 0, p, p, None, None) == -1                           # max_shell < 2
+    assert lib.llvq_search(p, 10, 11, 0, p, p, None, None) == -1                          # max_shell > 10
+    assert lib.llvq_search(p, 10, 10, 2, p, p, None, None) == -1                          # bad objective
+    assert lib.llvq_search(p, -1, 10, 0, p, p, None, None) == -1                          # negative n
+    assert lib.llvq_search(None, 10, 10, 0, p, p, None, None) == -1                       # null x
+    assert lib.llvq_search(p, 10, 10, 0, None, p, None, None) == -1                       # null points
+    assert lib.llvq_search(p, 10, 10, 1, p, ctypes.c_void_p(0x10004), None, None) == -1   # indices alignment
+    assert lib.llvq_search(ctypes.c_void_p(0x10002), 10, 10, 0, p, p, None, None) == -1   # x alignment
+    assert lib.llvq_search(None, 0, 10, 0, None, None, None, None) == 0                   # empty: no-op
+
+
 def test_error_strings(lib):
     for code in (0, -1, -2, -3, 42):
         assert isinstance(lib.llvq_error_string(code), bytes)

@@ -1,0 +1,140 @@
+"""GPU parity of the nearest-point search (llvq_search) against the CPU oracle's exact
+class x codeword search (oracle/search.py).
+
+The search picks a maximum of a float objective, so the bar is: the GPU's index equals
+the oracle's; where it does not, both candidates are optimal up to rounding (their
+objectives, recomputed in fp64 from the two points, agree to 1e-6 relative), which can
+only happen on a near-tie such as collinear points of different shells under the angular
+objective.  Every GPU index must rank its GPU point (checked with the oracle's bijection)
+and lie in shells 2..M.  Inputs: seeded Gaussian blocks, the fidelity rows of the
+MLP-shaped workload (dense N(0, 0.02^2) weights, whose oracle search results are stored
+under tests/golden/), and perturbed lattice points.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import weight_decompression_amd as wd
+from oracle import bijection, leech, search
+from weight_decompression_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+MODES = {"angular": wd.SEARCH_ANGULAR, "euclid": wd.SEARCH_EUCLID}
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    wd.load_library()
+    torch.cuda.init()
+    yield
+
+
+def gpu_search(x, M, mode):
+    xt = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    n = xt.shape[0]
+    pts = torch.empty((n, 24), dtype=torch.int8, device="cuda")
+    idx = torch.empty(n, dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.search(xt, M, MODES[mode], pts, idx, err)
+    torch.cuda.synchronize()
+    return pts.cpu().numpy().astype(np.int64), idx.cpu().numpy().view(np.uint64), int(err.item())
+
+
+def objective(x, v, mode):
+    v = np.asarray(v, dtype=np.float64)
+    s = float(np.dot(np.asarray(x, dtype=np.float64), v))
+    m = float(np.dot(v, v)) / 16.0
+    return s / (4.0 * np.sqrt(m)) if mode == "angular" else 2.0 * s - 16.0 * m
+
+
+def check_against(x, want_idx, M, mode, label):
+    """GPU search of blocks x against the oracle's indices want_idx."""
+    pts, idx, err = gpu_search(x, M, mode)
+    assert err == 0, label
+    C = leech.index_count(M)
+    assert np.all(idx < C), label
+    diff = np.nonzero(idx != np.asarray(want_idx, dtype=np.uint64))[0]
+    for i in diff:
+        gv = bijection.unrank(int(idx[i]), M)
+        ov = bijection.unrank(int(want_idx[i]), M)
+        assert list(pts[i]) == gv, (label, i)
+        og, oo = objective(x[i], gv, mode), objective(x[i], ov, mode)
+        assert og >= oo - 1e-6 * (1.0 + abs(oo)), (label, i, og, oo)
+    # the GPU point of a sample of agreeing blocks is the unranked index
+    for i in range(0, len(x), max(1, len(x) // 16)):
+        assert list(pts[i]) == bijection.unrank(int(idx[i]), M), (label, i)
+    say(f"{label}: {len(x)} blocks, {len(diff)} near-tie differences from the oracle")
+    assert len(diff) <= len(x) // 1000, label   # fp32 vs fp64 near-ties are rare
+    return pts, idx
+
+
+@pytest.mark.parametrize("mode,M,scale", [("angular", 10, 1.0), ("euclid", 10, 2.2), ("angular", 2, 1.0),
+                                          ("euclid", 3, 1.6), ("angular", 6, 0.3), ("euclid", 5, 1.9)])
+def test_search_matches_oracle_on_gaussian_blocks(mode, M, scale):
+    rng = np.random.default_rng(100 + M + (mode == "euclid"))
+    x = (rng.standard_normal((96, 24)) * scale).astype(np.float32)
+    want = [search.search(x[i].astype(np.float64), M, mode)[0] for i in range(len(x))]
+    check_against(x, want, M, mode, f"{mode} M={M}")
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_search_reproduces_fidelity_fixture(which):
+    # the stored oracle results of the MLP-shaped workload's first 64 rows (angular, M = 10)
+    rows, cols = ((11008, 4096), (4096, 11008))[which]
+    fx = np.load(os.path.join(HERE, "golden", f"fidelity_c3_{which}.npz"))
+    want = fx["shape_idx"]
+    nrows, kb = want.shape
+    W = synth.fidelity_weights(3, which, nrows, cols)
+    wpad = np.zeros((nrows, kb * 24), dtype=np.float32)
+    wpad[:, :cols] = W
+    x = wpad.reshape(-1, 24)
+    check_against(x, want.reshape(-1), 10, "angular", f"fidelity rows {rows}x{cols}")
+
+
+def test_search_recovers_perturbed_lattice_points():
+    # Euclidean: a point plus noise well inside its Voronoi cell comes back exactly
+    rng = np.random.default_rng(5)
+    C = leech.index_count(10)
+    I = rng.integers(0, C, size=200, dtype=np.uint64)
+    v = np.array([bijection.unrank(int(i), 10) for i in I], dtype=np.float64)
+    x = (v + rng.uniform(-0.4, 0.4, size=v.shape)).astype(np.float32)
+    pts, idx, err = gpu_search(x, 10, "euclid")
+    assert err == 0
+    assert np.array_equal(idx, I.astype(np.uint64))
+    assert np.array_equal(pts, v.astype(np.int64))
+
+
+def test_search_many_blocks_grid_stride_and_edge_inputs():
+    # more vectors than workgroups in the grid, plus a zero vector (every angular objective
+    # ties at 0: any point is optimal) and a vector with a NaN coordinate
+    rng = np.random.default_rng(9)
+    n = 20000
+    x = rng.standard_normal((n, 24)).astype(np.float32)
+    x[7] = 0.0
+    x[11, 3] = np.nan
+    pts, idx, err = gpu_search(x, 10, "angular")
+    assert err == 1
+    assert idx[11] == np.uint64(2**64 - 1) and not pts[11].any()
+    ok = np.ones(n, dtype=bool)
+    ok[11] = False
+    assert np.all(idx[ok] < leech.index_count(10))
+    assert list(pts[7]) == bijection.unrank(int(idx[7]), 10)
+    for i in rng.choice(np.nonzero(ok)[0], size=24, replace=False):
+        if i == 7:
+            continue
+        I, _ = search.search(x[i].astype(np.float64), 10, "angular")
+        if I != idx[i]:
+            og = objective(x[i], bijection.unrank(int(idx[i]), 10), "angular")
+            oo = objective(x[i], bijection.unrank(int(I), 10), "angular")
+            assert og >= oo - 1e-6 * (1.0 + abs(oo)), i

@@ -15,6 +15,8 @@ OUT_POINTS_I8 = 0
 OUT_BF16 = 1
 X_F32 = 0
 X_BF16 = 1
+SEARCH_ANGULAR = 0
+SEARCH_EUCLID = 1
 MAX_BATCH = 16
 
 _ERRORS = {0: "ok", -1: "invalid argument", -2: "unsupported request", -3: "HIP launch error"}
@@ -22,7 +24,7 @@ _ERRORS = {0: "ok", -1: "invalid argument", -2: "unsupported request", -3: "HIP 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllvq.so")
 
 EXPORTED_SYMBOLS = ("llvq_index_count", "llvq_packed_bytes", "llvq_error_string",
-                    "llvq_decode", "llvq_gemv", "llvq_encode_ref")
+                    "llvq_decode", "llvq_gemv", "llvq_encode_ref", "llvq_search")
 
 
 class LlvqError(RuntimeError):
@@ -73,6 +75,8 @@ def load_library(path=LIB_PATH):
     lib.llvq_gemv.restype = ctypes.c_int
     lib.llvq_encode_ref.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.llvq_encode_ref.restype = ctypes.c_int
+    lib.llvq_search.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
+    lib.llvq_search.restype = ctypes.c_int
     _libs[path] = lib
     return lib
 
@@ -135,3 +139,12 @@ def encode_ref(points, max_shell, indices, err_count=None, stream=None):
     n = points.shape[0] if points.dim() > 1 else points.numel() // 24
     _check(load_library().llvq_encode_ref(_ptr(points), n, max_shell, _ptr(indices), _ptr(err_count),
                                           _stream(stream)), "llvq_encode_ref")
+
+
+def search(x, max_shell, objective, points, indices, err_count=None, stream=None):
+    """Nearest point of shells 2..max_shell to each fp32 24-vector x [n][24]
+    (SEARCH_ANGULAR or SEARCH_EUCLID): int8 points [n][24] and uint64 indices [n]
+    (int64 tensor) are written."""
+    n = x.shape[0] if x.dim() > 1 else x.numel() // 24
+    _check(load_library().llvq_search(_ptr(x), n, max_shell, objective, _ptr(points), _ptr(indices),
+                                      _ptr(err_count), _stream(stream)), "llvq_search")

@@ -2,7 +2,8 @@
 
 Steps:
   1. compile the host table generator (csrc/gen_tables.cpp) with g++;
-  2. run it to write the table header (and a JSON dump of the same tables);
+  2. run it to write the table header (and a JSON dump of the same tables) and the
+     generated device code of the nearest-point search;
   3. compile csrc/llvq.hip for gfx950 with hipcc into weight_decompression_amd/libllvq.so.
 
 Generated files go to <repo>/_build/ (not committed).  Packed-fp32 VALU instructions
@@ -22,6 +23,7 @@ BUILD_DIR = os.path.join(REPO_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libllvq.so")
 TABLES_INC = os.path.join(BUILD_DIR, "llvq_tables.inc")
 TABLES_JSON = os.path.join(BUILD_DIR, "llvq_tables.json")
+SEARCH_INC = os.path.join(BUILD_DIR, "llvq_search.inc")
 GEN_BIN = os.path.join(BUILD_DIR, "gen_tables")
 
 OFFLOAD_ARCH = "gfx950"
@@ -38,6 +40,7 @@ def build_tables(verbose=True):
     _run(["g++", "-O2", "-std=c++17", "-Wall", "-o", GEN_BIN, os.path.join(CSRC, "gen_tables.cpp")], verbose)
     _run([GEN_BIN, "--header", TABLES_INC], verbose)
     _run([GEN_BIN, "--json", TABLES_JSON], verbose)
+    _run([GEN_BIN, "--search", SEARCH_INC], verbose)
 
 
 def hipcc_path():

@@ -45,6 +45,19 @@ namespace dev_tables {
 #undef LLVQ_TABLE
 }  // namespace dev_tables
 
+// key order of the generated sorting network (floats, or unsigned integer keys)
+__device__ __forceinline__ float llvq_kmin(float a, float b) { return __builtin_fminf(a, b); }
+__device__ __forceinline__ float llvq_kmax(float a, float b) { return __builtin_fmaxf(a, b); }
+__device__ __forceinline__ uint32_t llvq_kmin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint32_t llvq_kmax(uint32_t a, uint32_t b) { return a < b ? b : a; }
+
+// nearest-point search: sorting network, class records and per-class objectives
+namespace dev_tables {
+#define LLVQ_TABLE __device__ const
+#include "llvq_search.inc"
+#undef LLVQ_TABLE
+}  // namespace dev_tables
+
 namespace {
 
 constexpr int kDim = 24;
@@ -299,6 +312,7 @@ __global__ __launch_bounds__(256) void k_gemv(KDesc d, const uint8_t* __restrict
 }
 
 #include "llvq_rank.h"
+#include "llvq_search.h"
 
 // ---------------------------------------------------------------------------
 // host side
@@ -641,6 +655,24 @@ LLVQ_API int llvq_gemv(const llvq_desc* d, const void* packed, const void* scale
     default:
       return LLVQ_EINVAL;
   }
+}
+
+LLVQ_API int llvq_search(const float* x, int64_t n, int32_t max_shell, int32_t objective, int8_t* points,
+                         uint64_t* indices, int32_t* err_count, void* stream) {
+  if (max_shell < 2 || max_shell > LLVQ_MAX_SHELL || n < 0) return LLVQ_EINVAL;
+  if (objective != LLVQ_SEARCH_ANGULAR && objective != LLVQ_SEARCH_EUCLID) return LLVQ_EINVAL;
+  if (n == 0) return LLVQ_OK;
+  if (!x || !points || !indices || !aligned(x, 4) || !aligned(indices, 8)) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const unsigned grid = n < 8192 ? (unsigned)n : 8192u;
+  if (objective == LLVQ_SEARCH_EUCLID)
+    hipLaunchKernelGGL((k_search<true>), dim3(grid), dim3(kSearchThreads), 0, s, x, n, max_shell, points);
+  else
+    hipLaunchKernelGGL((k_search<false>), dim3(grid), dim3(kSearchThreads), 0, s, x, n, max_shell, points);
+  const int st = launch_status();
+  if (st != LLVQ_OK) return st;
+  return llvq_encode_ref(points, n, max_shell, indices, err_count, stream);
 }
 
 LLVQ_API int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell, uint64_t* indices,

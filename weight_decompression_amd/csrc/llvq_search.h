@@ -1,0 +1,265 @@
+// Nearest-point search over the shell union 2..M (gfx950).  Included once by llvq.hip.
+//
+// The quantiser step before the decode path: for each 24-vector x find the point v of
+// shells 2..M of the Leech lattice that maximises <x, v> / |v| (angular, shape-gain) or
+// minimises |x - v|^2 (Euclidean, x in the lattice's integer units) (papernotes.org notes,
+// 关键设计 1: search extended from one shell to the union of shells with an angular or a
+// Euclidean objective; gist.science page, Methodik / 2. Multi-Shell Search).
+//
+// Exhaustive over every class of shells 2..M and every Golay codeword the class can use.
+// Inside one (class, codeword) pair the best point is fixed by the rearrangement
+// inequality, so the objective is a short fixed expression in prefix sums of sorted
+// coordinates (both objectives are <x, v> up to a per-class constant, since |v| is
+// constant on a class):
+//   odd coset, codeword c:  y_i = x_i (i in c) or -x_i; the class's values b (b = a if
+//     a = 1 mod 4, else -a) paired in ascending order with ascending y;
+//   even coset, weight-w codeword c: ascending |x| on the support paired with the
+//     ascending support values, likewise on the complement, signs following x; when the
+//     support's count of negative x has the wrong parity the support entry with the
+//     smallest |x| flips, costing 2 min|x| times the smallest support value.
+// The sorting network and the per-class expressions are generated at build time
+// (llvq_search.inc, from the class table).
+//
+// One 256-lane workgroup per vector: lane l scores the odd coset's codewords l + 256 j
+// (every odd class for each), then its share of each codeword weight of the even coset
+// (the classes of that weight).  The workgroup keeps the largest objective; exact float
+// ties go to the smaller candidate number (even codeword position, or 4096 + odd codeword
+// position) across lanes and to the earlier codeword within a lane.  Wavefront 0 then
+// rebuilds the winner: the argmax class for that codeword, the coordinates by ranking
+// (ties by position, as a stable sort), and writes the int8 point.  Under the angular
+// objective a winner 2u in shell 8 with u a lattice point is replaced by u: the two tie
+// exactly, u has the smaller index, and within shells 2..10 this is the only collinear
+// pair.  A vector with a non-finite coordinate gets the zero vector, which the rank step
+// rejects.
+
+#pragma once
+
+constexpr int kSearchThreads = 256;
+constexpr int kSearchNone = 0x7fffffff;
+
+// objective maximum over the classes of one even-coset weight (classes of shells <= M)
+template <bool EUCLID, int W>
+__device__ __forceinline__ float search_even_max(const float (&Ss)[W + 1], const float (&Sc)[25 - W], float pen0,
+                                                 float pen1, int M) {
+  using namespace dev_tables;
+  if constexpr (W == 0) return EUCLID ? llvq_even0_max_euclid(Ss, Sc, pen0, pen1, M) : llvq_even0_max_angular(Ss, Sc, pen0, pen1, M);
+  if constexpr (W == 8) return EUCLID ? llvq_even8_max_euclid(Ss, Sc, pen0, pen1, M) : llvq_even8_max_angular(Ss, Sc, pen0, pen1, M);
+  if constexpr (W == 12) return EUCLID ? llvq_even12_max_euclid(Ss, Sc, pen0, pen1, M) : llvq_even12_max_angular(Ss, Sc, pen0, pen1, M);
+  if constexpr (W == 16) return EUCLID ? llvq_even16_max_euclid(Ss, Sc, pen0, pen1, M) : llvq_even16_max_angular(Ss, Sc, pen0, pen1, M);
+  if constexpr (W == 24) return EUCLID ? llvq_even24_max_euclid(Ss, Sc, pen0, pen1, M) : llvq_even24_max_angular(Ss, Sc, pen0, pen1, M);
+  return -__builtin_inff();
+}
+
+template <bool EUCLID, int W>
+__device__ __forceinline__ int search_even_argmax(const float (&Ss)[W + 1], const float (&Sc)[25 - W], float pen0,
+                                                  float pen1, int M, float* best) {
+  using namespace dev_tables;
+  if constexpr (W == 0) return EUCLID ? llvq_even0_argmax_euclid(Ss, Sc, pen0, pen1, M, best) : llvq_even0_argmax_angular(Ss, Sc, pen0, pen1, M, best);
+  if constexpr (W == 8) return EUCLID ? llvq_even8_argmax_euclid(Ss, Sc, pen0, pen1, M, best) : llvq_even8_argmax_angular(Ss, Sc, pen0, pen1, M, best);
+  if constexpr (W == 12) return EUCLID ? llvq_even12_argmax_euclid(Ss, Sc, pen0, pen1, M, best) : llvq_even12_argmax_angular(Ss, Sc, pen0, pen1, M, best);
+  if constexpr (W == 16) return EUCLID ? llvq_even16_argmax_euclid(Ss, Sc, pen0, pen1, M, best) : llvq_even16_argmax_angular(Ss, Sc, pen0, pen1, M, best);
+  if constexpr (W == 24) return EUCLID ? llvq_even24_argmax_euclid(Ss, Sc, pen0, pen1, M, best) : llvq_even24_argmax_angular(Ss, Sc, pen0, pen1, M, best);
+  return -1;
+}
+
+// Prefix sums of one even-coset codeword: keys = |x| bits with bit 31 set off the support,
+// sorted as unsigned integers, give the ascending support values then the ascending
+// complement values.  pen_pi = -2 min|x| on the support when the support's negative count
+// has parity != pi, else 0.
+template <int W>
+__device__ __forceinline__ void even_sums(const uint32_t (&ab)[24], uint32_t xneg, uint32_t c, float (&Ss)[W + 1],
+                                          float (&Sc)[25 - W], float* pen0, float* pen1) {
+  uint32_t k[24];
+#pragma unroll
+  for (int i = 0; i < 24; ++i) k[i] = ab[i] | ((~c << (31 - i)) & 0x80000000u);
+  dev_tables::llvq_sort24(k);
+  Ss[0] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < W; ++t) Ss[t + 1] = Ss[t] + __uint_as_float(k[t]);
+  Sc[0] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 24 - W; ++t) Sc[t + 1] = Sc[t] + __uint_as_float(k[W + t] & 0x7fffffffu);
+  const bool odd_neg = (__builtin_popcount(c & xneg) & 1) != 0;
+  const float m2 = W ? -2.0f * __uint_as_float(k[0]) : 0.0f;
+  *pen0 = odd_neg ? m2 : 0.0f;
+  *pen1 = odd_neg ? 0.0f : m2;
+}
+
+// prefix sums of the ascending y of one odd-coset codeword
+__device__ __forceinline__ void odd_sums(const float (&xv)[24], uint32_t c, float (&S)[25]) {
+  float y[24];
+#pragma unroll
+  for (int i = 0; i < 24; ++i) y[i] = __uint_as_float(__float_as_uint(xv[i]) ^ ((~c << (31 - i)) & 0x80000000u));
+  dev_tables::llvq_sort24(y);
+  S[0] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 24; ++t) S[t + 1] = S[t] + y[t];
+}
+
+// the lane's share of the weight-W codewords (positions off .. off + count - 1 of the table)
+template <bool EUCLID, int W>
+__device__ __forceinline__ void search_even_weight(const uint32_t (&ab)[24], uint32_t xneg, int M, int off, int count,
+                                                   int tid, float* best, int* cand) {
+  for (int p = off + tid; p < off + count; p += kSearchThreads) {
+    const uint32_t c = dev_tables::kGolayTable[p];
+    float Ss[W + 1], Sc[25 - W], pen0, pen1;
+    even_sums<W>(ab, xneg, c, Ss, Sc, &pen0, &pen1);
+    const float o = search_even_max<EUCLID, W>(Ss, Sc, pen0, pen1, M);
+    if (o > *best) {
+      *best = o;
+      *cand = p;
+    }
+  }
+}
+
+// Winner of an even-coset codeword: class, then lane i < 24 returns coordinate i.
+template <bool EUCLID, int W>
+__device__ __forceinline__ int even_point(const float (&xv)[24], const uint32_t (&ab)[24], uint32_t xneg, uint32_t c,
+                                          int M, int lane) {
+  float Ss[W + 1], Sc[25 - W], pen0, pen1, best;
+  even_sums<W>(ab, xneg, c, Ss, Sc, &pen0, &pen1);
+  const int k = search_even_argmax<EUCLID, W>(Ss, Sc, pen0, pen1, M, &best);
+  if (k < 0) return 0;
+  const dev_tables::LlvqSearchClass& sc = dev_tables::kSearchClass[k];
+  int v = 0;
+  bool on = false;
+  int rank = 0;
+  if (lane < 24) {
+    on = (c >> lane) & 1u;
+    uint32_t me = 0u;
+#pragma unroll
+    for (int j = 0; j < 24; ++j) me = j == lane ? ab[j] : me;
+#pragma unroll
+    for (int j = 0; j < 24; ++j) {
+      const bool same_side = (((c >> j) & 1u) != 0u) == on;
+      rank += (same_side && (ab[j] < me || (ab[j] == me && j < lane))) ? 1 : 0;
+    }
+    const int a = sc.vals[on ? rank : W + rank];
+    v = ((xneg >> lane) & 1u) ? -a : a;
+  }
+  // parity of the support's negative entries; the wrong parity flips the smallest |x|
+  const uint64_t negm = __ballot(lane < 24 && on && v < 0);
+  if (W > 0 && (int)(__popcll(negm) & 1) != (int)sc.pi && lane < 24 && on && rank == 0) v = -v;
+  return v;
+}
+
+template <bool EUCLID>
+__global__ __launch_bounds__(kSearchThreads) void k_search(const float* __restrict__ x, int64_t n, int M,
+                                                           int8_t* __restrict__ pts) {
+  __shared__ float rv[kSearchThreads / 64];
+  __shared__ int rc[kSearchThreads / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int64_t blk = blockIdx.x; blk < n; blk += gridDim.x) {
+    float xv[24];
+    uint32_t ab[24];
+    uint32_t xneg = 0u;
+    bool finite = true;
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      xv[i] = x[blk * 24 + i];
+      ab[i] = __float_as_uint(xv[i]) & 0x7fffffffu;
+      xneg |= (xv[i] < 0.0f ? 1u : 0u) << i;
+      finite = finite && ab[i] < 0x7f800000u;
+    }
+    float best = -__builtin_inff();
+    int cand = kSearchNone;
+    if (finite) {
+      // ---- even coset, by support weight (positions of each weight in the sorted table)
+      search_even_weight<EUCLID, 0>(ab, xneg, M, 0, 1, tid, &best, &cand);
+      search_even_weight<EUCLID, 8>(ab, xneg, M, 1, 759, tid, &best, &cand);
+      search_even_weight<EUCLID, 12>(ab, xneg, M, 760, 2576, tid, &best, &cand);
+      search_even_weight<EUCLID, 16>(ab, xneg, M, 3336, 759, tid, &best, &cand);
+      search_even_weight<EUCLID, 24>(ab, xneg, M, 4095, 1, tid, &best, &cand);
+      // ---- odd coset: every codeword against every odd class
+      for (int j = 0; j < 4096 / kSearchThreads; ++j) {
+        const int pos = tid + kSearchThreads * j;
+        float S[25];
+        odd_sums(xv, dev_tables::kGolayTable[pos], S);
+        const float o = EUCLID ? dev_tables::llvq_odd_max_euclid(S, M) : dev_tables::llvq_odd_max_angular(S, M);
+        if (o > best) {
+          best = o;
+          cand = 4096 + pos;
+        }
+      }
+    }
+    // ---- largest objective of the workgroup; ties to the smaller candidate number
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ob = __shfl_xor(best, off, 64);
+      const int oc = __shfl_xor(cand, off, 64);
+      if (ob > best || (ob == best && oc < cand)) {
+        best = ob;
+        cand = oc;
+      }
+    }
+    if (lane == 0) {
+      rv[wave] = best;
+      rc[wave] = cand;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      float b = rv[0];
+      int cd = rc[0];
+#pragma unroll
+      for (int w = 1; w < kSearchThreads / 64; ++w)
+        if (rv[w] > b || (rv[w] == b && rc[w] < cd)) {
+          b = rv[w];
+          cd = rc[w];
+        }
+      int v = 0;
+      if (cd != kSearchNone && cd >= 4096) {
+        const uint32_t c = dev_tables::kGolayTable[cd - 4096];
+        float S[25], ob;
+        odd_sums(xv, c, S);
+        const int k = EUCLID ? dev_tables::llvq_odd_argmax_euclid(S, M, &ob) : dev_tables::llvq_odd_argmax_angular(S, M, &ob);
+        if (k >= 0 && lane < 24) {
+          // rank of y_lane among the 24 y (ties by position)
+          float yv[24];
+#pragma unroll
+          for (int i = 0; i < 24; ++i) yv[i] = __uint_as_float(__float_as_uint(xv[i]) ^ ((~c << (31 - i)) & 0x80000000u));
+          float me = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 24; ++j) me = j == lane ? yv[j] : me;
+          int rank = 0;
+#pragma unroll
+          for (int j = 0; j < 24; ++j) rank += (yv[j] < me || (yv[j] == me && j < lane)) ? 1 : 0;
+          const int bv = dev_tables::kSearchClass[k].vals[rank];
+          v = ((c >> lane) & 1u) ? bv : -bv;
+        }
+      } else if (cd != kSearchNone) {
+        const uint32_t c = dev_tables::kGolayTable[cd];
+        switch (__builtin_popcount(c)) {
+          case 0: v = even_point<EUCLID, 0>(xv, ab, xneg, c, M, lane); break;
+          case 8: v = even_point<EUCLID, 8>(xv, ab, xneg, c, M, lane); break;
+          case 12: v = even_point<EUCLID, 12>(xv, ab, xneg, c, M, lane); break;
+          case 16: v = even_point<EUCLID, 16>(xv, ab, xneg, c, M, lane); break;
+          default: v = even_point<EUCLID, 24>(xv, ab, xneg, c, M, lane); break;
+        }
+      }
+      if (!EUCLID) {
+        // The angular objective ignores |v|: a shell-8 point 2u with u in the lattice ties
+        // exactly with u (shell 2), whose index is smaller, and u is the answer (fp32
+        // rounding need not have seen the tie).
+        int n2 = lane < 24 ? v * v : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) n2 += __shfl_xor(n2, off, 64);
+        const uint64_t oddc = __ballot(lane < 24 && (v & 1) != 0);
+        if (n2 == 16 * 8 && oddc == 0u) {
+          const int u = v / 2;
+          const int p = __shfl(u, 0, 64) & 1;
+          const uint64_t par = __ballot(lane < 24 && (u & 1) != p);
+          int su = lane < 24 ? u : 0;
+#pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) su += __shfl_xor(su, off, 64);
+          const uint32_t mask = (uint32_t)__ballot(lane < 24 && (u & 3) == (p ? 1 : 2)) & 0xffffffu;
+          const bool cw = dev_tables::kGolayTable[dev_tables::kGolayInfoPos[(mask >> 11) & 0xfffu]] == mask;
+          if (par == 0u && ((su - 4 * p) & 7) == 0 && cw) v = u;
+        }
+      }
+      if (lane < 24) pts[blk * 24 + lane] = (int8_t)v;
+    }
+    __syncthreads();   // rv / rc are rewritten for the next vector
+  }
+}
