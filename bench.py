@@ -20,6 +20,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-rows R] [--no-
        python bench.py --workload {gemv_11008x4096,gemv_4096x4096,gemv_28672x8192} [--batch B]
        python bench.py --workload decode_bf16_7b [--layers 32]
        python bench.py --workload roundtrip [--points 100000000]
+       python bench.py --workload search [--cpu-blocks 2048]
 The other workloads print one line each in the same format (their own metric).
 """
 
@@ -46,23 +47,23 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "e7ef51fb352c9bcc09a67daeec50ab75473c498c8335924b045a7c2b76c7b40a",
+        "source_sha256": "5e30e8e6495a05c5f8ef907c800352cca1fd4b2b619a2dcdd50060cca0922c1d",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
         "valu_lane_ops_per_unit": 670.3,       # SQ_INSTS_VALU * 64 / blocks
-        "fetch_bytes_per_launch": 12228493,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "fetch_bytes_per_launch": 12226438,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "e7ef51fb352c9bcc09a67daeec50ab75473c498c8335924b045a7c2b76c7b40a",
+        "source_sha256": "5e30e8e6495a05c5f8ef907c800352cca1fd4b2b619a2dcdd50060cca0922c1d",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
         "valu_lane_ops_per_unit": 695.4,
-        "fetch_bytes_per_launch": 61928800,
+        "fetch_bytes_per_launch": 61927806,
         "write_bytes_per_launch": 1835008,
     },
     "decode_bf16": {
-        "source_sha256": "e7ef51fb352c9bcc09a67daeec50ab75473c498c8335924b045a7c2b76c7b40a",
+        "source_sha256": "5e30e8e6495a05c5f8ef907c800352cca1fd4b2b619a2dcdd50060cca0922c1d",
         "summary": "profiles/decode_bf16_7b_layer_k_decode_tile.md",
         "unit_of_work": "24-weight block (k_decode_tile<bf16>)",
         "valu_lane_ops_per_unit": 760.4,
@@ -70,10 +71,18 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": None,
     },
     "roundtrip": {
-        "source_sha256": "e7ef51fb352c9bcc09a67daeec50ab75473c498c8335924b045a7c2b76c7b40a",
+        "source_sha256": "5e30e8e6495a05c5f8ef907c800352cca1fd4b2b619a2dcdd50060cca0922c1d",
         "summary": "profiles/roundtrip_1e7_k_decode_tile_k_rank.md",
         "unit_of_work": "point: decode to int8 (627.0) + rank (951.2)",
         "valu_lane_ops_per_unit": 1578.2,
+        "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
+        "write_bytes_per_launch": None,
+    },
+    "search": {
+        "source_sha256": "5e30e8e6495a05c5f8ef907c800352cca1fd4b2b619a2dcdd50060cca0922c1d",
+        "summary": "profiles/search_4096x4096_k_search_k_rank.md",
+        "unit_of_work": "24-block: search (4643368.8) + rank (955.4)",
+        "valu_lane_ops_per_unit": 4644324.2,
         "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
         "write_bytes_per_launch": None,
     },
@@ -322,9 +331,55 @@ def run_roundtrip(a):
     return out
 
 
+def run_search(a):
+    """Quantise a 4096x4096 tensor of dense N(0, 0.02^2) weights: the exact angular search
+    over shells 2..10 for each of its 24-blocks (zero-padded past the last column), then the
+    rank of each chosen point (llvq_search)."""
+    import numpy as np
+    import torch
+    import weight_decompression_amd as wd
+    from weight_decompression_amd import synth
+
+    lib = wd.load_library()
+    rows, cols, M = 4096, 4096, 10
+    kb = synth.blocks_per_row(cols)
+    W = synth.fidelity_weights(2, 0, rows, cols)
+    wpad = np.zeros((rows, kb * 24), dtype=np.float32)
+    wpad[:, :cols] = W
+    blocks = wpad.reshape(-1, 24)
+    n = blocks.shape[0]
+    x = torch.from_numpy(blocks).cuda()
+    pts = torch.empty((n, 24), dtype=torch.int8, device="cuda:0")
+    idx = torch.empty(n, dtype=torch.int64, device="cuda:0")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    args = (ctypes.c_void_p(x.data_ptr()), n, M, wd.SEARCH_ANGULAR, ctypes.c_void_p(pts.data_ptr()),
+            ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(err.data_ptr()), sptr)
+    sec, wall = time_steps(lambda i: lib.llvq_search(*args), a.steps, a.warmup, stream)
+    if int(err.item()) != 0:
+        raise RuntimeError("search reported invalid points")
+    out = base_line("LLVQ quantisation throughput (exact multi-shell angular search + rank), 1 MI355X",
+                    n / sec, "blocks/s", a.steps, a.warmup, sec, "f32",
+                    f"llvq_search angular, shells 2..{M}, {rows}x{cols} dense N(0, 0.02^2) weights",
+                    {"rows": rows, "cols": cols, "blocks": n, "max_shell": M})
+    out["weights_per_s"] = rows * cols / sec
+    out["roofline"] = roofline("search", n, sec, n * (96 + 24 + 8),
+                               "96 B fp32 block read + 24 B point written + 8 B index written")
+    out["wall_s_timed"] = wall
+    if not a.no_cpu:
+        from oracle import cpu_baseline as cb
+        sample = blocks[: a.cpu_blocks].astype(np.float64)
+        dt, procs = cb.time_search(sample, M, "angular")
+        out["cpu_baseline"] = {"value": len(sample) / dt, "unit": "blocks/s", "cores": procs, "kind": "oracle",
+                               "sample": f"the first {len(sample)} blocks of the same tensor: exact class x "
+                                         f"codeword search in numpy, {procs} processes, {dt:.2f} s wall"}
+    return out
+
+
 DEFAULT_WORKLOAD = "gemv_4096x11008"
 WORKLOADS = ("gemv_4096x11008", "gemv_11008x4096", "gemv_4096x4096", "gemv_28672x8192", "decode_bf16_7b",
-             "roundtrip")
+             "roundtrip", "search")
 
 
 def main():
@@ -339,6 +394,7 @@ def main():
     ap.add_argument("--batch", type=int, default=1, help="activation rows (GEMV workloads)")
     ap.add_argument("--layers", type=int, default=32, help="layers of the 7B-shaped set (decode_bf16_7b)")
     ap.add_argument("--points", type=int, default=100_000_000, help="indices in the round trip")
+    ap.add_argument("--cpu-blocks", type=int, default=2048, help="blocks the CPU oracle search is timed on (search)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB mebibytes (HBM counter calibration)")
     a = ap.parse_args()
@@ -384,6 +440,8 @@ def main():
                        f"llvq_gemv 2-bit shape-gain 28672x8192, batch {a.batch}")
     elif w == "decode_bf16_7b":
         out = run_decode_7b(a)
+    elif w == "search":
+        out = run_search(a)
     else:
         out = run_roundtrip(a)
     print(json.dumps(out), flush=True)

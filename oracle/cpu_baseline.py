@@ -33,3 +33,27 @@ def time_gemv_rows(packed, rows, cols, M, mode, shape_bits, gain_bits, gains, ro
         dt = time.perf_counter() - t0
     assert done == len(row_list)
     return dt, len(args)
+
+
+def _search_chunk(args):
+    blocks, M, mode = args
+    from . import search
+    for b in blocks:
+        search.search(b, M, mode)
+    return len(blocks)
+
+
+def time_search(blocks, M, mode, procs=None):
+    """Wall seconds for the oracle's exact search (oracle/search.py) of every block in
+    `blocks` (float64 [n][24]) over a process pool, and the number of processes used."""
+    procs = procs or os.cpu_count() or 1
+    procs = max(1, min(procs, len(blocks)))
+    chunks = [blocks[i::procs] for i in range(procs)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(procs) as pool:
+        pool.map(_search_chunk, [(blocks[:1], M, mode)] * procs)   # warm the per-process tables
+        t0 = time.perf_counter()
+        done = sum(pool.map(_search_chunk, [(c, M, mode) for c in chunks]))
+        dt = time.perf_counter() - t0
+    assert done == len(blocks)
+    return dt, procs
