@@ -20,11 +20,15 @@
 // The sorting network and the per-class expressions are generated at build time
 // (llvq_search.inc, from the class table).
 //
-// One 256-lane workgroup per vector: lane l scores the odd coset's codewords l + 256 j
-// (every odd class for each), then its share of each codeword weight of the even coset
-// (the classes of that weight).  The workgroup keeps the largest objective; exact float
-// ties go to the smaller candidate number (even codeword position, or 4096 + odd codeword
-// position) across lanes and to the earlier codeword within a lane.  Wavefront 0 then
+// One 256-lane workgroup per vector.  The all-ones word is a codeword, so codewords come
+// in complement pairs (c, ~c) and one sort serves both: in the odd coset y(~c) = -y(c),
+// in the even coset the support of ~c is the complement of c.  Lane l takes the even
+// coset's pairs l + 256 j (weight-8 words with their weight-16 complements, weight-12
+// words with bit 23 clear, and the pair of weights 0 and 24), then the odd coset's pairs
+// (representatives with bit 23 clear), scoring every class the pair's weights admit.
+// The workgroup keeps the largest objective; exact float ties go to the smaller candidate
+// number (the codeword mask, plus 2^24 in the odd coset) across lanes and to the earlier
+// candidate within a lane.  Wavefront 0 then
 // rebuilds the winner: the argmax class for that codeword, the coordinates by ranking
 // (ties by position, as a stable sort), and writes the int8 point.  Under the angular
 // objective a winner 2u in shell 8 with u a lattice point is replaced by u: the two tie
@@ -96,19 +100,28 @@ __device__ __forceinline__ void odd_sums(const float (&xv)[24], uint32_t c, floa
   for (int t = 0; t < 24; ++t) S[t + 1] = S[t] + y[t];
 }
 
-// the lane's share of the weight-W codewords (positions off .. off + count - 1 of the table)
+// An even-coset complement pair: representative c of weight W and ~c of weight 24 - W
+// share one sort (the support of ~c is the complement of c).  Candidates are numbered by
+// their codeword mask (even coset: bit 24 clear).
 template <bool EUCLID, int W>
-__device__ __forceinline__ void search_even_weight(const uint32_t (&ab)[24], uint32_t xneg, int M, int off, int count,
-                                                   int tid, float* best, int* cand) {
-  for (int p = off + tid; p < off + count; p += kSearchThreads) {
-    const uint32_t c = dev_tables::kGolayTable[p];
-    float Ss[W + 1], Sc[25 - W], pen0, pen1;
-    even_sums<W>(ab, xneg, c, Ss, Sc, &pen0, &pen1);
-    const float o = search_even_max<EUCLID, W>(Ss, Sc, pen0, pen1, M);
-    if (o > *best) {
-      *best = o;
-      *cand = p;
-    }
+__device__ __forceinline__ void search_even_pair(const uint32_t (&ab)[24], uint32_t xneg, uint32_t c, int M,
+                                                 float* best, int* cand) {
+  float Ss[W + 1], Sc[25 - W], pen0, pen1;
+  even_sums<W>(ab, xneg, c, Ss, Sc, &pen0, &pen1);
+  const float o = search_even_max<EUCLID, W>(Ss, Sc, pen0, pen1, M);
+  if (o > *best) {
+    *best = o;
+    *cand = (int)c;
+  }
+  // ~c: negative count on its support = all negatives minus those on c's support; its
+  // smallest support |x| is c's smallest complement |x| = Sc[1]
+  const uint32_t cc = ~c & 0xffffffu;
+  const bool odd_neg = (__builtin_popcount(cc & xneg) & 1) != 0;
+  const float m2 = W < 24 ? -2.0f * Sc[1] : 0.0f;
+  const float o2 = search_even_max<EUCLID, 24 - W>(Sc, Ss, odd_neg ? m2 : 0.0f, odd_neg ? 0.0f : m2, M);
+  if (o2 > *best) {
+    *best = o2;
+    *cand = (int)cc;
   }
 }
 
@@ -166,21 +179,30 @@ __global__ __launch_bounds__(kSearchThreads) void k_search(const float* __restri
     float best = -__builtin_inff();
     int cand = kSearchNone;
     if (finite) {
-      // ---- even coset, by support weight (positions of each weight in the sorted table)
-      search_even_weight<EUCLID, 0>(ab, xneg, M, 0, 1, tid, &best, &cand);
-      search_even_weight<EUCLID, 8>(ab, xneg, M, 1, 759, tid, &best, &cand);
-      search_even_weight<EUCLID, 12>(ab, xneg, M, 760, 2576, tid, &best, &cand);
-      search_even_weight<EUCLID, 16>(ab, xneg, M, 3336, 759, tid, &best, &cand);
-      search_even_weight<EUCLID, 24>(ab, xneg, M, 4095, 1, tid, &best, &cand);
-      // ---- odd coset: every codeword against every odd class
-      for (int j = 0; j < 4096 / kSearchThreads; ++j) {
-        const int pos = tid + kSearchThreads * j;
-        float S[25];
-        odd_sums(xv, dev_tables::kGolayTable[pos], S);
+      // ---- even coset: 2048 complement pairs (weights 8 + 16, 12 + 12, 0 + 24)
+      for (int j = 0; j < 2048 / kSearchThreads; ++j) {
+        const int i = tid + kSearchThreads * j;
+        if (i < 759) search_even_pair<EUCLID, 8>(ab, xneg, dev_tables::kGolayTable[1 + i], M, &best, &cand);
+        else if (i < 2047) search_even_pair<EUCLID, 12>(ab, xneg, dev_tables::kSearchW12Rep[i - 759], M, &best, &cand);
+        else search_even_pair<EUCLID, 0>(ab, xneg, 0u, M, &best, &cand);
+      }
+      // ---- odd coset: 2048 complement pairs against every odd class; y(~c) = -y(c), so
+      // the prefix sums of ~c are S'[k] = S[24 - k] - S[24]
+      for (int j = 0; j < 2048 / kSearchThreads; ++j) {
+        const uint32_t c = dev_tables::kSearchOddRep[tid + kSearchThreads * j];
+        float S[25], S2[25];
+        odd_sums(xv, c, S);
+#pragma unroll
+        for (int k = 0; k <= 24; ++k) S2[k] = S[24 - k] - S[24];
         const float o = EUCLID ? dev_tables::llvq_odd_max_euclid(S, M) : dev_tables::llvq_odd_max_angular(S, M);
         if (o > best) {
           best = o;
-          cand = 4096 + pos;
+          cand = (int)(c | (1u << 24));
+        }
+        const float o2 = EUCLID ? dev_tables::llvq_odd_max_euclid(S2, M) : dev_tables::llvq_odd_max_angular(S2, M);
+        if (o2 > best) {
+          best = o2;
+          cand = (int)((~c & 0xffffffu) | (1u << 24));
         }
       }
     }
@@ -209,8 +231,8 @@ __global__ __launch_bounds__(kSearchThreads) void k_search(const float* __restri
           cd = rc[w];
         }
       int v = 0;
-      if (cd != kSearchNone && cd >= 4096) {
-        const uint32_t c = dev_tables::kGolayTable[cd - 4096];
+      if (cd != kSearchNone && (cd >> 24) != 0) {
+        const uint32_t c = (uint32_t)cd & 0xffffffu;
         float S[25], ob;
         odd_sums(xv, c, S);
         const int k = EUCLID ? dev_tables::llvq_odd_argmax_euclid(S, M, &ob) : dev_tables::llvq_odd_argmax_angular(S, M, &ob);
@@ -229,7 +251,7 @@ __global__ __launch_bounds__(kSearchThreads) void k_search(const float* __restri
           v = ((c >> lane) & 1u) ? bv : -bv;
         }
       } else if (cd != kSearchNone) {
-        const uint32_t c = dev_tables::kGolayTable[cd];
+        const uint32_t c = (uint32_t)cd;
         switch (__builtin_popcount(c)) {
           case 0: v = even_point<EUCLID, 0>(xv, ab, xneg, c, M, lane); break;
           case 8: v = even_point<EUCLID, 8>(xv, ab, xneg, c, M, lane); break;
