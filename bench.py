@@ -81,6 +81,11 @@ KERNEL_PROFILES = {
     "search": {
         "source_sha256": "5e30e8e6495a05c5f8ef907c800352cca1fd4b2b619a2dcdd50060cca0922c1d",
         "summary": "profiles/search_4096x4096_k_search_k_rank.md",
+        # The search issues more VALU instructions per clock than one per CU (mostly fp32
+        # add / fma / max, which issue at up to 1.46 wave-instructions per CU per clock on
+        # gfx950, profiles/valu_issue_rates_gfx950.md), so its peak is the fastest measured
+        # single-instruction rate, 1.464 x 39.32 T lane-ops/s.
+        "valu_peak_tops": 57.56,
         "unit_of_work": "24-block: search (4643368.8) + rank (955.4)",
         "valu_lane_ops_per_unit": 4644324.2,
         "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
@@ -151,8 +156,9 @@ def roofline(profile_key, ops_units, sec, alg_bytes, per_unit_text):
         traffic = prof["fetch_bytes_per_launch"] + prof["write_bytes_per_launch"]
     if prof_ok and prof.get("valu_lane_ops_per_unit"):
         ops = prof["valu_lane_ops_per_unit"] * ops_units
-        return {"bound": "alu", "achieved": ops / sec / 1e12, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
-                "frac": ops / sec / 1e12 / VALU_PEAK_TOPS, "traffic": traffic,
+        peak = prof.get("valu_peak_tops", VALU_PEAK_TOPS)
+        return {"bound": "alu", "achieved": ops / sec / 1e12, "peak": peak, "unit": "TOP/s",
+                "frac": ops / sec / 1e12 / peak, "traffic": traffic,
                 "valu_lane_ops_per_unit": prof["valu_lane_ops_per_unit"], "unit_of_work": prof["unit_of_work"],
                 "profile": prof["summary"], "hbm": hbm}
     roof = dict(hbm)

@@ -83,6 +83,11 @@ K32(k_perm_b32, "v_perm_b32 %0, %0, %1, %2")
 K32(k_dot4_u32_u8, "v_dot4_u32_u8 %0, %0, %1, %2")
 K32(k_bcnt_u32_b32, "v_bcnt_u32_b32 %0, %0, %1")
 K32(k_med3_u32, "v_med3_u32 %0, %0, %1, %2")
+K32(k_min_f32, "v_min_f32 %0, %0, %1")
+K32(k_max_f32, "v_max_f32 %0, %0, %1")
+K32(k_min_u32, "v_min_u32 %0, %0, %1")
+K32(k_max_u32, "v_max_u32 %0, %0, %1")
+K32(k_max3_f32, "v_max3_f32 %0, %0, %1, %2")
 K64(k_fma_f64, "v_fma_f64 %0, %0, %1, %2")
 K64(k_mul_f64, "v_mul_f64 %0, %0, %1")
 K64(k_add_f64, "v_add_f64 %0, %0, %1")
@@ -93,7 +98,8 @@ static const kfn kKernels[] = {
     k_lshrrev_b32, k_lshlrev_b32,  k_cndmask_b32,    k_mul_f32,      k_add_f32,      k_fmac_f32,     k_fma_f32,
     k_cvt_f32_u32, k_cvt_f32_ubyte0, k_xad_u32,      k_ffbl_b32,     k_bfi_b32,      k_bfe_u32,      k_alignbit_b32,
     k_lshl_or_b32, k_lshl_add_u32, k_add3_u32,       k_and_or_b32,   k_or3_b32,      k_mad_u32_u24,  k_mul_lo_u32,
-    k_perm_b32,    k_dot4_u32_u8,  k_bcnt_u32_b32,   k_med3_u32,     k_fma_f64,      k_mul_f64,      k_add_f64};
+    k_perm_b32,    k_dot4_u32_u8,  k_bcnt_u32_b32,   k_med3_u32,     k_min_f32,      k_max_f32,      k_min_u32,
+    k_max_u32,     k_max3_f32,     k_fma_f64,        k_mul_f64,      k_add_f64};
 
 extern "C" __attribute__((visibility("default"))) int ir_count() { return (int)(sizeof(kKernels) / sizeof(kKernels[0])); }
 

@@ -34,8 +34,8 @@ NAMES = ["v_add_u32", "v_sub_u32", "v_and_b32", "v_or_b32", "v_xor_b32", "v_not_
          "v_lshrrev_b32", "v_lshlrev_b32", "v_cndmask_b32", "v_mul_f32", "v_add_f32", "v_fmac_f32", "v_fma_f32",
          "v_cvt_f32_u32", "v_cvt_f32_ubyte0", "v_xad_u32", "v_ffbl_b32", "v_bfi_b32", "v_bfe_u32", "v_alignbit_b32",
          "v_lshl_or_b32", "v_lshl_add_u32", "v_add3_u32", "v_and_or_b32", "v_or3_b32", "v_mad_u32_u24",
-         "v_mul_lo_u32", "v_perm_b32", "v_dot4_u32_u8", "v_bcnt_u32_b32", "v_med3_u32", "v_fma_f64", "v_mul_f64",
-         "v_add_f64"]
+         "v_mul_lo_u32", "v_perm_b32", "v_dot4_u32_u8", "v_bcnt_u32_b32", "v_med3_u32", "v_min_f32", "v_max_f32",
+         "v_min_u32", "v_max_u32", "v_max3_f32", "v_fma_f64", "v_mul_f64", "v_add_f64"]
 
 
 def build(verbose=True):
