@@ -47,7 +47,7 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "5e30e8e6495a05c5f8ef907c800352cca1fd4b2b619a2dcdd50060cca0922c1d",
+        "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
         "valu_lane_ops_per_unit": 670.3,       # SQ_INSTS_VALU * 64 / blocks
@@ -55,15 +55,15 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "5e30e8e6495a05c5f8ef907c800352cca1fd4b2b619a2dcdd50060cca0922c1d",
+        "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
         "valu_lane_ops_per_unit": 695.4,
-        "fetch_bytes_per_launch": 61927806,
+        "fetch_bytes_per_launch": 61927758,
         "write_bytes_per_launch": 1835008,
     },
     "decode_bf16": {
-        "source_sha256": "5e30e8e6495a05c5f8ef907c800352cca1fd4b2b619a2dcdd50060cca0922c1d",
+        "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
         "summary": "profiles/decode_bf16_7b_layer_k_decode_tile.md",
         "unit_of_work": "24-weight block (k_decode_tile<bf16>)",
         "valu_lane_ops_per_unit": 760.4,
@@ -71,7 +71,7 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": None,
     },
     "roundtrip": {
-        "source_sha256": "5e30e8e6495a05c5f8ef907c800352cca1fd4b2b619a2dcdd50060cca0922c1d",
+        "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
         "summary": "profiles/roundtrip_1e7_k_decode_tile_k_rank.md",
         "unit_of_work": "point: decode to int8 (627.0) + rank (951.2)",
         "valu_lane_ops_per_unit": 1578.2,
@@ -79,15 +79,15 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": None,
     },
     "search": {
-        "source_sha256": "5e30e8e6495a05c5f8ef907c800352cca1fd4b2b619a2dcdd50060cca0922c1d",
+        "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
         "summary": "profiles/search_4096x4096_k_search_k_rank.md",
         # The search issues more VALU instructions per clock than one per CU (mostly fp32
         # add / fma / max, which issue at up to 1.46 wave-instructions per CU per clock on
         # gfx950, profiles/valu_issue_rates_gfx950.md), so its peak is the fastest measured
         # single-instruction rate, 1.464 x 39.32 T lane-ops/s.
         "valu_peak_tops": 57.56,
-        "unit_of_work": "24-block: search (4643368.8) + rank (955.4)",
-        "valu_lane_ops_per_unit": 4644324.2,
+        "unit_of_work": "24-block: search (3284603.5) + rank (955.4)",
+        "valu_lane_ops_per_unit": 3285558.9,
         "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
         "write_bytes_per_launch": None,
     },
