@@ -155,6 +155,35 @@ int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell, uint64_t
 int llvq_search(const float* x, int64_t n, int32_t max_shell, int32_t objective, int8_t* points,
                 uint64_t* indices, int32_t* err_count, void* stream);
 
+/* Bytes of device workspace llvq_quantize needs for descriptor d (24 + 8 bytes per block,
+ * the chosen points and their indices), or a negative LLVQ_* code for a bad descriptor. */
+int64_t llvq_quantize_workspace_bytes(const llvq_desc* d);
+
+/* Quantise a weight matrix into the packed stream that llvq_decode / llvq_gemv read: each
+ * 24-block (zero-padded past the last column) gets its nearest point of shells 2..M and
+ * the block's field is written (papernotes.org notes, 整体框架 and 关键设计 1: shape-gain
+ * puts the block's direction on the lattice with the angular objective and scalar-quantises
+ * the gain; spherical shaping takes the Euclidean nearest point; gist.science page,
+ * Methodik / 2. Multi-Shell Search).
+ *   d         : descriptor of the output tensor (as for llvq_decode).
+ *   w         : fp32 [rows][cols] weights, 4-byte aligned.
+ *   scales    : fp16, 2-byte aligned.  SHAPEGAIN: the gain table [2^gain_bits]; the block's
+ *               shape is its angular nearest point and its gain index the nearest table
+ *               entry to the block's norm (ties to the lower index).  EUCLID: per-row scales
+ *               [rows]; the block divided by its row's scale (the lattice's integer units)
+ *               gets its Euclidean nearest point.
+ *   packed    : output stream of llvq_packed_bytes(d) bytes (16-byte aligned), every byte
+ *               written (fields, then zero padding).
+ *   workspace : llvq_quantize_workspace_bytes(d) bytes of device memory (8-byte aligned),
+ *               owned by the caller; its contents are not meaningful after the call.
+ *   err_count : nullable; a block with a non-finite value (after the row scale) is written
+ *               with the all-ones shape field, which decodes to the zero block and is
+ *               counted again by llvq_decode.
+ * Exact ties of the search objective resolve as in llvq_search.  Runs on `stream`; the
+ * call allocates nothing.  Returns LLVQ_OK, LLVQ_EINVAL or LLVQ_EHIP. */
+int llvq_quantize(const llvq_desc* d, const float* w, const void* scales, void* packed, void* workspace,
+                  int32_t* err_count, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

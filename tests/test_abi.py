@@ -105,6 +105,23 @@ def test_search_validation_and_empty(lib):
     assert lib.llvq_search(None, 0, 10, 0, None, None, None, None) == 0                   # empty: no-op
 
 
+def test_quantize_validation(lib):
+    p = ctypes.c_void_p(0x10000)
+    d = wd.make_desc(wd.MODE_SHAPEGAIN, 4, 100, 10, 44, 4)
+    assert lib.llvq_quantize_workspace_bytes(ctypes.byref(d)) == 4 * 5 * 32
+    d3 = wd.make_desc(wd.MODE_EUCLID, 3, 25, 3, 25, 0)
+    assert lib.llvq_quantize_workspace_bytes(ctypes.byref(d3)) == (3 * 2 * 24 + 7) // 8 * 8 + 3 * 2 * 8
+    bad = wd.make_desc(wd.MODE_SHAPEGAIN, 4, 100, 11, 44, 4)
+    assert lib.llvq_quantize_workspace_bytes(ctypes.byref(bad)) == -1
+    assert lib.llvq_quantize(ctypes.byref(bad), p, p, p, p, None, None) == -1
+    assert lib.llvq_quantize(ctypes.byref(d), None, p, p, p, None, None) == -1                # null w
+    assert lib.llvq_quantize(ctypes.byref(d), p, None, p, p, None, None) == -1                # null scales
+    assert lib.llvq_quantize(ctypes.byref(d), p, p, ctypes.c_void_p(0x10008), p, None, None) == -1   # packed alignment
+    assert lib.llvq_quantize(ctypes.byref(d), p, p, p, ctypes.c_void_p(0x10004), None, None) == -1   # workspace alignment
+    assert lib.llvq_quantize(ctypes.byref(d), ctypes.c_void_p(0x10002), p, p, p, None, None) == -1   # w alignment
+    assert lib.llvq_quantize(None, p, p, p, p, None, None) == -1
+
+
 def test_error_strings(lib):
     for code in (0, -1, -2, -3, 42):
         assert isinstance(lib.llvq_error_string(code), bytes)

@@ -138,3 +138,86 @@ def test_search_many_blocks_grid_stride_and_edge_inputs():
             og = objective(x[i], bijection.unrank(int(idx[i]), 10), "angular")
             oo = objective(x[i], bijection.unrank(int(I), 10), "angular")
             assert og >= oo - 1e-6 * (1.0 + abs(oo)), i
+
+
+def gpu_quantize(desc, w, scales):
+    n_ws = wd.quantize_workspace_bytes(desc)
+    wt = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).cuda()
+    st = torch.from_numpy(np.ascontiguousarray(scales, dtype=np.float16)).cuda()
+    packed = torch.full((wd.packed_bytes(desc),), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.quantize(desc, wt, st, packed, ws, err)
+    torch.cuda.synchronize()
+    return packed.cpu().numpy(), int(err.item())
+
+
+def oracle_fields(w, scales, M, mode, gain_bits, shape_bits):
+    rows, cols = w.shape
+    kb = synth.blocks_per_row(cols)
+    fields = np.zeros(rows * kb, dtype=np.uint64)
+    for r in range(rows):
+        wpad = np.zeros(kb * 24)
+        wpad[:cols] = w[r]
+        for b in range(kb):
+            blk = wpad[b * 24:(b + 1) * 24]
+            if mode == wd.MODE_SHAPEGAIN:
+                I, _ = search.search(blk, M, "angular")
+                g = search.nearest_gain(np.linalg.norm(blk), scales.astype(np.float64))
+                fields[r * kb + b] = np.uint64(I) | (np.uint64(g) << np.uint64(shape_bits))
+            else:
+                I, _ = search.search(blk / float(scales[r]), M, "euclid")
+                fields[r * kb + b] = np.uint64(I)
+    return fields
+
+
+def test_quantize_shapegain_stream_matches_oracle():
+    # 13 x 226 N(0, 0.02^2) weights (10 blocks per row, the last of 10 columns), 44 + 4 bits
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((13, 226)) * 0.02).astype(np.float32)
+    gains = synth.draw_gain_table(3, 0, 16, 0.02)
+    desc = wd.make_desc(wd.MODE_SHAPEGAIN, 13, 226, 10, 44, 4)
+    got, err = gpu_quantize(desc, w, gains)
+    assert err == 0
+    want = synth.pack_fields(oracle_fields(w, gains, 10, wd.MODE_SHAPEGAIN, 4, 44), 48)
+    assert got.size == want.size and np.array_equal(got, want)
+
+
+def test_quantize_euclid_stream_matches_oracle():
+    # shells 2..3, 25-bit fields (not byte aligned), per-row fp16 scales
+    rng = np.random.default_rng(22)
+    rows, cols = 9, 24 * 7 + 3
+    s = rng.uniform(0.5, 2.0, size=rows).astype(np.float16)
+    w = (rng.standard_normal((rows, cols)) * 1.6 * s.astype(np.float32)[:, None]).astype(np.float32)
+    desc = wd.make_desc(wd.MODE_EUCLID, rows, cols, 3, 25, 0)
+    got, err = gpu_quantize(desc, w, s)
+    assert err == 0
+    want = synth.pack_fields(oracle_fields(w, s, 3, wd.MODE_EUCLID, 0, 25), 25)
+    assert got.size == want.size and np.array_equal(got, want)
+
+
+def test_quantize_then_decode_and_gemv():
+    # the quantiser's stream decodes to its search points; a non-finite block is written
+    # as an invalid field (zero block, counted by the decoder)
+    rng = np.random.default_rng(23)
+    rows, cols = 40, 24 * 20
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    w[5, 30] = np.inf
+    gains = synth.draw_gain_table(3, 1, 16, 0.02)
+    desc = wd.make_desc(wd.MODE_SHAPEGAIN, rows, cols, 10, 44, 4)
+    packed, err = gpu_quantize(desc, w, gains)
+    assert err == 1
+    pk = torch.from_numpy(packed).cuda()
+    out = torch.empty((rows, cols), dtype=torch.int8, device="cuda")
+    derr = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.decode(desc, pk, torch.from_numpy(gains).cuda(), wd.OUT_POINTS_I8, out, derr)
+    torch.cuda.synchronize()
+    assert int(derr.item()) == 1
+    pts = out.cpu().numpy().reshape(rows, 20, 24).astype(np.int64)
+    assert not pts[5, 1].any()
+    xt = torch.from_numpy(w.reshape(-1, 24).copy())
+    xt[5 * 20 + 1] = 0.0
+    spts, _, _ = gpu_search(xt.numpy(), 10, "angular")
+    sp = spts.reshape(rows, 20, 24)
+    sp[5, 1] = 0
+    assert np.array_equal(pts, sp)

@@ -24,7 +24,8 @@ _ERRORS = {0: "ok", -1: "invalid argument", -2: "unsupported request", -3: "HIP 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllvq.so")
 
 EXPORTED_SYMBOLS = ("llvq_index_count", "llvq_packed_bytes", "llvq_error_string",
-                    "llvq_decode", "llvq_gemv", "llvq_encode_ref", "llvq_search")
+                    "llvq_decode", "llvq_gemv", "llvq_encode_ref", "llvq_search", "llvq_quantize_workspace_bytes",
+                    "llvq_quantize")
 
 
 class LlvqError(RuntimeError):
@@ -77,6 +78,10 @@ def load_library(path=LIB_PATH):
     lib.llvq_encode_ref.restype = ctypes.c_int
     lib.llvq_search.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
     lib.llvq_search.restype = ctypes.c_int
+    lib.llvq_quantize_workspace_bytes.argtypes = [dp]
+    lib.llvq_quantize_workspace_bytes.restype = i64
+    lib.llvq_quantize.argtypes = [dp, vp, vp, vp, vp, vp, vp]
+    lib.llvq_quantize.restype = ctypes.c_int
     _libs[path] = lib
     return lib
 
@@ -148,3 +153,17 @@ def search(x, max_shell, objective, points, indices, err_count=None, stream=None
     n = x.shape[0] if x.dim() > 1 else x.numel() // 24
     _check(load_library().llvq_search(_ptr(x), n, max_shell, objective, _ptr(points), _ptr(indices),
                                       _ptr(err_count), _stream(stream)), "llvq_search")
+
+
+def quantize_workspace_bytes(desc: Desc) -> int:
+    n = load_library().llvq_quantize_workspace_bytes(ctypes.byref(desc))
+    if n < 0:
+        raise LlvqError(int(n), "llvq_quantize_workspace_bytes")
+    return n
+
+
+def quantize(desc, w, scales, packed, workspace, err_count=None, stream=None):
+    """Quantise fp32 weights w [rows][cols] into the packed stream (uint8 tensor of
+    packed_bytes(desc) bytes); workspace: quantize_workspace_bytes(desc) bytes of device memory."""
+    _check(load_library().llvq_quantize(ctypes.byref(desc), _ptr(w), _ptr(scales), _ptr(packed), _ptr(workspace),
+                                        _ptr(err_count), _stream(stream)), "llvq_quantize")

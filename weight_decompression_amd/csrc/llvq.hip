@@ -667,12 +667,55 @@ LLVQ_API int llvq_search(const float* x, int64_t n, int32_t max_shell, int32_t o
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const unsigned grid = n < 8192 ? (unsigned)n : 8192u;
   if (objective == LLVQ_SEARCH_EUCLID)
-    hipLaunchKernelGGL((k_search<true>), dim3(grid), dim3(kSearchThreads), 0, s, x, n, max_shell, points);
+    hipLaunchKernelGGL((k_search<true>), dim3(grid), dim3(kSearchThreads), 0, s, x, n, max_shell, 24, 1,
+                       (const __half*)nullptr, points);
   else
-    hipLaunchKernelGGL((k_search<false>), dim3(grid), dim3(kSearchThreads), 0, s, x, n, max_shell, points);
+    hipLaunchKernelGGL((k_search<false>), dim3(grid), dim3(kSearchThreads), 0, s, x, n, max_shell, 24, 1,
+                       (const __half*)nullptr, points);
   const int st = launch_status();
   if (st != LLVQ_OK) return st;
   return llvq_encode_ref(points, n, max_shell, indices, err_count, stream);
+}
+
+namespace {
+uint64_t quantize_points_bytes(const KDesc& k) { return ((uint64_t)k.rows * (uint64_t)k.kb * 24u + 7u) / 8u * 8u; }
+}  // namespace
+
+LLVQ_API int64_t llvq_quantize_workspace_bytes(const llvq_desc* d) {
+  KDesc k;
+  const int st = make_kdesc(d, &k);
+  if (st != LLVQ_OK) return st;
+  return (int64_t)(quantize_points_bytes(k) + (uint64_t)k.rows * (uint64_t)k.kb * 8u);
+}
+
+LLVQ_API int llvq_quantize(const llvq_desc* d, const float* w, const void* scales, void* packed, void* workspace,
+                           int32_t* err_count, void* stream) {
+  KDesc k;
+  const int st = make_kdesc(d, &k);
+  if (st != LLVQ_OK) return st;
+  if (!w || !scales || !packed || !workspace) return LLVQ_EINVAL;
+  if (!aligned(w, 4) || !aligned(scales, 2) || !aligned(packed, 16) || !aligned(workspace, 8)) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t n = (int64_t)k.rows * (int64_t)k.kb;
+  int8_t* pts = static_cast<int8_t*>(workspace);
+  uint64_t* idx = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + quantize_points_bytes(k));
+  const unsigned grid = n < 8192 ? (unsigned)n : 8192u;
+  if (k.mode == LLVQ_MODE_EUCLID)
+    hipLaunchKernelGGL((k_search<true>), dim3(grid), dim3(kSearchThreads), 0, s, w, n, k.max_shell, k.cols, k.kb,
+                       static_cast<const __half*>(scales), pts);
+  else
+    hipLaunchKernelGGL((k_search<false>), dim3(grid), dim3(kSearchThreads), 0, s, w, n, k.max_shell, k.cols, k.kb,
+                       (const __half*)nullptr, pts);
+  int st1 = launch_status();
+  if (st1 != LLVQ_OK) return st1;
+  st1 = llvq_encode_ref(pts, n, k.max_shell, idx, err_count, stream);
+  if (st1 != LLVQ_OK) return st1;
+  const int64_t nwords = packed_bytes_of(k) / 4;
+  hipLaunchKernelGGL(k_pack, dim3(grid_for((uint64_t)nwords, 256)), dim3(256), 0, s, k, w,
+                     k.mode == LLVQ_MODE_SHAPEGAIN ? static_cast<const __half*>(scales) : (const __half*)nullptr, idx,
+                     static_cast<uint32_t*>(packed), nwords);
+  return launch_status();
 }
 
 LLVQ_API int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell, uint64_t* indices,

@@ -156,8 +156,13 @@ __device__ __forceinline__ int even_point(const float (&xv)[24], const uint32_t 
   return v;
 }
 
+// Vectors: block b of row r of a [rows][cols] fp32 matrix with kb = ceil(cols / 24)
+// blocks per row (zero past the last column), vector index r kb + b; a plain [n][24]
+// array is cols = 24, kb = 1.  With rscale, row r is divided by its fp16 scale first
+// (the Euclidean quantiser takes the lattice's integer units).
 template <bool EUCLID>
-__global__ __launch_bounds__(kSearchThreads) void k_search(const float* __restrict__ x, int64_t n, int M,
+__global__ __launch_bounds__(kSearchThreads) void k_search(const float* __restrict__ x, int64_t n, int M, int cols,
+                                                           int kb, const __half* __restrict__ rscale,
                                                            int8_t* __restrict__ pts) {
   __shared__ float rv[kSearchThreads / 64];
   __shared__ int rc[kSearchThreads / 64];
@@ -169,9 +174,14 @@ __global__ __launch_bounds__(kSearchThreads) void k_search(const float* __restri
     uint32_t ab[24];
     uint32_t xneg = 0u;
     bool finite = true;
+    const int64_t row = blk / kb;
+    const int c0 = (int)(blk - row * kb) * 24;
+    const float* xr = x + row * (int64_t)cols;
+    const float rs = rscale ? __half2float(rscale[row]) : 1.0f;
 #pragma unroll
     for (int i = 0; i < 24; ++i) {
-      xv[i] = x[blk * 24 + i];
+      xv[i] = c0 + i < cols ? xr[c0 + i] : 0.0f;
+      if (rscale) xv[i] = xv[i] / rs;
       ab[i] = __float_as_uint(xv[i]) & 0x7fffffffu;
       xneg |= (xv[i] < 0.0f ? 1u : 0u) << i;
       finite = finite && ab[i] < 0x7f800000u;
@@ -283,5 +293,59 @@ __global__ __launch_bounds__(kSearchThreads) void k_search(const float* __restri
       if (lane < 24) pts[blk * 24 + lane] = (int8_t)v;
     }
     __syncthreads();   // rv / rc are rewritten for the next vector
+  }
+}
+
+// Packed stream of the quantiser: one thread per 32-bit word of the stream, assembling the
+// bits of the (at most three) fields that overlap it, so no word is written twice.  Field j
+// = shape index | gain index << shape_bits; an index the rank step rejected (UINT64_MAX)
+// is written as the all-ones shape field, which every decoder treats as invalid (it is >=
+// the shell union's size).  Shape-gain: the gain index is the nearest entry of the fp16
+// gain table to the block's norm (computed in fp64), ties to the lower index.
+__device__ __forceinline__ uint64_t quant_field(const KDesc& d, const float* __restrict__ w,
+                                                const __half* __restrict__ gains, const uint64_t* __restrict__ idx,
+                                                uint64_t j) {
+  uint64_t I = idx[j];
+  if (I >= d.index_count) I = d.shape_mask;
+  uint64_t F = I & d.shape_mask;
+  if (d.mode == LLVQ_MODE_SHAPEGAIN) {
+    const uint64_t row = j / (uint64_t)d.kb;
+    const int c0 = (int)(j - row * (uint64_t)d.kb) * 24;
+    const float* xr = w + row * (uint64_t)d.cols;
+    double s2 = 0.0;
+    for (int i = 0; i < 24 && c0 + i < d.cols; ++i) {
+      const double v = (double)xr[c0 + i];
+      s2 = __builtin_fma(v, v, s2);
+    }
+    const double nrm = __builtin_sqrt(s2);
+    int g = 0;
+    double best = __builtin_fabs((double)__half2float(gains[0]) - nrm);
+    for (int t = 1; t < (1 << d.gain_bits); ++t) {
+      const double e = __builtin_fabs((double)__half2float(gains[t]) - nrm);
+      if (e < best) {
+        best = e;
+        g = t;
+      }
+    }
+    F |= (uint64_t)g << d.shape_bits;
+  }
+  return F;
+}
+
+__global__ __launch_bounds__(256) void k_pack(KDesc d, const float* __restrict__ w, const __half* __restrict__ gains,
+                                              const uint64_t* __restrict__ idx, uint32_t* __restrict__ out,
+                                              int64_t nwords) {
+  const uint64_t nfields = (uint64_t)d.rows * (uint64_t)d.kb;
+  const uint64_t f = (uint64_t)d.field_bits;
+  for (int64_t wd = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; wd < nwords;
+       wd += (int64_t)gridDim.x * blockDim.x) {
+    const uint64_t bit0 = (uint64_t)wd * 32u;
+    uint32_t word = 0u;
+    for (uint64_t j = bit0 / f; j < nfields && j * f < bit0 + 32u; ++j) {
+      const uint64_t F = quant_field(d, w, gains, idx, j);
+      const int64_t off = (int64_t)(j * f) - (int64_t)bit0;   // -64 < off < 32
+      word |= off >= 0 ? (uint32_t)(F << off) : (uint32_t)(F >> (-off));
+    }
+    out[wd] = word;
   }
 }
