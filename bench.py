@@ -21,6 +21,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-rows R] [--no-
        python bench.py --workload decode_bf16_7b [--layers 32]
        python bench.py --workload roundtrip [--points 100000000]
        python bench.py --workload search [--cpu-blocks 2048]
+       python bench.py --workload fidelity [--fidelity-blocks 262144]
 The other workloads print one line each in the same format (their own metric).
 """
 
@@ -383,9 +384,95 @@ def run_search(a):
     return out
 
 
+def run_fidelity(a):
+    """Distortion of the quantiser on the memoryless unit Gaussian source: n 24-blocks as a
+    [n/128][3072] tensor.  Shape-gain at 2.0 bits/dim (44-bit shape index over shells 2..10 +
+    4-bit gain, gain table = chi_24 equal-probability cell means) and Euclidean spherical
+    shaping with the same 44-bit shape index (1.83 bits/dim, one scale swept on a subset).
+    Reconstruction through llvq_decode to bf16; MSE per dimension against the source."""
+    import numpy as np
+    import torch
+    import weight_decompression_amd as wd
+    from weight_decompression_amd import synth
+
+    lib = wd.load_library()
+    n = a.fidelity_blocks
+    kb = 128
+    rows = n // kb
+    n = rows * kb
+    cols = kb * 24
+    x = synth.gaussian_source(6, n)
+    W = torch.from_numpy(x.reshape(rows, cols)).cuda()
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def quantize_and_mse(desc, scales, timed):
+        packed = torch.empty(wd.packed_bytes(desc), dtype=torch.uint8, device="cuda:0")
+        ws = torch.empty(wd.quantize_workspace_bytes(desc), dtype=torch.uint8, device="cuda:0")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+        args = (ctypes.byref(desc), ctypes.c_void_p(W.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ctypes.c_void_p(err.data_ptr()),
+                sptr)
+        if timed:
+            sec, _ = time_steps(lambda i: lib.llvq_quantize(*args), a.steps, a.warmup, stream)
+        else:
+            if lib.llvq_quantize(*args) != 0:
+                raise RuntimeError("llvq_quantize failed")
+            sec = None
+        out = torch.empty((desc.rows, desc.cols), dtype=torch.bfloat16, device="cuda:0")
+        if lib.llvq_decode(ctypes.byref(desc), ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                           wd.OUT_BF16, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(err.data_ptr()), sptr) != 0:
+            raise RuntimeError("llvq_decode failed")
+        torch.cuda.synchronize()
+        if int(err.item()) != 0:
+            raise RuntimeError("quantiser reported invalid blocks")
+        mse = float(((W[: desc.rows].double() - out.double()) ** 2).mean())
+        return mse, sec
+
+    # shape-gain, 48 bits per block
+    gains = torch.from_numpy(synth.chi_gain_table(16)).cuda()
+    dsg = wd.make_desc(wd.MODE_SHAPEGAIN, rows, cols, 10, 44, 4)
+    mse_sg, sec = quantize_and_mse(dsg, gains, True)
+    # Euclidean, 44 bits per block: the scale that minimises the MSE on a 1/8 subset
+    sub = max(1, rows // 8)
+    best = None
+    for sc in np.arange(0.30, 0.96, 0.05):
+        de = wd.make_desc(wd.MODE_EUCLID, sub, cols, 10, 44, 0)
+        srow = torch.full((sub,), float(sc), dtype=torch.float16, device="cuda:0")
+        m, _ = quantize_and_mse(de, srow, False)
+        if best is None or m < best[0]:
+            best = (m, float(torch.tensor(float(sc), dtype=torch.float16)))
+    de = wd.make_desc(wd.MODE_EUCLID, rows, cols, 10, 44, 0)
+    mse_eu, _ = quantize_and_mse(de, torch.full((rows,), best[1], dtype=torch.float16, device="cuda:0"), False)
+
+    def eff(mse, rate):
+        bits = -0.5 * math.log2(mse)
+        return {"mse_per_dim": mse, "effective_bits": bits, "rate_bits_per_dim": rate,
+                "pct_of_shannon": 100.0 * bits / rate, "shannon_mse": 2.0 ** (-2.0 * rate)}
+
+    out = base_line("LLVQ shape-gain distortion on a unit Gaussian source at 2 bits/dim (MSE per dimension), "
+                    "1 MI355X", mse_sg, "MSE/dim", a.steps, a.warmup, sec, "f32",
+                    f"llvq_quantize + llvq_decode, {n} i.i.d. N(0,1) 24-blocks, shells 2..10",
+                    {"blocks": n, "max_shell": 10, "shape_bits": 44, "gain_bits": 4})
+    out["higher_is_better"] = False
+    out["shape_gain"] = eff(mse_sg, 48 / 24)
+    out["euclid"] = dict(eff(mse_eu, 44 / 24), scale=best[1], scale_grid="0.30..0.95 step 0.05 on 1/8 of the blocks")
+    out["quantize_blocks_per_s"] = n / sec
+    out["roofline"] = roofline("search", n, sec, n * (96 + 24 + 8 + 6),
+                               "96 B fp32 block read + 32 B workspace + 6 B packed field per block")
+    if not a.no_cpu:
+        from oracle import cpu_baseline as cb
+        sample = x[: a.cpu_blocks].astype(np.float64)
+        dt, procs = cb.time_search(sample, 10, "angular")
+        out["cpu_baseline"] = {"value": len(sample) / dt, "unit": "blocks/s", "cores": procs, "kind": "oracle",
+                               "sample": f"exact angular search of the first {len(sample)} source blocks in numpy, "
+                                         f"{procs} processes, {dt:.2f} s wall (the quantiser's time, not its MSE)"}
+    return out
+
+
 DEFAULT_WORKLOAD = "gemv_4096x11008"
 WORKLOADS = ("gemv_4096x11008", "gemv_11008x4096", "gemv_4096x4096", "gemv_28672x8192", "decode_bf16_7b",
-             "roundtrip", "search")
+             "roundtrip", "search", "fidelity")
 
 
 def main():
@@ -401,6 +488,7 @@ def main():
     ap.add_argument("--layers", type=int, default=32, help="layers of the 7B-shaped set (decode_bf16_7b)")
     ap.add_argument("--points", type=int, default=100_000_000, help="indices in the round trip")
     ap.add_argument("--cpu-blocks", type=int, default=2048, help="blocks the CPU oracle search is timed on (search)")
+    ap.add_argument("--fidelity-blocks", type=int, default=262144, help="Gaussian source blocks (fidelity)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB mebibytes (HBM counter calibration)")
     a = ap.parse_args()
@@ -448,6 +536,8 @@ def main():
         out = run_decode_7b(a)
     elif w == "search":
         out = run_search(a)
+    elif w == "fidelity":
+        out = run_fidelity(a)
     else:
         out = run_roundtrip(a)
     print(json.dumps(out), flush=True)

@@ -115,6 +115,23 @@ def draw_gain_table(workload, tensor, n, scale=1.0) -> np.ndarray:
     return g.astype(np.float16)
 
 
+def gaussian_source(workload, n_blocks) -> np.ndarray:
+    """n_blocks x 24 i.i.d. N(0, 1) samples (fp32), the memoryless Gaussian source."""
+    return rng(workload, 0, 7).standard_normal((n_blocks, DIM)).astype(np.float32)
+
+
+def chi_gain_table(levels, dim=DIM) -> np.ndarray:
+    """Gain table for the norm of a dim-dimensional standard Gaussian vector (chi
+    distribution with dim degrees of freedom): the conditional means of `levels` cells of
+    equal probability, ascending, as fp16.  Uses E[R; a < R < b] = c (F'(b) - F'(a)) with
+    F' the chi CDF of dim + 1 degrees of freedom and c = sqrt(2) G((dim+1)/2) / G(dim/2)."""
+    from scipy import special, stats
+    q = stats.chi(dim).ppf(np.linspace(0.0, 1.0, levels + 1))
+    c = np.sqrt(2.0) * np.exp(special.gammaln((dim + 1) / 2.0) - special.gammaln(dim / 2.0))
+    upper = stats.chi(dim + 1).cdf(q)
+    return (c * np.diff(upper) * levels).astype(np.float16)
+
+
 def draw_activations(workload, tensor, batch, cols, dtype="bf16"):
     xs = np.stack([rng(workload, tensor, 4 + b).standard_normal(cols).astype(np.float32)
                    for b in range(batch)])
