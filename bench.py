@@ -22,6 +22,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-rows R] [--no-
        python bench.py --workload roundtrip [--points 100000000]
        python bench.py --workload search [--cpu-blocks 2048]
        python bench.py --workload fidelity [--fidelity-blocks 262144]
+       python bench.py --workload gptq [--cpu-rows-gptq 8]
 The other workloads print one line each in the same format (their own metric).
 """
 
@@ -470,9 +471,71 @@ def run_fidelity(a):
     return out
 
 
+def run_gptq(a):
+    """Spherical GPTQ of a 4096 x 4096 layer: dense N(0, 0.02^2) weights, Hessian of 4096
+    correlated activation samples with log-normal channel scales; shells 2..10, 44-bit shape
+    + 4-bit gain (gain table 0.02 x the chi_24 cell means).  Reports the relative layer-output
+    error tr(dW H dW^T) / tr(W H W^T) of spherical GPTQ, Euclidean-feedback GPTQ and direct
+    quantisation (weights decoded through llvq_decode to bf16), and the GPU time."""
+    import numpy as np
+    import torch
+    import weight_decompression_amd as wd
+    from weight_decompression_amd import gptq, synth
+
+    lib = wd.load_library()
+    N, K, S = 4096, 4096, 4096
+    W, X = synth.gptq_layer(34, N, K, S)
+    Wt = torch.from_numpy(W).cuda()
+    Xt = torch.from_numpy(X).cuda().double()
+    H = Xt.T @ Xt / S
+    del Xt
+    gains = torch.from_numpy((synth.chi_gain_table(16).astype(np.float64) * 0.02).astype(np.float16)).cuda()
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    Wd = Wt.double()
+    base = float(((Wd @ H) * Wd).sum())
+
+    def loss(desc, packed):
+        out = torch.empty((N, K), dtype=torch.bfloat16, device="cuda:0")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+        if lib.llvq_decode(ctypes.byref(desc), ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(gains.data_ptr()),
+                           wd.OUT_BF16, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(err.data_ptr()), sptr) != 0:
+            raise RuntimeError("llvq_decode failed")
+        D = Wd - out.double()
+        return float(((D @ H) * D).sum()) / base
+
+    res = {}
+    for variant in ("direct", "euclid", "spherical"):
+        desc, packed, _, _ = gptq.gptq(Wt, H, 10, gains, variant=variant)
+        res[variant] = loss(desc, packed)
+    sec, wall = time_steps(lambda i: (gptq.gptq(Wt, H, 10, gains, variant="spherical"), 0)[1], a.steps, a.warmup,
+                           stream)
+    kb = synth.blocks_per_row(K)
+    out = base_line("LLVQ spherical GPTQ layer-output error (relative, 2 bits/weight), 1 MI355X", res["spherical"],
+                    "tr(dW H dW^T)/tr(W H W^T)", a.steps, a.warmup, sec, "f64",
+                    f"weight_decompression_amd.gptq (llvq_search per block column + fp64 feedback), "
+                    f"{N}x{K} N(0, 0.02^2) layer, {S} correlated activation samples",
+                    {"rows": N, "cols": K, "samples": S, "max_shell": 10, "shape_bits": 44, "gain_bits": 4})
+    out["higher_is_better"] = False
+    out["relative_error"] = res
+    out["blocks_per_s"] = N * kb / sec
+    out["wall_s_timed"] = wall
+    if not a.no_cpu:
+        import time as _t
+        from oracle import gptq as ogptq
+        rows = list(range(a.cpu_rows_gptq))
+        t0 = _t.perf_counter()
+        ogptq.gptq(W, H.cpu().numpy(), 10, gains.cpu().numpy(), variant="spherical", rows=rows)
+        dt = _t.perf_counter() - t0
+        out["cpu_baseline"] = {"value": len(rows) * kb / dt, "unit": "blocks/s", "cores": 1, "kind": "oracle",
+                               "sample": f"oracle spherical GPTQ of rows 0..{len(rows) - 1} of the same layer "
+                                         f"(rows do not interact), one process, {dt:.1f} s wall"}
+    return out
+
+
 DEFAULT_WORKLOAD = "gemv_4096x11008"
 WORKLOADS = ("gemv_4096x11008", "gemv_11008x4096", "gemv_4096x4096", "gemv_28672x8192", "decode_bf16_7b",
-             "roundtrip", "search", "fidelity")
+             "roundtrip", "search", "fidelity", "gptq")
 
 
 def main():
@@ -489,6 +552,7 @@ def main():
     ap.add_argument("--points", type=int, default=100_000_000, help="indices in the round trip")
     ap.add_argument("--cpu-blocks", type=int, default=2048, help="blocks the CPU oracle search is timed on (search)")
     ap.add_argument("--fidelity-blocks", type=int, default=262144, help="Gaussian source blocks (fidelity)")
+    ap.add_argument("--cpu-rows-gptq", type=int, default=8, help="rows the CPU oracle GPTQ is timed on (gptq)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB mebibytes (HBM counter calibration)")
     a = ap.parse_args()
@@ -538,6 +602,8 @@ def main():
         out = run_search(a)
     elif w == "fidelity":
         out = run_fidelity(a)
+    elif w == "gptq":
+        out = run_gptq(a)
     else:
         out = run_roundtrip(a)
     print(json.dumps(out), flush=True)

@@ -184,6 +184,15 @@ int64_t llvq_quantize_workspace_bytes(const llvq_desc* d);
 int llvq_quantize(const llvq_desc* d, const float* w, const void* scales, void* packed, void* workspace,
                   int32_t* err_count, void* stream);
 
+/* Write finished fields as the packed stream (the layout of llvq_decode's input): for
+ * quantisers that choose the indices themselves (e.g. with error feedback between blocks).
+ *   fields : uint64 [rows * Kb], field of block (r, b) at r * Kb + b, = shape index |
+ *            gain index << shape_bits; bits above shape_bits + gain_bits are ignored
+ *            (8-byte aligned).
+ *   packed : llvq_packed_bytes(d) bytes (16-byte aligned), every byte written.
+ * Returns LLVQ_OK, LLVQ_EINVAL or LLVQ_EHIP. */
+int llvq_pack_fields(const llvq_desc* d, const uint64_t* fields, void* packed, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -130,3 +130,12 @@ def test_error_strings(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         wd.load_library(str(tmp_path / "missing.so"))
+
+
+def test_pack_fields_validation(lib):
+    p = ctypes.c_void_p(0x10000)
+    d = wd.make_desc(wd.MODE_SHAPEGAIN, 4, 100, 10, 44, 4)
+    assert lib.llvq_pack_fields(ctypes.byref(d), None, p, None) == -1
+    assert lib.llvq_pack_fields(ctypes.byref(d), ctypes.c_void_p(0x10004), p, None) == -1
+    assert lib.llvq_pack_fields(ctypes.byref(d), p, ctypes.c_void_p(0x10008), None) == -1
+    assert lib.llvq_pack_fields(None, p, p, None) == -1

@@ -221,3 +221,21 @@ def test_quantize_then_decode_and_gemv():
     sp = spts.reshape(rows, 20, 24)
     sp[5, 1] = 0
     assert np.array_equal(pts, sp)
+
+
+@pytest.mark.parametrize("variant", ["spherical", "euclid", "direct"])
+def test_gptq_matches_oracle(variant):
+    # spherical GPTQ on a seeded 12 x 240 layer (10 block columns) with a correlated Hessian
+    from oracle import gptq as ogptq
+    from weight_decompression_amd import gptq as ggptq
+    W, H = synth.gptq_problem(33, 12, 240, 1024)
+    gains = (synth.chi_gain_table(16).astype(np.float64) * 0.02).astype(np.float16)
+    want_idx, want_g = ogptq.gptq(W, H, 10, gains, variant=variant)
+    desc, packed, idx, gidx = ggptq.gptq(torch.from_numpy(W).cuda(), torch.from_numpy(H).cuda(), 10,
+                                         torch.from_numpy(gains).cuda(), variant=variant)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy().view(np.uint64), want_idx)
+    assert np.array_equal(gidx.cpu().numpy(), want_g)
+    fields = want_idx | (want_g.astype(np.uint64) << np.uint64(44))
+    assert np.array_equal(packed.cpu().numpy(), synth.pack_fields(fields.reshape(-1), 48))
+    say(f"gptq {variant}: 120 blocks equal to the oracle")

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllvq.so"
 
 EXPORTED_SYMBOLS = ("llvq_index_count", "llvq_packed_bytes", "llvq_error_string",
                     "llvq_decode", "llvq_gemv", "llvq_encode_ref", "llvq_search", "llvq_quantize_workspace_bytes",
-                    "llvq_quantize")
+                    "llvq_quantize", "llvq_pack_fields")
 
 
 class LlvqError(RuntimeError):
@@ -82,6 +82,8 @@ def load_library(path=LIB_PATH):
     lib.llvq_quantize_workspace_bytes.restype = i64
     lib.llvq_quantize.argtypes = [dp, vp, vp, vp, vp, vp, vp]
     lib.llvq_quantize.restype = ctypes.c_int
+    lib.llvq_pack_fields.argtypes = [dp, vp, vp, vp]
+    lib.llvq_pack_fields.restype = ctypes.c_int
     _libs[path] = lib
     return lib
 
@@ -167,3 +169,9 @@ def quantize(desc, w, scales, packed, workspace, err_count=None, stream=None):
     packed_bytes(desc) bytes); workspace: quantize_workspace_bytes(desc) bytes of device memory."""
     _check(load_library().llvq_quantize(ctypes.byref(desc), _ptr(w), _ptr(scales), _ptr(packed), _ptr(workspace),
                                         _ptr(err_count), _stream(stream)), "llvq_quantize")
+
+
+def pack_fields(desc, fields, packed, stream=None):
+    """Write uint64 fields [rows * Kb] (int64 tensor) as the packed stream of desc."""
+    _check(load_library().llvq_pack_fields(ctypes.byref(desc), _ptr(fields), _ptr(packed), _stream(stream)),
+           "llvq_pack_fields")

@@ -712,8 +712,20 @@ LLVQ_API int llvq_quantize(const llvq_desc* d, const float* w, const void* scale
   st1 = llvq_encode_ref(pts, n, k.max_shell, idx, err_count, stream);
   if (st1 != LLVQ_OK) return st1;
   const int64_t nwords = packed_bytes_of(k) / 4;
-  hipLaunchKernelGGL(k_pack, dim3(grid_for((uint64_t)nwords, 256)), dim3(256), 0, s, k, w,
+  hipLaunchKernelGGL((k_pack<false>), dim3(grid_for((uint64_t)nwords, 256)), dim3(256), 0, s, k, w,
                      k.mode == LLVQ_MODE_SHAPEGAIN ? static_cast<const __half*>(scales) : (const __half*)nullptr, idx,
+                     static_cast<uint32_t*>(packed), nwords);
+  return launch_status();
+}
+
+LLVQ_API int llvq_pack_fields(const llvq_desc* d, const uint64_t* fields, void* packed, void* stream) {
+  KDesc k;
+  const int st = make_kdesc(d, &k);
+  if (st != LLVQ_OK) return st;
+  if (!fields || !packed || !aligned(fields, 8) || !aligned(packed, 16)) return LLVQ_EINVAL;
+  const int64_t nwords = packed_bytes_of(k) / 4;
+  hipLaunchKernelGGL((k_pack<true>), dim3(grid_for((uint64_t)nwords, 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), k, (const float*)nullptr, (const __half*)nullptr, fields,
                      static_cast<uint32_t*>(packed), nwords);
   return launch_status();
 }

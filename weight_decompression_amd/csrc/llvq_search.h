@@ -332,6 +332,9 @@ __device__ __forceinline__ uint64_t quant_field(const KDesc& d, const float* __r
   return F;
 }
 
+// FIELDS: idx holds the finished fields (llvq_pack_fields); otherwise the fields are
+// built from the shape indices, the weights and the gain table (llvq_quantize).
+template <bool FIELDS>
 __global__ __launch_bounds__(256) void k_pack(KDesc d, const float* __restrict__ w, const __half* __restrict__ gains,
                                               const uint64_t* __restrict__ idx, uint32_t* __restrict__ out,
                                               int64_t nwords) {
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(256) void k_pack(KDesc d, const float* __restrict__
     const uint64_t bit0 = (uint64_t)wd * 32u;
     uint32_t word = 0u;
     for (uint64_t j = bit0 / f; j < nfields && j * f < bit0 + 32u; ++j) {
-      const uint64_t F = quant_field(d, w, gains, idx, j);
+      const uint64_t F = FIELDS ? idx[j] & (f == 64 ? ~0ull : ((1ull << f) - 1ull)) : quant_field(d, w, gains, idx, j);
       const int64_t off = (int64_t)(j * f) - (int64_t)bit0;   // -64 < off < 32
       word |= off >= 0 ? (uint32_t)(F << off) : (uint32_t)(F >> (-off));
     }

@@ -132,6 +132,32 @@ def chi_gain_table(levels, dim=DIM) -> np.ndarray:
     return (c * np.diff(upper) * levels).astype(np.float16)
 
 
+def gptq_layer(workload, rows, cols, samples, std=0.02):
+    """The weights and activations behind gptq_problem: (W [rows][cols] fp32,
+    X [samples][cols] fp32), H = X^T X / samples."""
+    W = (rng(workload, 0, 8).standard_normal((rows, cols)) * std).astype(np.float32)
+    r = rng(workload, 0, 9)
+    mix = r.standard_normal((cols, cols)) / np.sqrt(cols) + np.eye(cols)
+    scale = np.exp(0.5 * r.standard_normal(cols))
+    X = (r.standard_normal((samples, cols)) @ mix) * scale
+    return W, X.astype(np.float32)
+
+
+def gptq_problem(workload, rows, cols, samples, std=0.02):
+    """A layer for error-feedback quantisation: dense N(0, std^2) weights W [rows][cols]
+    (fp32) and the Hessian H = X^T X / samples (fp64) of activations X [samples][cols] with
+    correlated channels (standard normals mixed by I + a random Gaussian matrix / sqrt(cols))
+    and log-normal channel scales exp(0.5 N(0, 1)) (some larger channels, as in LLM
+    activations)."""
+    W = (rng(workload, 0, 8).standard_normal((rows, cols)) * std).astype(np.float32)
+    r = rng(workload, 0, 9)
+    mix = r.standard_normal((cols, cols)) / np.sqrt(cols) + np.eye(cols)
+    scale = np.exp(0.5 * r.standard_normal(cols))
+    X = (r.standard_normal((samples, cols)) @ mix) * scale
+    H = X.T @ X / samples
+    return W, H
+
+
 def draw_activations(workload, tensor, batch, cols, dtype="bf16"):
     xs = np.stack([rng(workload, tensor, 4 + b).standard_normal(cols).astype(np.float32)
                    for b in range(batch)])
