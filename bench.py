@@ -66,11 +66,11 @@ KERNEL_PROFILES = {
     },
     "decode_bf16": {
         "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
-        "summary": "profiles/decode_bf16_7b_layer_k_decode_tile.md",
-        "unit_of_work": "24-weight block (k_decode_tile<bf16>)",
+        "summary": "profiles/decode_bf16_7b_k_decode_many.md",
+        "unit_of_work": "24-weight block (k_decode_many<bf16>)",
         "valu_lane_ops_per_unit": 760.4,
-        "fetch_bytes_per_launch": None,        # per-launch figures of a mixed-shape layer; see the summary
-        "write_bytes_per_launch": None,
+        "fetch_bytes_per_launch": 0,           # one launch = two layers (14 tensors)
+        "write_bytes_per_launch": 0,
     },
     "roundtrip": {
         "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
@@ -262,9 +262,25 @@ def run_decode_7b(a):
         print(f"bench: layer {L} generated", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
-    calls = [(ctypes.byref(d), ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(s.data_ptr()), wd.OUT_BF16,
-              ctypes.c_void_p(o.data_ptr()), None, sptr) for d, p, s, o in items]
-    dec = lib.llvq_decode
+    if a.many > 0:
+        # llvq_decode_many over groups of a.many tensors (host argument arrays built once)
+        calls, keep = [], []
+        for g0 in range(0, len(items), a.many):
+            grp = items[g0:g0 + a.many]
+            n = len(grp)
+            darr = (wd.Desc * n)(*[d for d, _, _, _ in grp])
+            parr = (ctypes.c_void_p * n)(*[p.data_ptr() for _, p, _, _ in grp])
+            sarr = (ctypes.c_void_p * n)(*[s.data_ptr() for _, _, s, _ in grp])
+            oarr = (ctypes.c_void_p * n)(*[o.data_ptr() for _, _, _, o in grp])
+            calls.append((ctypes.cast(darr, ctypes.c_void_p), n, ctypes.cast(parr, ctypes.c_void_p),
+                          ctypes.cast(sarr, ctypes.c_void_p), wd.OUT_BF16, ctypes.cast(oarr, ctypes.c_void_p),
+                          None, sptr))
+            keep.append((darr, parr, sarr, oarr))
+        dec = lib.llvq_decode_many
+    else:
+        calls = [(ctypes.byref(d), ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(s.data_ptr()), wd.OUT_BF16,
+                  ctypes.c_void_p(o.data_ptr()), None, sptr) for d, p, s, o in items]
+        dec = lib.llvq_decode
 
     def step(_):
         rc = 0
@@ -277,13 +293,16 @@ def run_decode_7b(a):
     alg_bytes = packed_bytes + 2 * weights
     out = base_line("bulk LLVQ decode-to-bf16 throughput, 7B-shaped weight set, 1 MI355X",
                     weights / sec, "weights/s", a.steps, a.warmup, sec, "f32",
-                    f"llvq_decode bf16, {layers} layers x (4 x 4096x4096 + 3 x 4096x11008)",
-                    {"layers": layers, "tensors": len(items), "blocks": blocks, "weights": weights,
-                     "packed_bytes": packed_bytes, "bf16_bytes": 2 * weights})
+                    (f"llvq_decode_many bf16, {a.many} tensors per call" if a.many > 0 else "llvq_decode bf16")
+                    + f", {layers} layers x (4 x 4096x4096 + 3 x 4096x11008)",
+                    {"layers": layers, "tensors": len(items), "tensors_per_call": max(a.many, 1), "blocks": blocks,
+                     "weights": weights, "packed_bytes": packed_bytes, "bf16_bytes": 2 * weights})
     out["compressed_GBps"] = packed_bytes / sec / 1e9
     out["bf16_written_GBps"] = 2 * weights / sec / 1e9
     out["roofline"] = roofline("decode_bf16", blocks, sec, alg_bytes,
                                "6 B packed index read + 48 B bf16 written per 24-weight block")
+    out["roofline"]["launches_per_step"] = len(calls)
+    out["roofline"]["hbm"]["bytes_per_launch"] = alg_bytes / len(calls)
     out["wall_s_timed"] = wall
     return out
 
@@ -549,6 +568,8 @@ def main():
                     help="default: the 4096x11008 batch-1 GEMV (the headline line)")
     ap.add_argument("--batch", type=int, default=1, help="activation rows (GEMV workloads)")
     ap.add_argument("--layers", type=int, default=32, help="layers of the 7B-shaped set (decode_bf16_7b)")
+    ap.add_argument("--many", type=int, default=14, metavar="N",
+                    help="tensors per llvq_decode_many call (decode_bf16_7b; 0: one llvq_decode per tensor)")
     ap.add_argument("--points", type=int, default=100_000_000, help="indices in the round trip")
     ap.add_argument("--cpu-blocks", type=int, default=2048, help="blocks the CPU oracle search is timed on (search)")
     ap.add_argument("--fidelity-blocks", type=int, default=262144, help="Gaussian source blocks (fidelity)")

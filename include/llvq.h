@@ -107,6 +107,23 @@ const char* llvq_error_string(int code);
 int llvq_decode(const llvq_desc* d, const void* packed, const void* scales, int32_t out_kind,
                 void* out, int32_t* err_count, void* stream);
 
+/* Decode several tensors in one call: the same result as llvq_decode on each, in one
+ * launch when their tiles fit (one set-up, and the workgroups' stores spread over the
+ * decode of other tiles instead of arriving together), else tensor by tensor.
+ *   descs     : n descriptors (host array) with equal mode, max_shell, shape_bits and
+ *               gain_bits; shapes may differ.
+ *   n         : 1..16.
+ *   packed    : host array of n device pointers (16-byte aligned), as for llvq_decode.
+ *   scales    : host array of n device pointers (required for LLVQ_OUT_BF16, else may be
+ *               NULL), as for llvq_decode.
+ *   out_kind  : LLVQ_OUT_POINTS_I8 or LLVQ_OUT_BF16, for every tensor.
+ *   outs      : host array of n device pointers, each laid out as llvq_decode's output.
+ *   err_count : nullable; invalid indices of all tensors are counted together.
+ * Returns LLVQ_OK, LLVQ_EINVAL (also for tensors that differ in widths or shell range) or
+ * LLVQ_EHIP. */
+int llvq_decode_many(const llvq_desc* descs, int32_t n, const void* const* packed, const void* const* scales,
+                     int32_t out_kind, void* const* outs, int32_t* err_count, void* stream);
+
 /* Fused dequantise-GEMV / small-batch GEMM: y[b][r] = sum_k W_hat[r][k] * x[b][k]
  * (papernotes.org, 关键设计 4: decode each block from its index and accumulate its dot
  * product with the activations without writing W_hat to memory).

@@ -139,3 +139,31 @@ def test_pack_fields_validation(lib):
     assert lib.llvq_pack_fields(ctypes.byref(d), ctypes.c_void_p(0x10004), p, None) == -1
     assert lib.llvq_pack_fields(ctypes.byref(d), p, ctypes.c_void_p(0x10008), None) == -1
     assert lib.llvq_pack_fields(None, p, p, None) == -1
+
+
+def test_decode_many_validation(lib):
+    d = wd.make_desc(wd.MODE_SHAPEGAIN, 8, 48, 10, 44, 4)
+    other = wd.make_desc(wd.MODE_SHAPEGAIN, 8, 48, 10, 46, 4)       # valid, other shape width
+    assert lib.llvq_packed_bytes(ctypes.byref(other)) > 0
+    p = ctypes.c_void_p(0x10000)
+
+    def call(descs, n, packed=None, scales=None, kind=1, outs=None, err=None):
+        darr = (wd.Desc * len(descs))(*descs)
+        parr = (ctypes.c_void_p * len(descs))(*([p.value] * len(descs) if packed is None else packed))
+        sarr = (ctypes.c_void_p * len(descs))(*([p.value] * len(descs) if scales is None else scales))
+        oarr = (ctypes.c_void_p * len(descs))(*([p.value] * len(descs) if outs is None else outs))
+        return lib.llvq_decode_many(ctypes.cast(darr, ctypes.c_void_p), n, ctypes.cast(parr, ctypes.c_void_p),
+                                    ctypes.cast(sarr, ctypes.c_void_p), kind, ctypes.cast(oarr, ctypes.c_void_p),
+                                    err, None)
+
+    assert call([d], 0) == -1                                    # no tensors
+    assert call([d] * 17, 17) == -1                              # more than 16
+    assert call([d, other], 2) == -1                             # widths differ
+    assert call([d, d], 2, kind=5) == -1                         # bad out kind
+    assert call([d, d], 2, packed=[0x10000, 0x10008]) == -1      # misaligned stream
+    assert call([d, d], 2, scales=[0x10000, 0]) == -1            # bf16 needs every gain table
+    assert call([d, d], 2, kind=0, outs=[0x10000, 0x10002]) == -1    # int8 output not 4-aligned
+    bad = wd.make_desc(wd.MODE_SHAPEGAIN, 8, 48, 10, 44, 4)
+    bad.max_shell = 1
+    assert call([d, bad], 2) == -1                               # invalid descriptor
+    assert lib.llvq_decode_many(None, 1, p, p, 1, p, None, None) == -1

@@ -235,6 +235,84 @@ def test_decode_bf16_euclid_ragged_bit_exact():
 
 
 # ---------------------------------------------------------------------------
+# several tensors in one call
+
+def _decode_one(t, kind):
+    desc, packed, scales, _ = dev(t)
+    shape = (t.rows, t.kb * 24) if kind == wd.OUT_POINTS_I8 else (t.rows, t.cols)
+    out = torch.empty(shape, dtype=torch.int8 if kind == wd.OUT_POINTS_I8 else torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.decode(desc, packed, scales, kind, out, err)
+    return out, err
+
+
+def _check_many(ts, kind, oracle_rows=4):
+    devs = [dev(t) for t in ts]
+    outs = []
+    for t in ts:
+        shape = (t.rows, t.kb * 24) if kind == wd.OUT_POINTS_I8 else (t.rows, t.cols)
+        dt = torch.int8 if kind == wd.OUT_POINTS_I8 else torch.bfloat16
+        outs.append(torch.full(shape, 0x55 if kind == wd.OUT_POINTS_I8 else 7.0, dtype=dt, device="cuda"))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.decode_many([d for d, _, _, _ in devs], [p for _, p, _, _ in devs], [s for _, _, s, _ in devs], kind,
+                   outs, err)
+    torch.cuda.synchronize()
+    err_sum = 0
+    for j, t in enumerate(ts):
+        one, e1 = _decode_one(t, kind)
+        torch.cuda.synchronize()
+        err_sum += int(e1.item())
+        a = outs[j].view(torch.int8 if kind == wd.OUT_POINTS_I8 else torch.int16).cpu().numpy()
+        b = one.view(torch.int8 if kind == wd.OUT_POINTS_I8 else torch.int16).cpu().numpy()
+        assert np.array_equal(a, b), (j, t.rows, t.cols)
+        raw = t.packed.tobytes()
+        rows = sample_rows(t.rows, oracle_rows, 100 + j) if t.rows > 2 else range(t.rows)
+        for r in [r for r in rows if np.all(t.shape_idx[r] < np.uint64(leech.index_count(t.max_shell)))]:
+            if kind == wd.OUT_POINTS_I8:
+                ref = reference.decode_row_points(raw, t.rows, t.cols, t.max_shell, t.shape_bits, t.gain_bits, r)
+                assert np.array_equal(a[r].astype(np.int64), ref), (j, r)
+            else:
+                sg = t.mode == synth.MODE_SHAPEGAIN
+                ref = reference.decode_row_bf16(raw, t.rows, t.cols, t.max_shell, t.mode, t.shape_bits, t.gain_bits,
+                                                t.scales_f16 if sg else None, None if sg else t.scales_f16, r)
+                assert np.array_equal(a[r].view(np.uint16), ref), (j, r)
+    assert int(err.item()) == err_sum
+    say(f"decode_many: {len(ts)} tensors, {sum(t.rows * t.kb for t in ts)} blocks, kind {kind}, errors {err_sum}")
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_decode_many_mixed_shapes_equal_single_decodes(kind):
+    # shapes of one transformer layer cut down, ragged rows and columns, a one-block tensor
+    # and invalid blocks (counted once, over all tensors, and decoded to zero)
+    ts = [synth.make_tensor("m0", 31, 0, 48, 4096, C10, batch=0),
+          synth.make_tensor("m1", 31, 1, 37, 11008, C10, batch=0),
+          synth.make_tensor("m2", 31, 2, 100, 100, C10, batch=0),
+          synth.make_tensor("m3", 31, 3, 1, 24, C10, batch=0),
+          synth.make_tensor("m4", 31, 4, 700, 4096, C10, batch=0)]
+    ts[1] = _with_invalid_blocks(ts[1], [(0, 0), (36, 458), (20, 100)])
+    _check_many(ts, kind)
+
+
+def test_decode_many_sixteen_tensors_and_euclid():
+    rng = np.random.default_rng(32)
+    ts = [synth.make_tensor(f"s{j}", 32, j, int(rng.integers(1, 90)), int(rng.integers(1, 3000)), C10, batch=0)
+          for j in range(16)]
+    _check_many(ts, wd.OUT_BF16, oracle_rows=2)
+    C3_ = leech.index_count(3)
+    te = [synth.make_tensor(f"e{j}", 33, j, r, c, C3_, mode=synth.MODE_EUCLID, max_shell=3, shape_bits=25,
+                            gain_bits=0, batch=0) for j, (r, c) in enumerate([(37, 100), (64, 4096), (1, 24)])]
+    _check_many(te, wd.OUT_BF16)
+    _check_many(te, wd.OUT_POINTS_I8)
+
+
+def test_decode_many_falls_back_for_rows_longer_than_a_tile():
+    # 96000 columns (4000 blocks per row) do not fit a tile buffer: tensor-by-tensor decode
+    ts = [synth.make_tensor("w0", 34, 0, 3, 96000, C10, batch=0),
+          synth.make_tensor("w1", 34, 1, 40, 4096, C10, batch=0)]
+    _check_many(ts, wd.OUT_BF16, oracle_rows=3)
+
+
+# ---------------------------------------------------------------------------
 # fused GEMV
 
 def test_gemv_tiny_workload_all_rows():

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllvq.so"
 
 EXPORTED_SYMBOLS = ("llvq_index_count", "llvq_packed_bytes", "llvq_error_string",
                     "llvq_decode", "llvq_gemv", "llvq_encode_ref", "llvq_search", "llvq_quantize_workspace_bytes",
-                    "llvq_quantize", "llvq_pack_fields")
+                    "llvq_quantize", "llvq_pack_fields", "llvq_decode_many")
 
 
 class LlvqError(RuntimeError):
@@ -84,6 +84,8 @@ def load_library(path=LIB_PATH):
     lib.llvq_quantize.restype = ctypes.c_int
     lib.llvq_pack_fields.argtypes = [dp, vp, vp, vp]
     lib.llvq_pack_fields.restype = ctypes.c_int
+    lib.llvq_decode_many.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp]
+    lib.llvq_decode_many.restype = ctypes.c_int
     _libs[path] = lib
     return lib
 
@@ -175,3 +177,16 @@ def pack_fields(desc, fields, packed, stream=None):
     """Write uint64 fields [rows * Kb] (int64 tensor) as the packed stream of desc."""
     _check(load_library().llvq_pack_fields(ctypes.byref(desc), _ptr(fields), _ptr(packed), _stream(stream)),
            "llvq_pack_fields")
+
+
+def decode_many(descs, packed, scales, out_kind, outs, err_count=None, stream=None):
+    """llvq_decode of several tensors in one call (equal widths and shell range)."""
+    n = len(descs)
+    darr = (Desc * n)(*descs)
+    parr = (ctypes.c_void_p * n)(*[p.data_ptr() for p in packed])
+    sarr = None if scales is None else (ctypes.c_void_p * n)(*[x.data_ptr() for x in scales])
+    oarr = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    _check(load_library().llvq_decode_many(ctypes.cast(darr, ctypes.c_void_p), n, ctypes.cast(parr, ctypes.c_void_p),
+                                           None if sarr is None else ctypes.cast(sarr, ctypes.c_void_p), out_kind,
+                                           ctypes.cast(oarr, ctypes.c_void_p), _ptr(err_count), _stream(stream)),
+           "llvq_decode_many")

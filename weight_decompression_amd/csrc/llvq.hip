@@ -190,6 +190,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 #include "llvq_gemv_b1.h"
 #include "llvq_tile.h"
 #include "llvq_gemm.h"
+#include "llvq_many.h"
 
 // ---------------------------------------------------------------------------
 // kernels
@@ -617,6 +618,83 @@ LLVQ_API int llvq_decode(const llvq_desc* d, const void* packed, const void* sca
                      static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales),
                      static_cast<uint16_t*>(out), err_count);
   return launch_status();
+}
+
+namespace {
+// One launch for several tensors (llvq_many.h): tiles of at most tmax blocks (two tile
+// buffers), each tensor's rows cut into the largest tiles that fit.  LLVQ_EUNSUPPORTED
+// when a row does not fit a tile (the caller then decodes tensor by tensor).
+int launch_decode_many(const KDesc* k, int n, const void* const* packed, const void* const* scales,
+                       int32_t out_kind, void* const* outs, int32_t* err, hipStream_t s) {
+  const KDesc& k0 = k[0];
+  const int nbuckets = (int)(((host_tables::kIndexCount[k0.max_shell] - 1) >> k0.bshift) + 1);
+  const int ng = (k0.mode == LLVQ_MODE_SHAPEGAIN ? 1 << k0.gain_bits : 1) * n;
+  ELayout L;
+  const uint32_t base2 = engine_layout_base(L, k0.ncls, ng, nbuckets, 0, 2);
+  if (base2 + 64u + 48u * 16u > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((kLdsBudget - base2 - 64u) / 48u) & ~15;
+  if (tmax > kETileMax) tmax = kETileMax;
+  MArgs m = {};
+  m.n = n;
+  int tiles = 0, Tmax = 0;
+  for (int i = 0; i < n; ++i) {
+    if (k[i].kb > tmax || (uint64_t)k[i].rows * (uint64_t)k[i].kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;
+    const int r = min(k[i].rows, tmax / k[i].kb);
+    MTensor& t = m.t[i];
+    t.packed = static_cast<const uint8_t*>(packed[i]);
+    t.scales = scales ? static_cast<const __half*>(scales[i]) : nullptr;
+    t.out = outs[i];
+    t.rows = k[i].rows;
+    t.cols = k[i].cols;
+    t.kb = k[i].kb;
+    t.rows_per_tile = r;
+    t.tile0 = tiles;
+    tiles += (k[i].rows + r - 1) / r;
+    Tmax = max(Tmax, r * k[i].kb);
+  }
+  m.ntiles = tiles;
+  m.e.nbuckets = nbuckets;
+  engine_layout_base(m.e.L, k0.ncls, ng, nbuckets, Tmax, 2);
+  m.e.xs = m.e.L.total;
+  const uint32_t total = m.e.xs + align16(24u * (uint32_t)Tmax);
+  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  const int grid = tiles < kGridMax ? tiles : kGridMax;
+  if (out_kind == LLVQ_OUT_POINTS_I8)
+    hipLaunchKernelGGL((k_decode_many<LLVQ_OUT_POINTS_I8>), dim3(grid), dim3(kEThreads), total, s, k0, m, err);
+  else
+    hipLaunchKernelGGL((k_decode_many<LLVQ_OUT_BF16>), dim3(grid), dim3(kEThreads), total, s, k0, m, err);
+  return launch_status();
+}
+}  // namespace
+
+LLVQ_API int llvq_decode_many(const llvq_desc* descs, int32_t n, const void* const* packed,
+                              const void* const* scales, int32_t out_kind, void* const* outs, int32_t* err_count,
+                              void* stream) {
+  if (!descs || !packed || !outs || n < 1 || n > kManyMax) return LLVQ_EINVAL;
+  if (out_kind != LLVQ_OUT_POINTS_I8 && out_kind != LLVQ_OUT_BF16) return LLVQ_EINVAL;
+  if (out_kind == LLVQ_OUT_BF16 && !scales) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  KDesc k[kManyMax];
+  for (int i = 0; i < n; ++i) {
+    const int st = make_kdesc(&descs[i], &k[i]);
+    if (st != LLVQ_OK) return st;
+    if (k[i].mode != k[0].mode || k[i].max_shell != k[0].max_shell || k[i].shape_bits != k[0].shape_bits ||
+        k[i].gain_bits != k[0].gain_bits)
+      return LLVQ_EINVAL;
+    if (!packed[i] || !outs[i] || !aligned(packed[i], 16)) return LLVQ_EINVAL;
+    if (out_kind == LLVQ_OUT_POINTS_I8 && !aligned(outs[i], 4)) return LLVQ_EINVAL;
+    if (out_kind == LLVQ_OUT_BF16 && (!scales[i] || !aligned(outs[i], 2) || !aligned(scales[i], 2))) return LLVQ_EINVAL;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int st = launch_decode_many(k, n, packed, out_kind == LLVQ_OUT_BF16 ? scales : nullptr, out_kind, outs,
+                                    err_count, s);
+  if (st != LLVQ_EUNSUPPORTED) return st;
+  for (int i = 0; i < n; ++i) {
+    const int st1 = llvq_decode(&descs[i], packed[i], scales ? scales[i] : nullptr, out_kind, outs[i], err_count,
+                                stream);
+    if (st1 != LLVQ_OK) return st1;
+  }
+  return LLVQ_OK;
 }
 
 LLVQ_API int llvq_gemv(const llvq_desc* d, const void* packed, const void* scales, const void* x, int32_t x_dtype,

@@ -76,6 +76,66 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // between bytes: (u | 0x80) - 12 stays in [0x74, 0x8c] for u in [0, 24].
 __device__ __forceinline__ uint32_t unbias4(uint32_t u) { return ((u | 0x80808080u) - 0x0c0c0c0cu) ^ 0x80808080u; }
 
+// Store phase: the byte tile of rows row0 .. row0 + nrows - 1 to the output, row by row
+// with 8 consecutive columns per lane (the global writes of a wavefront are contiguous).
+template <int OUT>
+__device__ __forceinline__ void store_tile(const uint8_t* smem, uint32_t tb, const float* part, const KDesc& d,
+                                           int row0, int nrows, const __half* __restrict__ scales,
+                                           void* __restrict__ out, int tid) {
+  const int kb = d.kb;
+  const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
+  const uint32_t rowbytes = (uint32_t)kb * 24u;
+  if (OUT == LLVQ_OUT_POINTS_I8) {
+    const bool a8 = (((uintptr_t)out) & 7u) == 0u;
+    const uint32_t n8 = rowbytes >> 3;
+    for (int rl = 0; rl < nrows; ++rl) {
+      int8_t* orow = static_cast<int8_t*>(out) + (size_t)(row0 + rl) * rowbytes;
+      const uint8_t* trow = smem + tb + (uint32_t)rl * rowbytes;
+      for (uint32_t j = (uint32_t)tid; j < n8; j += kEThreads) {
+        const uint2 u = *reinterpret_cast<const uint2*>(trow + 8u * j);
+        const uint32_t lo = unbias4(u.x), hi = unbias4(u.y);
+        if (a8) {
+          *reinterpret_cast<uint2*>(orow + 8u * j) = make_uint2(lo, hi);
+        } else {
+          reinterpret_cast<uint32_t*>(orow + 8u * j)[0] = lo;
+          reinterpret_cast<uint32_t*>(orow + 8u * j)[1] = hi;
+        }
+      }
+    }
+  } else {
+    const int K = d.cols;
+    const bool a16 = ((((uintptr_t)out) & 15u) == 0u) && ((K & 7) == 0);
+    const uint32_t n8 = (uint32_t)(K + 7) >> 3;
+    for (int rl = 0; rl < nrows; ++rl) {
+      const int r = row0 + rl;
+      uint16_t* orow = static_cast<uint16_t*>(out) + (size_t)r * (size_t)K;
+      const uint8_t* trow = smem + tb + (uint32_t)rl * rowbytes;
+      const float rs = sg ? 0.0f : __half2float(scales[r]);
+      for (uint32_t j = (uint32_t)tid; j < n8; j += kEThreads) {
+        const uint2 u = *reinterpret_cast<const uint2*>(trow + 8u * j);
+        const float sc = sg ? part[rl * kb + (int)(j / 3u)] : rs;
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t byte = ((q < 4 ? u.x : u.y) >> (8 * (q & 3))) & 0xffu;
+          v[q] = __fmul_rn((float)((int)byte - kBias), sc);
+        }
+        const uint4 pk = make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
+                                    pack_bf16(v[6], v[7]));
+        const uint32_t col = 8u * j;
+        if (a16) {
+          *reinterpret_cast<uint4*>(orow + col) = pk;
+        } else {
+          const uint32_t w[4] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if ((int)(col + q) < K) orow[col + q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+        }
+      }
+    }
+  }
+}
+
 template <int OUT>
 __global__ __launch_bounds__(kEThreads) void k_decode_tile(KDesc d, EArgs a, const uint8_t* __restrict__ packed,
                                                             const __half* __restrict__ scales, void* __restrict__ out,
@@ -86,9 +146,7 @@ __global__ __launch_bounds__(kEThreads) void k_decode_tile(KDesc d, EArgs a, con
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int kb = d.kb;
-  const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
   const uint32_t tb = a.xs;                 // byte tile
-  const uint32_t rowbytes = (uint32_t)kb * 24u;
   const float inv_kb = 1.0f / (float)kb;
 
   // Tiles of this workgroup: blockIdx.x + lt * gridDim.x, queues and scale slots in buffer
@@ -153,58 +211,7 @@ __global__ __launch_bounds__(kEThreads) void k_decode_tile(KDesc d, EArgs a, con
       }
     }
     __syncthreads();
-    const float* part = reinterpret_cast<const float*>(smem + cur.part);
-
-    // ---- store phase
-    if (OUT == LLVQ_OUT_POINTS_I8) {
-      const bool a8 = (((uintptr_t)out) & 7u) == 0u;
-      const uint32_t n8 = rowbytes >> 3;
-      for (int rl = 0; rl < nrows; ++rl) {
-        int8_t* orow = static_cast<int8_t*>(out) + (size_t)(row0 + rl) * rowbytes;
-        const uint8_t* trow = smem + tb + (uint32_t)rl * rowbytes;
-        for (uint32_t j = (uint32_t)tid; j < n8; j += kEThreads) {
-          const uint2 u = *reinterpret_cast<const uint2*>(trow + 8u * j);
-          const uint32_t lo = unbias4(u.x), hi = unbias4(u.y);
-          if (a8) {
-            *reinterpret_cast<uint2*>(orow + 8u * j) = make_uint2(lo, hi);
-          } else {
-            reinterpret_cast<uint32_t*>(orow + 8u * j)[0] = lo;
-            reinterpret_cast<uint32_t*>(orow + 8u * j)[1] = hi;
-          }
-        }
-      }
-    } else {
-      const int K = d.cols;
-      const bool a16 = ((((uintptr_t)out) & 15u) == 0u) && ((K & 7) == 0);
-      const uint32_t n8 = (uint32_t)(K + 7) >> 3;
-      for (int rl = 0; rl < nrows; ++rl) {
-        const int r = row0 + rl;
-        uint16_t* orow = static_cast<uint16_t*>(out) + (size_t)r * (size_t)K;
-        const uint8_t* trow = smem + tb + (uint32_t)rl * rowbytes;
-        const float rs = sg ? 0.0f : __half2float(scales[r]);
-        for (uint32_t j = (uint32_t)tid; j < n8; j += kEThreads) {
-          const uint2 u = *reinterpret_cast<const uint2*>(trow + 8u * j);
-          const float sc = sg ? part[rl * kb + (int)(j / 3u)] : rs;
-          float v[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const uint32_t byte = ((q < 4 ? u.x : u.y) >> (8 * (q & 3))) & 0xffu;
-            v[q] = __fmul_rn((float)((int)byte - kBias), sc);
-          }
-          const uint4 pk = make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
-                                      pack_bf16(v[6], v[7]));
-          const uint32_t col = 8u * j;
-          if (a16) {
-            *reinterpret_cast<uint4*>(orow + col) = pk;
-          } else {
-            const uint32_t w[4] = {pk.x, pk.y, pk.z, pk.w};
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-              if ((int)(col + q) < K) orow[col + q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
-          }
-        }
-      }
-    }
+    store_tile<OUT>(smem, tb, reinterpret_cast<const float*>(smem + cur.part), d, row0, nrows, scales, out, tid);
     if (tid == 0) {
       int* cc = reinterpret_cast<int*>(smem + cur.ctr);
       cc[0] = 0;
