@@ -49,47 +49,47 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
+        "source_sha256": "96d7f605419a9bf22345749f6fa04e476a8acff4e894fb272c217644df56652d",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
         "valu_lane_ops_per_unit": 670.3,       # SQ_INSTS_VALU * 64 / blocks
-        "fetch_bytes_per_launch": 12226438,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "fetch_bytes_per_launch": 12228484,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
+        "source_sha256": "96d7f605419a9bf22345749f6fa04e476a8acff4e894fb272c217644df56652d",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
         "valu_lane_ops_per_unit": 695.4,
-        "fetch_bytes_per_launch": 61927758,
+        "fetch_bytes_per_launch": 61929817,
         "write_bytes_per_launch": 1835008,
     },
     "decode_bf16": {
-        "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
+        "source_sha256": "96d7f605419a9bf22345749f6fa04e476a8acff4e894fb272c217644df56652d",
         "summary": "profiles/decode_bf16_7b_k_decode_many.md",
         "unit_of_work": "24-weight block (k_decode_many<bf16>)",
-        "valu_lane_ops_per_unit": 760.4,
-        "fetch_bytes_per_launch": 0,           # one launch = two layers (14 tensors)
-        "write_bytes_per_launch": 0,
+        "valu_lane_ops_per_unit": 738.4,
+        "fetch_bytes_per_launch": 103347333,           # one launch = two layers (14 tensors)
+        "write_bytes_per_launch": 809500672,
     },
     "roundtrip": {
-        "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
+        "source_sha256": "96d7f605419a9bf22345749f6fa04e476a8acff4e894fb272c217644df56652d",
         "summary": "profiles/roundtrip_1e7_k_decode_tile_k_rank.md",
-        "unit_of_work": "point: decode to int8 (627.0) + rank (951.2)",
-        "valu_lane_ops_per_unit": 1578.2,
+        "unit_of_work": "point: decode to int8 (626.0) + rank (951.2)",
+        "valu_lane_ops_per_unit": 1577.2,
         "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
         "write_bytes_per_launch": None,
     },
     "search": {
-        "source_sha256": "87e513321c28babe76c4ba6b6b9fe61beadeea1e79a576200e6b27acfe37cf65",
+        "source_sha256": "96d7f605419a9bf22345749f6fa04e476a8acff4e894fb272c217644df56652d",
         "summary": "profiles/search_4096x4096_k_search_k_rank.md",
         # The search issues more VALU instructions per clock than one per CU (mostly fp32
         # add / fma / max, which issue at up to 1.46 wave-instructions per CU per clock on
         # gfx950, profiles/valu_issue_rates_gfx950.md), so its peak is the fastest measured
         # single-instruction rate, 1.464 x 39.32 T lane-ops/s.
         "valu_peak_tops": 57.56,
-        "unit_of_work": "24-block: search (3284603.5) + rank (955.4)",
-        "valu_lane_ops_per_unit": 3285558.9,
+        "unit_of_work": "24-block: search (3351362.3) + rank (955.4)",
+        "valu_lane_ops_per_unit": 3352317.7,
         "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
         "write_bytes_per_launch": None,
     },
@@ -147,10 +147,14 @@ def time_steps(launch, steps, warmup, stream):
     return ev0.elapsed_time(ev1) / steps * 1e-3, wall
 
 
-def roofline(profile_key, ops_units, sec, alg_bytes, per_unit_text):
-    """VALU roofline from the profiled lane-op count of the current source, with the HBM figure beside it."""
+def roofline(profile_key, ops_units, sec, alg_bytes, per_unit_text, launches=1):
+    """VALU roofline from the profiled lane-op count of the current source, with the HBM figure beside it.
+    ops_units and alg_bytes cover one step of `launches` launches."""
     hbm = {"bound": "hbm", "achieved": alg_bytes / sec / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-           "frac": alg_bytes / sec / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": alg_bytes, "per_unit": per_unit_text}
+           "frac": alg_bytes / sec / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": alg_bytes / launches,
+           "per_unit": per_unit_text}
+    if launches != 1:
+        hbm["launches_per_step"] = launches
     prof = KERNEL_PROFILES.get(profile_key, {})
     prof_ok = prof.get("source_sha256") == kernel_source_sha()
     traffic = None
@@ -300,9 +304,7 @@ def run_decode_7b(a):
     out["compressed_GBps"] = packed_bytes / sec / 1e9
     out["bf16_written_GBps"] = 2 * weights / sec / 1e9
     out["roofline"] = roofline("decode_bf16", blocks, sec, alg_bytes,
-                               "6 B packed index read + 48 B bf16 written per 24-weight block")
-    out["roofline"]["launches_per_step"] = len(calls)
-    out["roofline"]["hbm"]["bytes_per_launch"] = alg_bytes / len(calls)
+                               "6 B packed index read + 48 B bf16 written per 24-weight block", launches=len(calls))
     out["wall_s_timed"] = wall
     return out
 
