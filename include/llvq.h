@@ -74,15 +74,29 @@ typedef struct {
   int32_t mode;        /* LLVQ_MODE_EUCLID or LLVQ_MODE_SHAPEGAIN                        */
   int32_t rows;        /* N >= 1: output features                                        */
   int32_t cols;        /* K >= 1: input features; Kb = ceil(K/24) blocks per row          */
-  int32_t max_shell;   /* M in [2, 10]: shape indices cover shells 2..M                  */
-  int32_t shape_bits;  /* 1..60, with llvq_index_count(M) <= 2^shape_bits                 */
-  int32_t gain_bits;   /* EUCLID: 0.  SHAPEGAIN: 1..8.  shape_bits + gain_bits <= 64      */
+  int32_t max_shell;   /* M in [2, 42]: shape indices cover shells 2..M                  */
+  int32_t shape_bits;  /* 1..120, with the index count of shells 2..M <= 2^shape_bits     */
+  int32_t gain_bits;   /* EUCLID: 0.  SHAPEGAIN: 1..8.  shape_bits + gain_bits <= 128     */
 } llvq_desc;
+
+/* Rates.  The 2-bit kernels cover M <= 10 with shape_bits <= 60 and fields of at most 64
+ * bits (2 bits per weight: 44 shape + 4 gain bits, M = 10).  Other rates (LLVQ,
+ * papernotes.org notes, 关键设计 2: the same index hierarchy at any shell radius) go to a
+ * general decoder: M up to 42 and fields up to 128 bits, e.g. 46 + 2 or 47 + 1 bits at
+ * M = 11 or 12, or 3 bits per weight as 68 + 4 bits at M = 42, where global indices pass
+ * 2^64.  Such descriptors are taken by llvq_packed_bytes, llvq_decode, llvq_decode_many
+ * (one launch per tensor) and llvq_gemv; llvq_quantize, llvq_quantize_workspace_bytes and
+ * llvq_pack_fields return LLVQ_EUNSUPPORTED for them. */
 
 /* Number of valid shape indices for shells 2..max_shell (|Lambda24(M)|).  Host only.
  * Writes *out and returns LLVQ_OK, or LLVQ_EINVAL if max_shell is outside [2, 10] or out
  * is NULL. */
 int llvq_index_count(int32_t max_shell, uint64_t* out);
+
+/* The same for M in [2, 42] as a 128-bit number (*lo | *hi << 64): past shell 33 the count
+ * exceeds 64 bits (shell 42: just below 2^68).  Host only.  LLVQ_EINVAL for M outside
+ * [2, 42] or a NULL output. */
+int llvq_index_count_wide(int32_t max_shell, uint64_t* lo, uint64_t* hi);
 
 /* Bytes the packed buffer of `d` must hold (see "Packed weights"), or a negative error
  * code for an invalid descriptor.  Host only. */
@@ -94,7 +108,7 @@ const char* llvq_error_string(int code);
 /* Decode every block of a packed tensor (gist.science, Methodik / 4.
  * Dequantisierungskernel: the index -> vector walk back through shell, class and the
  * local symmetries).
- *   packed  : llvq_packed_bytes(d) bytes, any alignment.
+ *   packed  : llvq_packed_bytes(d) bytes, 16-byte aligned.
  *   scales  : fp16; SHAPEGAIN: gain table [2^gain_bits]; EUCLID: row scales [rows].
  *             Unused (may be NULL) for LLVQ_OUT_POINTS_I8.
  *   out_kind: LLVQ_OUT_POINTS_I8 -> out is int8 [rows][Kb*24], the raw integer lattice

@@ -157,8 +157,24 @@ def class_sizes_by_shell(M: int) -> dict:
     return sizes
 
 
+@lru_cache(maxsize=None)
+def _starts(M: int) -> tuple:
+    return tuple(c.start for c in class_table(M))
+
+
 def find_class(I: int, M: int) -> LeechClass:
-    """The class whose interval holds global index I (plain linear scan)."""
+    """The class whose interval holds global index I: the last class starting at or
+    before I (the intervals are contiguous and ascending), checked to contain I."""
+    import bisect
+    table = class_table(M)
+    k = bisect.bisect_right(_starts(M), I) - 1
+    if k < 0 or not table[k].start <= I < table[k].end:
+        raise ValueError(f"shape index {I} outside the shell union 2..{M}")
+    return table[k]
+
+
+def find_class_linear(I: int, M: int) -> LeechClass:
+    """The same by a plain scan of every interval (a pin for find_class)."""
     for c in class_table(M):
         if c.start <= I < c.end:
             return c

@@ -54,10 +54,12 @@ def test_packed_bytes_rule(lib):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(mode=2), dict(rows=0), dict(cols=-1), dict(max_shell=1), dict(max_shell=11),
+    dict(mode=2), dict(rows=0), dict(cols=-1), dict(max_shell=1),
+    dict(max_shell=11),                  # C_11 > 2^44
+    dict(max_shell=43, shape_bits=70),   # past the general decoder's shell range
     dict(shape_bits=43),                 # C_10 > 2^43
     dict(gain_bits=0),                   # shape-gain needs a gain field
-    dict(gain_bits=9), dict(shape_bits=61),
+    dict(gain_bits=9), dict(shape_bits=121),
     dict(mode=0, gain_bits=4),           # Euclidean mode has no gain field
 ])
 def test_descriptor_validation(lib, bad):
@@ -167,3 +169,31 @@ def test_decode_many_validation(lib):
     bad.max_shell = 1
     assert call([d, bad], 2) == -1                               # invalid descriptor
     assert lib.llvq_decode_many(None, 1, p, p, 1, p, None, None) == -1
+
+
+def test_wide_descriptors(lib):
+    # other rates: shells past 10 and fields past 64 bits (the general decoder)
+    for M in range(2, 43):
+        lo, hi = ctypes.c_uint64(), ctypes.c_uint64()
+        assert lib.llvq_index_count_wide(M, ctypes.byref(lo), ctypes.byref(hi)) == 0
+        assert lo.value | (hi.value << 64) == leech.index_count(M)
+    assert lib.llvq_index_count_wide(43, ctypes.byref(ctypes.c_uint64()), ctypes.byref(ctypes.c_uint64())) == -1
+    assert wd.index_count(42) == leech.index_count(42)
+    from weight_decompression_amd import synth
+    for M, sb, gb in [(42, 68, 4), (12, 47, 1), (11, 46, 2), (10, 61, 3), (42, 120, 8)]:
+        d = wd.make_desc(wd.MODE_SHAPEGAIN, 7, 100, M, sb, gb)
+        assert lib.llvq_packed_bytes(ctypes.byref(d)) == synth.packed_nbytes(7 * 5, sb + gb)
+    bad = [(42, 67, 4), (43, 70, 4), (42, 121, 4), (12, 46, 2)]     # too few shape bits, shell, width
+    for M, sb, gb in bad:
+        d = wd.make_desc(wd.MODE_SHAPEGAIN, 7, 100, M, sb, gb)
+        assert lib.llvq_packed_bytes(ctypes.byref(d)) == -1, (M, sb, gb)
+    d = wd.make_desc(wd.MODE_SHAPEGAIN, 7, 100, 42, 68, 4)
+    p = ctypes.c_void_p(0x10000)
+    assert lib.llvq_quantize_workspace_bytes(ctypes.byref(d)) == -2             # unsupported, not invalid
+    assert lib.llvq_pack_fields(ctypes.byref(d), p, p, None) == -2
+    assert lib.llvq_decode(ctypes.byref(d), ctypes.c_void_p(0x10004), p, 1, p, None, None) == -1
+    assert lib.llvq_decode(ctypes.byref(d), p, None, 1, p, None, None) == -1
+    assert lib.llvq_gemv(ctypes.byref(d), p, p, p, 1, 17, p, None, None) == -1
+    assert lib.llvq_gemv(ctypes.byref(d), p, p, p, 3, 1, p, None, None) == -1
+    e = wd.make_desc(wd.MODE_EUCLID, 7, 100, 24, 60, 1)                        # Euclidean: no gain field
+    assert lib.llvq_packed_bytes(ctypes.byref(e)) == -1

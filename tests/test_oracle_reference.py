@@ -89,3 +89,18 @@ def test_tolerance_rule():
     mag = np.array([10.0, 4.0, 0.0])
     ok = reference.gemv_within_tolerance(np.array([1.0 + 9e-4, -2.0 - 5e-4, 0.0]), y_ref, mag)
     assert list(ok) == [True, False, True]
+
+
+def test_reader_inverts_wide_packer():
+    # fields past 64 bits (3 bits per weight: 68 + 4) and odd widths around the word edge
+    from weight_decompression_amd import synth
+    for M, sb, gb in [(42, 68, 4), (12, 47, 1), (16, 60, 5), (42, 120, 8)]:
+        t = synth.make_wide_tensor("w", 3, M, 4, 100, leech.index_count(M), max_shell=M, shape_bits=sb,
+                                   gain_bits=gb, batch=0)
+        raw = t.packed.tobytes()
+        assert len(raw) == synth.packed_nbytes(4 * 5, sb + gb)
+        for r in range(4):
+            f = reference.block_fields(raw, 4, 100, sb, gb, r)
+            assert [a for a, _ in f] == list(t.shape_idx[r])
+            assert [g for _, g in f] == [int(g) for g in t.gain_idx[r]]
+        assert max(t.shape_idx.ravel()) < leech.index_count(M)

@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllvq.so"
 
 EXPORTED_SYMBOLS = ("llvq_index_count", "llvq_packed_bytes", "llvq_error_string",
                     "llvq_decode", "llvq_gemv", "llvq_encode_ref", "llvq_search", "llvq_quantize_workspace_bytes",
-                    "llvq_quantize", "llvq_pack_fields", "llvq_decode_many")
+                    "llvq_quantize", "llvq_pack_fields", "llvq_decode_many",
+                    "llvq_index_count_wide")
 
 
 class LlvqError(RuntimeError):
@@ -66,6 +67,8 @@ def load_library(path=LIB_PATH):
     dp = ctypes.POINTER(Desc)
     lib.llvq_index_count.argtypes = [i32, u64p]
     lib.llvq_index_count.restype = ctypes.c_int
+    lib.llvq_index_count_wide.argtypes = [i32, u64p, u64p]
+    lib.llvq_index_count_wide.restype = ctypes.c_int
     lib.llvq_packed_bytes.argtypes = [dp]
     lib.llvq_packed_bytes.restype = i64
     lib.llvq_error_string.argtypes = [ctypes.c_int]
@@ -111,9 +114,11 @@ def make_desc(mode, rows, cols, max_shell, shape_bits, gain_bits) -> Desc:
 
 
 def index_count(max_shell: int) -> int:
-    out = ctypes.c_uint64()
-    _check(load_library().llvq_index_count(max_shell, ctypes.byref(out)), "llvq_index_count")
-    return out.value
+    """C_M as a Python integer (shells 2..42; past shell 33 it exceeds 64 bits)."""
+    lo, hi = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(load_library().llvq_index_count_wide(max_shell, ctypes.byref(lo), ctypes.byref(hi)),
+           "llvq_index_count_wide")
+    return lo.value | (hi.value << 64)
 
 
 def packed_bytes(desc: Desc) -> int:

@@ -2,8 +2,9 @@
 
 Steps:
   1. compile the host table generator (csrc/gen_tables.cpp) with g++;
-  2. run it to write the table header (and a JSON dump of the same tables) and the
-     generated device code of the nearest-point search;
+  2. run it to write the table header (and a JSON dump of the same tables), the
+     generated device code of the nearest-point search, and the class records of the
+     general decoder (shells beyond 10, fields beyond 64 bits; also dumped as JSON);
   3. compile csrc/llvq.hip for gfx950 with hipcc into weight_decompression_amd/libllvq.so.
 
 Generated files go to <repo>/_build/ (not committed).  Packed-fp32 VALU instructions
@@ -24,6 +25,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libllvq.so")
 TABLES_INC = os.path.join(BUILD_DIR, "llvq_tables.inc")
 TABLES_JSON = os.path.join(BUILD_DIR, "llvq_tables.json")
 SEARCH_INC = os.path.join(BUILD_DIR, "llvq_search.inc")
+WIDE_INC = os.path.join(BUILD_DIR, "llvq_wide.inc")
+WIDE_JSON = os.path.join(BUILD_DIR, "llvq_wide.json")
 GEN_BIN = os.path.join(BUILD_DIR, "gen_tables")
 
 OFFLOAD_ARCH = "gfx950"
@@ -41,6 +44,8 @@ def build_tables(verbose=True):
     _run([GEN_BIN, "--header", TABLES_INC], verbose)
     _run([GEN_BIN, "--json", TABLES_JSON], verbose)
     _run([GEN_BIN, "--search", SEARCH_INC], verbose)
+    _run([GEN_BIN, "--wide", WIDE_INC], verbose)
+    _run([GEN_BIN, "--wide-json", WIDE_JSON], verbose)
 
 
 def hipcc_path():

@@ -58,6 +58,20 @@ namespace dev_tables {
 #undef LLVQ_TABLE
 }  // namespace dev_tables
 
+// general decoder: shells 2..42, fields up to 128 bits (the class records on the device only)
+namespace host_tables {
+#define LLVQ_TABLE static const
+#include "llvq_wide.inc"
+#undef LLVQ_TABLE
+}  // namespace host_tables
+namespace dev_tables {
+#define LLVQ_TABLE __device__ const
+#define LLVQ_WIDE_CLASSES
+#include "llvq_wide.inc"
+#undef LLVQ_WIDE_CLASSES
+#undef LLVQ_TABLE
+}  // namespace dev_tables
+
 namespace {
 
 constexpr int kDim = 24;
@@ -191,6 +205,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 #include "llvq_tile.h"
 #include "llvq_gemm.h"
 #include "llvq_many.h"
+#include "llvq_wide.h"
 
 // ---------------------------------------------------------------------------
 // kernels
@@ -348,6 +363,52 @@ int make_kdesc(const llvq_desc* d, KDesc* k) {
   return LLVQ_OK;
 }
 
+// Descriptors beyond the 2-bit kernels' range: shells past 10 or fields past 64 bits.
+bool wide_needed(const llvq_desc* d) {
+  return d->max_shell > LLVQ_MAX_SHELL || d->shape_bits > 60 || d->shape_bits + d->gain_bits > 64;
+}
+
+int make_wdesc(const llvq_desc* d, WDesc* w) {
+  if (!d) return LLVQ_EINVAL;
+  if (d->mode != LLVQ_MODE_EUCLID && d->mode != LLVQ_MODE_SHAPEGAIN) return LLVQ_EINVAL;
+  if (d->rows <= 0 || d->cols <= 0) return LLVQ_EINVAL;
+  if (d->max_shell < 2 || d->max_shell > LLVQ_WIDE_MAX_SHELL) return LLVQ_EINVAL;
+  if (d->shape_bits < 1 || d->shape_bits > 120) return LLVQ_EINVAL;
+  if (d->mode == LLVQ_MODE_EUCLID && d->gain_bits != 0) return LLVQ_EINVAL;
+  if (d->mode == LLVQ_MODE_SHAPEGAIN && (d->gain_bits < 1 || d->gain_bits > 8)) return LLVQ_EINVAL;
+  const uint64_t clo = host_tables::kWideShellStart[d->max_shell + 1][0];
+  const uint64_t chi = host_tables::kWideShellStart[d->max_shell + 1][1];
+  // index count <= 2^shape_bits
+  if (d->shape_bits < 64) {
+    if (chi != 0 || clo > (1ull << d->shape_bits)) return LLVQ_EINVAL;
+  } else if (d->shape_bits < 128) {
+    const int hb = d->shape_bits - 64;
+    if (chi > (1ull << hb) || (chi == (1ull << hb) && clo != 0)) return LLVQ_EINVAL;
+  }
+  w->mode = d->mode;
+  w->rows = d->rows;
+  w->cols = d->cols;
+  w->kb = (d->cols + kDim - 1) / kDim;
+  w->max_shell = d->max_shell;
+  w->shape_bits = d->shape_bits;
+  w->gain_bits = d->gain_bits;
+  w->field_bits = d->shape_bits + d->gain_bits;
+  w->count_lo = clo;
+  w->count_hi = chi;
+  return LLVQ_OK;
+}
+
+// make_kdesc for the calls that only run the 2-bit kernels: a descriptor that only the
+// general decoder takes is LLVQ_EUNSUPPORTED there
+int make_kdesc_narrow(const llvq_desc* d, KDesc* k) {
+  const int st = make_kdesc(d, k);
+  if (st == LLVQ_EINVAL && d && wide_needed(d)) {
+    WDesc w;
+    if (make_wdesc(d, &w) == LLVQ_OK) return LLVQ_EUNSUPPORTED;
+  }
+  return st;
+}
+
 int64_t packed_bytes_of(const KDesc& k) {
   const uint64_t nbits = (uint64_t)k.rows * (uint64_t)k.kb * (uint64_t)k.field_bits;
   uint64_t nbytes = (nbits + 7) / 8;
@@ -375,7 +436,24 @@ LLVQ_API int llvq_index_count(int32_t max_shell, uint64_t* out) {
   return LLVQ_OK;
 }
 
+LLVQ_API int llvq_index_count_wide(int32_t max_shell, uint64_t* lo, uint64_t* hi) {
+  if (!lo || !hi || max_shell < 2 || max_shell > LLVQ_WIDE_MAX_SHELL) return LLVQ_EINVAL;
+  *lo = host_tables::kWideShellStart[max_shell + 1][0];
+  *hi = host_tables::kWideShellStart[max_shell + 1][1];
+  return LLVQ_OK;
+}
+
 LLVQ_API int64_t llvq_packed_bytes(const llvq_desc* d) {
+  if (d && wide_needed(d)) {
+    WDesc w;
+    const int st = make_wdesc(d, &w);
+    if (st != LLVQ_OK) return st;
+    KDesc k = {};
+    k.rows = w.rows;
+    k.kb = w.kb;
+    k.field_bits = w.field_bits;
+    return packed_bytes_of(k);
+  }
   KDesc k;
   const int st = make_kdesc(d, &k);
   if (st != LLVQ_OK) return st;
@@ -589,8 +667,67 @@ int launch_gemv(const KDesc& k, const void* packed, const void* scales, const vo
 }
 }  // namespace
 
+namespace {
+// General decoder (llvq_wide.h): one 24-block per lane.
+int decode_wide(const llvq_desc* d, const void* packed, const void* scales, int32_t out_kind, void* out,
+                int32_t* err_count, void* stream) {
+  WDesc w;
+  const int st = make_wdesc(d, &w);
+  if (st != LLVQ_OK) return st;
+  if (!packed || !out || !aligned(packed, 16)) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  if (out_kind == LLVQ_OUT_POINTS_I8) {
+    if (!aligned(out, 4)) return LLVQ_EINVAL;
+  } else if (out_kind == LLVQ_OUT_BF16) {
+    if (!scales || !aligned(out, 2) || !aligned(scales, 2)) return LLVQ_EINVAL;
+  } else {
+    return LLVQ_EINVAL;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const uint64_t nblocks = (uint64_t)w.rows * (uint64_t)w.kb;
+  const unsigned grid = grid_for(nblocks, kWideThreads);
+  if (out_kind == LLVQ_OUT_POINTS_I8)
+    hipLaunchKernelGGL((k_decode_wide<LLVQ_OUT_POINTS_I8>), dim3(grid), dim3(kWideThreads), 0, s, w,
+                       static_cast<const uint8_t*>(packed), nullptr, out, err_count);
+  else
+    hipLaunchKernelGGL((k_decode_wide<LLVQ_OUT_BF16>), dim3(grid), dim3(kWideThreads), 0, s, w,
+                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), out, err_count);
+  return launch_status();
+}
+
+int gemv_wide(const llvq_desc* d, const void* packed, const void* scales, const void* x, int32_t x_dtype,
+              int32_t batch, float* y, int32_t* err_count, void* stream) {
+  WDesc w;
+  const int st = make_wdesc(d, &w);
+  if (st != LLVQ_OK) return st;
+  if (!packed || !scales || !x || !y) return LLVQ_EINVAL;
+  if (!aligned(packed, 16) || !aligned(scales, 2) || !aligned(y, 4)) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  if (x_dtype == LLVQ_X_F32) {
+    if (!aligned(x, 4)) return LLVQ_EINVAL;
+  } else if (x_dtype == LLVQ_X_BF16) {
+    if (!aligned(x, 2)) return LLVQ_EINVAL;
+  } else {
+    return LLVQ_EINVAL;
+  }
+  if (batch < 1 || batch > LLVQ_MAX_BATCH) return LLVQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const unsigned grid = grid_for((uint64_t)w.rows, kWideThreads / 64);
+  if (x_dtype == LLVQ_X_BF16)
+    hipLaunchKernelGGL((k_gemv_wide<true>), dim3(grid), dim3(kWideThreads), 0, s, w,
+                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, batch, y,
+                       err_count);
+  else
+    hipLaunchKernelGGL((k_gemv_wide<false>), dim3(grid), dim3(kWideThreads), 0, s, w,
+                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, batch, y,
+                       err_count);
+  return launch_status();
+}
+}  // namespace
+
 LLVQ_API int llvq_decode(const llvq_desc* d, const void* packed, const void* scales, int32_t out_kind,
                          void* out, int32_t* err_count, void* stream) {
+  if (d && wide_needed(d)) return decode_wide(d, packed, scales, out_kind, out, err_count, stream);
   KDesc k;
   int st = make_kdesc(d, &k);
   if (st != LLVQ_OK) return st;
@@ -674,6 +811,27 @@ LLVQ_API int llvq_decode_many(const llvq_desc* descs, int32_t n, const void* con
   if (out_kind != LLVQ_OUT_POINTS_I8 && out_kind != LLVQ_OUT_BF16) return LLVQ_EINVAL;
   if (out_kind == LLVQ_OUT_BF16 && !scales) return LLVQ_EINVAL;
   if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  bool wide = false;
+  for (int i = 0; i < n; ++i) wide = wide || wide_needed(&descs[i]);
+  if (wide) {
+    // the general decoder: one call per tensor, after every descriptor and pointer is checked
+    for (int i = 0; i < n; ++i) {
+      WDesc w;
+      KDesc k1;
+      const int st = wide_needed(&descs[i]) ? make_wdesc(&descs[i], &w) : make_kdesc(&descs[i], &k1);
+      if (st != LLVQ_OK) return st;
+      if (!packed[i] || !outs[i] || !aligned(packed[i], 16)) return LLVQ_EINVAL;
+      if (out_kind == LLVQ_OUT_POINTS_I8 && !aligned(outs[i], 4)) return LLVQ_EINVAL;
+      if (out_kind == LLVQ_OUT_BF16 && (!scales[i] || !aligned(outs[i], 2) || !aligned(scales[i], 2)))
+        return LLVQ_EINVAL;
+    }
+    for (int i = 0; i < n; ++i) {
+      const int st1 = llvq_decode(&descs[i], packed[i], scales ? scales[i] : nullptr, out_kind, outs[i], err_count,
+                                  stream);
+      if (st1 != LLVQ_OK) return st1;
+    }
+    return LLVQ_OK;
+  }
   KDesc k[kManyMax];
   for (int i = 0; i < n; ++i) {
     const int st = make_kdesc(&descs[i], &k[i]);
@@ -699,6 +857,7 @@ LLVQ_API int llvq_decode_many(const llvq_desc* descs, int32_t n, const void* con
 
 LLVQ_API int llvq_gemv(const llvq_desc* d, const void* packed, const void* scales, const void* x, int32_t x_dtype,
                        int32_t batch, float* y, int32_t* err_count, void* stream) {
+  if (d && wide_needed(d)) return gemv_wide(d, packed, scales, x, x_dtype, batch, y, err_count, stream);
   KDesc k;
   int st = make_kdesc(d, &k);
   if (st != LLVQ_OK) return st;
@@ -761,7 +920,7 @@ uint64_t quantize_points_bytes(const KDesc& k) { return ((uint64_t)k.rows * (uin
 
 LLVQ_API int64_t llvq_quantize_workspace_bytes(const llvq_desc* d) {
   KDesc k;
-  const int st = make_kdesc(d, &k);
+  const int st = make_kdesc_narrow(d, &k);
   if (st != LLVQ_OK) return st;
   return (int64_t)(quantize_points_bytes(k) + (uint64_t)k.rows * (uint64_t)k.kb * 8u);
 }
@@ -769,7 +928,7 @@ LLVQ_API int64_t llvq_quantize_workspace_bytes(const llvq_desc* d) {
 LLVQ_API int llvq_quantize(const llvq_desc* d, const float* w, const void* scales, void* packed, void* workspace,
                            int32_t* err_count, void* stream) {
   KDesc k;
-  const int st = make_kdesc(d, &k);
+  const int st = make_kdesc_narrow(d, &k);
   if (st != LLVQ_OK) return st;
   if (!w || !scales || !packed || !workspace) return LLVQ_EINVAL;
   if (!aligned(w, 4) || !aligned(scales, 2) || !aligned(packed, 16) || !aligned(workspace, 8)) return LLVQ_EINVAL;
@@ -798,7 +957,7 @@ LLVQ_API int llvq_quantize(const llvq_desc* d, const float* w, const void* scale
 
 LLVQ_API int llvq_pack_fields(const llvq_desc* d, const uint64_t* fields, void* packed, void* stream) {
   KDesc k;
-  const int st = make_kdesc(d, &k);
+  const int st = make_kdesc_narrow(d, &k);
   if (st != LLVQ_OK) return st;
   if (!fields || !packed || !aligned(fields, 8) || !aligned(packed, 16)) return LLVQ_EINVAL;
   const int64_t nwords = packed_bytes_of(k) / 4;

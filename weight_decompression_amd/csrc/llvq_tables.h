@@ -72,3 +72,15 @@ struct LlvqClassRank {
   uint32_t cnt_t;    // counts of the complement slots (odd classes: all values)
   uint32_t meta;     // B | w << 8 | pi << 16 | parity << 17 | m << 20
 };
+
+// Class record of the general decoder (shells 2..42; gen_tables --wide).  Inside a class
+// every quantity fits 64 bits; the global start needs 128.
+struct LlvqWideClass {
+  uint64_t start_lo, start_hi;   // first global shape index
+  uint64_t P_S;                  // arrangements of the support values (even classes; 1 for odd)
+  uint64_t P_T;                  // arrangements of the complement values (odd classes: all 24)
+  uint8_t m, parity, w, B, pi;   // shell, coset, support length, sign bits, support sign parity
+  uint8_t nsup, ncomp, pad;      // distinct support / complement values
+  uint8_t sv[8], sc[8];          // support multiset: distinct values ascending, their counts
+  uint8_t cv[8], cc[8];          // complement multiset (odd classes: all 24 values)
+};

@@ -1,0 +1,317 @@
+// General decoder (gfx950): shells 2..42 of the Leech lattice and index fields up to 128
+// bits, for rates other than the 2-bit configuration ("LLVQ: Leech Lattice Vector
+// Quantization", papernotes.org notes, 关键设计 2: the same hierarchy shell -> class ->
+// codeword / sign pattern / permutation rank at any shell radius; 3 bits per weight is a
+// 72-bit field per 24-block, 68 shape bits reach shell 42).
+//
+// Beyond shell 10 the fixed-width shortcuts of the 2-bit kernels no longer hold (class
+// sizes reach 2^60, the index past the codeword reaches 2^53, up to 8 distinct absolute
+// values up to 25 per class, global indices past 2^64), so this decoder works with exact
+// 64-bit integers inside a class and 128-bit compares for the global index:
+//   * shell and class by binary search over 128-bit starts (records in global memory,
+//     read through the caches: 38,649 classes, 2.8 MB);
+//   * J = I - start < 2^63; r = J mod A, I' = J div A; s = I' mod 2^B, R = I' >> B;
+//     even classes R = rank_S * P_T + rank_T;
+//   * both multiset unrankings advance in one pass over the 24 positions: position p takes
+//     the next value of the support sequence if p is on the codeword, of the complement
+//     sequence otherwise (each sequence fills its positions in ascending order).  The
+//     arrangements starting with value v are rem * count(v) / n, an exact quotient taken
+//     as a product with the inverse of n's odd part modulo 2^64;
+//   * signs as in the 2-bit kernels.
+// One 24-block per lane; VALU-bound.  Included once by llvq.hip after the generated
+// tables.
+
+#pragma once
+
+constexpr int kWideThreads = 256;
+
+struct WDesc {
+  int32_t mode, rows, cols, kb;
+  int32_t max_shell, shape_bits, gain_bits, field_bits;
+  uint64_t count_lo, count_hi;    // index count of shells 2..max_shell (128-bit)
+};
+
+struct U128 {
+  uint64_t lo, hi;
+};
+
+__device__ __forceinline__ bool u128_le(uint64_t alo, uint64_t ahi, uint64_t blo, uint64_t bhi) {
+  return ahi < bhi || (ahi == bhi && alo <= blo);
+}
+
+// field j of a little-endian bitstream of f-bit fields (f <= 128); reads only the dwords
+// that hold the field's bits
+__device__ __forceinline__ U128 read_field_wide(const uint8_t* __restrict__ packed, uint64_t j, int f) {
+  const uint64_t bit = j * (uint64_t)f;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(packed) + (bit >> 5);
+  const uint32_t sh = (uint32_t)(bit & 31u);
+  const uint32_t nw = (sh + (uint32_t)f + 31u) >> 5;     // 1..5 dwords
+  uint32_t d[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) d[k] = (uint32_t)k < nw ? w[k] : 0u;
+  const uint64_t a = (uint64_t)d[0] | ((uint64_t)d[1] << 32);
+  const uint64_t b = (uint64_t)d[2] | ((uint64_t)d[3] << 32);
+  const uint64_t c = (uint64_t)d[4];
+  U128 r;
+  r.lo = sh ? ((a >> sh) | (b << (64u - sh))) : a;
+  r.hi = sh ? ((b >> sh) | (c << (64u - sh))) : b;
+  if (f < 64) {
+    r.lo &= (1ull << f) - 1ull;
+    r.hi = 0;
+  } else if (f == 64) {
+    r.hi = 0;
+  } else if (f < 128) {
+    r.hi &= (1ull << (f - 64)) - 1ull;
+  }
+  return r;
+}
+
+// q = x / n for n in 1..24 dividing x: (x >> t) times the inverse of n's odd part mod 2^64
+__device__ __forceinline__ uint64_t exact_div_small(uint64_t x, uint32_t n) {
+  const uint32_t t = (uint32_t)__builtin_ctz(n);
+  return (x >> t) * dev_tables::kWideOddInverse[n >> (t + 1)];
+}
+
+// class holding global index I (< the index count of shells 2..M)
+__device__ __forceinline__ int wide_find_class(uint64_t lo, uint64_t hi, int M) {
+  // shell: the last m in 2..M with start(m) <= I
+  int a = 2, b = M;
+  while (a < b) {
+    const int mid = (a + b + 1) >> 1;
+    if (u128_le(dev_tables::kWideShellStart[mid][0], dev_tables::kWideShellStart[mid][1], lo, hi))
+      a = mid;
+    else
+      b = mid - 1;
+  }
+  // class: the last one of shell a with start <= I
+  int ca = dev_tables::kWideShellFirst[a], cb = dev_tables::kWideShellFirst[a + 1] - 1;
+  while (ca < cb) {
+    const int mid = (ca + cb + 1) >> 1;
+    const LlvqWideClass& c = dev_tables::kWideClass[mid];
+    if (u128_le(c.start_lo, c.start_hi, lo, hi))
+      ca = mid;
+    else
+      cb = mid - 1;
+  }
+  return ca;
+}
+
+// one multiset unranking in progress: rem = arrangements of what is left, n values left,
+// counts and values of the distinct values (ascending) one per byte
+struct Unranker {
+  uint64_t rem, rank, cnts, vals;
+  uint32_t n;
+};
+
+__device__ __forceinline__ uint64_t bytes8(const uint8_t* p) {
+  uint64_t v = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v |= (uint64_t)p[k] << (8 * k);
+  return v;
+}
+
+// Integer lattice point of global shape index I (valid: I < count).  Returns the shell.
+__device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M, int v[kDim]) {
+  const int k = wide_find_class(lo, hi, M);
+  const LlvqWideClass& cr = dev_tables::kWideClass[k];
+  const uint64_t J = lo - cr.start_lo;      // < 2^63: the high words cancel
+  const int w = cr.w;
+  const uint32_t A = cr.parity ? 4096u : dev_tables::kWideCodewords[w];
+  uint64_t r, ip;
+  if (A == 4096u) {
+    r = J & 4095u;
+    ip = J >> 12;
+  } else if (A == 1u) {
+    r = 0;
+    ip = J;
+  } else {
+    ip = J / A;
+    r = J - ip * A;
+  }
+  const uint32_t B = cr.B;
+  const uint32_t s = (uint32_t)(ip & ((1ull << B) - 1ull));
+  const uint64_t R = ip >> B;
+  const uint32_t c = dev_tables::kGolayTable[(cr.parity ? 0u : dev_tables::kWideGolayOffset[w]) + (uint32_t)r];
+
+  // support sequence (even classes, on the codeword) and complement sequence
+  Unranker S, T;
+  S.rank = cr.P_T ? R / cr.P_T : 0;
+  T.rank = R - S.rank * cr.P_T;
+  S.rem = cr.P_S;
+  T.rem = cr.P_T;
+  S.n = (uint32_t)w;
+  T.n = (uint32_t)(kDim - w);
+  S.cnts = bytes8(cr.sc);
+  S.vals = bytes8(cr.sv);
+  T.cnts = bytes8(cr.cc);
+  T.vals = bytes8(cr.cv);
+
+  const uint32_t sel = (cr.parity == 0 && w) ? c : 0u;
+  const int q = (cr.parity == 0 && w) ? (31 - __clz((int)c)) : -1;
+  const uint32_t wm1 = w ? (uint32_t)(w - 1) : 0u;
+  uint32_t bitsS = s;
+  uint32_t bitsT = (cr.parity == 0 && w) ? (s >> wm1) : s;
+  const uint32_t negq = (cr.parity == 0 && w) ? (((uint32_t)__popc(s & ((1u << wm1) - 1u)) & 1u) ^ cr.pi) : 0u;
+#pragma unroll
+  for (int p = 0; p < kDim; ++p) {
+    const bool inS = (sel >> p) & 1u;
+    Unranker U = inS ? S : T;
+    uint32_t kk = 0;
+    uint64_t sw = U.rem;
+    for (; kk < 7u; ++kk) {
+      const uint32_t ck = (uint32_t)(U.cnts >> (8 * kk)) & 0xffu;
+      if (ck == 0u) continue;
+      sw = exact_div_small(U.rem * ck, U.n);
+      if (U.rank < sw) break;
+      U.rank -= sw;
+    }
+    if (kk == 7u) sw = exact_div_small(U.rem * ((uint32_t)(U.cnts >> 56) & 0xffu), U.n);
+    const int a = (int)((U.vals >> (8 * kk)) & 0xffu);
+    U.cnts -= 1ull << (8 * kk);
+    U.rem = sw;
+    U.n -= 1u;
+    if (inS)
+      S = U;
+    else
+      T = U;
+    uint32_t neg;
+    if (cr.parity) {
+      neg = (uint32_t)(((a & 3) == 1) != (((c >> p) & 1u) != 0u));
+    } else if (a == 0) {
+      neg = 0u;
+    } else if (p == q) {
+      neg = negq;
+    } else if (inS) {
+      neg = bitsS & 1u;
+      bitsS >>= 1;
+    } else {
+      neg = bitsT & 1u;
+      bitsT >>= 1;
+    }
+    v[p] = neg ? -a : a;
+  }
+  return cr.m;
+}
+
+// shape index and gain of block j, and whether the index is in range
+__device__ __forceinline__ bool wide_block(const WDesc& d, const uint8_t* __restrict__ packed, uint64_t j,
+                                           uint64_t& lo, uint64_t& hi, uint32_t& g) {
+  const U128 fv = read_field_wide(packed, j, d.field_bits);
+  const int sb = d.shape_bits;
+  if (sb < 64) {
+    lo = fv.lo & ((1ull << sb) - 1ull);
+    hi = 0;
+    g = (uint32_t)((fv.lo >> sb) | (sb ? (fv.hi << (64 - sb)) : 0ull));
+  } else if (sb == 64) {
+    lo = fv.lo;
+    hi = 0;
+    g = (uint32_t)fv.hi;
+  } else {
+    lo = fv.lo;
+    hi = fv.hi & ((1ull << (sb - 64)) - 1ull);
+    g = (uint32_t)(fv.hi >> (sb - 64));
+  }
+  g &= (1u << d.gain_bits) - 1u;
+  return !u128_le(d.count_lo, d.count_hi, lo, hi);     // I < count
+}
+
+template <int OUT>
+__global__ __launch_bounds__(kWideThreads) void k_decode_wide(WDesc d, const uint8_t* __restrict__ packed,
+                                                              const __half* __restrict__ scales,
+                                                              void* __restrict__ out, int32_t* err) {
+  const uint64_t nblocks = (uint64_t)d.rows * (uint64_t)d.kb;
+  for (uint64_t j = (uint64_t)blockIdx.x * kWideThreads + threadIdx.x; j < nblocks;
+       j += (uint64_t)gridDim.x * kWideThreads) {
+    uint64_t lo, hi;
+    uint32_t g;
+    int v[kDim];
+    int m = 0;
+    if (wide_block(d, packed, j, lo, hi, g)) {
+      m = wide_decode_point(lo, hi, d.max_shell, v);
+    } else {
+#pragma unroll
+      for (int p = 0; p < kDim; ++p) v[p] = 0;
+      if (err) atomicAdd(err, 1);
+    }
+    const uint64_t r = j / (uint64_t)d.kb;
+    const int b = (int)(j - r * (uint64_t)d.kb);
+    if (OUT == LLVQ_OUT_POINTS_I8) {
+      uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<int8_t*>(out) + j * kDim);
+#pragma unroll
+      for (int q = 0; q < kDim / 4; ++q)
+        o[q] = (uint32_t)(uint8_t)v[4 * q] | ((uint32_t)(uint8_t)v[4 * q + 1] << 8) |
+               ((uint32_t)(uint8_t)v[4 * q + 2] << 16) | ((uint32_t)(uint8_t)v[4 * q + 3] << 24);
+    } else {
+      const float sc = d.mode == LLVQ_MODE_SHAPEGAIN
+                           ? (m ? __fmul_rn(__half2float(scales[g]), dev_tables::kWideInvNorm32[m]) : 0.0f)
+                           : __half2float(scales[r]);
+      uint16_t* o = static_cast<uint16_t*>(out) + r * (uint64_t)d.cols + (uint64_t)b * kDim;
+      const int lim = min(kDim, d.cols - b * kDim);
+#pragma unroll
+      for (int p = 0; p < kDim; ++p)
+        if (p < lim) o[p] = f32_to_bf16_rne(__fmul_rn((float)v[p], sc));
+    }
+  }
+}
+
+// y[bi][r] = sum over blocks of scale * (v . x[bi]); one wave per row, lanes over the
+// row's blocks, fixed-order wave reduction (repeatable bit for bit)
+template <bool XBF16>
+__global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8_t* __restrict__ packed,
+                                                            const __half* __restrict__ scales,
+                                                            const void* __restrict__ xv, int batch,
+                                                            float* __restrict__ y, int32_t* err) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int K = d.cols;
+  for (int r = blockIdx.x * (kWideThreads / 64) + wave; r < d.rows; r += gridDim.x * (kWideThreads / 64)) {
+    float acc[LLVQ_MAX_BATCH];
+#pragma unroll
+    for (int bi = 0; bi < LLVQ_MAX_BATCH; ++bi) acc[bi] = 0.0f;
+    const float rs = d.mode == LLVQ_MODE_SHAPEGAIN ? 0.0f : __half2float(scales[r]);
+    for (int b = lane; b < d.kb; b += 64) {
+      const uint64_t j = (uint64_t)r * (uint64_t)d.kb + (uint64_t)b;
+      uint64_t lo, hi;
+      uint32_t g;
+      int v[kDim];
+      int m = 0;
+      if (wide_block(d, packed, j, lo, hi, g)) {
+        m = wide_decode_point(lo, hi, d.max_shell, v);
+      } else {
+#pragma unroll
+        for (int p = 0; p < kDim; ++p) v[p] = 0;
+        if (err) atomicAdd(err, 1);
+      }
+      const float sc = d.mode == LLVQ_MODE_SHAPEGAIN
+                           ? (m ? __fmul_rn(__half2float(scales[g]), dev_tables::kWideInvNorm32[m]) : 0.0f)
+                           : rs;
+      const int k0 = b * kDim;
+      const int lim = min(kDim, K - k0);
+#pragma unroll
+      for (int bi = 0; bi < LLVQ_MAX_BATCH; ++bi) {
+        if (bi < batch) {
+          float t = 0.0f;
+#pragma unroll
+          for (int p = 0; p < kDim; ++p) {
+            if (p < lim) {
+              const size_t xi = (size_t)bi * (size_t)K + (size_t)(k0 + p);
+              const float xf = XBF16 ? bf16_to_f32(static_cast<const uint16_t*>(xv)[xi])
+                                     : static_cast<const float*>(xv)[xi];
+              t = fmaf((float)v[p], xf, t);
+            }
+          }
+          acc[bi] = fmaf(sc, t, acc[bi]);
+        }
+      }
+    }
+#pragma unroll
+    for (int bi = 0; bi < LLVQ_MAX_BATCH; ++bi) {
+      if (bi < batch) {
+        float a = acc[bi];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
+        if (lane == 0) y[(size_t)bi * (size_t)d.rows + (size_t)r] = a;
+      }
+    }
+  }
+}

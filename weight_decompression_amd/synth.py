@@ -191,6 +191,77 @@ def make_tensor(name, workload, tensor, rows, cols, index_count, *, mode=MODE_SH
                   scales, packed, xb, xf)
 
 
+# ---------------------------------------------------------------------------
+# fields wider than 64 bits (other rates): 128-bit values as (lo, hi) uint64 pairs
+
+def draw_indices_wide(workload, tensor, shape, index_count):
+    """Uniform shape indices over [0, index_count) for counts up to 2^128, as (lo, hi)
+    uint64 arrays: random words of index_count's bit length, redrawn while >= the count."""
+    n = int(np.prod(shape))
+    g = rng(workload, tensor, 0)
+    nbits = (index_count - 1).bit_length()
+    hb = max(nbits - 64, 0)
+    lo = np.zeros(n, dtype=np.uint64)
+    hi = np.zeros(n, dtype=np.uint64)
+    todo = np.arange(n)
+    c_lo, c_hi = np.uint64(index_count & (2**64 - 1)), np.uint64(index_count >> 64)
+    while todo.size:
+        if hb:
+            l = g.integers(0, 2**64 - 1, size=todo.size, dtype=np.uint64, endpoint=True)
+            h = g.integers(0, (1 << hb) - 1, size=todo.size, dtype=np.uint64, endpoint=True)
+        else:
+            l = g.integers(0, index_count, size=todo.size, dtype=np.uint64)
+            h = np.zeros(todo.size, dtype=np.uint64)
+        ok = (h < c_hi) | ((h == c_hi) & (l < c_lo))
+        lo[todo[ok]] = l[ok]
+        hi[todo[ok]] = h[ok]
+        todo = todo[~ok]
+    return lo.reshape(shape), hi.reshape(shape)
+
+
+def pack_fields_wide(lo, hi, width: int) -> np.ndarray:
+    """Write 128-bit values (lo | hi << 64) as consecutive little-endian `width`-bit fields."""
+    lo = np.ascontiguousarray(lo, dtype=np.uint64).ravel()
+    hi = np.ascontiguousarray(hi, dtype=np.uint64).ravel()
+    n = lo.size
+    out = np.zeros(packed_nbytes(n, width), dtype=np.uint8)
+    if n == 0:
+        return out
+    parts = [((lo[:, None] >> np.arange(min(width, 64), dtype=np.uint64)[None, :]) & np.uint64(1)).astype(np.uint8)]
+    if width > 64:
+        parts.append(((hi[:, None] >> np.arange(width - 64, dtype=np.uint64)[None, :]) & np.uint64(1))
+                     .astype(np.uint8))
+    packed = np.packbits(np.concatenate(parts, axis=1).ravel(), bitorder="little")
+    out[: packed.size] = packed
+    return out
+
+
+def make_wide_tensor(name, workload, tensor, rows, cols, index_count, *, mode=MODE_SHAPEGAIN, max_shell=42,
+                     shape_bits=68, gain_bits=4, batch=1, x_dtype="bf16") -> Tensor:
+    """Random packed tensor with fields of any width up to 128 bits; shape_idx is an object
+    array of Python integers."""
+    kb = blocks_per_row(cols)
+    s_lo, s_hi = draw_indices_wide(workload, tensor, (rows, kb), index_count)
+    if gain_bits:
+        gain_idx = rng(workload, tensor, 1).integers(0, 1 << gain_bits, size=(rows, kb), dtype=np.uint64)
+        scales = draw_gain_table(workload, tensor, 1 << gain_bits)
+    else:
+        gain_idx = np.zeros((rows, kb), dtype=np.uint64)
+        scales = rng(workload, tensor, 3).uniform(0.5, 2.0, size=rows).astype(np.float16)
+    f_lo, f_hi = s_lo.copy(), s_hi.copy()
+    if shape_bits >= 64:
+        f_hi |= gain_idx << np.uint64(shape_bits - 64)
+    else:
+        f_lo |= gain_idx << np.uint64(shape_bits)
+        if shape_bits + gain_bits > 64:
+            f_hi |= gain_idx >> np.uint64(64 - shape_bits)
+    packed = pack_fields_wide(f_lo, f_hi, shape_bits + gain_bits)
+    shape_idx = s_lo.astype(object) + (s_hi.astype(object) << 64)
+    xb, xf = draw_activations(workload, tensor, batch, cols, x_dtype) if batch else (None, None)
+    return Tensor(name, mode, rows, cols, max_shell, shape_bits, gain_bits, shape_idx, gain_idx,
+                  scales, packed, xb, xf)
+
+
 def fidelity_weights(workload, tensor, rows, cols, std=0.02) -> np.ndarray:
     """Dense N(0, std^2) fp32 weights for the fidelity rows."""
     return (rng(workload, tensor, 64).standard_normal((rows, cols)) * std).astype(np.float32)
