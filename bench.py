@@ -64,6 +64,14 @@ KERNEL_PROFILES = {
         "fetch_bytes_per_launch": 61929817,
         "write_bytes_per_launch": 1835008,
     },
+    "gemv_3bit_b1": {
+        "source_sha256": "0000000000000000000000000000000000000000000000000000000000000000",
+        "summary": "profiles/gemv_3bit_4096x11008_batch1_k_gemv_wide.md",
+        "unit_of_work": "24-weight block (k_gemv_wide)",
+        "valu_lane_ops_per_unit": 0,
+        "fetch_bytes_per_launch": 0,
+        "write_bytes_per_launch": 0,
+    },
     "decode_bf16": {
         "source_sha256": "96d7f605419a9bf22345749f6fa04e476a8acff4e894fb272c217644df56652d",
         "summary": "profiles/decode_bf16_7b_k_decode_many.md",
@@ -556,7 +564,7 @@ def run_gptq(a):
 
 DEFAULT_WORKLOAD = "gemv_4096x11008"
 WORKLOADS = ("gemv_4096x11008", "gemv_11008x4096", "gemv_4096x4096", "gemv_28672x8192", "decode_bf16_7b",
-             "roundtrip", "search", "fidelity", "gptq")
+             "roundtrip", "search", "fidelity", "gptq", "gemv_3bit_4096x11008")
 
 
 def main():
@@ -619,6 +627,11 @@ def main():
         t = synth.workload4(C10, a.batch)
         out = run_gemv(a, w, t, f"gemv_28672x8192_b{a.batch}",
                        f"llvq_gemv 2-bit shape-gain 28672x8192, batch {a.batch}")
+    elif w == "gemv_3bit_4096x11008":
+        # 3 bits per weight: 72-bit fields (68-bit shape index over shells 2..42 + 4-bit gain)
+        t = synth.make_wide_tensor("gemv3", 9, 0, 4096, 11008, wd.index_count(42), batch=a.batch)
+        out = run_gemv(a, w, t, f"gemv_3bit_b{a.batch}",
+                       f"llvq_gemv 3-bit shape-gain 4096x11008 (68+4-bit fields, shells 2..42), batch {a.batch}")
     elif w == "decode_bf16_7b":
         out = run_decode_7b(a)
     elif w == "search":

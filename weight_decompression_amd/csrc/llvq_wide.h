@@ -66,10 +66,24 @@ __device__ __forceinline__ U128 read_field_wide(const uint8_t* __restrict__ pack
   return r;
 }
 
-// q = x / n for n in 1..24 dividing x: (x >> t) times the inverse of n's odd part mod 2^64
-__device__ __forceinline__ uint64_t exact_div_small(uint64_t x, uint32_t n) {
-  const uint32_t t = (uint32_t)__builtin_ctz(n);
-  return (x >> t) * dev_tables::kWideOddInverse[n >> (t + 1)];
+// q, r = x div d, x mod d for x < 2^63, 0 < d < 2^62: an fp64 estimate, one fp64 refinement
+// of the signed remainder, then exact integer steps (the estimate is off by at most a few
+// units, so the steps run at most a few times; the remainder never overflows)
+__device__ __forceinline__ uint64_t div_u64(uint64_t x, uint64_t d, uint64_t& r) {
+  uint64_t q = (uint64_t)((double)x / (double)d);
+  int64_t rr = (int64_t)(x - q * d);
+  q += (uint64_t)(int64_t)floor((double)rr / (double)d);
+  rr = (int64_t)(x - q * d);
+  while (rr < 0) {
+    --q;
+    rr += (int64_t)d;
+  }
+  while (rr >= (int64_t)d) {
+    ++q;
+    rr -= (int64_t)d;
+  }
+  r = (uint64_t)rr;
+  return q;
 }
 
 // class holding global index I (< the index count of shells 2..M)
@@ -83,8 +97,16 @@ __device__ __forceinline__ int wide_find_class(uint64_t lo, uint64_t hi, int M) 
     else
       b = mid - 1;
   }
-  // class: the last one of shell a with start <= I
-  int ca = dev_tables::kWideShellFirst[a], cb = dev_tables::kWideShellFirst[a + 1] - 1;
+  // bucket of the offset inside the shell (the offset is below 2^68, the shift below 64)
+  const uint64_t slo = dev_tables::kWideShellStart[a][0], shi = dev_tables::kWideShellStart[a][1];
+  const uint64_t jlo = lo - slo;
+  const uint64_t jhi = hi - shi - (lo < slo ? 1u : 0u);
+  const int sh = dev_tables::kWideBucketShift[a];
+  const uint32_t bkt = (uint32_t)(sh ? ((jlo >> sh) | (jhi << (64 - sh))) : jlo);
+  const uint16_t* bk = dev_tables::kWideBucket + dev_tables::kWideBucketOff[a];
+  const int f0 = dev_tables::kWideShellFirst[a];
+  // class: the last one between the bucket's two bounds with start <= I
+  int ca = f0 + bk[bkt], cb = f0 + bk[bkt + 1];
   while (ca < cb) {
     const int mid = (ca + cb + 1) >> 1;
     const LlvqWideClass& c = dev_tables::kWideClass[mid];
@@ -111,7 +133,8 @@ __device__ __forceinline__ uint64_t bytes8(const uint8_t* p) {
 }
 
 // Integer lattice point of global shape index I (valid: I < count).  Returns the shell.
-__device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M, int v[kDim]) {
+// inv: the inverses mod 2^64 of 1, 3, ..., 23 (staged in LDS by the kernel).
+__device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M, const uint64_t* inv, int v[kDim]) {
   const int k = wide_find_class(lo, hi, M);
   const LlvqWideClass& cr = dev_tables::kWideClass[k];
   const uint64_t J = lo - cr.start_lo;      // < 2^63: the high words cancel
@@ -125,8 +148,7 @@ __device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M
     r = 0;
     ip = J;
   } else {
-    ip = J / A;
-    r = J - ip * A;
+    ip = div_u64(J, A, r);
   }
   const uint32_t B = cr.B;
   const uint32_t s = (uint32_t)(ip & ((1ull << B) - 1ull));
@@ -135,8 +157,12 @@ __device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M
 
   // support sequence (even classes, on the codeword) and complement sequence
   Unranker S, T;
-  S.rank = cr.P_T ? R / cr.P_T : 0;
-  T.rank = R - S.rank * cr.P_T;
+  if (cr.P_S == 1) {
+    S.rank = 0;
+    T.rank = R;
+  } else {
+    S.rank = div_u64(R, cr.P_T, T.rank);
+  }
   S.rem = cr.P_S;
   T.rem = cr.P_T;
   S.n = (uint32_t)w;
@@ -156,19 +182,24 @@ __device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M
   for (int p = 0; p < kDim; ++p) {
     const bool inS = (sel >> p) & 1u;
     Unranker U = inS ? S : T;
-    uint32_t kk = 0;
-    uint64_t sw = U.rem;
-    for (; kk < 7u; ++kk) {
-      const uint32_t ck = (uint32_t)(U.cnts >> (8 * kk)) & 0xffu;
-      if (ck == 0u) continue;
-      sw = exact_div_small(U.rem * ck, U.n);
-      if (U.rank < sw) break;
-      U.rank -= sw;
+    // the arrangements starting with value slot k number rem * c_k / n; the slot holding
+    // rank is the first k with rank * n < rem * (c_0 + ... + c_k), compared without dividing
+    const uint64_t t_n = U.rank * U.n;
+    uint32_t kk = 0, ck = (uint32_t)U.cnts & 0xffu;
+    uint64_t below = 0, upto = U.rem * ck;
+    while (kk < 7u && t_n >= upto) {
+      ++kk;
+      ck = (uint32_t)(U.cnts >> (8 * kk)) & 0xffu;
+      below = upto;
+      upto += U.rem * ck;
     }
-    if (kk == 7u) sw = exact_div_small(U.rem * ((uint32_t)(U.cnts >> 56) & 0xffu), U.n);
+    // new rank and count of arrangements: exact quotients by n
+    const uint32_t tz = (uint32_t)__builtin_ctz(U.n);
+    const uint64_t iv = inv[U.n >> (tz + 1)];
+    U.rank = ((t_n - below) >> tz) * iv;
+    U.rem = ((U.rem * ck) >> tz) * iv;
     const int a = (int)((U.vals >> (8 * kk)) & 0xffu);
     U.cnts -= 1ull << (8 * kk);
-    U.rem = sw;
     U.n -= 1u;
     if (inS)
       S = U;
@@ -215,10 +246,18 @@ __device__ __forceinline__ bool wide_block(const WDesc& d, const uint8_t* __rest
   return !u128_le(d.count_lo, d.count_hi, lo, hi);     // I < count
 }
 
+// the inverses of the odd numbers below 24 in LDS (read once per unranked position)
+__device__ __forceinline__ void stage_inverses(uint64_t* inv) {
+  if (threadIdx.x < 12) inv[threadIdx.x] = dev_tables::kWideOddInverse[threadIdx.x];
+  __syncthreads();
+}
+
 template <int OUT>
 __global__ __launch_bounds__(kWideThreads) void k_decode_wide(WDesc d, const uint8_t* __restrict__ packed,
                                                               const __half* __restrict__ scales,
                                                               void* __restrict__ out, int32_t* err) {
+  __shared__ uint64_t inv[12];
+  stage_inverses(inv);
   const uint64_t nblocks = (uint64_t)d.rows * (uint64_t)d.kb;
   for (uint64_t j = (uint64_t)blockIdx.x * kWideThreads + threadIdx.x; j < nblocks;
        j += (uint64_t)gridDim.x * kWideThreads) {
@@ -227,7 +266,7 @@ __global__ __launch_bounds__(kWideThreads) void k_decode_wide(WDesc d, const uin
     int v[kDim];
     int m = 0;
     if (wide_block(d, packed, j, lo, hi, g)) {
-      m = wide_decode_point(lo, hi, d.max_shell, v);
+      m = wide_decode_point(lo, hi, d.max_shell, inv, v);
     } else {
 #pragma unroll
       for (int p = 0; p < kDim; ++p) v[p] = 0;
@@ -261,6 +300,8 @@ __global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8
                                                             const __half* __restrict__ scales,
                                                             const void* __restrict__ xv, int batch,
                                                             float* __restrict__ y, int32_t* err) {
+  __shared__ uint64_t inv[12];
+  stage_inverses(inv);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int K = d.cols;
@@ -276,7 +317,7 @@ __global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8
       int v[kDim];
       int m = 0;
       if (wide_block(d, packed, j, lo, hi, g)) {
-        m = wide_decode_point(lo, hi, d.max_shell, v);
+        m = wide_decode_point(lo, hi, d.max_shell, inv, v);
       } else {
 #pragma unroll
         for (int p = 0; p < kDim; ++p) v[p] = 0;
