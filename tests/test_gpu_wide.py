@@ -193,3 +193,19 @@ def test_decode_many_with_wide_tensors_equals_single_calls():
         wd.decode(d, p, s, wd.OUT_BF16, one)
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), one.view(torch.int16))
+
+
+@pytest.mark.parametrize("xd", ["bf16", "f32"])
+def test_gemv_unaligned_activations_equal_aligned(xd):
+    # 16-byte activation loads (aligned x, aligned rows) and element loads give the same sums
+    t = synth.make_wide_tensor("wu", 90, 0, 40, 480, leech.index_count(42), batch=3, x_dtype=xd)
+    desc, packed, scales, x = dev(t)
+    y0 = torch.empty((3, 40), dtype=torch.float32, device="cuda")
+    wd.gemv(desc, packed, scales, x, y0)
+    buf = torch.zeros(x.numel() + 8, dtype=x.dtype, device="cuda")
+    xu = buf[1:1 + x.numel()].view(3, 480)
+    xu.copy_(x)
+    y1 = torch.empty_like(y0)
+    wd.gemv(desc, packed, scales, xu, y1)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)

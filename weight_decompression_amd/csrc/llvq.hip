@@ -713,13 +713,15 @@ int gemv_wide(const llvq_desc* d, const void* packed, const void* scales, const 
   if (batch < 1 || batch > LLVQ_MAX_BATCH) return LLVQ_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const unsigned grid = grid_for((uint64_t)w.rows, kWideThreads / 64);
+  const int xbytes = x_dtype == LLVQ_X_BF16 ? 2 : 4;
+  const bool xvec = aligned(x, 16) && ((uint64_t)w.cols * (uint64_t)xbytes) % 16u == 0;
   if (x_dtype == LLVQ_X_BF16)
     hipLaunchKernelGGL((k_gemv_wide<true>), dim3(grid), dim3(kWideThreads), 0, s, w,
-                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, batch, y,
+                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, batch, xvec, y,
                        err_count);
   else
     hipLaunchKernelGGL((k_gemv_wide<false>), dim3(grid), dim3(kWideThreads), 0, s, w,
-                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, batch, y,
+                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, batch, xvec, y,
                        err_count);
   return launch_status();
 }

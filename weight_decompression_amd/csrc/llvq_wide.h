@@ -294,11 +294,12 @@ __global__ __launch_bounds__(kWideThreads) void k_decode_wide(WDesc d, const uin
 }
 
 // y[bi][r] = sum over blocks of scale * (v . x[bi]); one wave per row, lanes over the
-// row's blocks, fixed-order wave reduction (repeatable bit for bit)
+// row's blocks, fixed-order wave reduction (repeatable bit for bit).  xvec: x is 16-byte
+// aligned with 16-byte aligned rows, so a full block's activations load as 16-byte words.
 template <bool XBF16>
 __global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8_t* __restrict__ packed,
                                                             const __half* __restrict__ scales,
-                                                            const void* __restrict__ xv, int batch,
+                                                            const void* __restrict__ xv, int batch, bool xvec,
                                                             float* __restrict__ y, int32_t* err) {
   __shared__ uint64_t inv[12];
   stage_inverses(inv);
@@ -332,13 +333,40 @@ __global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8
       for (int bi = 0; bi < LLVQ_MAX_BATCH; ++bi) {
         if (bi < batch) {
           float t = 0.0f;
+          const size_t x0 = (size_t)bi * (size_t)K + (size_t)k0;
+          if (xvec && lim == kDim) {
+            // the block's 24 activations as 16-byte loads (3 for bf16, 6 for fp32)
+            if (XBF16) {
+              const uint4* xp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + x0);
 #pragma unroll
-          for (int p = 0; p < kDim; ++p) {
-            if (p < lim) {
-              const size_t xi = (size_t)bi * (size_t)K + (size_t)(k0 + p);
-              const float xf = XBF16 ? bf16_to_f32(static_cast<const uint16_t*>(xv)[xi])
-                                     : static_cast<const float*>(xv)[xi];
-              t = fmaf((float)v[p], xf, t);
+              for (int q = 0; q < 3; ++q) {
+                const uint4 u = xp[q];
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  t = fmaf((float)v[8 * q + 2 * e], __uint_as_float(w4[e] << 16), t);
+                  t = fmaf((float)v[8 * q + 2 * e + 1], __uint_as_float(w4[e] & 0xffff0000u), t);
+                }
+              }
+            } else {
+              const float4* xp = reinterpret_cast<const float4*>(static_cast<const float*>(xv) + x0);
+#pragma unroll
+              for (int q = 0; q < 6; ++q) {
+                const float4 u = xp[q];
+                t = fmaf((float)v[4 * q], u.x, t);
+                t = fmaf((float)v[4 * q + 1], u.y, t);
+                t = fmaf((float)v[4 * q + 2], u.z, t);
+                t = fmaf((float)v[4 * q + 3], u.w, t);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int p = 0; p < kDim; ++p) {
+              if (p < lim) {
+                const float xf = XBF16 ? bf16_to_f32(static_cast<const uint16_t*>(xv)[x0 + p])
+                                       : static_cast<const float*>(xv)[x0 + p];
+                t = fmaf((float)v[p], xf, t);
+              }
             }
           }
           acc[bi] = fmaf(sc, t, acc[bi]);
