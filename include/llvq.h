@@ -85,8 +85,12 @@ typedef struct {
  * general decoder: M up to 42 and fields up to 128 bits, e.g. 46 + 2 or 47 + 1 bits at
  * M = 11 or 12, or 3 bits per weight as 68 + 4 bits at M = 42, where global indices pass
  * 2^64.  Such descriptors are taken by llvq_packed_bytes, llvq_decode, llvq_decode_many
- * (one launch per tensor) and llvq_gemv; llvq_quantize, llvq_quantize_workspace_bytes and
- * llvq_pack_fields return LLVQ_EUNSUPPORTED for them. */
+ * (one launch per tensor) and llvq_gemv.  The quantiser (llvq_search, llvq_quantize,
+ * llvq_quantize_workspace_bytes) covers M <= 13 with fields of at most 64 bits (2 bits
+ * per weight with 46..48 shape bits), the rank (llvq_encode_ref) M <= 33 (indices below
+ * 2^64); past those, and for llvq_pack_fields past M = 10 or 64-bit fields, the calls
+ * return LLVQ_EUNSUPPORTED (llvq_search and llvq_encode_ref, which take M directly,
+ * LLVQ_EINVAL). */
 
 /* Number of valid shape indices for shells 2..max_shell (|Lambda24(M)|).  Host only.
  * Writes *out and returns LLVQ_OK, or LLVQ_EINVAL if max_shell is outside [2, 10] or out
@@ -155,7 +159,7 @@ int llvq_gemv(const llvq_desc* d, const void* packed, const void* scales, const 
  * and from bitstrings without materialising the codebook).
  *   points    : int8 [n][24] integer lattice coordinates (any alignment).
  *   n         : number of points, >= 0 (0 is a no-op).
- *   max_shell : M in [2, 10].
+ *   max_shell : M in [2, 33] (shells past 10 take a general rank kernel).
  *   indices   : uint64 [n] output shape indices (8-byte aligned); UINT64_MAX for a point
  *               that is not in the lattice or not in shells 2..M (counted in err_count).
  * Returns LLVQ_OK, LLVQ_EINVAL or LLVQ_EHIP. */
@@ -172,9 +176,10 @@ int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell, uint64_t
  *               lattice's integer units (sqrt(8) x standard coordinates, shell m has
  *               squared norm 16 m).
  *   n         : number of vectors, >= 0 (0 is a no-op).
- *   max_shell : M in [2, 10].
+ *   max_shell : M in [2, 13].
  *   objective : LLVQ_SEARCH_ANGULAR maximises <x, v> / |v| (scale-free: collinear points
- *               of different shells tie); LLVQ_SEARCH_EUCLID minimises |x - v|^2.
+ *               of different shells tie, and the point of the lower shell is returned:
+ *               u rather than 2u); LLVQ_SEARCH_EUCLID minimises |x - v|^2.
  *   points    : int8 [n][24] output, the chosen points (any alignment; also the input of
  *               the rank step that follows on the same stream).
  *   indices   : uint64 [n] output, the points' shape indices (8-byte aligned).

@@ -22,13 +22,13 @@ pattern and permutation follow in closed form:
 
 Both objectives reduce to max <x, v> inside one class because the norm is constant on
 a class.  Exact ties between candidates are broken towards the smaller global index.
-The angular objective does not see the scale of v, so a shell-8 point 2u whose half u
-is a lattice point ties exactly with u (shell 2); the fp64 objectives of the two are
+The angular objective does not see the scale of v, so a point k u (k >= 2) whose
+fraction u is a lattice point ties exactly with u; the fp64 objectives of the two are
 computed along different paths and need not come out equal, so that tie is resolved
-explicitly: a shell-8 winner of that form is replaced by u, whose index is smaller
-(indices ascend with the shell).  Within shells 2..10 this is the only collinear pair
-(k v needs shell k^2 m <= 10).  The tests pin this against literal enumeration of whole
-shells.
+explicitly: the winner is replaced by the smallest lattice point on its ray, whose index
+is smallest (indices ascend with the shell).  k u lies in shell k^2 m, so up to shell 13
+this concerns 2u in shell 8 (u in shell 2) and in shell 12 (u in shell 3).  The tests
+pin this against literal enumeration of whole shells.
 """
 
 import numpy as np
@@ -174,19 +174,29 @@ def search(x, M, mode="angular"):
             candidates.append((rank(v, M), v))
     I, v = min(candidates, key=lambda t: t[0])
     if mode == "angular":
-        u = primitive_half(v)
+        u = smallest_on_ray(v)
         if u is not None:
             return rank(u, M), u
     return I, v
 
 
-def primitive_half(v):
-    """u = v / 2 when v is in shell 8 and u is a lattice point (then u is in shell 2 and
-    ties with v under the angular objective), else None."""
-    if sum(int(a) * int(a) for a in v) != 16 * 8 or any(int(a) % 2 for a in v):
-        return None
-    u = [int(a) // 2 for a in v]
-    return u if in_leech(u) else None
+def smallest_on_ray(v):
+    """The lattice point of smallest norm on the ray through v other than v itself: v / k
+    for the largest k >= 2 with v / k in the lattice (norm >= 32, so in a shell >= 2), or
+    None when there is none.  Such a point ties with v under the angular objective."""
+    import math
+    v = [int(a) for a in v]
+    g = 0
+    for a in v:
+        g = math.gcd(g, abs(a))
+    best = None
+    for k in range(2, g + 1):
+        if g % k:
+            continue
+        u = [a // k for a in v]
+        if sum(a * a for a in u) >= 32 and in_leech(u):
+            best = u
+    return best
 
 
 def nearest_gain(norm, gains):

@@ -97,7 +97,7 @@ def test_encode_validation_and_empty(lib):
 def test_search_validation_and_empty(lib):
     p = ctypes.c_void_p(0x10000)
     assert lib.llvq_search(p, 10, 1, 0, p, p, None, None) == -1                           # max_shell < 2
-    assert lib.llvq_search(p, 10, 11, 0, p, p, None, None) == -1                          # max_shell > 10
+    assert lib.llvq_search(p, 10, 14, 0, p, p, None, None) == -1                          # max_shell > 13
     assert lib.llvq_search(p, 10, 10, 2, p, p, None, None) == -1                          # bad objective
     assert lib.llvq_search(p, -1, 10, 0, p, p, None, None) == -1                          # negative n
     assert lib.llvq_search(None, 10, 10, 0, p, p, None, None) == -1                       # null x
@@ -113,9 +113,13 @@ def test_quantize_validation(lib):
     assert lib.llvq_quantize_workspace_bytes(ctypes.byref(d)) == 4 * 5 * 32
     d3 = wd.make_desc(wd.MODE_EUCLID, 3, 25, 3, 25, 0)
     assert lib.llvq_quantize_workspace_bytes(ctypes.byref(d3)) == (3 * 2 * 24 + 7) // 8 * 8 + 3 * 2 * 8
-    bad = wd.make_desc(wd.MODE_SHAPEGAIN, 4, 100, 11, 44, 4)
+    bad = wd.make_desc(wd.MODE_SHAPEGAIN, 4, 100, 11, 44, 4)         # C_11 > 2^44
     assert lib.llvq_quantize_workspace_bytes(ctypes.byref(bad)) == -1
     assert lib.llvq_quantize(ctypes.byref(bad), p, p, p, p, None, None) == -1
+    d11 = wd.make_desc(wd.MODE_SHAPEGAIN, 4, 100, 11, 46, 2)         # shells past 10: up to 13
+    assert lib.llvq_quantize_workspace_bytes(ctypes.byref(d11)) == 4 * 5 * 32
+    d14 = wd.make_desc(wd.MODE_SHAPEGAIN, 4, 100, 14, 50, 4)
+    assert lib.llvq_quantize_workspace_bytes(ctypes.byref(d14)) == -2
     assert lib.llvq_quantize(ctypes.byref(d), None, p, p, p, None, None) == -1                # null w
     assert lib.llvq_quantize(ctypes.byref(d), p, None, p, p, None, None) == -1                # null scales
     assert lib.llvq_quantize(ctypes.byref(d), p, p, ctypes.c_void_p(0x10008), p, None, None) == -1   # packed alignment

@@ -12,13 +12,14 @@ under tests/golden/), and perturbed lattice points.
 """
 
 import os
+import random
 
 import numpy as np
 import pytest
 import torch
 
 import weight_decompression_amd as wd
-from oracle import bijection, leech, search
+from oracle import bijection, classes, leech, search
 from weight_decompression_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -239,3 +240,92 @@ def test_gptq_matches_oracle(variant):
     fields = want_idx | (want_g.astype(np.uint64) << np.uint64(44))
     assert np.array_equal(packed.cpu().numpy(), synth.pack_fields(fields.reshape(-1), 48))
     say(f"gptq {variant}: 120 blocks equal to the oracle")
+
+
+# ---------------------------------------------------------------------------
+# shells past 10: the search up to shell 13 (2 bits per weight with 46..48 shape bits) and
+# the general rank
+
+@pytest.mark.parametrize("mode,M,scale", [("angular", 11, 1.0), ("angular", 12, 1.0), ("angular", 13, 0.7),
+                                          ("euclid", 12, 2.4), ("euclid", 13, 2.5)])
+def test_search_past_shell_10_matches_oracle(mode, M, scale):
+    rng = np.random.default_rng(200 + M + (mode == "euclid"))
+    x = (rng.standard_normal((64, 24)) * scale).astype(np.float32)
+    want = [search.search(x[i].astype(np.float64), M, mode)[0] for i in range(len(x))]
+    check_against(x, want, M, mode, f"{mode} M={M}")
+
+
+def test_search_shell12_collinear_tie_goes_to_shell3():
+    # u (shell 3) and 2u (shell 12) tie under the angular objective; u has the smaller index
+    rng = np.random.default_rng(31)
+    lo, hi = leech.index_count(2), leech.index_count(3)
+    I = [int(i) for i in rng.integers(lo, hi, size=8)]
+    u = np.array([bijection.unrank(i, 3) for i in I], dtype=np.float32)
+    x = np.concatenate([u, 2.0 * u])
+    for M in (12, 13):
+        pts, idx, err = gpu_search(x, M, "angular")
+        assert err == 0
+        assert list(idx) == I + I, M
+
+
+@pytest.mark.parametrize("M", [11, 13, 24, 33])
+def test_rank_past_shell_10_matches_oracle(M):
+    rng = random.Random(M)
+    C = leech.index_count(M)
+    T = classes.class_table(M)
+    I = [rng.randrange(C) for _ in range(400)]
+    for k in rng.sample(range(len(T)), min(len(T), 300)):
+        I += [T[k].start, T[k].end - 1]
+    pts = np.array([bijection.unrank(i, M) for i in I], dtype=np.int8)
+    bad = pts[:6].copy()
+    bad[0, 0] += 2          # one coordinate's residue mod 4 changes: not a codeword pattern
+    bad[1, :] = 0           # the zero vector
+    bad[2, 0] += 1          # mixed parity
+    bad[3, :] = 2 * pts[3]  # shell 4m: beyond M, or a member the oracle ranks
+    bad[4, [0, 5]] = bad[4, [5, 0]]   # two coordinates swapped: usually not a member
+    bad[5, 7] = -bad[5, 7] if bad[5, 7] else bad[5, 7] + 4
+    allp = np.concatenate([pts, bad])
+    d = torch.from_numpy(allp.copy()).cuda()
+    out = torch.empty(len(allp), dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.encode_ref(d, M, out, err)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint64)
+    assert [int(g) for g in got[:len(I)]] == I
+    nbad = 0
+    for j, p in enumerate(bad):
+        try:
+            want = bijection.rank([int(a) for a in p], M)
+        except ValueError:
+            want = None
+        g = int(got[len(I) + j])
+        if want is None:
+            assert g == 2**64 - 1, j
+            nbad += 1
+        else:
+            assert g == want, j
+    assert int(err.item()) == nbad and nbad >= 3
+    say(f"general rank M={M}: {len(I)} points, {nbad} rejected")
+
+
+@pytest.mark.parametrize("M,sb,gb", [(11, 46, 2), (12, 47, 1)])
+def test_quantize_past_shell_10_stream_matches_oracle(M, sb, gb):
+    # 2 bits per weight with the pages' split: 46 + 2 (shell 11) and 47 + 1 (shell 12)
+    rng = np.random.default_rng(40 + M)
+    w = rng.standard_normal((6, 100)).astype(np.float32)
+    gains = synth.chi_gain_table(1 << gb)
+    desc = wd.make_desc(wd.MODE_SHAPEGAIN, 6, 100, M, sb, gb)
+    got, err = gpu_quantize(desc, w, gains)
+    assert err == 0
+    want = synth.pack_fields(oracle_fields(w, gains, M, wd.MODE_SHAPEGAIN, gb, sb), sb + gb)
+    assert got.size == want.size and np.array_equal(got, want)
+    # the stream decodes (general decoder) to the search points
+    pk = torch.from_numpy(got).cuda()
+    out = torch.empty((6, 5 * 24), dtype=torch.int8, device="cuda")
+    wd.decode(desc, pk, torch.from_numpy(gains).cuda(), wd.OUT_POINTS_I8, out)
+    torch.cuda.synchronize()
+    fields = oracle_fields(w, gains, M, wd.MODE_SHAPEGAIN, gb, sb).reshape(6, 5)
+    for r in (0, 5):
+        for b in range(5):
+            I = int(fields[r, b]) & ((1 << sb) - 1)
+            assert list(out[r, 24 * b:24 * b + 24].cpu().numpy().astype(int)) == bijection.unrank(I, M)

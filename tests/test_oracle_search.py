@@ -108,10 +108,10 @@ def test_angular_collinear_tie_goes_to_the_shell2_point(shell2_points):
         for x in (np.array(u, dtype=np.float64), 2.0 * np.array(u, dtype=np.float64)):
             J, v = search.search(x, 10, "angular")
             assert (J, v) == (int(I), u)
-        assert search.primitive_half([2 * a for a in u]) == u
+        assert search.smallest_on_ray([2 * a for a in u]) == u
 
 
-def test_primitive_half_only_for_halvable_shell8_points(shell2_points):
+def test_smallest_on_ray_only_for_halvable_shell8_points(shell2_points):
     # a shell-8 point with even coordinates halves to a lattice point exactly when its half
     # is one of the enumerated shell-2 points
     s2 = {tuple(int(a) for a in p) for p in shell2_points}
@@ -120,7 +120,7 @@ def test_primitive_half_only_for_halvable_shell8_points(shell2_points):
     seen_even = 0
     for I in rng.integers(lo, hi, size=4000):
         v = bijection.unrank(int(I), 8)
-        h = search.primitive_half(v)
+        h = search.smallest_on_ray(v)
         if all(a % 2 == 0 for a in v):
             seen_even += 1
             half = tuple(a // 2 for a in v)
@@ -130,4 +130,37 @@ def test_primitive_half_only_for_halvable_shell8_points(shell2_points):
         else:
             assert h is None
     assert seen_even > 0
-    assert search.primitive_half(bijection.unrank(5, 10)) is None      # a shell-2 point
+    assert search.smallest_on_ray(bijection.unrank(5, 10)) is None      # a shell-2 point
+
+
+def test_angular_collinear_tie_shell12_goes_to_the_shell3_point():
+    # up to shell 13 the other collinear pair: u in shell 3 and 2u in shell 12 tie exactly
+    # under the angular objective; x = u and x = 2u come back as u at M = 12 and 13
+    rng = np.random.default_rng(12)
+    lo, hi = leech.index_count(2), leech.index_count(3)
+    for I in rng.integers(lo, hi, size=4):
+        u = bijection.unrank(int(I), 3)
+        assert search.smallest_on_ray([2 * a for a in u]) == u
+        assert search.smallest_on_ray(u) is None
+        for M in (12, 13):
+            for x in (np.array(u, dtype=np.float64), 2.0 * np.array(u, dtype=np.float64)):
+                J, v = search.search(x, M, "angular")
+                assert (J, v) == (int(I), u)
+
+
+def test_smallest_on_ray_rejects_non_lattice_fractions():
+    # 2w for a shell-2 point w is in shell 8; 4w (shell 32) halves twice, to w
+    w = bijection.unrank(777, 2)
+    assert search.smallest_on_ray([4 * a for a in w]) == w
+    # a shell-12 point with all coordinates even whose half is not a lattice point
+    rng = np.random.default_rng(13)
+    lo, hi = leech.index_count(11), leech.index_count(12)
+    found = 0
+    for I in rng.integers(lo, hi, size=3000):
+        v = bijection.unrank(int(I), 12)
+        if all(a % 2 == 0 for a in v):
+            h = search.smallest_on_ray(v)
+            half = [a // 2 for a in v]
+            assert (h == half) == leech.in_leech(half)
+            found += 1
+    assert found > 0

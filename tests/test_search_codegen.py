@@ -11,7 +11,7 @@ coordinates.  These tests read that generated file and check it against the orac
   the oracle's objective of the best point of that class for that codeword, for
   codewords of every weight, both objectives;
 * the expressions appear shell by shell, so a search limited to shells <= M sees exactly
-  the classes of those shells.
+  the classes of those shells (shells 2..13).
 """
 
 import re
@@ -21,6 +21,8 @@ import pytest
 
 from oracle import classes, golay, search
 from weight_decompression_amd import build_lib
+
+M_SEARCH = 13          # the search covers shells 2..13 (383 classes)
 
 FN_RE = re.compile(r"__device__ __forceinline__ (?:float|int) (llvq_\w+)\(.*?\) \{\n(.*?)\n\}\n", re.S)
 
@@ -69,8 +71,9 @@ def _class_records(inc):
 
 def test_class_records_match_oracle(inc):
     recs = _class_records(inc)
-    ours = classes.class_table(10)
-    assert len(recs) == len(ours) == 168
+    ours = classes.class_table(M_SEARCH)
+    assert len(recs) == len(ours) == 383
+    assert f"#define LLVQ_SEARCH_MAX_SHELL {M_SEARCH}" in inc
     for (vals, (m, parity, w, pi)), c in zip(recs, ours):
         assert (m, parity, w, pi) == (c.m, c.parity, c.w, c.pi)
         if c.parity:
@@ -117,7 +120,7 @@ def _objective(x, v, m, euclid):
 @pytest.mark.parametrize("euclid", [False, True])
 def test_class_objectives_match_oracle_points(inc, euclid):
     fns = _argmax_bodies(inc)
-    cls = classes.class_table(10)
+    cls = classes.class_table(M_SEARCH)
     T = golay.table()
     rng = np.random.default_rng(7 + euclid)
     suffix = "_euclid" if euclid else "_angular"
@@ -160,12 +163,12 @@ def test_class_objectives_match_oracle_points(inc, euclid):
                     want = _objective(x, v, cls[k].m, euclid)
                     assert abs(got - want) <= 1e-6 * (1.0 + abs(want)), (k, w, c, got, want)
                     seen.add(k)
-    assert seen == set(range(168))
+    assert seen == set(range(383))
 
 
 def test_shell_breaks_follow_class_shells(inc):
     # each class is preceded by the limit check of its own shell (shell 2 needs none)
-    cls = classes.class_table(10)
+    cls = classes.class_table(M_SEARCH)
     for name, items in _argmax_bodies(inc).items():
         shell = 2
         for k, item in items:

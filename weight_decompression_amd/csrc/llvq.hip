@@ -898,7 +898,7 @@ LLVQ_API int llvq_gemv(const llvq_desc* d, const void* packed, const void* scale
 
 LLVQ_API int llvq_search(const float* x, int64_t n, int32_t max_shell, int32_t objective, int8_t* points,
                          uint64_t* indices, int32_t* err_count, void* stream) {
-  if (max_shell < 2 || max_shell > LLVQ_MAX_SHELL || n < 0) return LLVQ_EINVAL;
+  if (max_shell < 2 || max_shell > LLVQ_SEARCH_MAX_SHELL || n < 0) return LLVQ_EINVAL;
   if (objective != LLVQ_SEARCH_ANGULAR && objective != LLVQ_SEARCH_EUCLID) return LLVQ_EINVAL;
   if (n == 0) return LLVQ_OK;
   if (!x || !points || !indices || !aligned(x, 4) || !aligned(indices, 8)) return LLVQ_EINVAL;
@@ -918,11 +918,37 @@ LLVQ_API int llvq_search(const float* x, int64_t n, int32_t max_shell, int32_t o
 
 namespace {
 uint64_t quantize_points_bytes(const KDesc& k) { return ((uint64_t)k.rows * (uint64_t)k.kb * 24u + 7u) / 8u * 8u; }
+
+// descriptor of the quantiser: shells 2..LLVQ_SEARCH_MAX_SHELL, fields of at most 64 bits
+// (past shell 10 only the fields the search, rank and pack steps read are set)
+int make_kdesc_quant(const llvq_desc* d, KDesc* k) {
+  if (d && d->max_shell > LLVQ_MAX_SHELL && d->max_shell <= LLVQ_SEARCH_MAX_SHELL && d->shape_bits <= 60 &&
+      d->shape_bits + d->gain_bits <= 64) {
+    WDesc w;
+    const int st = make_wdesc(d, &w);
+    if (st != LLVQ_OK) return st;
+    *k = KDesc{};
+    k->mode = w.mode;
+    k->rows = w.rows;
+    k->cols = w.cols;
+    k->kb = w.kb;
+    k->max_shell = w.max_shell;
+    k->shape_bits = w.shape_bits;
+    k->gain_bits = w.gain_bits;
+    k->field_bits = w.field_bits;
+    k->index_count = w.count_lo;
+    k->shape_mask = (1ull << w.shape_bits) - 1ull;
+    k->shape_mask_lo = (uint32_t)k->shape_mask;
+    k->shape_mask_hi = (uint32_t)(k->shape_mask >> 32);
+    return LLVQ_OK;
+  }
+  return make_kdesc_narrow(d, k);
+}
 }  // namespace
 
 LLVQ_API int64_t llvq_quantize_workspace_bytes(const llvq_desc* d) {
   KDesc k;
-  const int st = make_kdesc_narrow(d, &k);
+  const int st = make_kdesc_quant(d, &k);
   if (st != LLVQ_OK) return st;
   return (int64_t)(quantize_points_bytes(k) + (uint64_t)k.rows * (uint64_t)k.kb * 8u);
 }
@@ -930,7 +956,7 @@ LLVQ_API int64_t llvq_quantize_workspace_bytes(const llvq_desc* d) {
 LLVQ_API int llvq_quantize(const llvq_desc* d, const float* w, const void* scales, void* packed, void* workspace,
                            int32_t* err_count, void* stream) {
   KDesc k;
-  const int st = make_kdesc_narrow(d, &k);
+  const int st = make_kdesc_quant(d, &k);
   if (st != LLVQ_OK) return st;
   if (!w || !scales || !packed || !workspace) return LLVQ_EINVAL;
   if (!aligned(w, 4) || !aligned(scales, 2) || !aligned(packed, 16) || !aligned(workspace, 8)) return LLVQ_EINVAL;
@@ -971,11 +997,17 @@ LLVQ_API int llvq_pack_fields(const llvq_desc* d, const uint64_t* fields, void* 
 
 LLVQ_API int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell, uint64_t* indices,
                              int32_t* err_count, void* stream) {
-  if (max_shell < 2 || max_shell > LLVQ_MAX_SHELL || n < 0) return LLVQ_EINVAL;
+  if (max_shell < 2 || max_shell > kRankWideMaxShell || n < 0) return LLVQ_EINVAL;
   if (n == 0) return LLVQ_OK;
   if (!points || !indices || !aligned(indices, 8)) return LLVQ_EINVAL;
   if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
   const unsigned block = 256;
+  if (max_shell > LLVQ_MAX_SHELL) {
+    // the general rank (shells past 10)
+    hipLaunchKernelGGL(k_rank_wide, dim3(grid_for((uint64_t)n, kWideThreads)), dim3(kWideThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), points, n, max_shell, indices, err_count);
+    return launch_status();
+  }
   if (aligned(points, 8))
     hipLaunchKernelGGL((k_rank<true>), dim3(grid_for((uint64_t)n, block)), dim3(block), 0,
                        reinterpret_cast<hipStream_t>(stream), points, n, max_shell, indices, err_count);

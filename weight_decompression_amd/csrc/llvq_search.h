@@ -31,10 +31,10 @@
 // candidate within a lane.  Wavefront 0 then
 // rebuilds the winner: the argmax class for that codeword, the coordinates by ranking
 // (ties by position, as a stable sort), and writes the int8 point.  Under the angular
-// objective a winner 2u in shell 8 with u a lattice point is replaced by u: the two tie
-// exactly, u has the smaller index, and within shells 2..10 this is the only collinear
-// pair.  A vector with a non-finite coordinate gets the zero vector, which the rank step
-// rejects.
+// objective a winner 2u in shell 8 or 12 with u a lattice point is replaced by u: the two
+// tie exactly and u (shell 2 or 3) has the smaller index; within shells 2..13 these are
+// the only collinear pairs (k v lies in shell k^2 m).  A vector with a non-finite
+// coordinate gets the zero vector, which the rank step rejects.
 
 #pragma once
 
@@ -271,14 +271,14 @@ __global__ __launch_bounds__(kSearchThreads) void k_search(const float* __restri
         }
       }
       if (!EUCLID) {
-        // The angular objective ignores |v|: a shell-8 point 2u with u in the lattice ties
-        // exactly with u (shell 2), whose index is smaller, and u is the answer (fp32
-        // rounding need not have seen the tie).
+        // The angular objective ignores |v|: a shell-8 or shell-12 point 2u with u in the
+        // lattice ties exactly with u (shell 2 or 3), whose index is smaller, and u is the
+        // answer (fp32 rounding need not have seen the tie).
         int n2 = lane < 24 ? v * v : 0;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) n2 += __shfl_xor(n2, off, 64);
         const uint64_t oddc = __ballot(lane < 24 && (v & 1) != 0);
-        if (n2 == 16 * 8 && oddc == 0u) {
+        if ((n2 == 16 * 8 || n2 == 16 * 12) && oddc == 0u) {
           const int u = v / 2;
           const int p = __shfl(u, 0, 64) & 1;
           const uint64_t par = __ballot(lane < 24 && (u & 1) != p);

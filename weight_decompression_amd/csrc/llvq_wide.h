@@ -24,6 +24,7 @@
 #pragma once
 
 constexpr int kWideThreads = 256;
+constexpr int kRankWideMaxShell = 33;   // the rank's output is 64-bit: shells 2..33 (C_33 < 2^64)
 
 struct WDesc {
   int32_t mode, rows, cols, kb;
@@ -381,6 +382,141 @@ __global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8
         for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
         if (lane == 0) y[(size_t)bi * (size_t)d.rows + (size_t)r] = a;
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Rank at shells 2..M (lattice point -> global index), the inverse of wide_decode_point.
+// Membership as in the 2-bit rank (common parity p, sum = 4p mod 8, norm 16 m with
+// 2 <= m <= M, the positions = 2 (p = 0) or = 1 (p = 1) mod 4 a Golay codeword, found from
+// its information bits); the class by binary search of the point's key (coset, then the
+// counts of its absolute values from the largest down) among the shell's class keys; the
+// multiset ranks R_S, R_T accumulate rem * (c_0 + .. + c_{k-1}) / n per position (exact
+// quotients); the free signs in decode order.  Returns false for a point that is not in
+// the shell union.
+
+// one multiset ranking in progress: rank so far, arrangements left, counts, values left
+struct Ranker {
+  uint64_t rank, rem, cnts;
+  uint32_t n, present;     // present: bit v set for each value v of the multiset (fixed)
+};
+
+__device__ __forceinline__ bool wide_rank_point(const int (&v)[kDim], int M, const uint64_t* inv, uint64_t& lo,
+                                                uint64_t& hi) {
+  const int par = v[0] & 1;
+  int n2 = 0, sum = 0;
+  uint32_t odd = 0, mask = 0, neg = 0, nz = 0;
+  uint64_t key = (uint64_t)par << 62;
+#pragma unroll
+  for (int p = 0; p < kDim; ++p) {
+    const int a = v[p];
+    n2 += a * a;
+    sum += a;
+    odd |= (uint32_t)(a & 1) << p;
+    mask |= (uint32_t)((a & 3) == (par ? 1 : 2)) << p;
+    neg |= (uint32_t)(a < 0) << p;
+    nz |= (uint32_t)(a != 0) << p;
+  }
+  if (odd != (par ? 0xffffffu : 0u) || (n2 & 15) || ((sum - 4 * par) & 7)) return false;
+  const int m = n2 >> 4;
+  if (m < 2 || m > M) return false;
+  const uint32_t pos = dev_tables::kGolayInfoPos[(mask >> 11) & 0xfffu];
+  if (dev_tables::kGolayTable[pos] != mask) return false;
+#pragma unroll
+  for (int p = 0; p < kDim; ++p) {
+    const int a = v[p] < 0 ? -v[p] : v[p];
+    if (a > par) key += 1ull << (5 * ((a - par) / 2 - 1));
+  }
+  int ca = dev_tables::kWideShellFirst[m], cb = dev_tables::kWideShellFirst[m + 1] - 1;
+  while (ca < cb) {
+    const int mid = (ca + cb + 1) >> 1;
+    if (dev_tables::kWideKey[mid] <= key)
+      ca = mid;
+    else
+      cb = mid - 1;
+  }
+  if (dev_tables::kWideKey[ca] != key) return false;
+  const LlvqWideClass& cr = dev_tables::kWideClass[ca];
+  const int w = cr.w;
+  const bool two = cr.parity == 0 && w > 0;              // support part on the codeword
+  const uint32_t sel = two ? mask : 0u;
+  Ranker S, T;
+  S.rank = 0;
+  T.rank = 0;
+  S.rem = cr.P_S;
+  T.rem = cr.P_T;
+  S.cnts = bytes8(cr.sc);
+  T.cnts = bytes8(cr.cc);
+  S.n = (uint32_t)w;
+  T.n = (uint32_t)(kDim - w);
+  S.present = 0;
+  T.present = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (cr.sc[k]) S.present |= 1u << cr.sv[k];
+    if (cr.cc[k]) T.present |= 1u << cr.cv[k];
+  }
+  const int q = two ? (31 - __clz((int)mask)) : -1;
+  uint64_t s_sup = 0, s_comp = 0;
+  uint32_t js = 0, jt = 0;
+#pragma unroll
+  for (int p = 0; p < kDim; ++p) {
+    const bool inS = (sel >> p) & 1u;
+    Ranker U = inS ? S : T;
+    const uint32_t a = (uint32_t)(v[p] < 0 ? -v[p] : v[p]);
+    const uint32_t k = (uint32_t)__popc(U.present & ((1u << a) - 1u));
+    const uint64_t below = U.cnts & ((1ull << (8 * k)) - 1ull);   // k <= 7
+    const uint32_t cum = (uint32_t)((below * 0x0101010101010101ull) >> 56);
+    const uint32_t ck = (uint32_t)(U.cnts >> (8 * k)) & 0xffu;
+    const uint32_t tz = (uint32_t)__builtin_ctz(U.n);
+    const uint64_t iv = inv[U.n >> (tz + 1)];
+    U.rank += ((U.rem * cum) >> tz) * iv;
+    U.rem = ((U.rem * ck) >> tz) * iv;
+    U.cnts -= 1ull << (8 * k);
+    U.n -= 1u;
+    if (inS)
+      S = U;
+    else
+      T = U;
+    // free signs: support positions but q, then nonzero complement positions
+    const uint64_t nb = (neg >> p) & 1u;
+    if (inS) {
+      if (p != q) {
+        s_sup |= nb << js;
+        ++js;
+      }
+    } else if ((nz >> p) & 1u) {
+      s_comp |= nb << jt;
+      ++jt;
+    }
+  }
+  const uint64_t s = cr.parity ? 0ull : (s_sup | (s_comp << js));
+  const uint64_t R = S.rank * cr.P_T + T.rank;
+  const uint32_t A = cr.parity ? 4096u : dev_tables::kWideCodewords[w];
+  const uint64_t r = cr.parity ? pos : pos - dev_tables::kWideGolayOffset[w];
+  const uint64_t J = r + (uint64_t)A * (s + (R << cr.B));
+  lo = cr.start_lo + J;
+  hi = cr.start_hi + (lo < J ? 1u : 0u);
+  return true;
+}
+
+// one point per lane; M <= 33 (indices below 2^64); a point outside the shell union gets
+// UINT64_MAX and is counted
+__global__ __launch_bounds__(kWideThreads) void k_rank_wide(const int8_t* __restrict__ pts, int64_t n, int M,
+                                                            uint64_t* __restrict__ out, int32_t* err) {
+  __shared__ uint64_t inv[12];
+  stage_inverses(inv);
+  for (int64_t i = (int64_t)blockIdx.x * kWideThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWideThreads) {
+    int v[kDim];
+#pragma unroll
+    for (int p = 0; p < kDim; ++p) v[p] = pts[i * kDim + p];
+    uint64_t lo, hi;
+    if (wide_rank_point(v, M, inv, lo, hi)) {
+      out[i] = lo;
+    } else {
+      out[i] = ~0ull;
+      if (err) atomicAdd(err, 1);
     }
   }
 }
