@@ -414,6 +414,13 @@ def run_search(a):
     return out
 
 
+def eff_of(mse, rate):
+    """MSE per dimension as effective bits (SQNR / 6.02 dB) and % of the Shannon bound at `rate`."""
+    bits = -0.5 * math.log2(mse)
+    return {"mse_per_dim": mse, "effective_bits": bits, "rate_bits_per_dim": rate,
+            "pct_of_shannon": 100.0 * bits / rate, "shannon_mse": 2.0 ** (-2.0 * rate)}
+
+
 def run_fidelity(a):
     """Distortion of the quantiser on the memoryless unit Gaussian source: n 24-blocks as a
     [n/128][3072] tensor.  Shape-gain at 2.0 bits/dim (44-bit shape index over shells 2..10 +
@@ -475,10 +482,27 @@ def run_fidelity(a):
     de = wd.make_desc(wd.MODE_EUCLID, rows, cols, 10, 44, 0)
     mse_eu, _ = quantize_and_mse(de, torch.full((rows,), best[1], dtype=torch.float16, device="cuda:0"), False)
 
-    def eff(mse, rate):
-        bits = -0.5 * math.log2(mse)
-        return {"mse_per_dim": mse, "effective_bits": bits, "rate_bits_per_dim": rate,
-                "pct_of_shannon": 100.0 * bits / rate, "shannon_mse": 2.0 ** (-2.0 * rate)}
+    # the pages' bit split at 2 bits/dim: a 46- or 47-bit shape (shells 2..11 / 2..12) with a
+    # 2- or 1-bit gain, and Euclidean spherical clipping with all 48 bits (shells 2..13)
+    split = {}
+    for M, sb, gb in ((11, 46, 2), (12, 47, 1)):
+        g = torch.from_numpy(synth.chi_gain_table(1 << gb)).cuda()
+        m, _ = quantize_and_mse(wd.make_desc(wd.MODE_SHAPEGAIN, rows, cols, M, sb, gb), g, False)
+        split[f"shape_gain_{sb}+{gb}"] = dict(max_shell=M, shape_bits=sb, gain_bits=gb, **eff_of(m, 2.0))
+        print(f"bench: fidelity shape-gain {sb}+{gb} done", file=sys.stderr, flush=True)
+    best13 = None
+    for sc in np.arange(0.20, 0.71, 0.025):
+        de = wd.make_desc(wd.MODE_EUCLID, sub, cols, 13, 48, 0)
+        srow = torch.full((sub,), float(sc), dtype=torch.float16, device="cuda:0")
+        m, _ = quantize_and_mse(de, srow, False)
+        if best13 is None or m < best13[0]:
+            best13 = (m, float(torch.tensor(float(sc), dtype=torch.float16)))
+    de = wd.make_desc(wd.MODE_EUCLID, rows, cols, 13, 48, 0)
+    m13, _ = quantize_and_mse(de, torch.full((rows,), best13[1], dtype=torch.float16, device="cuda:0"), False)
+    split["euclid_48"] = dict(max_shell=13, shape_bits=48, gain_bits=0, scale=best13[1],
+                              scale_grid="0.200..0.700 step 0.025 on 1/8 of the blocks", **eff_of(m13, 2.0))
+
+    eff = eff_of
 
     out = base_line("LLVQ shape-gain distortion on a unit Gaussian source at 2 bits/dim (MSE per dimension), "
                     "1 MI355X", mse_sg, "MSE/dim", a.steps, a.warmup, sec, "f32",
@@ -487,6 +511,7 @@ def run_fidelity(a):
     out["higher_is_better"] = False
     out["shape_gain"] = eff(mse_sg, 48 / 24)
     out["euclid"] = dict(eff(mse_eu, 44 / 24), scale=best[1], scale_grid="0.30..0.95 step 0.05 on 1/8 of the blocks")
+    out["pages_bit_split"] = split
     out["quantize_blocks_per_s"] = n / sec
     out["roofline"] = roofline("search", n, sec, n * (96 + 24 + 8 + 6),
                                "96 B fp32 block read + 32 B workspace + 6 B packed field per block")

@@ -209,3 +209,70 @@ def test_gemv_unaligned_activations_equal_aligned(xd):
     wd.gemv(desc, packed, scales, xu, y1)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
+
+
+def test_rank_full_grid_of_repeated_points():
+    # 2,000 points tiled to 262,144 (1,024 workgroups, several per CU): every copy ranks to
+    # its index
+    M = 24
+    rng = random.Random(77)
+    C = leech.index_count(M)
+    I = [rng.randrange(C) for _ in range(2000)]
+    base = np.array([bijection.unrank(i, M) for i in I], dtype=np.int8)
+    reps = 262144 // len(I) + 1
+    P = np.tile(base, (reps, 1))[:262144]
+    want = np.tile(np.array(I, dtype=np.uint64), reps)[:262144]
+    out = torch.empty(len(P), dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.encode_ref(torch.from_numpy(P).cuda(), M, out, err)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint64)
+    assert int(err.item()) == 0
+    assert np.array_equal(got, want), int((got != want).sum())
+
+
+def test_decode_rank_round_trip_every_block_4096x11008():
+    # shell 33, 64 + 4-bit fields: decode every block of a 4096 x 11008 tensor to points on
+    # the GPU and rank them back; every block's index must return
+    M = 33
+    t = synth.make_wide_tensor("rt33", 71, 0, 4096, 11008, leech.index_count(M), max_shell=M, shape_bits=64,
+                               gain_bits=4, batch=0)
+    desc, packed, scales, _ = dev(t)
+    pts = torch.empty((4096, t.kb * 24), dtype=torch.int8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.decode(desc, packed, scales, wd.OUT_POINTS_I8, pts, err)
+    idx = torch.empty(4096 * t.kb, dtype=torch.int64, device="cuda")
+    wd.encode_ref(pts.view(-1, 24), M, idx, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = idx.cpu().numpy().view(np.uint64)
+    want = np.array(t.shape_idx.ravel(), dtype=np.uint64)
+    assert np.array_equal(got, want), int((got != want).sum())
+    raw = t.packed.tobytes()
+    p = pts.cpu().numpy()
+    for r in (0, 2222, 4095):
+        assert np.array_equal(p[r].astype(np.int64), reference.decode_row_points(raw, 4096, 11008, M, 64, 4, r)), r
+
+
+def test_gemv_every_row_against_decoded_weights_3bit():
+    # the 3-bit GEMV of all 4,096 rows against an fp64 product of the decoded points (the
+    # points themselves checked by the round trip above and the oracle rows)
+    C = leech.index_count(42)
+    t = synth.make_wide_tensor("w3all", 72, 0, 4096, 11008, C)
+    desc, packed, scales, x = dev(t)
+    y = torch.empty((1, 4096), dtype=torch.float32, device="cuda")
+    wd.gemv(desc, packed, scales, x, y)
+    pts = torch.empty((4096, t.kb * 24), dtype=torch.int8, device="cuda")
+    wd.decode(desc, packed, scales, wd.OUT_POINTS_I8, pts)
+    torch.cuda.synchronize()
+    # per-block scale G[g] / (4 sqrt m) in fp64 from the decoded point's norm
+    v = pts.view(4096, t.kb, 24).double()
+    m = (v * v).sum(-1) / 16.0
+    g = torch.from_numpy(t.gain_idx.astype(np.int64)).cuda()
+    G = torch.from_numpy(t.scales_f16.astype(np.float64)).cuda()[g]
+    w = (v * (G / (4.0 * torch.sqrt(m)))[..., None]).reshape(4096, -1)[:, :11008]
+    xf = x.double().reshape(-1)
+    ref = w @ xf
+    mag = (w.abs() @ xf.abs())
+    ok = (y[0].double() - ref).abs() <= 1e-4 * mag
+    assert bool(ok.all()), int((~ok).sum())

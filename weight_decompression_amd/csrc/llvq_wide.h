@@ -16,7 +16,9 @@
 //     the next value of the support sequence if p is on the codeword, of the complement
 //     sequence otherwise (each sequence fills its positions in ascending order).  The
 //     arrangements starting with value v are rem * count(v) / n, an exact quotient taken
-//     as a product with the inverse of n's odd part modulo 2^64;
+//     as a product with the inverse of n's odd part modulo 2^64 (a 96-byte table read
+//     through the caches; an LDS copy of it gave wrong quotients in workgroups that
+//     shared a CU with another, a cause not found, so it stays in global memory);
 //   * signs as in the 2-bit kernels.
 // One 24-block per lane; VALU-bound.  Included once by llvq.hip after the generated
 // tables.
@@ -134,8 +136,8 @@ __device__ __forceinline__ uint64_t bytes8(const uint8_t* p) {
 }
 
 // Integer lattice point of global shape index I (valid: I < count).  Returns the shell.
-// inv: the inverses mod 2^64 of 1, 3, ..., 23 (staged in LDS by the kernel).
-__device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M, const uint64_t* inv, int v[kDim]) {
+__device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M, int v[kDim]) {
+  const uint64_t* inv = dev_tables::kWideOddInverse;
   const int k = wide_find_class(lo, hi, M);
   const LlvqWideClass& cr = dev_tables::kWideClass[k];
   const uint64_t J = lo - cr.start_lo;      // < 2^63: the high words cancel
@@ -247,18 +249,10 @@ __device__ __forceinline__ bool wide_block(const WDesc& d, const uint8_t* __rest
   return !u128_le(d.count_lo, d.count_hi, lo, hi);     // I < count
 }
 
-// the inverses of the odd numbers below 24 in LDS (read once per unranked position)
-__device__ __forceinline__ void stage_inverses(uint64_t* inv) {
-  if (threadIdx.x < 12) inv[threadIdx.x] = dev_tables::kWideOddInverse[threadIdx.x];
-  __syncthreads();
-}
-
 template <int OUT>
 __global__ __launch_bounds__(kWideThreads) void k_decode_wide(WDesc d, const uint8_t* __restrict__ packed,
                                                               const __half* __restrict__ scales,
                                                               void* __restrict__ out, int32_t* err) {
-  __shared__ uint64_t inv[12];
-  stage_inverses(inv);
   const uint64_t nblocks = (uint64_t)d.rows * (uint64_t)d.kb;
   for (uint64_t j = (uint64_t)blockIdx.x * kWideThreads + threadIdx.x; j < nblocks;
        j += (uint64_t)gridDim.x * kWideThreads) {
@@ -267,7 +261,7 @@ __global__ __launch_bounds__(kWideThreads) void k_decode_wide(WDesc d, const uin
     int v[kDim];
     int m = 0;
     if (wide_block(d, packed, j, lo, hi, g)) {
-      m = wide_decode_point(lo, hi, d.max_shell, inv, v);
+      m = wide_decode_point(lo, hi, d.max_shell, v);
     } else {
 #pragma unroll
       for (int p = 0; p < kDim; ++p) v[p] = 0;
@@ -302,8 +296,6 @@ __global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8
                                                             const __half* __restrict__ scales,
                                                             const void* __restrict__ xv, int batch, bool xvec,
                                                             float* __restrict__ y, int32_t* err) {
-  __shared__ uint64_t inv[12];
-  stage_inverses(inv);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int K = d.cols;
@@ -319,7 +311,7 @@ __global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8
       int v[kDim];
       int m = 0;
       if (wide_block(d, packed, j, lo, hi, g)) {
-        m = wide_decode_point(lo, hi, d.max_shell, inv, v);
+        m = wide_decode_point(lo, hi, d.max_shell, v);
       } else {
 #pragma unroll
         for (int p = 0; p < kDim; ++p) v[p] = 0;
@@ -402,8 +394,8 @@ struct Ranker {
   uint32_t n, present;     // present: bit v set for each value v of the multiset (fixed)
 };
 
-__device__ __forceinline__ bool wide_rank_point(const int (&v)[kDim], int M, const uint64_t* inv, uint64_t& lo,
-                                                uint64_t& hi) {
+__device__ __forceinline__ bool wide_rank_point(const int (&v)[kDim], int M, uint64_t& lo, uint64_t& hi) {
+  const uint64_t* inv = dev_tables::kWideOddInverse;
   const int par = v[0] & 1;
   int n2 = 0, sum = 0;
   uint32_t odd = 0, mask = 0, neg = 0, nz = 0;
@@ -505,14 +497,12 @@ __device__ __forceinline__ bool wide_rank_point(const int (&v)[kDim], int M, con
 // UINT64_MAX and is counted
 __global__ __launch_bounds__(kWideThreads) void k_rank_wide(const int8_t* __restrict__ pts, int64_t n, int M,
                                                             uint64_t* __restrict__ out, int32_t* err) {
-  __shared__ uint64_t inv[12];
-  stage_inverses(inv);
   for (int64_t i = (int64_t)blockIdx.x * kWideThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWideThreads) {
     int v[kDim];
 #pragma unroll
     for (int p = 0; p < kDim; ++p) v[p] = pts[i * kDim + p];
     uint64_t lo, hi;
-    if (wide_rank_point(v, M, inv, lo, hi)) {
+    if (wide_rank_point(v, M, lo, hi)) {
       out[i] = lo;
     } else {
       out[i] = ~0ull;
