@@ -715,14 +715,20 @@ int gemv_wide(const llvq_desc* d, const void* packed, const void* scales, const 
   const unsigned grid = grid_for((uint64_t)w.rows, kWideThreads / 64);
   const int xbytes = x_dtype == LLVQ_X_BF16 ? 2 : 4;
   const bool xvec = aligned(x, 16) && ((uint64_t)w.cols * (uint64_t)xbytes) % 16u == 0;
-  if (x_dtype == LLVQ_X_BF16)
-    hipLaunchKernelGGL((k_gemv_wide<true>), dim3(grid), dim3(kWideThreads), 0, s, w,
-                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, batch, xvec, y,
-                       err_count);
-  else
-    hipLaunchKernelGGL((k_gemv_wide<false>), dim3(grid), dim3(kWideThreads), 0, s, w,
-                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, batch, xvec, y,
-                       err_count);
+  const uint8_t* pk = static_cast<const uint8_t*>(packed);
+  const __half* sc = static_cast<const __half*>(scales);
+  const dim3 g(grid), t(kWideThreads);
+  if (x_dtype == LLVQ_X_BF16) {
+    if (batch == 1)
+      hipLaunchKernelGGL((k_gemv_wide<true, 1>), g, t, 0, s, w, pk, sc, x, batch, xvec, y, err_count);
+    else
+      hipLaunchKernelGGL((k_gemv_wide<true, LLVQ_MAX_BATCH>), g, t, 0, s, w, pk, sc, x, batch, xvec, y, err_count);
+  } else {
+    if (batch == 1)
+      hipLaunchKernelGGL((k_gemv_wide<false, 1>), g, t, 0, s, w, pk, sc, x, batch, xvec, y, err_count);
+    else
+      hipLaunchKernelGGL((k_gemv_wide<false, LLVQ_MAX_BATCH>), g, t, 0, s, w, pk, sc, x, batch, xvec, y, err_count);
+  }
   return launch_status();
 }
 }  // namespace

@@ -289,9 +289,10 @@ __global__ __launch_bounds__(kWideThreads) void k_decode_wide(WDesc d, const uin
 }
 
 // y[bi][r] = sum over blocks of scale * (v . x[bi]); one wave per row, lanes over the
-// row's blocks, fixed-order wave reduction (repeatable bit for bit).  xvec: x is 16-byte
+// row's blocks, fixed-order wave reduction (repeatable bit for bit).  MAXB: 1 for batch 1
+// (fewer registers, more waves in flight to cover the table reads), else 16.  xvec: x is 16-byte
 // aligned with 16-byte aligned rows, so a full block's activations load as 16-byte words.
-template <bool XBF16>
+template <bool XBF16, int MAXB>
 __global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8_t* __restrict__ packed,
                                                             const __half* __restrict__ scales,
                                                             const void* __restrict__ xv, int batch, bool xvec,
@@ -300,9 +301,9 @@ __global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8
   const int wave = threadIdx.x >> 6;
   const int K = d.cols;
   for (int r = blockIdx.x * (kWideThreads / 64) + wave; r < d.rows; r += gridDim.x * (kWideThreads / 64)) {
-    float acc[LLVQ_MAX_BATCH];
+    float acc[MAXB];
 #pragma unroll
-    for (int bi = 0; bi < LLVQ_MAX_BATCH; ++bi) acc[bi] = 0.0f;
+    for (int bi = 0; bi < MAXB; ++bi) acc[bi] = 0.0f;
     const float rs = d.mode == LLVQ_MODE_SHAPEGAIN ? 0.0f : __half2float(scales[r]);
     for (int b = lane; b < d.kb; b += 64) {
       const uint64_t j = (uint64_t)r * (uint64_t)d.kb + (uint64_t)b;
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8
       const int k0 = b * kDim;
       const int lim = min(kDim, K - k0);
 #pragma unroll
-      for (int bi = 0; bi < LLVQ_MAX_BATCH; ++bi) {
+      for (int bi = 0; bi < MAXB; ++bi) {
         if (bi < batch) {
           float t = 0.0f;
           const size_t x0 = (size_t)bi * (size_t)K + (size_t)k0;
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(kWideThreads) void k_gemv_wide(WDesc d, const uint8
       }
     }
 #pragma unroll
-    for (int bi = 0; bi < LLVQ_MAX_BATCH; ++bi) {
+    for (int bi = 0; bi < MAXB; ++bi) {
       if (bi < batch) {
         float a = acc[bi];
 #pragma unroll
