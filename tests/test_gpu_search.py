@@ -329,3 +329,16 @@ def test_quantize_past_shell_10_stream_matches_oracle(M, sb, gb):
         for b in range(5):
             I = int(fields[r, b]) & ((1 << sb) - 1)
             assert list(out[r, 24 * b:24 * b + 24].cpu().numpy().astype(int)) == bijection.unrank(I, M)
+
+
+def test_quantize_euclid_48bit_shell13_stream_matches_oracle():
+    # Euclidean spherical shaping with all 48 bits on the shape (shells 2..13), row scales
+    rng = np.random.default_rng(45)
+    rows, cols = 5, 24 * 4 + 7
+    s = rng.uniform(0.3, 0.45, size=rows).astype(np.float16)
+    w = rng.standard_normal((rows, cols)).astype(np.float32)
+    desc = wd.make_desc(wd.MODE_EUCLID, rows, cols, 13, 48, 0)
+    got, err = gpu_quantize(desc, w, s)
+    assert err == 0
+    want = synth.pack_fields(oracle_fields(w, s, 13, wd.MODE_EUCLID, 0, 48), 48)
+    assert got.size == want.size and np.array_equal(got, want)
