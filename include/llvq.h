@@ -166,6 +166,17 @@ int llvq_gemv(const llvq_desc* d, const void* packed, const void* scales, const 
 int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell, uint64_t* indices,
                     int32_t* err_count, void* stream);
 
+/* The same with 128-bit indices, for shells up to 42 (past shell 33 indices exceed 64 bits;
+ * 3 bits per weight is shell 42).
+ *   points    : int8 [n][24], any alignment.
+ *   max_shell : M in [2, 42].
+ *   indices   : uint64 [n][2] output (8-byte aligned): index i is indices[2i] | indices[2i+1] << 64;
+ *               both words all ones for a point that is not in the lattice or not in shells
+ *               2..M (counted in err_count).
+ * Returns LLVQ_OK, LLVQ_EINVAL or LLVQ_EHIP. */
+int llvq_encode_wide(const int8_t* points, int64_t n, int32_t max_shell, uint64_t* indices,
+                     int32_t* err_count, void* stream);
+
 /* Quantise: nearest point of the shell union 2..M to each 24-vector, and its index
  * (papernotes.org notes, 关键设计 1: the single-shell search extended to the union of
  * shells 2..M, with an angular objective for shape-gain and a Euclidean one for spherical

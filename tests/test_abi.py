@@ -201,3 +201,13 @@ def test_wide_descriptors(lib):
     assert lib.llvq_gemv(ctypes.byref(d), p, p, p, 3, 1, p, None, None) == -1
     e = wd.make_desc(wd.MODE_EUCLID, 7, 100, 24, 60, 1)                        # Euclidean: no gain field
     assert lib.llvq_packed_bytes(ctypes.byref(e)) == -1
+
+
+def test_encode_wide_validation(lib):
+    p = ctypes.c_void_p(0x10000)
+    assert lib.llvq_encode_wide(p, 10, 43, p, None, None) == -1          # past shell 42
+    assert lib.llvq_encode_wide(p, 10, 1, p, None, None) == -1
+    assert lib.llvq_encode_wide(p, -1, 42, p, None, None) == -1
+    assert lib.llvq_encode_wide(p, 10, 42, ctypes.c_void_p(0x10004), None, None) == -1
+    assert lib.llvq_encode_wide(None, 0, 42, None, None, None) == 0      # empty: no-op
+    assert lib.llvq_encode_ref(p, 10, 34, p, None, None) == -1           # 64-bit output: shells <= 33

@@ -276,3 +276,46 @@ def test_gemv_every_row_against_decoded_weights_3bit():
     mag = (w.abs() @ xf.abs())
     ok = (y[0].double() - ref).abs() <= 1e-4 * mag
     assert bool(ok.all()), int((~ok).sum())
+
+
+def test_round_trip_3bit_every_block_128bit_indices():
+    # 3 bits per weight (shell 42, indices past 2^64): decode every block of a 2048 x 4096
+    # tensor to points and rank them back to 128-bit indices
+    M = 42
+    t = synth.make_wide_tensor("rt42", 73, 0, 2048, 4096, leech.index_count(M), batch=0)
+    desc, packed, scales, _ = dev(t)
+    pts = torch.empty((2048, t.kb * 24), dtype=torch.int8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.decode(desc, packed, scales, wd.OUT_POINTS_I8, pts, err)
+    idx = torch.empty((2048 * t.kb, 2), dtype=torch.int64, device="cuda")
+    wd.encode_wide(pts.view(-1, 24), M, idx, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = idx.cpu().numpy().view(np.uint64)
+    flat = t.shape_idx.ravel()
+    want_lo = np.array([int(i) & (2**64 - 1) for i in flat], dtype=np.uint64)
+    want_hi = np.array([int(i) >> 64 for i in flat], dtype=np.uint64)
+    assert np.array_equal(got[:, 0], want_lo) and np.array_equal(got[:, 1], want_hi)
+    assert (want_hi > 0).any()                                      # indices past 2^64 present
+
+
+def test_encode_wide_matches_oracle_and_rejects():
+    M = 42
+    rnd = random.Random(421)
+    C = leech.index_count(M)
+    T = classes.class_table(M)
+    I = [rnd.randrange(C) for _ in range(300)] + [T[k].start for k in rnd.sample(range(len(T)), 300)]
+    P = np.array([bijection.unrank(i, M) for i in I], dtype=np.int8)
+    bad = P[:3].copy()
+    bad[0, 0] += 2
+    bad[1, :] = 0
+    bad[2, 0] += 1
+    allp = np.concatenate([P, bad])
+    out = torch.empty((len(allp), 2), dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd.encode_wide(torch.from_numpy(allp).cuda(), M, out, err)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint64)
+    vals = [int(a) | (int(b) << 64) for a, b in got]
+    assert vals[:len(I)] == I
+    assert vals[len(I):] == [2**128 - 1] * 3 and int(err.item()) == 3

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllvq.so"
 EXPORTED_SYMBOLS = ("llvq_index_count", "llvq_packed_bytes", "llvq_error_string",
                     "llvq_decode", "llvq_gemv", "llvq_encode_ref", "llvq_search", "llvq_quantize_workspace_bytes",
                     "llvq_quantize", "llvq_pack_fields", "llvq_decode_many",
-                    "llvq_index_count_wide")
+                    "llvq_index_count_wide", "llvq_encode_wide")
 
 
 class LlvqError(RuntimeError):
@@ -79,6 +79,8 @@ def load_library(path=LIB_PATH):
     lib.llvq_gemv.restype = ctypes.c_int
     lib.llvq_encode_ref.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.llvq_encode_ref.restype = ctypes.c_int
+    lib.llvq_encode_wide.argtypes = [vp, i64, i32, vp, vp, vp]
+    lib.llvq_encode_wide.restype = ctypes.c_int
     lib.llvq_search.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
     lib.llvq_search.restype = ctypes.c_int
     lib.llvq_quantize_workspace_bytes.argtypes = [dp]
@@ -195,3 +197,10 @@ def decode_many(descs, packed, scales, out_kind, outs, err_count=None, stream=No
                                            None if sarr is None else ctypes.cast(sarr, ctypes.c_void_p), out_kind,
                                            ctypes.cast(oarr, ctypes.c_void_p), _ptr(err_count), _stream(stream)),
            "llvq_decode_many")
+
+
+def encode_wide(points, max_shell, indices, err_count=None, stream=None):
+    """llvq_encode_wide: int8 points [n][24] -> 128-bit indices as int64 pairs [n][2] (lo, hi)."""
+    n = points.shape[0] if points.dim() > 1 else points.numel() // 24
+    _check(load_library().llvq_encode_wide(_ptr(points), n, max_shell, _ptr(indices),
+                                           _ptr(err_count), _stream(stream)), "llvq_encode_wide")

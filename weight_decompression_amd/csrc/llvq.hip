@@ -1010,7 +1010,7 @@ LLVQ_API int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell,
   const unsigned block = 256;
   if (max_shell > LLVQ_MAX_SHELL) {
     // the general rank (shells past 10)
-    hipLaunchKernelGGL(k_rank_wide, dim3(grid_for((uint64_t)n, kWideThreads)), dim3(kWideThreads), 0,
+    hipLaunchKernelGGL(k_rank_wide<false>, dim3(grid_for((uint64_t)n, kWideThreads)), dim3(kWideThreads), 0,
                        reinterpret_cast<hipStream_t>(stream), points, n, max_shell, indices, err_count);
     return launch_status();
   }
@@ -1020,5 +1020,16 @@ LLVQ_API int llvq_encode_ref(const int8_t* points, int64_t n, int32_t max_shell,
   else
     hipLaunchKernelGGL((k_rank<false>), dim3(grid_for((uint64_t)n, block)), dim3(block), 0,
                        reinterpret_cast<hipStream_t>(stream), points, n, max_shell, indices, err_count);
+  return launch_status();
+}
+
+LLVQ_API int llvq_encode_wide(const int8_t* points, int64_t n, int32_t max_shell, uint64_t* indices,
+                              int32_t* err_count, void* stream) {
+  if (max_shell < 2 || max_shell > LLVQ_WIDE_MAX_SHELL || n < 0) return LLVQ_EINVAL;
+  if (n == 0) return LLVQ_OK;
+  if (!points || !indices || !aligned(indices, 8)) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  hipLaunchKernelGGL(k_rank_wide<true>, dim3(grid_for((uint64_t)n, kWideThreads)), dim3(kWideThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), points, n, max_shell, indices, err_count);
   return launch_status();
 }

@@ -494,8 +494,10 @@ __device__ __forceinline__ bool wide_rank_point(const int (&v)[kDim], int M, uin
   return true;
 }
 
-// one point per lane; M <= 33 (indices below 2^64); a point outside the shell union gets
-// UINT64_MAX and is counted
+// one point per lane; WIDE: 128-bit indices as (lo, hi) pairs, shells 2..42; otherwise 64-bit
+// indices, shells 2..33 (below 2^64).  A point outside the shell union gets all ones and is
+// counted.
+template <bool WIDE>
 __global__ __launch_bounds__(kWideThreads) void k_rank_wide(const int8_t* __restrict__ pts, int64_t n, int M,
                                                             uint64_t* __restrict__ out, int32_t* err) {
   for (int64_t i = (int64_t)blockIdx.x * kWideThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kWideThreads) {
@@ -503,11 +505,17 @@ __global__ __launch_bounds__(kWideThreads) void k_rank_wide(const int8_t* __rest
 #pragma unroll
     for (int p = 0; p < kDim; ++p) v[p] = pts[i * kDim + p];
     uint64_t lo, hi;
-    if (wide_rank_point(v, M, lo, hi)) {
-      out[i] = lo;
-    } else {
-      out[i] = ~0ull;
+    const bool ok = wide_rank_point(v, M, lo, hi);
+    if (!ok) {
+      lo = ~0ull;
+      hi = ~0ull;
       if (err) atomicAdd(err, 1);
+    }
+    if (WIDE) {
+      out[2 * i] = lo;
+      out[2 * i + 1] = hi;
+    } else {
+      out[i] = lo;
     }
   }
 }
