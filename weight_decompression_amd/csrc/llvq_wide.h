@@ -126,7 +126,24 @@ __device__ __forceinline__ int wide_find_class(uint64_t lo, uint64_t hi, int M) 
 struct Unranker {
   uint64_t rem, rank, cnts, vals;
   uint32_t n;
+  bool fp;      // the rank is carried as u = (rank + 1/2) / rem in fp64 (rem < 2^kFpRem)
+  double u;
 };
+
+// Below 2^kFpRem arrangements left, a part is finished by arithmetic decoding in fp64: u
+// locates the rank inside [0, 1) in an interval of half-width 1/(2 rem); each step
+// u' = (u n - C_k) / c_k scales the interval by n / c_k and adds three roundings of at most
+// 24 x 2^-53.  An error made while rem_t arrangements were left is scaled by rem_t / rem at a
+// later step, so against that step's half-width the at most 24 errors sum to below
+// 2 x 24 x 3 x 24 x 2^-53 x 2^kFpRem = 0.11 (kFpRem = 38): every slot choice is exact.
+constexpr int kFpRem = 38;
+
+__device__ __forceinline__ void to_fp(Unranker& U) {
+  if (!U.fp && U.rem < (1ull << kFpRem)) {
+    U.u = ((double)U.rank + 0.5) / (double)U.rem;
+    U.fp = true;
+  }
+}
 
 __device__ __forceinline__ uint64_t bytes8(const uint8_t* p) {
   uint64_t v = 0;
@@ -174,6 +191,12 @@ __device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M
   S.vals = bytes8(cr.sv);
   T.cnts = bytes8(cr.cc);
   T.vals = bytes8(cr.cv);
+  S.fp = false;
+  T.fp = false;
+  S.u = 0.0;
+  T.u = 0.0;
+  to_fp(S);
+  to_fp(T);
 
   const uint32_t sel = (cr.parity == 0 && w) ? c : 0u;
   const int q = (cr.parity == 0 && w) ? (31 - __clz((int)c)) : -1;
@@ -185,22 +208,39 @@ __device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M
   for (int p = 0; p < kDim; ++p) {
     const bool inS = (sel >> p) & 1u;
     Unranker U = inS ? S : T;
-    // the arrangements starting with value slot k number rem * c_k / n; the slot holding
-    // rank is the first k with rank * n < rem * (c_0 + ... + c_k), compared without dividing
-    const uint64_t t_n = U.rank * U.n;
-    uint32_t kk = 0, ck = (uint32_t)U.cnts & 0xffu;
-    uint64_t below = 0, upto = U.rem * ck;
-    while (kk < 7u && t_n >= upto) {
-      ++kk;
-      ck = (uint32_t)(U.cnts >> (8 * kk)) & 0xffu;
-      below = upto;
-      upto += U.rem * ck;
+    uint32_t kk;
+    if (U.fp) {
+      // arithmetic decoding: slot k is the number of running counts c_0 + .. + c_j at most
+      // floor(u n) (one per byte, all below 25, compared at once)
+      const double y = U.u * (double)U.n;
+      const int fy = (int)y;
+      const uint64_t run = U.cnts * 0x0101010101010101ull;
+      const uint64_t over = (run + (uint64_t)(127 - fy) * 0x0101010101010101ull) & 0x8080808080808080ull;
+      kk = 8u - (uint32_t)__popcll(over);
+      const uint32_t ck = (uint32_t)(U.cnts >> (8 * kk)) & 0xffu;
+      const uint32_t below = kk ? (uint32_t)(run >> (8 * (kk - 1))) & 0xffu : 0u;
+      U.u = (y - (double)below) / (double)ck;
+    } else {
+      // the arrangements starting with value slot k number rem * c_k / n; the slot holding
+      // rank is the first k with rank * n < rem * (c_0 + ... + c_k), compared without
+      // dividing
+      const uint64_t t_n = U.rank * U.n;
+      uint32_t ck = (uint32_t)U.cnts & 0xffu;
+      uint64_t below = 0, upto = U.rem * ck;
+      kk = 0;
+      while (kk < 7u && t_n >= upto) {
+        ++kk;
+        ck = (uint32_t)(U.cnts >> (8 * kk)) & 0xffu;
+        below = upto;
+        upto += U.rem * ck;
+      }
+      // new rank and count of arrangements: exact quotients by n
+      const uint32_t tz = (uint32_t)__builtin_ctz(U.n);
+      const uint64_t iv = inv[U.n >> (tz + 1)];
+      U.rank = ((t_n - below) >> tz) * iv;
+      U.rem = ((U.rem * ck) >> tz) * iv;
+      to_fp(U);
     }
-    // new rank and count of arrangements: exact quotients by n
-    const uint32_t tz = (uint32_t)__builtin_ctz(U.n);
-    const uint64_t iv = inv[U.n >> (tz + 1)];
-    U.rank = ((t_n - below) >> tz) * iv;
-    U.rem = ((U.rem * ck) >> tz) * iv;
     const int a = (int)((U.vals >> (8 * kk)) & 0xffu);
     U.cnts -= 1ull << (8 * kk);
     U.n -= 1u;
