@@ -49,7 +49,7 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "1eb01ff3a8937e4e5d4eea0a90fa751e8a94377d5c501249946b834815d9ab54",
+        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
         "valu_lane_ops_per_unit": 670.3,       # SQ_INSTS_VALU * 64 / blocks
@@ -57,7 +57,7 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "1eb01ff3a8937e4e5d4eea0a90fa751e8a94377d5c501249946b834815d9ab54",
+        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
         "valu_lane_ops_per_unit": 695.4,
@@ -65,7 +65,7 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": 1835008,
     },
     "gemv_3bit_b1": {
-        "source_sha256": "1eb01ff3a8937e4e5d4eea0a90fa751e8a94377d5c501249946b834815d9ab54",
+        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
         "summary": "profiles/gemv_3bit_4096x11008_batch1_k_gemv_wide.md",
         "unit_of_work": "24-weight block (k_gemv_wide)",
         "valu_lane_ops_per_unit": 3696.2,
@@ -73,7 +73,7 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": 32769,
     },
     "decode_bf16": {
-        "source_sha256": "1eb01ff3a8937e4e5d4eea0a90fa751e8a94377d5c501249946b834815d9ab54",
+        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
         "summary": "profiles/decode_bf16_7b_k_decode_many.md",
         "unit_of_work": "24-weight block (k_decode_many<bf16>)",
         "valu_lane_ops_per_unit": 738.4,
@@ -81,7 +81,7 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": 809500672,
     },
     "roundtrip": {
-        "source_sha256": "1eb01ff3a8937e4e5d4eea0a90fa751e8a94377d5c501249946b834815d9ab54",
+        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
         "summary": "profiles/roundtrip_1e7_k_decode_tile_k_rank.md",
         "unit_of_work": "point: decode to int8 (626.0) + rank (951.2)",
         "valu_lane_ops_per_unit": 1577.2,
@@ -89,7 +89,7 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": None,
     },
     "search": {
-        "source_sha256": "1eb01ff3a8937e4e5d4eea0a90fa751e8a94377d5c501249946b834815d9ab54",
+        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
         "summary": "profiles/search_4096x4096_k_search_k_rank.md",
         # The search issues more VALU instructions per clock than one per CU (mostly fp32
         # add / fma / max, which issue at up to 1.46 wave-instructions per CU per clock on

@@ -8,8 +8,10 @@
 // sizes reach 2^60, the index past the codeword reaches 2^53, up to 8 distinct absolute
 // values up to 25 per class, global indices past 2^64), so this decoder works with exact
 // 64-bit integers inside a class and 128-bit compares for the global index:
-//   * shell and class by binary search over 128-bit starts (records in global memory,
-//     read through the caches: 38,649 classes, 2.8 MB);
+//   * shell by binary search over 128-bit starts; class through a per-shell bucket table
+//     (the offset inside the shell shifted to at most 1024 buckets) and a binary search
+//     over the few class starts it leaves (records in global memory, read through the
+//     caches: 38,649 classes, 2.8 MB);
 //   * J = I - start < 2^63; r = J mod A, I' = J div A; s = I' mod 2^B, R = I' >> B;
 //     even classes R = rank_S * P_T + rank_T;
 //   * both multiset unrankings advance in one pass over the 24 positions: position p takes
@@ -18,7 +20,9 @@
 //     arrangements starting with value v are rem * count(v) / n, an exact quotient taken
 //     as a product with the inverse of n's odd part modulo 2^64 (a 96-byte table read
 //     through the caches; an LDS copy of it gave wrong quotients in workgroups that
-//     shared a CU with another, a cause not found, so it stays in global memory);
+//     shared a CU with another, a cause not found, so it stays in global memory); once
+//     fewer than 2^kFpRem arrangements are left the part is finished by fp64 arithmetic
+//     decoding (see kFpRem);
 //   * signs as in the 2-bit kernels.
 // One 24-block per lane; VALU-bound.  Included once by llvq.hip after the generated
 // tables.
