@@ -72,6 +72,14 @@ KERNEL_PROFILES = {
         "fetch_bytes_per_launch": 32838808,
         "write_bytes_per_launch": 32769,
     },
+    "decode_3bit": {
+        "source_sha256": "0000000000000000000000000000000000000000000000000000000000000000",
+        "summary": "profiles/decode_bf16_3bit_4096x11008_k_decode_wide.md",
+        "unit_of_work": "24-weight block (k_decode_wide<bf16>)",
+        "valu_lane_ops_per_unit": 0,
+        "fetch_bytes_per_launch": 0,
+        "write_bytes_per_launch": 0,
+    },
     "decode_bf16": {
         "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
         "summary": "profiles/decode_bf16_7b_k_decode_many.md",
@@ -315,6 +323,36 @@ def run_decode_7b(a):
                                "6 B packed index read + 48 B bf16 written per 24-weight block", launches=len(calls))
     out["wall_s_timed"] = wall
     return out
+
+
+def run_decode_3bit(a):
+    """Decode-to-bf16 of a 4096 x 11008 tensor at 3 bits per weight (68 + 4-bit fields,
+    shells 2..42), through the general decoder."""
+    import torch
+    import weight_decompression_amd as wd
+    from weight_decompression_amd import synth
+
+    lib = wd.load_library()
+    t = synth.make_wide_tensor("dec3", 10, 0, 4096, 11008, wd.index_count(42), batch=0)
+    desc = wd.make_desc(t.mode, t.rows, t.cols, t.max_shell, t.shape_bits, t.gain_bits)
+    packed = torch.from_numpy(t.packed).cuda()
+    scales = torch.from_numpy(t.scales_f16.copy()).cuda()
+    out = torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    args = (ctypes.byref(desc), ctypes.c_void_p(packed.data_ptr()), ctypes.c_void_p(scales.data_ptr()), wd.OUT_BF16,
+            ctypes.c_void_p(out.data_ptr()), None, ctypes.c_void_p(stream.cuda_stream))
+    sec, wall = time_steps(lambda i: lib.llvq_decode(*args), a.steps, a.warmup, stream)
+    blocks = t.rows * t.kb
+    weights = t.rows * t.cols
+    alg_bytes = blocks * t.field_bits / 8 + 2 * weights
+    res = base_line("LLVQ decode-to-bf16 throughput at 3 bits per weight, 1 MI355X", weights / sec, "weights/s",
+                    a.steps, a.warmup, sec, "f32",
+                    "llvq_decode bf16, 4096x11008, 68+4-bit fields (shells 2..42), general decoder",
+                    {"rows": t.rows, "cols": t.cols, "blocks": blocks, "field_bits": t.field_bits, "max_shell": 42})
+    res["roofline"] = roofline("decode_3bit", blocks, sec, alg_bytes,
+                               "9 B packed index read + 48 B bf16 written per 24-weight block")
+    res["wall_s_timed"] = wall
+    return res
 
 
 def run_roundtrip(a):
@@ -589,7 +627,7 @@ def run_gptq(a):
 
 DEFAULT_WORKLOAD = "gemv_4096x11008"
 WORKLOADS = ("gemv_4096x11008", "gemv_11008x4096", "gemv_4096x4096", "gemv_28672x8192", "decode_bf16_7b",
-             "roundtrip", "search", "fidelity", "gptq", "gemv_3bit_4096x11008")
+             "roundtrip", "search", "fidelity", "gptq", "gemv_3bit_4096x11008", "decode_3bit_4096x11008")
 
 
 def main():
@@ -659,6 +697,8 @@ def main():
                        f"llvq_gemv 3-bit shape-gain 4096x11008 (68+4-bit fields, shells 2..42), batch {a.batch}")
     elif w == "decode_bf16_7b":
         out = run_decode_7b(a)
+    elif w == "decode_3bit_4096x11008":
+        out = run_decode_3bit(a)
     elif w == "search":
         out = run_search(a)
     elif w == "fidelity":

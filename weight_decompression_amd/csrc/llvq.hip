@@ -686,12 +686,14 @@ int decode_wide(const llvq_desc* d, const void* packed, const void* scales, int3
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint64_t nblocks = (uint64_t)w.rows * (uint64_t)w.kb;
   const unsigned grid = grid_for(nblocks, kWideThreads);
+  const bool ovec = aligned(out, 16) && (w.cols % 8) == 0;
   if (out_kind == LLVQ_OUT_POINTS_I8)
     hipLaunchKernelGGL((k_decode_wide<LLVQ_OUT_POINTS_I8>), dim3(grid), dim3(kWideThreads), 0, s, w,
-                       static_cast<const uint8_t*>(packed), nullptr, out, err_count);
+                       static_cast<const uint8_t*>(packed), nullptr, out, err_count, false);
   else
     hipLaunchKernelGGL((k_decode_wide<LLVQ_OUT_BF16>), dim3(grid), dim3(kWideThreads), 0, s, w,
-                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), out, err_count);
+                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), out, err_count,
+                       ovec);
   return launch_status();
 }
 

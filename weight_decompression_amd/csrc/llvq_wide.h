@@ -293,10 +293,12 @@ __device__ __forceinline__ bool wide_block(const WDesc& d, const uint8_t* __rest
   return !u128_le(d.count_lo, d.count_hi, lo, hi);     // I < count
 }
 
+// ovec (bf16): the output and its rows are 16-byte aligned, so a full block's 24 weights
+// leave as three 16-byte stores
 template <int OUT>
 __global__ __launch_bounds__(kWideThreads) void k_decode_wide(WDesc d, const uint8_t* __restrict__ packed,
                                                               const __half* __restrict__ scales,
-                                                              void* __restrict__ out, int32_t* err) {
+                                                              void* __restrict__ out, int32_t* err, bool ovec) {
   const uint64_t nblocks = (uint64_t)d.rows * (uint64_t)d.kb;
   for (uint64_t j = (uint64_t)blockIdx.x * kWideThreads + threadIdx.x; j < nblocks;
        j += (uint64_t)gridDim.x * kWideThreads) {
@@ -325,9 +327,21 @@ __global__ __launch_bounds__(kWideThreads) void k_decode_wide(WDesc d, const uin
                            : __half2float(scales[r]);
       uint16_t* o = static_cast<uint16_t*>(out) + r * (uint64_t)d.cols + (uint64_t)b * kDim;
       const int lim = min(kDim, d.cols - b * kDim);
+      if (ovec && lim == kDim) {
+        uint32_t w[12];
 #pragma unroll
-      for (int p = 0; p < kDim; ++p)
-        if (p < lim) o[p] = f32_to_bf16_rne(__fmul_rn((float)v[p], sc));
+        for (int q = 0; q < 12; ++q)
+          w[q] = (uint32_t)f32_to_bf16_rne(__fmul_rn((float)v[2 * q], sc)) |
+                 ((uint32_t)f32_to_bf16_rne(__fmul_rn((float)v[2 * q + 1], sc)) << 16);
+        uint4* o4 = reinterpret_cast<uint4*>(o);
+        o4[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        o4[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        o4[2] = make_uint4(w[8], w[9], w[10], w[11]);
+      } else {
+#pragma unroll
+        for (int p = 0; p < kDim; ++p)
+          if (p < lim) o[p] = f32_to_bf16_rne(__fmul_rn((float)v[p], sc));
+      }
     }
   }
 }
