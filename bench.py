@@ -49,47 +49,47 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
+        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
         "valu_lane_ops_per_unit": 670.3,       # SQ_INSTS_VALU * 64 / blocks
-        "fetch_bytes_per_launch": 12228484,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "fetch_bytes_per_launch": 12222331,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
+        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
         "valu_lane_ops_per_unit": 695.4,
-        "fetch_bytes_per_launch": 61908339,
+        "fetch_bytes_per_launch": 61917531,
         "write_bytes_per_launch": 1835008,
     },
     "gemv_3bit_b1": {
-        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
+        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
         "summary": "profiles/gemv_3bit_4096x11008_batch1_k_gemv_wide.md",
         "unit_of_work": "24-weight block (k_gemv_wide)",
         "valu_lane_ops_per_unit": 3696.2,
-        "fetch_bytes_per_launch": 32838808,
-        "write_bytes_per_launch": 32769,
+        "fetch_bytes_per_launch": 32877490,
+        "write_bytes_per_launch": 32768,
     },
     "decode_3bit": {
-        "source_sha256": "0000000000000000000000000000000000000000000000000000000000000000",
+        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
         "summary": "profiles/decode_bf16_3bit_4096x11008_k_decode_wide.md",
         "unit_of_work": "24-weight block (k_decode_wide<bf16>)",
-        "valu_lane_ops_per_unit": 0,
-        "fetch_bytes_per_launch": 0,
-        "write_bytes_per_launch": 0,
+        "valu_lane_ops_per_unit": 3389.7,
+        "fetch_bytes_per_launch": 38061810,
+        "write_bytes_per_launch": 90295866,
     },
     "decode_bf16": {
-        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
+        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
         "summary": "profiles/decode_bf16_7b_k_decode_many.md",
         "unit_of_work": "24-weight block (k_decode_many<bf16>)",
         "valu_lane_ops_per_unit": 738.4,
-        "fetch_bytes_per_launch": 103305929,           # one launch = two layers (14 tensors)
+        "fetch_bytes_per_launch": 103320234,           # one launch = two layers (14 tensors)
         "write_bytes_per_launch": 809500672,
     },
     "roundtrip": {
-        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
+        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
         "summary": "profiles/roundtrip_1e7_k_decode_tile_k_rank.md",
         "unit_of_work": "point: decode to int8 (626.0) + rank (951.2)",
         "valu_lane_ops_per_unit": 1577.2,
@@ -97,7 +97,7 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": None,
     },
     "search": {
-        "source_sha256": "7da66c15a4513d83340d41f195d9418ab5e7dc7fa8ae2b54d61b2f7b6c7d9714",
+        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
         "summary": "profiles/search_4096x4096_k_search_k_rank.md",
         # The search issues more VALU instructions per clock than one per CU (mostly fp32
         # add / fma / max, which issue at up to 1.46 wave-instructions per CU per clock on
