@@ -107,9 +107,11 @@ def _even_point(x, cl, c):
     return v
 
 
-def class_scores(x, M):
-    """For every class of shells 2..M: (best <x,v> in the class, list of codeword
-    positions in T attaining it).  Exhaustive over codewords."""
+def codeword_scores(x, M):
+    """For every class of shells 2..M: (class, position in T of its first usable codeword,
+    array of the best <x, v> over the class's points that use each usable codeword, in
+    table order).  Odd classes use all 4096 codewords, even classes the A codewords of
+    weight w."""
     P = _prep(M)
     x = np.asarray(x, dtype=np.float64)
     ax = np.abs(x)
@@ -141,6 +143,15 @@ def class_scores(x, M):
             if cl.w < DIM:
                 scores = scores + comp_abs @ np.array(cl.complement_values, dtype=np.float64)
             base = golay.weight_offset()[cl.w]
+        out.append((cl, base, scores))
+    return out
+
+
+def class_scores(x, M):
+    """For every class of shells 2..M: (best <x,v> in the class, list of codeword
+    positions in T attaining it).  Exhaustive over codewords."""
+    out = []
+    for _cl, base, scores in codeword_scores(x, M):
         best = scores.max()
         winners = [int(base + j) for j in np.nonzero(scores == best)[0]]
         out.append((float(best), winners))

@@ -56,3 +56,46 @@ def test_feedback_lowers_the_layer_error():
         losses[variant] = gptq.proxy_loss(W, gptq.reconstruct(idx, gi, 10, gains), H)
     assert losses["spherical"] < 0.9 * losses["direct"], losses
     assert losses["euclid"] < 0.9 * losses["direct"], losses
+
+
+def test_two_block_step_by_hand_fixes_the_retraction():
+    # A hand-worked two-block layer (one row, K = 48) whose feedback is known in closed
+    # form.  With H = [[2I, -I], [-I, I]] (damp 0), H^-1 = [[I, I], [I, 2I]], so
+    # U = chol(H^-1)^T = [[I, I], [0, I]]: U_SS = I and U_SF = I, and fixing block 0 with
+    # error E moves block 1 to w1 - E.
+    #   block 0: w0 = (3.5, 2.5, 0, ...); its nearest direction is (1, 1)/sqrt 2 (the
+    #            shell-2 point (4, 4, 0, ...)), |w0| = sqrt 18.5.
+    #   spherical: w_hat = |w0| v/|v| = sqrt 9.25 (1, 1)       -> E = (0.45862, -0.54138)
+    #   euclid:    w_hat = G[g] v/|v| with G[g] = 2 (nearest gain) -> E = (2.08579, 1.08579)
+    #   direct:    no feedback.
+    #   block 1: w1 = (0.5, 0.5, 0, ...) becomes (0.04138, 1.04138) (spherical), nearest
+    #            direction (0, 8, 0, ...) (shell 4); (-1.58579, -0.58579) (euclid), nearest
+    #            direction (-12, -4, 0, ...) (shell 10, 1.84 degrees off); or stays
+    #            (0.5, 0.5) (direct): (4, 4, 0, ...).
+    # (papernotes.org page, 关键设计 3: the candidate is rescaled to the block's norm
+    # before its residual is fed back.)
+    from oracle import bijection
+    I24 = np.eye(24)
+    H = np.block([[2 * I24, -I24], [-I24, I24]])
+    U = gptq.inverse_hessian_factor(H, 0.0)
+    assert np.allclose(U, np.block([[I24, I24], [0 * I24, I24]]), atol=1e-12)
+    W = np.zeros((1, 48))
+    W[0, 0:2] = (3.5, 2.5)
+    W[0, 24:26] = (0.5, 0.5)
+    gains = np.array([0.25, 0.5, 1.0, 2.0], dtype=np.float16)
+
+    def pt(**kv):
+        v = [0] * 24
+        for k, a in kv.items():
+            v[int(k[1:])] = a
+        return v
+
+    v0 = pt(p0=4, p1=4)
+    want = {"spherical": (pt(p1=8), 2),      # |(0.04138, 1.04138)| = 1.0422 -> gain 1.0
+            "euclid": (pt(p0=-12, p1=-4), 3),  # |(-1.58579, -0.58579)| = 1.6905 -> gain 2.0
+            "direct": (pt(p0=4, p1=4), 1)}   # |(0.5, 0.5)| = 0.7071 -> gain 0.5
+    for variant, (v1, g1) in want.items():
+        idx, gi = gptq.gptq(W, H, 10, gains, damp=0.0, variant=variant)
+        assert int(idx[0, 0]) == bijection.rank(v0, 10) and int(gi[0, 0]) == 3, variant
+        assert int(idx[0, 1]) == bijection.rank(v1, 10), variant
+        assert int(gi[0, 1]) == g1, variant

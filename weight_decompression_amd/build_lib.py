@@ -39,13 +39,23 @@ def _run(cmd, verbose):
 
 
 def build_tables(verbose=True):
+    """Compile the generator and write its outputs.  Every file is written under a name
+    private to this process and renamed into place, so concurrent builds (parallel test
+    workers) never read a half-written table or run a generator that is being linked."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    _run(["g++", "-O2", "-std=c++17", "-Wall", "-o", GEN_BIN, os.path.join(CSRC, "gen_tables.cpp")], verbose)
-    _run([GEN_BIN, "--header", TABLES_INC], verbose)
-    _run([GEN_BIN, "--json", TABLES_JSON], verbose)
-    _run([GEN_BIN, "--search", SEARCH_INC], verbose)
-    _run([GEN_BIN, "--wide", WIDE_INC], verbose)
-    _run([GEN_BIN, "--wide-json", WIDE_JSON], verbose)
+    tag = f".{os.getpid()}.tmp"
+    gen = GEN_BIN + tag
+    _run(["g++", "-O2", "-std=c++17", "-Wall", "-o", gen, os.path.join(CSRC, "gen_tables.cpp")], verbose)
+    try:
+        for flag, path in (("--header", TABLES_INC), ("--json", TABLES_JSON), ("--search", SEARCH_INC),
+                           ("--wide", WIDE_INC), ("--wide-json", WIDE_JSON)):
+            _run([gen, flag, path + tag], verbose)
+            os.replace(path + tag, path)
+        os.replace(gen, GEN_BIN)
+    finally:
+        for path in (gen,) + tuple(p + tag for p in (TABLES_INC, TABLES_JSON, SEARCH_INC, WIDE_INC, WIDE_JSON)):
+            if os.path.exists(path):
+                os.remove(path)
 
 
 def hipcc_path():
