@@ -111,6 +111,62 @@ def _stream(stream):
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+# ---------------------------------------------------------------------------
+# argument checks: every tensor handed to the library is a contiguous device tensor of
+# the right dtype and at least the size the call will touch, checked here before the
+# library is loaded or a kernel launched (a short, strided or host buffer would
+# otherwise become an out-of-bounds device access)
+
+def _tensor(t, name, dtypes=None, min_bytes=0, nullable=False):
+    import torch
+    if t is None:
+        if nullable:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    nbytes = t.numel() * t.element_size()
+    if nbytes < min_bytes:
+        raise ValueError(f"{name} holds {nbytes} bytes; the call needs at least {min_bytes}")
+
+
+def _blocks(desc):
+    if desc.rows <= 0 or desc.cols <= 0:
+        raise ValueError(f"descriptor needs rows > 0 and cols > 0: {desc!r}")
+    return desc.rows * ((desc.cols + 23) // 24)
+
+
+def _packed_nbytes(desc):
+    """Bytes of the packed stream (the layout of include/llvq.h: fields rounded up to a
+    16-byte multiple, plus 16 bytes that kernels may over-read)."""
+    from .synth import packed_nbytes
+    return packed_nbytes(_blocks(desc), desc.shape_bits + desc.gain_bits)
+
+
+def _scales_count(desc):
+    return desc.rows if desc.mode == MODE_EUCLID else (1 << max(desc.gain_bits, 0))
+
+
+def _check_decode_args(desc, packed, scales, out_kind, out, err_count, what="llvq_decode"):
+    import torch
+    _tensor(packed, f"{what}: packed", (torch.uint8, torch.int8), _packed_nbytes(desc))
+    _tensor(err_count, f"{what}: err_count", (torch.int32,), 4, nullable=True)
+    if out_kind == OUT_POINTS_I8:
+        _tensor(out, f"{what}: out", (torch.int8,), _blocks(desc) * 24)
+        _tensor(scales, f"{what}: scales", (torch.float16,), 0, nullable=True)
+    elif out_kind == OUT_BF16:
+        _tensor(out, f"{what}: out", (torch.bfloat16,), 2 * desc.rows * desc.cols)
+        _tensor(scales, f"{what}: scales", (torch.float16,), 2 * _scales_count(desc))
+    else:
+        raise ValueError(f"{what}: out_kind must be OUT_POINTS_I8 or OUT_BF16, got {out_kind}")
+
+
 def make_desc(mode, rows, cols, max_shell, shape_bits, gain_bits) -> Desc:
     return Desc(mode, rows, cols, max_shell, shape_bits, gain_bits)
 
@@ -132,6 +188,7 @@ def packed_bytes(desc: Desc) -> int:
 
 def decode(desc, packed, scales, out_kind, out, err_count=None, stream=None):
     """Decode all blocks into `out` (int8 points [rows][Kb*24] or bf16 [rows][cols])."""
+    _check_decode_args(desc, packed, scales, out_kind, out, err_count)
     _check(load_library().llvq_decode(ctypes.byref(desc), _ptr(packed), _ptr(scales), out_kind, _ptr(out),
                                       _ptr(err_count), _stream(stream)), "llvq_decode")
 
@@ -139,20 +196,35 @@ def decode(desc, packed, scales, out_kind, out, err_count=None, stream=None):
 def gemv(desc, packed, scales, x, y, err_count=None, stream=None):
     """y[b][r] = sum_k W_hat[r][k] x[b][k]; x is fp32 or bf16 [batch][cols], y fp32 [batch][rows]."""
     import torch
-    if x.dtype == torch.bfloat16:
-        xd = X_BF16
-    elif x.dtype == torch.float32:
-        xd = X_F32
-    else:
-        raise TypeError("x must be float32 or bfloat16")
+    _tensor(x, "llvq_gemv: x", (torch.float32, torch.bfloat16))
+    xd = X_BF16 if x.dtype == torch.bfloat16 else X_F32
+    if x.dim() not in (1, 2) or x.shape[-1] != desc.cols:
+        raise ValueError(f"llvq_gemv: x must be [batch][{desc.cols}] or [{desc.cols}], got {tuple(x.shape)}")
     batch = 1 if x.dim() == 1 else x.shape[0]
+    if not 1 <= batch <= MAX_BATCH:
+        raise ValueError(f"llvq_gemv: batch must be 1..{MAX_BATCH}, got {batch}")
+    _tensor(packed, "llvq_gemv: packed", (torch.uint8, torch.int8), _packed_nbytes(desc))
+    _tensor(scales, "llvq_gemv: scales", (torch.float16,), 2 * _scales_count(desc))
+    _tensor(y, "llvq_gemv: y", (torch.float32,), 4 * batch * desc.rows)
+    _tensor(err_count, "llvq_gemv: err_count", (torch.int32,), 4, nullable=True)
     _check(load_library().llvq_gemv(ctypes.byref(desc), _ptr(packed), _ptr(scales), _ptr(x), xd, batch, _ptr(y),
                                     _ptr(err_count), _stream(stream)), "llvq_gemv")
 
 
+def _check_points(points, indices, err_count, words, what):
+    import torch
+    _tensor(points, f"{what}: points", (torch.int8,))
+    if points.numel() % 24:
+        raise ValueError(f"{what}: points must hold whole 24-vectors, got {points.numel()} values")
+    n = points.numel() // 24
+    _tensor(indices, f"{what}: indices", (torch.int64,), 8 * words * n)
+    _tensor(err_count, f"{what}: err_count", (torch.int32,), 4, nullable=True)
+    return n
+
+
 def encode_ref(points, max_shell, indices, err_count=None, stream=None):
     """Rank int8 lattice points [n][24] into uint64 shape indices [n] (int64 tensor)."""
-    n = points.shape[0] if points.dim() > 1 else points.numel() // 24
+    n = _check_points(points, indices, err_count, 1, "llvq_encode_ref")
     _check(load_library().llvq_encode_ref(_ptr(points), n, max_shell, _ptr(indices), _ptr(err_count),
                                           _stream(stream)), "llvq_encode_ref")
 
@@ -161,7 +233,14 @@ def search(x, max_shell, objective, points, indices, err_count=None, stream=None
     """Nearest point of shells 2..max_shell to each fp32 24-vector x [n][24]
     (SEARCH_ANGULAR or SEARCH_EUCLID): int8 points [n][24] and uint64 indices [n]
     (int64 tensor) are written."""
-    n = x.shape[0] if x.dim() > 1 else x.numel() // 24
+    import torch
+    _tensor(x, "llvq_search: x", (torch.float32,))
+    if x.numel() % 24:
+        raise ValueError(f"llvq_search: x must hold whole 24-blocks, got {x.numel()} values")
+    n = x.numel() // 24
+    _tensor(points, "llvq_search: points", (torch.int8,), 24 * n)
+    _tensor(indices, "llvq_search: indices", (torch.int64,), 8 * n)
+    _tensor(err_count, "llvq_search: err_count", (torch.int32,), 4, nullable=True)
     _check(load_library().llvq_search(_ptr(x), n, max_shell, objective, _ptr(points), _ptr(indices),
                                       _ptr(err_count), _stream(stream)), "llvq_search")
 
@@ -176,12 +255,22 @@ def quantize_workspace_bytes(desc: Desc) -> int:
 def quantize(desc, w, scales, packed, workspace, err_count=None, stream=None):
     """Quantise fp32 weights w [rows][cols] into the packed stream (uint8 tensor of
     packed_bytes(desc) bytes); workspace: quantize_workspace_bytes(desc) bytes of device memory."""
+    import torch
+    n = _blocks(desc)
+    _tensor(w, "llvq_quantize: w", (torch.float32,), 4 * desc.rows * desc.cols)
+    _tensor(scales, "llvq_quantize: scales", (torch.float16,), 2 * _scales_count(desc))
+    _tensor(packed, "llvq_quantize: packed", (torch.uint8, torch.int8), _packed_nbytes(desc))
+    _tensor(workspace, "llvq_quantize: workspace", None, (24 * n + 7) // 8 * 8 + 8 * n)
+    _tensor(err_count, "llvq_quantize: err_count", (torch.int32,), 4, nullable=True)
     _check(load_library().llvq_quantize(ctypes.byref(desc), _ptr(w), _ptr(scales), _ptr(packed), _ptr(workspace),
                                         _ptr(err_count), _stream(stream)), "llvq_quantize")
 
 
 def pack_fields(desc, fields, packed, stream=None):
     """Write uint64 fields [rows * Kb] (int64 tensor) as the packed stream of desc."""
+    import torch
+    _tensor(fields, "llvq_pack_fields: fields", (torch.int64,), 8 * _blocks(desc))
+    _tensor(packed, "llvq_pack_fields: packed", (torch.uint8, torch.int8), _packed_nbytes(desc))
     _check(load_library().llvq_pack_fields(ctypes.byref(desc), _ptr(fields), _ptr(packed), _stream(stream)),
            "llvq_pack_fields")
 
@@ -189,6 +278,11 @@ def pack_fields(desc, fields, packed, stream=None):
 def decode_many(descs, packed, scales, out_kind, outs, err_count=None, stream=None):
     """llvq_decode of several tensors in one call (equal widths and shell range)."""
     n = len(descs)
+    if not (len(packed) == len(outs) == n and (scales is None or len(scales) == n)):
+        raise ValueError("llvq_decode_many: descs, packed, scales and outs need one entry per tensor")
+    for i in range(n):
+        _check_decode_args(descs[i], packed[i], None if scales is None else scales[i], out_kind, outs[i],
+                           err_count, f"llvq_decode_many[{i}]")
     darr = (Desc * n)(*descs)
     parr = (ctypes.c_void_p * n)(*[p.data_ptr() for p in packed])
     sarr = None if scales is None else (ctypes.c_void_p * n)(*[x.data_ptr() for x in scales])
@@ -201,6 +295,6 @@ def decode_many(descs, packed, scales, out_kind, outs, err_count=None, stream=No
 
 def encode_wide(points, max_shell, indices, err_count=None, stream=None):
     """llvq_encode_wide: int8 points [n][24] -> 128-bit indices as int64 pairs [n][2] (lo, hi)."""
-    n = points.shape[0] if points.dim() > 1 else points.numel() // 24
+    n = _check_points(points, indices, err_count, 2, "llvq_encode_wide")
     _check(load_library().llvq_encode_wide(_ptr(points), n, max_shell, _ptr(indices),
                                            _ptr(err_count), _stream(stream)), "llvq_encode_wide")
