@@ -131,15 +131,30 @@ def load_fidelity(which):
 
 
 def cpu_baseline(t, rows):
-    from oracle import cpu_baseline as cb
+    """The oracle GEMV of rows 0..rows-1 of tensor t, timed on the host cores: the baseline
+    dict and the oracle's fp64 (y, sum of |terms|) for the parity check."""
+    from oracle import cpu_baseline as cb, parallel
     row_list = list(range(rows))
     x = t.x_as_f64()
-    dt, procs = cb.time_gemv_rows(t.packed.tobytes(), t.rows, t.cols, t.max_shell, t.mode, t.shape_bits,
-                                  t.gain_bits, t.scales_f16, t.scales_f16, x, row_list)
+    dt, procs, y, mag = cb.time_gemv_rows(t.packed.tobytes(), t.rows, t.cols, t.max_shell, t.mode, t.shape_bits,
+                                          t.gain_bits, t.scales_f16, t.scales_f16, x, row_list)
     nbytes = rows * t.kb * t.field_bits / 8
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": procs, "kind": "oracle",
+    base = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": procs, "kind": "oracle",
+            "cpu_model": parallel.cpu_model(),
             "sample": f"rows 0..{rows - 1} of the same tensor ({rows * t.kb} blocks): pure-Python decode "
                       f"+ fp64 GEMV, {procs} processes, {dt:.2f} s wall"}
+    return base, y, mag
+
+
+def gemv_parity(y_gpu, y_ref, mag, rows_checked, what):
+    """Parity verdict of a GEMV output against the oracle: every checked output within
+    1e-4 of the fp64 result, normalised by the sum of |terms| of its row."""
+    import numpy as np
+    from oracle import reference
+    e = reference.normalized_errors(np.asarray(y_gpu, dtype=np.float64), y_ref, mag)
+    return {"what": what, "rows_checked": int(rows_checked), "outputs_checked": int(e.size),
+            "max_norm_err": float(e.max()), "tol": reference.GEMV_REL_TOL,
+            "pass": bool(np.all(reference.gemv_within_tolerance(y_gpu, y_ref, mag)))}
 
 
 def time_steps(launch, steps, warmup, stream):
@@ -237,8 +252,7 @@ def run_gemv(a, name, t, profile_key, label):
             for i in range(ncopies)]
     gemv = lib.llvq_gemv
     sec, wall = time_steps(lambda i: gemv(*args[i % ncopies]), a.steps, a.warmup, stream)
-    if not bool(torch.isfinite(y).all()):
-        raise RuntimeError("non-finite GEMV output")
+    y_host = y.cpu().numpy()
     packed_bytes = blocks * t.field_bits / 8
     alg_bytes = packed_bytes + xb * t.cols * batch + 4 * t.rows * batch
     out = base_line(METRIC if name == DEFAULT_WORKLOAD else
@@ -253,7 +267,19 @@ def run_gemv(a, name, t, profile_key, label):
     out["weights_per_s"] = t.rows * t.cols * batch / sec
     out["wall_s_timed"] = wall
     if name == DEFAULT_WORKLOAD and not a.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(t, min(a.cpu_rows, t.rows))
+        rows = min(a.cpu_rows, t.rows)
+        out["cpu_baseline"], y_ref, mag = cpu_baseline(t, rows)
+        out["parity"] = gemv_parity(y_host[:, :rows], y_ref, mag, rows,
+                                    f"rows 0..{rows - 1} of the timed output vs the fp64 oracle (cpu_baseline leg)")
+    else:
+        from oracle import parallel
+        rng = np.random.default_rng(7)
+        k = min(a.parity_rows, t.rows)
+        rows = sorted(set([0, t.rows - 1] + [int(r) for r in rng.choice(t.rows, k, replace=False)]))
+        y_ref, mag = parallel.gemv_rows(t.packed.tobytes(), t.rows, t.cols, t.max_shell, t.mode, t.shape_bits,
+                                        t.gain_bits, t.scales_f16, t.scales_f16, t.x_as_f64(), rows)
+        out["parity"] = gemv_parity(y_host[:, rows], y_ref, mag, len(rows),
+                                    f"{len(rows)} seeded rows of the timed output vs the fp64 oracle")
     return out
 
 
@@ -267,6 +293,7 @@ def run_decode_7b(a):
     C10 = wd.index_count(10)
     layers = a.layers
     items = []
+    host = []
     blocks = 0
     weights = 0
     for L in range(layers):
@@ -277,6 +304,8 @@ def run_decode_7b(a):
             scales = torch.from_numpy(t.scales_f16.copy()).cuda()
             out = torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device="cuda:0")
             items.append((desc, packed, scales, out))
+            host.append((t.packed.tobytes(), t.rows, t.cols, t.max_shell, t.mode, t.shape_bits, t.gain_bits,
+                         t.scales_f16, None))
             blocks += t.rows * t.kb
             weights += t.rows * t.cols
         print(f"bench: layer {L} generated", file=sys.stderr, flush=True)
@@ -322,6 +351,18 @@ def run_decode_7b(a):
     out["roofline"] = roofline("decode_bf16", blocks, sec, alg_bytes,
                                "6 B packed index read + 48 B bf16 written per 24-weight block", launches=len(calls))
     out["wall_s_timed"] = wall
+    # parity: two seeded rows of every tensor, bit for bit against the oracle's bf16 decode
+    import numpy as np
+    from oracle import parallel
+    rng = np.random.default_rng(5)
+    pairs = [(i, int(r)) for i in range(len(items)) for r in rng.choice(items[i][0].rows, 2, replace=False)]
+    want = parallel.decode_rows_bf16_many(host, pairs)
+    bad = 0
+    for (i, r), ref in zip(pairs, want):
+        got = items[i][3][r].view(torch.int16).cpu().numpy().view(np.uint16)
+        bad += int(not np.array_equal(got, ref))
+    out["parity"] = {"what": "2 seeded rows of each of the tensors, bf16 bit patterns vs the oracle",
+                     "rows_checked": len(pairs), "rows_differing": bad, "pass": bad == 0}
     return out
 
 
@@ -370,6 +411,8 @@ def run_roundtrip(a):
     n = rows * kb
     idx = synth.workload5_roundtrip_indices(C10, n)
     packed = synth.pack_fields(idx, 48)
+    sample = np.random.default_rng(6).choice(n, min(a.parity_points, n), replace=False)
+    sample_idx = idx[sample]
     del idx
     desc = wd.make_desc(wd.MODE_SHAPEGAIN, rows, kb * 24, 10, 44, 4)
     pk = torch.from_numpy(packed).cuda()
@@ -398,6 +441,12 @@ def run_roundtrip(a):
                     f"llvq_decode points + llvq_encode_ref, {n} uniform indices over shells 2..10",
                     {"points": n})
     out["round_trip_exact"] = ok
+    from oracle import parallel
+    want = parallel.unrank_many(sample_idx, 10)
+    got = pts[torch.from_numpy(sample).cuda()].cpu().numpy().astype(np.int64)
+    out["parity"] = {"what": f"{len(sample)} seeded points of the timed decode vs the oracle's unrank, and every "
+                             f"index equal after the rank", "points_checked": int(len(sample)),
+                     "round_trip_exact": ok, "pass": bool(ok and np.array_equal(got, want))}
     out["roofline"] = roofline("roundtrip", n, sec, n * (6 + 24 + 24 + 8),
                                "6 B index read + 24 B point written (decode); 24 B read + 8 B written (rank)")
     out["wall_s_timed"] = wall
@@ -647,6 +696,9 @@ def main():
     ap.add_argument("--cpu-blocks", type=int, default=2048, help="blocks the CPU oracle search is timed on (search)")
     ap.add_argument("--fidelity-blocks", type=int, default=262144, help="Gaussian source blocks (fidelity)")
     ap.add_argument("--cpu-rows-gptq", type=int, default=8, help="rows the CPU oracle GPTQ is timed on (gptq)")
+    ap.add_argument("--parity-rows", type=int, default=256, help="oracle-checked rows (GEMV workloads other than "
+                    "the headline, which checks the cpu_baseline rows)")
+    ap.add_argument("--parity-points", type=int, default=20000, help="oracle-checked points (roundtrip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB mebibytes (HBM counter calibration)")
     a = ap.parse_args()
@@ -708,6 +760,9 @@ def main():
     else:
         out = run_roundtrip(a)
     print(json.dumps(out), flush=True)
+    if "parity" in out and not out["parity"]["pass"]:
+        print("bench.py: the timed output does not match the oracle", file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

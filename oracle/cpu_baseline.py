@@ -1,38 +1,42 @@
 """Timed CPU oracle run used as the reported CPU baseline of the benchmark.
 
-Runs the oracle exactly as it stands (decode every block of the sampled rows with the
-pure-Python bijection, then the fp64 dot products; oracle/reference.py) in a process
-pool over rows, and reports the wall time.  It is a reported baseline, not a target.
+Test infrastructure: only the benchmark's CPU-baseline leg uses it.  Runs the oracle
+exactly as it stands (decode every block of the sampled rows with the pure-Python
+bijection, then the fp64 dot products; oracle/reference.py) in a process pool over rows
+(at most 16 processes: a GPU machine's CPU share), and reports the wall time.  It is a
+reported baseline, not a target.
 """
 
 import multiprocessing as mp
-import os
 import time
 
-from . import reference
+import numpy as np
 
-
-def _rows(args):
-    packed, rows, cols, M, mode, sb, gb, gains, scales, x, row_list = args
-    reference.gemv(packed, rows, cols, M, mode, sb, gb, gains, scales, x, row_list)
-    return len(row_list)
+from . import parallel
 
 
 def time_gemv_rows(packed, rows, cols, M, mode, shape_bits, gain_bits, gains, row_scales, x, row_list,
                    procs=None):
-    """Wall seconds for the oracle GEMV of `row_list`, and the number of processes used."""
-    procs = procs or os.cpu_count() or 1
+    """Wall seconds for the oracle GEMV of `row_list` over a process pool (oracle/parallel.py),
+    the number of processes used, and the oracle's fp64 (y [batch][len(row_list)], sum of
+    |terms| of the same shape), so the caller can check its own output against it."""
+    procs = procs or parallel.cores()
     procs = max(1, min(procs, len(row_list)))
-    chunks = [row_list[i::procs] for i in range(procs)]
-    args = [(packed, rows, cols, M, mode, shape_bits, gain_bits, gains, row_scales, x, c) for c in chunks if c]
-    ctx = mp.get_context("fork")
-    with ctx.Pool(len(args)) as pool:
-        pool.map(_rows, [(packed, rows, cols, M, mode, shape_bits, gain_bits, gains, row_scales, x, [row_list[0]])])
-        t0 = time.perf_counter()
-        done = sum(pool.map(_rows, args))
-        dt = time.perf_counter() - t0
-    assert done == len(row_list)
-    return dt, len(args)
+    chunks = parallel._chunks(row_list, procs)
+    parallel._JOB = (bytes(packed), rows, cols, M, mode, shape_bits, gain_bits, gains, row_scales,
+                     np.atleast_2d(x))
+    try:
+        with mp.get_context("fork").Pool(procs) as pool:
+            pool.map(parallel._gemv_chunk, [[row_list[0]]] * procs)      # start every worker
+            t0 = time.perf_counter()
+            parts = pool.map(parallel._gemv_chunk, chunks)
+            dt = time.perf_counter() - t0
+    finally:
+        parallel._JOB = None
+    y = np.concatenate([p[0] for p in parts], axis=1)
+    mag = np.concatenate([p[1] for p in parts], axis=1)
+    assert y.shape[1] == len(row_list)
+    return dt, procs, y, mag
 
 
 def _search_chunk(args):
@@ -46,7 +50,7 @@ def _search_chunk(args):
 def time_search(blocks, M, mode, procs=None):
     """Wall seconds for the oracle's exact search (oracle/search.py) of every block in
     `blocks` (float64 [n][24]) over a process pool, and the number of processes used."""
-    procs = procs or os.cpu_count() or 1
+    procs = procs or parallel.cores()
     procs = max(1, min(procs, len(blocks)))
     chunks = [blocks[i::procs] for i in range(procs)]
     ctx = mp.get_context("fork")

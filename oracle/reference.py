@@ -106,17 +106,29 @@ def bf16_bits_to_f32(b) -> np.ndarray:
     return b.view(np.float32)
 
 
+def block_f32(I, g, M, mode, gains, row_scale):
+    """fp32 values of one decoded block before the bf16 rounding: f32(v) * f32 scale, the
+    scale being f32(G[g]) * f32(1/(4 sqrt m)) (shape-gain) or the row's scale (Euclidean)."""
+    v = np.array(unrank(I, M), dtype=np.float32)
+    if mode == MODE_SHAPEGAIN:
+        m = find_class(I, M).m
+        scale = np.float32(np.float32(gains[g]) * inv_norm_f32(m))
+    else:
+        scale = np.float32(row_scale)
+    return v * scale
+
+
+def block_bf16(I, g, M, mode, gains, row_scale):
+    """bf16 bit patterns of one decoded block (all 24 values, pad columns included)."""
+    return f32_to_bf16_bits(block_f32(I, g, M, mode, gains, row_scale))
+
+
 def decode_row_bf16(packed, rows, cols, M, mode, shape_bits, gain_bits, gains, row_scales, row):
     """bf16 bit patterns of one decoded row, shape [cols] (pad columns dropped)."""
     vals = np.empty(blocks_per_row(cols) * DIM, dtype=np.float32)
+    rs = None if row_scales is None else row_scales[row]
     for b, (I, g) in enumerate(block_fields(packed, rows, cols, shape_bits, gain_bits, row)):
-        v = np.array(unrank(I, M), dtype=np.float32)
-        if mode == MODE_SHAPEGAIN:
-            m = find_class(I, M).m
-            scale = np.float32(np.float32(gains[g]) * inv_norm_f32(m))
-        else:
-            scale = np.float32(row_scales[row])
-        vals[b * DIM:(b + 1) * DIM] = v * scale
+        vals[b * DIM:(b + 1) * DIM] = block_f32(I, g, M, mode, gains, rs)
     return f32_to_bf16_bits(vals[:cols])
 
 
