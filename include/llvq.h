@@ -59,7 +59,8 @@ enum {
   LLVQ_OK = 0,
   LLVQ_EINVAL = -1,        /* invalid argument (null pointer, bad size, bad descriptor) */
   LLVQ_EUNSUPPORTED = -2,  /* valid request this build does not implement              */
-  LLVQ_EHIP = -3           /* the HIP runtime reported an error at launch              */
+  LLVQ_EHIP = -3,          /* the HIP runtime reported an error at launch              */
+  LLVQ_ETOOLARGE = -4      /* more blocks than llvq_quantize_noalloc's fixed workspace */
 };
 
 enum { LLVQ_MODE_EUCLID = 0, LLVQ_MODE_SHAPEGAIN = 1 };
@@ -230,6 +231,25 @@ int64_t llvq_quantize_workspace_bytes(const llvq_desc* d);
  * call allocates nothing.  Returns LLVQ_OK, LLVQ_EINVAL or LLVQ_EHIP. */
 int llvq_quantize(const llvq_desc* d, const float* w, const void* scales, void* packed, void* workspace,
                   int32_t* err_count, void* stream);
+
+/* llvq_quantize for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and the
+ * same output, with the workspace held by the library instead of passed in.
+ *   d, w, scales, packed, err_count, stream : as for llvq_quantize.
+ * The workspace is a file-scope device array of llvq_quantize_noalloc_max_blocks() x 32
+ * bytes (2^21 blocks, 64 MiB) that every GPU the library runs on holds until the process
+ * ends; its device address is looked up once per GPU (with that GPU current) on the first
+ * call that uses it.  Nothing in it has to start at zero: each call writes what it reads.
+ * All calls on one GPU share the array, so calls that overlap on one GPU (several streams
+ * or host threads at once) race and give undefined streams; serialise them.
+ * The call allocates nothing (no hipMalloc / hipFree, no allocating library routine).
+ * Returns LLVQ_ETOOLARGE (before any launch) when rows * Kb exceeds the maximum, else as
+ * llvq_quantize (LLVQ_EHIP also when the array's address cannot be obtained). */
+int llvq_quantize_noalloc(const llvq_desc* d, const float* w, const void* scales, void* packed,
+                          int32_t* err_count, void* stream);
+
+/* The most blocks (rows * Kb) llvq_quantize_noalloc accepts.  Host only. */
+int64_t llvq_quantize_noalloc_max_blocks(void);
 
 /* Write finished fields as the packed stream (the layout of llvq_decode's input): for
  * quantisers that choose the indices themselves (e.g. with error feedback between blocks).

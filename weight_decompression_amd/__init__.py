@@ -19,14 +19,16 @@ SEARCH_ANGULAR = 0
 SEARCH_EUCLID = 1
 MAX_BATCH = 16
 
-_ERRORS = {0: "ok", -1: "invalid argument", -2: "unsupported request", -3: "HIP launch error"}
+_ERRORS = {0: "ok", -1: "invalid argument", -2: "unsupported request", -3: "HIP launch error",
+           -4: "request larger than the library's fixed workspace"}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllvq.so")
 
 EXPORTED_SYMBOLS = ("llvq_index_count", "llvq_packed_bytes", "llvq_error_string",
                     "llvq_decode", "llvq_gemv", "llvq_encode_ref", "llvq_search", "llvq_quantize_workspace_bytes",
                     "llvq_quantize", "llvq_pack_fields", "llvq_decode_many",
-                    "llvq_index_count_wide", "llvq_encode_wide")
+                    "llvq_index_count_wide", "llvq_encode_wide", "llvq_quantize_noalloc",
+                    "llvq_quantize_noalloc_max_blocks")
 
 
 class LlvqError(RuntimeError):
@@ -87,6 +89,10 @@ def load_library(path=LIB_PATH):
     lib.llvq_quantize_workspace_bytes.restype = i64
     lib.llvq_quantize.argtypes = [dp, vp, vp, vp, vp, vp, vp]
     lib.llvq_quantize.restype = ctypes.c_int
+    lib.llvq_quantize_noalloc.argtypes = [dp, vp, vp, vp, vp, vp]
+    lib.llvq_quantize_noalloc.restype = ctypes.c_int
+    lib.llvq_quantize_noalloc_max_blocks.argtypes = []
+    lib.llvq_quantize_noalloc_max_blocks.restype = i64
     lib.llvq_pack_fields.argtypes = [dp, vp, vp, vp]
     lib.llvq_pack_fields.restype = ctypes.c_int
     lib.llvq_decode_many.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp]
@@ -264,6 +270,22 @@ def quantize(desc, w, scales, packed, workspace, err_count=None, stream=None):
     _tensor(err_count, "llvq_quantize: err_count", (torch.int32,), 4, nullable=True)
     _check(load_library().llvq_quantize(ctypes.byref(desc), _ptr(w), _ptr(scales), _ptr(packed), _ptr(workspace),
                                         _ptr(err_count), _stream(stream)), "llvq_quantize")
+
+
+def quantize_noalloc(desc, w, scales, packed, err_count=None, stream=None):
+    """quantize() without a workspace argument: the library's own fixed device array is used
+    (at most quantize_noalloc_max_blocks() blocks; calls that overlap on one GPU race)."""
+    import torch
+    _tensor(w, "llvq_quantize_noalloc: w", (torch.float32,), 4 * desc.rows * desc.cols)
+    _tensor(scales, "llvq_quantize_noalloc: scales", (torch.float16,), 2 * _scales_count(desc))
+    _tensor(packed, "llvq_quantize_noalloc: packed", (torch.uint8, torch.int8), _packed_nbytes(desc))
+    _tensor(err_count, "llvq_quantize_noalloc: err_count", (torch.int32,), 4, nullable=True)
+    _check(load_library().llvq_quantize_noalloc(ctypes.byref(desc), _ptr(w), _ptr(scales), _ptr(packed),
+                                                _ptr(err_count), _stream(stream)), "llvq_quantize_noalloc")
+
+
+def quantize_noalloc_max_blocks() -> int:
+    return int(load_library().llvq_quantize_noalloc_max_blocks())
 
 
 def pack_fields(desc, fields, packed, stream=None):

@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "llvq.h"
 #include "llvq_tables.h"
 
@@ -466,6 +468,7 @@ LLVQ_API const char* llvq_error_string(int code) {
     case LLVQ_EINVAL: return "invalid argument";
     case LLVQ_EUNSUPPORTED: return "unsupported request";
     case LLVQ_EHIP: return "HIP launch error";
+    case LLVQ_ETOOLARGE: return "request larger than the library's fixed workspace (llvq_quantize_noalloc)";
     default: return "unknown error code";
   }
 }
@@ -961,14 +964,12 @@ LLVQ_API int64_t llvq_quantize_workspace_bytes(const llvq_desc* d) {
   return (int64_t)(quantize_points_bytes(k) + (uint64_t)k.rows * (uint64_t)k.kb * 8u);
 }
 
-LLVQ_API int llvq_quantize(const llvq_desc* d, const float* w, const void* scales, void* packed, void* workspace,
-                           int32_t* err_count, void* stream) {
-  KDesc k;
-  const int st = make_kdesc_quant(d, &k);
-  if (st != LLVQ_OK) return st;
-  if (!w || !scales || !packed || !workspace) return LLVQ_EINVAL;
-  if (!aligned(w, 4) || !aligned(scales, 2) || !aligned(packed, 16) || !aligned(workspace, 8)) return LLVQ_EINVAL;
-  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+namespace {
+// The quantiser's steps on a workspace of llvq_quantize_workspace_bytes: k_search writes
+// the chosen points, the rank writes their indices, k_pack the fields.  Every byte of the
+// workspace that a later step reads is written by an earlier step of the same call.
+int quantize_into(const KDesc& k, const float* w, const void* scales, void* packed, void* workspace,
+                  int32_t* err_count, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t n = (int64_t)k.rows * (int64_t)k.kb;
   int8_t* pts = static_cast<int8_t*>(workspace);
@@ -990,6 +991,74 @@ LLVQ_API int llvq_quantize(const llvq_desc* d, const float* w, const void* scale
                      static_cast<uint32_t*>(packed), nwords);
   return launch_status();
 }
+
+int check_quantize_args(const KDesc& k, const float* w, const void* scales, const void* packed, int32_t* err_count) {
+  (void)k;
+  if (!w || !scales || !packed) return LLVQ_EINVAL;
+  if (!aligned(w, 4) || !aligned(scales, 2) || !aligned(packed, 16)) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  return LLVQ_OK;
+}
+
+// Workspace of llvq_quantize_noalloc, owned by the library: the points and indices of at
+// most kNoAllocBlocks blocks (24 + 8 bytes each, 64 MiB).  Each GPU holds its own copy
+// from the library's load until the process ends.  In host code the array's name is not
+// a device address: kernels get the address hipGetSymbolAddress returns for the device.
+constexpr uint64_t kNoAllocBlocks = 1ull << 21;
+constexpr uint64_t kNoAllocBytes = kNoAllocBlocks * 32u;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that `stream` belongs to, looked up once per
+// device with that device current.
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = -1, cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return LLVQ_EHIP;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return LLVQ_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return LLVQ_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return LLVQ_EHIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return LLVQ_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LLVQ_OK;
+}
+}  // namespace
+
+LLVQ_API int llvq_quantize(const llvq_desc* d, const float* w, const void* scales, void* packed, void* workspace,
+                           int32_t* err_count, void* stream) {
+  KDesc k;
+  const int st = make_kdesc_quant(d, &k);
+  if (st != LLVQ_OK) return st;
+  const int st2 = check_quantize_args(k, w, scales, packed, err_count);
+  if (st2 != LLVQ_OK) return st2;
+  if (!workspace || !aligned(workspace, 8)) return LLVQ_EINVAL;
+  return quantize_into(k, w, scales, packed, workspace, err_count, stream);
+}
+
+LLVQ_API int llvq_quantize_noalloc(const llvq_desc* d, const float* w, const void* scales, void* packed,
+                                   int32_t* err_count, void* stream) {
+  KDesc k;
+  const int st = make_kdesc_quant(d, &k);
+  if (st != LLVQ_OK) return st;
+  const int st2 = check_quantize_args(k, w, scales, packed, err_count);
+  if (st2 != LLVQ_OK) return st2;
+  if ((uint64_t)k.rows * (uint64_t)k.kb > kNoAllocBlocks) return LLVQ_ETOOLARGE;
+  void* ws = nullptr;
+  const int st3 = scratch_address(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (st3 != LLVQ_OK) return st3;
+  return quantize_into(k, w, scales, packed, ws, err_count, stream);
+}
+
+LLVQ_API int64_t llvq_quantize_noalloc_max_blocks(void) { return (int64_t)kNoAllocBlocks; }
 
 LLVQ_API int llvq_pack_fields(const llvq_desc* d, const uint64_t* fields, void* packed, void* stream) {
   KDesc k;
