@@ -91,6 +91,7 @@ struct EArgs {
   ELayout L;
   uint32_t xs;     // GEMV: x, kb*24 elements (fp32 or bf16), zero padded
   uint32_t xsum;   // GEMV: float[kb], sum of the 24 x values of each block column
+  uint32_t rings;  // batch-1 GEMV: the waves' ring queues, then the shared leftover queue
 };
 
 // ---------------------------------------------------------------------------
@@ -243,6 +244,24 @@ struct OddDec {
     }
     return __builtin_amdgcn_perm(svhi, svlo, k);
   }
+
+  // The batch-1 GEMV's form: the fp8 value table (load_fp8) and, per position, the value's
+  // selector into it (byte 0: slot 0..3, + 4 off the codeword; bytes 1-3: 0x0c) instead of
+  // the value itself, so that two positions share one v_perm.
+  __device__ __forceinline__ void load_fp8(const LlvqClassHot& h) {
+    svlo = h.sv0lo8;
+    svhi = h.sv0hi8;
+  }
+
+  __device__ __forceinline__ uint32_t slot(const uint8_t* smem, const ELayout& L, int p) {
+    const uint32_t sel = ((notc4 >> p) & 4u) | 0x0c0c0c00u;
+    if (p < kSteps) {
+      const uint32_t k = decode_step(smem, y, nc, cnt8, sel, kFRow * (uint32_t)p).k;
+      if (p == kSteps - 1) codes = tail_codes(smem, L, cnt8, y);
+      return k;
+    }
+    return __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | sel;
+  }
 };
 
 // Even coset: support values (on the codeword's positions, ascending) then complement
@@ -314,6 +333,48 @@ struct EvenDec {
     pos = (uint32_t)__builtin_ctz(m);
     m &= m - 1u;
     return __builtin_amdgcn_perm(svhi, svlo, kb + (neg << 2));
+  }
+
+  // The batch-1 GEMV's form (see OddDec::slot): fp8 tables, and the selector of the i-th
+  // decoded value (byte 0: slot 0..3, + 4 when negative; bytes 1-3: 0x0c) with its position.  A two-part class
+  // switches to the complement's fp8 table at an even i, so the two positions of a pair
+  // always share a table.
+  __device__ __forceinline__ void load_fp8(const LlvqClassHot& h) {
+    svlo = h.sv0lo8;
+    svhi = h.sv0hi8;
+  }
+
+  __device__ __forceinline__ uint32_t slot(const uint8_t* smem, const ELayout& L, int i, uint32_t& pos) {
+    if (i == 8 || i == 12 || i == 16) {
+      if (swi == (uint32_t)i) {   // two-part class: the complement's tables
+        const uint2 q = *reinterpret_cast<const uint2*>(smem + hp + 64u);
+        const uint2 t = *reinterpret_cast<const uint2*>(smem + hp + 88u);
+        nc = q.x;
+        cnt8 = q.y;
+        svlo = t.x;
+        svhi = t.y;
+        nz0 = nz1;
+        m = ~c & 0xffffffu;
+      }
+    }
+    uint32_t kb, free_;
+    if (i < kSteps) {
+      // (decode_step picks the count byte with v_perm, so its selector keeps the 0x0c bytes)
+      const StepOut so = decode_step(smem, y, nc, cnt8, 0x0c0c0c00u, fo + kFRow * (uint32_t)i);
+      kb = so.k;
+      free_ = med3_1(so.g, nz0);
+      if (i == 6 || i == 10 || i == 14) fo = swi == (uint32_t)(i + 2) ? 0u : fo;
+      if (i == kSteps - 1) codes = tail_codes(smem, L, cnt8, y);
+    } else {
+      const uint32_t code = __builtin_amdgcn_ubfe(codes, 2 * (i - kSteps), 2);
+      kb = code | 0x0c0c0c00u;
+      free_ = med3_1(code, nz0);
+    }
+    const uint32_t neg = s & free_;
+    s >>= free_;
+    pos = (uint32_t)__builtin_ctz(m);
+    m &= m - 1u;
+    return kb + (neg << 2);
   }
 };
 

@@ -1,43 +1,49 @@
 // Fused LLVQ dequant-GEMV for one activation row (batch 1), gfx950.
 // Included once by llvq.hip after llvq_engine.h.
 //
-// The tile engine decodes each block; this consumer dots the 24 decoded values with the
-// block's 24 activations straight from registers (odd blocks, position order) or from
-// LDS by position (even blocks, decode order), never storing the weights.  Block results
-// are scaled in their LDS slot, and the tile's rows are summed in a fixed order, so
-// results do not depend on which wave decoded which block.
+// The tile engine's decoders turn each block back into its 24 values; this consumer dots
+// them with the block's 24 activations straight from registers (odd blocks, position
+// order) or from LDS by position (even blocks, decode order), never storing the weights.
+// Values leave the decoders as selectors into an 8-entry table of fp8 codes; two positions
+// share one v_perm, one fp8 -> bf16 conversion and one v_dot2c_f32_bf16 with the bf16
+// activation pair (the products are exact; the sums are fp32).  Block results are scaled in
+// their LDS slot and each row is summed in a fixed order, so results do not depend on which
+// wave decoded which block.
+//
+// Streaming classification.  A workgroup (16 waves, one per CU) owns tiles of whole rows.
+// Inside a tile the waves take units of 64 consecutive fields from an LDS counter; a wave
+// requests the fields of its next unit before it classifies the current one, so the
+// packed stream arrives while the workgroup decodes instead of in one burst before it.
+// Classification appends each block to one of the wave's two ring queues in LDS (odd or
+// even coset, so a wavefront runs one of the two very different decoders without
+// divergence), and the wave decodes a full chunk of 64 blocks whenever a ring holds one.
+// At the end of the tile the rings' remainders (fewer than 64 per ring) are gathered into
+// one shared queue between two barriers and decoded as full chunks by all waves; then the
+// rows are summed.  No wave ever waits on another except at those barriers.
 
 #pragma once
 
-template <bool XF32>
-__device__ __forceinline__ void load_x24(const uint8_t* smem, uint32_t xs, uint32_t blk, float xv[24]) {
-  if (XF32) {
-    const float4* p = reinterpret_cast<const float4*>(smem + xs + blk * 96u);
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      const float4 v = p[q];
-      xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
-    }
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(smem + xs + blk * 48u);
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const uint4 v = p[q];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        xv[8 * q + 2 * h] = __uint_as_float(w[h] << 16);
-        xv[8 * q + 2 * h + 1] = __uint_as_float(w[h] & 0xffff0000u);
-      }
-    }
-  }
+constexpr int kRing = 128;              // entries per ring (a ring never holds more than 127)
+constexpr int kRingBytes = 2 * kEWaves * kRing * 8;   // odd and even ring of every wave
+
+typedef __bf16 llvq_bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two decoded values (selectors ka, kb into the fp8 table svhi:svlo, each in byte 0 with
+// 0x0c above) as a bf16 pair: one v_perm joins the selectors, one picks both fp8 codes, one
+// conversion widens them exactly.
+__device__ __forceinline__ llvq_bf16x2 value_pair(uint32_t svhi, uint32_t svlo, uint32_t ka, uint32_t kb) {
+  const uint32_t sel = __builtin_amdgcn_perm(kb, ka, 0x0c0c0400u);     // ka.byte0, kb.byte0, 0, 0
+  const uint32_t codes = __builtin_amdgcn_perm(svhi, svlo, sel);
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);
 }
 
-// activation at column col (LDS)
+// acc + v.x a.x + v.y a.y for bf16 activations (one v_dot2c_f32_bf16) or fp32 ones
 template <bool XF32>
-__device__ __forceinline__ float x_at(const uint8_t* smem, uint32_t xs, uint32_t col) {
-  if (XF32) return reinterpret_cast<const float*>(smem + xs)[col];
-  return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(smem + xs)[col] << 16);
+__device__ __forceinline__ float dot_pair(float acc, llvq_bf16x2 v, uint32_t xb, float x0, float x1) {
+  if (!XF32) return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(llvq_bf16x2, xb), v, acc, false);
+  const uint32_t vb = __builtin_bit_cast(uint32_t, v);
+  acc = __builtin_fmaf(__uint_as_float(vb << 16), x0, acc);
+  return __builtin_fmaf(__uint_as_float(vb & 0xffff0000u), x1, acc);
 }
 
 __device__ __forceinline__ uint32_t block_col(uint32_t f, float inv_kb, uint32_t kb) {
@@ -45,62 +51,162 @@ __device__ __forceinline__ uint32_t block_col(uint32_t f, float inv_kb, uint32_t
   return f - rl * kb;
 }
 
-// One decode chunk: 64 consecutive entries of one parity queue (chunks 0..nco-1 are the
-// odd queue, the rest the even queue), one block per lane.  Result: part[f] *= dot.
+// Decode one odd-coset block (queue entry e) and multiply its slot by the dot product.
+// The block's activations are read as 16-byte words (bf16 pairs, or fp32 values).
 template <bool XF32>
-__device__ __forceinline__ void gemv_chunk(uint8_t* smem, const EArgs& a, const TileBuf& tb, int T, uint32_t kb,
-                                           float inv_kb, int c, int nco, int nodd, int neven, int lane) {
+__device__ __forceinline__ void gemv_odd(uint8_t* smem, const EArgs& a, float* part, uint64_t e, uint32_t kb,
+                                         float inv_kb) {
   const ELayout& L = a.L;
   const LlvqClassHot* cls = reinterpret_cast<const LlvqClassHot*>(smem + L.cls);
-  const float* xsum = reinterpret_cast<const float*>(smem + a.xsum);
-  const uint64_t* queue = reinterpret_cast<const uint64_t*>(smem + tb.queue);
-  float* part = reinterpret_cast<float*>(smem + tb.part);
-  if (c < nco) {
-    const int e = (c << 6) + lane;
-    if (e >= nodd) return;
-    const uint64_t eo = queue[e];
-    const uint32_t fo = entry_f(eo);
-    const uint32_t bo = block_col(fo, inv_kb, kb);
-    const LlvqClassHot hO = cls[entry_k(eo)];
-    const BlockStart so = block_start(smem, L, entry_J(eo), hO);
-    float xv[24];
-    load_x24<XF32>(smem, a.xs, bo, xv);
-    OddDec od;
-    od.init(hO, so);
-    float ao0 = 0.0f, ao1 = 0.0f;
+  const uint32_t fo = entry_f(e);
+  const uint32_t bo = block_col(fo, inv_kb, kb);
+  const LlvqClassHot hO = cls[entry_k(e)];
+  const BlockStart so = block_start(smem, L, entry_J(e), hO);
+  uint32_t xw[12];
+  float xf[24];
+  if (XF32) {
+    const float4* p = reinterpret_cast<const float4*>(smem + a.xs + bo * 96u);
 #pragma unroll
-    for (int i = 0; i < 24; ++i) {
-      const uint32_t bvo = od.step(smem, L, i);
-      if (i & 1)
-        ao1 = __builtin_fmaf((float)(bvo & 0xffu), xv[i], ao1);
-      else
-        ao0 = __builtin_fmaf((float)(bvo & 0xffu), xv[i], ao0);
+    for (int q = 0; q < 6; ++q) {
+      const float4 v = p[q];
+      xf[4 * q] = v.x; xf[4 * q + 1] = v.y; xf[4 * q + 2] = v.z; xf[4 * q + 3] = v.w;
     }
-    part[fo] *= __builtin_fmaf(-(float)kBias, xsum[bo], ao0 + ao1);
   } else {
-    const int e = ((c - nco) << 6) + lane;
-    if (e >= neven) return;
-    const uint64_t ee = queue[T - 1 - e];
-    const uint32_t fe = entry_f(ee);
-    const uint32_t be = block_col(fe, inv_kb, kb);
-    const LlvqClassHot hE = cls[entry_k(ee)];
-    const BlockStart se = block_start(smem, L, entry_J(ee), hE);
-    EvenDec ev;
-    ev.init(hE, se, L.cls + entry_k(ee) * (uint32_t)sizeof(LlvqClassHot));
-    const uint32_t col0 = be * 24u;
-    float ae0 = 0.0f, ae1 = 0.0f;
+    const uint4* p = reinterpret_cast<const uint4*>(smem + a.xs + bo * 48u);
 #pragma unroll
-    for (int i = 0; i < 24; ++i) {
-      uint32_t pos;
-      const uint32_t bve = ev.step(smem, L, i, pos);
-      const float xp = x_at<XF32>(smem, a.xs, col0 + pos);
-      if (i & 1)
-        ae1 = __builtin_fmaf((float)(bve & 0xffu), xp, ae1);
-      else
-        ae0 = __builtin_fmaf((float)(bve & 0xffu), xp, ae0);
+    for (int q = 0; q < 3; ++q) {
+      const uint4 v = p[q];
+      xw[4 * q] = v.x; xw[4 * q + 1] = v.y; xw[4 * q + 2] = v.z; xw[4 * q + 3] = v.w;
     }
-    part[fe] *= __builtin_fmaf(-(float)kBias, xsum[be], ae0 + ae1);
   }
+  OddDec od;
+  od.init(hO, so);
+  od.load_fp8(hO);
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    const uint32_t ka = od.slot(smem, L, 2 * i);
+    const uint32_t kb2 = od.slot(smem, L, 2 * i + 1);
+    const llvq_bf16x2 v = value_pair(od.svhi, od.svlo, ka, kb2);
+    if (i & 1)
+      a1 = dot_pair<XF32>(a1, v, XF32 ? 0u : xw[i], XF32 ? xf[2 * i] : 0.0f, XF32 ? xf[2 * i + 1] : 0.0f);
+    else
+      a0 = dot_pair<XF32>(a0, v, XF32 ? 0u : xw[i], XF32 ? xf[2 * i] : 0.0f, XF32 ? xf[2 * i + 1] : 0.0f);
+  }
+  part[fo] *= a0 + a1;
+}
+
+// The same for an even-coset block; its values come in decode order, so each one's
+// activation is read from LDS by position.
+template <bool XF32>
+__device__ __forceinline__ void gemv_even(uint8_t* smem, const EArgs& a, float* part, uint64_t e, uint32_t kb,
+                                          float inv_kb) {
+  const ELayout& L = a.L;
+  const LlvqClassHot* cls = reinterpret_cast<const LlvqClassHot*>(smem + L.cls);
+  const uint32_t fe = entry_f(e);
+  const uint32_t be = block_col(fe, inv_kb, kb);
+  const LlvqClassHot hE = cls[entry_k(e)];
+  const BlockStart se = block_start(smem, L, entry_J(e), hE);
+  EvenDec ev;
+  ev.init(hE, se, L.cls + entry_k(e) * (uint32_t)sizeof(LlvqClassHot));
+  ev.load_fp8(hE);
+  const uint32_t col0 = be * 24u;
+  const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(smem + a.xs);
+  const float* xs32 = reinterpret_cast<const float*>(smem + a.xs);
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    uint32_t pa, pb;
+    const uint32_t ka = ev.slot(smem, L, 2 * i, pa);
+    const uint32_t kb2 = ev.slot(smem, L, 2 * i + 1, pb);
+    const llvq_bf16x2 v = value_pair(ev.svhi, ev.svlo, ka, kb2);
+    uint32_t xb = 0u;
+    float x0 = 0.0f, x1 = 0.0f;
+    if (XF32) {
+      x0 = xs32[col0 + pa];
+      x1 = xs32[col0 + pb];
+    } else {
+      xb = (uint32_t)xs16[col0 + pa] | ((uint32_t)xs16[col0 + pb] << 16);
+    }
+    if (i & 1)
+      a1 = dot_pair<XF32>(a1, v, xb, x0, x1);
+    else
+      a0 = dot_pair<XF32>(a0, v, xb, x0, x1);
+  }
+  part[fe] *= a0 + a1;
+}
+
+// A wave's two rings: entry i of a ring sits at (head + i) mod kRing.  Heads and counts
+// are the same in every lane (they change only by wave-wide ballot counts).
+struct Rings {
+  uint64_t* odd;
+  uint64_t* even;
+  uint32_t oh, on, eh, en;
+};
+
+// One field per lane (unit u of the tile: f = 64 u + lane), loaded as three words.
+struct LaneField {
+  uint32_t w0, w1, w2, sh;
+};
+
+__device__ __forceinline__ LaneField load_lane_field(const KDesc& d, const uint8_t* __restrict__ packed,
+                                                     uint32_t j0, int T, int u, int lane) {
+  LaneField lf;
+  const int f = min(u * 64 + lane, T - 1);       // past the tile: the tile's last field, unused
+  const uint64_t bit = (uint64_t)(j0 + (uint32_t)f) * (uint32_t)d.field_bits;
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(packed) + (bit >> 5);
+  lf.w0 = p[0];
+  lf.w1 = p[1];
+  lf.w2 = p[2];
+  lf.sh = (uint32_t)bit & 31u;
+  return lf;
+}
+
+// Classify the lane's field: class search (bucket table on the top index bits, then the
+// class starts), the block's scale into its slot, and the block appended to the wave's
+// odd or even ring.  An index >= the shell-union size gets slot 0 (it contributes
+// nothing), is counted and is not queued.
+__device__ __forceinline__ void classify_lane(uint8_t* smem, const ELayout& L, float* part, const KDesc& d,
+                                              const LaneField& lf, int T, int u, int lane, int32_t* err, Rings& R) {
+  const LlvqClassHot* cls = reinterpret_cast<const LlvqClassHot*>(smem + L.cls);
+  const float* G = reinterpret_cast<const float*>(smem + L.gains);
+  const uint8_t* bk = smem + L.bucket;
+  const int f = u * 64 + lane;
+  const uint32_t flo = __builtin_amdgcn_alignbit(lf.w1, lf.w0, lf.sh);
+  const uint32_t fhi = __builtin_amdgcn_alignbit(lf.w2, lf.w1, lf.sh);
+  const uint32_t ilo = flo & d.shape_mask_lo;
+  const uint32_t ihi = fhi & d.shape_mask_hi;
+  const uint64_t I = ((uint64_t)ihi << 32) | ilo;
+  const bool valid = f < T && I < d.index_count;
+  const double Id = valid ? __builtin_fma((double)ihi, 4294967296.0, (double)ilo) : 0.0;
+  const uint32_t bidx = d.bshift >= 32 ? (ihi >> (d.bshift - 32)) : __builtin_amdgcn_alignbit(ihi, ilo, d.bshift);
+  uint32_t k = bk[valid ? bidx : 0u];
+  const bool c1 = Id >= cls[k + 1].start;
+  const bool c2 = Id >= cls[k + 2].start;
+  k += (uint32_t)c1 + (uint32_t)c2;                 // c2 implies c1
+  if (__ballot(c2)) {
+    while (Id >= cls[k + 1].start) ++k;             // the sentinel records end the scan
+  }
+  const LlvqClassHot& h = cls[k];
+  const bool odd = ((h.meta >> 17) & 1u) != 0u;
+  // J = I - start as the low bits of 2^52 + J (exact: J < 2^41 < 2^52)
+  const uint64_t jb = __builtin_bit_cast(uint64_t, Id + (0x1p52 - h.start));
+  const uint32_t ehi = ((uint32_t)(jb >> 32) & 0x3ffu) | ((uint32_t)f << 10) | (k << 24);
+  const uint64_t entry = ((uint64_t)ehi << 32) | (uint32_t)jb;
+  const uint32_t gsh = d.shape_bits >= 32 ? (fhi >> (d.shape_bits - 32))
+                                          : __builtin_amdgcn_alignbit(fhi, flo, d.shape_bits);
+  const uint32_t g = gsh & ((1u << d.gain_bits) - 1u);
+  const float sc = d.mode == LLVQ_MODE_SHAPEGAIN ? G[g] * h.invnorm : 1.0f;
+  if (f < T) part[f] = valid ? sc : 0.0f;
+  if (f < T && !valid && err) atomicAdd(err, 1);
+  const uint64_t bo = __ballot(valid && odd);
+  const uint64_t be = __ballot(valid && !odd);
+  const uint32_t po = __builtin_amdgcn_mbcnt_hi((uint32_t)(bo >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bo, 0u));
+  const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+  if (valid && odd) R.odd[(R.oh + R.on + po) & (kRing - 1)] = entry;
+  if (valid && !odd) R.even[(R.eh + R.en + pe) & (kRing - 1)] = entry;
+  R.on += (uint32_t)__popcll(bo);
+  R.en += (uint32_t)__popcll(be);
 }
 
 template <bool XF32>
@@ -114,16 +220,17 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
   const int wave = tid >> 6;
   const int kb = d.kb;
   const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
+  float* part = reinterpret_cast<float*>(smem + L.buf[0].part);
+  int* work = reinterpret_cast<int*>(smem + L.work);   // unit counter, leftover counts, chunk counter
+  uint64_t* shq = reinterpret_cast<uint64_t*>(smem + a.rings);   // the rings, then the leftover queue
+  const float inv_kb = 1.0f / (float)kb;
 
-  // ---- set-up: the first tile's fields are requested before the tables and activations
-  // are staged in LDS, so their memory latency overlaps the staging
-  const float inv_kb0 = 1.0f / (float)kb;
-  int row00 = blockIdx.x * a.rows_per_tile;
+  // ---- set-up: the first unit's fields are requested before the tables and activations
+  // are staged in LDS, so their memory latency overlaps the staging.  (The grid never
+  // exceeds the tile count, so tile blockIdx.x exists and T0 >= 1.)
+  const int row00 = blockIdx.x * a.rows_per_tile;
   const int T0 = min(a.rows_per_tile, d.rows - row00) * kb;
-  const TileMap tm0 = {(uint32_t)(row00 * kb), (uint32_t)kb, (uint32_t)kb, inv_kb0};
-  // (unconditional, so the loads stay in flight: the grid never exceeds the tile count, so
-  // T0 >= 1, and a wave without a unit of tile 0 reads unit 0 and ignores it)
-  const UnitFields uf0 = load_unit(d, packed, tm0, T0, min(wave, (T0 - 1) / kEUnit), lane);
+  LaneField lf = load_lane_field(d, packed, (uint32_t)(row00 * kb), T0, min(wave, (T0 - 1) >> 6), lane);
   // activations: the whole 16-byte words of a 16-byte aligned bf16 row go with the table
   // copies; the rest (and the zero padding to Kb * 24 columns) follows
   const bool xa16 = !XF32 && ((((uintptr_t)xv) & 15u) == 0u);
@@ -154,88 +261,77 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
       }
     }
   }
+  if (tid < 4) work[tid] = 0;
   __syncthreads();
-  {
-    float* xsum = reinterpret_cast<float*>(smem + a.xsum);
-    for (int b = tid; b < kb; b += kEThreads) {
-      float xx[24];
-      load_x24<XF32>(smem, a.xs, (uint32_t)b, xx);
-      float s0 = 0.0f;
-#pragma unroll
-      for (int p = 0; p < 24; ++p) s0 += xx[p];
-      xsum[b] = s0;
-    }
-  }
-  int* work = reinterpret_cast<int*>(smem + L.work);
-  const float inv_kb = 1.0f / (float)kb;
 
-  // Tiles of this workgroup: blockIdx.x + lt * gridDim.x, using buffer lt & 1.  Phase lt
-  // decodes tile lt and, as work runs out, classifies tile lt + 1 into the other buffer, so
-  // the classification fills the tail of the decode; then the rows of tile lt are summed.
-  auto tile_rows = [&](int tile, int* row0, int* nrows) {
-    *row0 = tile * a.rows_per_tile;
-    *nrows = min(a.rows_per_tile, d.rows - *row0);
-  };
-  // classify tile 0 (fields loaded above)
-  if (blockIdx.x < a.ntiles) {
-    if (tid == 0) {
-      int* c0 = reinterpret_cast<int*>(smem + L.buf[0].ctr);
-      int* c1 = reinterpret_cast<int*>(smem + L.buf[1].ctr);
-      c0[0] = 0; c0[1] = 0; c1[0] = 0; c1[1] = 0; work[0] = 0; work[1] = 0;
-    }
-    __syncthreads();
-    const int nun0 = (T0 + kEUnit - 1) / kEUnit;
-    if (wave < nun0) classify_fields(smem, L, L.buf[0], d, uf0, T0, wave, lane, err);
-    // units past the first kEWaves (tiles of more than kEWaves * kEUnit blocks), handed out
-    // by their own counter
-    for (;;) {
-      int u = 0;
-      if (lane == 0) u = atomicAdd(&work[1], 1);
-      u = __builtin_amdgcn_readfirstlane(u) + kEWaves;
-      if (u >= nun0) break;
-      classify_unit(smem, L, L.buf[0], d, packed, tm0, T0, u, lane, err);
-    }
-    __syncthreads();
-  }
-  int lt = 0;
-  for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x, ++lt) {
-    const TileBuf& cur = L.buf[lt & 1];
-    const TileBuf& nxt = L.buf[(lt & 1) ^ 1];
-    int row0, nrows;
-    tile_rows(tile, &row0, &nrows);
+  Rings R;
+  R.odd = shq + (size_t)(2 * wave) * kRing;
+  R.even = R.odd + kRing;
+  for (int tile = blockIdx.x, lt = 0; tile < a.ntiles; tile += gridDim.x, ++lt) {
+    const int row0 = tile * a.rows_per_tile;
+    const int nrows = min(a.rows_per_tile, d.rows - row0);
     const int T = nrows * kb;
-    const int* ctr = reinterpret_cast<const int*>(smem + cur.ctr);
-    const int nodd = ctr[0];
-    const int neven = ctr[1];
-    const int nco = (nodd + 63) >> 6;
-    const int nch = nco + ((neven + 63) >> 6);
-    // next tile's classify units
-    const int tile1 = tile + gridDim.x;
-    int row1 = 0, nrows1 = 0, T1 = 0, nun1 = 0;
-    if (tile1 < a.ntiles) {
-      tile_rows(tile1, &row1, &nrows1);
-      T1 = nrows1 * kb;
-      nun1 = (T1 + kEUnit - 1) / kEUnit;
+    const int nun = (T + 63) >> 6;
+    const uint32_t j0 = (uint32_t)(row0 * kb);
+    // units 0..kEWaves-1 go to the waves in order, the rest through the counter
+    int u = wave;
+    if (lt > 0) lf = load_lane_field(d, packed, j0, T, min(u, nun - 1), lane);
+    R.oh = R.on = R.eh = R.en = 0u;
+    while (u < nun) {
+      int u2 = 0;
+      if (lane == 0) u2 = atomicAdd(&work[0], 1);
+      u2 = __builtin_amdgcn_readfirstlane(u2) + kEWaves;
+      const LaneField lf2 = load_lane_field(d, packed, j0, T, min(u2, nun - 1), lane);
+      classify_lane(smem, L, part, d, lf, T, u, lane, err, R);
+      while (R.on >= 64u) {
+        gemv_odd<XF32>(smem, a, part, R.odd[(R.oh + (uint32_t)lane) & (kRing - 1)], (uint32_t)kb, inv_kb);
+        R.oh = (R.oh + 64u) & (kRing - 1);
+        R.on -= 64u;
+      }
+      while (R.en >= 64u) {
+        gemv_even<XF32>(smem, a, part, R.even[(R.eh + (uint32_t)lane) & (kRing - 1)], (uint32_t)kb, inv_kb);
+        R.eh = (R.eh + 64u) & (kRing - 1);
+        R.en -= 64u;
+      }
+      u = u2;
+      lf = lf2;
     }
-    const TileMap tm1 = {(uint32_t)(row1 * kb), (uint32_t)kb, (uint32_t)kb, inv_kb};
 
-    // ---- decode + dot of this tile (odd chunks first), then classify units of the next
+    // ---- the rings' remainders into one shared queue (odd entries from the front, even
+    // from position kLeftEven), then decoded by all waves as full chunks
+    constexpr int kLeftEven = kEWaves * 64;
+    int bo = 0, be = 0;
+    if (lane == 0) {
+      bo = atomicAdd(&work[1], (int)R.on);
+      be = atomicAdd(&work[2], (int)R.en);
+    }
+    bo = __builtin_amdgcn_readfirstlane(bo);
+    be = __builtin_amdgcn_readfirstlane(be);
+    const uint64_t lo = (uint32_t)lane < R.on ? R.odd[(R.oh + (uint32_t)lane) & (kRing - 1)] : 0ull;
+    const uint64_t le = (uint32_t)lane < R.en ? R.even[(R.eh + (uint32_t)lane) & (kRing - 1)] : 0ull;
+    __syncthreads();                        // every ring read; the queue may overwrite them
+    if ((uint32_t)lane < R.on) shq[bo + lane] = lo;
+    if ((uint32_t)lane < R.en) shq[kLeftEven + be + lane] = le;
+    __syncthreads();
+    const int nlo = work[1], nle = work[2];
+    const int nco = (nlo + 63) >> 6;
+    const int nch = nco + ((nle + 63) >> 6);
     for (;;) {
       int c = 0;
-      if (lane == 0) c = atomicAdd(&work[0], 1);
+      if (lane == 0) c = atomicAdd(&work[3], 1);
       c = __builtin_amdgcn_readfirstlane(c);
-      if (c < nch) {
-        gemv_chunk<XF32>(smem, a, cur, T, (uint32_t)kb, inv_kb, c, nco, nodd, neven, lane);
-      } else if (c < nch + nun1) {
-        classify_unit(smem, L, nxt, d, packed, tm1, T1, c - nch, lane, err);
+      if (c >= nch) break;
+      if (c < nco) {
+        const int e = (c << 6) + lane;
+        if (e < nlo) gemv_odd<XF32>(smem, a, part, shq[e], (uint32_t)kb, inv_kb);
       } else {
-        break;
+        const int e = ((c - nco) << 6) + lane;
+        if (e < nle) gemv_even<XF32>(smem, a, part, shq[kLeftEven + e], (uint32_t)kb, inv_kb);
       }
     }
     __syncthreads();
 
-    // ---- row sums of this tile (fixed order); reset this buffer's counters for tile lt + 2
-    const float* part = reinterpret_cast<const float*>(smem + cur.part);
+    // ---- row sums of this tile (fixed order); counters reset for the next tile
     for (int rl = wave; rl < nrows; rl += kEWaves) {
       float acc = 0.0f;
       for (int b = lane; b < kb; b += 64) acc += part[rl * kb + b];
@@ -247,12 +343,7 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
         y[r] = acc * rs;
       }
     }
-    if (tid == 0) {
-      int* cc = reinterpret_cast<int*>(smem + cur.ctr);
-      cc[0] = 0;
-      cc[1] = 0;
-      work[0] = 0;
-    }
+    if (tid < 4) work[tid] = 0;
     __syncthreads();
   }
 }

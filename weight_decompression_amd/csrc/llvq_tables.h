@@ -24,7 +24,7 @@ struct LlvqClassRec {
   uint8_t pad;
 };
 
-// Hot-path class record kept in LDS by the fused GEMV (80 bytes, five 16-byte rows).
+// Hot-path class record kept in LDS by the fused kernels (96 bytes, six 16-byte rows).
 // The absolute values of a class are unranked in at most two parts.  Odd classes and
 // even classes with w = 0 or w = 24 have one part of 24 values; other even classes have
 // the support part (w values, placed on the codeword's positions) followed by the
@@ -37,6 +37,8 @@ struct LlvqClassRec {
 //        even classes: bytes 0-3 = 12 + |v_j|, bytes 4-7 = 12 - |v_j| (negative sign);
 //        odd classes:  bytes 0-3 = 12 + b(v_j) for positions on the codeword,
 //                      bytes 4-7 = 12 - b(v_j) off it, b(v) = v if v = 1 mod 4 else -v.
+//   svX8 the same 8-byte table with signed values as OCP fp8 E4M3 codes (exact for |v| <= 12;
+//        zero as 0x00), read by the batch-1 GEMV, which converts value pairs to bf16.
 // meta: B (bits 0-4) | w (bits 8-12) | pi (bit 16) | parity (bit 17) |
 //       nonzero mask of part-0 slots (bits 20-23) | nonzero mask of part-1 slots (24-27).
 struct LlvqClassHot {
@@ -50,6 +52,7 @@ struct LlvqClassHot {
   uint32_t m;        // shell
   uint32_t nc0, cnt0, sv0lo, sv0hi;   // part 0 (byte offset 48)
   uint32_t nc1, cnt1, sv1lo, sv1hi;   // part 1 (byte offset 64: one 16-byte read)
+  uint32_t sv0lo8, sv0hi8, sv1lo8, sv1hi8;   // fp8 tables of parts 0 and 1 (byte offset 80)
 };
 
 // Composition record of the 6-position tail table (see gen_tables.cpp).

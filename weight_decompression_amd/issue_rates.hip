@@ -92,6 +92,49 @@ K64(k_fma_f64, "v_fma_f64 %0, %0, %1, %2")
 K64(k_mul_f64, "v_mul_f64 %0, %0, %1")
 K64(k_add_f64, "v_add_f64 %0, %0, %1")
 
+// conversions between fp64 and u32 (the arithmetic decoder's per-step pair)
+__global__ __launch_bounds__(256) void k_cvt_u32_f64(uint32_t* out, uint32_t seed) {
+  uint32_t a[CH];
+  const double b = 3.5 + seed;
+  for (int j = 0; j < CH; ++j) a[j] = threadIdx.x * 7u + j + seed;
+  for (int it = 0; it < ITERS; ++it) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) asm volatile("v_cvt_u32_f64 %0, %1" : "+v"(a[j]) : "v"(b));
+  }
+  uint32_t s = 0;
+  for (int j = 0; j < CH; ++j) s ^= a[j];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+__global__ __launch_bounds__(256) void k_cvt_f64_u32(uint32_t* out, uint32_t seed) {
+  double a[CH];
+  const uint32_t b = seed + 5u;
+  for (int j = 0; j < CH; ++j) a[j] = threadIdx.x * 0.5 + j;
+  for (int it = 0; it < ITERS; ++it) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) asm volatile("v_cvt_f64_u32 %0, %1" : "+v"(a[j]) : "v"(b));
+  }
+  double s = 0;
+  for (int j = 0; j < CH; ++j) s += a[j];
+  out[blockIdx.x * 256 + threadIdx.x] = (uint32_t)s;
+}
+// bf16 pair dot product accumulating in fp32, and the fp8 pair -> bf16 pair conversion
+K32(k_dot2c_f32_bf16, "v_dot2c_f32_bf16 %0, %1, %2")
+K32(k_cvt_scalef32_pk_bf16_fp8, "v_cvt_scalef32_pk_bf16_fp8 %0, %0, %1")
+K32(k_bitop3_b32, "v_bitop3_b32 %0, %0, %1, %2 bitop3:0xc")
+K32(k_mbcnt_lo_u32_b32, "v_mbcnt_lo_u32_b32 %0, %1, %0")
+__global__ __launch_bounds__(256) void k_cmp_ne_u32(uint32_t* out, uint32_t seed) {
+  uint32_t a[CH];
+  const uint32_t b = seed;
+  for (int j = 0; j < CH; ++j) a[j] = threadIdx.x * 7u + j + seed;
+  for (int it = 0; it < ITERS; ++it) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) asm volatile("v_cmp_ne_u32_e32 vcc, %0, %1" : : "v"(a[j]), "v"(b) : "vcc");
+  }
+  uint32_t s = 0;
+  for (int j = 0; j < CH; ++j) s ^= a[j];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 typedef void (*kfn)(uint32_t*, uint32_t);
 static const kfn kKernels[] = {
     k_add_u32,     k_sub_u32,      k_and_b32,        k_or_b32,       k_xor_b32,      k_not_b32,      k_mov_b32,
@@ -99,7 +142,8 @@ static const kfn kKernels[] = {
     k_cvt_f32_u32, k_cvt_f32_ubyte0, k_xad_u32,      k_ffbl_b32,     k_bfi_b32,      k_bfe_u32,      k_alignbit_b32,
     k_lshl_or_b32, k_lshl_add_u32, k_add3_u32,       k_and_or_b32,   k_or3_b32,      k_mad_u32_u24,  k_mul_lo_u32,
     k_perm_b32,    k_dot4_u32_u8,  k_bcnt_u32_b32,   k_med3_u32,     k_min_f32,      k_max_f32,      k_min_u32,
-    k_max_u32,     k_max3_f32,     k_fma_f64,        k_mul_f64,      k_add_f64};
+    k_max_u32,     k_max3_f32,     k_fma_f64,        k_mul_f64,      k_add_f64,      k_cvt_u32_f64,  k_cvt_f64_u32,
+    k_dot2c_f32_bf16, k_cvt_scalef32_pk_bf16_fp8, k_bitop3_b32, k_mbcnt_lo_u32_b32, k_cmp_ne_u32};
 
 extern "C" __attribute__((visibility("default"))) int ir_count() { return (int)(sizeof(kKernels) / sizeof(kKernels[0])); }
 
