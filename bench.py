@@ -647,14 +647,14 @@ def run_gptq(a):
 
     res = {}
     for variant in ("direct", "euclid", "spherical"):
-        desc, packed, _, _ = gptq.gptq(Wt, H, 10, gains, variant=variant)
+        desc, packed, _ = gptq.gptq(Wt, H, 10, gains, variant=variant)
         res[variant] = loss(desc, packed)
     sec, wall = time_steps(lambda i: (gptq.gptq(Wt, H, 10, gains, variant="spherical"), 0)[1], a.steps, a.warmup,
                            stream)
     kb = synth.blocks_per_row(K)
     out = base_line("LLVQ spherical GPTQ layer-output error (relative, 2 bits/weight), 1 MI355X", res["spherical"],
                     "tr(dW H dW^T)/tr(W H W^T)", a.steps, a.warmup, sec, "f64",
-                    f"weight_decompression_amd.gptq (llvq_search per block column + fp64 feedback), "
+                    f"weight_decompression_amd.gptq (llvq_gptq_factor, then llvq_search + llvq_gptq_column per block column), "
                     f"{N}x{K} N(0, 0.02^2) layer, {S} correlated activation samples",
                     {"rows": N, "cols": K, "samples": S, "max_shell": 10, "shape_bits": 44, "gain_bits": 4})
     out["higher_is_better"] = False

@@ -232,6 +232,49 @@ int64_t llvq_quantize_workspace_bytes(const llvq_desc* d);
 int llvq_quantize(const llvq_desc* d, const float* w, const void* scales, void* packed, void* workspace,
                   int32_t* err_count, void* stream);
 
+/* Spherical GPTQ (papernotes.org notes, 关键设计 3): quantisation with the layer Hessian's
+ * error feedback, the block's lattice direction rescaled to the block's own norm (a
+ * retraction onto the product of spheres) and its residual spread over the columns not yet
+ * quantised through U = chol(H^-1)^T.  A caller runs, for a weight matrix W [rows][cols]:
+ *   llvq_gptq_factor once, llvq_gptq_begin once, then for b = 0 .. Kb-1: llvq_search of the
+ *   block column x (angular, shells 2..M) and llvq_gptq_column(b); finally llvq_pack_fields.
+ * All matrices are fp64 on the device, row-major; Kp = 24 * Kb (cols rounded up to a whole
+ * block); the calls allocate nothing and run on `stream`.
+ *
+ * Workspace bytes llvq_gptq_factor needs for `cols` columns (Kp*Kp*8 + Kb*576*8 + 256), or
+ * LLVQ_EINVAL.  Host only. */
+int64_t llvq_gptq_workspace_bytes(int32_t cols);
+
+/* U [Kp][Kp] (upper triangular) with Hd^-1 = U^T U, Hd = Hp + damp * mean(diag H) * I, Hp =
+ * H [cols][cols] padded to Kp with an uncoupled diagonal equal to mean(diag H) (pad columns
+ * stay zero).  Computed without inverting Hd: with P the index reversal, P Hd P = M M^T
+ * (Cholesky, blocked by 24) and U = P M^-1 P (blocked triangular inverse).
+ *   H         : fp64 [cols][cols], symmetric positive (semi)definite.
+ *   workspace : llvq_gptq_workspace_bytes(cols) bytes, 8-byte aligned, contents not kept.
+ *   err_count : nullable; counts non-positive pivots (Hd not positive definite: U is then
+ *               not meaningful).
+ * Returns LLVQ_OK, LLVQ_EINVAL (null / misaligned pointer, cols <= 0, damp < 0) or LLVQ_EHIP. */
+int llvq_gptq_factor(int32_t cols, const double* H, double damp, double* U, void* workspace,
+                     int32_t* err_count, void* stream);
+
+/* Wq [rows][Kp] fp64 = W [rows][cols] fp32 zero-padded, and x0 [rows][24] fp32 = the first
+ * block column (the first search's input).  Returns LLVQ_OK, LLVQ_EINVAL or LLVQ_EHIP. */
+int llvq_gptq_begin(int32_t rows, int32_t cols, const float* W, double* Wq, float* x0, void* stream);
+
+/* One block column b after its search: for every row, the gain index nearest to the block's
+ * norm (ties to the lower index), the field indices[r] | gain << shape_bits into
+ * fields[r * Kb + b], the residual E = w - len v/|v| with len = |w| (variant 0, spherical)
+ * or G[gain] (variant 1, Euclidean feedback), E' = E U_SS^-1, and W[:, F] -= E' U_SF for the
+ * columns F after the block (variant 2, direct: no feedback); x_next [rows][24] fp32 receives
+ * block column b + 1 (not written for the last block).
+ *   d       : SHAPEGAIN descriptor (rows, cols, max_shell <= 13, shape_bits + gain_bits <= 64).
+ *   gains   : fp16 [2^gain_bits].   points, indices: llvq_search's output for block b.
+ *   ework   : fp64 [rows][24] scratch (may be NULL for variant 2).
+ * Returns LLVQ_OK, LLVQ_EINVAL, LLVQ_EUNSUPPORTED or LLVQ_EHIP. */
+int llvq_gptq_column(const llvq_desc* d, int32_t block, int32_t variant, const void* gains, double* Wq,
+                     const double* U, const int8_t* points, const uint64_t* indices, uint64_t* fields,
+                     double* ework, float* x_next, void* stream);
+
 /* llvq_quantize for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and the
  * same output, with the workspace held by the library instead of passed in.

@@ -11,6 +11,7 @@ MLP-shaped workload (dense N(0, 0.02^2) weights, whose oracle search results are
 under tests/golden/), and perturbed lattice points.
 """
 
+import ctypes
 import os
 import random
 
@@ -224,22 +225,93 @@ def test_quantize_then_decode_and_gemv():
     assert np.array_equal(pts, sp)
 
 
+
+@pytest.mark.parametrize("K", [72, 240, 1001])
+def test_gptq_factor_matches_oracle(K):
+    # U = chol(Hd^-1)^T from the library's blocked kernels (reversed Cholesky + triangular
+    # inverse) against the oracle's plain inverse + Cholesky; K = 1001 pads to 1008
+    from oracle import gptq as ogptq
+    from weight_decompression_amd import gptq as ggptq  # noqa: F401  (binding loaded)
+    rng = np.random.default_rng(K)
+    X = rng.standard_normal((2 * K, K)) * np.exp(0.5 * rng.standard_normal(K))
+    H = X.T @ X / (2 * K)
+    kp = 24 * ((K + 23) // 24)
+    Hp = np.eye(kp) * np.mean(np.diag(H))
+    Hp[:K, :K] = H
+    want = ogptq.inverse_hessian_factor(Hp, 0.01)
+    lib = wd.load_library()
+    Ht = torch.from_numpy(H).cuda()
+    U = torch.full((kp, kp), float("nan"), dtype=torch.float64, device="cuda")
+    ws = torch.empty(lib.llvq_gptq_workspace_bytes(K), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.llvq_gptq_factor(K, ctypes.c_void_p(Ht.data_ptr()), 0.01, ctypes.c_void_p(U.data_ptr()),
+                                ctypes.c_void_p(ws.data_ptr()), ctypes.c_void_p(err.data_ptr()), sp) == 0
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = U.cpu().numpy()
+    rel = np.abs(got - want).max() / np.abs(want).max()
+    say(f"gptq factor K={K}: max |dU| / max |U| = {rel:.2e}")
+    assert rel < 1e-10
+    assert np.array_equal(got, np.triu(got))
+
+
+def test_gptq_factor_reports_an_indefinite_hessian():
+    # -I damped by 0.01 * mean(diag) stays negative definite: every pivot is counted; with
+    # no counter the call still completes (the pivots are replaced, nothing is written)
+    lib = wd.load_library()
+    K = 48
+    H = torch.from_numpy(-np.eye(K)).cuda()
+    U = torch.empty((K, K), dtype=torch.float64, device="cuda")
+    ws = torch.empty(lib.llvq_gptq_workspace_bytes(K), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.llvq_gptq_factor(K, ctypes.c_void_p(H.data_ptr()), 0.01, ctypes.c_void_p(U.data_ptr()),
+                                ctypes.c_void_p(ws.data_ptr()), ctypes.c_void_p(err.data_ptr()), sp) == 0
+    assert lib.llvq_gptq_factor(K, ctypes.c_void_p(H.data_ptr()), 0.01, ctypes.c_void_p(U.data_ptr()),
+                                ctypes.c_void_p(ws.data_ptr()), None, sp) == 0
+    torch.cuda.synchronize()
+    assert int(err.item()) == K
+    assert lib.llvq_gptq_factor(K, ctypes.c_void_p(H.data_ptr()), -1.0, ctypes.c_void_p(U.data_ptr()),
+                                ctypes.c_void_p(ws.data_ptr()), None, sp) == -1
+
+
+def _gptq_fields(W, H, gains, variant):
+    from weight_decompression_amd import gptq as ggptq
+    desc, packed, fields = ggptq.gptq(torch.from_numpy(W).cuda(), torch.from_numpy(H).cuda(), 10,
+                                      torch.from_numpy(gains).cuda(), variant=variant)
+    torch.cuda.synchronize()
+    f = fields.cpu().numpy().view(np.uint64)
+    return packed.cpu().numpy(), f & np.uint64((1 << 44) - 1), (f >> np.uint64(44)).astype(np.int64)
+
+
 @pytest.mark.parametrize("variant", ["spherical", "euclid", "direct"])
 def test_gptq_matches_oracle(variant):
     # spherical GPTQ on a seeded 12 x 240 layer (10 block columns) with a correlated Hessian
     from oracle import gptq as ogptq
-    from weight_decompression_amd import gptq as ggptq
     W, H = synth.gptq_problem(33, 12, 240, 1024)
     gains = (synth.chi_gain_table(16).astype(np.float64) * 0.02).astype(np.float16)
     want_idx, want_g = ogptq.gptq(W, H, 10, gains, variant=variant)
-    desc, packed, idx, gidx = ggptq.gptq(torch.from_numpy(W).cuda(), torch.from_numpy(H).cuda(), 10,
-                                         torch.from_numpy(gains).cuda(), variant=variant)
-    torch.cuda.synchronize()
-    assert np.array_equal(idx.cpu().numpy().view(np.uint64), want_idx)
-    assert np.array_equal(gidx.cpu().numpy(), want_g)
+    packed, idx, gidx = _gptq_fields(W, H, gains, variant)
+    assert np.array_equal(idx, want_idx)
+    assert np.array_equal(gidx, want_g)
     fields = want_idx | (want_g.astype(np.uint64) << np.uint64(44))
-    assert np.array_equal(packed.cpu().numpy(), synth.pack_fields(fields.reshape(-1), 48))
+    assert np.array_equal(packed, synth.pack_fields(fields.reshape(-1), 48))
     say(f"gptq {variant}: 120 blocks equal to the oracle")
+
+
+def test_gptq_layer_spanning_every_workgroup_matches_oracle_rows():
+    # 512 x 1000 (42 block columns, the last ragged): every kernel runs on many workgroups;
+    # rows do not interact, so the oracle runs on a sample of them
+    from oracle import gptq as ogptq
+    W, H = synth.gptq_problem(35, 512, 1000, 2048)
+    gains = (synth.chi_gain_table(16).astype(np.float64) * 0.02).astype(np.float16)
+    _, idx, gidx = _gptq_fields(W, H, gains, "spherical")
+    rows = [0, 1, 255, 256, 511]
+    want_idx, want_g = ogptq.gptq(W, H, 10, gains, variant="spherical", rows=rows)
+    assert np.array_equal(idx[rows], want_idx)
+    assert np.array_equal(gidx[rows], want_g)
+    say(f"gptq 512x1000: rows {rows} ({len(rows) * 42} blocks) equal to the oracle")
 
 
 # ---------------------------------------------------------------------------

@@ -28,7 +28,8 @@ EXPORTED_SYMBOLS = ("llvq_index_count", "llvq_packed_bytes", "llvq_error_string"
                     "llvq_decode", "llvq_gemv", "llvq_encode_ref", "llvq_search", "llvq_quantize_workspace_bytes",
                     "llvq_quantize", "llvq_pack_fields", "llvq_decode_many",
                     "llvq_index_count_wide", "llvq_encode_wide", "llvq_quantize_noalloc",
-                    "llvq_quantize_noalloc_max_blocks")
+                    "llvq_quantize_noalloc_max_blocks", "llvq_gptq_workspace_bytes", "llvq_gptq_factor",
+                    "llvq_gptq_begin", "llvq_gptq_column")
 
 
 class LlvqError(RuntimeError):
@@ -93,6 +94,14 @@ def load_library(path=LIB_PATH):
     lib.llvq_quantize_noalloc.restype = ctypes.c_int
     lib.llvq_quantize_noalloc_max_blocks.argtypes = []
     lib.llvq_quantize_noalloc_max_blocks.restype = i64
+    lib.llvq_gptq_workspace_bytes.argtypes = [i32]
+    lib.llvq_gptq_workspace_bytes.restype = i64
+    lib.llvq_gptq_factor.argtypes = [i32, vp, ctypes.c_double, vp, vp, vp, vp]
+    lib.llvq_gptq_factor.restype = ctypes.c_int
+    lib.llvq_gptq_begin.argtypes = [i32, i32, vp, vp, vp, vp]
+    lib.llvq_gptq_begin.restype = ctypes.c_int
+    lib.llvq_gptq_column.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.llvq_gptq_column.restype = ctypes.c_int
     lib.llvq_pack_fields.argtypes = [dp, vp, vp, vp]
     lib.llvq_pack_fields.restype = ctypes.c_int
     lib.llvq_decode_many.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp]

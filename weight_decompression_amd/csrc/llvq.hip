@@ -333,6 +333,7 @@ __global__ __launch_bounds__(256) void k_gemv(KDesc d, const uint8_t* __restrict
 
 #include "llvq_rank.h"
 #include "llvq_search.h"
+#include "llvq_gptq.h"
 
 // ---------------------------------------------------------------------------
 // host side
@@ -1101,5 +1102,96 @@ LLVQ_API int llvq_encode_wide(const int8_t* points, int64_t n, int32_t max_shell
   if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
   hipLaunchKernelGGL(k_rank_wide<true>, dim3(grid_for((uint64_t)n, kWideThreads)), dim3(kWideThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), points, n, max_shell, indices, err_count);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// spherical GPTQ (llvq_gptq.h)
+
+namespace {
+int64_t gptq_kp(int32_t cols) { return 24ll * ((cols + 23) / 24); }
+}  // namespace
+
+LLVQ_API int64_t llvq_gptq_workspace_bytes(int32_t cols) {
+  if (cols <= 0 || cols > (1 << 20)) return LLVQ_EINVAL;
+  const int64_t kp = gptq_kp(cols), kb = kp / 24;
+  return kp * kp * 8 + kb * 576 * 8 + 256;
+}
+
+LLVQ_API int llvq_gptq_factor(int32_t cols, const double* H, double damp, double* U, void* workspace,
+                              int32_t* err_count, void* stream) {
+  if (cols <= 0 || cols > (1 << 20) || !H || !U || !workspace || !(damp >= 0.0) || !(damp < 1e300)) return LLVQ_EINVAL;
+  if (!aligned(H, 8) || !aligned(U, 8) || !aligned(workspace, 8)) return LLVQ_EINVAL;
+  if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int Kp = (int)gptq_kp(cols), Kb = Kp / 24;
+  double* A = static_cast<double*>(workspace);
+  double* Linv = A + (size_t)Kp * (size_t)Kp;
+  double* mean = Linv + (size_t)Kb * 576;
+  const unsigned gfull = grid_for((uint64_t)Kp * (uint64_t)Kp, 256);
+  hipLaunchKernelGGL(k_gptq_diag_mean, dim3(1), dim3(256), 0, s, H, cols, mean);
+  hipLaunchKernelGGL(k_gptq_reverse_damp, dim3(gfull), dim3(256), 0, s, H, cols, Kp, mean, damp, A);
+  for (int jb = 0; jb < Kb; ++jb) {
+    const int j0 = 24 * jb;
+    hipLaunchKernelGGL(k_gptq_potrf_diag, dim3(1), dim3(64), 0, s, A, Kp, j0, Linv + (size_t)jb * 576, err_count);
+    const int rest = Kp - j0 - 24;
+    if (rest > 0) {
+      hipLaunchKernelGGL(k_gptq_panel, dim3((rest + 255) / 256), dim3(256), 0, s, A, Kp, j0,
+                         Linv + (size_t)jb * 576);
+      const int nt = (rest + kGTile - 1) / kGTile;
+      hipLaunchKernelGGL(k_gptq_syrk, dim3(nt, nt), dim3(256), 0, s, A, Kp, j0);
+    }
+  }
+  hipLaunchKernelGGL(k_gptq_inv_diag, dim3(gfull), dim3(256), 0, s, Kp, Linv, U);
+  for (int ib = 1; ib < Kb; ++ib)
+    hipLaunchKernelGGL(k_gptq_inv_row, dim3(ib), dim3(576), 0, s, A, Kp, ib, Linv, U);
+  hipLaunchKernelGGL(k_gptq_reverse, dim3(gfull), dim3(256), 0, s, Kp, U);
+  return launch_status();
+}
+
+LLVQ_API int llvq_gptq_begin(int32_t rows, int32_t cols, const float* W, double* Wq, float* x0, void* stream) {
+  if (rows <= 0 || cols <= 0 || cols > (1 << 20) || !W || !Wq || !x0) return LLVQ_EINVAL;
+  if (!aligned(W, 4) || !aligned(Wq, 8) || !aligned(x0, 4)) return LLVQ_EINVAL;
+  const int Kp = (int)gptq_kp(cols);
+  hipLaunchKernelGGL(k_gptq_begin, dim3(grid_for((uint64_t)rows * (uint64_t)Kp, 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), W, rows, cols, Kp, Wq, x0);
+  return launch_status();
+}
+
+LLVQ_API int llvq_gptq_column(const llvq_desc* d, int32_t block, int32_t variant, const void* gains, double* Wq,
+                              const double* U, const int8_t* points, const uint64_t* indices, uint64_t* fields,
+                              double* ework, float* x_next, void* stream) {
+  KDesc k;
+  const int st = make_kdesc_quant(d, &k);
+  if (st != LLVQ_OK) return st;
+  if (k.mode != LLVQ_MODE_SHAPEGAIN) return LLVQ_EINVAL;
+  if (variant < 0 || variant > 2 || block < 0 || block >= k.kb) return LLVQ_EINVAL;
+  const bool last = block == k.kb - 1;
+  if (!gains || !Wq || !U || !points || !indices || !fields || (!last && !x_next) || (variant != 2 && !ework))
+    return LLVQ_EINVAL;
+  if (!aligned(gains, 2) || !aligned(Wq, 8) || !aligned(U, 8) || !aligned(indices, 8) || !aligned(fields, 8) ||
+      (ework && !aligned(ework, 8)) || (x_next && !aligned(x_next, 4)))
+    return LLVQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  GptqCol g;
+  g.rows = k.rows;
+  g.Kp = 24 * k.kb;
+  g.kb = k.kb;
+  g.block = block;
+  g.variant = variant;
+  g.gain_bits = k.gain_bits;
+  g.shape_bits = k.shape_bits;
+  g.last = last ? 1 : 0;
+  hipLaunchKernelGGL(k_gptq_residual, dim3((k.rows + 255) / 256), dim3(256), 0, s, g, Wq, U,
+                     static_cast<const __half*>(gains), points, indices, fields, ework);
+  if (!last) {
+    if (variant != 2) {
+      const int f0 = (block + 1) * 24;
+      hipLaunchKernelGGL(k_gptq_update, dim3((g.Kp - f0 + 255) / 256, (k.rows + 31) / 32), dim3(256), 0, s, g, Wq, U,
+                         ework, x_next);
+    } else {
+      hipLaunchKernelGGL(k_gptq_next, dim3(grid_for((uint64_t)k.rows * 24u, 256)), dim3(256), 0, s, g, Wq, x_next);
+    }
+  }
   return launch_status();
 }

@@ -2,87 +2,73 @@
 notes, 关键设计 3 and 整体框架).
 
 For each 24-column block S in order, every row's block gets its angular nearest point of
-shells 2..M from llvq_search (the HIP search kernel); the block is replaced by its
-retraction onto the sphere of its own norm, w_hat = |w| v / |v|, and the residual
-E = w - w_hat is spread over the later columns F through U = chol(H^-1)^T:
-W[:, F] -= (E U_SS^-1) U_SF (the optimal correction for fixing the block).  The gain
-index of each block is the table entry nearest to the norm it had when it was quantised;
-the fields go to the packed stream through llvq_pack_fields.  The 'euclid' variant feeds
-back the gain-quantised reconstruction G[g] v / |v| instead, 'direct' feeds back nothing.
+shells 2..M from llvq_search; the block is replaced by its retraction onto the sphere of
+its own norm, w_hat = |w| v / |v|, and the residual E = w - w_hat is spread over the later
+columns F through U = chol(H^-1)^T: W[:, F] -= (E U_SS^-1) U_SF (the optimal correction for
+fixing the block).  The gain index of each block is the table entry nearest to the norm it
+had when it was quantised; the fields go to the packed stream through llvq_pack_fields.
+The 'euclid' variant feeds back the gain-quantised reconstruction G[g] v / |v| instead,
+'direct' feeds back nothing.
 
-The search and the packing run in the library's kernels; the per-block feedback is a
-triangular solve and a matrix product (torch.linalg / torch.matmul on the device, fp64).
+Every step runs in the library's kernels (llvq_gptq_factor for U, llvq_gptq_begin,
+llvq_search and llvq_gptq_column per block column, llvq_pack_fields); this module only
+allocates the device buffers and runs the loop.
 """
 
 import ctypes
 
-from . import SEARCH_ANGULAR, load_library, make_desc, packed_bytes, MODE_SHAPEGAIN, _check
+from . import (SEARCH_ANGULAR, MODE_SHAPEGAIN, _check, _packed_nbytes, _tensor, load_library, make_desc)
+
+VARIANTS = {"spherical": 0, "euclid": 1, "direct": 2}
 
 
-def inverse_hessian_factor(H, damp=0.01):
-    """Upper triangular U (fp64, on H's device) with (H + damp mean(diag H) I)^-1 = U^T U."""
-    import torch
-    H = H.to(torch.float64)
-    Hd = H + damp * torch.mean(torch.diagonal(H)) * torch.eye(H.shape[0], dtype=H.dtype, device=H.device)
-    Hinv = torch.cholesky_inverse(torch.linalg.cholesky(Hd))
-    return torch.linalg.cholesky(Hinv).mT    # Hinv = L L^T, U = L^T
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def gptq(W, H, max_shell, gains, shape_bits=44, damp=0.01, variant="spherical", stream=None):
-    """Quantise W [N][K] (torch fp32/fp64 on the GPU) with Hessian H [K][K].  When K is not a
-    multiple of 24 the last block is zero-padded (the pad columns get an uncoupled unit
-    Hessian, so they stay zero).  gains: fp16 gain table (torch, 2^gain_bits entries).
-    Returns (descriptor, packed uint8 stream, shape indices int64 [N][Kb], gain indices
-    int64 [N][Kb])."""
+    """Quantise W [N][K] (fp32 on the GPU) with the layer Hessian H [K][K] (fp64 on the
+    GPU).  When K is not a multiple of 24 the last block is zero-padded (the pad columns get
+    an uncoupled Hessian diagonal, so they stay zero).  gains: fp16 gain table (2^gain_bits
+    entries).  Returns (descriptor, packed uint8 stream, fields int64 [N][Kb] with
+    shape index | gain index << shape_bits)."""
     import torch
-    if variant not in ("spherical", "euclid", "direct"):
+    if variant not in VARIANTS:
         raise ValueError(variant)
-    lib = load_library()
-    dev = W.device
-    N, K0 = W.shape
-    kb = (K0 + 23) // 24
-    K = 24 * kb
-    if K != K0:
-        Wp = torch.zeros((N, K), dtype=W.dtype, device=dev)
-        Wp[:, :K0] = W
-        Hp = torch.eye(K, dtype=torch.float64, device=dev) * torch.mean(torch.diagonal(H.to(torch.float64)))
-        Hp[:K0, :K0] = H
-        W, H = Wp, Hp
+    N, K = W.shape
+    kb = (K + 23) // 24
+    kp = 24 * kb
     gain_bits = int(gains.numel()).bit_length() - 1
     if (1 << gain_bits) != gains.numel():
         raise ValueError("the gain table needs 2^gain_bits entries")
-    U = inverse_hessian_factor(H.to(dev), damp)
-    G = gains.to(torch.float64)
-    Wq = W.to(torch.float64).clone()
-    idx = torch.empty((N, kb), dtype=torch.int64, device=dev)
-    gidx = torch.empty((N, kb), dtype=torch.int64, device=dev)
+    _tensor(W, "gptq: W", (torch.float32,), 4 * N * K)
+    _tensor(H, "gptq: H", (torch.float64,), 8 * K * K)
+    _tensor(gains, "gptq: gains", (torch.float16,), 2 * gains.numel())
+    lib = load_library()
+    dev = W.device
+    sp = ctypes.c_void_p(stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    U = torch.empty((kp, kp), dtype=torch.float64, device=dev)
+    ws = torch.empty(int(lib.llvq_gptq_workspace_bytes(K)), dtype=torch.uint8, device=dev)
+    _check(lib.llvq_gptq_factor(K, _p(H), float(damp), _p(U), _p(ws), _p(err), sp), "llvq_gptq_factor")
+    del ws
+    Wq = torch.empty((N, kp), dtype=torch.float64, device=dev)
+    xs = [torch.empty((N, 24), dtype=torch.float32, device=dev) for _ in range(2)]
+    _check(lib.llvq_gptq_begin(N, K, _p(W), _p(Wq), _p(xs[0]), sp), "llvq_gptq_begin")
+    desc = make_desc(MODE_SHAPEGAIN, N, K, max_shell, shape_bits, gain_bits)
     pts = torch.empty((N, 24), dtype=torch.int8, device=dev)
     ind = torch.empty(N, dtype=torch.int64, device=dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    sptr = ctypes.c_void_p(stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream)
+    fields = torch.empty((N, kb), dtype=torch.int64, device=dev)
+    ework = torch.empty((N, 24), dtype=torch.float64, device=dev)
+    v = VARIANTS[variant]
     for b in range(kb):
-        s0, s1 = 24 * b, 24 * b + 24
-        blk = Wq[:, s0:s1]
-        xs = blk.to(torch.float32).contiguous()
-        _check(lib.llvq_search(ctypes.c_void_p(xs.data_ptr()), N, max_shell, SEARCH_ANGULAR,
-                               ctypes.c_void_p(pts.data_ptr()), ctypes.c_void_p(ind.data_ptr()),
-                               ctypes.c_void_p(err.data_ptr()), sptr), "llvq_search")
-        v = pts.to(torch.float64)
-        vhat = v / torch.linalg.vector_norm(v, dim=1, keepdim=True)
-        nrm = torch.linalg.vector_norm(blk, dim=1)
-        gi = torch.argmin(torch.abs(G[None, :] - nrm[:, None]), dim=1)    # first minimum: ties to the lower
-        idx[:, b] = ind
-        gidx[:, b] = gi
-        if variant != "direct" and s1 < K:
-            what = (G[gi] if variant == "euclid" else nrm)[:, None] * vhat
-            E = blk - what
-            Ep = torch.linalg.solve_triangular(U[s0:s1, s0:s1], E, upper=True, left=False)   # E U_SS^-1
-            Wq[:, s1:] -= Ep @ U[s0:s1, s1:]
+        x, x_next = xs[b & 1], xs[(b + 1) & 1]
+        _check(lib.llvq_search(_p(x), N, max_shell, SEARCH_ANGULAR, _p(pts), _p(ind), _p(err), sp), "llvq_search")
+        _check(lib.llvq_gptq_column(ctypes.byref(desc), b, v, _p(gains), _p(Wq), _p(U), _p(pts), _p(ind),
+                                    _p(fields), _p(ework), None if b == kb - 1 else _p(x_next), sp),
+               "llvq_gptq_column")
+    packed = torch.empty(_packed_nbytes(desc), dtype=torch.uint8, device=dev)
+    _check(lib.llvq_pack_fields(ctypes.byref(desc), _p(fields), _p(packed), sp), "llvq_pack_fields")
     if int(err.item()) != 0:
-        raise RuntimeError("search returned invalid points (non-finite weights?)")
-    desc = make_desc(MODE_SHAPEGAIN, N, K0, max_shell, shape_bits, gain_bits)
-    fields = idx | (gidx << shape_bits)
-    packed = torch.empty(packed_bytes(desc), dtype=torch.uint8, device=dev)
-    _check(lib.llvq_pack_fields(ctypes.byref(desc), ctypes.c_void_p(fields.data_ptr()),
-                                ctypes.c_void_p(packed.data_ptr()), sptr), "llvq_pack_fields")
-    return desc, packed, idx, gidx
+        raise RuntimeError("GPTQ: Hessian not positive definite after damping, or non-finite weights")
+    return desc, packed, fields
