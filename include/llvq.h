@@ -59,9 +59,13 @@ enum {
   LLVQ_OK = 0,
   LLVQ_EINVAL = -1,        /* invalid argument (null pointer, bad size, bad descriptor) */
   LLVQ_EUNSUPPORTED = -2,  /* valid request this build does not implement              */
-  LLVQ_EHIP = -3,          /* the HIP runtime reported an error at launch              */
+  LLVQ_EHIP = -3,          /* the HIP runtime reported an error at launch (see below)  */
   LLVQ_ETOOLARGE = -4      /* more blocks than llvq_quantize_noalloc's fixed workspace */
 };
+/* LLVQ_EHIP: after its launches an entry point reads (and so clears) the calling thread's
+ * last HIP error, as hipGetLastError does.  An error left pending by an earlier HIP call
+ * of the same thread is therefore reported by the next LLVQ call as LLVQ_EHIP; the call's
+ * own launches have still been made. */
 
 enum { LLVQ_MODE_EUCLID = 0, LLVQ_MODE_SHAPEGAIN = 1 };
 enum { LLVQ_OUT_POINTS_I8 = 0, LLVQ_OUT_BF16 = 1 };
@@ -274,6 +278,15 @@ int llvq_gptq_begin(int32_t rows, int32_t cols, const float* W, double* Wq, floa
 int llvq_gptq_column(const llvq_desc* d, int32_t block, int32_t variant, const void* gains, double* Wq,
                      const double* U, const int8_t* points, const uint64_t* indices, uint64_t* fields,
                      double* ework, float* x_next, void* stream);
+
+/* Invariant checks inside the kernels (a library built with LLVQ_DEVICE_CHECKS, for tests):
+ * class and table indices in range, a positive count for every chosen value slot, queue
+ * and ring capacities, codeword index below A.  A failed check adds one to a device
+ * counter; nothing traps.  Writes the counter to *failures (host memory) and clears it when
+ * reset != 0; synchronises with the device (it copies from a device symbol).  Returns
+ * LLVQ_OK, LLVQ_EINVAL (failures NULL), LLVQ_EHIP, or LLVQ_EUNSUPPORTED in a library built
+ * without the checks. */
+int llvq_device_checks(uint32_t* failures, int32_t reset);
 
 /* llvq_quantize for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and the

@@ -26,6 +26,14 @@
 #define __forceinline__ inline
 #define __global__ static inline
 #define __launch_bounds__(x)
+// the in-kernel invariant checks of the device-checks build: fatal here
+#define LLVQ_DCHECK(cond)                                           \
+  do {                                                              \
+    if (!(cond)) {                                                  \
+      fprintf(stderr, "invariant failed: %s (line %d)\n", #cond, __LINE__); \
+      abort();                                                      \
+    }                                                               \
+  } while (0)
 
 struct HostDim3 {
   unsigned x, y, z;

@@ -11,6 +11,11 @@
 * the build-time table generator (128-bit class starts, bucket tables, generated code)
   under the same sanitizers: it must run clean and write exactly the files of the normal
   build.
+* the whole library source (csrc/llvq.hip) with its host side under the same sanitizers,
+  driven by tests/host_build/abi_host.cpp through the C ABI with arguments that every entry
+  point must refuse before any launch (bad descriptors, null and misaligned pointers, sizes
+  out of range, the no-allocation quantiser's size limit), plus the pure host queries.
+  Device code is compiled at -O0 here: nothing of it runs.
 """
 
 import os
@@ -122,6 +127,25 @@ def test_rank_rejects_non_members(wide_host):
     got = _rank(wide_host, 16, pts)
     assert got == want
     assert sum(w is None for w in want) > 0
+
+
+def test_c_abi_validation_is_clean_under_sanitizers(tables, tmp_path):
+    try:
+        hipcc = build_lib.hipcc_path()
+    except RuntimeError:
+        pytest.skip("needs hipcc")
+    exe = str(tmp_path / "abi_host")
+    host = [a for f in SAN for a in ("-Xarch_host", f)]
+    subprocess.run([hipcc, f"--offload-arch={build_lib.OFFLOAD_ARCH}", "-O1", "-g", "-std=c++17",
+                    "-Xarch_device", "-O0", *host,
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                    "-I", build_lib.INCLUDE, "-I", build_lib.CSRC, "-I", tables, "-o", exe,
+                    os.path.join(build_lib.CSRC, "llvq.hip"), os.path.join(HERE, "host_build", "abi_host.cpp")],
+                   check=True, capture_output=True)
+    p = subprocess.run([exe], capture_output=True, text=True, env=ENV, timeout=120)
+    assert p.returncode == 0, p.stdout[-1000:] + p.stderr[-3000:]
+    assert "runtime error" not in p.stderr and "AddressSanitizer" not in p.stderr, p.stderr[-3000:]
+    assert p.stdout.startswith("ok ") and int(p.stdout.split()[1]) >= 70
 
 
 def test_table_generator_is_clean_under_sanitizers(tables, tmp_path):

@@ -23,13 +23,14 @@ _ERRORS = {0: "ok", -1: "invalid argument", -2: "unsupported request", -3: "HIP 
            -4: "request larger than the library's fixed workspace"}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllvq.so")
+CHECKS_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllvq_checks.so")
 
 EXPORTED_SYMBOLS = ("llvq_index_count", "llvq_packed_bytes", "llvq_error_string",
                     "llvq_decode", "llvq_gemv", "llvq_encode_ref", "llvq_search", "llvq_quantize_workspace_bytes",
                     "llvq_quantize", "llvq_pack_fields", "llvq_decode_many",
                     "llvq_index_count_wide", "llvq_encode_wide", "llvq_quantize_noalloc",
                     "llvq_quantize_noalloc_max_blocks", "llvq_gptq_workspace_bytes", "llvq_gptq_factor",
-                    "llvq_gptq_begin", "llvq_gptq_column")
+                    "llvq_gptq_begin", "llvq_gptq_column", "llvq_device_checks")
 
 
 class LlvqError(RuntimeError):
@@ -102,6 +103,8 @@ def load_library(path=LIB_PATH):
     lib.llvq_gptq_begin.restype = ctypes.c_int
     lib.llvq_gptq_column.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.llvq_gptq_column.restype = ctypes.c_int
+    lib.llvq_device_checks.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
+    lib.llvq_device_checks.restype = ctypes.c_int
     lib.llvq_pack_fields.argtypes = [dp, vp, vp, vp]
     lib.llvq_pack_fields.restype = ctypes.c_int
     lib.llvq_decode_many.argtypes = [vp, i32, vp, vp, i32, vp, vp, vp]

@@ -65,9 +65,15 @@ def hipcc_path():
     return p
 
 
-def build(verbose=True):
+CHECKS_LIB_PATH = os.path.join(PKG_DIR, "libllvq_checks.so")
+
+
+def build(verbose=True, device_checks=False):
+    """Build libllvq.so, or with device_checks the same library with the in-kernel invariant
+    checks on (LLVQ_DEVICE_CHECKS) as libllvq_checks.so, for tests."""
     build_tables(verbose)
-    tmp = LIB_PATH + ".tmp"
+    out = CHECKS_LIB_PATH if device_checks else LIB_PATH
+    tmp = out + ".tmp"
     cmd = [
         hipcc_path(),
         f"--offload-arch={OFFLOAD_ARCH}",
@@ -84,11 +90,14 @@ def build(verbose=True):
         "-o", tmp,
         os.path.join(CSRC, "llvq.hip"),
     ]
+    if device_checks:
+        cmd.insert(1, "-DLLVQ_DEVICE_CHECKS")
     _run(cmd, verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
     build(verbose=True)
+    build(verbose=True, device_checks=True)
     sys.exit(0)

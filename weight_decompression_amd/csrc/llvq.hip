@@ -76,6 +76,22 @@ namespace dev_tables {
 #undef LLVQ_TABLE
 }  // namespace dev_tables
 
+// Device checks (build flag LLVQ_DEVICE_CHECKS): invariants the kernels rely on for their
+// memory accesses and for exact decoding are tested in the kernels, and every failure adds
+// one to a device counter that llvq_device_checks reads.  Nothing traps; a normal build
+// compiles the checks away.
+#ifdef LLVQ_DEVICE_CHECKS
+__device__ unsigned int g_llvq_check_failures;
+#define LLVQ_DCHECK(cond)                                               \
+  do {                                                                  \
+    if (!(cond)) atomicAdd(&g_llvq_check_failures, 1u);                 \
+  } while (0)
+#else
+#define LLVQ_DCHECK(cond) \
+  do {                    \
+  } while (0)
+#endif
+
 namespace {
 
 constexpr int kDim = 24;
@@ -1194,4 +1210,21 @@ LLVQ_API int llvq_gptq_column(const llvq_desc* d, int32_t block, int32_t variant
     }
   }
   return launch_status();
+}
+
+LLVQ_API int llvq_device_checks(uint32_t* failures, int32_t reset) {
+#ifdef LLVQ_DEVICE_CHECKS
+  if (!failures) return LLVQ_EINVAL;
+  if (hipMemcpyFromSymbol(failures, HIP_SYMBOL(g_llvq_check_failures), sizeof(uint32_t)) != hipSuccess)
+    return LLVQ_EHIP;
+  if (reset) {
+    const uint32_t zero = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_llvq_check_failures), &zero, sizeof(uint32_t)) != hipSuccess) return LLVQ_EHIP;
+  }
+  return LLVQ_OK;
+#else
+  (void)failures;
+  (void)reset;
+  return LLVQ_EUNSUPPORTED;
+#endif
 }

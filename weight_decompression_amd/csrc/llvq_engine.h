@@ -176,6 +176,7 @@ __device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELa
   BlockStart bs;
   const uint32_t q = (uint32_t)__builtin_fma(Jd, h.inv_a, 0x1p-13);    // floor(J / A), exact
   const uint32_t r = (uint32_t)__builtin_fma(-(double)q, h.a, Jd);      // J - q A, exact
+  LLVQ_DCHECK((double)r < h.a);
   const uint32_t B = h.meta & 31u;
   bs.s = q & ((1u << B) - 1u);
   const uint32_t R = q >> B;
@@ -188,8 +189,10 @@ __device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELa
 // the counts left (times 8, sum 48) and y in [0, 6).
 __device__ __forceinline__ uint32_t tail_codes(const uint8_t* smem, const ELayout& L, uint32_t cnt8, double y) {
   const uint32_t ci8 = __builtin_amdgcn_udot4(cnt8, 0x00310701u, 0u, false);   // 8 (c0 + 7 c1 + 49 c2)
+  LLVQ_DCHECK(ci8 < 343u * 8u);
   const LlvqTailComp tc = *reinterpret_cast<const LlvqTailComp*>(smem + L.tcomp + ci8);
   const uint32_t r = (uint32_t)((float)y * tc.q_over_6);
+  LLVQ_DCHECK(tc.offset + r < 4096u && (float)r < tc.q_over_6 * 6.0f);
   return reinterpret_cast<const uint16_t*>(smem + L.tail)[tc.offset + r];
 }
 
@@ -206,6 +209,7 @@ __device__ __forceinline__ StepOut decode_step(const uint8_t* smem, double& y, u
   const uint32_t k = bcnt_addv(g, sel);
   const uint32_t c8 = __builtin_amdgcn_perm(cnt8, cnt8, k);        // 8 c_k (selector 0..7)
   const uint32_t C8 = __builtin_amdgcn_udot4(g, cnt8, 0u, false);  // 8 C_k
+  LLVQ_DCHECK(c8 != 0u && c8 <= 192u && fo + c8 < 25u * kFRow);    // the chosen slot has values left
   const double fac = ftab_at(smem, fo + c8);                       // n' / (8 c_k)
   y = __builtin_fma(y, 8.0, -(double)C8) * fac;
   cnt8 -= dec8(g);
@@ -555,6 +559,7 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
   for (int t = 0; t < kPer; ++t) {
     const int f = u * kEUnit + t * 64 + lane;
     const uint32_t k = kk[t];
+    LLVQ_DCHECK(!valid[t] || (int)k < d.ncls);
     const LlvqClassHot& h = cls[k];
     const bool odd = ((h.meta >> 17) & 1u) != 0u;
     // J = I - start as the low bits of 2^52 + J (exact: J < 2^41 < 2^52)
@@ -593,6 +598,7 @@ __device__ __forceinline__ void classify_fields(uint8_t* smem, const ELayout& L,
   for (int t = 0; t < kPer; ++t) {
     const bool odd = (bo[t] >> lane) & 1u;
     const bool even = (be[t] >> lane) & 1u;
+    LLVQ_DCHECK(!(odd || even) || baseo + (int)po[t] < T - (basee + (int)pe[t]));
     if (odd) queue[baseo + (int)po[t]] = entry[t];
     if (even) queue[T - 1 - (basee + (int)pe[t])] = entry[t];
     baseo += __popcll(bo[t]);

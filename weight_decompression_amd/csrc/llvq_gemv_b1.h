@@ -187,6 +187,7 @@ __device__ __forceinline__ void classify_lane(uint8_t* smem, const ELayout& L, f
   if (__ballot(c2)) {
     while (Id >= cls[k + 1].start) ++k;             // the sentinel records end the scan
   }
+  LLVQ_DCHECK(!valid || (int)k < d.ncls);
   const LlvqClassHot& h = cls[k];
   const bool odd = ((h.meta >> 17) & 1u) != 0u;
   // J = I - start as the low bits of 2^52 + J (exact: J < 2^41 < 2^52)
@@ -207,6 +208,7 @@ __device__ __forceinline__ void classify_lane(uint8_t* smem, const ELayout& L, f
   if (valid && !odd) R.even[(R.eh + R.en + pe) & (kRing - 1)] = entry;
   R.on += (uint32_t)__popcll(bo);
   R.en += (uint32_t)__popcll(be);
+  LLVQ_DCHECK(R.on < (uint32_t)kRing && R.en < (uint32_t)kRing);
 }
 
 template <bool XF32>
@@ -307,6 +309,7 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
     }
     bo = __builtin_amdgcn_readfirstlane(bo);
     be = __builtin_amdgcn_readfirstlane(be);
+    LLVQ_DCHECK(bo + (int)R.on <= kLeftEven && be + (int)R.en <= kLeftEven && R.on < 64u && R.en < 64u);
     const uint64_t lo = (uint32_t)lane < R.on ? R.odd[(R.oh + (uint32_t)lane) & (kRing - 1)] : 0ull;
     const uint64_t le = (uint32_t)lane < R.en ? R.even[(R.eh + (uint32_t)lane) & (kRing - 1)] : 0ull;
     __syncthreads();                        // every ring read; the queue may overwrite them

@@ -160,6 +160,7 @@ __device__ __forceinline__ uint64_t bytes8(const uint8_t* p) {
 __device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M, int v[kDim]) {
   const uint64_t* inv = dev_tables::kWideOddInverse;
   const int k = wide_find_class(lo, hi, M);
+  LLVQ_DCHECK(k >= 0 && k < LLVQ_WIDE_NUM_CLASSES && dev_tables::kWideClass[k].m <= M);
   const LlvqWideClass& cr = dev_tables::kWideClass[k];
   const uint64_t J = lo - cr.start_lo;      // < 2^63: the high words cancel
   const int w = cr.w;
@@ -222,6 +223,7 @@ __device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M
       const uint64_t over = (run + (uint64_t)(127 - fy) * 0x0101010101010101ull) & 0x8080808080808080ull;
       kk = 8u - (uint32_t)__popcll(over);
       const uint32_t ck = (uint32_t)(U.cnts >> (8 * kk)) & 0xffu;
+      LLVQ_DCHECK(kk < 8u && ck != 0u);
       const uint32_t below = kk ? (uint32_t)(run >> (8 * (kk - 1))) & 0xffu : 0u;
       U.u = (y - (double)below) / (double)ck;
     } else {
@@ -239,6 +241,7 @@ __device__ __forceinline__ int wide_decode_point(uint64_t lo, uint64_t hi, int M
         upto += U.rem * ck;
       }
       // new rank and count of arrangements: exact quotients by n
+      LLVQ_DCHECK(U.n >= 1u && U.n <= 24u && ck != 0u && t_n < upto);
       const uint32_t tz = (uint32_t)__builtin_ctz(U.n);
       const uint64_t iv = inv[U.n >> (tz + 1)];
       U.rank = ((t_n - below) >> tz) * iv;
