@@ -194,10 +194,16 @@ def roofline(profile_key, ops_units, sec, alg_bytes, per_unit_text, launches=1):
     if prof_ok and prof.get("valu_lane_ops_per_unit"):
         ops = prof["valu_lane_ops_per_unit"] * ops_units
         peak = prof.get("valu_peak_tops", VALU_PEAK_TOPS)
-        return {"bound": "alu", "achieved": ops / sec / 1e12, "peak": peak, "unit": "TOP/s",
-                "frac": ops / sec / 1e12 / peak, "traffic": traffic,
-                "valu_lane_ops_per_unit": prof["valu_lane_ops_per_unit"], "unit_of_work": prof["unit_of_work"],
-                "profile": prof["summary"], "hbm": hbm}
+        out = {"bound": "alu", "achieved": ops / sec / 1e12, "peak": peak, "unit": "TOP/s",
+               "frac": ops / sec / 1e12 / peak, "traffic": traffic,
+               "valu_lane_ops_per_unit": prof["valu_lane_ops_per_unit"], "unit_of_work": prof["unit_of_work"],
+               "profile": prof["summary"], "hbm": hbm}
+        if prof.get("valu_mix_peak_tops"):
+            # the peak weighted by the kernel's executed instruction mix (per-type SQ counters,
+            # measured issue rates): the same achieved rate against it
+            out["mix_peak"] = prof["valu_mix_peak_tops"]
+            out["frac_mix"] = ops / sec / 1e12 / prof["valu_mix_peak_tops"]
+        return out
     roof = dict(hbm)
     roof["traffic"] = traffic
     roof["note"] = "VALU instructions not profiled for this kernel source"

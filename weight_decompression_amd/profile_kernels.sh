@@ -7,9 +7,13 @@
 #   pmc_valu       SQ counters (VALU / LDS / SALU instructions, wave cycles)
 #   pmc_fetch      FETCH_SIZE;  pmc_write  WRITE_SIZE
 #   copy_fetch, copy_write   the same two counters over a plain 256 MiB device copy
+#   mix_a, mix_b   the per-type VALU counters (issue_rates.MIX_PASSES)
 # then writes OUTDIR/summary.md with one section per KERNEL (a substring of the kernel
 # name), UNITS its work units per launch (24-blocks or points) and ALG_BYTES its
-# algorithmic HBM bytes per launch.
+# algorithmic HBM bytes per launch; KERNEL may carry a fourth field, the substring of the
+# mangled symbol whose device assembly gives the static split inside each counter category.
+# With RATES_MD (default profiles/valu_issue_rates_gfx950.md, written by profile_rates.sh)
+# the summary also gives each kernel's dynamic-mix VALU peak (issue_rates.mix_peak).
 set -o pipefail
 OUT="$(cd "$(dirname "$1")" && pwd)/$(basename "$1")"
 ARGS="$2"
@@ -26,6 +30,12 @@ run valu timeout -s KILL 300 rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_INST
 run fetch timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/pmc_fetch" -o pmc -- \
   python3 "$REPO/bench.py" --no-cpu $ARGS
 run write timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/pmc_write" -o pmc -- \
+  python3 "$REPO/bench.py" --no-cpu $ARGS
+PASS_A="SQ_INSTS_VALU SQ_INSTS_VALU_INT32 SQ_INSTS_VALU_INT64 SQ_INSTS_VALU_CVT SQ_INSTS_VALU_FMA_F64 SQ_INSTS_VALU_MUL_F64 SQ_INSTS_VALU_ADD_F64 SQ_INSTS_VALU_TRANS_F64"
+PASS_B="SQ_INSTS_VALU SQ_INSTS_VALU_FMA_F32 SQ_INSTS_VALU_ADD_F32 SQ_INSTS_VALU_MUL_F32 SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_MFMA SQ_INSTS_VALU_MFMA_BF16"
+run mix_a timeout -s KILL 300 rocprofv3 --pmc $PASS_A --output-format csv -d "$OUT/mix_a" -o pmc -- \
+  python3 "$REPO/bench.py" --no-cpu $ARGS
+run mix_b timeout -s KILL 300 rocprofv3 --pmc $PASS_B --output-format csv -d "$OUT/mix_b" -o pmc -- \
   python3 "$REPO/bench.py" --no-cpu $ARGS
 run copy_fetch timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/copy_fetch" -o pmc -- \
   python3 "$REPO/bench.py" --copy-calibration 256

@@ -8,7 +8,10 @@ device copy of known size) and prints, for each kernel asked for:
 * SQ_INSTS_VALU x 64 / units = VALU lane-operations per work unit (24-block or point),
   and the VALU utilisation against 256 CUs x 64 lanes x 2.4 GHz;
 * FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the factor that maps the
-  counter to the known byte count of the copy kernel, next to the algorithmic bytes.
+  counter to the known byte count of the copy kernel, next to the algorithmic bytes;
+* when the per-type counter passes (mix_a, mix_b) and an issue-rate table are there: the
+  kernel's executed VALU instructions per counter category and its dynamic-mix peak
+  (issue_rates.mix_peak), and the utilisation against that peak.
 
 Usage: python -m weight_decompression_amd.profile_summary OUTDIR "BENCH ARGS" KERNEL:UNITS:ALG_BYTES [...]
 """
@@ -17,6 +20,8 @@ import csv
 import os
 import sys
 from collections import defaultdict
+
+from . import issue_rates
 
 VALU_PEAK = 256 * 64 * 2.4e9
 COPY_BYTES = 256 * 1024 * 1024
@@ -43,6 +48,39 @@ def _copy_kib(path, counter):
     return sum(vals) / len(vals) if vals else None
 
 
+def _mix_section(outdir, kernel, symbol, avg_ns, units, rates_md, asm):
+    a, _ = _pmc(os.path.join(outdir, "mix_a"), kernel)
+    b, _ = _pmc(os.path.join(outdir, "mix_b"), kernel)
+    dyn = dict(a)
+    dyn.update(b)
+    dyn["SQ_INSTS_VALU"] = a["SQ_INSTS_VALU"]
+    rates, cats = issue_rates.read_rates_md(rates_md)
+    static = issue_rates.kernel_mix(asm, symbol)
+    rate, table, unplaced = issue_rates.mix_peak(dyn, static, rates, cats)
+    peak = rate * issue_rates.NCU * 64 * issue_rates.CLOCK_HZ
+    util = dyn["SQ_INSTS_VALU"] * 64 / (avg_ns * 1e-9) / peak
+    lines = [f"Dynamic VALU mix (per dispatch; static split inside a category from `{symbol}`):", "",
+             "| category | instructions | share | static-split rate | most frequent in the assembly |",
+             "|---|---|---|---|---|"]
+    tot = sum(n for _, n, _, _ in table)
+    for c, n, r, used in table:
+        lines.append(f"| {c} | {n:.0f} | {n / tot:.3f} | {r:.3f} | {used} |")
+    lines.append("")
+    if dyn.get("SQ_INSTS_MFMA"):
+        lines.append(f"MFMA instructions (matrix pipe, left out of the VALU mix): {dyn['SQ_INSTS_MFMA']:.0f}")
+    if dyn.get("SQ_ACTIVE_INST_VALU2") is not None:
+        lines.append(f"SQ_ACTIVE_INST_VALU2 (quad-cycles with two VALU issues): {dyn['SQ_ACTIVE_INST_VALU2']:.0f}")
+    if unplaced:
+        lines.append("Static instructions without a measured rate or category (left out of the split): " +
+                     ", ".join(f"{i} {k}" for i, k in unplaced.most_common(8)))
+    lines.append("")
+    lines.append(f"* dynamic-mix VALU peak = **{rate:.3f}** wave-instructions per CU per clock = "
+                 f"**{peak / 1e12:.2f} T lane-ops/s**")
+    lines.append(f"* VALU utilisation against it at the traced average duration = **{util:.3f}**")
+    lines.append("")
+    return lines, peak
+
+
 def summarise(outdir, bench_args, specs):
     lines = ["# rocprofv3 summary: bench.py " + bench_args, ""]
     lines.append("Command (from the repository root):")
@@ -59,8 +97,19 @@ def summarise(outdir, bench_args, specs):
     lines.append(f"HBM counter calibration: a device copy of {COPY_BYTES} B reads FETCH_SIZE = {cf:.2f} KiB "
                  f"(factor {ff:.4f}) and WRITE_SIZE = {cw:.2f} KiB (factor {fw:.4f}).")
     lines.append("")
+    rates_md = os.environ.get("RATES_MD") or os.path.join(issue_rates.PKG_DIR, "..", "profiles",
+                                                          "valu_issue_rates_gfx950.md")
+    do_mix = os.path.isdir(os.path.join(outdir, "mix_a")) and os.path.isdir(os.path.join(outdir, "mix_b")) \
+        and os.path.exists(rates_md)
+    asm = None
+    if do_mix:
+        asm = os.environ.get("LLVQ_ASM") or issue_rates.device_asm(outdir)
+        lines.append(f"Issue rates and counter categories: `{os.path.relpath(rates_md, issue_rates.PKG_DIR + '/..')}`.")
+        lines.append("")
     for spec in specs:
-        kernel, units, alg = spec.split(":")
+        f = spec.split(":")
+        kernel, units, alg = f[:3]
+        symbol = f[3] if len(f) > 3 else kernel
         units = int(units)
         alg = float(alg)
         st = [r for r in stats if kernel in r["Name"]]
@@ -96,8 +145,13 @@ def summarise(outdir, bench_args, specs):
                      f"-> {wb:.0f} B; total **{fb + wb:.0f} B** per launch")
         lines.append(f"* algorithmic bytes per launch {alg:.0f}; measured / algorithmic = {(fb + wb) / alg:.3f}")
         lines.append("")
+        mix_peak = None
+        if do_mix:
+            ml, mix_peak = _mix_section(outdir, kernel, symbol, avg_ns, units, rates_md, asm)
+            lines += ml
+        mp = "" if mix_peak is None else f" valu_mix_peak_tops={mix_peak / 1e12:.2f}"
         lines.append(f"<!-- profile {kernel} valu_lane_ops_per_unit={per_unit:.1f} fetch={fb:.0f} write={wb:.0f} "
-                     f"avg_ns={avg_ns:.0f} -->")
+                     f"avg_ns={avg_ns:.0f}{mp} -->")
         lines.append("")
     return "\n".join(lines) + "\n"
 
