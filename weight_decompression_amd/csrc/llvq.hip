@@ -224,7 +224,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 #include "llvq_gemv_b1.h"
 #include "llvq_tile.h"
 #include "llvq_gemm.h"
-#include "llvq_many.h"
+#include "llvq_stream.h"
 #include "llvq_wide.h"
 
 // ---------------------------------------------------------------------------
@@ -534,11 +534,12 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;   // 32-bit field index
   const bool xf32 = x_dtype == LLVQ_X_F32;
   const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
-  // LDS: fixed tables, the waves' rings, 4 bytes per block of the tile (its slot), x, xsum
+  // LDS: fixed tables and the Golay table, the waves' rings, 4 bytes per block of the
+  // tile (its slot), x
   ELayout L;
   const uint32_t xbytes = align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u));
   const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 1);
-  const uint32_t fixed = base + (uint32_t)kRingBytes + xbytes + 16u;
+  const uint32_t fixed = base + 4096u * 4u + (uint32_t)kRingBytes + xbytes + 16u;
   if (fixed + 4u * (uint32_t)k.kb > kLdsBudget) return LLVQ_EUNSUPPORTED;
   int tmax = (int)((kLdsBudget - fixed) / 4u);
   if (tmax > kETileMax) tmax = kETileMax;
@@ -560,7 +561,8 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   }
   a.nbuckets = nbuckets;
   engine_layout_base(a.L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 1);
-  a.rings = align16(a.L.total);
+  a.L.golay = align16(a.L.total);
+  a.rings = a.L.golay + 4096u * 4u;
   a.L.buf[0].part = a.rings + (uint32_t)kRingBytes;
   a.xs = align16(a.L.buf[0].part + 4u * (uint32_t)(a.rows_per_tile * k.kb));
   const uint32_t total = a.xs + align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u));
@@ -574,56 +576,53 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   return launch_status();
 }
 
-// Whole-tensor decode through the byte tile (llvq_tile.h).  LLVQ_EUNSUPPORTED when the
-// shape does not fit (the one-block-per-lane kernels then run).
-int launch_decode_tile(const KDesc& k, const void* packed, const void* scales, int32_t out_kind, void* out,
-                       int32_t* err, hipStream_t s) {
-  if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;
-  const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
-  // LDS per block: queue entry 8 B + scale 4 B per tile buffer, 24 value bytes.  One buffer
-  // when every workgroup's rows fit one tile (and that costs the busiest workgroup no more),
-  // else two, the next tile classified during the decode of the current one.
-  ELayout L;
-  const int ng = 1 << k.gain_bits;
-  const uint32_t base2 = engine_layout_base(L, k.ncls, ng, nbuckets, 0, 2);
-  int r2 = 0, nt2 = 0, g2 = 0;
-  long cost2 = -1;
-  if (base2 + 64u + 48u * (uint32_t)k.kb <= kLdsBudget) {
-    int tmax2 = (int)((kLdsBudget - base2 - 64u) / 48u) & ~15;
-    if (tmax2 > kETileMax) tmax2 = kETileMax;
-    r2 = pick_rows_per_tile(k.rows, k.kb, tmax2, &nt2, &g2);
-    if (r2 > 0) cost2 = (long)((nt2 + g2 - 1) / g2) * ((long)r2 * k.kb + kTileOverhead);
-  }
-  const uint32_t base1 = engine_layout_base(L, k.ncls, ng, nbuckets, 0, 1);
-  const int r1 = (k.rows + kGridMax - 1) / kGridMax;
-  const long t1 = (long)r1 * k.kb;
-  EArgs a = {};
-  int grid = 0, nbuf = 2;
-  if (t1 <= kETileMax && base1 + 64u + 36u * (uint32_t)t1 <= kLdsBudget &&
-      (cost2 < 0 || t1 + kTileOverhead <= cost2)) {
-    nbuf = 1;
-    a.rows_per_tile = r1;
-    a.ntiles = (k.rows + r1 - 1) / r1;
-    grid = a.ntiles;
-  } else {
-    if (r2 == 0) return LLVQ_EUNSUPPORTED;
-    a.rows_per_tile = r2;
-    a.ntiles = nt2;
-    grid = g2;
-  }
-  a.nbuckets = nbuckets;
-  const int T = a.rows_per_tile * k.kb;
-  engine_layout_base(a.L, k.ncls, ng, nbuckets, T, nbuf);
-  a.xs = a.L.total;
-  a.xsum = 0;
-  const uint32_t total = a.xs + align16(24u * (uint32_t)T);
+// Streamed decode of one or several tensors (llvq_stream.h): LDS holds the tables (with
+// the Golay table), the waves' rings, the lanes' 24-byte value slots and 4 bytes per
+// block of a tile.
+// LLVQ_EUNSUPPORTED when a row does not fit a tile (the caller then falls back).
+int launch_decode_stream(const KDesc* k, int n, const void* const* packed, const void* const* scales,
+                         int32_t out_kind, void* const* outs, int32_t* err, hipStream_t s) {
+  const KDesc& k0 = k[0];
+  const int nbuckets = (int)(((host_tables::kIndexCount[k0.max_shell] - 1) >> k0.bshift) + 1);
+  const int ng = (k0.mode == LLVQ_MODE_SHAPEGAIN ? 1 << k0.gain_bits : 1) * n;
+  SArgs m = {};
+  const uint32_t base = engine_layout_base(m.L, k0.ncls, ng, nbuckets, 0, 1);
+  m.L.golay = align16(base);
+  m.rings = m.L.golay + 4096u * 4u;
+  m.part = m.rings + (uint32_t)kRingBytes;
+  const uint32_t fixed = m.part + (uint32_t)kStageBytes + 32u;
+  if (fixed >= kLdsBudget) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((kLdsBudget - fixed) / 4u) & ~15;
+  if (tmax > kETileMax) tmax = kETileMax;
+  m.tmax = tmax;
+  m.stage = align16(m.part + 4u * (uint32_t)tmax);
+  const uint32_t total = m.stage + (uint32_t)kStageBytes;
   if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  m.nbuckets = nbuckets;
+  m.n = n;
+  long long blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    if (k[i].kb > tmax || (uint64_t)k[i].rows * (uint64_t)k[i].kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;
+    STensor& t = m.t[i];
+    t.packed = static_cast<const uint8_t*>(packed[i]);
+    t.scales = scales ? static_cast<const __half*>(scales[i]) : nullptr;
+    t.out = outs[i];
+    t.rows = k[i].rows;
+    t.cols = k[i].cols;
+    t.kb = k[i].kb;
+    t.blk0 = blocks;
+    blocks += (long long)k[i].rows * k[i].kb;
+  }
+  m.total = blocks;
+  // at least ~2K blocks per workgroup, at most one workgroup per CU
+  long long g = (blocks + 2047) / 2048;
+  if (g > kGridMax) g = kGridMax;
+  if (g < 1) g = 1;
   if (out_kind == LLVQ_OUT_POINTS_I8)
-    hipLaunchKernelGGL((k_decode_tile<LLVQ_OUT_POINTS_I8>), dim3(grid), dim3(kEThreads), total, s, k, a,
-                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), out, err);
+    hipLaunchKernelGGL((k_decode_stream<LLVQ_OUT_POINTS_I8>), dim3((unsigned)g), dim3(kEThreads), total, s, k0, m,
+                       err);
   else
-    hipLaunchKernelGGL((k_decode_tile<LLVQ_OUT_BF16>), dim3(grid), dim3(kEThreads), total, s, k, a,
-                       static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), out, err);
+    hipLaunchKernelGGL((k_decode_stream<LLVQ_OUT_BF16>), dim3((unsigned)g), dim3(kEThreads), total, s, k0, m, err);
   return launch_status();
 }
 
@@ -770,8 +769,11 @@ LLVQ_API int llvq_decode(const llvq_desc* d, const void* packed, const void* sca
     return LLVQ_EINVAL;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int st1 = launch_decode_tile(k, packed, out_kind == LLVQ_OUT_BF16 ? scales : nullptr, out_kind, out,
-                                     err_count, s);
+  const void* pk[1] = {packed};
+  const void* sc[1] = {out_kind == LLVQ_OUT_BF16 ? scales : nullptr};
+  void* oo[1] = {out};
+  const int st1 = launch_decode_stream(&k, 1, pk, out_kind == LLVQ_OUT_BF16 ? sc : nullptr, out_kind, oo,
+                                       err_count, s);
   if (st1 != LLVQ_EUNSUPPORTED) return st1;
   const uint64_t nblocks = (uint64_t)k.rows * (uint64_t)k.kb;
   const unsigned block = 256;
@@ -785,53 +787,6 @@ LLVQ_API int llvq_decode(const llvq_desc* d, const void* packed, const void* sca
                      static_cast<uint16_t*>(out), err_count);
   return launch_status();
 }
-
-namespace {
-// One launch for several tensors (llvq_many.h): tiles of at most tmax blocks (two tile
-// buffers), each tensor's rows cut into the largest tiles that fit.  LLVQ_EUNSUPPORTED
-// when a row does not fit a tile (the caller then decodes tensor by tensor).
-int launch_decode_many(const KDesc* k, int n, const void* const* packed, const void* const* scales,
-                       int32_t out_kind, void* const* outs, int32_t* err, hipStream_t s) {
-  const KDesc& k0 = k[0];
-  const int nbuckets = (int)(((host_tables::kIndexCount[k0.max_shell] - 1) >> k0.bshift) + 1);
-  const int ng = (k0.mode == LLVQ_MODE_SHAPEGAIN ? 1 << k0.gain_bits : 1) * n;
-  ELayout L;
-  const uint32_t base2 = engine_layout_base(L, k0.ncls, ng, nbuckets, 0, 2);
-  if (base2 + 64u + 48u * 16u > kLdsBudget) return LLVQ_EUNSUPPORTED;
-  int tmax = (int)((kLdsBudget - base2 - 64u) / 48u) & ~15;
-  if (tmax > kETileMax) tmax = kETileMax;
-  MArgs m = {};
-  m.n = n;
-  int tiles = 0, Tmax = 0;
-  for (int i = 0; i < n; ++i) {
-    if (k[i].kb > tmax || (uint64_t)k[i].rows * (uint64_t)k[i].kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;
-    const int r = min(k[i].rows, tmax / k[i].kb);
-    MTensor& t = m.t[i];
-    t.packed = static_cast<const uint8_t*>(packed[i]);
-    t.scales = scales ? static_cast<const __half*>(scales[i]) : nullptr;
-    t.out = outs[i];
-    t.rows = k[i].rows;
-    t.cols = k[i].cols;
-    t.kb = k[i].kb;
-    t.rows_per_tile = r;
-    t.tile0 = tiles;
-    tiles += (k[i].rows + r - 1) / r;
-    Tmax = max(Tmax, r * k[i].kb);
-  }
-  m.ntiles = tiles;
-  m.e.nbuckets = nbuckets;
-  engine_layout_base(m.e.L, k0.ncls, ng, nbuckets, Tmax, 2);
-  m.e.xs = m.e.L.total;
-  const uint32_t total = m.e.xs + align16(24u * (uint32_t)Tmax);
-  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
-  const int grid = tiles < kGridMax ? tiles : kGridMax;
-  if (out_kind == LLVQ_OUT_POINTS_I8)
-    hipLaunchKernelGGL((k_decode_many<LLVQ_OUT_POINTS_I8>), dim3(grid), dim3(kEThreads), total, s, k0, m, err);
-  else
-    hipLaunchKernelGGL((k_decode_many<LLVQ_OUT_BF16>), dim3(grid), dim3(kEThreads), total, s, k0, m, err);
-  return launch_status();
-}
-}  // namespace
 
 LLVQ_API int llvq_decode_many(const llvq_desc* descs, int32_t n, const void* const* packed,
                               const void* const* scales, int32_t out_kind, void* const* outs, int32_t* err_count,
@@ -873,8 +828,8 @@ LLVQ_API int llvq_decode_many(const llvq_desc* descs, int32_t n, const void* con
     if (out_kind == LLVQ_OUT_BF16 && (!scales[i] || !aligned(outs[i], 2) || !aligned(scales[i], 2))) return LLVQ_EINVAL;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int st = launch_decode_many(k, n, packed, out_kind == LLVQ_OUT_BF16 ? scales : nullptr, out_kind, outs,
-                                    err_count, s);
+  const int st = launch_decode_stream(k, n, packed, out_kind == LLVQ_OUT_BF16 ? scales : nullptr, out_kind, outs,
+                                      err_count, s);
   if (st != LLVQ_EUNSUPPORTED) return st;
   for (int i = 0; i < n; ++i) {
     const int st1 = llvq_decode(&descs[i], packed[i], scales ? scales[i] : nullptr, out_kind, outs[i], err_count,

@@ -48,7 +48,7 @@ struct TileBuf {
 
 struct ELayout {
   // byte offsets inside the dynamic LDS segment
-  uint32_t ftab;      // double F[25][25]: F[r][c] = (23 - r) / (8 c), always at offset 0
+  uint32_t ftab;      // double F[25][25] (+1 pad): F[r][c] = (23 - r) / (8 c), always at offset 0
   uint32_t cls;       // LlvqClassHot[ncls + 2]: the last two are sentinels (start only, +inf)
   uint32_t gains;     // float[2^gain_bits]
   uint32_t bucket;    // uint8[nbuckets]
@@ -57,6 +57,7 @@ struct ELayout {
   uint32_t work;      // int[4]: work-item counter of the current phase
   TileBuf buf[2];     // one or two tile buffers
   uint32_t total;     // end of the engine's part; consumer data follows
+  uint32_t golay;     // uint32[4096]: a copy of the Golay codeword table, when a consumer stages one
 };
 
 __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
@@ -64,7 +65,8 @@ __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15
 __host__ __device__ inline uint32_t engine_layout_base(ELayout& L, int ncls, int ngains, int nbuckets, int tmax,
                                                       int nbuf = 1) {
   uint32_t o = 0;
-  L.ftab = o;     o = align16(o + 25u * kFStride * 8u);
+  L.ftab = o;     o = align16(o + 626u * 8u);
+  L.golay = 0u;
   L.cls = o;      o = align16(o + (uint32_t)(ncls + 2) * (uint32_t)sizeof(LlvqClassHot));
   L.gains = o;    o = align16(o + (uint32_t)ngains * 4u);
   L.bucket = o;   o = align16(o + (uint32_t)nbuckets);
@@ -171,6 +173,10 @@ struct BlockStart {
   double y;     // y_0 = (R + 1/2) * n0 / P
 };
 
+// LG: the codeword comes from the LDS copy of the Golay table at L.golay (a kernel that
+// also stores to global memory then never waits on its stores for it: on gfx9 a load's
+// wait counts every older vector-memory operation, stores included).
+template <bool LG = false>
 __device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELayout& L, double Jd,
                                                   const LlvqClassHot& h) {
   BlockStart bs;
@@ -180,7 +186,7 @@ __device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELa
   const uint32_t B = h.meta & 31u;
   bs.s = q & ((1u << B) - 1u);
   const uint32_t R = q >> B;
-  bs.c = dev_tables::kGolayTable[h.toff + r];
+  bs.c = LG ? reinterpret_cast<const uint32_t*>(smem + L.golay)[h.toff + r] : dev_tables::kGolayTable[h.toff + r];
   bs.y = __builtin_fma((double)R, h.y0s, 0.5 * h.y0s);
   return bs;
 }
@@ -422,9 +428,11 @@ __device__ __forceinline__ void copy_word_tail(uint8_t* smem, uint32_t dst, cons
     reinterpret_cast<uint32_t*>(smem + dst)[i] = reinterpret_cast<const uint32_t*>(src)[i];
 }
 
-// Tables into LDS, plus an optional extra segment (a consumer's activations).  All of a
-// lane's global loads are issued before its first LDS store, so the workgroup waits for
-// about one memory latency rather than one per copy.  The caller synchronises afterwards.
+// Tables into LDS (the step factors F, the class records, the tail tables, the bucket
+// table, the Golay table when the layout has a place for it), plus an optional extra
+// segment (a consumer's activations).  All of a lane's global loads are issued before its
+// first LDS store, so the workgroup waits for about one memory latency rather than one
+// per copy.  The caller synchronises afterwards.
 __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L, const KDesc& d, int nbuckets,
                                                 const __half* __restrict__ scales, int tid,
                                                 CopySeg extra = {nullptr, 0u, 0}) {
@@ -435,16 +443,15 @@ __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L,
   const CopySeg s_tail = {reinterpret_cast<const uint4*>(dev_tables::kTail6), L.tail, 4096 * 2 / 16};
   const CopySeg s_tcomp = {reinterpret_cast<const uint4*>(dev_tables::kTailComp), L.tcomp, (343 * 2) >> 2};
   const CopySeg s_bk = {reinterpret_cast<const uint4*>(bk_src), L.bucket, bk_w >> 2};
+  const CopySeg s_f = {reinterpret_cast<const uint4*>(dev_tables::kFTable), L.ftab, 626 * 8 / 16};
+  const CopySeg s_g = {reinterpret_cast<const uint4*>(dev_tables::kGolayTable), L.golay, L.golay ? 4096 * 4 / 16 : 0};
   const CopyRegs v_cls = copy_issue(s_cls, tid);
   const CopyRegs v_tail = copy_issue(s_tail, tid);
   const CopyRegs v_tcomp = copy_issue(s_tcomp, tid);
   const CopyRegs v_bk = copy_issue(s_bk, tid);
+  const CopyRegs v_f = copy_issue(s_f, tid);
+  const CopyRegs v_g = copy_issue(s_g, tid);
   const CopyRegs v_x = copy_issue(extra, tid);
-  double* F = reinterpret_cast<double*>(smem + L.ftab);
-  for (int i = tid; i < 25 * kFStride; i += kEThreads) {
-    const int r = i / kFStride, c = i - r * kFStride;
-    F[i] = (c >= 1 && r <= 23) ? (double)(23 - r) / (double)(8 * c) : 0.0;
-  }
   if (d.mode == LLVQ_MODE_SHAPEGAIN && scales != nullptr) {
     float* G = reinterpret_cast<float*>(smem + L.gains);
     for (int i = tid; i < (1 << d.gain_bits); i += kEThreads) G[i] = __half2float(scales[i]);
@@ -453,6 +460,8 @@ __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L,
   copy_finish(smem, v_tail, s_tail, tid);
   copy_finish(smem, v_tcomp, s_tcomp, tid);
   copy_finish(smem, v_bk, s_bk, tid);
+  copy_finish(smem, v_f, s_f, tid);
+  copy_finish(smem, v_g, s_g, tid);
   copy_finish(smem, v_x, extra, tid);
   copy_word_tail(smem, L.cls, dev_tables::kClassHot, cls_w, tid);
   if (tid < 2) reinterpret_cast<LlvqClassHot*>(smem + L.cls)[d.ncls + tid].start = __builtin_inf();

@@ -61,7 +61,7 @@ __device__ __forceinline__ void gemv_odd(uint8_t* smem, const EArgs& a, float* p
   const uint32_t fo = entry_f(e);
   const uint32_t bo = block_col(fo, inv_kb, kb);
   const LlvqClassHot hO = cls[entry_k(e)];
-  const BlockStart so = block_start(smem, L, entry_J(e), hO);
+  const BlockStart so = block_start<true>(smem, L, entry_J(e), hO);
   uint32_t xw[12];
   float xf[24];
   if (XF32) {
@@ -106,7 +106,7 @@ __device__ __forceinline__ void gemv_even(uint8_t* smem, const EArgs& a, float* 
   const uint32_t fe = entry_f(e);
   const uint32_t be = block_col(fe, inv_kb, kb);
   const LlvqClassHot hE = cls[entry_k(e)];
-  const BlockStart se = block_start(smem, L, entry_J(e), hE);
+  const BlockStart se = block_start<true>(smem, L, entry_J(e), hE);
   EvenDec ev;
   ev.init(hE, se, L.cls + entry_k(e) * (uint32_t)sizeof(LlvqClassHot));
   ev.load_fp8(hE);
@@ -165,9 +165,13 @@ __device__ __forceinline__ LaneField load_lane_field(const KDesc& d, const uint8
 // Classify the lane's field: class search (bucket table on the top index bits, then the
 // class starts), the block's scale into its slot, and the block appended to the wave's
 // odd or even ring.  An index >= the shell-union size gets slot 0 (it contributes
-// nothing), is counted and is not queued.
-__device__ __forceinline__ void classify_lane(uint8_t* smem, const ELayout& L, float* part, const KDesc& d,
-                                              const LaneField& lf, int T, int u, int lane, int32_t* err, Rings& R) {
+// nothing), is counted and is not queued; the return value says so (true for such a
+// field inside the tile).  ROWSCALE (the Euclidean decode): the slot takes the scale of
+// the block's row, rs[f / Kb], instead of 1.
+template <bool ROWSCALE = false>
+__device__ __forceinline__ bool classify_lane(uint8_t* smem, const ELayout& L, float* part, const KDesc& d,
+                                              const LaneField& lf, int T, int u, int lane, int32_t* err, Rings& R,
+                                              const __half* rs = nullptr, float inv_kb = 0.0f) {
   const LlvqClassHot* cls = reinterpret_cast<const LlvqClassHot*>(smem + L.cls);
   const float* G = reinterpret_cast<const float*>(smem + L.gains);
   const uint8_t* bk = smem + L.bucket;
@@ -197,7 +201,9 @@ __device__ __forceinline__ void classify_lane(uint8_t* smem, const ELayout& L, f
   const uint32_t gsh = d.shape_bits >= 32 ? (fhi >> (d.shape_bits - 32))
                                           : __builtin_amdgcn_alignbit(fhi, flo, d.shape_bits);
   const uint32_t g = gsh & ((1u << d.gain_bits) - 1u);
-  const float sc = d.mode == LLVQ_MODE_SHAPEGAIN ? G[g] * h.invnorm : 1.0f;
+  float sc = d.mode == LLVQ_MODE_SHAPEGAIN ? G[g] * h.invnorm : 1.0f;
+  if (ROWSCALE && d.mode != LLVQ_MODE_SHAPEGAIN && f < T)
+    sc = __half2float(rs[(uint32_t)(((float)f + 0.5f) * inv_kb)]);
   if (f < T) part[f] = valid ? sc : 0.0f;
   if (f < T && !valid && err) atomicAdd(err, 1);
   const uint64_t bo = __ballot(valid && odd);
@@ -209,6 +215,7 @@ __device__ __forceinline__ void classify_lane(uint8_t* smem, const ELayout& L, f
   R.on += (uint32_t)__popcll(bo);
   R.en += (uint32_t)__popcll(be);
   LLVQ_DCHECK(R.on < (uint32_t)kRing && R.en < (uint32_t)kRing);
+  return f < T && !valid;
 }
 
 template <bool XF32>
