@@ -49,60 +49,67 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
+        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
-        "valu_lane_ops_per_unit": 670.3,       # SQ_INSTS_VALU * 64 / blocks
-        "fetch_bytes_per_launch": 12222331,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "valu_lane_ops_per_unit": 613.8,       # SQ_INSTS_VALU * 64 / blocks
+        "valu_mix_peak_tops": 38.92,           # peak for the executed instruction mix
+        "fetch_bytes_per_launch": 12255109,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
+        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
-        "valu_lane_ops_per_unit": 695.4,
-        "fetch_bytes_per_launch": 61917531,
+        "valu_lane_ops_per_unit": 696.1,
+        "valu_mix_peak_tops": 38.53,
+        "fetch_bytes_per_launch": 61982738,
         "write_bytes_per_launch": 1835008,
     },
     "gemv_3bit_b1": {
-        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
+        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
         "summary": "profiles/gemv_3bit_4096x11008_batch1_k_gemv_wide.md",
         "unit_of_work": "24-weight block (k_gemv_wide)",
         "valu_lane_ops_per_unit": 3696.2,
-        "fetch_bytes_per_launch": 32877490,
+        "valu_mix_peak_tops": 35.20,
+        "fetch_bytes_per_launch": 32853425,
         "write_bytes_per_launch": 32768,
     },
     "decode_3bit": {
-        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
+        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
         "summary": "profiles/decode_bf16_3bit_4096x11008_k_decode_wide.md",
         "unit_of_work": "24-weight block (k_decode_wide<bf16>)",
         "valu_lane_ops_per_unit": 3389.7,
-        "fetch_bytes_per_launch": 38061810,
-        "write_bytes_per_launch": 90295866,
+        "valu_mix_peak_tops": 35.15,
+        "fetch_bytes_per_launch": 37935042,
+        "write_bytes_per_launch": 90295163,
     },
     "decode_bf16": {
-        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
-        "summary": "profiles/decode_bf16_7b_k_decode_many.md",
-        "unit_of_work": "24-weight block (k_decode_many<bf16>)",
-        "valu_lane_ops_per_unit": 738.4,
-        "fetch_bytes_per_launch": 103320234,           # one launch = two layers (14 tensors)
-        "write_bytes_per_launch": 809500672,
+        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
+        "summary": "profiles/decode_bf16_7b_k_decode_stream.md",
+        "unit_of_work": "24-weight block (k_decode_stream<bf16>)",
+        "valu_lane_ops_per_unit": 668.4,
+        "valu_mix_peak_tops": 38.88,
+        "fetch_bytes_per_launch": 102475494,           # one launch = two layers (14 tensors)
+        "write_bytes_per_launch": 1016186360,
     },
     "roundtrip": {
-        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
-        "summary": "profiles/roundtrip_1e7_k_decode_tile_k_rank.md",
-        "unit_of_work": "point: decode to int8 (626.0) + rank (951.2)",
-        "valu_lane_ops_per_unit": 1577.2,
+        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
+        "summary": "profiles/roundtrip_1e7_k_decode_stream_k_rank.md",
+        "unit_of_work": "point: decode to int8 (616.0) + rank (951.2)",
+        "valu_lane_ops_per_unit": 1567.2,
+        # the two kernels' mix peaks (39.23, 36.48) weighted by their lane-ops
+        "valu_mix_peak_tops": 37.52,
         "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
         "write_bytes_per_launch": None,
     },
     "search": {
-        "source_sha256": "27f825e1fb3c8f860e5ac90c297d49dfab5e0f3a1f83b4616d1d8d924f54bd05",
+        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
         "summary": "profiles/search_4096x4096_k_search_k_rank.md",
         # The search issues more VALU instructions per clock than one per CU (mostly fp32
-        # add / fma / max, which issue at up to 1.46 wave-instructions per CU per clock on
-        # gfx950, profiles/valu_issue_rates_gfx950.md), so its peak is the fastest measured
-        # single-instruction rate, 1.464 x 39.32 T lane-ops/s.
+        # fma / max / compares), and more than the harmonic mix of single-instruction
+        # rates allows (utilisation 1.27 against it: such classes co-issue), so its peak
+        # is the fastest measured single-instruction rate, 1.464 x 39.32 T lane-ops/s.
         "valu_peak_tops": 57.56,
         "unit_of_work": "24-block: search (3375276.2) + rank (955.4)",
         "valu_lane_ops_per_unit": 3376231.6,

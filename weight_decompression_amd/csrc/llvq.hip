@@ -534,12 +534,11 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;   // 32-bit field index
   const bool xf32 = x_dtype == LLVQ_X_F32;
   const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
-  // LDS: fixed tables and the Golay table, the waves' rings, 4 bytes per block of the
-  // tile (its slot), x
+  // LDS: fixed tables, the waves' rings, 4 bytes per block of the tile (its slot), x
   ELayout L;
   const uint32_t xbytes = align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u));
   const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 1);
-  const uint32_t fixed = base + 4096u * 4u + (uint32_t)kRingBytes + xbytes + 16u;
+  const uint32_t fixed = base + (uint32_t)kRingBytes + xbytes + 16u;
   if (fixed + 4u * (uint32_t)k.kb > kLdsBudget) return LLVQ_EUNSUPPORTED;
   int tmax = (int)((kLdsBudget - fixed) / 4u);
   if (tmax > kETileMax) tmax = kETileMax;
@@ -561,8 +560,7 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   }
   a.nbuckets = nbuckets;
   engine_layout_base(a.L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 1);
-  a.L.golay = align16(a.L.total);
-  a.rings = a.L.golay + 4096u * 4u;
+  a.rings = align16(a.L.total);
   a.L.buf[0].part = a.rings + (uint32_t)kRingBytes;
   a.xs = align16(a.L.buf[0].part + 4u * (uint32_t)(a.rows_per_tile * k.kb));
   const uint32_t total = a.xs + align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u));

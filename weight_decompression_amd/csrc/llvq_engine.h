@@ -173,9 +173,10 @@ struct BlockStart {
   double y;     // y_0 = (R + 1/2) * n0 / P
 };
 
-// LG: the codeword comes from the LDS copy of the Golay table at L.golay (a kernel that
-// also stores to global memory then never waits on its stores for it: on gfx9 a load's
-// wait counts every older vector-memory operation, stores included).
+// LG: the codeword comes from the LDS copy of the Golay table at L.golay (the streamed
+// decode, which stores to global memory while it decodes: on gfx9 the wait for a load
+// counts every older vector-memory operation, stores included, so a global table read
+// would wait for the chunk stores in flight).
 template <bool LG = false>
 __device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELayout& L, double Jd,
                                                   const LlvqClassHot& h) {

@@ -61,7 +61,7 @@ __device__ __forceinline__ void gemv_odd(uint8_t* smem, const EArgs& a, float* p
   const uint32_t fo = entry_f(e);
   const uint32_t bo = block_col(fo, inv_kb, kb);
   const LlvqClassHot hO = cls[entry_k(e)];
-  const BlockStart so = block_start<true>(smem, L, entry_J(e), hO);
+  const BlockStart so = block_start(smem, L, entry_J(e), hO);
   uint32_t xw[12];
   float xf[24];
   if (XF32) {
@@ -106,7 +106,7 @@ __device__ __forceinline__ void gemv_even(uint8_t* smem, const EArgs& a, float* 
   const uint32_t fe = entry_f(e);
   const uint32_t be = block_col(fe, inv_kb, kb);
   const LlvqClassHot hE = cls[entry_k(e)];
-  const BlockStart se = block_start<true>(smem, L, entry_J(e), hE);
+  const BlockStart se = block_start(smem, L, entry_J(e), hE);
   EvenDec ev;
   ev.init(hE, se, L.cls + entry_k(e) * (uint32_t)sizeof(LlvqClassHot));
   ev.load_fp8(hE);
