@@ -135,6 +135,9 @@ def test_decode_bf16_bit_exact(M, sb, gb, rows, cols, mode):
 
 @pytest.mark.parametrize("M,sb,gb,rows,cols,batch,xd,mode", [
     (42, 68, 4, 300, 1000, 1, "bf16", synth.MODE_SHAPEGAIN),
+    (42, 68, 4, 333, 1000, 1, "f32", synth.MODE_SHAPEGAIN),
+    (24, 59, 0, 66, 777, 1, "bf16", synth.MODE_EUCLID),
+    (11, 46, 2, 50, 2400, 1, "f32", synth.MODE_SHAPEGAIN),
     (42, 68, 4, 70, 4096, 5, "f32", synth.MODE_SHAPEGAIN),
     (12, 47, 1, 129, 2000, 16, "bf16", synth.MODE_SHAPEGAIN),
     (24, 59, 0, 66, 777, 2, "bf16", synth.MODE_EUCLID),
@@ -177,6 +180,55 @@ def test_gemv_3bit_4096x11008_sampled_rows():
                                 t.x_as_f64(), rows_s)
     got = y.cpu().numpy()[:, rows_s].astype(np.float64)
     assert np.all(reference.gemv_within_tolerance(got, y_ref, mag))
+
+
+def test_gemv_batch1_tiles_and_invalid_blocks():
+    # 20000 x 4096 at shell 42: a workgroup's rows (79 x 171 blocks) exceed one LDS tile, so
+    # the batch-1 coset-queue kernel walks several tiles; blocks with indices past the shell
+    # union are spread over the tensor (zero contribution, counted)
+    import dataclasses
+    M, rows, cols = 42, 20000, 4096
+    C = leech.index_count(M)
+    t = synth.make_wide_tensor("wtile", 74, 0, rows, cols, C)
+    bad = [(0, 0), (0, 170), (9999, 55), (19999, 170), (12345, 1)]
+    shape = t.shape_idx.copy()
+    for j, (r, b) in enumerate(bad):
+        shape[r, b] = C + 1000 * j
+    lo = np.array([[int(v) & (2**64 - 1) for v in row] for row in shape], dtype=np.uint64)
+    hi = np.array([[int(v) >> 64 for v in row] for row in shape], dtype=np.uint64)
+    hi |= t.gain_idx << np.uint64(68 - 64)
+    t = dataclasses.replace(t, shape_idx=shape, packed=synth.pack_fields_wide(lo, hi, 72))
+    desc, packed, scales, x = dev(t)
+    outs = []
+    for _ in range(2):
+        y = torch.full((1, rows), float("nan"), dtype=torch.float32, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        wd.gemv(desc, packed, scales, x, y, err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == len(bad)
+        outs.append(y.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    # oracle rows without invalid blocks; rows with them against the oracle's sum over the rest
+    rows_s = [1, 5000, 19998]
+    y_ref, mag = reference.gemv(t.packed.tobytes(), rows, cols, M, t.mode, 68, 4, t.scales_f16, None,
+                                t.x_as_f64(), rows_s)
+    got = outs[0][:, rows_s].astype(np.float64)
+    assert np.all(reference.gemv_within_tolerance(got, y_ref, mag))
+    xf = t.x_as_f64()[0]
+    for r in sorted({r for r, _ in bad}):
+        ref, m = 0.0, 0.0
+        for b in range(t.kb):
+            if (r, b) in bad:
+                continue
+            I = int(shape[r, b])
+            vals = reference.block_f32(I, int(t.gain_idx[r, b]), M, t.mode, t.scales_f16, None).astype(np.float64)
+            xs = np.zeros(24)
+            seg = xf[24 * b:min(24 * b + 24, cols)]
+            xs[:seg.size] = seg
+            ref += float(vals @ xs)
+            m += float(np.abs(vals) @ np.abs(xs))
+        say(f"row {r}: gpu {outs[0][0, r]:.6e} oracle {ref:.6e}")
+        assert abs(outs[0][0, r] - ref) <= 1e-4 * m
 
 
 def test_decode_many_with_wide_tensors_equals_single_calls():

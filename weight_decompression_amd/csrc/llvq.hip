@@ -226,6 +226,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 #include "llvq_gemm.h"
 #include "llvq_stream.h"
 #include "llvq_wide.h"
+#include "llvq_wide_tile.h"
 
 // ---------------------------------------------------------------------------
 // kernels
@@ -713,6 +714,52 @@ int decode_wide(const llvq_desc* d, const void* packed, const void* scales, int3
   return launch_status();
 }
 
+// Batch-1 GEMV of the general decoder with coset queues (llvq_wide_tile.h): LDS holds x
+// of all columns, the reciprocals and 16 bytes per block of a tile.  LLVQ_EUNSUPPORTED
+// when x or a row does not fit (the one-block-per-lane kernel then runs).
+int launch_gemv_wide_tile(const WDesc& w, const void* packed, const void* scales, const void* x, int32_t x_dtype,
+                          float* y, int32_t* err, hipStream_t s) {
+  if ((uint64_t)w.rows * (uint64_t)w.kb >= (1ull << 31)) return LLVQ_EUNSUPPORTED;
+  const bool xbf16 = x_dtype == LLVQ_X_BF16;
+  WTArgs a = {};
+  a.xs = 0;
+  a.rc = align16((uint32_t)w.kb * 24u * (xbf16 ? 2u : 4u));
+  a.ctr = a.rc + 32u * 8u;
+  const uint32_t fixed = a.ctr + 16u + 64u;
+  if (fixed >= kLdsBudget) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((kLdsBudget - fixed) / 16u) & ~15;
+  if (tmax > kWTTileMax) tmax = kWTTileMax;
+  if (w.kb > tmax) return LLVQ_EUNSUPPORTED;
+  a.tmax = tmax;
+  int grid = 0;
+  const int r1 = (w.rows + kGridMax - 1) / kGridMax;
+  if ((long)r1 * w.kb <= tmax) {
+    a.rows_per_tile = r1;
+    a.ntiles = (w.rows + r1 - 1) / r1;
+    grid = a.ntiles;
+  } else {
+    int nt = 0, g = 0;
+    const int r = pick_rows_per_tile(w.rows, w.kb, tmax, &nt, &g);
+    if (r == 0) return LLVQ_EUNSUPPORTED;
+    a.rows_per_tile = r;
+    a.ntiles = nt;
+    grid = g;
+  }
+  const uint32_t T = (uint32_t)(a.rows_per_tile * w.kb);
+  a.qj = align16(a.ctr + 16u);
+  a.qk = a.qj + 8u * T;
+  a.part = align16(a.qk + 4u * T);
+  const uint32_t total = a.part + 4u * T;
+  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  const uint8_t* pk = static_cast<const uint8_t*>(packed);
+  const __half* sc = static_cast<const __half*>(scales);
+  if (xbf16)
+    hipLaunchKernelGGL((k_gemv_wide_tile<true>), dim3(grid), dim3(kWTThreads), total, s, w, a, pk, sc, x, y, err);
+  else
+    hipLaunchKernelGGL((k_gemv_wide_tile<false>), dim3(grid), dim3(kWTThreads), total, s, w, a, pk, sc, x, y, err);
+  return launch_status();
+}
+
 int gemv_wide(const llvq_desc* d, const void* packed, const void* scales, const void* x, int32_t x_dtype,
               int32_t batch, float* y, int32_t* err_count, void* stream) {
   WDesc w;
@@ -730,6 +777,10 @@ int gemv_wide(const llvq_desc* d, const void* packed, const void* scales, const 
   }
   if (batch < 1 || batch > LLVQ_MAX_BATCH) return LLVQ_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (batch == 1) {
+    const int st1 = launch_gemv_wide_tile(w, packed, scales, x, x_dtype, y, err_count, s);
+    if (st1 != LLVQ_EUNSUPPORTED) return st1;
+  }
   const unsigned grid = grid_for((uint64_t)w.rows, kWideThreads / 64);
   const int xbytes = x_dtype == LLVQ_X_BF16 ? 2 : 4;
   const bool xvec = aligned(x, 16) && ((uint64_t)w.cols * (uint64_t)xbytes) % 16u == 0;

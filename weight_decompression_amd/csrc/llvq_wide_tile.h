@@ -1,0 +1,330 @@
+// Batch-1 GEMV of the general decoder with coset queues (gfx950).  Included once by
+// llvq.hip after llvq_wide.h, whose class search and unranking state it uses.
+//
+// The one-block-per-lane kernel (k_gemv_wide) lets a wavefront mix both cosets, one- and
+// two-part classes and the exact and fp64 regimes of the unranking; its single pass over
+// the 24 positions picks, per position and per lane, the support or complement unranker,
+// so every step copies both states in and out.  Here a 1024-lane workgroup (one per CU)
+// takes tiles of whole rows:
+//   1. classify: each lane takes blocks of the tile, finds the class (shell and class
+//      search as in k_gemv_wide), keeps the block's scale in its LDS slot and queues the
+//      block (J = I - class start, class, block) for the odd or the even coset;
+//   2. decode: waves take 64-entry chunks of one queue through an LDS counter.  An odd
+//      block is one multiset over all 24 positions, decoded in position order against the
+//      activations held in registers; an even block decodes its support values (on the
+//      codeword's positions, ascending) and then its complement values, each part in its
+//      own loop with its own state, reading each value's activation from LDS by position.
+//      The signs follow the same rules as wide_decode_point, in the same order;
+//   3. the block results scale their slots and the rows are summed in a fixed order.
+// The fp64 arithmetic-decoding step multiplies by 1/c from an LDS table instead of
+// dividing by c: one more rounding per step (four of at most 24 x 2^-53), so the bound of
+// kFpRem becomes 2 x 24 x 4 x 24 x 2^-53 x 2^38 = 0.14, every slot choice still exact.
+
+#pragma once
+
+constexpr int kWTThreads = 1024;
+constexpr int kWTWaves = kWTThreads / 64;
+constexpr int kWTTileMax = 16384;         // block index in 16 bits with the class index
+
+struct WTArgs {
+  int rows_per_tile, ntiles;
+  uint32_t xs;      // LDS: x of all kb * 24 columns, zero padded (bf16 or fp32)
+  uint32_t rc;      // LDS: double[32], rc[c] = 1 / c
+  uint32_t qj;      // LDS: uint64[tmax] queue: J
+  uint32_t qk;      // LDS: uint32[tmax] queue: class | block << 16
+  uint32_t part;    // LDS: float[tmax] block scale, then the block's result
+  uint32_t ctr;     // LDS: int[4]: odd fill, even fill, chunk counter
+  int tmax;
+};
+
+// One value of a multiset unranking in progress (fp64 arithmetic decoding below 2^kFpRem
+// arrangements left, exact 64-bit steps above): returns the value and advances U.
+__device__ __forceinline__ uint32_t wt_next(Unranker& U, const double* rc) {
+  uint32_t kk;
+  if (U.fp) {
+    const double y = U.u * (double)U.n;
+    const int fy = (int)y;
+    const uint64_t run = U.cnts * 0x0101010101010101ull;
+    const uint64_t over = (run + (uint64_t)(127 - fy) * 0x0101010101010101ull) & 0x8080808080808080ull;
+    kk = 8u - (uint32_t)__popcll(over);
+    const uint32_t ck = (uint32_t)(U.cnts >> (8 * kk)) & 0xffu;
+    LLVQ_DCHECK(kk < 8u && ck != 0u);
+    const uint32_t below = kk ? (uint32_t)(run >> (8 * (kk - 1))) & 0xffu : 0u;
+    U.u = (y - (double)below) * rc[ck];
+  } else {
+    const uint64_t t_n = U.rank * U.n;
+    uint32_t ck = (uint32_t)U.cnts & 0xffu;
+    uint64_t below = 0, upto = U.rem * ck;
+    kk = 0;
+    while (kk < 7u && t_n >= upto) {
+      ++kk;
+      ck = (uint32_t)(U.cnts >> (8 * kk)) & 0xffu;
+      below = upto;
+      upto += U.rem * ck;
+    }
+    LLVQ_DCHECK(U.n >= 1u && U.n <= 24u && ck != 0u && t_n < upto);
+    const uint32_t tz = (uint32_t)__builtin_ctz(U.n);
+    const uint64_t iv = dev_tables::kWideOddInverse[U.n >> (tz + 1)];
+    U.rank = ((t_n - below) >> tz) * iv;
+    U.rem = ((U.rem * ck) >> tz) * iv;
+    to_fp(U);
+  }
+  const uint32_t a = (uint32_t)(U.vals >> (8 * kk)) & 0xffu;
+  U.cnts -= 1ull << (8 * kk);
+  U.n -= 1u;
+  return a;
+}
+
+__device__ __forceinline__ void wt_init(Unranker& U, uint64_t rank, uint64_t rem, uint32_t n, const uint8_t* cnt,
+                                        const uint8_t* val) {
+  U.rank = rank;
+  U.rem = rem;
+  U.n = n;
+  U.cnts = bytes8(cnt);
+  U.vals = bytes8(val);
+  U.fp = false;
+  U.u = 0.0;
+  to_fp(U);
+}
+
+template <bool XBF16>
+__device__ __forceinline__ float wt_x(const uint8_t* smem, uint32_t xs, uint32_t col) {
+  if (XBF16) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(smem + xs)[col] << 16);
+  return reinterpret_cast<const float*>(smem + xs)[col];
+}
+
+// odd block: <v, x> over its 24 positions, x of the block column b
+template <bool XBF16>
+__device__ __forceinline__ float wt_odd_dot(const uint8_t* smem, const WTArgs& a, const double* rc, uint64_t J,
+                                            const LlvqWideClass& cr, uint32_t b) {
+  const uint32_t c = dev_tables::kGolayTable[(uint32_t)(J & 4095u)];
+  Unranker T;
+  wt_init(T, J >> 12, cr.P_T, 24u, cr.cc, cr.cv);
+  float xr[24];
+  if (XBF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(smem + a.xs + b * 48u);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const uint4 u = p[q];
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xr[8 * q + 2 * e] = __uint_as_float(w4[e] << 16);
+        xr[8 * q + 2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(smem + a.xs + b * 96u);
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      const float4 u = p[q];
+      xr[4 * q] = u.x; xr[4 * q + 1] = u.y; xr[4 * q + 2] = u.z; xr[4 * q + 3] = u.w;
+    }
+  }
+  float t = 0.0f;
+#pragma unroll
+  for (int p = 0; p < kDim; ++p) {
+    const int v = (int)wt_next(T, rc);
+    const bool neg = ((v & 3) == 1) != (((c >> p) & 1u) != 0u);
+    t = fmaf((float)(neg ? -v : v), xr[p], t);
+  }
+  return t;
+}
+
+// even block: the support part (codeword positions, ascending), then the complement part
+template <bool XBF16>
+__device__ __forceinline__ float wt_even_dot(const uint8_t* smem, const WTArgs& a, const double* rc, uint64_t J,
+                                             const LlvqWideClass& cr, uint32_t b) {
+  const uint32_t w = cr.w;
+  const uint32_t A = dev_tables::kWideCodewords[w];
+  uint64_t r, ip;
+  if (A == 1u) {
+    r = 0;
+    ip = J;
+  } else {
+    ip = div_u64(J, A, r);
+  }
+  const uint32_t B = cr.B;
+  const uint32_t s = (uint32_t)(ip & ((1ull << B) - 1ull));
+  const uint64_t R = ip >> B;
+  const uint32_t c = dev_tables::kGolayTable[dev_tables::kWideGolayOffset[w] + (uint32_t)r];
+  uint64_t rs, rt;
+  if (cr.P_S == 1) {
+    rs = 0;
+    rt = R;
+  } else {
+    rs = div_u64(R, cr.P_T, rt);
+  }
+  const uint32_t col0 = b * 24u;
+  float t = 0.0f;
+  // support: w values, all nonzero; the last (highest position) takes the parity sign
+  {
+    Unranker S;
+    wt_init(S, rs, cr.P_S, w, cr.sc, cr.sv);
+    const uint32_t wm1 = w ? w - 1u : 0u;
+    const uint32_t negq = (((uint32_t)__popc(s & ((1u << wm1) - 1u))) & 1u) ^ cr.pi;
+    uint32_t bits = s, cm = c;
+    for (uint32_t i = 0; i < w; ++i) {
+      const uint32_t p = (uint32_t)__builtin_ctz(cm);
+      cm &= cm - 1u;
+      const int v = (int)wt_next(S, rc);
+      uint32_t neg;
+      if (i + 1u == w) {
+        neg = negq;
+      } else {
+        neg = bits & 1u;
+        bits >>= 1;
+      }
+      t = fmaf((float)(neg ? -v : v), wt_x<XBF16>(smem, a.xs, col0 + p), t);
+    }
+  }
+  // complement: 24 - w values on the other positions, the free signs after the support's
+  {
+    Unranker T;
+    wt_init(T, rt, cr.P_T, 24u - w, cr.cc, cr.cv);
+    uint32_t bits = w ? s >> (w - 1u) : s;
+    uint32_t cm = ~c & 0xffffffu;
+    for (uint32_t i = w; i < 24u; ++i) {
+      const uint32_t p = (uint32_t)__builtin_ctz(cm);
+      cm &= cm - 1u;
+      const int v = (int)wt_next(T, rc);
+      uint32_t neg = 0u;
+      if (v != 0) {
+        neg = bits & 1u;
+        bits >>= 1;
+      }
+      t = fmaf((float)(neg ? -v : v), wt_x<XBF16>(smem, a.xs, col0 + p), t);
+    }
+  }
+  return t;
+}
+
+template <bool XBF16>
+__global__ __launch_bounds__(kWTThreads) void k_gemv_wide_tile(WDesc d, WTArgs a, const uint8_t* __restrict__ packed,
+                                                               const __half* __restrict__ scales,
+                                                               const void* __restrict__ xv, float* __restrict__ y,
+                                                               int32_t* err) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
+  const int kb = d.kb;
+  const float inv_kb = 1.0f / (float)kb;
+  double* rc = reinterpret_cast<double*>(smem + a.rc);
+  uint64_t* qj = reinterpret_cast<uint64_t*>(smem + a.qj);
+  uint32_t* qk = reinterpret_cast<uint32_t*>(smem + a.qk);
+  float* part = reinterpret_cast<float*>(smem + a.part);
+  int* ctr = reinterpret_cast<int*>(smem + a.ctr);
+
+  // activations (zero past K) and the reciprocals
+  {
+    const int ncol = kb * 24;
+    if (XBF16) {
+      uint16_t* xs = reinterpret_cast<uint16_t*>(smem + a.xs);
+      const uint16_t* xg = static_cast<const uint16_t*>(xv);
+      for (int i = tid; i < ncol; i += kWTThreads) xs[i] = i < d.cols ? xg[i] : (uint16_t)0;
+    } else {
+      float* xs = reinterpret_cast<float*>(smem + a.xs);
+      const float* xg = static_cast<const float*>(xv);
+      for (int i = tid; i < ncol; i += kWTThreads) xs[i] = i < d.cols ? xg[i] : 0.0f;
+    }
+    if (tid < 32) rc[tid] = tid ? 1.0 / (double)tid : 0.0;
+    if (tid < 4) ctr[tid] = 0;
+  }
+  __syncthreads();
+
+  for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    const int row0 = tile * a.rows_per_tile;
+    const int nrows = min(a.rows_per_tile, d.rows - row0);
+    const int T = nrows * kb;
+    const uint64_t j0 = (uint64_t)row0 * (uint64_t)kb;
+
+    // 1. classify (odd entries from the front of the queue, even entries from the back)
+    for (int f0 = wave * 64; f0 < T; f0 += kWTThreads) {
+      const int f = f0 + lane;
+      bool odd = false, even = false;
+      uint64_t J = 0;
+      uint32_t k = 0;
+      if (f < T) {
+        uint64_t lo, hi;
+        uint32_t g;
+        float sc = 0.0f;
+        if (wide_block(d, packed, j0 + (uint64_t)f, lo, hi, g)) {
+          k = (uint32_t)wide_find_class(lo, hi, d.max_shell);
+          LLVQ_DCHECK(k < (uint32_t)LLVQ_WIDE_NUM_CLASSES && dev_tables::kWideClass[k].m <= d.max_shell);
+          const LlvqWideClass& cr = dev_tables::kWideClass[k];
+          J = lo - cr.start_lo;
+          odd = cr.parity != 0;
+          even = !odd;
+          sc = sg ? __fmul_rn(__half2float(scales[g]), dev_tables::kWideInvNorm32[cr.m]) : 1.0f;
+        } else if (err) {
+          atomicAdd(err, 1);
+        }
+        part[f] = sc;
+      }
+      const uint64_t bo = __ballot(odd), be = __ballot(even);
+      int baseo = 0, basee = 0;
+      if (lane == 0) {
+        baseo = atomicAdd(&ctr[0], __popcll(bo));
+        basee = atomicAdd(&ctr[1], __popcll(be));
+      }
+      baseo = __builtin_amdgcn_readfirstlane(baseo);
+      basee = __builtin_amdgcn_readfirstlane(basee);
+      const uint32_t po = __builtin_amdgcn_mbcnt_hi((uint32_t)(bo >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bo, 0u));
+      const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+      const int slot = odd ? baseo + (int)po : T - 1 - (basee + (int)pe);
+      if (odd || even) {
+        LLVQ_DCHECK(slot >= 0 && slot < T);
+        qj[slot] = J;
+        qk[slot] = k | ((uint32_t)f << 16);
+      }
+    }
+    __syncthreads();
+
+    // 2. decode chunks: odd queue, then even queue
+    const int nodd = ctr[0], neven = ctr[1];
+    const int nco = (nodd + 63) >> 6;
+    const int nch = nco + ((neven + 63) >> 6);
+    for (;;) {
+      int c = 0;
+      if (lane == 0) c = atomicAdd(&ctr[2], 1);
+      c = __builtin_amdgcn_readfirstlane(c);
+      if (c >= nch) break;
+      if (c < nco) {
+        const int e = (c << 6) + lane;
+        if (e < nodd) {
+          const uint32_t kf = qk[e];
+          const uint32_t f = kf >> 16;
+          const uint32_t b = f - (uint32_t)(((float)f + 0.5f) * inv_kb) * (uint32_t)kb;
+          const float t = wt_odd_dot<XBF16>(smem, a, rc, qj[e], dev_tables::kWideClass[kf & 0xffffu], b);
+          part[f] *= t;
+        }
+      } else {
+        const int e = ((c - nco) << 6) + lane;
+        if (e < neven) {
+          const uint32_t kf = qk[T - 1 - e];
+          const uint32_t f = kf >> 16;
+          const uint32_t b = f - (uint32_t)(((float)f + 0.5f) * inv_kb) * (uint32_t)kb;
+          const float t = wt_even_dot<XBF16>(smem, a, rc, qj[T - 1 - e], dev_tables::kWideClass[kf & 0xffffu], b);
+          part[f] *= t;
+        }
+      }
+    }
+    __syncthreads();
+
+    // 3. row sums in a fixed order
+    for (int rl = wave; rl < nrows; rl += kWTWaves) {
+      float acc = 0.0f;
+      for (int bb = lane; bb < kb; bb += 64) acc += part[rl * kb + bb];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      if (lane == 0) {
+        const int r = row0 + rl;
+        y[r] = sg ? acc : acc * __half2float(scales[r]);
+      }
+    }
+    if (tid < 4) ctr[tid] = 0;
+    __syncthreads();
+  }
+}
