@@ -406,6 +406,16 @@ def run_decode_3bit(a):
     res["roofline"] = roofline("decode_3bit", blocks, sec, alg_bytes,
                                "9 B packed index read + 48 B bf16 written per 24-weight block")
     res["wall_s_timed"] = wall
+    # parity: seeded rows of the timed output, bf16 bit patterns vs the oracle's decode
+    import numpy as np
+    from oracle import parallel
+    rows = sorted(set([0, t.rows - 1] + [int(r) for r in np.random.default_rng(9).choice(t.rows, 14, replace=False)]))
+    ref = parallel.decode_rows_bf16(t.packed.tobytes(), t.rows, t.cols, 42, t.mode, t.shape_bits, t.gain_bits,
+                                    t.scales_f16, None, rows)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    bad = int(np.sum(np.any(got != ref, axis=1)))
+    res["parity"] = {"what": f"{len(rows)} seeded rows of the timed output, bf16 bit patterns vs the oracle",
+                     "rows_checked": len(rows), "rows_differing": bad, "pass": bad == 0}
     return res
 
 

@@ -686,6 +686,9 @@ int launch_gemv(const KDesc& k, const void* packed, const void* scales, const vo
 
 namespace {
 // General decoder (llvq_wide.h): one 24-block per lane.
+int launch_decode_wide_tile(const WDesc& w, const void* packed, const void* scales, int32_t out_kind, void* out,
+                            int32_t* err, bool ovec, hipStream_t s);
+
 int decode_wide(const llvq_desc* d, const void* packed, const void* scales, int32_t out_kind, void* out,
                 int32_t* err_count, void* stream) {
   WDesc w;
@@ -704,6 +707,9 @@ int decode_wide(const llvq_desc* d, const void* packed, const void* scales, int3
   const uint64_t nblocks = (uint64_t)w.rows * (uint64_t)w.kb;
   const unsigned grid = grid_for(nblocks, kWideThreads);
   const bool ovec = aligned(out, 16) && (w.cols % 8) == 0;
+  const int st1 = launch_decode_wide_tile(w, packed, out_kind == LLVQ_OUT_BF16 ? scales : nullptr, out_kind, out,
+                                          err_count, out_kind == LLVQ_OUT_POINTS_I8 ? aligned(out, 8) : ovec, s);
+  if (st1 != LLVQ_EUNSUPPORTED) return st1;
   if (out_kind == LLVQ_OUT_POINTS_I8)
     hipLaunchKernelGGL((k_decode_wide<LLVQ_OUT_POINTS_I8>), dim3(grid), dim3(kWideThreads), 0, s, w,
                        static_cast<const uint8_t*>(packed), nullptr, out, err_count, false);
@@ -757,6 +763,52 @@ int launch_gemv_wide_tile(const WDesc& w, const void* packed, const void* scales
     hipLaunchKernelGGL((k_gemv_wide_tile<true>), dim3(grid), dim3(kWTThreads), total, s, w, a, pk, sc, x, y, err);
   else
     hipLaunchKernelGGL((k_gemv_wide_tile<false>), dim3(grid), dim3(kWTThreads), total, s, w, a, pk, sc, x, y, err);
+  return launch_status();
+}
+
+// Decode of the general decoder with coset queues (llvq_wide_tile.h): LDS holds the
+// reciprocals and 40 bytes per block of a tile (queue, scale, 24 value bytes).
+// LLVQ_EUNSUPPORTED when a row does not fit (the one-block-per-lane kernel then runs).
+int launch_decode_wide_tile(const WDesc& w, const void* packed, const void* scales, int32_t out_kind, void* out,
+                            int32_t* err, bool ovec, hipStream_t s) {
+  if ((uint64_t)w.rows * (uint64_t)w.kb >= (1ull << 31)) return LLVQ_EUNSUPPORTED;
+  WTArgs a = {};
+  a.rc = 0;
+  a.ctr = 32u * 8u;
+  const uint32_t fixed = a.ctr + 16u + 64u;
+  int tmax = (int)((kLdsBudget - fixed) / 40u) & ~15;
+  if (tmax > kWTTileMax) tmax = kWTTileMax;
+  if (w.kb > tmax) return LLVQ_EUNSUPPORTED;
+  a.tmax = tmax;
+  int grid = 0;
+  const int r1 = (w.rows + kGridMax - 1) / kGridMax;
+  if ((long)r1 * w.kb <= tmax) {
+    a.rows_per_tile = r1;
+    a.ntiles = (w.rows + r1 - 1) / r1;
+    grid = a.ntiles;
+  } else {
+    int nt = 0, g = 0;
+    const int r = pick_rows_per_tile(w.rows, w.kb, tmax, &nt, &g);
+    if (r == 0) return LLVQ_EUNSUPPORTED;
+    a.rows_per_tile = r;
+    a.ntiles = nt;
+    grid = g;
+  }
+  const uint32_t T = (uint32_t)(a.rows_per_tile * w.kb);
+  a.qj = align16(a.ctr + 16u);
+  a.qk = a.qj + 8u * T;
+  a.part = align16(a.qk + 4u * T);
+  a.xs = align16(a.part + 4u * T);        // the value tile, 24 bytes per block
+  const uint32_t total = a.xs + 24u * T;
+  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  const uint8_t* pk = static_cast<const uint8_t*>(packed);
+  const __half* sc = static_cast<const __half*>(scales);
+  if (out_kind == LLVQ_OUT_POINTS_I8)
+    hipLaunchKernelGGL((k_decode_wide_tile<LLVQ_OUT_POINTS_I8>), dim3(grid), dim3(kWTThreads), total, s, w, a, pk,
+                       sc, out, err, ovec);
+  else
+    hipLaunchKernelGGL((k_decode_wide_tile<LLVQ_OUT_BF16>), dim3(grid), dim3(kWTThreads), total, s, w, a, pk, sc,
+                       out, err, ovec);
   return launch_status();
 }
 

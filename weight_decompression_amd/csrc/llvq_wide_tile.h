@@ -328,3 +328,248 @@ __global__ __launch_bounds__(kWTThreads) void k_gemv_wide_tile(WDesc d, WTArgs a
     __syncthreads();
   }
 }
+
+// ---------------------------------------------------------------------------
+// Decode of the general decoder with coset queues: the same classification and per-part
+// decoders, each block's 24 values written as int8 into an LDS tile laid out like the
+// output ([rows][kb * 24]); then a store phase walks the tile row by row, 8 columns per lane
+// (bf16 = RNE(fp32(v) x scale), or the int8 values), so a wavefront's stores are contiguous.
+// The decode itself reads class records and the inverse table from global memory, which
+// never waits on stores: they all come after the tile's last barrier.
+
+// odd block's values in position order into the tile (3 x 8 bytes)
+__device__ __forceinline__ void wt_odd_vals(uint8_t* tile, const double* rc, uint64_t J, const LlvqWideClass& cr) {
+  const uint32_t c = dev_tables::kGolayTable[(uint32_t)(J & 4095u)];
+  Unranker T;
+  wt_init(T, J >> 12, cr.P_T, 24u, cr.cc, cr.cv);
+  uint32_t w[6];
+#pragma unroll
+  for (int q = 0; q < 6; ++q) {
+    uint32_t x = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p = 4 * q + e;
+      const int v = (int)wt_next(T, rc);
+      const bool neg = ((v & 3) == 1) != (((c >> p) & 1u) != 0u);
+      x |= (uint32_t)(uint8_t)(neg ? -v : v) << (8 * e);
+    }
+    w[q] = x;
+  }
+  uint2* d = reinterpret_cast<uint2*>(tile);
+  d[0] = make_uint2(w[0], w[1]);
+  d[1] = make_uint2(w[2], w[3]);
+  d[2] = make_uint2(w[4], w[5]);
+}
+
+// even block's values by position into the tile
+__device__ __forceinline__ void wt_even_vals(uint8_t* tile, const double* rc, uint64_t J, const LlvqWideClass& cr) {
+  const uint32_t w = cr.w;
+  const uint32_t A = dev_tables::kWideCodewords[w];
+  uint64_t r, ip;
+  if (A == 1u) {
+    r = 0;
+    ip = J;
+  } else {
+    ip = div_u64(J, A, r);
+  }
+  const uint32_t B = cr.B;
+  const uint32_t s = (uint32_t)(ip & ((1ull << B) - 1ull));
+  const uint64_t R = ip >> B;
+  const uint32_t c = dev_tables::kGolayTable[dev_tables::kWideGolayOffset[w] + (uint32_t)r];
+  uint64_t rs, rt;
+  if (cr.P_S == 1) {
+    rs = 0;
+    rt = R;
+  } else {
+    rs = div_u64(R, cr.P_T, rt);
+  }
+  {
+    Unranker S;
+    wt_init(S, rs, cr.P_S, w, cr.sc, cr.sv);
+    const uint32_t wm1 = w ? w - 1u : 0u;
+    const uint32_t negq = (((uint32_t)__popc(s & ((1u << wm1) - 1u))) & 1u) ^ cr.pi;
+    uint32_t bits = s, cm = c;
+    for (uint32_t i = 0; i < w; ++i) {
+      const uint32_t p = (uint32_t)__builtin_ctz(cm);
+      cm &= cm - 1u;
+      const int v = (int)wt_next(S, rc);
+      uint32_t neg;
+      if (i + 1u == w) {
+        neg = negq;
+      } else {
+        neg = bits & 1u;
+        bits >>= 1;
+      }
+      tile[p] = (uint8_t)(neg ? -v : v);
+    }
+  }
+  {
+    Unranker T;
+    wt_init(T, rt, cr.P_T, 24u - w, cr.cc, cr.cv);
+    uint32_t bits = w ? s >> (w - 1u) : s;
+    uint32_t cm = ~c & 0xffffffu;
+    for (uint32_t i = w; i < 24u; ++i) {
+      const uint32_t p = (uint32_t)__builtin_ctz(cm);
+      cm &= cm - 1u;
+      const int v = (int)wt_next(T, rc);
+      uint32_t neg = 0u;
+      if (v != 0) {
+        neg = bits & 1u;
+        bits >>= 1;
+      }
+      tile[p] = (uint8_t)(neg ? -v : v);
+    }
+  }
+}
+
+// int8 byte q of u as fp32
+__device__ __forceinline__ float wt_i8(uint32_t u, int q) {
+  return (float)(int)__builtin_amdgcn_sbfe(u, 8 * q, 8);
+}
+
+template <int OUT>
+__global__ __launch_bounds__(kWTThreads) void k_decode_wide_tile(WDesc d, WTArgs a, const uint8_t* __restrict__ packed,
+                                                                 const __half* __restrict__ scales,
+                                                                 void* __restrict__ out, int32_t* err, bool ovec) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
+  const int kb = d.kb;
+  const uint32_t rowbytes = (uint32_t)kb * 24u;
+  double* rc = reinterpret_cast<double*>(smem + a.rc);
+  uint64_t* qj = reinterpret_cast<uint64_t*>(smem + a.qj);
+  uint32_t* qk = reinterpret_cast<uint32_t*>(smem + a.qk);
+  float* part = reinterpret_cast<float*>(smem + a.part);
+  int* ctr = reinterpret_cast<int*>(smem + a.ctr);
+  uint8_t* tile = smem + a.xs;            // the value tile takes the place of x
+  if (tid < 32) rc[tid] = tid ? 1.0 / (double)tid : 0.0;
+  if (tid < 4) ctr[tid] = 0;
+  __syncthreads();
+
+  for (int tl = blockIdx.x; tl < a.ntiles; tl += gridDim.x) {
+    const int row0 = tl * a.rows_per_tile;
+    const int nrows = min(a.rows_per_tile, d.rows - row0);
+    const int T = nrows * kb;
+    const uint64_t j0 = (uint64_t)row0 * (uint64_t)kb;
+
+    // 1. classify (as the GEMV; an index past the shell union writes zeros into the tile)
+    for (int f0 = wave * 64; f0 < T; f0 += kWTThreads) {
+      const int f = f0 + lane;
+      bool odd = false, even = false;
+      uint64_t J = 0;
+      uint32_t k = 0;
+      if (f < T) {
+        uint64_t lo, hi;
+        uint32_t g;
+        float sc = 0.0f;
+        if (wide_block(d, packed, j0 + (uint64_t)f, lo, hi, g)) {
+          k = (uint32_t)wide_find_class(lo, hi, d.max_shell);
+          LLVQ_DCHECK(k < (uint32_t)LLVQ_WIDE_NUM_CLASSES && dev_tables::kWideClass[k].m <= d.max_shell);
+          const LlvqWideClass& cr = dev_tables::kWideClass[k];
+          J = lo - cr.start_lo;
+          odd = cr.parity != 0;
+          even = !odd;
+          if (OUT == LLVQ_OUT_BF16)
+            sc = sg ? __fmul_rn(__half2float(scales[g]), dev_tables::kWideInvNorm32[cr.m])
+                    : __half2float(scales[row0 + (int)(((float)f + 0.5f) / (float)kb)]);
+        } else {
+          if (err) atomicAdd(err, 1);
+          uint2* z = reinterpret_cast<uint2*>(tile + 24u * (uint32_t)f);
+          z[0] = make_uint2(0u, 0u);
+          z[1] = make_uint2(0u, 0u);
+          z[2] = make_uint2(0u, 0u);
+        }
+        part[f] = sc;
+      }
+      const uint64_t bo = __ballot(odd), be = __ballot(even);
+      int baseo = 0, basee = 0;
+      if (lane == 0) {
+        baseo = atomicAdd(&ctr[0], __popcll(bo));
+        basee = atomicAdd(&ctr[1], __popcll(be));
+      }
+      baseo = __builtin_amdgcn_readfirstlane(baseo);
+      basee = __builtin_amdgcn_readfirstlane(basee);
+      const uint32_t po = __builtin_amdgcn_mbcnt_hi((uint32_t)(bo >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bo, 0u));
+      const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+      const int slot = odd ? baseo + (int)po : T - 1 - (basee + (int)pe);
+      if (odd || even) {
+        LLVQ_DCHECK(slot >= 0 && slot < T);
+        qj[slot] = J;
+        qk[slot] = k | ((uint32_t)f << 16);
+      }
+    }
+    __syncthreads();
+
+    // 2. decode chunks into the tile: odd queue, then even queue
+    const int nodd = ctr[0], neven = ctr[1];
+    const int nco = (nodd + 63) >> 6;
+    const int nch = nco + ((neven + 63) >> 6);
+    for (;;) {
+      int c = 0;
+      if (lane == 0) c = atomicAdd(&ctr[2], 1);
+      c = __builtin_amdgcn_readfirstlane(c);
+      if (c >= nch) break;
+      if (c < nco) {
+        const int e = (c << 6) + lane;
+        if (e < nodd) {
+          const uint32_t kf = qk[e];
+          wt_odd_vals(tile + 24u * (kf >> 16), rc, qj[e], dev_tables::kWideClass[kf & 0xffffu]);
+        }
+      } else {
+        const int e = ((c - nco) << 6) + lane;
+        if (e < neven) {
+          const uint32_t kf = qk[T - 1 - e];
+          wt_even_vals(tile + 24u * (kf >> 16), rc, qj[T - 1 - e], dev_tables::kWideClass[kf & 0xffffu]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // 3. store the tile row by row, 8 columns per lane
+    if (OUT == LLVQ_OUT_POINTS_I8) {
+      const uint32_t n8 = rowbytes >> 3;
+      for (int rl = 0; rl < nrows; ++rl) {
+        int8_t* orow = static_cast<int8_t*>(out) + (size_t)(row0 + rl) * rowbytes;
+        const uint8_t* trow = tile + (uint32_t)rl * rowbytes;
+        for (uint32_t j = (uint32_t)tid; j < n8; j += kWTThreads) {
+          const uint2 u = *reinterpret_cast<const uint2*>(trow + 8u * j);
+          if (ovec) {
+            *reinterpret_cast<uint2*>(orow + 8u * j) = u;
+          } else {
+            reinterpret_cast<uint32_t*>(orow + 8u * j)[0] = u.x;   // rows are whole dwords, out 4-byte aligned
+            reinterpret_cast<uint32_t*>(orow + 8u * j)[1] = u.y;
+          }
+        }
+      }
+    } else {
+      const int K = d.cols;
+      const uint32_t n8 = (uint32_t)(K + 7) >> 3;
+      for (int rl = 0; rl < nrows; ++rl) {
+        uint16_t* orow = static_cast<uint16_t*>(out) + (size_t)(row0 + rl) * (size_t)K;
+        const uint8_t* trow = tile + (uint32_t)rl * rowbytes;
+        for (uint32_t j = (uint32_t)tid; j < n8; j += kWTThreads) {
+          const uint2 u = *reinterpret_cast<const uint2*>(trow + 8u * j);
+          const float sc = part[rl * kb + (int)(j / 3u)];
+          float v[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] = __fmul_rn(wt_i8(q < 4 ? u.x : u.y, q & 3), sc);
+          const uint4 pk = make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
+                                      pack_bf16(v[6], v[7]));
+          const uint32_t col = 8u * j;
+          if (ovec && (int)col + 8 <= K) {
+            *reinterpret_cast<uint4*>(orow + col) = pk;
+          } else {
+            const uint32_t wv[4] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if ((int)(col + q) < K) orow[col + q] = (uint16_t)(wv[q >> 1] >> (16 * (q & 1)));
+          }
+        }
+      }
+    }
+    if (tid < 4) ctr[tid] = 0;
+    __syncthreads();
+  }
+}
