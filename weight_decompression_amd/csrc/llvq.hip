@@ -498,8 +498,34 @@ static_assert(offsetof(LlvqClassHot, nc1) == 64 && offsetof(LlvqClassHot, sv1lo8
               "the even decoder reads part 1 at these offsets");
 
 namespace {
-constexpr uint32_t kLdsBudget = 160u * 1024u;   // one workgroup per CU
-constexpr int kGridMax = 256;                    // one workgroup per CU
+// Per-device launch limits of the one-workgroup-per-CU kernels: the workgroups of a grid
+// (one per CU) and the LDS of one workgroup (at most 160 KB, the gfx950 figure the tiles are
+// sized for).  Queried once per device and kept.
+struct DevLimits {
+  uint32_t lds;
+  int grid;
+};
+constexpr int kMaxLimitDevices = 64;
+std::mutex g_limits_mu;
+DevLimits g_limits[kMaxLimitDevices];
+
+DevLimits device_limits(hipStream_t stream) {
+  DevLimits l = {160u * 1024u, 256};
+  int dev = -1;
+  // (a failed query leaves its error pending, so the call's launch status reports it; a
+  // caller's pending error is not cleared here either)
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxLimitDevices) return l;
+  std::lock_guard<std::mutex> lock(g_limits_mu);
+  if (g_limits[dev].grid == 0) {
+    int cus = 0, lds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) l.grid = cus;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && lds > 0 &&
+        (uint32_t)lds < l.lds)
+      l.lds = (uint32_t)lds;
+    g_limits[dev] = l;
+  }
+  return g_limits[dev];
+}
 
 // Rows per tile for the engine kernels: among the R with R * Kb <= tmax, the one that
 // minimises the work of the busiest workgroup, counting each tile as its blocks plus a
@@ -507,7 +533,7 @@ constexpr int kGridMax = 256;                    // one workgroup per CU
 // partly filled chunks leave waves idle).  Ties go to larger tiles.
 constexpr long kTileOverhead = 1024;
 
-int pick_rows_per_tile(int rows, int kb, int tmax, int* ntiles_out, int* grid_out) {
+int pick_rows_per_tile(int rows, int kb, int tmax, int gmax, int* ntiles_out, int* grid_out) {
   int rmax = tmax / kb;
   if (rmax > rows) rmax = rows;
   if (rmax < 1) return 0;
@@ -515,7 +541,7 @@ int pick_rows_per_tile(int rows, int kb, int tmax, int* ntiles_out, int* grid_ou
   long best_cost = -1;
   for (int r = rmax; r >= 1; --r) {
     const long nt = (rows + r - 1) / r;
-    const long g = nt < kGridMax ? nt : kGridMax;
+    const long g = nt < gmax ? nt : gmax;
     const long cost = ((nt + g - 1) / g) * ((long)r * kb + kTileOverhead);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
@@ -524,7 +550,7 @@ int pick_rows_per_tile(int rows, int kb, int tmax, int* ntiles_out, int* grid_ou
   }
   const int nt = (rows + best_r - 1) / best_r;
   *ntiles_out = nt;
-  *grid_out = nt < kGridMax ? nt : kGridMax;
+  *grid_out = nt < gmax ? nt : gmax;
   return best_r;
 }
 
@@ -532,6 +558,9 @@ int pick_rows_per_tile(int rows, int kb, int tmax, int* ntiles_out, int* grid_ou
 // not fit its tiling (the generic kernel then runs).
 int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype,
                    float* y, int32_t* err, hipStream_t s) {
+  const DevLimits lim = device_limits(s);
+  const uint32_t lds = lim.lds;
+  const int gmax = lim.grid;
   if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;   // 32-bit field index
   const bool xf32 = x_dtype == LLVQ_X_F32;
   const int nbuckets = (int)(((host_tables::kIndexCount[k.max_shell] - 1) >> k.bshift) + 1);
@@ -540,20 +569,20 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   const uint32_t xbytes = align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u));
   const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 1);
   const uint32_t fixed = base + (uint32_t)kRingBytes + xbytes + 16u;
-  if (fixed + 4u * (uint32_t)k.kb > kLdsBudget) return LLVQ_EUNSUPPORTED;
-  int tmax = (int)((kLdsBudget - fixed) / 4u);
+  if (fixed + 4u * (uint32_t)k.kb > lds) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((lds - fixed) / 4u);
   if (tmax > kETileMax) tmax = kETileMax;
   EArgs a = {};
   int grid = 0;
   // every workgroup's rows as one tile when they fit, else the cost-model tiling
-  const int r1 = (k.rows + kGridMax - 1) / kGridMax;
+  const int r1 = (k.rows + gmax - 1) / gmax;
   if ((long)r1 * k.kb <= tmax) {
     a.rows_per_tile = r1;
     a.ntiles = (k.rows + r1 - 1) / r1;
     grid = a.ntiles;
   } else {
     int nt = 0, g = 0;
-    const int r = pick_rows_per_tile(k.rows, k.kb, tmax, &nt, &g);
+    const int r = pick_rows_per_tile(k.rows, k.kb, tmax, gmax, &nt, &g);
     if (r == 0) return LLVQ_EUNSUPPORTED;
     a.rows_per_tile = r;
     a.ntiles = nt;
@@ -565,7 +594,7 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   a.L.buf[0].part = a.rings + (uint32_t)kRingBytes;
   a.xs = align16(a.L.buf[0].part + 4u * (uint32_t)(a.rows_per_tile * k.kb));
   const uint32_t total = a.xs + align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u));
-  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  if (total > lds) return LLVQ_EUNSUPPORTED;
   if (xf32)
     hipLaunchKernelGGL((k_gemv_b1<true>), dim3(grid), dim3(kEThreads), total, s, k, a,
                        static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, y, err);
@@ -581,6 +610,9 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
 // LLVQ_EUNSUPPORTED when a row does not fit a tile (the caller then falls back).
 int launch_decode_stream(const KDesc* k, int n, const void* const* packed, const void* const* scales,
                          int32_t out_kind, void* const* outs, int32_t* err, hipStream_t s) {
+  const DevLimits lim = device_limits(s);
+  const uint32_t lds = lim.lds;
+  const int gmax = lim.grid;
   const KDesc& k0 = k[0];
   const int nbuckets = (int)(((host_tables::kIndexCount[k0.max_shell] - 1) >> k0.bshift) + 1);
   const int ng = (k0.mode == LLVQ_MODE_SHAPEGAIN ? 1 << k0.gain_bits : 1) * n;
@@ -590,13 +622,13 @@ int launch_decode_stream(const KDesc* k, int n, const void* const* packed, const
   m.rings = m.L.golay + 4096u * 4u;
   m.part = m.rings + (uint32_t)kRingBytes;
   const uint32_t fixed = m.part + (uint32_t)kStageBytes + 32u;
-  if (fixed >= kLdsBudget) return LLVQ_EUNSUPPORTED;
-  int tmax = (int)((kLdsBudget - fixed) / 4u) & ~15;
+  if (fixed >= lds) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((lds - fixed) / 4u) & ~15;
   if (tmax > kETileMax) tmax = kETileMax;
   m.tmax = tmax;
   m.stage = align16(m.part + 4u * (uint32_t)tmax);
   const uint32_t total = m.stage + (uint32_t)kStageBytes;
-  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  if (total > lds) return LLVQ_EUNSUPPORTED;
   m.nbuckets = nbuckets;
   m.n = n;
   long long blocks = 0;
@@ -615,7 +647,7 @@ int launch_decode_stream(const KDesc* k, int n, const void* const* packed, const
   m.total = blocks;
   // at least ~2K blocks per workgroup, at most one workgroup per CU
   long long g = (blocks + 2047) / 2048;
-  if (g > kGridMax) g = kGridMax;
+  if (g > gmax) g = gmax;
   if (g < 1) g = 1;
   if (out_kind == LLVQ_OUT_POINTS_I8)
     hipLaunchKernelGGL((k_decode_stream<LLVQ_OUT_POINTS_I8>), dim3((unsigned)g), dim3(kEThreads), total, s, k0, m,
@@ -629,6 +661,9 @@ int launch_decode_stream(const KDesc* k, int n, const void* const* packed, const
 // LLVQ_EUNSUPPORTED when the shape does not fit (the VALU kernel then runs).
 int launch_gemm_mfma(const KDesc& k, const void* packed, const void* scales, const void* x, int batch, float* y,
                      int32_t* err, hipStream_t s) {
+  const DevLimits lim = device_limits(s);
+  const uint32_t lds = lim.lds;
+  const int gmax = lim.grid;
   if ((uint64_t)k.rows * (uint64_t)k.kb >= (1ull << 30)) return LLVQ_EUNSUPPORTED;
   // the activations are addressed with 32-bit buffer offsets (bit 31 marks "no data")
   if ((uint64_t)batch * (uint64_t)k.cols * 2u + 8192u >= (1ull << 31)) return LLVQ_EUNSUPPORTED;
@@ -638,8 +673,8 @@ int launch_gemm_mfma(const KDesc& k, const void* packed, const void* scales, con
   const uint32_t red = (uint32_t)kEWaves * 64u * 4u * 4u;   // reduction buffer, over the byte tile
   // per block: queue entry 8 B + two block scales 8 B + 24 value bytes; at least one
   // block column; slack for the alignment of the three arrays
-  if (base + 64u + 40u * kGRows > kLdsBudget) return LLVQ_EUNSUPPORTED;
-  int tmax = (int)((kLdsBudget - base - 64u) / 40u);
+  if (base + 64u + 40u * kGRows > lds) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((lds - base - 64u) / 40u);
   if (tmax > kETileMax) tmax = kETileMax;
   // chunks of at most kEWaves units of kEUnit blocks: one classification unit per wave
   const int wmax = min(tmax / kGRows, kEWaves * kEUnit / kGRows);
@@ -660,8 +695,8 @@ int launch_gemm_mfma(const KDesc& k, const void* packed, const void* scales, con
   // (16 bytes past the tile: the k 24..31 lanes of the last block read 8 bytes beyond it)
   const uint32_t tile = align16(24u * T) + 16u;
   const uint32_t total = g.e.xs + (tile > red ? tile : red);
-  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
-  const int grid = g.ngroups < kGridMax ? g.ngroups : kGridMax;
+  if (total > lds) return LLVQ_EUNSUPPORTED;
+  const int grid = g.ngroups < gmax ? g.ngroups : gmax;
   hipLaunchKernelGGL(k_gemm_mfma, dim3(grid), dim3(kEThreads), total, s, k, g, static_cast<const uint8_t*>(packed),
                      static_cast<const __half*>(scales), static_cast<const uint16_t*>(x), y, err);
   return launch_status();
@@ -725,6 +760,9 @@ int decode_wide(const llvq_desc* d, const void* packed, const void* scales, int3
 // when x or a row does not fit (the one-block-per-lane kernel then runs).
 int launch_gemv_wide_tile(const WDesc& w, const void* packed, const void* scales, const void* x, int32_t x_dtype,
                           float* y, int32_t* err, hipStream_t s) {
+  const DevLimits lim = device_limits(s);
+  const uint32_t lds = lim.lds;
+  const int gmax = lim.grid;
   if ((uint64_t)w.rows * (uint64_t)w.kb >= (1ull << 31)) return LLVQ_EUNSUPPORTED;
   const bool xbf16 = x_dtype == LLVQ_X_BF16;
   WTArgs a = {};
@@ -732,20 +770,20 @@ int launch_gemv_wide_tile(const WDesc& w, const void* packed, const void* scales
   a.rc = align16((uint32_t)w.kb * 24u * (xbf16 ? 2u : 4u));
   a.ctr = a.rc + 32u * 8u;
   const uint32_t fixed = a.ctr + 16u + 64u;
-  if (fixed >= kLdsBudget) return LLVQ_EUNSUPPORTED;
-  int tmax = (int)((kLdsBudget - fixed) / 16u) & ~15;
+  if (fixed >= lds) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((lds - fixed) / 16u) & ~15;
   if (tmax > kWTTileMax) tmax = kWTTileMax;
   if (w.kb > tmax) return LLVQ_EUNSUPPORTED;
   a.tmax = tmax;
   int grid = 0;
-  const int r1 = (w.rows + kGridMax - 1) / kGridMax;
+  const int r1 = (w.rows + gmax - 1) / gmax;
   if ((long)r1 * w.kb <= tmax) {
     a.rows_per_tile = r1;
     a.ntiles = (w.rows + r1 - 1) / r1;
     grid = a.ntiles;
   } else {
     int nt = 0, g = 0;
-    const int r = pick_rows_per_tile(w.rows, w.kb, tmax, &nt, &g);
+    const int r = pick_rows_per_tile(w.rows, w.kb, tmax, gmax, &nt, &g);
     if (r == 0) return LLVQ_EUNSUPPORTED;
     a.rows_per_tile = r;
     a.ntiles = nt;
@@ -756,7 +794,7 @@ int launch_gemv_wide_tile(const WDesc& w, const void* packed, const void* scales
   a.qk = a.qj + 8u * T;
   a.part = align16(a.qk + 4u * T);
   const uint32_t total = a.part + 4u * T;
-  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  if (total > lds) return LLVQ_EUNSUPPORTED;
   const uint8_t* pk = static_cast<const uint8_t*>(packed);
   const __half* sc = static_cast<const __half*>(scales);
   if (xbf16)
@@ -771,24 +809,27 @@ int launch_gemv_wide_tile(const WDesc& w, const void* packed, const void* scales
 // LLVQ_EUNSUPPORTED when a row does not fit (the one-block-per-lane kernel then runs).
 int launch_decode_wide_tile(const WDesc& w, const void* packed, const void* scales, int32_t out_kind, void* out,
                             int32_t* err, bool ovec, hipStream_t s) {
+  const DevLimits lim = device_limits(s);
+  const uint32_t lds = lim.lds;
+  const int gmax = lim.grid;
   if ((uint64_t)w.rows * (uint64_t)w.kb >= (1ull << 31)) return LLVQ_EUNSUPPORTED;
   WTArgs a = {};
   a.rc = 0;
   a.ctr = 32u * 8u;
   const uint32_t fixed = a.ctr + 16u + 64u;
-  int tmax = (int)((kLdsBudget - fixed) / 40u) & ~15;
+  int tmax = (int)((lds - fixed) / 40u) & ~15;
   if (tmax > kWTTileMax) tmax = kWTTileMax;
   if (w.kb > tmax) return LLVQ_EUNSUPPORTED;
   a.tmax = tmax;
   int grid = 0;
-  const int r1 = (w.rows + kGridMax - 1) / kGridMax;
+  const int r1 = (w.rows + gmax - 1) / gmax;
   if ((long)r1 * w.kb <= tmax) {
     a.rows_per_tile = r1;
     a.ntiles = (w.rows + r1 - 1) / r1;
     grid = a.ntiles;
   } else {
     int nt = 0, g = 0;
-    const int r = pick_rows_per_tile(w.rows, w.kb, tmax, &nt, &g);
+    const int r = pick_rows_per_tile(w.rows, w.kb, tmax, gmax, &nt, &g);
     if (r == 0) return LLVQ_EUNSUPPORTED;
     a.rows_per_tile = r;
     a.ntiles = nt;
@@ -800,7 +841,7 @@ int launch_decode_wide_tile(const WDesc& w, const void* packed, const void* scal
   a.part = align16(a.qk + 4u * T);
   a.xs = align16(a.part + 4u * T);        // the value tile, 24 bytes per block
   const uint32_t total = a.xs + 24u * T;
-  if (total > kLdsBudget) return LLVQ_EUNSUPPORTED;
+  if (total > lds) return LLVQ_EUNSUPPORTED;
   const uint8_t* pk = static_cast<const uint8_t*>(packed);
   const __half* sc = static_cast<const __half*>(scales);
   if (out_kind == LLVQ_OUT_POINTS_I8)
