@@ -49,52 +49,52 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
+        "source_sha256": "0dad868da423e8d45ffbf85960f5b12cbf1cf0964cd52b055ac70191be363a0f",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
         "valu_lane_ops_per_unit": 613.8,       # SQ_INSTS_VALU * 64 / blocks
         "valu_mix_peak_tops": 38.92,           # peak for the executed instruction mix
-        "fetch_bytes_per_launch": 12255109,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "fetch_bytes_per_launch": 12255155,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
+        "source_sha256": "0dad868da423e8d45ffbf85960f5b12cbf1cf0964cd52b055ac70191be363a0f",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
         "valu_lane_ops_per_unit": 696.1,
         "valu_mix_peak_tops": 38.53,
-        "fetch_bytes_per_launch": 61982738,
+        "fetch_bytes_per_launch": 61982099,
         "write_bytes_per_launch": 1835008,
     },
     "gemv_3bit_b1": {
-        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
-        "summary": "profiles/gemv_3bit_4096x11008_batch1_k_gemv_wide.md",
-        "unit_of_work": "24-weight block (k_gemv_wide)",
-        "valu_lane_ops_per_unit": 3696.2,
-        "valu_mix_peak_tops": 35.20,
-        "fetch_bytes_per_launch": 32853425,
-        "write_bytes_per_launch": 32768,
+        "source_sha256": "0dad868da423e8d45ffbf85960f5b12cbf1cf0964cd52b055ac70191be363a0f",
+        "summary": "profiles/gemv_3bit_4096x11008_batch1_k_gemv_wide_tile.md",
+        "unit_of_work": "24-weight block (k_gemv_wide_tile)",
+        "valu_lane_ops_per_unit": 2018.5,
+        "valu_mix_peak_tops": 36.04,
+        "fetch_bytes_per_launch": 32855878,
+        "write_bytes_per_launch": 16384,
     },
     "decode_3bit": {
-        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
-        "summary": "profiles/decode_bf16_3bit_4096x11008_k_decode_wide.md",
-        "unit_of_work": "24-weight block (k_decode_wide<bf16>)",
-        "valu_lane_ops_per_unit": 3389.7,
-        "valu_mix_peak_tops": 35.15,
-        "fetch_bytes_per_launch": 37935042,
-        "write_bytes_per_launch": 90295163,
+        "source_sha256": "0dad868da423e8d45ffbf85960f5b12cbf1cf0964cd52b055ac70191be363a0f",
+        "summary": "profiles/decode_bf16_3bit_4096x11008_k_decode_wide_tile.md",
+        "unit_of_work": "24-weight block (k_decode_wide_tile<bf16>)",
+        "valu_lane_ops_per_unit": 2020.3,
+        "valu_mix_peak_tops": 35.80,
+        "fetch_bytes_per_launch": 43991438,
+        "write_bytes_per_launch": 90177536,
     },
     "decode_bf16": {
-        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
+        "source_sha256": "0dad868da423e8d45ffbf85960f5b12cbf1cf0964cd52b055ac70191be363a0f",
         "summary": "profiles/decode_bf16_7b_k_decode_stream.md",
         "unit_of_work": "24-weight block (k_decode_stream<bf16>)",
         "valu_lane_ops_per_unit": 668.4,
         "valu_mix_peak_tops": 38.88,
-        "fetch_bytes_per_launch": 102475494,           # one launch = two layers (14 tensors)
-        "write_bytes_per_launch": 1016186360,
+        "fetch_bytes_per_launch": 102476292,           # one launch = two layers (14 tensors)
+        "write_bytes_per_launch": 1022047544,
     },
     "roundtrip": {
-        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
+        "source_sha256": "0dad868da423e8d45ffbf85960f5b12cbf1cf0964cd52b055ac70191be363a0f",
         "summary": "profiles/roundtrip_1e7_k_decode_stream_k_rank.md",
         "unit_of_work": "point: decode to int8 (616.0) + rank (951.2)",
         "valu_lane_ops_per_unit": 1567.2,
@@ -104,7 +104,7 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": None,
     },
     "search": {
-        "source_sha256": "4f0aab86adb02e533b0947997f95eac03855d1042807d51dcf8c2660860ef67d",
+        "source_sha256": "0dad868da423e8d45ffbf85960f5b12cbf1cf0964cd52b055ac70191be363a0f",
         "summary": "profiles/search_4096x4096_k_search_k_rank.md",
         # The search issues more VALU instructions per clock than one per CU (mostly fp32
         # fma / max / compares), and more than the harmonic mix of single-instruction
