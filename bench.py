@@ -517,10 +517,27 @@ def run_search(a):
     if not a.no_cpu:
         from oracle import cpu_baseline as cb
         sample = blocks[: a.cpu_blocks].astype(np.float64)
-        dt, procs = cb.time_search(sample, M, "angular")
+        dt, procs, ref = cb.time_search(sample, M, "angular")
         out["cpu_baseline"] = {"value": len(sample) / dt, "unit": "blocks/s", "cores": procs, "kind": "oracle",
                                "sample": f"the first {len(sample)} blocks of the same tensor: exact class x "
                                          f"codeword search in numpy, {procs} processes, {dt:.2f} s wall"}
+        # parity: the GPU's index of each sampled block equals the oracle's, or (a near tie of
+        # the fp32 objective) its point scores the same fp64 objective to 1e-6
+        gi = idx[: len(sample)].cpu().numpy().astype(np.uint64)
+        gp = pts[: len(sample)].cpu().numpy().astype(np.float64)
+        same = ties = 0
+        for j, (I, v) in enumerate(ref):
+            if int(gi[j]) == int(I):
+                same += 1
+                continue
+            vo = np.asarray(v, dtype=np.float64)
+            og = float(sample[j] @ gp[j]) / float(np.linalg.norm(gp[j]))
+            oo = float(sample[j] @ vo) / float(np.linalg.norm(vo))
+            if abs(og - oo) <= 1e-6 * abs(oo):
+                ties += 1
+        out["parity"] = {"what": f"the first {len(sample)} blocks' indices vs the oracle's exact search",
+                         "blocks_checked": len(sample), "equal": same, "near_ties": ties,
+                         "pass": same + ties == len(sample)}
     return out
 
 
@@ -574,12 +591,14 @@ def run_fidelity(a):
         if int(err.item()) != 0:
             raise RuntimeError("quantiser reported invalid blocks")
         mse = float(((W[: desc.rows].double() - out.double()) ** 2).mean())
+        quantize_and_mse.last_packed = packed
         return mse, sec
 
     # shape-gain, 48 bits per block
     gains = torch.from_numpy(synth.chi_gain_table(16)).cuda()
     dsg = wd.make_desc(wd.MODE_SHAPEGAIN, rows, cols, 10, 44, 4)
     mse_sg, sec = quantize_and_mse(dsg, gains, True)
+    packed_sg, gains_sg = quantize_and_mse.last_packed, gains
     # Euclidean, 44 bits per block: the scale that minimises the MSE on a 1/8 subset
     sub = max(1, rows // 8)
     best = None
@@ -628,10 +647,36 @@ def run_fidelity(a):
     if not a.no_cpu:
         from oracle import cpu_baseline as cb
         sample = x[: a.cpu_blocks].astype(np.float64)
-        dt, procs = cb.time_search(sample, 10, "angular")
+        dt, procs, ref = cb.time_search(sample, 10, "angular")
         out["cpu_baseline"] = {"value": len(sample) / dt, "unit": "blocks/s", "cores": procs, "kind": "oracle",
                                "sample": f"exact angular search of the first {len(sample)} source blocks in numpy, "
                                          f"{procs} processes, {dt:.2f} s wall (the quantiser's time, not its MSE)"}
+        # parity of the shape-gain stream: each sampled block's 44-bit shape index equals the
+        # oracle search's (or ties it on the fp64 objective), and its gain index is the table
+        # entry nearest to the block's norm (fp64, ties to the lower index)
+        raw = packed_sg.cpu().numpy()[: 6 * len(sample)].reshape(-1, 6)
+        fv = np.zeros(len(sample), dtype=np.uint64)
+        for k in range(6):
+            fv |= raw[:, k].astype(np.uint64) << np.uint64(8 * k)
+        gtab = gains_sg.cpu().numpy().astype(np.float64)
+        from oracle import bijection
+        same = ties = gok = 0
+        for jb, (I, v) in enumerate(ref):
+            gi = int(fv[jb] & np.uint64((1 << 44) - 1))
+            gg = int(fv[jb] >> np.uint64(44))
+            if gi == int(I):
+                same += 1
+            else:
+                vg = np.asarray(bijection.unrank(gi, 10), dtype=np.float64)
+                vo = np.asarray(v, dtype=np.float64)
+                og = float(sample[jb] @ vg) / float(np.linalg.norm(vg))
+                oo = float(sample[jb] @ vo) / float(np.linalg.norm(vo))
+                ties += int(abs(og - oo) <= 1e-6 * abs(oo))
+            gok += int(gg == int(np.argmin(np.abs(gtab - np.linalg.norm(sample[jb])))))
+        out["parity"] = {"what": f"shape and gain indices of the first {len(sample)} blocks of the shape-gain stream "
+                                 f"vs the oracle's exact search and nearest gain",
+                         "blocks_checked": len(sample), "shape_equal": same, "near_ties": ties, "gain_equal": gok,
+                         "pass": same + ties == len(sample) and gok == len(sample)}
     return out
 
 
@@ -669,9 +714,12 @@ def run_gptq(a):
         return float(((D @ H) * D).sum()) / base
 
     res = {}
+    fields_sph = None
     for variant in ("direct", "euclid", "spherical"):
-        desc, packed, _ = gptq.gptq(Wt, H, 10, gains, variant=variant)
+        desc, packed, fields = gptq.gptq(Wt, H, 10, gains, variant=variant)
         res[variant] = loss(desc, packed)
+        if variant == "spherical":
+            fields_sph = fields.cpu().numpy().view(np.uint64)
     sec, wall = time_steps(lambda i: (gptq.gptq(Wt, H, 10, gains, variant="spherical"), 0)[1], a.steps, a.warmup,
                            stream)
     kb = synth.blocks_per_row(K)
@@ -689,11 +737,17 @@ def run_gptq(a):
         from oracle import gptq as ogptq
         rows = list(range(a.cpu_rows_gptq))
         t0 = _t.perf_counter()
-        ogptq.gptq(W, H.cpu().numpy(), 10, gains.cpu().numpy(), variant="spherical", rows=rows)
+        want_idx, want_g = ogptq.gptq(W, H.cpu().numpy(), 10, gains.cpu().numpy(), variant="spherical", rows=rows)
         dt = _t.perf_counter() - t0
         out["cpu_baseline"] = {"value": len(rows) * kb / dt, "unit": "blocks/s", "cores": 1, "kind": "oracle",
                                "sample": f"oracle spherical GPTQ of rows 0..{len(rows) - 1} of the same layer "
                                          f"(rows do not interact), one process, {dt:.1f} s wall"}
+        f = fields_sph.reshape(N, kb)[rows]
+        ok = np.logical_and((f & np.uint64((1 << 44) - 1)) == want_idx,
+                            (f >> np.uint64(44)).astype(np.int64) == want_g)
+        out["parity"] = {"what": f"shape and gain indices of rows 0..{len(rows) - 1} of the spherical GPTQ run vs "
+                                 f"the oracle's GPTQ of the same rows", "blocks_checked": int(ok.size),
+                         "blocks_differing": int(ok.size - ok.sum()), "pass": bool(ok.all())}
     return out
 
 

@@ -42,14 +42,13 @@ def time_gemv_rows(packed, rows, cols, M, mode, shape_bits, gain_bits, gains, ro
 def _search_chunk(args):
     blocks, M, mode = args
     from . import search
-    for b in blocks:
-        search.search(b, M, mode)
-    return len(blocks)
+    return [search.search(b, M, mode) for b in blocks]
 
 
 def time_search(blocks, M, mode, procs=None):
     """Wall seconds for the oracle's exact search (oracle/search.py) of every block in
-    `blocks` (float64 [n][24]) over a process pool, and the number of processes used."""
+    `blocks` (float64 [n][24]) over a process pool, the number of processes used, and the
+    oracle's (global index, point) of every block in order."""
     procs = procs or parallel.cores()
     procs = max(1, min(procs, len(blocks)))
     chunks = [blocks[i::procs] for i in range(procs)]
@@ -57,7 +56,10 @@ def time_search(blocks, M, mode, procs=None):
     with ctx.Pool(procs) as pool:
         pool.map(_search_chunk, [(blocks[:1], M, mode)] * procs)   # warm the per-process tables
         t0 = time.perf_counter()
-        done = sum(pool.map(_search_chunk, [(c, M, mode) for c in chunks]))
+        parts = pool.map(_search_chunk, [(c, M, mode) for c in chunks])
         dt = time.perf_counter() - t0
-    assert done == len(blocks)
-    return dt, procs
+    res = [None] * len(blocks)
+    for i, part in enumerate(parts):
+        res[i::procs] = part
+    assert all(r is not None for r in res)
+    return dt, procs, res
