@@ -534,3 +534,40 @@ def test_rank_perturbed_points_and_unaligned_input():
         got = [int(v) for v in out.cpu().numpy().view(np.uint64)]
         assert got == expect
         assert int(err.item()) == nbad
+
+
+@pytest.mark.parametrize("wide", [False, True])
+def test_decode_into_unaligned_outputs_equals_aligned(wide):
+    # bf16 rows 2-byte aligned only, int8 points 4-byte aligned only: the element-wise store
+    # paths of the streamed decode (2-bit) and of the general decoder's tile decode give the
+    # same bytes as the vector stores; cols 4000 is not a multiple of 24 (ragged last block)
+    if wide:
+        t = synth.make_wide_tensor("wunal", 91, 0, 61, 4000, leech.index_count(42), batch=0)
+    else:
+        t = synth.make_tensor("unal", 91, 0, 61, 4000, C10, batch=0)
+    desc, packed, scales, _ = dev(t)
+    n16 = t.rows * t.cols
+    ref = torch.empty((t.rows, t.cols), dtype=torch.bfloat16, device="cuda")
+    wd.decode(desc, packed, scales, wd.OUT_BF16, ref)
+    buf = torch.zeros(n16 + 8, dtype=torch.bfloat16, device="cuda")
+    view = buf[1:1 + n16].view(t.rows, t.cols)                   # 2-byte aligned
+    wd.decode(desc, packed, scales, wd.OUT_BF16, view)
+    n8 = t.rows * t.kb * 24
+    pref = torch.empty((t.rows, t.kb * 24), dtype=torch.int8, device="cuda")
+    wd.decode(desc, packed, scales, wd.OUT_POINTS_I8, pref)
+    pbuf = torch.zeros(n8 + 16, dtype=torch.int8, device="cuda")
+    pview = pbuf[4:4 + n8].view(t.rows, t.kb * 24)               # 4-byte aligned
+    wd.decode(desc, packed, scales, wd.OUT_POINTS_I8, pview)
+    torch.cuda.synchronize()
+    assert torch.equal(view.view(torch.int16), ref.view(torch.int16))
+    assert not buf[:1].view(torch.int16).any() and not buf[1 + n16:].view(torch.int16).any()
+    assert torch.equal(pview, pref)
+    assert not pbuf[:4].any() and not pbuf[4 + n8:].any()
+    raw = t.packed.tobytes()
+    M = t.max_shell
+    for r in (0, t.rows - 1):
+        got = view[r].view(torch.int16).cpu().numpy().view(np.uint16)
+        want = reference.decode_row_bf16(raw, t.rows, t.cols, M, t.mode, t.shape_bits, t.gain_bits, t.scales_f16,
+                                         None, r)
+        assert np.array_equal(got, want), r
+    say(f"decode into unaligned outputs ({'general decoder' if wide else '2-bit'}): equal to aligned")
