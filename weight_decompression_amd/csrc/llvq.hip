@@ -756,8 +756,9 @@ int decode_wide(const llvq_desc* d, const void* packed, const void* scales, int3
 }
 
 // Batch-1 GEMV of the general decoder with coset queues (llvq_wide_tile.h): LDS holds x
-// of all columns, the reciprocals and 16 bytes per block of a tile.  LLVQ_EUNSUPPORTED
-// when x or a row does not fit (the one-block-per-lane kernel then runs).
+// of all columns, the reciprocals, the waves' rings (12 bytes an entry) and 4 bytes per
+// block of a tile.  LLVQ_EUNSUPPORTED when x or a row does not fit (the
+// one-block-per-lane kernel then runs).
 int launch_gemv_wide_tile(const WDesc& w, const void* packed, const void* scales, const void* x, int32_t x_dtype,
                           float* y, int32_t* err, hipStream_t s) {
   const DevLimits lim = device_limits(s);
@@ -769,9 +770,12 @@ int launch_gemv_wide_tile(const WDesc& w, const void* packed, const void* scales
   a.xs = 0;
   a.rc = align16((uint32_t)w.kb * 24u * (xbf16 ? 2u : 4u));
   a.ctr = a.rc + 32u * 8u;
-  const uint32_t fixed = a.ctr + 16u + 64u;
+  a.qj = align16(a.ctr + 16u);
+  a.qk = a.qj + 8u * (uint32_t)kWRingEntries;
+  a.part = align16(a.qk + 4u * (uint32_t)kWRingEntries);
+  const uint32_t fixed = a.part + 64u;
   if (fixed >= lds) return LLVQ_EUNSUPPORTED;
-  int tmax = (int)((lds - fixed) / 16u) & ~15;
+  int tmax = (int)((lds - a.part) / 4u) & ~15;
   if (tmax > kWTTileMax) tmax = kWTTileMax;
   if (w.kb > tmax) return LLVQ_EUNSUPPORTED;
   a.tmax = tmax;
@@ -790,9 +794,6 @@ int launch_gemv_wide_tile(const WDesc& w, const void* packed, const void* scales
     grid = g;
   }
   const uint32_t T = (uint32_t)(a.rows_per_tile * w.kb);
-  a.qj = align16(a.ctr + 16u);
-  a.qk = a.qj + 8u * T;
-  a.part = align16(a.qk + 4u * T);
   const uint32_t total = a.part + 4u * T;
   if (total > lds) return LLVQ_EUNSUPPORTED;
   const uint8_t* pk = static_cast<const uint8_t*>(packed);
@@ -805,7 +806,7 @@ int launch_gemv_wide_tile(const WDesc& w, const void* packed, const void* scales
 }
 
 // Decode of the general decoder with coset queues (llvq_wide_tile.h): LDS holds the
-// reciprocals and 40 bytes per block of a tile (queue, scale, 24 value bytes).
+// reciprocals, the waves' rings and 28 bytes per block of a tile (scale, 24 value bytes).
 // LLVQ_EUNSUPPORTED when a row does not fit (the one-block-per-lane kernel then runs).
 int launch_decode_wide_tile(const WDesc& w, const void* packed, const void* scales, int32_t out_kind, void* out,
                             int32_t* err, bool ovec, hipStream_t s) {
@@ -816,8 +817,12 @@ int launch_decode_wide_tile(const WDesc& w, const void* packed, const void* scal
   WTArgs a = {};
   a.rc = 0;
   a.ctr = 32u * 8u;
-  const uint32_t fixed = a.ctr + 16u + 64u;
-  int tmax = (int)((lds - fixed) / 40u) & ~15;
+  a.qj = align16(a.ctr + 16u);
+  a.qk = a.qj + 8u * (uint32_t)kWRingEntries;
+  a.part = align16(a.qk + 4u * (uint32_t)kWRingEntries);
+  const uint32_t fixed = a.part + 64u;
+  if (fixed >= lds) return LLVQ_EUNSUPPORTED;
+  int tmax = (int)((lds - a.part - 16u) / 28u) & ~15;
   if (tmax > kWTTileMax) tmax = kWTTileMax;
   if (w.kb > tmax) return LLVQ_EUNSUPPORTED;
   a.tmax = tmax;
@@ -836,9 +841,6 @@ int launch_decode_wide_tile(const WDesc& w, const void* packed, const void* scal
     grid = g;
   }
   const uint32_t T = (uint32_t)(a.rows_per_tile * w.kb);
-  a.qj = align16(a.ctr + 16u);
-  a.qk = a.qj + 8u * T;
-  a.part = align16(a.qk + 4u * T);
   a.xs = align16(a.part + 4u * T);        // the value tile, 24 bytes per block
   const uint32_t total = a.xs + 24u * T;
   if (total > lds) return LLVQ_EUNSUPPORTED;

@@ -1,22 +1,26 @@
-// Batch-1 GEMV of the general decoder with coset queues (gfx950).  Included once by
-// llvq.hip after llvq_wide.h, whose class search and unranking state it uses.
+// Batch-1 GEMV and bulk decode of the general decoder with coset queues (gfx950).
+// Included once by llvq.hip after llvq_wide.h, whose class search and unranking state it
+// uses.
 //
-// The one-block-per-lane kernel (k_gemv_wide) lets a wavefront mix both cosets, one- and
-// two-part classes and the exact and fp64 regimes of the unranking; its single pass over
-// the 24 positions picks, per position and per lane, the support or complement unranker,
-// so every step copies both states in and out.  Here a 1024-lane workgroup (one per CU)
-// takes tiles of whole rows:
-//   1. classify: each lane takes blocks of the tile, finds the class (shell and class
-//      search as in k_gemv_wide), keeps the block's scale in its LDS slot and queues the
-//      block (J = I - class start, class, block) for the odd or the even coset;
-//   2. decode: waves take 64-entry chunks of one queue through an LDS counter.  An odd
-//      block is one multiset over all 24 positions, decoded in position order against the
-//      activations held in registers; an even block decodes its support values (on the
-//      codeword's positions, ascending) and then its complement values, each part in its
-//      own loop with its own state, reading each value's activation from LDS by position.
-//      The signs follow the same rules as wide_decode_point, in the same order;
-//   3. the block results scale their slots and the rows are summed in a fixed order.
-// The fp64 arithmetic-decoding step multiplies by 1/c from an LDS table instead of
+// The one-block-per-lane kernels (k_gemv_wide, k_decode_wide) let a wavefront mix both
+// cosets, one- and two-part classes and the exact and fp64 regimes of the unranking; their
+// single pass over the 24 positions picks, per position and per lane, the support or
+// complement unranker, so every step copies both states in and out.  Here a 1024-lane
+// workgroup (one per CU) takes tiles of whole rows and streams them as the 2-bit kernels
+// do: each wave takes units of 64 consecutive blocks from an LDS counter, classifies them
+// (shell and class search as in the one-block-per-lane kernels, latency-bound global
+// reads that the other waves' decode covers), keeps each block's scale in its LDS slot
+// and appends the block (J = I - class start, class, block) to its odd or even ring, and
+// decodes a full chunk of 64 blocks of one coset whenever a ring holds one.  The rings'
+// remainders are gathered and decoded by all waves at the end of the tile.
+//   An odd block is one multiset over all 24 positions, decoded in position order; an
+// even block decodes its support values (on the codeword's positions, ascending) and then
+// its complement values, each part in its own loop with its own state.  The signs follow
+// the same rules as wide_decode_point, in the same order.  The GEMV dots the values with
+// the activations (registers for odd blocks, LDS by position for even ones), scales the
+// block's slot and sums the rows in a fixed order; the decode writes the int8 values into
+// an LDS tile laid out like the output and then stores the tile row by row.
+//   The fp64 arithmetic-decoding step multiplies by 1/c from an LDS table instead of
 // dividing by c: one more rounding per step (four of at most 24 x 2^-53), so the bound of
 // kFpRem becomes 2 x 24 x 4 x 24 x 2^-53 x 2^38 = 0.14, every slot choice still exact.
 
@@ -26,16 +30,178 @@ constexpr int kWTThreads = 1024;
 constexpr int kWTWaves = kWTThreads / 64;
 constexpr int kWTTileMax = 16384;         // block index in 16 bits with the class index
 
+constexpr int kWRing = 128;                              // entries per ring (never more than 127)
+constexpr int kWRingEntries = 2 * kWTWaves * kWRing;     // odd and even ring of every wave
+
 struct WTArgs {
   int rows_per_tile, ntiles;
-  uint32_t xs;      // LDS: x of all kb * 24 columns, zero padded (bf16 or fp32)
+  uint32_t xs;      // LDS: GEMV: x of all kb * 24 columns, zero padded (bf16 or fp32);
+                    //      decode: the value tile, int8 [rows][kb * 24]
   uint32_t rc;      // LDS: double[32], rc[c] = 1 / c
-  uint32_t qj;      // LDS: uint64[tmax] queue: J
-  uint32_t qk;      // LDS: uint32[tmax] queue: class | block << 16
-  uint32_t part;    // LDS: float[tmax] block scale, then the block's result
-  uint32_t ctr;     // LDS: int[4]: odd fill, even fill, chunk counter
+  uint32_t qj;      // LDS: uint64[kWRingEntries]: the rings' J, then the shared leftover queue's
+  uint32_t qk;      // LDS: uint32[kWRingEntries]: class | block << 16, the same way
+  uint32_t part;    // LDS: float[tmax] block scale, then (GEMV) the block's result
+  uint32_t ctr;     // LDS: int[4]: unit counter, leftover fills, chunk counter
   int tmax;
 };
+
+// A wave's rings: odd entries at j[0 .. kWRing), even at j[kWRing .. 2 kWRing) (and k the
+// same); entry i of a ring at (head + i) mod kWRing.  Heads and counts are wave-uniform.
+struct WRings {
+  uint64_t* j;
+  uint32_t* k;
+  uint32_t oh, on, eh, en;
+};
+
+// Classify field f of the tile (f >= T: nothing) and append it to the wave's ring of its
+// coset.  The block's scale goes to part[f] (SCALE: G[g] / (4 sqrt m), or the row scale
+// with ROWSCALE), 0 for an index past the shell union, which is counted, not queued, and
+// (ZERO) gets 24 zero values in the value tile.
+template <bool SCALE, bool ROWSCALE, bool ZERO>
+__device__ __forceinline__ void wt_classify(const WDesc& d, const uint8_t* __restrict__ packed,
+                                            const __half* __restrict__ scales, uint64_t j0, int row0, int T, int f,
+                                            int lane, float* part, uint8_t* tile, int32_t* err, WRings& R) {
+  bool odd = false, even = false;
+  uint64_t J = 0;
+  uint32_t k = 0;
+  if (f < T) {
+    uint64_t lo, hi;
+    uint32_t g;
+    float sc = 0.0f;
+    if (wide_block(d, packed, j0 + (uint64_t)f, lo, hi, g)) {
+      k = (uint32_t)wide_find_class(lo, hi, d.max_shell);
+      LLVQ_DCHECK(k < (uint32_t)LLVQ_WIDE_NUM_CLASSES && dev_tables::kWideClass[k].m <= d.max_shell);
+      const LlvqWideClass& cr = dev_tables::kWideClass[k];
+      J = lo - cr.start_lo;
+      odd = cr.parity != 0;
+      even = !odd;
+      if (SCALE) {
+        if (d.mode == LLVQ_MODE_SHAPEGAIN)
+          sc = __fmul_rn(__half2float(scales[g]), dev_tables::kWideInvNorm32[cr.m]);
+        else
+          sc = ROWSCALE ? __half2float(scales[row0 + (int)(((float)f + 0.5f) / (float)d.kb)]) : 1.0f;
+      }
+    } else {
+      if (err) atomicAdd(err, 1);
+      if (ZERO) {
+        uint2* z = reinterpret_cast<uint2*>(tile + 24u * (uint32_t)f);
+        z[0] = make_uint2(0u, 0u);
+        z[1] = make_uint2(0u, 0u);
+        z[2] = make_uint2(0u, 0u);
+      }
+    }
+    part[f] = sc;
+  }
+  const uint64_t bo = __ballot(odd), be = __ballot(even);
+  const uint32_t po = __builtin_amdgcn_mbcnt_hi((uint32_t)(bo >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bo, 0u));
+  const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+  const uint32_t kf = k | ((uint32_t)f << 16);
+  if (odd) {
+    const uint32_t i = (R.oh + R.on + po) & (kWRing - 1);
+    R.j[i] = J;
+    R.k[i] = kf;
+  }
+  if (even) {
+    const uint32_t i = kWRing + ((R.eh + R.en + pe) & (kWRing - 1));
+    R.j[i] = J;
+    R.k[i] = kf;
+  }
+  R.on += (uint32_t)__popcll(bo);
+  R.en += (uint32_t)__popcll(be);
+  LLVQ_DCHECK(R.on < (uint32_t)kWRing && R.en < (uint32_t)kWRing);
+  // other lanes of the wave read these entries and slots next
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One tile streamed through the rings; odd_fn(J, kf) / even_fn(J, kf) decode one block.
+// Ends with the tile's every block decoded and the workgroup synchronised.
+template <bool SCALE, bool ROWSCALE, bool ZERO, class OddF, class EvenF>
+__device__ __forceinline__ void wt_stream_tile(uint8_t* smem, const WDesc& d, const WTArgs& a,
+                                               const uint8_t* __restrict__ packed, const __half* __restrict__ scales,
+                                               int row0, int T, float* part, uint8_t* tile, int32_t* err, int wave,
+                                               int lane, OddF odd_fn, EvenF even_fn) {
+  uint64_t* qj = reinterpret_cast<uint64_t*>(smem + a.qj);
+  uint32_t* qk = reinterpret_cast<uint32_t*>(smem + a.qk);
+  int* ctr = reinterpret_cast<int*>(smem + a.ctr);
+  const uint64_t j0 = (uint64_t)row0 * (uint64_t)d.kb;
+  const int nun = (T + 63) >> 6;
+  WRings R;
+  R.j = qj + (size_t)wave * 2 * kWRing;
+  R.k = qk + (size_t)wave * 2 * kWRing;
+  R.oh = R.on = R.eh = R.en = 0u;
+  int u = wave;
+  while (u < nun) {
+    int u2 = 0;
+    if (lane == 0) u2 = atomicAdd(&ctr[0], 1);
+    u2 = __builtin_amdgcn_readfirstlane(u2) + kWTWaves;
+    wt_classify<SCALE, ROWSCALE, ZERO>(d, packed, scales, j0, row0, T, u * 64 + lane, lane, part, tile, err, R);
+    while (R.on >= 64u) {
+      const uint32_t i = (R.oh + (uint32_t)lane) & (kWRing - 1);
+      odd_fn(R.j[i], R.k[i]);
+      R.oh = (R.oh + 64u) & (kWRing - 1);
+      R.on -= 64u;
+    }
+    while (R.en >= 64u) {
+      const uint32_t i = kWRing + ((R.eh + (uint32_t)lane) & (kWRing - 1));
+      even_fn(R.j[i], R.k[i]);
+      R.eh = (R.eh + 64u) & (kWRing - 1);
+      R.en -= 64u;
+    }
+    u = u2;
+  }
+  // the rings' remainders (< 64 each) into one shared queue: odd from the front, even from
+  // kLeftEven; then decoded by all waves as full chunks
+  constexpr int kLeftEven = kWTWaves * 64;
+  int bo = 0, be = 0;
+  if (lane == 0) {
+    bo = atomicAdd(&ctr[1], (int)R.on);
+    be = atomicAdd(&ctr[2], (int)R.en);
+  }
+  bo = __builtin_amdgcn_readfirstlane(bo);
+  be = __builtin_amdgcn_readfirstlane(be);
+  LLVQ_DCHECK(bo + (int)R.on <= kLeftEven && be + (int)R.en <= kLeftEven && R.on < 64u && R.en < 64u);
+  uint64_t lj = 0, ej = 0;
+  uint32_t lk = 0, ek = 0;
+  if ((uint32_t)lane < R.on) {
+    const uint32_t i = (R.oh + (uint32_t)lane) & (kWRing - 1);
+    lj = R.j[i];
+    lk = R.k[i];
+  }
+  if ((uint32_t)lane < R.en) {
+    const uint32_t i = kWRing + ((R.eh + (uint32_t)lane) & (kWRing - 1));
+    ej = R.j[i];
+    ek = R.k[i];
+  }
+  __syncthreads();                        // every ring read; the queue may overwrite them
+  if ((uint32_t)lane < R.on) {
+    qj[bo + lane] = lj;
+    qk[bo + lane] = lk;
+  }
+  if ((uint32_t)lane < R.en) {
+    qj[kLeftEven + be + lane] = ej;
+    qk[kLeftEven + be + lane] = ek;
+  }
+  __syncthreads();
+  const int nlo = ctr[1], nle = ctr[2];
+  const int nco = (nlo + 63) >> 6;
+  const int nch = nco + ((nle + 63) >> 6);
+  for (;;) {
+    int c = 0;
+    if (lane == 0) c = atomicAdd(&ctr[3], 1);
+    c = __builtin_amdgcn_readfirstlane(c);
+    if (c >= nch) break;
+    if (c < nco) {
+      const int e = (c << 6) + lane;
+      if (e < nlo) odd_fn(qj[e], qk[e]);
+    } else {
+      const int e = ((c - nco) << 6) + lane;
+      if (e < nle) even_fn(qj[kLeftEven + e], qk[kLeftEven + e]);
+    }
+  }
+  __syncthreads();
+}
 
 // One value of a multiset unranking in progress (fp64 arithmetic decoding below 2^kFpRem
 // arrangements left, exact 64-bit steps above): returns the value and advances U.
@@ -212,8 +378,6 @@ __global__ __launch_bounds__(kWTThreads) void k_gemv_wide_tile(WDesc d, WTArgs a
   const int kb = d.kb;
   const float inv_kb = 1.0f / (float)kb;
   double* rc = reinterpret_cast<double*>(smem + a.rc);
-  uint64_t* qj = reinterpret_cast<uint64_t*>(smem + a.qj);
-  uint32_t* qk = reinterpret_cast<uint32_t*>(smem + a.qk);
   float* part = reinterpret_cast<float*>(smem + a.part);
   int* ctr = reinterpret_cast<int*>(smem + a.ctr);
 
@@ -234,86 +398,22 @@ __global__ __launch_bounds__(kWTThreads) void k_gemv_wide_tile(WDesc d, WTArgs a
   }
   __syncthreads();
 
+  auto col_of = [&](uint32_t f) { return f - (uint32_t)(((float)f + 0.5f) * inv_kb) * (uint32_t)kb; };
+  auto odd_fn = [&](uint64_t J, uint32_t kf) {
+    const uint32_t f = kf >> 16;
+    part[f] *= wt_odd_dot<XBF16>(smem, a, rc, J, dev_tables::kWideClass[kf & 0xffffu], col_of(f));
+  };
+  auto even_fn = [&](uint64_t J, uint32_t kf) {
+    const uint32_t f = kf >> 16;
+    part[f] *= wt_even_dot<XBF16>(smem, a, rc, J, dev_tables::kWideClass[kf & 0xffffu], col_of(f));
+  };
   for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
     const int row0 = tile * a.rows_per_tile;
     const int nrows = min(a.rows_per_tile, d.rows - row0);
     const int T = nrows * kb;
-    const uint64_t j0 = (uint64_t)row0 * (uint64_t)kb;
-
-    // 1. classify (odd entries from the front of the queue, even entries from the back)
-    for (int f0 = wave * 64; f0 < T; f0 += kWTThreads) {
-      const int f = f0 + lane;
-      bool odd = false, even = false;
-      uint64_t J = 0;
-      uint32_t k = 0;
-      if (f < T) {
-        uint64_t lo, hi;
-        uint32_t g;
-        float sc = 0.0f;
-        if (wide_block(d, packed, j0 + (uint64_t)f, lo, hi, g)) {
-          k = (uint32_t)wide_find_class(lo, hi, d.max_shell);
-          LLVQ_DCHECK(k < (uint32_t)LLVQ_WIDE_NUM_CLASSES && dev_tables::kWideClass[k].m <= d.max_shell);
-          const LlvqWideClass& cr = dev_tables::kWideClass[k];
-          J = lo - cr.start_lo;
-          odd = cr.parity != 0;
-          even = !odd;
-          sc = sg ? __fmul_rn(__half2float(scales[g]), dev_tables::kWideInvNorm32[cr.m]) : 1.0f;
-        } else if (err) {
-          atomicAdd(err, 1);
-        }
-        part[f] = sc;
-      }
-      const uint64_t bo = __ballot(odd), be = __ballot(even);
-      int baseo = 0, basee = 0;
-      if (lane == 0) {
-        baseo = atomicAdd(&ctr[0], __popcll(bo));
-        basee = atomicAdd(&ctr[1], __popcll(be));
-      }
-      baseo = __builtin_amdgcn_readfirstlane(baseo);
-      basee = __builtin_amdgcn_readfirstlane(basee);
-      const uint32_t po = __builtin_amdgcn_mbcnt_hi((uint32_t)(bo >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bo, 0u));
-      const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
-      const int slot = odd ? baseo + (int)po : T - 1 - (basee + (int)pe);
-      if (odd || even) {
-        LLVQ_DCHECK(slot >= 0 && slot < T);
-        qj[slot] = J;
-        qk[slot] = k | ((uint32_t)f << 16);
-      }
-    }
-    __syncthreads();
-
-    // 2. decode chunks: odd queue, then even queue
-    const int nodd = ctr[0], neven = ctr[1];
-    const int nco = (nodd + 63) >> 6;
-    const int nch = nco + ((neven + 63) >> 6);
-    for (;;) {
-      int c = 0;
-      if (lane == 0) c = atomicAdd(&ctr[2], 1);
-      c = __builtin_amdgcn_readfirstlane(c);
-      if (c >= nch) break;
-      if (c < nco) {
-        const int e = (c << 6) + lane;
-        if (e < nodd) {
-          const uint32_t kf = qk[e];
-          const uint32_t f = kf >> 16;
-          const uint32_t b = f - (uint32_t)(((float)f + 0.5f) * inv_kb) * (uint32_t)kb;
-          const float t = wt_odd_dot<XBF16>(smem, a, rc, qj[e], dev_tables::kWideClass[kf & 0xffffu], b);
-          part[f] *= t;
-        }
-      } else {
-        const int e = ((c - nco) << 6) + lane;
-        if (e < neven) {
-          const uint32_t kf = qk[T - 1 - e];
-          const uint32_t f = kf >> 16;
-          const uint32_t b = f - (uint32_t)(((float)f + 0.5f) * inv_kb) * (uint32_t)kb;
-          const float t = wt_even_dot<XBF16>(smem, a, rc, qj[T - 1 - e], dev_tables::kWideClass[kf & 0xffffu], b);
-          part[f] *= t;
-        }
-      }
-    }
-    __syncthreads();
-
-    // 3. row sums in a fixed order
+    wt_stream_tile<true, false, false>(smem, d, a, packed, scales, row0, T, part, nullptr, err, wave, lane, odd_fn,
+                                       even_fn);
+    // row sums in a fixed order
     for (int rl = wave; rl < nrows; rl += kWTWaves) {
       float acc = 0.0f;
       for (int bb = lane; bb < kb; bb += 64) acc += part[rl * kb + bb];
@@ -435,99 +535,30 @@ __global__ __launch_bounds__(kWTThreads) void k_decode_wide_tile(WDesc d, WTArgs
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const bool sg = d.mode == LLVQ_MODE_SHAPEGAIN;
   const int kb = d.kb;
   const uint32_t rowbytes = (uint32_t)kb * 24u;
   double* rc = reinterpret_cast<double*>(smem + a.rc);
-  uint64_t* qj = reinterpret_cast<uint64_t*>(smem + a.qj);
-  uint32_t* qk = reinterpret_cast<uint32_t*>(smem + a.qk);
   float* part = reinterpret_cast<float*>(smem + a.part);
   int* ctr = reinterpret_cast<int*>(smem + a.ctr);
-  uint8_t* tile = smem + a.xs;            // the value tile takes the place of x
+  uint8_t* tile = smem + a.xs;
   if (tid < 32) rc[tid] = tid ? 1.0 / (double)tid : 0.0;
   if (tid < 4) ctr[tid] = 0;
   __syncthreads();
 
+  auto odd_fn = [&](uint64_t J, uint32_t kf) {
+    wt_odd_vals(tile + 24u * (kf >> 16), rc, J, dev_tables::kWideClass[kf & 0xffffu]);
+  };
+  auto even_fn = [&](uint64_t J, uint32_t kf) {
+    wt_even_vals(tile + 24u * (kf >> 16), rc, J, dev_tables::kWideClass[kf & 0xffffu]);
+  };
   for (int tl = blockIdx.x; tl < a.ntiles; tl += gridDim.x) {
     const int row0 = tl * a.rows_per_tile;
     const int nrows = min(a.rows_per_tile, d.rows - row0);
     const int T = nrows * kb;
-    const uint64_t j0 = (uint64_t)row0 * (uint64_t)kb;
+    wt_stream_tile<OUT == LLVQ_OUT_BF16, true, true>(smem, d, a, packed, scales, row0, T, part, tile, err, wave, lane,
+                                                     odd_fn, even_fn);
 
-    // 1. classify (as the GEMV; an index past the shell union writes zeros into the tile)
-    for (int f0 = wave * 64; f0 < T; f0 += kWTThreads) {
-      const int f = f0 + lane;
-      bool odd = false, even = false;
-      uint64_t J = 0;
-      uint32_t k = 0;
-      if (f < T) {
-        uint64_t lo, hi;
-        uint32_t g;
-        float sc = 0.0f;
-        if (wide_block(d, packed, j0 + (uint64_t)f, lo, hi, g)) {
-          k = (uint32_t)wide_find_class(lo, hi, d.max_shell);
-          LLVQ_DCHECK(k < (uint32_t)LLVQ_WIDE_NUM_CLASSES && dev_tables::kWideClass[k].m <= d.max_shell);
-          const LlvqWideClass& cr = dev_tables::kWideClass[k];
-          J = lo - cr.start_lo;
-          odd = cr.parity != 0;
-          even = !odd;
-          if (OUT == LLVQ_OUT_BF16)
-            sc = sg ? __fmul_rn(__half2float(scales[g]), dev_tables::kWideInvNorm32[cr.m])
-                    : __half2float(scales[row0 + (int)(((float)f + 0.5f) / (float)kb)]);
-        } else {
-          if (err) atomicAdd(err, 1);
-          uint2* z = reinterpret_cast<uint2*>(tile + 24u * (uint32_t)f);
-          z[0] = make_uint2(0u, 0u);
-          z[1] = make_uint2(0u, 0u);
-          z[2] = make_uint2(0u, 0u);
-        }
-        part[f] = sc;
-      }
-      const uint64_t bo = __ballot(odd), be = __ballot(even);
-      int baseo = 0, basee = 0;
-      if (lane == 0) {
-        baseo = atomicAdd(&ctr[0], __popcll(bo));
-        basee = atomicAdd(&ctr[1], __popcll(be));
-      }
-      baseo = __builtin_amdgcn_readfirstlane(baseo);
-      basee = __builtin_amdgcn_readfirstlane(basee);
-      const uint32_t po = __builtin_amdgcn_mbcnt_hi((uint32_t)(bo >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bo, 0u));
-      const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
-      const int slot = odd ? baseo + (int)po : T - 1 - (basee + (int)pe);
-      if (odd || even) {
-        LLVQ_DCHECK(slot >= 0 && slot < T);
-        qj[slot] = J;
-        qk[slot] = k | ((uint32_t)f << 16);
-      }
-    }
-    __syncthreads();
-
-    // 2. decode chunks into the tile: odd queue, then even queue
-    const int nodd = ctr[0], neven = ctr[1];
-    const int nco = (nodd + 63) >> 6;
-    const int nch = nco + ((neven + 63) >> 6);
-    for (;;) {
-      int c = 0;
-      if (lane == 0) c = atomicAdd(&ctr[2], 1);
-      c = __builtin_amdgcn_readfirstlane(c);
-      if (c >= nch) break;
-      if (c < nco) {
-        const int e = (c << 6) + lane;
-        if (e < nodd) {
-          const uint32_t kf = qk[e];
-          wt_odd_vals(tile + 24u * (kf >> 16), rc, qj[e], dev_tables::kWideClass[kf & 0xffffu]);
-        }
-      } else {
-        const int e = ((c - nco) << 6) + lane;
-        if (e < neven) {
-          const uint32_t kf = qk[T - 1 - e];
-          wt_even_vals(tile + 24u * (kf >> 16), rc, qj[T - 1 - e], dev_tables::kWideClass[kf & 0xffffu]);
-        }
-      }
-    }
-    __syncthreads();
-
-    // 3. store the tile row by row, 8 columns per lane
+    // store the tile row by row, 8 columns per lane
     if (OUT == LLVQ_OUT_POINTS_I8) {
       const uint32_t n8 = rowbytes >> 3;
       for (int rl = 0; rl < nrows; ++rl) {
