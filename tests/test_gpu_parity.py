@@ -348,6 +348,14 @@ def test_gemv_batch1_large_single_tile():
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
+@pytest.mark.parametrize("rows,cols,xd", [(40, 24 * 850, "f32"), (9, 24 * 1600 + 5, "bf16")])
+def test_gemv_batch1_rows_too_long_for_the_seven_value_tail(rows, cols, xd):
+    # rows whose activations leave no LDS for the 7-value tail table (fp32 Kb = 850, bf16
+    # Kb = 1601) run the batch-1 kernel with the 6-value tail
+    t = synth.make_tensor("tail6", 19, rows + cols, rows, cols, C10, x_dtype=xd)
+    check_gemv(t, list(range(rows)), f"tail-6 {rows}x{cols} x={xd}")
+
+
 def _fidelity(which):
     path = os.path.join(HERE, "golden", f"fidelity_c3_{which}.npz")
     if not os.path.exists(path):

@@ -65,3 +65,42 @@ def test_wide_class_table_equal(gen):
         assert int(wide["shell_start"][m]) == counts[m - 1]
         first = wide["shell_first"][m]
         assert first == len(ours) or (ours[first].m == m and (first == 0 or ours[first - 1].m == m - 1))
+
+
+def _inc_array(text, name):
+    """Initialiser of array `name` in the generated include: a list of the numbers, or of
+    brace groups of numbers."""
+    import re
+    start = text.index(name + "[")
+    body = text[text.index("{", start) + 1:text.index("};", start)]
+    if "{" in body:
+        return [[float(v.strip().rstrip("fu")) for v in g.split(",") if v.strip()]
+                for g in re.findall(r"\{([^}]*)\}", body)]
+    return [int(v.rstrip("u")) for v in body.replace("\n", "").split(",") if v.strip()]
+
+
+@pytest.mark.parametrize("n", [6, 7])
+def test_tail_tables_are_the_sorted_arrangements(gen, n):
+    # the table of the last n value slots: every composition's group holds its distinct
+    # arrangements in lexicographic order (brute force over itertools), and the record
+    # holds Q / n and the group's offset
+    import itertools
+    with open(build_lib.TABLES_INC) as f:
+        text = f.read()
+    tail = _inc_array(text, "kTail%d" % n)
+    comp = _inc_array(text, "kTailComp%d" % n)
+    b = n + 1
+    assert len(tail) == 4 ** n and len(comp) == b ** 3
+    seen = 0
+    for c0 in range(n + 1):
+        for c1 in range(n + 1 - c0):
+            for c2 in range(n + 1 - c0 - c1):
+                c3 = n - c0 - c1 - c2
+                seq = [0] * c0 + [1] * c1 + [2] * c2 + [3] * c3
+                arr = sorted(set(itertools.permutations(seq)))
+                q_over_n, off = comp[c0 + b * c1 + b * b * c2]
+                assert q_over_n == pytest.approx(len(arr) / n, rel=1e-7)
+                got = tail[int(off):int(off) + len(arr)]
+                assert got == [sum(s << (2 * i) for i, s in enumerate(a)) for a in arr]
+                seen += len(arr)
+    assert seen == 4 ** n

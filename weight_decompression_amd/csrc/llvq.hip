@@ -554,10 +554,11 @@ int pick_rows_per_tile(int rows, int kb, int tmax, int gmax, int* ntiles_out, in
   return best_r;
 }
 
-// Batch-1 fused GEMV (llvq_gemv_b1.h).  Returns LLVQ_EUNSUPPORTED when the shape does
-// not fit its tiling (the generic kernel then runs).
-int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype,
-                   float* y, int32_t* err, hipStream_t s) {
+// Batch-1 fused GEMV (llvq_gemv_b1.h) with a TAIL-value tail table.  Returns
+// LLVQ_EUNSUPPORTED when the shape does not fit its tiling.
+template <int TAIL>
+int launch_gemv_b1_tail(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype,
+                        float* y, int32_t* err, hipStream_t s) {
   const DevLimits lim = device_limits(s);
   const uint32_t lds = lim.lds;
   const int gmax = lim.grid;
@@ -567,7 +568,7 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
   // LDS: fixed tables, the waves' rings, 4 bytes per block of the tile (its slot), x
   ELayout L;
   const uint32_t xbytes = align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u));
-  const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 1);
+  const uint32_t base = engine_layout_base(L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 1, TAIL);
   const uint32_t fixed = base + (uint32_t)kRingBytes + xbytes + 16u;
   if (fixed + 4u * (uint32_t)k.kb > lds) return LLVQ_EUNSUPPORTED;
   int tmax = (int)((lds - fixed) / 4u);
@@ -589,19 +590,29 @@ int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const
     grid = g;
   }
   a.nbuckets = nbuckets;
-  engine_layout_base(a.L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 1);
+  engine_layout_base(a.L, k.ncls, 1 << k.gain_bits, nbuckets, 0, 1, TAIL);
   a.rings = align16(a.L.total);
   a.L.buf[0].part = a.rings + (uint32_t)kRingBytes;
   a.xs = align16(a.L.buf[0].part + 4u * (uint32_t)(a.rows_per_tile * k.kb));
   const uint32_t total = a.xs + align16((uint32_t)k.kb * 24u * (xf32 ? 4u : 2u));
   if (total > lds) return LLVQ_EUNSUPPORTED;
   if (xf32)
-    hipLaunchKernelGGL((k_gemv_b1<true>), dim3(grid), dim3(kEThreads), total, s, k, a,
+    hipLaunchKernelGGL((k_gemv_b1<true, TAIL>), dim3(grid), dim3(kEThreads), total, s, k, a,
                        static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, y, err);
   else
-    hipLaunchKernelGGL((k_gemv_b1<false>), dim3(grid), dim3(kEThreads), total, s, k, a,
+    hipLaunchKernelGGL((k_gemv_b1<false, TAIL>), dim3(grid), dim3(kEThreads), total, s, k, a,
                        static_cast<const uint8_t*>(packed), static_cast<const __half*>(scales), x, y, err);
   return launch_status();
+}
+
+// Batch-1 fused GEMV: the 7-value tail (one arithmetic-decoding step less per block) when
+// its 25 KB of extra tables fit beside the activations, else the 6-value tail.
+// LLVQ_EUNSUPPORTED when neither fits (the generic kernel then runs).
+int launch_gemv_b1(const KDesc& k, const void* packed, const void* scales, const void* x, int32_t x_dtype,
+                   float* y, int32_t* err, hipStream_t s) {
+  const int st = launch_gemv_b1_tail<7>(k, packed, scales, x, x_dtype, y, err, s);
+  if (st != LLVQ_EUNSUPPORTED) return st;
+  return launch_gemv_b1_tail<6>(k, packed, scales, x, x_dtype, y, err, s);
 }
 
 // Streamed decode of one or several tensors (llvq_stream.h): LDS holds the tables (with

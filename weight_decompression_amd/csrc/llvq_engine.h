@@ -22,9 +22,10 @@
 // byte offset of its table entry), so the step computes (8 y - 8 C_k) * (n' / 8 c_k),
 // which rounds exactly like the unscaled form.  The decision margins (>= n/(2Q),
 // Q <= 4.2e8 arrangements) exceed the accumulated rounding error by a factor > 1e5.  The last 6
-// values come from a table of all 4^6 slot sequences grouped by composition in
-// lexicographic order: with counts c (sum 6) and y in [0, 6), the rank inside the
-// group is floor(y * Q(c) / 6).
+// values (TAIL = 6, or 7 for the batch-1 GEMV, which has the LDS to spare) come from a
+// table of all 4^TAIL slot sequences grouped by composition in lexicographic order: with
+// counts c (sum TAIL) and y in [0, TAIL), the rank inside the group is
+// floor(y * Q(c) / TAIL).
 
 #pragma once
 
@@ -33,8 +34,18 @@ constexpr int kEWaves = kEThreads / 64;
 constexpr int kETileMax = 16384;    // block index inside a tile fits 14 bits
 constexpr int kEUnit = 256;         // fields per classify unit (4 per lane)
 constexpr int kBias = 12;           // value tables store 12 +- v (|v| <= 12)
-constexpr int kTail = 6;            // values resolved by the tail table
-constexpr int kSteps = 24 - kTail;  // values resolved step by step
+// Tail of TAIL values resolved by one table lookup (6 or 7; 7 is the most the even-coset
+// decoder allows: its part switch at value 16 must be a step).  steps: values resolved
+// step by step; wdot: udot4 weights of the composition index c0 + (TAIL+1) c1 +
+// (TAIL+1)^2 c2; ncomp / nseq: entries of the composition and sequence tables.
+template <int TAIL>
+struct TailSpec {
+  static_assert(TAIL == 6 || TAIL == 7, "tail of 6 or 7 values");
+  static constexpr int steps = 24 - TAIL;
+  static constexpr uint32_t wdot = (uint32_t)(1 | ((TAIL + 1) << 8) | ((TAIL + 1) * (TAIL + 1) << 16));
+  static constexpr int ncomp = (TAIL + 1) * (TAIL + 1) * (TAIL + 1);
+  static constexpr int nseq = 1 << (2 * TAIL);
+};
 constexpr int kFStride = 25;        // F row length (c = 0..24)
 constexpr uint32_t kInvalidClass = 0xffu;   // queue entry class of a block to be written as zeros
 constexpr uint32_t kFRow = kFStride * 8u;   // F row in bytes
@@ -52,8 +63,8 @@ struct ELayout {
   uint32_t cls;       // LlvqClassHot[ncls + 2]: the last two are sentinels (start only, +inf)
   uint32_t gains;     // float[2^gain_bits]
   uint32_t bucket;    // uint8[nbuckets]
-  uint32_t tail;      // uint16[4096]
-  uint32_t tcomp;     // LlvqTailComp[343]
+  uint32_t tail;      // uint16[4^TAIL]
+  uint32_t tcomp;     // LlvqTailComp[(TAIL+1)^3]
   uint32_t work;      // int[4]: work-item counter of the current phase
   TileBuf buf[2];     // one or two tile buffers
   uint32_t total;     // end of the engine's part; consumer data follows
@@ -63,15 +74,15 @@ struct ELayout {
 __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
 
 __host__ __device__ inline uint32_t engine_layout_base(ELayout& L, int ncls, int ngains, int nbuckets, int tmax,
-                                                      int nbuf = 1) {
+                                                      int nbuf = 1, int tail = 6) {
   uint32_t o = 0;
   L.ftab = o;     o = align16(o + 626u * 8u);
   L.golay = 0u;
   L.cls = o;      o = align16(o + (uint32_t)(ncls + 2) * (uint32_t)sizeof(LlvqClassHot));
   L.gains = o;    o = align16(o + (uint32_t)ngains * 4u);
   L.bucket = o;   o = align16(o + (uint32_t)nbuckets);
-  L.tail = o;     o = align16(o + 4096u * 2u);
-  L.tcomp = o;    o = align16(o + 343u * (uint32_t)sizeof(LlvqTailComp));
+  L.tail = o;     o = align16(o + (2u << (2 * tail)));
+  L.tcomp = o;    o = align16(o + (uint32_t)((tail + 1) * (tail + 1) * (tail + 1)) * (uint32_t)sizeof(LlvqTailComp));
   L.work = o;     o = align16(o + 16u);
   for (int b = 0; b < 2; ++b) {
     if (b < nbuf) {
@@ -192,14 +203,16 @@ __device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELa
   return bs;
 }
 
-// Slot codes of the last 6 values (2 bits each, first of the six in the low bits), from
-// the counts left (times 8, sum 48) and y in [0, 6).
+// Slot codes of the last TAIL values (2 bits each, first of them in the low bits), from
+// the counts left (times 8, sum 8 TAIL) and y in [0, TAIL).
+template <int TAIL>
 __device__ __forceinline__ uint32_t tail_codes(const uint8_t* smem, const ELayout& L, uint32_t cnt8, double y) {
-  const uint32_t ci8 = __builtin_amdgcn_udot4(cnt8, 0x00310701u, 0u, false);   // 8 (c0 + 7 c1 + 49 c2)
-  LLVQ_DCHECK(ci8 < 343u * 8u);
+  typedef TailSpec<TAIL> TS;
+  const uint32_t ci8 = __builtin_amdgcn_udot4(cnt8, TS::wdot, 0u, false);   // 8 (c0 + b c1 + b^2 c2)
+  LLVQ_DCHECK(ci8 < (uint32_t)TS::ncomp * 8u);
   const LlvqTailComp tc = *reinterpret_cast<const LlvqTailComp*>(smem + L.tcomp + ci8);
-  const uint32_t r = (uint32_t)((float)y * tc.q_over_6);
-  LLVQ_DCHECK(tc.offset + r < 4096u && (float)r < tc.q_over_6 * 6.0f);
+  const uint32_t r = (uint32_t)((float)y * tc.q_over_n);
+  LLVQ_DCHECK(tc.offset + r < (uint32_t)TS::nseq && (float)r < tc.q_over_n * (float)TAIL);
   return reinterpret_cast<const uint16_t*>(smem + L.tail)[tc.offset + r];
 }
 
@@ -229,7 +242,9 @@ __device__ __forceinline__ StepOut decode_step(const uint8_t* smem, double& y, u
 // follows from the codeword bit and the value mod 4, folded into one byte-table lookup:
 // the selector's +4 (negated entry) for positions off the codeword rides in the addend of
 // the slot popcount.
+template <int TAIL = 6>
 struct OddDec {
+  static constexpr int kSteps = TailSpec<TAIL>::steps;
   double y;
   uint32_t nc, cnt8, notc4, svlo, svhi, codes;
 
@@ -249,7 +264,7 @@ struct OddDec {
     if (p < kSteps) {
       // values left after the step: 23 - p, F row p
       k = decode_step(smem, y, nc, cnt8, sel, kFRow * (uint32_t)p).k;
-      if (p == kSteps - 1) codes = tail_codes(smem, L, cnt8, y);
+      if (p == kSteps - 1) codes = tail_codes<TAIL>(smem, L, cnt8, y);
     } else {
       k = __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | sel;
     }
@@ -268,7 +283,7 @@ struct OddDec {
     const uint32_t sel = ((notc4 >> p) & 4u) | 0x0c0c0c00u;
     if (p < kSteps) {
       const uint32_t k = decode_step(smem, y, nc, cnt8, sel, kFRow * (uint32_t)p).k;
-      if (p == kSteps - 1) codes = tail_codes(smem, L, cnt8, y);
+      if (p == kSteps - 1) codes = tail_codes<TAIL>(smem, L, cnt8, y);
       return k;
     }
     return __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | sel;
@@ -282,7 +297,9 @@ struct OddDec {
 // parity of negatives on the support, and init inserts it into s at bit w - 1 (the
 // support values are all nonzero, so they take bits 0..w-1).  Zero can only be a part's
 // slot 0, so a value takes a sign bit unless its slot is 0 and the part's slot 0 is zero.
+template <int TAIL = 6>
 struct EvenDec {
+  static constexpr int kSteps = TailSpec<TAIL>::steps;
   double y;
   uint32_t nc, cnt8, svlo, svhi, nz0, nz1, m, s, codes, c, hp, fo, swi;
 
@@ -333,7 +350,7 @@ struct EvenDec {
       kb = so.k;
       free_ = med3_1(so.g, nz0);
       if (i == 6 || i == 10 || i == 14) fo = swi == (uint32_t)(i + 2) ? 0u : fo;
-      if (i == kSteps - 1) codes = tail_codes(smem, L, cnt8, y);
+      if (i == kSteps - 1) codes = tail_codes<TAIL>(smem, L, cnt8, y);
     } else {
       const uint32_t code = __builtin_amdgcn_ubfe(codes, 2 * (i - kSteps), 2);
       kb = code | 0x0c0c0c00u;
@@ -375,7 +392,7 @@ struct EvenDec {
       kb = so.k;
       free_ = med3_1(so.g, nz0);
       if (i == 6 || i == 10 || i == 14) fo = swi == (uint32_t)(i + 2) ? 0u : fo;
-      if (i == kSteps - 1) codes = tail_codes(smem, L, cnt8, y);
+      if (i == kSteps - 1) codes = tail_codes<TAIL>(smem, L, cnt8, y);
     } else {
       const uint32_t code = __builtin_amdgcn_ubfe(codes, 2 * (i - kSteps), 2);
       kb = code | 0x0c0c0c00u;
@@ -434,15 +451,19 @@ __device__ __forceinline__ void copy_word_tail(uint8_t* smem, uint32_t dst, cons
 // segment (a consumer's activations).  All of a lane's global loads are issued before its
 // first LDS store, so the workgroup waits for about one memory latency rather than one
 // per copy.  The caller synchronises afterwards.
+template <int TAIL = 6>
 __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L, const KDesc& d, int nbuckets,
                                                 const __half* __restrict__ scales, int tid,
                                                 CopySeg extra = {nullptr, 0u, 0}) {
+  typedef TailSpec<TAIL> TS;
+  const uint16_t* tail_src = TAIL == 6 ? dev_tables::kTail6 : dev_tables::kTail7;
+  const LlvqTailComp* tcomp_src = TAIL == 6 ? dev_tables::kTailComp6 : dev_tables::kTailComp7;
   const int cls_w = d.ncls * (int)(sizeof(LlvqClassHot) / 4);
   const int bk_w = (nbuckets + 3) >> 2;
   const uint8_t* bk_src = dev_tables::kBucketTable[d.max_shell];
   const CopySeg s_cls = {reinterpret_cast<const uint4*>(dev_tables::kClassHot), L.cls, cls_w >> 2};
-  const CopySeg s_tail = {reinterpret_cast<const uint4*>(dev_tables::kTail6), L.tail, 4096 * 2 / 16};
-  const CopySeg s_tcomp = {reinterpret_cast<const uint4*>(dev_tables::kTailComp), L.tcomp, (343 * 2) >> 2};
+  const CopySeg s_tail = {reinterpret_cast<const uint4*>(tail_src), L.tail, TS::nseq * 2 / 16};
+  const CopySeg s_tcomp = {reinterpret_cast<const uint4*>(tcomp_src), L.tcomp, (TS::ncomp * 2) >> 2};
   const CopySeg s_bk = {reinterpret_cast<const uint4*>(bk_src), L.bucket, bk_w >> 2};
   const CopySeg s_f = {reinterpret_cast<const uint4*>(dev_tables::kFTable), L.ftab, 626 * 8 / 16};
   const CopySeg s_g = {reinterpret_cast<const uint4*>(dev_tables::kGolayTable), L.golay, L.golay ? 4096 * 4 / 16 : 0};
@@ -466,7 +487,7 @@ __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L,
   copy_finish(smem, v_x, extra, tid);
   copy_word_tail(smem, L.cls, dev_tables::kClassHot, cls_w, tid);
   if (tid < 2) reinterpret_cast<LlvqClassHot*>(smem + L.cls)[d.ncls + tid].start = __builtin_inf();
-  copy_word_tail(smem, L.tcomp, dev_tables::kTailComp, 343 * 2, tid);
+  copy_word_tail(smem, L.tcomp, tcomp_src, TS::ncomp * 2, tid);
   copy_word_tail(smem, L.bucket, bk_src, bk_w, tid);
 }
 

@@ -53,7 +53,7 @@ __device__ __forceinline__ uint32_t block_col(uint32_t f, float inv_kb, uint32_t
 
 // Decode one odd-coset block (queue entry e) and multiply its slot by the dot product.
 // The block's activations are read as 16-byte words (bf16 pairs, or fp32 values).
-template <bool XF32>
+template <bool XF32, int TAIL>
 __device__ __forceinline__ void gemv_odd(uint8_t* smem, const EArgs& a, float* part, uint64_t e, uint32_t kb,
                                          float inv_kb) {
   const ELayout& L = a.L;
@@ -79,7 +79,7 @@ __device__ __forceinline__ void gemv_odd(uint8_t* smem, const EArgs& a, float* p
       xw[4 * q] = v.x; xw[4 * q + 1] = v.y; xw[4 * q + 2] = v.z; xw[4 * q + 3] = v.w;
     }
   }
-  OddDec od;
+  OddDec<TAIL> od;
   od.init(hO, so);
   od.load_fp8(hO);
   float a0 = 0.0f, a1 = 0.0f;
@@ -98,7 +98,7 @@ __device__ __forceinline__ void gemv_odd(uint8_t* smem, const EArgs& a, float* p
 
 // The same for an even-coset block; its values come in decode order, so each one's
 // activation is read from LDS by position.
-template <bool XF32>
+template <bool XF32, int TAIL>
 __device__ __forceinline__ void gemv_even(uint8_t* smem, const EArgs& a, float* part, uint64_t e, uint32_t kb,
                                           float inv_kb) {
   const ELayout& L = a.L;
@@ -107,7 +107,7 @@ __device__ __forceinline__ void gemv_even(uint8_t* smem, const EArgs& a, float* 
   const uint32_t be = block_col(fe, inv_kb, kb);
   const LlvqClassHot hE = cls[entry_k(e)];
   const BlockStart se = block_start(smem, L, entry_J(e), hE);
-  EvenDec ev;
+  EvenDec<TAIL> ev;
   ev.init(hE, se, L.cls + entry_k(e) * (uint32_t)sizeof(LlvqClassHot));
   ev.load_fp8(hE);
   const uint32_t col0 = be * 24u;
@@ -218,7 +218,7 @@ __device__ __forceinline__ bool classify_lane(uint8_t* smem, const ELayout& L, f
   return f < T && !valid;
 }
 
-template <bool XF32>
+template <bool XF32, int TAIL>
 __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const uint8_t* __restrict__ packed,
                                                         const __half* __restrict__ scales, const void* __restrict__ xv,
                                                         float* __restrict__ y, int32_t* err) {
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
   // copies; the rest (and the zero padding to Kb * 24 columns) follows
   const bool xa16 = !XF32 && ((((uintptr_t)xv) & 15u) == 0u);
   const int xw = xa16 ? (d.cols >> 3) : 0;
-  engine_prologue(smem, L, d, a.nbuckets, scales, tid, CopySeg{reinterpret_cast<const uint4*>(xv), a.xs, xw});
+  engine_prologue<TAIL>(smem, L, d, a.nbuckets, scales, tid, CopySeg{reinterpret_cast<const uint4*>(xv), a.xs, xw});
   {
     const int ncol = kb * 24;
     if (xa16) {
@@ -293,12 +293,12 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
       const LaneField lf2 = load_lane_field(d, packed, j0, T, min(u2, nun - 1), lane);
       classify_lane(smem, L, part, d, lf, T, u, lane, err, R);
       while (R.on >= 64u) {
-        gemv_odd<XF32>(smem, a, part, R.odd[(R.oh + (uint32_t)lane) & (kRing - 1)], (uint32_t)kb, inv_kb);
+        gemv_odd<XF32, TAIL>(smem, a, part, R.odd[(R.oh + (uint32_t)lane) & (kRing - 1)], (uint32_t)kb, inv_kb);
         R.oh = (R.oh + 64u) & (kRing - 1);
         R.on -= 64u;
       }
       while (R.en >= 64u) {
-        gemv_even<XF32>(smem, a, part, R.even[(R.eh + (uint32_t)lane) & (kRing - 1)], (uint32_t)kb, inv_kb);
+        gemv_even<XF32, TAIL>(smem, a, part, R.even[(R.eh + (uint32_t)lane) & (kRing - 1)], (uint32_t)kb, inv_kb);
         R.eh = (R.eh + 64u) & (kRing - 1);
         R.en -= 64u;
       }
@@ -333,10 +333,10 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
       if (c >= nch) break;
       if (c < nco) {
         const int e = (c << 6) + lane;
-        if (e < nlo) gemv_odd<XF32>(smem, a, part, shq[e], (uint32_t)kb, inv_kb);
+        if (e < nlo) gemv_odd<XF32, TAIL>(smem, a, part, shq[e], (uint32_t)kb, inv_kb);
       } else {
         const int e = ((c - nco) << 6) + lane;
-        if (e < nle) gemv_even<XF32>(smem, a, part, shq[kLeftEven + e], (uint32_t)kb, inv_kb);
+        if (e < nle) gemv_even<XF32, TAIL>(smem, a, part, shq[kLeftEven + e], (uint32_t)kb, inv_kb);
       }
     }
     __syncthreads();

@@ -198,7 +198,7 @@ __device__ __forceinline__ uint32_t stream_odd_codes(uint8_t* smem, const ELayou
   const uint32_t f = entry_f(e);
   const LlvqClassHot h = cls[entry_k(e)];
   const BlockStart bs = block_start<true>(smem, L, entry_J(e), h);
-  OddDec od;
+  OddDec<> od;
   od.init(h, bs);
   uint32_t w[6];
   if (OUT == LLVQ_OUT_POINTS_I8) {
@@ -238,7 +238,7 @@ __device__ __forceinline__ uint32_t stream_even_codes(uint8_t* smem, const ELayo
   const uint32_t f = entry_f(e);
   const LlvqClassHot h = cls[entry_k(e)];
   const BlockStart bs = block_start<true>(smem, L, entry_J(e), h);
-  EvenDec ev;
+  EvenDec<> ev;
   ev.init(h, bs, L.cls + entry_k(e) * (uint32_t)sizeof(LlvqClassHot));
   if (OUT == LLVQ_OUT_POINTS_I8) {
 #pragma unroll

@@ -55,9 +55,9 @@ struct LlvqClassHot {
   uint32_t sv0lo8, sv0hi8, sv1lo8, sv1hi8;   // fp8 tables of parts 0 and 1 (byte offset 80)
 };
 
-// Composition record of the 6-position tail table (see gen_tables.cpp).
+// Composition record of a tail table of the last n = 6 or 7 positions (see gen_tables.cpp).
 struct LlvqTailComp {
-  float q_over_6;    // arrangements of the composition / 6
+  float q_over_n;    // arrangements of the composition / n (n = 6 or 7 tail positions)
   uint32_t offset;   // first entry of the composition's group in the tail table
 };
 

@@ -19,7 +19,7 @@ __device__ __forceinline__ void bytes_chunk(uint8_t* smem, const ELayout& L, con
     const uint32_t f = entry_f(eo);
     const LlvqClassHot h = cls[entry_k(eo)];
     const BlockStart bs = block_start(smem, L, entry_J(eo), h);
-    OddDec od;
+    OddDec<> od;
     od.init(h, bs);
     uint2* dst = reinterpret_cast<uint2*>(smem + tb + 24u * f);
     uint32_t w0 = 0u, w1 = 0u;
@@ -48,7 +48,7 @@ __device__ __forceinline__ void bytes_chunk(uint8_t* smem, const ELayout& L, con
     }
     const LlvqClassHot h = cls[entry_k(ee)];
     const BlockStart bs = block_start(smem, L, entry_J(ee), h);
-    EvenDec ev;
+    EvenDec<> ev;
     ev.init(h, bs, L.cls + entry_k(ee) * (uint32_t)sizeof(LlvqClassHot));
     uint8_t* dst = smem + tb + 24u * f;
 #pragma unroll

@@ -399,11 +399,11 @@ __global__ __launch_bounds__(kWTThreads) void k_gemv_wide_tile(WDesc d, WTArgs a
   __syncthreads();
 
   auto col_of = [&](uint32_t f) { return f - (uint32_t)(((float)f + 0.5f) * inv_kb) * (uint32_t)kb; };
-  auto odd_fn = [&](uint64_t J, uint32_t kf) {
+  auto odd_fn = [&](uint64_t J, uint32_t kf) __attribute__((always_inline)) {
     const uint32_t f = kf >> 16;
     part[f] *= wt_odd_dot<XBF16>(smem, a, rc, J, dev_tables::kWideClass[kf & 0xffffu], col_of(f));
   };
-  auto even_fn = [&](uint64_t J, uint32_t kf) {
+  auto even_fn = [&](uint64_t J, uint32_t kf) __attribute__((always_inline)) {
     const uint32_t f = kf >> 16;
     part[f] *= wt_even_dot<XBF16>(smem, a, rc, J, dev_tables::kWideClass[kf & 0xffffu], col_of(f));
   };
@@ -545,10 +545,10 @@ __global__ __launch_bounds__(kWTThreads) void k_decode_wide_tile(WDesc d, WTArgs
   if (tid < 4) ctr[tid] = 0;
   __syncthreads();
 
-  auto odd_fn = [&](uint64_t J, uint32_t kf) {
+  auto odd_fn = [&](uint64_t J, uint32_t kf) __attribute__((always_inline)) {
     wt_odd_vals(tile + 24u * (kf >> 16), rc, J, dev_tables::kWideClass[kf & 0xffffu]);
   };
-  auto even_fn = [&](uint64_t J, uint32_t kf) {
+  auto even_fn = [&](uint64_t J, uint32_t kf) __attribute__((always_inline)) {
     wt_even_vals(tile + 24u * (kf >> 16), rc, J, dev_tables::kWideClass[kf & 0xffffu]);
   };
   for (int tl = blockIdx.x; tl < a.ntiles; tl += gridDim.x) {
