@@ -46,7 +46,7 @@ struct TailSpec {
   static constexpr int ncomp = (TAIL + 1) * (TAIL + 1) * (TAIL + 1);
   static constexpr int nseq = 1 << (2 * TAIL);
 };
-constexpr int kFStride = 25;        // F row length (c = 0..24)
+constexpr int kFStride = 32;        // F row length (c = 0..24, padded to 256 bytes)
 constexpr uint32_t kInvalidClass = 0xffu;   // queue entry class of a block to be written as zeros
 constexpr uint32_t kFRow = kFStride * 8u;   // F row in bytes
 
@@ -59,7 +59,7 @@ struct TileBuf {
 
 struct ELayout {
   // byte offsets inside the dynamic LDS segment
-  uint32_t ftab;      // double F[25][25] (+1 pad): F[r][c] = (23 - r) / (8 c), always at offset 0
+  uint32_t ftab;      // double F[25][32]: F[r][c] = (23 - r) / (8 c) (c = 1..24), always at offset 0
   uint32_t cls;       // LlvqClassHot[ncls + 2]: the last two are sentinels (start only, +inf)
   uint32_t gains;     // float[2^gain_bits]
   uint32_t bucket;    // uint8[nbuckets]
@@ -76,7 +76,7 @@ __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15
 __host__ __device__ inline uint32_t engine_layout_base(ELayout& L, int ncls, int ngains, int nbuckets, int tmax,
                                                       int nbuf = 1, int tail = 6) {
   uint32_t o = 0;
-  L.ftab = o;     o = align16(o + 626u * 8u);
+  L.ftab = o;     o = align16(o + 800u * 8u);
   L.golay = 0u;
   L.cls = o;      o = align16(o + (uint32_t)(ncls + 2) * (uint32_t)sizeof(LlvqClassHot));
   L.gains = o;    o = align16(o + (uint32_t)ngains * 4u);
@@ -217,19 +217,23 @@ __device__ __forceinline__ uint32_t tail_codes(const uint8_t* smem, const ELayou
 }
 
 // One arithmetic-decoding step on (y, nc, cnt8) with F row offset fo (bytes): returns the
-// SWAR flags g of the chosen slot; k = popcount(g) + sel is the caller's selector.
+// SWAR flags g of the chosen slot; k = popcount(g) + sel is the caller's selector.  The
+// table entry's offset is v_perm(hi, cnt8, k): byte 0 is the count byte 8 c_k (selector
+// byte 0 picks a byte of cnt8, or of hi = cnt8 when the +4 rides there); a selector byte 1
+// of 4 adds byte 0 of hi as bits 8..15, a per-lane row offset in units of 256 bytes (the
+// even decoder's rows of a two-part class's support), else 0x0c makes it zero.
 struct StepOut {
   uint32_t g, k;
 };
 
 __device__ __forceinline__ StepOut decode_step(const uint8_t* smem, double& y, uint32_t& nc, uint32_t& cnt8,
-                                               uint32_t sel, uint32_t fo) {
+                                               uint32_t sel, uint32_t fo, uint32_t hi) {
   const uint32_t f = (uint32_t)y;
   const uint32_t g = swar_ge(f, nc);
   const uint32_t k = bcnt_addv(g, sel);
-  const uint32_t c8 = __builtin_amdgcn_perm(cnt8, cnt8, k);        // 8 c_k (selector 0..7)
+  const uint32_t c8 = __builtin_amdgcn_perm(hi, cnt8, k);          // 8 c_k (+ row offset)
   const uint32_t C8 = __builtin_amdgcn_udot4(g, cnt8, 0u, false);  // 8 C_k
-  LLVQ_DCHECK(c8 != 0u && c8 <= 192u && fo + c8 < 25u * kFRow);    // the chosen slot has values left
+  LLVQ_DCHECK((c8 & 0xffu) != 0u && (c8 & 0xffu) <= 192u && fo + c8 < 25u * kFRow);   // the slot has values left
   const double fac = ftab_at(smem, fo + c8);                       // n' / (8 c_k)
   y = __builtin_fma(y, 8.0, -(double)C8) * fac;
   cnt8 -= dec8(g);
@@ -263,7 +267,7 @@ struct OddDec {
     uint32_t k;
     if (p < kSteps) {
       // values left after the step: 23 - p, F row p
-      k = decode_step(smem, y, nc, cnt8, sel, kFRow * (uint32_t)p).k;
+      k = decode_step(smem, y, nc, cnt8, sel, kFRow * (uint32_t)p, cnt8).k;
       if (p == kSteps - 1) codes = tail_codes<TAIL>(smem, L, cnt8, y);
     } else {
       k = __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | sel;
@@ -282,7 +286,7 @@ struct OddDec {
   __device__ __forceinline__ uint32_t slot(const uint8_t* smem, const ELayout& L, int p) {
     const uint32_t sel = ((notc4 >> p) & 4u) | 0x0c0c0c00u;
     if (p < kSteps) {
-      const uint32_t k = decode_step(smem, y, nc, cnt8, sel, kFRow * (uint32_t)p).k;
+      const uint32_t k = decode_step(smem, y, nc, cnt8, sel, kFRow * (uint32_t)p, cnt8).k;
       if (p == kSteps - 1) codes = tail_codes<TAIL>(smem, L, cnt8, y);
       return k;
     }
@@ -297,6 +301,9 @@ struct OddDec {
 // parity of negatives on the support, and init inserts it into s at bit w - 1 (the
 // support values are all nonzero, so they take bits 0..w-1).  Zero can only be a part's
 // slot 0, so a value takes a sign bit unless its slot is 0 and the part's slot 0 is zero.
+// s is kept shifted left by 2, so the next sign bit sits at the selector's +4 bit and
+// joins the selector with one and-or; a zero value that takes no bit still gets the
+// current one in its selector, harmlessly, since the negated entry of a zero is zero.
 template <int TAIL = 6>
 struct EvenDec {
   static constexpr int kSteps = TailSpec<TAIL>::steps;
@@ -315,6 +322,7 @@ struct EvenDec {
       const uint32_t negq = ((uint32_t)__builtin_popcount(lo) & 1u) ^ pi;
       s = lo | (negq << (w - 1u)) | ((s >> (w - 1u)) << w);
     }
+    s <<= 2;
     y = bs.y;
     nc = h.nc0;
     cnt8 = h.cnt0;
@@ -346,7 +354,7 @@ struct EvenDec {
     }
     uint32_t kb, free_;
     if (i < kSteps) {
-      const StepOut so = decode_step(smem, y, nc, cnt8, 0x0c0c0c00u, fo + kFRow * (uint32_t)i);
+      const StepOut so = decode_step(smem, y, nc, cnt8, 0x0c0c0c00u, fo + kFRow * (uint32_t)i, cnt8);
       kb = so.k;
       free_ = med3_1(so.g, nz0);
       if (i == 6 || i == 10 || i == 14) fo = swi == (uint32_t)(i + 2) ? 0u : fo;
@@ -356,11 +364,11 @@ struct EvenDec {
       kb = code | 0x0c0c0c00u;
       free_ = med3_1(code, nz0);
     }
-    const uint32_t neg = s & free_;
+    const uint32_t sel = kb | (s & 4u);
     s >>= free_;
     pos = (uint32_t)__builtin_ctz(m);
     m &= m - 1u;
-    return __builtin_amdgcn_perm(svhi, svlo, kb + (neg << 2));
+    return __builtin_amdgcn_perm(svhi, svlo, sel);
   }
 
   // The batch-1 GEMV's form (see OddDec::slot): fp8 tables, and the selector of the i-th
@@ -387,8 +395,9 @@ struct EvenDec {
     }
     uint32_t kb, free_;
     if (i < kSteps) {
-      // (decode_step picks the count byte with v_perm, so its selector keeps the 0x0c bytes)
-      const StepOut so = decode_step(smem, y, nc, cnt8, 0x0c0c0c00u, fo + kFRow * (uint32_t)i);
+      // the row offset fo / 256 joins the table offset through the selector's byte 1 (only
+      // byte 0 of the returned selector is used)
+      const StepOut so = decode_step(smem, y, nc, cnt8, 0x0c0c0400u, kFRow * (uint32_t)i, fo >> 8);
       kb = so.k;
       free_ = med3_1(so.g, nz0);
       if (i == 6 || i == 10 || i == 14) fo = swi == (uint32_t)(i + 2) ? 0u : fo;
@@ -398,11 +407,11 @@ struct EvenDec {
       kb = code | 0x0c0c0c00u;
       free_ = med3_1(code, nz0);
     }
-    const uint32_t neg = s & free_;
+    const uint32_t sel = kb | (s & 4u);
     s >>= free_;
     pos = (uint32_t)__builtin_ctz(m);
     m &= m - 1u;
-    return kb + (neg << 2);
+    return sel;
   }
 };
 
@@ -465,7 +474,7 @@ __device__ __forceinline__ void engine_prologue(uint8_t* smem, const ELayout& L,
   const CopySeg s_tail = {reinterpret_cast<const uint4*>(tail_src), L.tail, TS::nseq * 2 / 16};
   const CopySeg s_tcomp = {reinterpret_cast<const uint4*>(tcomp_src), L.tcomp, (TS::ncomp * 2) >> 2};
   const CopySeg s_bk = {reinterpret_cast<const uint4*>(bk_src), L.bucket, bk_w >> 2};
-  const CopySeg s_f = {reinterpret_cast<const uint4*>(dev_tables::kFTable), L.ftab, 626 * 8 / 16};
+  const CopySeg s_f = {reinterpret_cast<const uint4*>(dev_tables::kFTable), L.ftab, 800 * 8 / 16};
   const CopySeg s_g = {reinterpret_cast<const uint4*>(dev_tables::kGolayTable), L.golay, L.golay ? 4096 * 4 / 16 : 0};
   const CopyRegs v_cls = copy_issue(s_cls, tid);
   const CopyRegs v_tail = copy_issue(s_tail, tid);
