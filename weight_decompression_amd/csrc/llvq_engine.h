@@ -275,22 +275,32 @@ struct OddDec {
     return __builtin_amdgcn_perm(svhi, svlo, k);
   }
 
-  // The batch-1 GEMV's form: the fp8 value table (load_fp8) and, per position, the value's
-  // selector into it (byte 0: slot 0..3, + 4 off the codeword; bytes 1-3: 0x0c) instead of
-  // the value itself, so that two positions share one v_perm.
+  // The fp8 form: the fp8 value table (load_fp8) and, per position, the value's slot
+  // selector into it (byte 0: slot 0..3; bytes 1-3: 0x0c) instead of the value itself, so
+  // that two positions share one v_perm.  The codeword's +4 (negated entry, off the
+  // codeword) is not in it: sign_quad gives it for four positions at once, to be added to
+  // the joined selector of each pair (one add per pair rather than a shift and an and-or
+  // per position).
   __device__ __forceinline__ void load_fp8(const LlvqClassHot& h) {
     svlo = h.sv0lo8;
     svhi = h.sv0hi8;
   }
 
   __device__ __forceinline__ uint32_t slot(const uint8_t* smem, const ELayout& L, int p) {
-    const uint32_t sel = ((notc4 >> p) & 4u) | 0x0c0c0c00u;
     if (p < kSteps) {
-      const uint32_t k = decode_step(smem, y, nc, cnt8, sel, kFRow * (uint32_t)p, cnt8).k;
+      const uint32_t k = decode_step(smem, y, nc, cnt8, 0x0c0c0c00u, kFRow * (uint32_t)p, cnt8).k;
       if (p == kSteps - 1) codes = tail_codes<TAIL>(smem, L, cnt8, y);
       return k;
     }
-    return __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | sel;
+    return __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | 0x0c0c0c00u;
+  }
+
+  // The +4 of positions 4q .. 4q+3 (set off the codeword) at bits 2, 10, 18 and 26: the
+  // nibble's bit e moves to bit 8 e + 2 under one multiply (its other shifted copies land
+  // on bits the mask clears, and no two copies overlap, so nothing carries).
+  __device__ __forceinline__ uint32_t sign_quad(int q) const {
+    const uint32_t nib = __builtin_amdgcn_ubfe(notc4, 4 * q + 2, 4);
+    return __umul24(nib, 0x00810204u) & 0x04040404u;
   }
 };
 

@@ -37,6 +37,14 @@ __device__ __forceinline__ llvq_bf16x2 value_pair(uint32_t svhi, uint32_t svlo, 
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);
 }
 
+// The same with the pair's +4 (negated entries) in bytes 0 and 1 of ysign.
+__device__ __forceinline__ llvq_bf16x2 value_pair_signed(uint32_t svhi, uint32_t svlo, uint32_t ka, uint32_t kb,
+                                                         uint32_t ysign) {
+  const uint32_t sel = __builtin_amdgcn_perm(kb, ka, 0x0c0c0400u) + ysign;
+  const uint32_t codes = __builtin_amdgcn_perm(svhi, svlo, sel);
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);
+}
+
 // acc + v.x a.x + v.y a.y for bf16 activations (one v_dot2c_f32_bf16) or fp32 ones
 template <bool XF32>
 __device__ __forceinline__ float dot_pair(float acc, llvq_bf16x2 v, uint32_t xb, float x0, float x1) {
@@ -48,7 +56,7 @@ __device__ __forceinline__ float dot_pair(float acc, llvq_bf16x2 v, uint32_t xb,
 
 __device__ __forceinline__ uint32_t block_col(uint32_t f, float inv_kb, uint32_t kb) {
   const uint32_t rl = (uint32_t)(((float)f + 0.5f) * inv_kb);
-  return f - rl * kb;
+  return f - __umul24(rl, kb);    // both below 2^24: the full-rate 24-bit multiply
 }
 
 // Decode one odd-coset block (queue entry e) and multiply its slot by the dot product.
@@ -83,11 +91,13 @@ __device__ __forceinline__ void gemv_odd(uint8_t* smem, const EArgs& a, float* p
   od.init(hO, so);
   od.load_fp8(hO);
   float a0 = 0.0f, a1 = 0.0f;
+  uint32_t sq = 0u;
 #pragma unroll
   for (int i = 0; i < 12; ++i) {
+    if ((i & 1) == 0) sq = od.sign_quad(i >> 1);
     const uint32_t ka = od.slot(smem, L, 2 * i);
     const uint32_t kb2 = od.slot(smem, L, 2 * i + 1);
-    const llvq_bf16x2 v = value_pair(od.svhi, od.svlo, ka, kb2);
+    const llvq_bf16x2 v = value_pair_signed(od.svhi, od.svlo, ka, kb2, (i & 1) ? sq >> 16 : sq & 0xffffu);
     if (i & 1)
       a1 = dot_pair<XF32>(a1, v, XF32 ? 0u : xw[i], XF32 ? xf[2 * i] : 0.0f, XF32 ? xf[2 * i + 1] : 0.0f);
     else
@@ -192,7 +202,9 @@ __device__ __forceinline__ bool classify_lane(uint8_t* smem, const ELayout& L, f
     while (Id >= cls[k + 1].start) ++k;             // the sentinel records end the scan
   }
   LLVQ_DCHECK(!valid || (int)k < d.ncls);
-  const LlvqClassHot& h = cls[k];
+  // (the record's byte offset by a 24-bit multiply-add, not the compiler's 32-bit multiply)
+  const LlvqClassHot& h = *reinterpret_cast<const LlvqClassHot*>(
+      smem + mad_u24(k, (uint32_t)sizeof(LlvqClassHot), L.cls));
   const bool odd = ((h.meta >> 17) & 1u) != 0u;
   // J = I - start as the low bits of 2^52 + J (exact: J < 2^41 < 2^52)
   const uint64_t jb = __builtin_bit_cast(uint64_t, Id + (0x1p52 - h.start));
