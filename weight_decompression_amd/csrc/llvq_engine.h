@@ -306,10 +306,11 @@ struct OddDec {
 
 // Even coset: support values (on the codeword's positions, ascending) then complement
 // values (other positions, ascending), on one arithmetic-decoding state.  step(i)
-// returns the biased value byte of the i-th decoded value and its position.  Nonzero
-// values take the bits of s in decode order; the last support value's sign fixes the
-// parity of negatives on the support, and init inserts it into s at bit w - 1 (the
-// support values are all nonzero, so they take bits 0..w-1).  Zero can only be a part's
+// returns the biased value byte of the i-th decoded value in its low 8 bits (the bits
+// above are not defined) and its position.  Nonzero values take the bits of s in decode
+// order; the last support value's sign fixes the parity of negatives on the support, and
+// init inserts it into s at bit w - 1 (the support values are all nonzero, so they take
+// bits 0..w-1).  Zero can only be a part's
 // slot 0, so a value takes a sign bit unless its slot is 0 and the part's slot 0 is zero.
 // s is kept shifted left by 2, so the next sign bit sits at the selector's +4 bit and
 // joins the selector with one and-or; a zero value that takes no bit still gets the
@@ -364,7 +365,9 @@ struct EvenDec {
     }
     uint32_t kb, free_;
     if (i < kSteps) {
-      const StepOut so = decode_step(smem, y, nc, cnt8, 0x0c0c0c00u, fo + kFRow * (uint32_t)i, cnt8);
+      // the row offset fo / 256 joins the table offset through the selector's byte 1, which
+      // also leaves garbage in bits 8..15 of the returned byte (callers keep the low byte)
+      const StepOut so = decode_step(smem, y, nc, cnt8, 0x0c0c0400u, kFRow * (uint32_t)i, fo >> 8);
       kb = so.k;
       free_ = med3_1(so.g, nz0);
       if (i == 6 || i == 10 || i == 14) fo = swi == (uint32_t)(i + 2) ? 0u : fo;
