@@ -76,7 +76,7 @@ def _inc_array(text, name):
     if "{" in body:
         return [[float(v.strip().rstrip("fu")) for v in g.split(",") if v.strip()]
                 for g in re.findall(r"\{([^}]*)\}", body)]
-    return [int(v.rstrip("u")) for v in body.replace("\n", "").split(",") if v.strip()]
+    return [int(v.strip().rstrip("u"), 0) for v in body.replace("\n", "").split(",") if v.strip()]
 
 
 @pytest.mark.parametrize("n", [6, 7])
@@ -104,3 +104,17 @@ def test_tail_tables_are_the_sorted_arrangements(gen, n):
                 assert got == [sum(s << (2 * i) for i, s in enumerate(a)) for a in arr]
                 seen += len(arr)
     assert seen == 4 ** n
+
+
+def test_even_position_table_is_the_even_decode_order(gen):
+    # for every codeword of the (oracle's) sorted Golay table: its positions ascending, then
+    # the other positions ascending, as bytes 2 p
+    with open(build_lib.TABLES_INC) as f:
+        text = f.read()
+    words = _inc_array(text, "kEvenPos")
+    table = list(golay.table())
+    assert len(words) == 6 * len(table) == 6 * 4096
+    for i, c in enumerate(table):
+        order = [p for p in range(24) if (c >> p) & 1] + [p for p in range(24) if not (c >> p) & 1]
+        got = [(words[6 * i + q // 4] >> (8 * (q % 4))) & 0xFF for q in range(24)]
+        assert got == [2 * p for p in order], i

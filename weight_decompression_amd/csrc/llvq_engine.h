@@ -179,7 +179,8 @@ __device__ __forceinline__ double ftab_at(const uint8_t* smem, uint32_t o) {
 
 // Common per-block setup from the class record: J / A split, codeword, initial y.
 struct BlockStart {
-  uint32_t c;   // codeword
+  uint32_t c;   // codeword (not loaded with WANTC = false)
+  uint32_t ci;  // its index in the Golay table
   uint32_t s;   // sign bits
   double y;     // y_0 = (R + 1/2) * n0 / P
 };
@@ -188,7 +189,7 @@ struct BlockStart {
 // decode, which stores to global memory while it decodes: on gfx9 the wait for a load
 // counts every older vector-memory operation, stores included, so a global table read
 // would wait for the chunk stores in flight).
-template <bool LG = false>
+template <bool LG = false, bool WANTC = true>
 __device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELayout& L, double Jd,
                                                   const LlvqClassHot& h) {
   BlockStart bs;
@@ -198,7 +199,9 @@ __device__ __forceinline__ BlockStart block_start(const uint8_t* smem, const ELa
   const uint32_t B = h.meta & 31u;
   bs.s = q & ((1u << B) - 1u);
   const uint32_t R = q >> B;
-  bs.c = LG ? reinterpret_cast<const uint32_t*>(smem + L.golay)[h.toff + r] : dev_tables::kGolayTable[h.toff + r];
+  bs.ci = h.toff + r;
+  bs.c = !WANTC ? 0u
+                : LG ? reinterpret_cast<const uint32_t*>(smem + L.golay)[bs.ci] : dev_tables::kGolayTable[bs.ci];
   bs.y = __builtin_fma((double)R, h.y0s, 0.5 * h.y0s);
   return bs;
 }
@@ -315,11 +318,17 @@ struct OddDec {
 // s is kept shifted left by 2, so the next sign bit sits at the selector's +4 bit and
 // joins the selector with one and-or; a zero value that takes no bit still gets the
 // current one in its selector, harmlessly, since the negated entry of a zero is zero.
-template <int TAIL = 6>
+// POSTAB: the positions in decode order come from kEvenPos (the block's codeword index,
+// 2 p per byte) instead of from the codeword's bits (a find-first-set and a clear per
+// value); step() and slot() then give 2 p (the byte offset of the position in bf16
+// activations) in place of p.  The table is read from global memory, so a kernel with
+// global stores in flight does not use this form.
+template <int TAIL = 6, bool POSTAB = false>
 struct EvenDec {
   static constexpr int kSteps = TailSpec<TAIL>::steps;
   double y;
   uint32_t nc, cnt8, svlo, svhi, nz0, nz1, m, s, codes, c, hp, fo, swi;
+  uint32_t pt[6];
 
   // hp: LDS byte offset of the class record
   __device__ __forceinline__ void init(const LlvqClassHot& h, const BlockStart& bs, uint32_t hp_) {
@@ -341,8 +350,16 @@ struct EvenDec {
     svhi = h.sv0hi;
     nz0 = (h.meta >> 20) & 1u;
     nz1 = (h.meta >> 24) & 1u;
-    c = bs.c;
-    m = w ? bs.c : 0xffffffu;
+    if (POSTAB) {
+      const uint2* t = reinterpret_cast<const uint2*>(dev_tables::kEvenPos + 6u * bs.ci);
+      const uint2 t0 = t[0], t1 = t[1], t2 = t[2];
+      pt[0] = t0.x; pt[1] = t0.y; pt[2] = t1.x; pt[3] = t1.y; pt[4] = t2.x; pt[5] = t2.y;
+      c = 0u;
+      m = 0u;
+    } else {
+      c = bs.c;
+      m = w ? bs.c : 0xffffffu;
+    }
     // F rows: values left after step i are w - 1 - i on the support of a two-part class
     // (row i + 24 - w), else 23 - i (row i); the last support step continues into the
     // complement (24 - w left), row i.
@@ -360,7 +377,7 @@ struct EvenDec {
         svlo = q.z;
         svhi = q.w;
         nz0 = nz1;
-        m = ~c & 0xffffffu;
+        if (!POSTAB) m = ~c & 0xffffffu;
       }
     }
     uint32_t kb, free_;
@@ -379,8 +396,12 @@ struct EvenDec {
     }
     const uint32_t sel = kb | (s & 4u);
     s >>= free_;
-    pos = (uint32_t)__builtin_ctz(m);
-    m &= m - 1u;
+    if (POSTAB) {
+      pos = (pt[i >> 2] >> (8 * (i & 3))) & 0xffu;
+    } else {
+      pos = (uint32_t)__builtin_ctz(m);
+      m &= m - 1u;
+    }
     return __builtin_amdgcn_perm(svhi, svlo, sel);
   }
 
@@ -403,7 +424,7 @@ struct EvenDec {
         svlo = t.x;
         svhi = t.y;
         nz0 = nz1;
-        m = ~c & 0xffffffu;
+        if (!POSTAB) m = ~c & 0xffffffu;
       }
     }
     uint32_t kb, free_;
@@ -422,8 +443,12 @@ struct EvenDec {
     }
     const uint32_t sel = kb | (s & 4u);
     s >>= free_;
-    pos = (uint32_t)__builtin_ctz(m);
-    m &= m - 1u;
+    if (POSTAB) {
+      pos = (pt[i >> 2] >> (8 * (i & 3))) & 0xffu;
+    } else {
+      pos = (uint32_t)__builtin_ctz(m);
+      m &= m - 1u;
+    }
     return sel;
   }
 };

@@ -116,13 +116,12 @@ __device__ __forceinline__ void gemv_even(uint8_t* smem, const EArgs& a, float* 
   const uint32_t fe = entry_f(e);
   const uint32_t be = block_col(fe, inv_kb, kb);
   const LlvqClassHot hE = cls[entry_k(e)];
-  const BlockStart se = block_start(smem, L, entry_J(e), hE);
-  EvenDec<TAIL> ev;
+  const BlockStart se = block_start<false, false>(smem, L, entry_J(e), hE);
+  EvenDec<TAIL, true> ev;
   ev.init(hE, se, L.cls + entry_k(e) * (uint32_t)sizeof(LlvqClassHot));
   ev.load_fp8(hE);
-  const uint32_t col0 = be * 24u;
-  const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(smem + a.xs);
-  const float* xs32 = reinterpret_cast<const float*>(smem + a.xs);
+  // the block's activations; a value's position comes as its byte offset 2 p in bf16
+  const uint8_t* xrow = smem + a.xs + be * (XF32 ? 96u : 48u);
   float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
   for (int i = 0; i < 12; ++i) {
@@ -133,10 +132,11 @@ __device__ __forceinline__ void gemv_even(uint8_t* smem, const EArgs& a, float* 
     uint32_t xb = 0u;
     float x0 = 0.0f, x1 = 0.0f;
     if (XF32) {
-      x0 = xs32[col0 + pa];
-      x1 = xs32[col0 + pb];
+      x0 = *reinterpret_cast<const float*>(xrow + 2u * pa);
+      x1 = *reinterpret_cast<const float*>(xrow + 2u * pb);
     } else {
-      xb = (uint32_t)xs16[col0 + pa] | ((uint32_t)xs16[col0 + pb] << 16);
+      xb = (uint32_t)*reinterpret_cast<const uint16_t*>(xrow + pa) |
+           ((uint32_t)*reinterpret_cast<const uint16_t*>(xrow + pb) << 16);
     }
     if (i & 1)
       a1 = dot_pair<XF32>(a1, v, xb, x0, x1);
