@@ -27,6 +27,7 @@ constexpr int kRing = 128;              // entries per ring (a ring never holds 
 constexpr int kRingBytes = 2 * kEWaves * kRing * 8;   // odd and even ring of every wave
 
 typedef __bf16 llvq_bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t llvq_u16x2 __attribute__((ext_vector_type(2)));
 
 // Two decoded values (selectors ka, kb into the fp8 table svhi:svlo, each in byte 0 with
 // 0x0c above) as a bf16 pair: one v_perm joins the selectors, one picks both fp8 codes, one
@@ -135,8 +136,11 @@ __device__ __forceinline__ void gemv_even(uint8_t* smem, const EArgs& a, float* 
       x0 = *reinterpret_cast<const float*>(xrow + 2u * pa);
       x1 = *reinterpret_cast<const float*>(xrow + 2u * pb);
     } else {
-      xb = (uint32_t)*reinterpret_cast<const uint16_t*>(xrow + pa) |
-           ((uint32_t)*reinterpret_cast<const uint16_t*>(xrow + pb) << 16);
+      // the two 16-bit loads fill the halves of one register (the second a d16_hi load)
+      llvq_u16x2 h2;
+      h2.x = *reinterpret_cast<const uint16_t*>(xrow + pa);
+      h2.y = *reinterpret_cast<const uint16_t*>(xrow + pb);
+      xb = __builtin_bit_cast(uint32_t, h2);
     }
     if (i & 1)
       a1 = dot_pair<XF32>(a1, v, xb, x0, x1);
@@ -150,7 +154,7 @@ __device__ __forceinline__ void gemv_even(uint8_t* smem, const EArgs& a, float* 
 // are the same in every lane (they change only by wave-wide ballot counts).
 struct Rings {
   uint64_t* odd;
-  uint64_t* even;
+  uint64_t* even;   // always odd + kRing
   uint32_t oh, on, eh, en;
 };
 
@@ -163,12 +167,16 @@ __device__ __forceinline__ LaneField load_lane_field(const KDesc& d, const uint8
                                                      uint32_t j0, int T, int u, int lane) {
   LaneField lf;
   const int f = min(u * 64 + lane, T - 1);       // past the tile: the tile's last field, unused
-  const uint64_t bit = (uint64_t)(j0 + (uint32_t)f) * (uint32_t)d.field_bits;
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(packed) + (bit >> 5);
+  // the tile's first bit in 64 bits (uniform), the lane's offset from its word in 32 bits
+  // (f < 2^14 and field_bits <= 64: a 24-bit multiply)
+  const uint64_t tbit = (uint64_t)j0 * (uint32_t)d.field_bits;
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(packed) + (tbit >> 5);
+  const uint32_t bit = ((uint32_t)tbit & 31u) + __umul24((uint32_t)f, (uint32_t)d.field_bits);
+  const uint32_t* p = base + (bit >> 5);
   lf.w0 = p[0];
   lf.w1 = p[1];
   lf.w2 = p[2];
-  lf.sh = (uint32_t)bit & 31u;
+  lf.sh = bit;                                   // the funnel shifts take its low 5 bits
   return lf;
 }
 
@@ -222,8 +230,9 @@ __device__ __forceinline__ bool classify_lane(uint8_t* smem, const ELayout& L, f
   const uint64_t be = __ballot(valid && !odd);
   const uint32_t po = __builtin_amdgcn_mbcnt_hi((uint32_t)(bo >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bo, 0u));
   const uint32_t pe = __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
-  if (valid && odd) R.odd[(R.oh + R.on + po) & (kRing - 1)] = entry;
-  if (valid && !odd) R.even[(R.eh + R.en + pe) & (kRing - 1)] = entry;
+  // one store: the even ring follows the odd one (R.even == R.odd + kRing)
+  const uint32_t slot = odd ? ((R.oh + R.on + po) & (kRing - 1)) : kRing + ((R.eh + R.en + pe) & (kRing - 1));
+  if (valid) R.odd[slot] = entry;
   R.on += (uint32_t)__popcll(bo);
   R.en += (uint32_t)__popcll(be);
   LLVQ_DCHECK(R.on < (uint32_t)kRing && R.en < (uint32_t)kRing);
