@@ -56,9 +56,9 @@ struct SArgs {
 
 // Where one tile's outputs go.
 struct SOut {
-  uint8_t* out;           // the tensor's output
+  uint8_t* out;           // the tile's first output row (tile offsets below are 32-bit)
   const __half* rs;       // the tile's first row scale (EUCLID)
-  int row0, cols, kb;
+  int cols, kb;
   float inv_kb;
   bool vec;               // whole-vector stores allowed (alignment)
 };
@@ -82,23 +82,22 @@ __device__ __forceinline__ SPos stream_snap(const SArgs& m, long long p) {
   return {m.n, 0};
 }
 
-// Output address of block f of the tile and its first column.
-__device__ __forceinline__ void stream_where(const SOut& o, uint32_t f, uint32_t& row, uint32_t& col0) {
-  const uint32_t rl = (uint32_t)(((float)f + 0.5f) * o.inv_kb);
-  row = (uint32_t)o.row0 + rl;
-  col0 = 24u * (f - rl * (uint32_t)o.kb);
+// Row of block f inside the tile and its first column (24-bit multiplies: rl, kb < 2^24).
+__device__ __forceinline__ void stream_where(const SOut& o, uint32_t f, uint32_t& rl, uint32_t& col0) {
+  rl = (uint32_t)(((float)f + 0.5f) * o.inv_kb);
+  col0 = 24u * (f - __umul24(rl, (uint32_t)o.kb));
 }
 
 // 24 zero outputs (an index past the shell union)
 template <int OUT>
 __device__ __forceinline__ void stream_zero(const SOut& o, uint32_t f) {
-  uint32_t row, col0;
-  stream_where(o, f, row, col0);
+  uint32_t rl, col0;
+  stream_where(o, f, rl, col0);
   if (OUT == LLVQ_OUT_POINTS_I8) {
-    uint8_t* dst = o.out + (size_t)row * (size_t)(o.kb * 24) + col0;
+    uint8_t* dst = o.out + rl * (uint32_t)(o.kb * 24) + col0;
     for (int q = 0; q < 24; ++q) dst[q] = 0;
   } else {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(o.out) + (size_t)row * (size_t)o.cols + col0;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(o.out) + rl * (uint32_t)o.cols + col0;
     for (int q = 0; q < 24; ++q)
       if ((int)col0 + q < o.cols) dst[q] = 0;
   }
@@ -112,7 +111,7 @@ __device__ __forceinline__ void stream_zero(const SOut& o, uint32_t f) {
 // as many cache lines.
 struct SPend {
   uint32_t d[3][4];
-  size_t off[3];    // byte offset of the piece in the output
+  uint32_t off[3];  // byte offset of the piece from the tile's first output row
   uint32_t m;       // bits 4q..4q+3: values of piece q to store (0: none, 8: the whole piece)
 };
 
@@ -168,13 +167,13 @@ __device__ __forceinline__ void stream_transpose(const uint8_t* smem, const floa
     const uint32_t fb = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(b << 2), (int)f);
     if ((int)b < n) {
       const uint2 c = *reinterpret_cast<const uint2*>(smem + wbase + 24u * b + 8u * r);
-      uint32_t row, col0;
-      stream_where(o, fb, row, col0);
+      uint32_t rl, col0;
+      stream_where(o, fb, rl, col0);
       const uint32_t col = col0 + 8u * r;
       if (OUT == LLVQ_OUT_POINTS_I8) {
         P.d[q][0] = unbias4(c.x);
         P.d[q][1] = unbias4(c.y);
-        P.off[q] = (size_t)row * (size_t)(o.kb * 24) + col;
+        P.off[q] = rl * (uint32_t)(o.kb * 24) + col;
         P.m |= 8u << (4 * q);
       } else {
         const float sc = part[fb];
@@ -182,7 +181,7 @@ __device__ __forceinline__ void stream_transpose(const uint8_t* smem, const floa
         P.d[q][1] = fp8_pair_bf16<true>(c.x, sc);
         P.d[q][2] = fp8_pair_bf16<false>(c.y, sc);
         P.d[q][3] = fp8_pair_bf16<true>(c.y, sc);
-        P.off[q] = ((size_t)row * (size_t)o.cols + col) * 2u;
+        P.off[q] = (rl * (uint32_t)o.cols + col) * 2u;
         const int left = o.cols - (int)col;
         P.m |= (uint32_t)(left >= 8 ? 8 : (left > 0 ? left : 0)) << (4 * q);
       }
@@ -330,9 +329,9 @@ __global__ __launch_bounds__(kEThreads) void k_decode_stream(KDesc d0, SArgs m, 
     const int nun = (T + 63) >> 6;
     const uint32_t j0 = (uint32_t)(row0 * ts.kb);
     SOut o;
-    o.out = static_cast<uint8_t*>(ts.out);
+    o.out = static_cast<uint8_t*>(ts.out) +
+            (size_t)row0 * (OUT == LLVQ_OUT_POINTS_I8 ? (size_t)ts.kb * 24u : (size_t)ts.cols * 2u);
     o.rs = (!sg && ts.scales) ? ts.scales + row0 : nullptr;
-    o.row0 = row0;
     o.cols = ts.cols;
     o.kb = ts.kb;
     o.inv_kb = 1.0f / (float)ts.kb;
