@@ -279,8 +279,8 @@ struct OddDec {
   }
 
   // The fp8 form: the fp8 value table (load_fp8) and, per position, the value's slot
-  // selector into it (byte 0: slot 0..3; bytes 1-3: 0x0c) instead of the value itself, so
-  // that two positions share one v_perm.  The codeword's +4 (negated entry, off the
+  // selector into it (byte 0: slot 0..3; callers use byte 0 only, the bytes above are not
+  // defined) instead of the value itself, so that two positions share one v_perm.  The codeword's +4 (negated entry, off the
   // codeword) is not in it: sign_quad gives it for four positions at once, to be added to
   // the joined selector of each pair (one add per pair rather than a shift and an and-or
   // per position).
@@ -295,7 +295,7 @@ struct OddDec {
       if (p == kSteps - 1) codes = tail_codes<TAIL>(smem, L, cnt8, y);
       return k;
     }
-    return __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | 0x0c0c0c00u;
+    return __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2);
   }
 
   // The +4 of positions 4q .. 4q+3 (set off the codeword) at bits 2, 10, 18 and 26: the
@@ -391,7 +391,7 @@ struct EvenDec {
       if (i == kSteps - 1) codes = tail_codes<TAIL>(smem, L, cnt8, y);
     } else {
       const uint32_t code = __builtin_amdgcn_ubfe(codes, 2 * (i - kSteps), 2);
-      kb = code | 0x0c0c0c00u;
+      kb = code;   // (byte 0 is the one used)
       free_ = med3_1(code, nz0);
     }
     const uint32_t sel = kb | (s & 4u);
@@ -405,10 +405,10 @@ struct EvenDec {
     return __builtin_amdgcn_perm(svhi, svlo, sel);
   }
 
-  // The batch-1 GEMV's form (see OddDec::slot): fp8 tables, and the selector of the i-th
-  // decoded value (byte 0: slot 0..3, + 4 when negative; bytes 1-3: 0x0c) with its position.  A two-part class
-  // switches to the complement's fp8 table at an even i, so the two positions of a pair
-  // always share a table.
+  // The fp8 form (see OddDec::slot): fp8 tables, and the selector of the i-th decoded
+  // value (byte 0: slot 0..3, + 4 when negative; callers use byte 0 only) with its
+  // position.  A two-part class switches to the complement's fp8 table at an even i, so
+  // the two positions of a pair always share a table.
   __device__ __forceinline__ void load_fp8(const LlvqClassHot& h) {
     svlo = h.sv0lo8;
     svhi = h.sv0hi8;
@@ -438,7 +438,7 @@ struct EvenDec {
       if (i == kSteps - 1) codes = tail_codes<TAIL>(smem, L, cnt8, y);
     } else {
       const uint32_t code = __builtin_amdgcn_ubfe(codes, 2 * (i - kSteps), 2);
-      kb = code | 0x0c0c0c00u;
+      kb = code;   // (byte 0 is the one used)
       free_ = med3_1(code, nz0);
     }
     const uint32_t sel = kb | (s & 4u);
