@@ -280,10 +280,10 @@ struct OddDec {
 
   // The fp8 form: the fp8 value table (load_fp8) and, per position, the value's slot
   // selector into it (byte 0: slot 0..3; callers use byte 0 only, the bytes above are not
-  // defined) instead of the value itself, so that two positions share one v_perm.  The codeword's +4 (negated entry, off the
-  // codeword) is not in it: sign_quad gives it for four positions at once, to be added to
-  // the joined selector of each pair (one add per pair rather than a shift and an and-or
-  // per position).
+  // defined) instead of the value itself, so that four positions share one v_perm
+  // (quad_codes).  The codeword's +4 (negated entry, off the codeword) is not in it:
+  // sign_quad gives it for four positions at once, added to their joined selector (one
+  // add per four positions rather than a shift and an and-or per position).
   __device__ __forceinline__ void load_fp8(const LlvqClassHot& h) {
     svlo = h.sv0lo8;
     svhi = h.sv0hi8;
@@ -296,6 +296,15 @@ struct OddDec {
       return k;
     }
     return __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2);
+  }
+
+  // The fp8 codes of positions 4q .. 4q+3 in one dword: the four slot selectors (byte 0
+  // of each) joined into one selector with their codeword +4s added (a byte never exceeds
+  // 7, so nothing carries), then one v_perm picks all four codes.
+  __device__ __forceinline__ uint32_t quad_codes(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3, int q) const {
+    const uint32_t j01 = __builtin_amdgcn_perm(k1, k0, 0x0c0c0400u);   // k0, k1, 0, 0
+    const uint32_t j23 = __builtin_amdgcn_perm(k3, k2, 0x04000c0cu);   // 0, 0, k2, k3
+    return __builtin_amdgcn_perm(svhi, svlo, j01 + j23 + sign_quad(q));
   }
 
   // The +4 of positions 4q .. 4q+3 (set off the codeword) at bits 2, 10, 18 and 26: the

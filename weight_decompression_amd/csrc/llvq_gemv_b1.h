@@ -38,14 +38,6 @@ __device__ __forceinline__ llvq_bf16x2 value_pair(uint32_t svhi, uint32_t svlo, 
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);
 }
 
-// The same with the pair's +4 (negated entries) in bytes 0 and 1 of ysign.
-__device__ __forceinline__ llvq_bf16x2 value_pair_signed(uint32_t svhi, uint32_t svlo, uint32_t ka, uint32_t kb,
-                                                         uint32_t ysign) {
-  const uint32_t sel = __builtin_amdgcn_perm(kb, ka, 0x0c0c0400u) + ysign;
-  const uint32_t codes = __builtin_amdgcn_perm(svhi, svlo, sel);
-  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);
-}
-
 // acc + v.x a.x + v.y a.y for bf16 activations (one v_dot2c_f32_bf16) or fp32 ones
 template <bool XF32>
 __device__ __forceinline__ float dot_pair(float acc, llvq_bf16x2 v, uint32_t xb, float x0, float x1) {
@@ -92,17 +84,18 @@ __device__ __forceinline__ void gemv_odd(uint8_t* smem, const EArgs& a, float* p
   od.init(hO, so);
   od.load_fp8(hO);
   float a0 = 0.0f, a1 = 0.0f;
-  uint32_t sq = 0u;
 #pragma unroll
-  for (int i = 0; i < 12; ++i) {
-    if ((i & 1) == 0) sq = od.sign_quad(i >> 1);
-    const uint32_t ka = od.slot(smem, L, 2 * i);
-    const uint32_t kb2 = od.slot(smem, L, 2 * i + 1);
-    const llvq_bf16x2 v = value_pair_signed(od.svhi, od.svlo, ka, kb2, (i & 1) ? sq >> 16 : sq & 0xffffu);
-    if (i & 1)
-      a1 = dot_pair<XF32>(a1, v, XF32 ? 0u : xw[i], XF32 ? xf[2 * i] : 0.0f, XF32 ? xf[2 * i + 1] : 0.0f);
-    else
-      a0 = dot_pair<XF32>(a0, v, XF32 ? 0u : xw[i], XF32 ? xf[2 * i] : 0.0f, XF32 ? xf[2 * i + 1] : 0.0f);
+  for (int q = 0; q < 6; ++q) {
+    const uint32_t k0 = od.slot(smem, L, 4 * q);
+    const uint32_t k1 = od.slot(smem, L, 4 * q + 1);
+    const uint32_t k2 = od.slot(smem, L, 4 * q + 2);
+    const uint32_t k3 = od.slot(smem, L, 4 * q + 3);
+    const uint32_t codes = od.quad_codes(k0, k1, k2, k3, q);
+    const llvq_bf16x2 v01 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false);
+    const llvq_bf16x2 v23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true);
+    a0 = dot_pair<XF32>(a0, v01, XF32 ? 0u : xw[2 * q], XF32 ? xf[4 * q] : 0.0f, XF32 ? xf[4 * q + 1] : 0.0f);
+    a1 = dot_pair<XF32>(a1, v23, XF32 ? 0u : xw[2 * q + 1], XF32 ? xf[4 * q + 2] : 0.0f,
+                        XF32 ? xf[4 * q + 3] : 0.0f);
   }
   part[fo] *= a0 + a1;
 }

@@ -213,16 +213,11 @@ __device__ __forceinline__ uint32_t stream_odd_codes(uint8_t* smem, const ELayou
     od.load_fp8(h);
 #pragma unroll
     for (int q = 0; q < 6; ++q) {
-      const uint32_t sq = od.sign_quad(q);   // the codeword's +4 of the four positions
       const uint32_t k0 = od.slot(smem, L, 4 * q);
       const uint32_t k1 = od.slot(smem, L, 4 * q + 1);
       const uint32_t k2 = od.slot(smem, L, 4 * q + 2);
       const uint32_t k3 = od.slot(smem, L, 4 * q + 3);
-      const uint32_t c01 =
-          __builtin_amdgcn_perm(od.svhi, od.svlo, __builtin_amdgcn_perm(k1, k0, 0x0c0c0400u) + (sq & 0xffffu));
-      const uint32_t c23 =
-          __builtin_amdgcn_perm(od.svhi, od.svlo, __builtin_amdgcn_perm(k3, k2, 0x0c0c0400u) + (sq >> 16));
-      w[q] = __builtin_amdgcn_perm(c23, c01, 0x05040100u);
+      w[q] = od.quad_codes(k0, k1, k2, k3, q);
     }
   }
   uint2* s2 = reinterpret_cast<uint2*>(slot);
