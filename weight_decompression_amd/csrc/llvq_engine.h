@@ -244,11 +244,12 @@ __device__ __forceinline__ StepOut decode_step(const uint8_t* smem, double& y, u
   return {g, k};
 }
 
-// Odd coset: one part of 24 values, visited in position order.  step(p) returns the
-// biased value byte 12 + v_p in the low 8 bits (upper bits zero).  The sign of each value
-// follows from the codeword bit and the value mod 4, folded into one byte-table lookup:
-// the selector's +4 (negated entry) for positions off the codeword rides in the addend of
-// the slot popcount.
+// Odd coset: one part of 24 values, visited in position order.  slot(p) returns the
+// value's slot selector; quad_codes turns four of them into four bytes of the class's
+// 8-byte value table (biased values 12 + v_p, or fp8 codes after load_fp8).  The sign of
+// each value follows from the codeword bit and the value mod 4, folded into the table
+// lookup: the table holds each slot's value and its negation, and the selector's +4
+// (negated entry) for positions off the codeword is added per four positions.
 template <int TAIL = 6>
 struct OddDec {
   static constexpr int kSteps = TailSpec<TAIL>::steps;
@@ -265,25 +266,12 @@ struct OddDec {
     codes = 0u;
   }
 
-  __device__ __forceinline__ uint32_t step(const uint8_t* smem, const ELayout& L, int p) {
-    const uint32_t sel = ((notc4 >> p) & 4u) | 0x0c0c0c00u;
-    uint32_t k;
-    if (p < kSteps) {
-      // values left after the step: 23 - p, F row p
-      k = decode_step(smem, y, nc, cnt8, sel, kFRow * (uint32_t)p, cnt8).k;
-      if (p == kSteps - 1) codes = tail_codes<TAIL>(smem, L, cnt8, y);
-    } else {
-      k = __builtin_amdgcn_ubfe(codes, 2 * (p - kSteps), 2) | sel;
-    }
-    return __builtin_amdgcn_perm(svhi, svlo, k);
-  }
-
-  // The fp8 form: the fp8 value table (load_fp8) and, per position, the value's slot
-  // selector into it (byte 0: slot 0..3; callers use byte 0 only, the bytes above are not
-  // defined) instead of the value itself, so that four positions share one v_perm
-  // (quad_codes).  The codeword's +4 (negated entry, off the codeword) is not in it:
-  // sign_quad gives it for four positions at once, added to their joined selector (one
-  // add per four positions rather than a shift and an and-or per position).
+  // load_fp8 switches to the fp8 value table.  slot(p): the value's slot selector (byte 0:
+  // slot 0..3; callers use byte 0 only, the bytes above are not defined), so that four
+  // positions share one v_perm (quad_codes).  The codeword's +4 (negated entry, off the
+  // codeword) is not in it: sign_quad gives it for four positions at once, added to their
+  // joined selector (one add per four positions rather than a shift and an and-or per
+  // position).
   __device__ __forceinline__ void load_fp8(const LlvqClassHot& h) {
     svlo = h.sv0lo8;
     svhi = h.sv0hi8;

@@ -200,17 +200,9 @@ __device__ __forceinline__ uint32_t stream_odd_codes(uint8_t* smem, const ELayou
   OddDec<> od;
   od.init(h, bs);
   uint32_t w[6];
-  if (OUT == LLVQ_OUT_POINTS_I8) {
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-      uint32_t x = od.step(smem, L, 4 * q);
-      x |= od.step(smem, L, 4 * q + 1) << 8;
-      x |= od.step(smem, L, 4 * q + 2) << 16;
-      x |= od.step(smem, L, 4 * q + 3) << 24;
-      w[q] = x;
-    }
-  } else {
-    od.load_fp8(h);
+  // four values per dword: biased bytes (the class's int8 table) or fp8 codes
+  if (OUT != LLVQ_OUT_POINTS_I8) od.load_fp8(h);
+  {
 #pragma unroll
     for (int q = 0; q < 6; ++q) {
       const uint32_t k0 = od.slot(smem, L, 4 * q);

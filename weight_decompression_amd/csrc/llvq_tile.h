@@ -22,16 +22,15 @@ __device__ __forceinline__ void bytes_chunk(uint8_t* smem, const ELayout& L, con
     OddDec<> od;
     od.init(h, bs);
     uint2* dst = reinterpret_cast<uint2*>(smem + tb + 24u * f);
-    uint32_t w0 = 0u, w1 = 0u;
+    uint32_t w[6];
 #pragma unroll
-    for (int p = 0; p < 24; ++p) {
-      const uint32_t bv = od.step(smem, L, p);
-      const int q = p & 7;
-      if (q == 0) w0 = bv;
-      else if (q < 4) w0 |= bv << (8 * q);
-      else if (q == 4) w1 = bv;
-      else w1 |= bv << (8 * (q - 4));
-      if (q == 7) dst[p >> 3] = make_uint2(w0, w1);
+    for (int q = 0; q < 6; ++q) {   // four biased bytes per dword
+      const uint32_t k0 = od.slot(smem, L, 4 * q);
+      const uint32_t k1 = od.slot(smem, L, 4 * q + 1);
+      const uint32_t k2 = od.slot(smem, L, 4 * q + 2);
+      const uint32_t k3 = od.slot(smem, L, 4 * q + 3);
+      w[q] = od.quad_codes(k0, k1, k2, k3, q);
+      if (q & 1) dst[q >> 1] = make_uint2(w[q - 1], w[q]);
     }
   } else {
     const int e = ((c - nco) << 6) + lane;
