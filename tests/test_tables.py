@@ -106,15 +106,16 @@ def test_tail_tables_are_the_sorted_arrangements(gen, n):
     assert seen == 4 ** n
 
 
-def test_even_position_table_is_the_even_decode_order(gen):
+@pytest.mark.parametrize("name,scale", [("kEvenIdx", 1), ("kEvenPos", 2)])
+def test_even_position_table_is_the_even_decode_order(gen, name, scale):
     # for every codeword of the (oracle's) sorted Golay table: its positions ascending, then
-    # the other positions ascending, as bytes 2 p
+    # the other positions ascending, as bytes p (kEvenIdx) or 2 p (kEvenPos)
     with open(build_lib.TABLES_INC) as f:
         text = f.read()
-    words = _inc_array(text, "kEvenPos")
+    words = _inc_array(text, name)
     table = list(golay.table())
     assert len(words) == 6 * len(table) == 6 * 4096
     for i, c in enumerate(table):
         order = [p for p in range(24) if (c >> p) & 1] + [p for p in range(24) if not (c >> p) & 1]
         got = [(words[6 * i + q // 4] >> (8 * (q % 4))) & 0xFF for q in range(24)]
-        assert got == [2 * p for p in order], i
+        assert got == [scale * p for p in order], i

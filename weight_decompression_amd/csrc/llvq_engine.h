@@ -315,12 +315,12 @@ struct OddDec {
 // s is kept shifted left by 2, so the next sign bit sits at the selector's +4 bit and
 // joins the selector with one and-or; a zero value that takes no bit still gets the
 // current one in its selector, harmlessly, since the negated entry of a zero is zero.
-// POSTAB: the positions in decode order come from kEvenPos (the block's codeword index,
-// 2 p per byte) instead of from the codeword's bits (a find-first-set and a clear per
-// value); step() and slot() then give 2 p (the byte offset of the position in bf16
-// activations) in place of p.  The table is read from global memory, so a kernel with
-// global stores in flight does not use this form.
-template <int TAIL = 6, bool POSTAB = false>
+// POSTAB: 0, the positions in decode order come from the codeword's bits (a find-first-set
+// and a clear per value); 1 or 2, from kEvenIdx or kEvenPos (indexed by the block's
+// codeword, p or 2 p per byte: one byte extract per value), and step() and slot() give p
+// or 2 p (the byte offset of the position in bf16 activations).  The table is read from
+// global memory at init: a kernel with global stores in flight issues init before them.
+template <int TAIL = 6, int POSTAB = 0>
 struct EvenDec {
   static constexpr int kSteps = TailSpec<TAIL>::steps;
   double y;
@@ -348,7 +348,8 @@ struct EvenDec {
     nz0 = (h.meta >> 20) & 1u;
     nz1 = (h.meta >> 24) & 1u;
     if (POSTAB) {
-      const uint2* t = reinterpret_cast<const uint2*>(dev_tables::kEvenPos + 6u * bs.ci);
+      const uint2* t = reinterpret_cast<const uint2*>((POSTAB == 2 ? dev_tables::kEvenPos : dev_tables::kEvenIdx) +
+                                                      6u * bs.ci);
       const uint2 t0 = t[0], t1 = t[1], t2 = t[2];
       pt[0] = t0.x; pt[1] = t0.y; pt[2] = t1.x; pt[3] = t1.y; pt[4] = t2.x; pt[5] = t2.y;
       c = 0u;

@@ -84,7 +84,7 @@ __device__ __forceinline__ SPos stream_snap(const SArgs& m, long long p) {
 
 // Row of block f inside the tile and its first column (24-bit multiplies: rl, kb < 2^24).
 __device__ __forceinline__ void stream_where(const SOut& o, uint32_t f, uint32_t& rl, uint32_t& col0) {
-  rl = (uint32_t)(((float)f + 0.5f) * o.inv_kb);
+  rl = (uint32_t)__builtin_fmaf((float)f, o.inv_kb, 0.5f * o.inv_kb);   // (f + 1/2) / Kb, f < 2^22
   col0 = 24u * (f - __umul24(rl, (uint32_t)o.kb));
 }
 

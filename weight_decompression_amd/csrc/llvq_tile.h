@@ -47,14 +47,14 @@ __device__ __forceinline__ void bytes_chunk(uint8_t* smem, const ELayout& L, con
     }
     const LlvqClassHot h = cls[entry_k(ee)];
     const BlockStart bs = block_start<false, false>(smem, L, entry_J(ee), h);
-    EvenDec<6, true> ev;   // positions from the table, as 2 p
+    EvenDec<6, 1> ev;   // positions from the table
     ev.init(h, bs, L.cls + entry_k(ee) * (uint32_t)sizeof(LlvqClassHot));
     uint8_t* dst = smem + tb + 24u * f;
 #pragma unroll
     for (int i = 0; i < 24; ++i) {
-      uint32_t pos2;
-      const uint32_t bv = ev.step(smem, L, i, pos2);
-      dst[pos2 >> 1] = (uint8_t)bv;
+      uint32_t pos;
+      const uint32_t bv = ev.step(smem, L, i, pos);
+      dst[pos] = (uint8_t)bv;
     }
   }
 }
