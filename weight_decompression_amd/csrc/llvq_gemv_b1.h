@@ -338,20 +338,21 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
     if ((uint32_t)lane < R.on) shq[bo + lane] = lo;
     if ((uint32_t)lane < R.en) shq[kLeftEven + be + lane] = le;
     __syncthreads();
+    // even chunks (the longer decode) first, so that the last ones handed out are short
     const int nlo = work[1], nle = work[2];
-    const int nco = (nlo + 63) >> 6;
-    const int nch = nco + ((nle + 63) >> 6);
+    const int nce = (nle + 63) >> 6;
+    const int nch = nce + ((nlo + 63) >> 6);
     for (;;) {
       int c = 0;
       if (lane == 0) c = atomicAdd(&work[3], 1);
       c = __builtin_amdgcn_readfirstlane(c);
       if (c >= nch) break;
-      if (c < nco) {
+      if (c < nce) {
         const int e = (c << 6) + lane;
-        if (e < nlo) gemv_odd<XF32, TAIL>(smem, a, part, shq[e], (uint32_t)kb, inv_kb);
-      } else {
-        const int e = ((c - nco) << 6) + lane;
         if (e < nle) gemv_even<XF32, TAIL>(smem, a, part, shq[kLeftEven + e], (uint32_t)kb, inv_kb);
+      } else {
+        const int e = ((c - nce) << 6) + lane;
+        if (e < nlo) gemv_odd<XF32, TAIL>(smem, a, part, shq[e], (uint32_t)kb, inv_kb);
       }
     }
     __syncthreads();
