@@ -49,62 +49,62 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "0baabec1814f2717b338aa8ae6018f99de387901e17ee55bf5902f0176003fd9",
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
-        "valu_lane_ops_per_unit": 518.8,       # SQ_INSTS_VALU * 64 / blocks
-        "valu_mix_peak_tops": 38.27,           # peak for the executed instruction mix
-        "fetch_bytes_per_launch": 13234978,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "valu_lane_ops_per_unit": 514.9,       # SQ_INSTS_VALU * 64 / blocks
+        "valu_mix_peak_tops": 38.26,           # peak for the executed instruction mix
+        "fetch_bytes_per_launch": 13232974,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "0baabec1814f2717b338aa8ae6018f99de387901e17ee55bf5902f0176003fd9",
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
-        "valu_lane_ops_per_unit": 646.5,
-        "valu_mix_peak_tops": 38.15,
-        "fetch_bytes_per_launch": 62777338,
+        "valu_lane_ops_per_unit": 605.3,
+        "valu_mix_peak_tops": 37.99,
+        "fetch_bytes_per_launch": 62773219,
         "write_bytes_per_launch": 1835008,
     },
     "gemv_3bit_b1": {
-        "source_sha256": "0baabec1814f2717b338aa8ae6018f99de387901e17ee55bf5902f0176003fd9",
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
         "summary": "profiles/gemv_3bit_4096x11008_batch1_k_gemv_wide_tile.md",
         "unit_of_work": "24-weight block (k_gemv_wide_tile)",
         "valu_lane_ops_per_unit": 2011.9,
         "valu_mix_peak_tops": 36.07,
-        "fetch_bytes_per_launch": 32959849,
+        "fetch_bytes_per_launch": 32948764,
         "write_bytes_per_launch": 16384,
     },
     "decode_3bit": {
-        "source_sha256": "0baabec1814f2717b338aa8ae6018f99de387901e17ee55bf5902f0176003fd9",
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
         "summary": "profiles/decode_bf16_3bit_4096x11008_k_decode_wide_tile.md",
         "unit_of_work": "24-weight block (k_decode_wide_tile<bf16>)",
         "valu_lane_ops_per_unit": 2022.0,
         "valu_mix_peak_tops": 35.83,
-        "fetch_bytes_per_launch": 44089917,
+        "fetch_bytes_per_launch": 44092694,
         "write_bytes_per_launch": 90177536,
     },
     "decode_bf16": {
-        "source_sha256": "0baabec1814f2717b338aa8ae6018f99de387901e17ee55bf5902f0176003fd9",
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
         "summary": "profiles/decode_bf16_7b_k_decode_stream.md",
         "unit_of_work": "24-weight block (k_decode_stream<bf16>)",
-        "valu_lane_ops_per_unit": 614.7,
-        "valu_mix_peak_tops": 38.48,
-        "fetch_bytes_per_launch": 102430886,           # one launch = two layers (14 tensors)
-        "write_bytes_per_launch": 1030471632,
+        "valu_lane_ops_per_unit": 611.8,
+        "valu_mix_peak_tops": 38.42,
+        "fetch_bytes_per_launch": 102433118,           # one launch = two layers (14 tensors)
+        "write_bytes_per_launch": 1029895088,
     },
     "roundtrip": {
-        "source_sha256": "0baabec1814f2717b338aa8ae6018f99de387901e17ee55bf5902f0176003fd9",
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
         "summary": "profiles/roundtrip_1e7_k_decode_stream_k_rank.md",
-        "unit_of_work": "point: decode to int8 (580.1) + rank (951.2)",
-        "valu_lane_ops_per_unit": 1531.3,
-        # the two kernels' mix peaks (38.88, 36.48) weighted by their lane-ops
-        "valu_mix_peak_tops": 37.39,
+        "unit_of_work": "point: decode to int8 (548.0) + rank (951.2)",
+        "valu_lane_ops_per_unit": 1499.2,
+        # the two kernels' mix peaks (38.77, 36.48) weighted by their lane-ops
+        "valu_mix_peak_tops": 37.32,
         "fetch_bytes_per_launch": None,        # two kernels per step; see the summary
         "write_bytes_per_launch": None,
     },
     "search": {
-        "source_sha256": "0baabec1814f2717b338aa8ae6018f99de387901e17ee55bf5902f0176003fd9",
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
         "summary": "profiles/search_4096x4096_k_search_k_rank.md",
         # The search issues more VALU instructions per clock than one per CU (mostly fp32
         # fma / max / compares), and more than the harmonic mix of single-instruction

@@ -19,7 +19,8 @@
 // divergence), and the wave decodes a full chunk of 64 blocks whenever a ring holds one.
 // At the end of the tile the rings' remainders (fewer than 64 per ring) are gathered into
 // one shared queue between two barriers and decoded as full chunks by all waves; then the
-// rows are summed.  No wave ever waits on another except at those barriers.
+// rows are summed (a fixed-order DPP reduction per row).  No wave ever waits on another
+// except at those barriers.
 
 #pragma once
 
@@ -45,6 +46,22 @@ __device__ __forceinline__ float dot_pair(float acc, llvq_bf16x2 v, uint32_t xb,
   const uint32_t vb = __builtin_bit_cast(uint32_t, v);
   acc = __builtin_fmaf(__uint_as_float(vb << 16), x0, acc);
   return __builtin_fmaf(__uint_as_float(vb & 0xffff0000u), x1, acc);
+}
+
+// Sum of a float over the 64 lanes in a fixed order: each 16-lane row is reduced by four
+// DPP rotations (8, 4, 2, 1) inside the row, then the four row totals (lanes 0, 16, 32,
+// 48) are added in row order.  Uniform result.
+__device__ __forceinline__ float wave_sum_fixed(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return ((r0 + r1) + r2) + r3;
 }
 
 __device__ __forceinline__ uint32_t block_col(uint32_t f, float inv_kb, uint32_t kb) {
@@ -361,12 +378,11 @@ __global__ __launch_bounds__(kEThreads) void k_gemv_b1(KDesc d, EArgs a, const u
     for (int rl = wave; rl < nrows; rl += kEWaves) {
       float acc = 0.0f;
       for (int b = lane; b < kb; b += 64) acc += part[rl * kb + b];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      const float tot = wave_sum_fixed(acc);
       if (lane == 0) {
         const int r = row0 + rl;
         const float rs = sg ? 1.0f : __half2float(scales[r]);
-        y[r] = acc * rs;
+        y[r] = tot * rs;
       }
     }
     if (tid < 4) work[tid] = 0;

@@ -41,5 +41,10 @@ run copy_fetch timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format cs
   python3 "$REPO/bench.py" --copy-calibration 256
 run copy_write timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/copy_write" -o pmc -- \
   python3 "$REPO/bench.py" --copy-calibration 256
-cd "$REPO" && python3 -m weight_decompression_amd.profile_summary "$OUT" "$ARGS" "$@" > "$OUT/summary.md" || exit $?
+# the summary compiles the kernels' assembly, which needs the generated table headers
+cd "$REPO" || exit 1
+if [ ! -f _build/llvq_tables.inc ] || [ ! -f _build/llvq_wide.inc ] || [ ! -f _build/llvq_search.inc ]; then
+  python3 -c "from weight_decompression_amd import build_lib; build_lib.build_tables(verbose=False)" || exit $?
+fi
+python3 -m weight_decompression_amd.profile_summary "$OUT" "$ARGS" "$@" > "$OUT/summary.md" || exit $?
 echo "profile done"
