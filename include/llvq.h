@@ -58,7 +58,7 @@ extern "C" {
 enum {
   LLVQ_OK = 0,
   LLVQ_EINVAL = -1,        /* invalid argument (null pointer, bad size, bad descriptor) */
-  LLVQ_EUNSUPPORTED = -2,  /* valid request this build does not implement              */
+  LLVQ_EUNSUPPORTED = -2,  /* valid request this library does not implement            */
   LLVQ_EHIP = -3,          /* the HIP runtime reported an error at launch (see below)  */
   LLVQ_ETOOLARGE = -4      /* more blocks than llvq_quantize_noalloc's fixed workspace */
 };

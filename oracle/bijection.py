@@ -10,7 +10,7 @@ The gist.science page (Methodik / 3. Indexierungsschema, 4. Dequantisierungskern
 describes the same walk: shell -> class -> local symmetries, undone with integer
 division and modulo.
 
-Readings taken (listed in the design doc):
+Readings taken (the pages leave these open):
 * codeword: c = T[offset(w) + r] for even classes, c = T[r] for odd classes (T sorted
   by weight then mask, see golay.py);
 * permutation rank: lexicographic rank among the distinct arrangements of the

@@ -8,7 +8,7 @@ coset, and each class owns one contiguous index interval.  Inside a class the fr
 choices are a Golay codeword, a sign pattern obeying the congruence rule, and a
 permutation of the leader.
 
-Readings taken here (the pages do not spell these out; listed in the design doc):
+Readings taken here (the pages do not spell these out):
 
 Even classes (p = 0; all values even).  w = number of values = 2 mod 4 must be the
 weight of a Golay codeword (0, 8, 12, 16 or 24); those values sit on the codeword's

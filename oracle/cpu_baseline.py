@@ -3,7 +3,7 @@
 Test infrastructure: only the benchmark's CPU-baseline leg uses it.  Runs the oracle
 exactly as it stands (decode every block of the sampled rows with the pure-Python
 bijection, then the fp64 dot products; oracle/reference.py) in a process pool over rows
-(at most 16 processes: a GPU machine's CPU share), and reports the wall time.  It is a
+(at most 16 processes: the CPU share of a one-GPU machine), and reports the wall time.  It is a
 reported baseline, not a target.
 """
 

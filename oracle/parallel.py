@@ -6,7 +6,7 @@ functions of reference.py and bijection.py on its share; nothing here computes a
 of its own.  The job's inputs are set before the pool forks, so the workers inherit the
 packed stream instead of receiving a pickled copy per task.
 
-Worker count: the host's usable cores, at most 16 (a GPU machine's CPU share).
+Worker count: the host's usable cores, at most 16 (the CPU share of a one-GPU machine).
 """
 
 import multiprocessing as mp

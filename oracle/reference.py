@@ -6,7 +6,7 @@ gist.science page, Methodik / 4. Dequantisierungskernel): weight rows are cut in
 into a Leech lattice point and its inner product with the matching slice of the
 activation vector is accumulated, so y = W_hat x without ever storing W_hat.
 
-Readings taken (listed in the design doc):
+Readings taken (the pages leave these open):
 
 * packing: a flat little-endian bitstream of fixed-width fields, one per block, in
   row-major block order; field j starts at bit f*j and holds shape | gain << shape_bits;
