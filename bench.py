@@ -57,6 +57,51 @@ KERNEL_PROFILES = {
         "fetch_bytes_per_launch": 13232974,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
+    "gemv_11008x4096_b1": {
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
+        "summary": "profiles/gemv_11008x4096_batch1_k_gemv_b1.md",
+        "unit_of_work": "24-weight block (k_gemv_b1)",
+        "valu_lane_ops_per_unit": 520.2,
+        "valu_mix_peak_tops": 38.32,
+        "fetch_bytes_per_launch": 13136673,
+        "write_bytes_per_launch": 51200,
+    },
+    "gemv_4096x4096_b1": {
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
+        "summary": "profiles/gemv_4096x4096_batch1_k_gemv_b1.md",
+        "unit_of_work": "24-weight block (k_gemv_b1)",
+        "valu_lane_ops_per_unit": 566.4,
+        "valu_mix_peak_tops": 38.46,
+        "fetch_bytes_per_launch": 6045179,
+        "write_bytes_per_launch": 16384,
+    },
+    "gemv_28672x8192_b1": {
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
+        "summary": "profiles/gemv_28672x8192_batch1_k_gemv_b1.md",
+        "unit_of_work": "24-weight block (k_gemv_b1)",
+        "valu_lane_ops_per_unit": 502.0,
+        "valu_mix_peak_tops": 38.22,
+        "fetch_bytes_per_launch": 60836265,
+        "write_bytes_per_launch": 131072,
+    },
+    "gemv_28672x8192_b4": {
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
+        "summary": "profiles/gemv_28672x8192_batch4_k_gemm_mfma.md",
+        "unit_of_work": "24-weight block (k_gemm_mfma)",
+        "valu_lane_ops_per_unit": 605.3,
+        "valu_mix_peak_tops": 37.99,
+        "fetch_bytes_per_launch": 61199727,
+        "write_bytes_per_launch": 458752,
+    },
+    "gemv_28672x8192_b8": {
+        "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
+        "summary": "profiles/gemv_28672x8192_batch8_k_gemm_mfma.md",
+        "unit_of_work": "24-weight block (k_gemm_mfma)",
+        "valu_lane_ops_per_unit": 605.3,
+        "valu_mix_peak_tops": 37.99,
+        "fetch_bytes_per_launch": 61724015,
+        "write_bytes_per_launch": 917504,
+    },
     "gemv_28672x8192_b16": {
         "source_sha256": "192ee3671252d45f2d3cb7363b50622ee8643fad78a47f5dc67c072f4d4dd070",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",

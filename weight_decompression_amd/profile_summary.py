@@ -19,6 +19,7 @@ Usage: python -m weight_decompression_amd.profile_summary OUTDIR "BENCH ARGS" KE
 import csv
 import os
 import sys
+import tempfile
 from collections import defaultdict
 
 from . import issue_rates
@@ -102,8 +103,13 @@ def summarise(outdir, bench_args, specs):
     do_mix = os.path.isdir(os.path.join(outdir, "mix_a")) and os.path.isdir(os.path.join(outdir, "mix_b")) \
         and os.path.exists(rates_md)
     asm = None
+    tmp = None
     if do_mix:
-        asm = os.environ.get("LLVQ_ASM") or issue_rates.device_asm(outdir)
+        # the library's device assembly (tens of MB) goes to a temporary folder, not the output
+        asm = os.environ.get("LLVQ_ASM")
+        if not asm:
+            tmp = tempfile.TemporaryDirectory()
+            asm = issue_rates.device_asm(tmp.name)
         lines.append(f"Issue rates and counter categories: `{os.path.relpath(rates_md, issue_rates.PKG_DIR + '/..')}`.")
         lines.append("")
     for spec in specs:
@@ -153,6 +159,8 @@ def summarise(outdir, bench_args, specs):
         lines.append(f"<!-- profile {kernel} valu_lane_ops_per_unit={per_unit:.1f} fetch={fb:.0f} write={wb:.0f} "
                      f"avg_ns={avg_ns:.0f}{mp} -->")
         lines.append("")
+    if tmp is not None:
+        tmp.cleanup()
     return "\n".join(lines) + "\n"
 
 
