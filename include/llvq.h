@@ -13,7 +13,10 @@
  * division and modulo) and, in the fused GEMV, dots them with the activations without
  * writing decoded weights to memory.  The pages state the problem as converting to
  * and from bitstrings without materialising the codebook, plus a fully parallel
- * dequantisation kernel; the three compute entry points below are exactly those.
+ * dequantisation kernel: llvq_decode / llvq_decode_many and llvq_gemv (index -> vector,
+ * fused with the product) and llvq_encode_ref / llvq_encode_wide (vector -> index).  The
+ * quantiser calls (llvq_search, llvq_quantize, the spherical-GPTQ calls) produce packed
+ * tensors from fp32 weights.
  *
  * Conventions fixed by this library (the pages leave them open):
  *   Lattice coordinates are integers, sqrt(8) times the standard ones; shell m is the
@@ -35,8 +38,11 @@
  * Memory and streams: every array argument of the compute calls is a device pointer
  * owned by the caller.  The calls validate their arguments on the host, enqueue work
  * on `stream` (a hipStream_t; NULL means the default stream) and return without
- * synchronising.  The library allocates no device memory and keeps no state between
- * calls; its tables are compiled into the shared object.  Calls are thread-safe.
+ * synchronising.  The library allocates no device memory; its tables are compiled into
+ * the shared object.  Its only state, per GPU and filled on first use under a lock, is
+ * the device's CU count and LDS size (which size the tiled kernels' grids) and the address
+ * of llvq_quantize_noalloc's workspace array.  Calls are thread-safe (llvq_quantize_noalloc
+ * excepted: see there).
  *
  * Errors: synchronous return codes (below) report invalid arguments and launch
  * failures; nothing is enqueued when a call returns an error.  Data errors found on
