@@ -839,7 +839,7 @@ def main():
         return
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this LLVQ build runs on exactly one GPU (no sharding or collectives are "
+        print("bench.py: this LLVQ library runs on exactly one GPU (no sharding or collectives are "
               "built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
