@@ -1251,9 +1251,7 @@ LLVQ_API int llvq_gptq_factor(int32_t cols, const double* H, double damp, double
   if (err_count && !aligned(err_count, 4)) return LLVQ_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int Kp = (int)gptq_kp(cols), Kb = Kp / 24;
-  // the factor starts at the workspace's first 16-byte boundary (its 256 bytes of slack cover
-  // the shift and the mean): the inverse reads its blocks as 16-byte pairs
-  double* A = reinterpret_cast<double*>((reinterpret_cast<uintptr_t>(workspace) + 15u) & ~(uintptr_t)15u);
+  double* A = static_cast<double*>(workspace);
   double* Linv = A + (size_t)Kp * (size_t)Kp;
   double* mean = Linv + (size_t)Kb * 576;
   const unsigned gfull = grid_for((uint64_t)Kp * (uint64_t)Kp, 256);
@@ -1271,7 +1269,10 @@ LLVQ_API int llvq_gptq_factor(int32_t cols, const double* H, double damp, double
     }
   }
   hipLaunchKernelGGL(k_gptq_inv_diag, dim3(gfull), dim3(256), 0, s, Kp, Linv, U);
-  if (Kb > 1) hipLaunchKernelGGL(k_gptq_inv_cols, dim3(Kb - 1), dim3(kInvThreads), 0, s, A, Kp, Kb, Linv, U);
+  for (int kb = 0; kb + 1 < Kb; ++kb) {
+    hipLaunchKernelGGL(k_gptq_inv_update, dim3(Kb - 1 - kb, kb + 1), dim3(576), 0, s, A, Kp, kb, U);
+    hipLaunchKernelGGL(k_gptq_inv_solve, dim3(kb + 1), dim3(576), 0, s, Kp, kb + 1, Linv, U);
+  }
   hipLaunchKernelGGL(k_gptq_reverse, dim3(gfull), dim3(256), 0, s, Kp, U);
   return launch_status();
 }

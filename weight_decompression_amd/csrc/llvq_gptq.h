@@ -166,96 +166,45 @@ __global__ __launch_bounds__(256) void k_gptq_syrk(double* __restrict__ A, int K
     }
 }
 
-// Block column j of the triangular inverse X = L^-1 (L = the factor in A), one workgroup
-// per block column j < nb - 1, by forward substitution down the column: for i = j+1 .. nb-1,
-//   T = sum_{j <= k < i} L_ik X_kj,   X_ij = -Linv_ii T.
-// The columns are independent, so one launch computes them all.  A lane owns a 2 x 2 patch
-// of the 24 x 24 block (kInvThreads = 144 lanes): per q it reads two values of L_ik and a
-// pair of X_kj from LDS for four fmas, so the products are not bound by LDS issue as with
-// one element per lane.  Each product's pair of blocks is staged in one of two LDS buffers
-// (one barrier per product) while the next pair is already requested; the staging lanes
-// of X_kj are the lanes that wrote it, so a lane reads back only its own results.  Every
-// element is summed over k, then q, in ascending order.  The diagonal blocks X_jj = Linv_jj
-// are written by k_gptq_inv_diag.
-constexpr int kInvThreads = 144;
-constexpr int kInvLd = kGB + 2;             // LDS row stride (doubles): rows 16-byte aligned
-
-__global__ __launch_bounds__(kInvThreads) void k_gptq_inv_cols(const double* __restrict__ A, int Kp, int nb,
-                                                               const double* __restrict__ Linv, double* X) {
-  typedef double llvq_f64x2 __attribute__((ext_vector_type(2)));
-  const int jb = blockIdx.x;                // < nb - 1
-  const int t = threadIdx.x;
-  const int r0 = 2 * (t / 12), c0 = 2 * (t % 12);     // the lane's patch: rows r0, r0+1, columns c0, c0+1
-  __shared__ __align__(16) double lt[2][kGB][kInvLd];
-  __shared__ __align__(16) double xt[2][kGB][kInvLd];
-  __shared__ __align__(16) double ld[kGB][kInvLd];
-  __shared__ __align__(16) double td[kGB][kInvLd];
-  const size_t j0 = (size_t)jb * kGB;
-  for (int ib = jb + 1; ib < nb; ++ib) {
-    const size_t i0 = (size_t)ib * kGB;
-    // staging: the lane moves the pairs (r0, c0..c0+1) and (r0+1, c0..c0+1) of each block
-    auto lrow = [&](int kb, int rr) {
-      return *reinterpret_cast<const llvq_f64x2*>(A + (i0 + (size_t)rr) * Kp + (size_t)kb * kGB + (size_t)c0);
-    };
-    auto xrow = [&](int kb, int rr) {    // X (= U) is only 8-byte aligned: two 8-byte loads
-      const double* p = X + ((size_t)kb * kGB + (size_t)rr) * Kp + j0 + (size_t)c0;
-      llvq_f64x2 v;
-      v.x = p[0];
-      v.y = p[1];
-      return v;
-    };
-    llvq_f64x2 la = lrow(jb, r0), lb = lrow(jb, r0 + 1), xa = xrow(jb, r0), xb = xrow(jb, r0 + 1);
-    const llvq_f64x2 ia = *reinterpret_cast<const llvq_f64x2*>(Linv + (size_t)ib * kGB * kGB + (size_t)r0 * kGB + c0);
-    const llvq_f64x2 ibv =
-        *reinterpret_cast<const llvq_f64x2*>(Linv + (size_t)ib * kGB * kGB + (size_t)(r0 + 1) * kGB + c0);
-    double s00 = 0.0, s01 = 0.0, s10 = 0.0, s11 = 0.0;
-    int b = 0;
-    for (int kb = jb; kb < ib; ++kb) {
-      *reinterpret_cast<llvq_f64x2*>(&lt[b][r0][c0]) = la;
-      *reinterpret_cast<llvq_f64x2*>(&lt[b][r0 + 1][c0]) = lb;
-      *reinterpret_cast<llvq_f64x2*>(&xt[b][r0][c0]) = xa;
-      *reinterpret_cast<llvq_f64x2*>(&xt[b][r0 + 1][c0]) = xb;
-      __syncthreads();
-      if (kb + 1 < ib) {
-        la = lrow(kb + 1, r0);
-        lb = lrow(kb + 1, r0 + 1);
-        xa = xrow(kb + 1, r0);
-        xb = xrow(kb + 1, r0 + 1);
-      }
+// The triangular inverse X = L^-1 (L = the factor in A) below the diagonal, right-looking:
+// block (i, j) first accumulates T_ij = sum_{j <= k < i} L_ik X_kj in place, one k per
+// step, and step i finishes it as X_ij = -Linv_ii T_ij.  Per step k two launches, each
+// spread over the whole chip (a column-by-column forward substitution would leave the first
+// column's ~nb^2/2 block products to one CU):
+//   k_gptq_inv_update(k): T_ij += L_ik X_kj for every i > k and j <= k (one workgroup per
+//     block, one lane per element; X_kk = Linv_kk, X_kj for j < k finished by the solve of
+//     step k), the first term (k = j) starting from 0;
+//   k_gptq_inv_solve(k + 1): X_{k+1, j} = -Linv_{k+1} T_{k+1, j} for every j <= k.
+// Every element is summed over k, then q, in ascending order (a partial sum T is stored
+// between steps exactly, in fp64).
+__global__ __launch_bounds__(576) void k_gptq_inv_update(const double* __restrict__ A, int Kp, int kb, double* X) {
+  const int ib = kb + 1 + (int)blockIdx.x, jb = (int)blockIdx.y;     // i > k, j <= k
+  const int r = threadIdx.x / kGB, c = threadIdx.x % kGB;
+  __shared__ double lt[kGB][kGB + 1];
+  __shared__ double xt[kGB][kGB + 1];
+  const size_t i0 = (size_t)ib * kGB, j0 = (size_t)jb * kGB, k0 = (size_t)kb * kGB;
+  double* t = X + (i0 + (size_t)r) * Kp + j0 + (size_t)c;
+  double s = jb == kb ? 0.0 : *t;
+  lt[r][c] = A[(i0 + (size_t)r) * Kp + k0 + (size_t)c];               // L_ik
+  xt[r][c] = X[(k0 + (size_t)r) * Kp + j0 + (size_t)c];               // X_kj
+  __syncthreads();
 #pragma unroll
-      for (int q = 0; q < kGB; ++q) {
-        const double a0 = lt[b][r0][q], a1 = lt[b][r0 + 1][q];
-        const llvq_f64x2 x = *reinterpret_cast<const llvq_f64x2*>(&xt[b][q][c0]);
-        s00 = fma(a0, x.x, s00);
-        s01 = fma(a0, x.y, s01);
-        s10 = fma(a1, x.x, s10);
-        s11 = fma(a1, x.y, s11);
-      }
-      b ^= 1;
-    }
-    *reinterpret_cast<llvq_f64x2*>(&ld[r0][c0]) = ia;
-    *reinterpret_cast<llvq_f64x2*>(&ld[r0 + 1][c0]) = ibv;
-    td[r0][c0] = s00;
-    td[r0][c0 + 1] = s01;
-    td[r0 + 1][c0] = s10;
-    td[r0 + 1][c0 + 1] = s11;
-    __syncthreads();
-    double x00 = 0.0, x01 = 0.0, x10 = 0.0, x11 = 0.0;
-    for (int q = 0; q <= r0; ++q) {
-      x00 = fma(ld[r0][q], td[q][c0], x00);
-      x01 = fma(ld[r0][q], td[q][c0 + 1], x01);
-    }
-    for (int q = 0; q <= r0 + 1; ++q) {
-      x10 = fma(ld[r0 + 1][q], td[q][c0], x10);
-      x11 = fma(ld[r0 + 1][q], td[q][c0 + 1], x11);
-    }
-    double* o0 = X + (i0 + (size_t)r0) * Kp + j0 + (size_t)c0;
-    double* o1 = o0 + Kp;
-    o0[0] = -x00;
-    o0[1] = -x01;
-    o1[0] = -x10;
-    o1[1] = -x11;
-  }
+  for (int q = 0; q < kGB; ++q) s = fma(lt[r][q], xt[q][c], s);
+  *t = s;
+}
+
+__global__ __launch_bounds__(576) void k_gptq_inv_solve(int Kp, int ib, const double* __restrict__ Linv, double* X) {
+  const int jb = (int)blockIdx.x;           // < ib
+  const int r = threadIdx.x / kGB, c = threadIdx.x % kGB;
+  __shared__ double ld[kGB][kGB + 1];
+  __shared__ double td[kGB][kGB + 1];
+  double* t = X + ((size_t)ib * kGB + (size_t)r) * Kp + (size_t)jb * kGB + (size_t)c;
+  ld[r][c] = Linv[(size_t)ib * kGB * kGB + threadIdx.x];
+  td[r][c] = *t;
+  __syncthreads();
+  double x = 0.0;
+  for (int q = 0; q <= r; ++q) x = fma(ld[r][q], td[q][c], x);
+  *t = -x;
 }
 
 // diagonal blocks of X (= Linv) and zeros above the diagonal
