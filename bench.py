@@ -49,97 +49,97 @@ ROTATE_BYTES = 512 * 1024 * 1024
 # apply and the benchmark reports null for them.
 KERNEL_PROFILES = {
     "gemv_4096x11008_b1": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/gemv_4096x11008_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
         "valu_lane_ops_per_unit": 514.9,       # SQ_INSTS_VALU * 64 / blocks
         "valu_mix_peak_tops": 38.26,           # peak for the executed instruction mix
-        "fetch_bytes_per_launch": 13231905,    # FETCH_SIZE scaled by the copy-kernel calibration
+        "fetch_bytes_per_launch": 13230938,    # FETCH_SIZE scaled by the copy-kernel calibration
         "write_bytes_per_launch": 16384,       # WRITE_SIZE, same calibration
     },
     "gemv_11008x4096_b1": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/gemv_11008x4096_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
         "valu_lane_ops_per_unit": 520.2,
         "valu_mix_peak_tops": 38.32,
-        "fetch_bytes_per_launch": 13135702,
+        "fetch_bytes_per_launch": 13134686,
         "write_bytes_per_launch": 51200,
     },
     "gemv_4096x4096_b1": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/gemv_4096x4096_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
         "valu_lane_ops_per_unit": 566.4,
         "valu_mix_peak_tops": 38.46,
-        "fetch_bytes_per_launch": 6044154,
+        "fetch_bytes_per_launch": 6043133,
         "write_bytes_per_launch": 16384,
     },
     "gemv_28672x8192_b1": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/gemv_28672x8192_batch1_k_gemv_b1.md",
         "unit_of_work": "24-weight block (k_gemv_b1)",
         "valu_lane_ops_per_unit": 502.0,
         "valu_mix_peak_tops": 38.22,
-        "fetch_bytes_per_launch": 60835192,
+        "fetch_bytes_per_launch": 60834186,
         "write_bytes_per_launch": 131072,
     },
     "gemv_28672x8192_b4": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/gemv_28672x8192_batch4_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
         "valu_lane_ops_per_unit": 605.3,
         "valu_mix_peak_tops": 37.99,
-        "fetch_bytes_per_launch": 61185644,
+        "fetch_bytes_per_launch": 61185676,
         "write_bytes_per_launch": 458752,
     },
     "gemv_28672x8192_b8": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/gemv_28672x8192_batch8_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
         "valu_lane_ops_per_unit": 605.3,
         "valu_mix_peak_tops": 37.99,
-        "fetch_bytes_per_launch": 61709864,
+        "fetch_bytes_per_launch": 61709903,
         "write_bytes_per_launch": 917504,
     },
     "gemv_28672x8192_b16": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/gemv_28672x8192_batch16_k_gemm_mfma.md",
         "unit_of_work": "24-weight block (k_gemm_mfma)",
         "valu_lane_ops_per_unit": 605.3,
         "valu_mix_peak_tops": 37.99,
-        "fetch_bytes_per_launch": 62758885,
+        "fetch_bytes_per_launch": 62758155,
         "write_bytes_per_launch": 1835008,
     },
     "gemv_3bit_b1": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/gemv_3bit_4096x11008_batch1_k_gemv_wide_tile.md",
         "unit_of_work": "24-weight block (k_gemv_wide_tile)",
         "valu_lane_ops_per_unit": 2011.9,
         "valu_mix_peak_tops": 36.07,
-        "fetch_bytes_per_launch": 33002607,
+        "fetch_bytes_per_launch": 32999272,
         "write_bytes_per_launch": 16384,
     },
     "decode_3bit": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/decode_bf16_3bit_4096x11008_k_decode_wide_tile.md",
         "unit_of_work": "24-weight block (k_decode_wide_tile<bf16>)",
         "valu_lane_ops_per_unit": 2022.0,
         "valu_mix_peak_tops": 35.83,
-        "fetch_bytes_per_launch": 44151754,
+        "fetch_bytes_per_launch": 44150320,
         "write_bytes_per_launch": 90177536,
     },
     "decode_bf16": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/decode_bf16_7b_k_decode_stream.md",
         "unit_of_work": "24-weight block (k_decode_stream<bf16>)",
         "valu_lane_ops_per_unit": 611.8,
         "valu_mix_peak_tops": 38.42,
-        "fetch_bytes_per_launch": 102428160,           # one launch = two layers (14 tensors)
-        "write_bytes_per_launch": 1029703272,
+        "fetch_bytes_per_launch": 102449744,           # one launch = two layers (14 tensors)
+        "write_bytes_per_launch": 1030306424,
     },
     "roundtrip": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/roundtrip_1e7_k_decode_stream_k_rank.md",
         "unit_of_work": "point: decode to int8 (548.0) + rank (951.2)",
         "valu_lane_ops_per_unit": 1499.2,
@@ -149,7 +149,7 @@ KERNEL_PROFILES = {
         "write_bytes_per_launch": None,
     },
     "search": {
-        "source_sha256": "ac7dc3bb74948806331d0163d7cd7b5205f5613e768d97f2468155c1ba2421e5",
+        "source_sha256": "8877de305f525f4a766bb6a5487c5916aa86d556825e37247766f369a2b9645e",
         "summary": "profiles/search_4096x4096_k_search_k_rank.md",
         # The search issues more VALU instructions per clock than one per CU (mostly fp32
         # fma / max / compares), and more than the harmonic mix of single-instruction

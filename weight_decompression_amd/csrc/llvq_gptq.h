@@ -71,29 +71,44 @@ __global__ __launch_bounds__(64) void k_gptq_potrf_diag(double* __restrict__ A, 
   __shared__ double a[kGB][kGB + 1];
   __shared__ double li[kGB][kGB + 1];
   const int t = threadIdx.x;
-  for (int e = t; e < kGB * kGB; e += 64) a[e / kGB][e % kGB] = A[(size_t)(j0 + e / kGB) * Kp + (size_t)(j0 + e % kGB)];
-  __syncthreads();
+  // lane t < 24 holds row t of the block in registers; the pivot and column k reach the
+  // other lanes by wave shuffles (one wave: no barrier inside the factorisation)
+  double row[kGB];
+#pragma unroll
+  for (int c = 0; c < kGB; ++c) row[c] = t < kGB ? A[(size_t)(j0 + t) * Kp + (size_t)(j0 + c)] : 0.0;
+#pragma unroll
   for (int k = 0; k < kGB; ++k) {
-    if (t == 0) {
-      const double d = a[k][k];
-      if (!(d > 0.0) && bad) atomicAdd(bad, 1);
-      a[k][k] = d > 0.0 ? sqrt(d) : 1.0;
+    const double d = __shfl(row[k], k, 64);               // a[k][k]
+    if (t == 0 && !(d > 0.0) && bad) atomicAdd(bad, 1);
+    const double akk = d > 0.0 ? sqrt(d) : 1.0;
+    if (t == k) row[k] = akk;
+    if (t > k && t < kGB) row[k] /= akk;
+    // rank-1 update of the rest of the block (lower part): a[t][c] -= a[t][k] a[c][k]
+#pragma unroll
+    for (int c = k + 1; c < kGB; ++c) {
+      const double ack = __shfl(row[k], c, 64);           // a[c][k], divided
+      if (t >= c && t < kGB) row[c] -= row[k] * ack;
     }
-    __syncthreads();
-    if (t > k && t < kGB) a[t][k] /= a[k][k];
-    __syncthreads();
-    // rank-1 update of the rest of the block (lower part), rows k+1.., one row per lane
-    if (t > k && t < kGB)
-      for (int c = k + 1; c <= t; ++c) a[t][c] -= a[t][k] * a[c][k];
-    __syncthreads();
   }
-  // inverse of the lower factor, column by column (forward substitution; lane c owns column c)
   if (t < kGB) {
+#pragma unroll
+    for (int c = 0; c < kGB; ++c) a[t][c] = row[c];
+  }
+  __syncthreads();
+  // inverse of the lower factor, column by column (forward substitution; lane c owns column
+  // c and keeps it in registers; the rows of the factor are LDS broadcasts)
+  if (t < kGB) {
+    double lc[kGB];
+#pragma unroll
     for (int r = 0; r < kGB; ++r) {
       double s = (r == t) ? 1.0 : 0.0;
-      for (int q = t; q < r; ++q) s -= a[r][q] * li[q][t];
-      li[r][t] = r < t ? 0.0 : s / a[r][r];
+#pragma unroll
+      for (int q = 0; q < r; ++q)
+        if (q >= t) s -= a[r][q] * lc[q];
+      lc[r] = r < t ? 0.0 : s / a[r][r];
     }
+#pragma unroll
+    for (int r = 0; r < kGB; ++r) li[r][t] = lc[r];
   }
   __syncthreads();
   for (int e = t; e < kGB * kGB; e += 64) {
